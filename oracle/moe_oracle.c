@@ -1,0 +1,477 @@
+/*
+ * CPU oracle for the DeepSeekMoE layer forward with auxiliary-loss-free
+ * (bias) routing.  TEST INFRASTRUCTURE: only the tests, the smoke check and
+ * the bench's CPU-baseline leg may load this library.  It shares no code,
+ * header or table with the HIP path.
+ *
+ * Plain loops, fp64 accumulation, one token at a time, written from the
+ * pages' statement of the method:
+ *   - DeepSeek V3 From Scratch, "The idea", "Worked example" (routing,
+ *     concretely) and "In code" (route, update_bias): sigmoid affinities,
+ *     the per-expert bias added for the top-8 choice only, combine weights
+ *     from the unbiased affinities of the chosen 8 renormalised to sum to 1,
+ *     and the sign-step bias update.
+ *   - kbwen.com DeepSeek feed, "A bias term for each expert": the bias moves
+ *     once per step, over the whole batch, by a fixed 0.001 up or down; no
+ *     token is dropped.
+ *   - Scaling Efficiency: A Deep Dive into the DeepSeek-V3 Architecture,
+ *     "Implementation: A Modular Look": shared expert added to the routed
+ *     sum; each routed expert applied to the tokens that chose it and its
+ *     output accumulated with that token's weight.
+ *   - crackai.dev DeepSeek-V3 summary, "How It Works": 256 routed + 1 shared
+ *     expert, top-8; FP8 with per-tile scaling and FP32 accumulation.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   - expert FFN is a bias-free SwiGLU: y = Wd (silu(Wg a) * (Wu a));
+ *   - ties among equal biased scores go to the lower expert id; the k chosen
+ *     ids are reported in ascending id order;
+ *   - the selection is decided on fp32 biased scores fl32(fl32(s) + b), the
+ *     precision the kernel decides in; the fp64 gap between the k-th and
+ *     (k+1)-th largest fp64 biased score is reported so that near-ties
+ *     (gap < 1e-6) can be told apart;
+ *   - load_i = c_i / T, target = k / E, so sign(target - load_i) =
+ *     sign(k*T - E*c_i), evaluated exactly in integers;
+ *   - rounding points: h and y_perm are rounded to the storage type the
+ *     kernel keeps them in (fp32, bf16, or e4m3 per 1x128 tile for h), the
+ *     shared expert's output and y stay unrounded until the fp32 output;
+ *   - e4m3 (OCP E4M3FN) tile/block scale = amax / 448 in fp32 (1 if amax = 0),
+ *     code = round-to-nearest-even(v / scale) with fp32 division, saturating.
+ *
+ * Build: gcc -O2 -fopenmp -fno-fast-math -ffp-contract=off -shared -fPIC
+ */
+#include <math.h>
+#include <omp.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_BF16 = 1, OR_E4M3 = 2 };
+
+typedef struct {
+    int32_t T, d, E, k, I;
+    int32_t act; /* storage type of x: OR_F32 or OR_BF16 */
+    int32_t wt;  /* storage type of expert weights = expert GEMM input type */
+} or_shape;
+
+typedef struct {
+    const void *gate, *up, *down;           /* [G,I,d], [G,I,d], [G,d,I] */
+    const float *s_gate, *s_up, *s_down;    /* e4m3 only: 128x128 block scales */
+} or_ffn;
+
+/* ------------------------------------------------------------------ codecs */
+
+/* bf16: the upper 16 bits of an IEEE binary32. */
+static double bf16_dec(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* Round a binary32 to the nearest bf16, ties to the even bf16. */
+static uint16_t bf16_enc(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint32_t lower = u & 0xFFFFu;
+    uint32_t upper = u >> 16;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;
+    return (uint16_t)upper;
+}
+
+static double bf16_round(double v) { return bf16_dec(bf16_enc((float)v)); }
+
+/* OCP E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; exponent field 0
+ * is subnormal (m/8 * 2^-6); S.1111.111 is NaN; no infinities; max 448. */
+static double e4m3_formula(uint8_t c) {
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m / 8.0, -6);
+    else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* The formula, evaluated once for each of the 256 codes. */
+static double e4m3_table[256];
+static int e4m3_table_ready;
+
+static double e4m3_dec(uint8_t c) {
+    if (!e4m3_table_ready) {
+#pragma omp critical(e4m3_init)
+        {
+            if (!e4m3_table_ready) {
+                for (int i = 0; i < 256; ++i) e4m3_table[i] = e4m3_formula((uint8_t)i);
+                __atomic_store_n(&e4m3_table_ready, 1, __ATOMIC_RELEASE);
+            }
+        }
+    }
+    return e4m3_table[c];
+}
+
+/* Nearest E4M3FN code to v (finite), ties to the code with even mantissa,
+ * magnitudes beyond 448 saturate to 448.  Written as a search over the 127
+ * non-negative finite codes, which increase in value with the code. */
+static uint8_t e4m3_enc(float vf) {
+    double v = (double)vf;
+    double a = fabs(v);
+    uint8_t sign = (v < 0.0 || (v == 0.0 && signbit(v))) ? 0x80 : 0x00;
+    if (a >= 448.0) return sign | 0x7E;
+    int lo = 0, hi = 0x7E; /* value(lo) <= a < value(hi) after the search */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (e4m3_dec((uint8_t)mid) <= a) lo = mid; else hi = mid;
+    }
+    double dlo = a - e4m3_dec((uint8_t)lo), dhi = e4m3_dec((uint8_t)hi) - a;
+    int c;
+    if (dlo < dhi) c = lo;
+    else if (dhi < dlo) c = hi;
+    else c = (lo & 1) ? hi : lo;
+    return sign | (uint8_t)c;
+}
+
+/* Exposed for the codec pins. */
+double oracle_bf16_decode(uint16_t b) { return bf16_dec(b); }
+uint16_t oracle_bf16_encode(float f) { return bf16_enc(f); }
+double oracle_e4m3_decode(uint8_t c) { return e4m3_dec(c); }
+uint8_t oracle_e4m3_encode(float f) { return e4m3_enc(f); }
+
+/* One 1x128 tile: scale = amax / 448 (fp32), codes of v / scale (fp32 division).
+ * Fine-grained fp8 tiles: crackai.dev DeepSeek-V3 summary, "How It Works"
+ * (per-tile scaling, FP32 accumulation); DeepSeek V3 From Scratch, "The idea". */
+static float quant_tile(const float *v, int n, uint8_t *q) {
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float a = fabsf(v[i]);
+        if (a > amax) amax = a;
+    }
+    float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    for (int i = 0; i < n; ++i) q[i] = e4m3_enc(v[i] / s);
+    return s;
+}
+
+/* Quantise rows of `cols` values (cols % 128 == 0) per 1x128 tile.
+ * in_dtype OR_F32 or OR_BF16.  q: [rows, cols], scales: [rows, cols/128]. */
+void oracle_quant_e4m3_rows(int64_t rows, int32_t cols, int32_t in_dtype, const void *in,
+                            uint8_t *q, float *scales) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        float v[128];
+        for (int tb = 0; tb < cols / 128; ++tb) {
+            for (int i = 0; i < 128; ++i) {
+                int64_t j = r * cols + tb * 128 + i;
+                v[i] = in_dtype == OR_BF16 ? (float)bf16_dec(((const uint16_t *)in)[j])
+                                           : ((const float *)in)[j];
+            }
+            scales[r * (cols / 128) + tb] = quant_tile(v, 128, q + r * cols + tb * 128);
+        }
+    }
+}
+
+/* ----------------------------------------------------------- element access */
+
+static double x_at(const or_shape *sh, const void *x, int64_t t, int64_t j) {
+    int64_t i = t * sh->d + j;
+    return sh->act == OR_BF16 ? bf16_dec(((const uint16_t *)x)[i]) : (double)((const float *)x)[i];
+}
+
+/* Weight element [g, n, j] of a [G, N, K] stack (with [G, N/128, K/128]
+ * block scales for e4m3). */
+static double w_at(int dtype, const void *w, const float *s, int64_t N, int64_t K, int64_t g,
+                   int64_t n, int64_t j) {
+    int64_t i = (g * N + n) * K + j;
+    if (dtype == OR_F32) return (double)((const float *)w)[i];
+    if (dtype == OR_BF16) return bf16_dec(((const uint16_t *)w)[i]);
+    double sc = (double)s[(g * (N / 128) + n / 128) * (K / 128) + j / 128];
+    return e4m3_dec(((const uint8_t *)w)[i]) * sc;
+}
+
+/* The expert FFN input for token t: x itself, or x quantised per 1x128 tile
+ * when the expert GEMMs run in e4m3 (dequantised values q * s). */
+static void gemm_input_row(const or_shape *sh, const void *x, int64_t t, double *a) {
+    if (sh->wt != OR_E4M3) {
+        for (int j = 0; j < sh->d; ++j) a[j] = x_at(sh, x, t, j);
+        return;
+    }
+    float v[128];
+    uint8_t q[128];
+    for (int tb = 0; tb < sh->d / 128; ++tb) {
+        for (int i = 0; i < 128; ++i) v[i] = (float)x_at(sh, x, t, tb * 128 + i);
+        double s = (double)quant_tile(v, 128, q);
+        for (int i = 0; i < 128; ++i) a[tb * 128 + i] = e4m3_dec(q[i]) * s;
+    }
+}
+
+/* Round an intermediate vector to the storage type the GEMM consumes it in. */
+static void round_to_gemm_input(int wt, double *h, int n) {
+    if (wt == OR_F32) {
+        for (int i = 0; i < n; ++i) h[i] = (double)(float)h[i];
+    } else if (wt == OR_BF16) {
+        for (int i = 0; i < n; ++i) h[i] = bf16_round(h[i]);
+    } else {
+        float v[128];
+        uint8_t q[128];
+        for (int tb = 0; tb < n / 128; ++tb) {
+            for (int i = 0; i < 128; ++i) v[i] = (float)h[tb * 128 + i];
+            double s = (double)quant_tile(v, 128, q);
+            for (int i = 0; i < 128; ++i) h[tb * 128 + i] = e4m3_dec(q[i]) * s;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------- the FFN */
+
+/* One SwiGLU expert (index g of the stack) on one input row a[d]:
+ *   u_g = Wg a, u_u = Wu a, h = silu(u_g) * u_u with silu(z) = z / (1 + e^-z),
+ *   h rounded to the GEMM input type, y = Wd h.  fp64 throughout.
+ * Expert structure: Scaling Efficiency ..., "Implementation: A Modular Look"
+ * (one MLP per routed expert plus one shared MLP); gated form: our reading. */
+static void ffn_row(const or_shape *sh, const or_ffn *w, int64_t g, const double *a, double *y,
+                    double *hbuf) {
+    const int64_t d = sh->d, I = sh->I;
+    for (int64_t n = 0; n < I; ++n) {
+        double ug = 0.0, uu = 0.0;
+        for (int64_t j = 0; j < d; ++j) {
+            ug += w_at(sh->wt, w->gate, w->s_gate, I, d, g, n, j) * a[j];
+            uu += w_at(sh->wt, w->up, w->s_up, I, d, g, n, j) * a[j];
+        }
+        hbuf[n] = ug / (1.0 + exp(-ug)) * uu;
+    }
+    round_to_gemm_input(sh->wt, hbuf, (int)I);
+    for (int64_t n = 0; n < d; ++n) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < I; ++i) acc += w_at(sh->wt, w->down, w->s_down, d, I, g, n, i) * hbuf[i];
+        y[n] = acc;
+    }
+}
+
+/* y_perm storage: fp32 when the layer is fp32, else bf16. */
+static double round_yperm(const or_shape *sh, double v) {
+    return sh->wt == OR_F32 ? (double)(float)v : bf16_round(v);
+}
+
+/* ------------------------------------------------------------- the router */
+
+/* Route one token.  DeepSeek V3 From Scratch, "In code" (route) and
+ * "Worked example": affinity s = sigmoid(x . g_i) for each expert; the k
+ * experts with the largest s + b are chosen; their unbiased s, divided by
+ * the sum over the chosen k, are the combine weights.  kbwen.com DeepSeek
+ * feed, "A bias term for each expert": the bias is used only for the choice.
+ *   idx[k]: chosen ids, ascending; wgt[k]: weights in that order;
+ *   *gap: (k-th largest) - ((k+1)-th largest) fp64 biased score;
+ *   s_out[E] (optional): fp64 affinities. */
+static void route_token(const or_shape *sh, const void *x, const float *wr, const float *bias,
+                        int64_t t, int32_t *idx, double *wgt, double *gap, double *s_out) {
+    const int E = sh->E, k = sh->k, d = sh->d;
+    double *s = (double *)malloc(sizeof(double) * E);
+    float *v32 = (float *)malloc(sizeof(float) * E);
+    char *taken = (char *)calloc((size_t)(E > 0 ? E : 1), 1);
+    for (int e = 0; e < E; ++e) {
+        double l = 0.0;
+        for (int j = 0; j < d; ++j) l += x_at(sh, x, t, j) * (double)wr[(int64_t)e * d + j];
+        s[e] = 1.0 / (1.0 + exp(-l));
+        v32[e] = (float)s[e] + bias[e]; /* fp32 add: the selection is decided in fp32 */
+    }
+    /* k rounds of "largest remaining biased score; equal scores -> lower id" */
+    for (int r = 0; r < k; ++r) {
+        int best = -1;
+        for (int e = 0; e < E; ++e)
+            if (!taken[e] && (best < 0 || v32[e] > v32[best])) best = e;
+        taken[best] = 1;
+    }
+    int n = 0;
+    for (int e = 0; e < E; ++e)
+        if (taken[e]) idx[n++] = e;
+    double sum = 0.0;
+    for (int j = 0; j < k; ++j) sum += s[idx[j]];
+    for (int j = 0; j < k; ++j) wgt[j] = s[idx[j]] / sum;
+    if (gap) {
+        /* fp64 biased scores: k-th and (k+1)-th largest */
+        double *v = (double *)malloc(sizeof(double) * E);
+        for (int e = 0; e < E; ++e) v[e] = s[e] + (double)bias[e];
+        double kth = 0.0, k1th = 0.0;
+        memset(taken, 0, (size_t)E);
+        for (int r = 0; r <= k && r < E; ++r) {
+            int best = -1;
+            for (int e = 0; e < E; ++e)
+                if (!taken[e] && (best < 0 || v[e] > v[best])) best = e;
+            taken[best] = 1;
+            if (r == k - 1) kth = v[best];
+            if (r == k) k1th = v[best];
+        }
+        *gap = (k < E) ? kth - k1th : INFINITY;
+        free(v);
+    }
+    if (s_out) memcpy(s_out, s, sizeof(double) * E);
+    free(s);
+    free(v32);
+    free(taken);
+}
+
+/* Route a list of tokens (tok == NULL: tokens 0..ntok-1).
+ * idx, g: [ntok, k]; gap: [ntok] or NULL; s_out: [ntok, E] or NULL. */
+void oracle_route(const or_shape *sh, const void *x, const float *wr, const float *bias,
+                  int64_t ntok, const int32_t *tok, int32_t *idx, float *g, double *gap,
+                  double *s_out) {
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t i = 0; i < ntok; ++i) {
+        int64_t t = tok ? tok[i] : i;
+        double w[64];
+        route_token(sh, x, wr, bias, t, idx + i * sh->k, w, gap ? gap + i : NULL,
+                    s_out ? s_out + i * sh->E : NULL);
+        for (int j = 0; j < sh->k; ++j) g[i * sh->k + j] = (float)w[j];
+    }
+}
+
+/* ----------------------------------------------------------- the dispatch */
+
+/* Load per expert, its exclusive prefix sum, and the stable grouping of the
+ * T*k assignments by expert (flat id f = t*k + j kept in ascending order
+ * within an expert).  Load: DeepSeek V3 From Scratch, "In code"
+ * (update_bias: fraction of tokens per expert); the per-expert gather:
+ * Scaling Efficiency ..., "Implementation: A Modular Look".
+ *   counts[E], offsets[E+1], row_src[T*k] (row -> flat id), row_of[T*k]. */
+void oracle_dispatch(int32_t T, int32_t E, int32_t k, const int32_t *idx, int32_t *counts,
+                     int32_t *offsets, int32_t *row_src, int32_t *row_of) {
+    int64_t A = (int64_t)T * k;
+    for (int e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t f = 0; f < A; ++f) counts[idx[f]]++;
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int32_t *fill = (int32_t *)calloc((size_t)(E > 0 ? E : 1), sizeof(int32_t));
+    for (int64_t f = 0; f < A; ++f) {
+        int e = idx[f];
+        int32_t r = offsets[e] + fill[e]++;
+        row_src[r] = (int32_t)f;
+        row_of[f] = r;
+    }
+    free(fill);
+}
+
+/* -------------------------------------------------------- the bias update */
+
+/* DeepSeek V3 From Scratch, "In code" (update_bias): b <- b + step *
+ * sign(target - load); kbwen.com DeepSeek feed, "A bias term for each
+ * expert": once per step over the whole batch, the same fixed amount up or
+ * down (0.001).  With load = c/T and target = k/E, sign(target - load) =
+ * sign(k*T - E*c).  b is fp32 state: b <- fl32(b + fl32(gamma) * sign). */
+void oracle_bias_update(int32_t E, int32_t k, int32_t T, const int32_t *counts, float gamma,
+                        float *bias) {
+    for (int e = 0; e < E; ++e) {
+        int64_t diff = (int64_t)k * T - (int64_t)E * counts[e];
+        float sg = diff > 0 ? 1.0f : (diff < 0 ? -1.0f : 0.0f);
+        bias[e] = bias[e] + gamma * sg;
+    }
+}
+
+/* -------------------------------------------------- expert FFN and combine */
+
+/* Routed expert FFN on permuted rows (the expert FFN stage on its own):
+ * row r in [offsets[e], offsets[e+1]) goes through expert e.
+ * a_rows: [A, d] in the GEMM input type (f32, bf16 bits, or e4m3 codes with
+ * a_scales [A, d/128]).  y_perm: [A, d] fp32 or bf16 bits (see round_yperm). */
+void oracle_expert_ffn(const or_shape *sh, const or_ffn *w, const int32_t *offsets,
+                       const void *a_rows, const float *a_scales, void *y_perm) {
+    const int64_t d = sh->d, A = (int64_t)sh->T * sh->k;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < A; ++r) {
+        int e = 0;
+        while (offsets[e + 1] <= r) ++e;
+        double *a = (double *)malloc(sizeof(double) * d);
+        double *y = (double *)malloc(sizeof(double) * d);
+        double *h = (double *)malloc(sizeof(double) * sh->I);
+        for (int64_t j = 0; j < d; ++j) {
+            int64_t i = r * d + j;
+            if (sh->wt == OR_F32) a[j] = ((const float *)a_rows)[i];
+            else if (sh->wt == OR_BF16) a[j] = bf16_dec(((const uint16_t *)a_rows)[i]);
+            else a[j] = e4m3_dec(((const uint8_t *)a_rows)[i]) * (double)a_scales[r * (d / 128) + j / 128];
+        }
+        ffn_row(sh, w, e, a, y, h);
+        for (int64_t j = 0; j < d; ++j) {
+            double v = round_yperm(sh, y[j]);
+            if (sh->wt == OR_F32) ((float *)y_perm)[r * d + j] = (float)v;
+            else ((uint16_t *)y_perm)[r * d + j] = bf16_enc((float)v);
+        }
+        free(a);
+        free(y);
+        free(h);
+    }
+}
+
+/* Shared expert plus the weighted sum of each token's k routed rows:
+ * y[t] = shared(x[t]) + sum_j g[t,j] * y_perm[row_of[t*k + j]], j ascending
+ * (= ascending expert id).  Scaling Efficiency ..., "Implementation: A
+ * Modular Look" (shared output + routed output, routed rows scaled by their
+ * weight); DeepSeek V3 From Scratch, "The idea" (one shared expert every
+ * token uses).  y: [ntok, d] fp32. */
+void oracle_combine(const or_shape *sh, const or_ffn *shared, const void *x, const void *y_perm,
+                    const int32_t *row_of, const float *g, int64_t ntok, const int32_t *tok,
+                    float *y) {
+    const int64_t d = sh->d, k = sh->k;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < ntok; ++i) {
+        int64_t t = tok ? tok[i] : i;
+        double *a = (double *)malloc(sizeof(double) * d);
+        double *ys = (double *)malloc(sizeof(double) * d);
+        double *h = (double *)malloc(sizeof(double) * sh->I);
+        gemm_input_row(sh, x, t, a);
+        ffn_row(sh, shared, 0, a, ys, h);
+        for (int64_t j = 0; j < d; ++j) {
+            double acc = ys[j];
+            for (int64_t q = 0; q < k; ++q) {
+                int64_t r = row_of[t * k + q];
+                double v = sh->wt == OR_F32 ? (double)((const float *)y_perm)[r * d + j]
+                                            : bf16_dec(((const uint16_t *)y_perm)[r * d + j]);
+                acc += (double)g[t * k + q] * v;
+            }
+            y[i * d + j] = (float)acc;
+        }
+        free(a);
+        free(ys);
+        free(h);
+    }
+}
+
+/* ------------------------------------------------------ the whole forward */
+
+/* The layer forward for a list of tokens (tok == NULL: 0..ntok-1).  Each
+ * token is independent of the others given the bias: route, run its k
+ * experts and the shared expert, combine.  idx, g: [ntok, k]; gap: [ntok]
+ * or NULL; y: [ntok, d] fp32. */
+void oracle_forward(const or_shape *sh, const void *x, const float *wr, const float *bias,
+                    const or_ffn *experts, const or_ffn *shared, int64_t ntok, const int32_t *tok,
+                    int32_t *idx, float *g, double *gap, float *y) {
+    const int64_t d = sh->d, k = sh->k;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < ntok; ++i) {
+        int64_t t = tok ? tok[i] : i;
+        double w[64];
+        route_token(sh, x, wr, bias, t, idx + i * k, w, gap ? gap + i : NULL, NULL);
+        for (int64_t j = 0; j < k; ++j) g[i * k + j] = (float)w[j];
+        double *a = (double *)malloc(sizeof(double) * d);
+        double *yr = (double *)malloc(sizeof(double) * d);
+        double *acc = (double *)malloc(sizeof(double) * d);
+        double *h = (double *)malloc(sizeof(double) * sh->I);
+        gemm_input_row(sh, x, t, a);
+        ffn_row(sh, shared, 0, a, acc, h);
+        for (int64_t j = 0; j < k; ++j) {
+            ffn_row(sh, experts, idx[i * k + j], a, yr, h);
+            for (int64_t n = 0; n < d; ++n) acc[n] += w[j] * round_yperm(sh, yr[n]);
+        }
+        for (int64_t n = 0; n < d; ++n) y[i * d + n] = (float)acc[n];
+        free(a);
+        free(yr);
+        free(acc);
+        free(h);
+    }
+}
+
+/* Threads an OpenMP region of this library uses (for reporting). */
+int oracle_num_threads(void) {
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        n = omp_get_num_threads();
+    }
+    return n;
+}

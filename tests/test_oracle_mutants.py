@@ -1,0 +1,55 @@
+"""Pin strength: plausible mistakes planted in a copy of the oracle (on the
+CPU) must each make the pin suite fail.  Nothing here touches a GPU or the
+HIP path; the mutant libraries live in a temporary directory."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
+
+# (name, text in moe_oracle.c, replacement)
+MUTANTS = [
+    ("sigmoid sign", "s[e] = 1.0 / (1.0 + exp(-l));", "s[e] = 1.0 / (1.0 + exp(l));"),
+    ("bias ignored in choice", "v32[e] = (float)s[e] + bias[e];", "v32[e] = (float)s[e];"),
+    ("weights from biased score", "for (int j = 0; j < k; ++j) wgt[j] = s[idx[j]] / sum;",
+     "for (int j = 0; j < k; ++j) wgt[j] = (s[idx[j]] + bias[idx[j]]) / sum;"),
+    ("ties to higher id", "if (!taken[e] && (best < 0 || v32[e] > v32[best])) best = e;",
+     "if (!taken[e] && (best < 0 || v32[e] >= v32[best])) best = e;"),
+    ("silu sign", "hbuf[n] = ug / (1.0 + exp(-ug)) * uu;", "hbuf[n] = ug / (1.0 + exp(ug)) * uu;"),
+    ("gate/up swapped", "hbuf[n] = ug / (1.0 + exp(-ug)) * uu;", "hbuf[n] = uu / (1.0 + exp(-uu)) * ug;"),
+    ("weight transposed", "int64_t i = (g * N + n) * K + j;", "int64_t i = (g * K + j) * N + n;"),
+    ("shared expert dropped", "        ffn_row(sh, shared, 0, a, acc, h);\n",
+     "        ffn_row(sh, shared, 0, a, acc, h);\n        for (int64_t n = 0; n < d; ++n) acc[n] = 0.0;\n"),
+    ("bias step sign flipped", "float sg = diff > 0 ? 1.0f : (diff < 0 ? -1.0f : 0.0f);",
+     "float sg = diff > 0 ? -1.0f : (diff < 0 ? 1.0f : 0.0f);"),
+    ("sign(0) moves the bias", "float sg = diff > 0 ? 1.0f : (diff < 0 ? -1.0f : 0.0f);",
+     "float sg = diff >= 0 ? 1.0f : -1.0f;"),
+    ("unstable dispatch", "    for (int64_t f = 0; f < A; ++f) {\n        int e = idx[f];",
+     "    for (int64_t f = A - 1; f >= 0; --f) {\n        int e = idx[f];"),
+    ("h not rounded to bf16", "for (int i = 0; i < n; ++i) h[i] = bf16_round(h[i]);", "(void)0;"),
+    ("y_perm not rounded", "return sh->wt == OR_F32 ? (double)(float)v : bf16_round(v);", "return v;"),
+    ("tile scale off", "float s = amax > 0.0f ? amax / 448.0f : 1.0f;", "float s = amax > 0.0f ? amax / 240.0f : 1.0f;"),
+    ("gap off by one", "if (r == k) k1th = v[best];", "if (r == k - 1) k1th = v[best];"),
+    ("bf16 rounding truncates", "if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;", "(void)lower;"),
+    ("e4m3 ties away from zero", "else c = (lo & 1) ? hi : lo;", "else c = hi;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pin_suite_catches_mutant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation site for '{name}' not found"
+    mut = src.replace(old, new, 1)
+    c = tmp_path / "mut.c"
+    c.write_text(mut)
+    so = tmp_path / "libmut.so"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fno-fast-math", "-ffp-contract=off", "-shared",
+                           "-fPIC", "-o", str(so), str(c), "-lm"])
+    env = dict(os.environ, MOE_ORACLE_LIB=str(so), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant '{name}' survived the pins:\n{r.stdout[-2000:]}"
