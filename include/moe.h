@@ -1,0 +1,200 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) DeepSeekMoE layer forward with
+ * auxiliary-loss-free (bias) routing.
+ *
+ * The layer, as the pages state it:
+ *   - DeepSeek V3 From Scratch, "The idea": 256 routed experts plus one shared
+ *     expert that every token uses; each token goes to its top 8 routed
+ *     experts; a per-expert bias, added to the router affinity, steers which
+ *     experts are chosen, while the combine weights come from the unbiased
+ *     affinities; the bias is a control loop, not a loss term.
+ *   - DeepSeek V3 From Scratch, "Worked example" (routing, concretely) and
+ *     "In code" (route, update_bias): sigmoid affinities, top-k of affinity
+ *     plus bias, the chosen k unbiased affinities renormalised to sum to 1,
+ *     and bias <- bias + step * sign(target - load).
+ *   - kbwen.com DeepSeek feed, "A bias term for each expert": the bias moves
+ *     once per step, from the load over the whole batch, by the same fixed
+ *     amount (0.001) up or down; no token is dropped.
+ *   - Scaling Efficiency: A Deep Dive into the DeepSeek-V3 Architecture,
+ *     "Implementation: A Modular Look": the output is the shared expert's
+ *     output plus, for each routed expert, its output on the tokens that
+ *     chose it scaled by their weight.
+ *   - crackai.dev DeepSeek-V3 summary, "How It Works": the routed work is
+ *     split into a dispatch and a combine around the expert computation; FP8
+ *     expert matmuls with per-tile scaling and FP32 accumulation.
+ * Our readings where the pages are silent: each expert is a bias-free SwiGLU
+ * FFN y = W_down (silu(W_gate a) * (W_up a)); equal biased scores go to the
+ * lower expert id; the k chosen ids are reported in ascending order.
+ *
+ * Conventions for every call:
+ *   - Tensors are row-major and contiguous, in device memory owned by the
+ *     caller.  The library never allocates, frees or synchronises, and never
+ *     reads device memory on the host.  Work is enqueued on `stream` (a
+ *     hipStream_t; NULL is the default stream) and the call returns.
+ *   - Arguments are validated on the host before anything is launched:
+ *     MOE_EINVAL for a null required pointer, non-positive sizes, k > E, or
+ *     d / I not multiples of 128 with e4m3; MOE_ENOTSUP for shapes this build
+ *     does not cover (E != 256, k != 8, d or I not a multiple of 64, an
+ *     unsupported dtype pair); MOE_EWORKSPACE when ws_bytes is below
+ *     moe_workspace_bytes(); MOE_EHIP when a launch reports an error.
+ *     Device faults surface at the caller's next synchronisation.
+ *   - No C++ exception crosses the ABI; the library never aborts.
+ *   - Calls are stateless and re-entrant; calls on different streams that
+ *     share output buffers race, as with any kernel launch.
+ *
+ * Storage types (moe_dtype_t): fp32; bf16 as 16-bit patterns (upper half of
+ * binary32); e4m3 as OCP FP8 E4M3FN bytes with fp32 scales.  Supported
+ * (act, wt) pairs: (F32, F32), (BF16, BF16), (BF16, E4M3).  The router is
+ * always fp32.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = 1,
+    MOE_ENOTSUP = 2,
+    MOE_EWORKSPACE = 3,
+    MOE_EHIP = 4
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2 } moe_dtype_t;
+
+/* Shape of one layer call.  T tokens, model width d, E routed experts, top-k,
+ * expert intermediate width I.  act: storage type of x.  wt: storage type of
+ * the expert weights, which is also the type the expert GEMMs read their
+ * activations in (x_perm and the intermediate h). */
+typedef struct {
+    int32_t T, d, E, k, I;
+    int32_t act;
+    int32_t wt;
+} moe_desc_t;
+
+/* Weights of a stack of G SwiGLU experts (G = E routed, or G = 1 shared):
+ * gate, up: [G, I, d]; down: [G, d, I] (each row contiguous along the reduced
+ * dimension).  For e4m3 the fp32 scales hold one value per 128x128 block:
+ * s_gate, s_up: [G, I/128, d/128]; s_down: [G, d/128, I/128]; the value of an
+ * element is code * scale.  Scales are NULL for fp32 and bf16. */
+typedef struct {
+    const void *gate, *up, *down;
+    const float *s_gate, *s_up, *s_down;
+} moe_ffn_weights_t;
+
+/* Workspace stages for moe_workspace_bytes. */
+enum { MOE_WS_DISPATCH = 0, MOE_WS_FFN = 1, MOE_WS_COMBINE = 2 };
+
+/*
+ * Router, biased top-k choice and combine weights (DeepSeek V3 From Scratch,
+ * "In code": route; "Worked example").
+ *   x        [T, d]  act type
+ *   w_router [E, d]  fp32; logit of expert e = x_t . w_router[e]
+ *   bias     [E]     fp32 balancing bias (read only)
+ *   idx      [T, k]  int32 out: the k experts with the largest
+ *                    fl32(sigmoid(logit)) + bias, ascending id order; equal
+ *                    scores go to the lower id
+ *   weights  [T, k]  fp32 out: sigmoid(logit) of each chosen expert divided by
+ *                    the sum over the k chosen (bias not included)
+ *   gap      [T]     fp32 out or NULL: k-th minus (k+1)-th largest biased
+ *                    score, as the kernel computed it
+ * All scores are computed in fp32 (bf16 x is widened exactly).
+ */
+moe_status_t moe_route(const moe_desc_t *desc, const void *x, const float *w_router,
+                       const float *bias, int32_t *idx, float *weights, float *gap,
+                       void *stream);
+
+/*
+ * Dispatch: per-expert load, its prefix sum and a stable grouping of the T*k
+ * (token, slot) assignments by expert, with the token rows gathered into that
+ * order (crackai.dev DeepSeek-V3 summary, "How It Works": dispatch; Scaling
+ * Efficiency ..., "Implementation: A Modular Look": each expert sees the
+ * tokens that chose it).  Every assignment is kept: no capacity, no drops
+ * (kbwen.com DeepSeek feed, "A bias term for each expert").
+ *   idx          [T, k]   int32 from moe_route (ids in [0, E), distinct per token)
+ *   x            [T, d]   act type
+ *   counts       [E]      int32 out: assignments per expert (the load)
+ *   offsets      [E+1]    int32 out: exclusive prefix sum of counts; offsets[E] = T*k
+ *   row_src      [T*k]    int32 out: flat assignment id t*k + j of permuted row r;
+ *                         within an expert rows are in ascending t*k + j order
+ *   row_of       [T*k]    int32 out: the inverse, permuted row of assignment t*k + j
+ *   x_perm       [T*k, d] out, in the expert GEMM input type: row r = x[row_src[r] / k];
+ *                         for e4m3 the row is quantised per 1x128 tile:
+ *   x_perm_scale [T*k, d/128] fp32 out (e4m3 only, else NULL): scale = amax/448
+ *                         (1 for an all-zero tile), code = e4m3_rne_sat(v / scale)
+ *   workspace    >= moe_workspace_bytes(desc, MOE_WS_DISPATCH) bytes of device memory
+ * Integer outputs are bit-exact and deterministic (no atomics decide order).
+ */
+moe_status_t moe_dispatch(const moe_desc_t *desc, const int32_t *idx, const void *x,
+                          int32_t *counts, int32_t *offsets, int32_t *row_src, int32_t *row_of,
+                          void *x_perm, float *x_perm_scale, void *workspace, size_t ws_bytes,
+                          void *stream);
+
+/*
+ * Routed expert FFNs, grouped: rows [offsets[e], offsets[e+1]) of x_perm go
+ * through expert e (DeepSeek V3 From Scratch, "The idea": fine-grained routed
+ * experts; crackai.dev DeepSeek-V3 summary, "How It Works": FP8 matmuls with
+ * per-tile scales and FP32 accumulation).
+ *   h = silu(x_perm W_gate[e]^T) * (x_perm W_up[e]^T), fp32 accumulation,
+ *       rounded to the wt type (bf16; or e4m3 per 1x128 tile with an fp32
+ *       scale, as in moe_dispatch; or fp32), kept in the workspace;
+ *   y_perm = h W_down[e]^T, fp32 accumulation, stored as fp32 (wt = F32) or
+ *       bf16 (otherwise).
+ *   x_perm, x_perm_scale, offsets: from moe_dispatch; offsets are read on the
+ *       device only (no host synchronisation).
+ *   experts   E routed experts (see moe_ffn_weights_t)
+ *   y_perm    [T*k, d] out
+ *   workspace >= moe_workspace_bytes(desc, MOE_WS_FFN) bytes of device memory
+ */
+moe_status_t moe_expert_ffn(const moe_desc_t *desc, const void *x_perm, const float *x_perm_scale,
+                            const int32_t *offsets, const moe_ffn_weights_t *experts,
+                            void *y_perm, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Shared expert plus weighted combine (Scaling Efficiency ..., "Implementation:
+ * A Modular Look": shared output plus the routed outputs scaled by their
+ * weights; DeepSeek V3 From Scratch, "The idea": one shared expert for every
+ * token).
+ *   y[t] = shared(x[t]) + sum_{j<k} weights[t, j] * y_perm[row_of[t*k + j]]
+ * with the j-sum in ascending expert-id order, in fp32; the shared expert's
+ * fp32 accumulator is not rounded before the sum.  The shared expert has the
+ * SwiGLU form of the routed ones; with wt = e4m3 its input is x quantised per
+ * 1x128 tile (as in moe_dispatch) inside the workspace.
+ *   x        [T, d] act type
+ *   shared   one expert (G = 1)
+ *   y_perm, row_of, weights: from moe_expert_ffn, moe_dispatch, moe_route
+ *   y        [T, d] fp32 out
+ *   workspace >= moe_workspace_bytes(desc, MOE_WS_COMBINE) bytes of device memory
+ */
+moe_status_t moe_combine(const moe_desc_t *desc, const void *x, const moe_ffn_weights_t *shared,
+                         const void *y_perm, const int32_t *row_of, const float *weights,
+                         float *y, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Sign-step bias update, once per step after the forward (DeepSeek V3 From
+ * Scratch, "In code": update_bias; kbwen.com DeepSeek feed, "A bias term for
+ * each expert"):  with load_e = counts[e] / T and target = k / E,
+ *   bias[e] <- fl32(bias[e] + gamma * sign(target - load_e)),
+ * sign(0) = 0.  The sign is evaluated exactly as sign(k*T - E*counts[e]).
+ *   counts [E] int32 (from moe_dispatch); bias [E] fp32, updated in place.
+ */
+moe_status_t moe_bias_update(const moe_desc_t *desc, const int32_t *counts, float gamma,
+                             float *bias, void *stream);
+
+/* Device workspace, in bytes, that a call of the given stage needs for this
+ * shape (0 when the shape is invalid). */
+size_t moe_workspace_bytes(const moe_desc_t *desc, int32_t stage);
+
+/* Static, human-readable name of a status code. */
+const char *moe_status_str(moe_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

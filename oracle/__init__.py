@@ -59,10 +59,11 @@ def lib():
         vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
         sig = {
             "oracle_route": [vp, vp, vp, vp, i64, vp, vp, vp, vp, vp],
+            "oracle_choose": [i64, i32, i32, vp, vp, vp, vp, vp],
             "oracle_dispatch": [i32, i32, i32, vp, vp, vp, vp, vp],
             "oracle_bias_update": [i32, i32, i32, vp, f32, vp],
             "oracle_quant_e4m3_rows": [i64, i32, i32, vp, vp, vp],
-            "oracle_expert_ffn": [vp, vp, vp, vp, vp, vp],
+            "oracle_expert_ffn": [vp, vp, vp, vp, vp, i64, vp, vp],
             "oracle_combine": [vp, vp, vp, vp, vp, vp, i64, vp, vp],
             "oracle_forward": [vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp],
         }
@@ -121,6 +122,18 @@ def route(sh: Shape, x, wr, bias, tokens=None, want_s=False):
     return idx, g, gap, s
 
 
+def choose(s: np.ndarray, bias, k: int):
+    """The choice alone from fp64 affinities s [n, E]: idx [n,k], g [n,k], gap [n]."""
+    n, E = s.shape
+    s = np.ascontiguousarray(s, dtype=np.float64)
+    b = np.ascontiguousarray(bias, dtype=np.float32)
+    idx = np.empty((n, k), np.int32)
+    g = np.empty((n, k), np.float32)
+    gap = np.empty(n, np.float64)
+    lib().oracle_choose(n, E, k, _p(s), _p(b), _p(idx), _p(g), _p(gap))
+    return idx, g, gap
+
+
 def dispatch(idx: np.ndarray, E: int):
     """counts [E], offsets [E+1], row_src [T*k], row_of [T*k] (all int32)."""
     T, k = idx.shape
@@ -151,14 +164,17 @@ def quant_e4m3_rows(v: np.ndarray, in_dtype="bf16"):
     return q, s
 
 
-def expert_ffn(sh: Shape, experts: dict, offsets, a_rows, a_scales=None):
-    """Routed FFN on permuted rows: y_perm [T*k, d] (f32, or bf16 bits as uint16)."""
+def expert_ffn(sh: Shape, experts: dict, offsets, a_rows, a_scales=None, rows=None):
+    """Routed FFN on permuted rows: y_perm [n, d] (f32, or bf16 bits as uint16) for
+    rows 0..T*k-1, or for the listed permuted rows (in list order)."""
     A = sh.T * sh.k
+    n = A if rows is None else len(rows)
+    rl = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
     w, keep = ffn(experts)
-    y = np.empty((A, sh.d), np.float32 if sh.wt == F32 else np.uint16)
+    y = np.empty((n, sh.d), np.float32 if sh.wt == F32 else np.uint16)
     offsets = np.ascontiguousarray(offsets, dtype=np.int32)
     lib().oracle_expert_ffn(ctypes.byref(sh), ctypes.byref(w), _p(offsets), _p(np.ascontiguousarray(a_rows)),
-                            _p(a_scales), _p(y))
+                            _p(a_scales), n, _p(rl), _p(y))
     del keep
     return y
 

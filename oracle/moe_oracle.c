@@ -251,26 +251,19 @@ static double round_yperm(const or_shape *sh, double v) {
 
 /* ------------------------------------------------------------- the router */
 
-/* Route one token.  DeepSeek V3 From Scratch, "In code" (route) and
- * "Worked example": affinity s = sigmoid(x . g_i) for each expert; the k
- * experts with the largest s + b are chosen; their unbiased s, divided by
- * the sum over the chosen k, are the combine weights.  kbwen.com DeepSeek
- * feed, "A bias term for each expert": the bias is used only for the choice.
+/* The choice for one token from its fp64 affinities s[E] (DeepSeek V3 From
+ * Scratch, "In code" (route) and "Worked example"; kbwen.com DeepSeek feed,
+ * "A bias term for each expert"): the k experts with the largest biased score
+ * s + b are chosen; their unbiased s, divided by the sum over the chosen k,
+ * are the combine weights.  The score is formed as the kernel forms it,
+ * fl32(fl32(s) + b), and equal scores go to the lower id.
  *   idx[k]: chosen ids, ascending; wgt[k]: weights in that order;
- *   *gap: (k-th largest) - ((k+1)-th largest) fp64 biased score;
- *   s_out[E] (optional): fp64 affinities. */
-static void route_token(const or_shape *sh, const void *x, const float *wr, const float *bias,
-                        int64_t t, int32_t *idx, double *wgt, double *gap, double *s_out) {
-    const int E = sh->E, k = sh->k, d = sh->d;
-    double *s = (double *)malloc(sizeof(double) * E);
+ *   *gap: (k-th largest) - ((k+1)-th largest) fp64 biased score s + b. */
+static void choose_token(int E, int k, const double *s, const float *bias, int32_t *idx, double *wgt,
+                         double *gap) {
     float *v32 = (float *)malloc(sizeof(float) * E);
     char *taken = (char *)calloc((size_t)(E > 0 ? E : 1), 1);
-    for (int e = 0; e < E; ++e) {
-        double l = 0.0;
-        for (int j = 0; j < d; ++j) l += x_at(sh, x, t, j) * (double)wr[(int64_t)e * d + j];
-        s[e] = 1.0 / (1.0 + exp(-l));
-        v32[e] = (float)s[e] + bias[e]; /* fp32 add: the selection is decided in fp32 */
-    }
+    for (int e = 0; e < E; ++e) v32[e] = (float)s[e] + bias[e]; /* fp32 add */
     /* k rounds of "largest remaining biased score; equal scores -> lower id" */
     for (int r = 0; r < k; ++r) {
         int best = -1;
@@ -285,7 +278,6 @@ static void route_token(const or_shape *sh, const void *x, const float *wr, cons
     for (int j = 0; j < k; ++j) sum += s[idx[j]];
     for (int j = 0; j < k; ++j) wgt[j] = s[idx[j]] / sum;
     if (gap) {
-        /* fp64 biased scores: k-th and (k+1)-th largest */
         double *v = (double *)malloc(sizeof(double) * E);
         for (int e = 0; e < E; ++e) v[e] = s[e] + (double)bias[e];
         double kth = 0.0, k1th = 0.0;
@@ -301,10 +293,39 @@ static void route_token(const or_shape *sh, const void *x, const float *wr, cons
         *gap = (k < E) ? kth - k1th : INFINITY;
         free(v);
     }
-    if (s_out) memcpy(s_out, s, sizeof(double) * E);
-    free(s);
     free(v32);
     free(taken);
+}
+
+/* Affinities of one token: s_e = sigmoid(x_t . w_e) = 1 / (1 + e^-l), fp64
+ * (DeepSeek V3 From Scratch, "In code": route).  No router bias term. */
+static void affinity_token(const or_shape *sh, const void *x, const float *wr, int64_t t, double *s) {
+    const int E = sh->E, d = sh->d;
+    for (int e = 0; e < E; ++e) {
+        double l = 0.0;
+        for (int j = 0; j < d; ++j) l += x_at(sh, x, t, j) * (double)wr[(int64_t)e * d + j];
+        s[e] = 1.0 / (1.0 + exp(-l));
+    }
+}
+
+static void route_token(const or_shape *sh, const void *x, const float *wr, const float *bias,
+                        int64_t t, int32_t *idx, double *wgt, double *gap, double *s_out) {
+    double *s = (double *)malloc(sizeof(double) * sh->E);
+    affinity_token(sh, x, wr, t, s);
+    choose_token(sh->E, sh->k, s, bias, idx, wgt, gap);
+    if (s_out) memcpy(s_out, s, sizeof(double) * sh->E);
+    free(s);
+}
+
+/* The choice alone for ntok tokens whose fp64 affinities are given ([ntok, E]). */
+void oracle_choose(int64_t ntok, int32_t E, int32_t k, const double *s, const float *bias, int32_t *idx,
+                   float *g, double *gap) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < ntok; ++i) {
+        double w[64];
+        choose_token(E, k, s + i * E, bias, idx + i * k, w, gap ? gap + i : NULL);
+        for (int j = 0; j < k; ++j) g[i * k + j] = (float)w[j];
+    }
 }
 
 /* Route a list of tokens (tok == NULL: tokens 0..ntok-1).
@@ -368,12 +389,15 @@ void oracle_bias_update(int32_t E, int32_t k, int32_t T, const int32_t *counts, 
 /* Routed expert FFN on permuted rows (the expert FFN stage on its own):
  * row r in [offsets[e], offsets[e+1]) goes through expert e.
  * a_rows: [A, d] in the GEMM input type (f32, bf16 bits, or e4m3 codes with
- * a_scales [A, d/128]).  y_perm: [A, d] fp32 or bf16 bits (see round_yperm). */
+ * a_scales [A, d/128]).  Rows computed: `rows` (nrows of them) or 0..nrows-1.
+ * y_perm: [nrows, d] fp32 or bf16 bits (see round_yperm), in list order. */
 void oracle_expert_ffn(const or_shape *sh, const or_ffn *w, const int32_t *offsets,
-                       const void *a_rows, const float *a_scales, void *y_perm) {
-    const int64_t d = sh->d, A = (int64_t)sh->T * sh->k;
+                       const void *a_rows, const float *a_scales, int64_t nrows, const int32_t *rows,
+                       void *y_perm) {
+    const int64_t d = sh->d;
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t r = 0; r < A; ++r) {
+    for (int64_t ri = 0; ri < nrows; ++ri) {
+        const int64_t r = rows ? rows[ri] : ri;
         int e = 0;
         while (offsets[e + 1] <= r) ++e;
         double *a = (double *)malloc(sizeof(double) * d);
@@ -388,8 +412,8 @@ void oracle_expert_ffn(const or_shape *sh, const or_ffn *w, const int32_t *offse
         ffn_row(sh, w, e, a, y, h);
         for (int64_t j = 0; j < d; ++j) {
             double v = round_yperm(sh, y[j]);
-            if (sh->wt == OR_F32) ((float *)y_perm)[r * d + j] = (float)v;
-            else ((uint16_t *)y_perm)[r * d + j] = bf16_enc((float)v);
+            if (sh->wt == OR_F32) ((float *)y_perm)[ri * d + j] = (float)v;
+            else ((uint16_t *)y_perm)[ri * d + j] = bf16_enc((float)v);
         }
         free(a);
         free(y);

@@ -1,0 +1,9 @@
+"""MI355X (gfx950) DeepSeekMoE layer forward with auxiliary-loss-free routing.
+
+The layer runs in hand-written HIP kernels behind a C ABI (include/moe.h);
+this package holds those sources (csrc/), the in-tree build (build.py), the
+ctypes binding (_lib.py) and a thin layer object (layer.py).
+"""
+from . import _lib  # noqa: F401
+from ._lib import (MoeError, desc, ffn_weights, moe_bias_update, moe_combine, moe_dispatch,  # noqa: F401
+                   moe_expert_ffn, moe_route, workspace_bytes)

@@ -1,0 +1,86 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE layer:
+// vector types for the MFMA builtins, bf16 and OCP e4m3 conversions, and
+// 64-lane wavefront reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// binary32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// binary32 -> OCP FP8 E4M3FN byte: round to nearest even, saturate to +-448
+// (the format has no infinity; S.1111.111 is NaN).  Normal range: keep the
+// top 3 mantissa bits with RNE on the 20 dropped bits; a mantissa carry moves
+// into the exponent field by plain addition.  Below 2^-6 the codes are the
+// multiples of 2^-9, so the code is rint(|v| * 512).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+    uint32_t u = __float_as_uint(v);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7fffffffu;
+    float af = __uint_as_float(a);
+    if (!(af < 464.0f)) return sign | 0x7eu;
+    if (af < 0.015625f) return sign | (uint32_t)__builtin_rintf(af * 512.0f);
+    uint32_t e = (a >> 23) - 120u;  // biased e4m3 exponent, 1..15
+    uint32_t keep = (a >> 20) & 7u, rem = a & 0xfffffu;
+    keep += (rem > 0x80000u) | ((rem == 0x80000u) & keep);
+    uint32_t code = (e << 3) + keep;
+    return sign | (code > 0x7eu ? 0x7eu : code);
+}
+
+// Totally ordered key of a float (larger float -> larger unsigned key).
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float f32_from_order_key(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) {
+        uint64_t o = __shfl_xor(v, s, kWave);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v, int width) {
+    for (int s = width / 2; s >= 1; s >>= 1) v = fmaxf(v, __shfl_xor(v, s, kWave));
+    return v;
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int s = 1; s < kWave; s <<= 1) {
+        int o = __shfl_up(v, s, kWave);
+        if (lane >= s) v += o;
+    }
+    return v;
+}
+
+}  // namespace moe

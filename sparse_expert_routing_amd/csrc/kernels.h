@@ -1,0 +1,71 @@
+// Internal launch interface between the C ABI (moe_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum Dtype { kF32 = 0, kBF16 = 1, kE4M3 = 2 };
+
+struct RouteArgs {
+    int T, d;
+    bool x_bf16;
+    const void *x;
+    const float *wr, *bias;
+    int32_t *idx;
+    float *w, *gap;
+};
+hipError_t launch_route(const RouteArgs &a, hipStream_t s);
+
+constexpr int kDispatchBlock = 256;  // tokens per dispatch workgroup
+
+struct DispatchArgs {
+    int T, d, E, k;
+    int act, wt;
+    const int32_t *idx;
+    const void *x;
+    int32_t *counts, *offsets, *row_src, *row_of;
+    void *x_perm;
+    float *x_perm_scale;
+    int32_t *block_base;  // workspace [ceil(T/256), E]
+};
+hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s);
+
+// Quantise T rows of bf16 x to e4m3 per 1x128 tile (no permutation).
+hipError_t launch_quant_rows_e4m3(int rows, int d, const uint16_t *x, uint8_t *q, float *scales,
+                                  hipStream_t s);
+
+struct FfnWeights {
+    const void *gate, *up, *down;
+    const float *s_gate, *s_up, *s_down;
+};
+
+// Grouped SwiGLU FFN over permuted rows (routed: offsets != nullptr, E groups)
+// or over plain rows (shared: offsets == nullptr, one group of M rows).
+struct FfnArgs {
+    int M;            // rows (T*k routed, T shared)
+    int d, I, E;      // E groups when offsets != nullptr
+    int wt;           // kF32, kBF16, kE4M3
+    const int32_t *offsets;
+    const void *a;    // [M, d] rows in wt type
+    const float *a_scale;  // e4m3: [M, d/128]
+    FfnWeights w;
+    void *h;          // workspace [M, I] in wt type
+    float *h_scale;   // e4m3: [M, I/128]
+    // output: either y_perm (routed) or the combine (shared)
+    void *y;          // routed: [M, d] f32 / bf16; shared: [M, d] f32
+    // combine epilogue (shared only)
+    bool combine;
+    int k;
+    const void *y_perm;
+    const int32_t *row_of;
+    const float *cw;
+};
+hipError_t launch_ffn(const FfnArgs &a, hipStream_t s);
+
+hipError_t launch_bias_update(int E, int k, int T, const int32_t *counts, float gamma, float *bias,
+                              hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,197 @@
+// C ABI of the MoE layer (declared in include/moe.h): host-side validation,
+// workspace sizing and kernel launches.  Nothing here allocates, frees,
+// synchronises or reads device memory.
+#include "moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace {
+
+using moe::kBF16;
+using moe::kE4M3;
+using moe::kF32;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+size_t elem_bytes(int dt) { return dt == kF32 ? 4 : dt == kBF16 ? 2 : 1; }
+
+// Shape validation shared by every call.
+moe_status_t check_desc(const moe_desc_t *d) {
+    if (d == nullptr) return MOE_EINVAL;
+    if (d->T <= 0 || d->d <= 0 || d->E <= 0 || d->k <= 0 || d->I <= 0) return MOE_EINVAL;
+    if (d->k > d->E) return MOE_EINVAL;
+    const bool pair_ok = (d->act == MOE_F32 && d->wt == MOE_F32) || (d->act == MOE_BF16 && d->wt == MOE_BF16) ||
+                         (d->act == MOE_BF16 && d->wt == MOE_E4M3);
+    if (d->act < 0 || d->act > 2 || d->wt < 0 || d->wt > 2) return MOE_EINVAL;
+    if (d->wt == MOE_E4M3 && (d->d % 128 != 0 || d->I % 128 != 0)) return MOE_EINVAL;
+    if (!pair_ok) return MOE_ENOTSUP;
+    if (d->E != 256 || d->k != 8) return MOE_ENOTSUP;
+    if (d->d % 64 != 0 || d->I % 64 != 0) return MOE_ENOTSUP;
+    if (d->wt == MOE_BF16 && d->d % 128 != 0) return MOE_ENOTSUP;
+    // 32-bit row indices and element offsets within one row block
+    if ((long long)d->T * d->k >= (1LL << 31)) return MOE_ENOTSUP;
+    return MOE_OK;
+}
+
+struct FfnWs {
+    size_t h, h_scale, total;
+};
+FfnWs ffn_ws(int rows, const moe_desc_t *d) {
+    FfnWs w{};
+    w.h = align_up((size_t)rows * d->I * elem_bytes(d->wt));
+    w.h_scale = d->wt == MOE_E4M3 ? align_up((size_t)rows * (d->I / 128) * sizeof(float)) : 0;
+    w.total = w.h + w.h_scale;
+    return w;
+}
+
+size_t dispatch_ws(const moe_desc_t *d) {
+    const size_t nblk = (d->T + moe::kDispatchBlock - 1) / moe::kDispatchBlock;
+    return align_up(nblk * d->E * sizeof(int32_t));
+}
+
+size_t combine_ws(const moe_desc_t *d) {
+    size_t t = ffn_ws(d->T, d).total;
+    if (d->wt == MOE_E4M3) t += align_up((size_t)d->T * d->d) + align_up((size_t)d->T * (d->d / 128) * sizeof(float));
+    return t;
+}
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+bool ffn_weights_ok(const moe_ffn_weights_t *w, int wt) {
+    if (w == nullptr || w->gate == nullptr || w->up == nullptr || w->down == nullptr) return false;
+    if (wt == MOE_E4M3 && (w->s_gate == nullptr || w->s_up == nullptr || w->s_down == nullptr)) return false;
+    return true;
+}
+
+moe::FfnWeights to_internal(const moe_ffn_weights_t *w) {
+    return moe::FfnWeights{w->gate, w->up, w->down, w->s_gate, w->s_up, w->s_down};
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_str(moe_status_t s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+        case MOE_ENOTSUP: return "MOE_ENOTSUP: shape or dtype not supported by this build";
+        case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace smaller than moe_workspace_bytes()";
+        case MOE_EHIP: return "MOE_EHIP: HIP launch error";
+    }
+    return "unknown moe_status_t";
+}
+
+size_t moe_workspace_bytes(const moe_desc_t *d, int32_t stage) {
+    if (check_desc(d) != MOE_OK) return 0;
+    switch (stage) {
+        case MOE_WS_DISPATCH: return dispatch_ws(d);
+        case MOE_WS_FFN: return ffn_ws(d->T * d->k, d).total;
+        case MOE_WS_COMBINE: return combine_ws(d);
+    }
+    return 0;
+}
+
+moe_status_t moe_route(const moe_desc_t *d, const void *x, const float *w_router, const float *bias,
+                       int32_t *idx, float *weights, float *gap, void *stream) {
+    moe_status_t st = check_desc(d);
+    if (st != MOE_OK) return st;
+    if (!x || !w_router || !bias || !idx || !weights) return MOE_EINVAL;
+    moe::RouteArgs a{d->T, d->d, d->act == MOE_BF16, x, w_router, bias, idx, weights, gap};
+    return hip_status(moe::launch_route(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_dispatch(const moe_desc_t *d, const int32_t *idx, const void *x, int32_t *counts,
+                          int32_t *offsets, int32_t *row_src, int32_t *row_of, void *x_perm,
+                          float *x_perm_scale, void *workspace, size_t ws_bytes, void *stream) {
+    moe_status_t st = check_desc(d);
+    if (st != MOE_OK) return st;
+    if (!idx || !x || !counts || !offsets || !row_src || !row_of || !x_perm) return MOE_EINVAL;
+    if (d->wt == MOE_E4M3 && !x_perm_scale) return MOE_EINVAL;
+    if (!workspace || ws_bytes < dispatch_ws(d)) return MOE_EWORKSPACE;
+    moe::DispatchArgs a{d->T, d->d, d->E, d->k, d->act, d->wt, idx, x, counts, offsets, row_src, row_of,
+                        x_perm, x_perm_scale, static_cast<int32_t *>(workspace)};
+    return hip_status(moe::launch_dispatch(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_expert_ffn(const moe_desc_t *d, const void *x_perm, const float *x_perm_scale,
+                            const int32_t *offsets, const moe_ffn_weights_t *experts, void *y_perm,
+                            void *workspace, size_t ws_bytes, void *stream) {
+    moe_status_t st = check_desc(d);
+    if (st != MOE_OK) return st;
+    if (!x_perm || !offsets || !y_perm || !ffn_weights_ok(experts, d->wt)) return MOE_EINVAL;
+    if (d->wt == MOE_E4M3 && !x_perm_scale) return MOE_EINVAL;
+    const FfnWs w = ffn_ws(d->T * d->k, d);
+    if (!workspace || ws_bytes < w.total) return MOE_EWORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    moe::FfnArgs a{};
+    a.M = d->T * d->k;
+    a.d = d->d;
+    a.I = d->I;
+    a.E = d->E;
+    a.wt = d->wt;
+    a.offsets = offsets;
+    a.a = x_perm;
+    a.a_scale = x_perm_scale;
+    a.w = to_internal(experts);
+    a.h = ws;
+    a.h_scale = w.h_scale ? reinterpret_cast<float *>(ws + w.h) : nullptr;
+    a.y = y_perm;
+    a.combine = false;
+    a.k = d->k;
+    return hip_status(moe::launch_ffn(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_combine(const moe_desc_t *d, const void *x, const moe_ffn_weights_t *shared,
+                         const void *y_perm, const int32_t *row_of, const float *weights, float *y,
+                         void *workspace, size_t ws_bytes, void *stream) {
+    moe_status_t st = check_desc(d);
+    if (st != MOE_OK) return st;
+    if (!x || !y_perm || !row_of || !weights || !y || !ffn_weights_ok(shared, d->wt)) return MOE_EINVAL;
+    if (!workspace || ws_bytes < combine_ws(d)) return MOE_EWORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    const FfnWs w = ffn_ws(d->T, d);
+    moe::FfnArgs a{};
+    a.M = d->T;
+    a.d = d->d;
+    a.I = d->I;
+    a.E = 1;
+    a.wt = d->wt;
+    a.offsets = nullptr;
+    a.a = x;
+    a.a_scale = nullptr;
+    if (d->wt == MOE_E4M3) {
+        char *xq = ws + w.total;
+        float *xs = reinterpret_cast<float *>(xq + align_up((size_t)d->T * d->d));
+        hipError_t e = moe::launch_quant_rows_e4m3(d->T, d->d, static_cast<const uint16_t *>(x),
+                                                   reinterpret_cast<uint8_t *>(xq), xs, s);
+        if (e != hipSuccess) return MOE_EHIP;
+        a.a = xq;
+        a.a_scale = xs;
+    }
+    a.w = to_internal(shared);
+    a.h = ws;
+    a.h_scale = w.h_scale ? reinterpret_cast<float *>(ws + w.h) : nullptr;
+    a.y = y;
+    a.combine = true;
+    a.k = d->k;
+    a.y_perm = y_perm;
+    a.row_of = row_of;
+    a.cw = weights;
+    return hip_status(moe::launch_ffn(a, s));
+}
+
+moe_status_t moe_bias_update(const moe_desc_t *d, const int32_t *counts, float gamma, float *bias,
+                             void *stream) {
+    moe_status_t st = check_desc(d);
+    if (st != MOE_OK) return st;
+    if (!counts || !bias) return MOE_EINVAL;
+    return hip_status(moe::launch_bias_update(d->E, d->k, d->T, counts, gamma, bias,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

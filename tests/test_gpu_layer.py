@@ -1,0 +1,105 @@
+"""GPU parity of the whole layer (route -> dispatch -> expert FFN -> combine ->
+bias update) against the oracle's independent forward on the same seeded
+inputs, per workload.
+
+Tokens whose routing differs between the two sides must all be near-ties
+(oracle fp64 gap < 1e-6); outputs are compared on the other tokens.  The
+dispatch arrays and the bias step are compared bit-exactly when no token
+flipped (when one did, the invariants are checked instead).  At the large
+workloads the oracle computes sampled tokens one by one (the forward is
+independent per token given the bias)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from sparse_expert_routing_amd import _lib
+from sparse_expert_routing_amd.layer import layer_from_inputs, upload
+from tests.gpu_util import NEAR_TIE, TOL, host, max_rel, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _lib.load()
+
+
+def sample_tokens(T, n, seed=0):
+    if n >= T:
+        return np.arange(T, dtype=np.int32)
+    rng = np.random.default_rng(seed)
+    s = np.unique(np.concatenate([[0, T - 1], rng.choice(T, n - 2, replace=False)]))
+    return s.astype(np.int32)
+
+
+def check_layer(cfg, inp, n_sample, route_all=True):
+    say(f"[layer] {cfg.name}: upload + forward")
+    layer = layer_from_inputs(inp)
+    x = upload(inp["x"])
+    b = upload(inp["bias"])
+    y = layer.forward(x, b, gap=True)
+    layer.update_bias(b, cfg.gamma)
+    torch.cuda.synchronize()
+    gi, gw, gy = host(layer.idx), host(layer.w), host(y)
+    counts, offsets, row_src, row_of = (host(t) for t in (layer.counts, layer.offsets, layer.row_src, layer.row_of))
+    gb = host(b)
+    sh = oracle.shape_of(cfg)
+
+    toks = sample_tokens(cfg.T, n_sample)
+    say(f"[layer] {cfg.name}: oracle forward on {len(toks)} tokens")
+    oi, og, ogap, oy = oracle.forward(sh, inp["x"], inp["wr"], inp["bias"], inp["experts"], inp["shared"], toks)
+    near = ogap < NEAR_TIE
+    mism = np.any(gi[toks] != oi, axis=1)
+    assert not np.any(mism & ~near), f"routing differs on non-near-tie tokens {toks[mism & ~near][:10]}"
+    ok = ~mism
+    err_y = max_rel(gy[toks][ok], oy[ok])
+    err_w = max_rel(gw[toks][ok], og[ok])
+    say(f"[layer] {cfg.name}: y max rel err {err_y:.3e}, weights {err_w:.3e}, sampled near-ties "
+        f"{int(near.sum())}, flipped {int(mism.sum())}")
+    assert err_y <= TOL[cfg.wt], err_y
+    assert err_w <= TOL["f32"], err_w
+
+    # invariants of the dispatch (no token dropped, a stable permutation)
+    assert counts.sum() == cfg.T * cfg.k and offsets[-1] == cfg.T * cfg.k
+    assert np.array_equal(row_of[row_src], np.arange(cfg.T * cfg.k))
+    assert np.array_equal(np.bincount(gi.ravel(), minlength=256), counts)
+
+    if route_all:
+        ri, _, rgap, _ = oracle.route(sh, inp["x"], inp["wr"], inp["bias"])
+        flip = np.any(gi != ri, axis=1)
+        assert not np.any(flip & (rgap >= NEAR_TIE))
+        say(f"[layer] {cfg.name}: all tokens: near-ties {int((rgap < NEAR_TIE).sum())}, flipped {int(flip.sum())}")
+        if not flip.any():
+            oc, oo, osrc, oof = oracle.dispatch(ri, 256)
+            assert np.array_equal(counts, oc) and np.array_equal(offsets, oo)
+            assert np.array_equal(row_src, osrc) and np.array_equal(row_of, oof)
+            assert np.array_equal(gb, oracle.bias_update(inp["bias"], oc, cfg.k, cfg.T, cfg.gamma))
+    return gi, gy
+
+
+def test_layer_config1_tiny_fp32_one_step():
+    cfg = synth.CONFIGS[1]
+    inp = synth.make_inputs(cfg)
+    check_layer(cfg, inp, n_sample=cfg.T)
+
+
+def test_layer_config2_mid_bf16():
+    cfg = synth.CONFIGS[2]
+    inp = synth.make_inputs(cfg)
+    check_layer(cfg, inp, n_sample=96)
+
+
+def test_layer_config2_ragged_T():
+    cfg = synth.CONFIGS[2].with_(T=777)
+    inp = synth.make_inputs(cfg)
+    check_layer(cfg, inp, n_sample=48)
+
+
+def test_layer_config3_decode_bf16():
+    cfg = synth.CONFIGS[3]
+    inp = synth.make_inputs(cfg)
+    check_layer(cfg, inp, n_sample=24)

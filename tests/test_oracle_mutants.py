@@ -13,6 +13,8 @@ SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
 # (name, text in moe_oracle.c, replacement)
 MUTANTS = [
     ("sigmoid sign", "s[e] = 1.0 / (1.0 + exp(-l));", "s[e] = 1.0 / (1.0 + exp(l));"),
+    ("router row/column swapped", "l += x_at(sh, x, t, j) * (double)wr[(int64_t)e * d + j];",
+     "l += x_at(sh, x, t, j) * (double)wr[(int64_t)j * E + e % d];"),
     ("bias ignored in choice", "v32[e] = (float)s[e] + bias[e];", "v32[e] = (float)s[e];"),
     ("weights from biased score", "for (int j = 0; j < k; ++j) wgt[j] = s[idx[j]] / sum;",
      "for (int j = 0; j < k; ++j) wgt[j] = (s[idx[j]] + bias[idx[j]]) / sum;"),
