@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""MoE-layer throughput on one MI355X.
+
+Workload (default): the skewed prefill layer -- T=16384 tokens, d_model=7168,
+256 routed experts + 1 shared expert, top-8, SwiGLU width 2048, bf16
+activations and weights with fp32 accumulation, fp32 router whose rows carry
+a Zipf(1.1) factor, bias starting at 0 -- run as its balancing loop: each
+step is one pass of the whole path (route, dispatch, routed expert FFN,
+shared expert + combine, sign-step bias update) over the same batch, and the
+bias carries from step to step.  Inputs are seeded synthetic data, resident
+in HBM before the timed region starts.
+
+Prints ONE JSON line on stdout (progress goes to stderr).
+  value          tokens/s over the timed steps (T * steps / wall time)
+  roofline       the dominant kernel (the routed gate/up grouped GEMM):
+                 algorithmic FLOPs per launch (2 * T*k * d * 2I) over its
+                 average duration from HIP events on the launch stream,
+                 against the dense bf16 MFMA peak
+  cpu_baseline   the CPU oracle (fp64, plain loops) timed on a sample of the
+                 same workload's tokens through the whole forward
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # dense bf16 MFMA, MI355X
+PEAK_FP8_TFLOPS = 5033.2    # dense fp8 MFMA, MI355X
+PEAK_HBM_GBS = 8000.0
+METRIC = "MoE-layer tokens/s (T=16384,d=7168,256e top-8) + % of MFMA/HBM peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100, help="timed steps of the balancing loop")
+    ap.add_argument("--warmup", type=int, default=5, help="untimed steps (on a scratch copy of the bias)")
+    ap.add_argument("--config", type=int, default=4, choices=[2, 3, 4, 5],
+                    help="workload (4: the skewed prefill layer the metric is quoted on)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures the layer on one GPU only (asked for {max(args.gpus, world)}); "
+              "multi-GPU runs are not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from sparse_expert_routing_amd import _lib
+    from sparse_expert_routing_amd.layer import layer_from_inputs, upload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    _lib.load()  # fails loudly without the HIP library
+    cfg = synth.CONFIGS[args.config]
+    T, d, I, E, k = cfg.T, cfg.d, cfg.I, cfg.E, cfg.k
+    A = T * k
+
+    t0 = time.time()
+    log(f"[bench] generating inputs for {cfg.name} (seed {cfg.seed})")
+    inp = synth.make_inputs(cfg)
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s; uploading")
+    layer = layer_from_inputs(inp)
+    x = upload(inp["x"])
+    bias0 = upload(inp["bias"])
+    D = layer.desc
+    stream = torch.cuda.current_stream()
+
+    def step(bias, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        _lib.moe_route(D, x, layer.wr, bias, layer.idx, layer.w, None, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        _lib.moe_dispatch(D, layer.idx, x, layer.counts, layer.offsets, layer.row_src, layer.row_of,
+                          layer.x_perm, layer.x_perm_scale, layer.ws, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        _lib.moe_expert_gate_up(D, layer.x_perm, layer.x_perm_scale, layer.offsets, layer.ex_w, layer.ws, stream)
+        if ev is not None:
+            ev[3].record(stream)
+        _lib.moe_expert_down(D, layer.offsets, layer.ex_w, layer.y_perm, layer.ws, stream)
+        if ev is not None:
+            ev[4].record(stream)
+        _lib.moe_combine(D, x, layer.sh_w, layer.y_perm, layer.row_of, layer.w, layer.y, layer.ws, stream)
+        if ev is not None:
+            ev[5].record(stream)
+        _lib.moe_bias_update(D, layer.counts, cfg.gamma, bias, stream)
+        if ev is not None:
+            ev[6].record(stream)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    scratch_bias = bias0.clone()
+    for _ in range(args.warmup):
+        step(scratch_bias)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    bias = bias0.clone()
+    counts_hist = torch.empty((K, E), dtype=torch.int32, device="cuda")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
+    log(f"[bench] timing {K} steps")
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(K):
+        step(bias, events[s])
+        counts_hist[s].copy_(layer.counts, non_blocking=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    names = ["route", "dispatch", "expert_gate_up", "expert_down", "combine", "bias_update"]
+    phase = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(K)]))
+             for i, n in enumerate(names)}
+    ch = counts_hist.cpu().numpy().astype(np.float64)
+    imb = ch.max(axis=1) / ch.mean(axis=1)
+
+    gate_up_flops = 2.0 * A * d * (2 * I)
+    gate_up_ms = phase["expert_gate_up"]
+    achieved = gate_up_flops / (gate_up_ms * 1e-3) / 1e12
+    peak = PEAK_FP8_TFLOPS if cfg.wt == "e4m3" else PEAK_BF16_TFLOPS
+    total_flops = 2.0 * T * d * E + 6.0 * (A + T) * d * I
+    ms_step = wall / K * 1e3
+    log(f"[bench] {ms_step:.3f} ms/step, phases (ms): " + ", ".join(f"{n} {v:.3f}" for n, v in phase.items()))
+    log(f"[bench] gate/up GEMM {achieved:.1f} TFLOP/s ({100 * achieved / peak:.1f}% of peak); "
+        f"layer {total_flops / (ms_step * 1e-3) / 1e12:.1f} TFLOP/s; max/mean load {imb[0]:.2f} -> {imb[-1]:.2f}")
+
+    out = {
+        "metric": METRIC,
+        "value": T * K / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "e4m3": "e4m3"}[cfg.wt],
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": T, "d_model": d, "experts": E, "top_k": k, "shared_experts": 1,
+                   "expert_intermediate": I, "router": "fp32 sigmoid", "router_row_skew": cfg.skew,
+                   "bias_start": cfg.bias, "gamma": cfg.gamma, "loop_steps_timed": K, "seed": cfg.seed},
+        "roofline": {"kernel": "routed gate/up grouped GEMM (k_gemm_bf16 SwiGLU)" if cfg.wt != "e4m3"
+                     else "routed gate/up grouped GEMM (k_gemm_fp8 SwiGLU+quant)",
+                     "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None,
+                     "flops_per_launch": gate_up_flops, "avg_launch_ms": gate_up_ms},
+        "phases_ms": phase,
+        "layer_tflops": total_flops / (ms_step * 1e-3) / 1e12,
+        "imbalance_max_over_mean": {"first": float(imb[0]), "last": float(imb[-1])},
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, inp, target_s):
+    """The oracle (plain fp64 loops, OpenMP over tokens), as it stands, on a
+    sample of the workload's tokens through the whole forward."""
+    import numpy as np
+
+    import oracle
+
+    sh = oracle.shape_of(cfg)
+
+    def run(n):
+        toks = (np.arange(n, dtype=np.int64) * (cfg.T // n)).astype(np.int32)
+        t = time.perf_counter()
+        oracle.forward(sh, inp["x"], inp["wr"], inp["bias"], inp["experts"], inp["shared"], toks)
+        return time.perf_counter() - t
+
+    cores = oracle.num_threads()
+    n0 = max(cores, 8)
+    t0 = run(n0)
+    n = int(min(cfg.T, max(n0, round(n0 * target_s / max(t0, 1e-3)))))
+    n = max(cores, (n // cores) * cores)
+    log(f"[bench] oracle: {n0} tokens in {t0:.2f}s; timing {n} tokens on {cores} threads")
+    t = run(n)
+    return {"value": n / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of the {cfg.T} tokens (every {cfg.T // n}th) through route + 8 routed experts + "
+                      f"shared expert + combine in fp64; {t:.1f}s"}
+
+
+if __name__ == "__main__":
+    main()

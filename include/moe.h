@@ -21,7 +21,7 @@
  *     chose it scaled by their weight.
  *   - crackai.dev DeepSeek-V3 summary, "How It Works": the routed work is
  *     split into a dispatch and a combine around the expert computation; FP8
- *     expert matmuls with per-tile scaling and FP32 accumulation.
+ *     expert matmuls with a scale per tile and FP32 accumulation.
  * Our readings where the pages are silent: each expert is a bias-free SwiGLU
  * FFN y = W_down (silu(W_gate a) * (W_up a)); equal biased scores go to the
  * lower expert id; the k chosen ids are reported in ascending order.
@@ -154,6 +154,20 @@ moe_status_t moe_dispatch(const moe_desc_t *desc, const int32_t *idx, const void
 moe_status_t moe_expert_ffn(const moe_desc_t *desc, const void *x_perm, const float *x_perm_scale,
                             const int32_t *offsets, const moe_ffn_weights_t *experts,
                             void *y_perm, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * The two halves of moe_expert_ffn, for callers that schedule or time them
+ * separately.  moe_expert_gate_up computes h (kept in `workspace`);
+ * moe_expert_down reads h from the same workspace and writes y_perm.  Called
+ * in that order on one stream with one workspace they are exactly
+ * moe_expert_ffn.  Arguments as for moe_expert_ffn.
+ */
+moe_status_t moe_expert_gate_up(const moe_desc_t *desc, const void *x_perm, const float *x_perm_scale,
+                                const int32_t *offsets, const moe_ffn_weights_t *experts,
+                                void *workspace, size_t ws_bytes, void *stream);
+moe_status_t moe_expert_down(const moe_desc_t *desc, const int32_t *offsets,
+                             const moe_ffn_weights_t *experts, void *y_perm, void *workspace,
+                             size_t ws_bytes, void *stream);
 
 /*
  * Shared expert plus weighted combine (Scaling Efficiency ..., "Implementation:

@@ -19,7 +19,7 @@
  *     sum; each routed expert applied to the tokens that chose it and its
  *     output accumulated with that token's weight.
  *   - crackai.dev DeepSeek-V3 summary, "How It Works": 256 routed + 1 shared
- *     expert, top-8; FP8 with per-tile scaling and FP32 accumulation.
+ *     expert, top-8; FP8 matmuls with a scale per tile and FP32 accumulation.
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *   - expert FFN is a bias-free SwiGLU: y = Wd (silu(Wg a) * (Wu a));
@@ -137,7 +137,7 @@ uint8_t oracle_e4m3_encode(float f) { return e4m3_enc(f); }
 
 /* One 1x128 tile: scale = amax / 448 (fp32), codes of v / scale (fp32 division).
  * Fine-grained fp8 tiles: crackai.dev DeepSeek-V3 summary, "How It Works"
- * (per-tile scaling, FP32 accumulation); DeepSeek V3 From Scratch, "The idea". */
+ * (a scale per tile, FP32 accumulation); DeepSeek V3 From Scratch, "The idea". */
 static float quant_tile(const float *v, int n, uint8_t *q) {
     float amax = 0.0f;
     for (int i = 0; i < n; ++i) {

@@ -7,7 +7,7 @@
 // Efficiency: A Deep Dive into the DeepSeek-V3 Architecture, "Implementation:
 // A Modular Look" (each expert runs on the tokens that chose it, in token
 // order).  No capacity and no drops: kbwen.com DeepSeek feed, "A bias term for
-// each expert".  FP8 per-tile scaling: crackai.dev DeepSeek-V3 summary, "How
+// each expert".  FP8 with a scale per tile: crackai.dev DeepSeek-V3 summary, "How
 // It Works".
 //
 // Determinism: no atomic return value ever decides a position.  Within a

@@ -289,13 +289,15 @@ hipError_t launch_ffn(const FfnArgs &a, hipStream_t s) {
     const bool routed = a.offsets != nullptr;
     if (a.wt == kF32) {
         dim3 g1((a.M + 3) / 4, (a.I + 63) / 64), g2((a.M + 3) / 4, (a.d + 63) / 64);
-        hipLaunchKernelGGL(k_f32_gateup, g1, dim3(256), 0, s, a.M, a.d, a.I, a.offsets,
-                           static_cast<const float *>(a.a), static_cast<const float *>(a.w.gate),
-                           static_cast<const float *>(a.w.up), static_cast<float *>(a.h));
-        hipLaunchKernelGGL(k_f32_down, g2, dim3(256), 0, s, a.M, a.d, a.I, a.offsets,
-                           static_cast<const float *>(a.h), static_cast<const float *>(a.w.down),
-                           static_cast<float *>(a.y), a.k, a.combine ? static_cast<const float *>(a.y_perm) : nullptr,
-                           a.row_of, a.cw);
+        if (a.phases & 1)
+            hipLaunchKernelGGL(k_f32_gateup, g1, dim3(256), 0, s, a.M, a.d, a.I, a.offsets,
+                               static_cast<const float *>(a.a), static_cast<const float *>(a.w.gate),
+                               static_cast<const float *>(a.w.up), static_cast<float *>(a.h));
+        if (a.phases & 2)
+            hipLaunchKernelGGL(k_f32_down, g2, dim3(256), 0, s, a.M, a.d, a.I, a.offsets,
+                               static_cast<const float *>(a.h), static_cast<const float *>(a.w.down),
+                               static_cast<float *>(a.y), a.k,
+                               a.combine ? static_cast<const float *>(a.y_perm) : nullptr, a.row_of, a.cw);
         return hipGetLastError();
     }
     if (a.wt == kBF16) {
@@ -309,7 +311,8 @@ hipError_t launch_ffn(const FfnArgs &a, hipStream_t s) {
         p.B1 = static_cast<const uint16_t *>(a.w.up);
         p.N = a.I;
         p.out = static_cast<uint16_t *>(a.h);
-        hipLaunchKernelGGL(k_gemm_bf16<EPI_SWIGLU>, dim3(slots, a.I / (BNB / 2)), dim3(256), 0, s, p);
+        if (a.phases & 1) hipLaunchKernelGGL(k_gemm_bf16<EPI_SWIGLU>, dim3(slots, a.I / (BNB / 2)), dim3(256), 0, s, p);
+        if (!(a.phases & 2)) return hipGetLastError();
         GemmParams q{};
         q.M = a.M;
         q.offsets = a.offsets;
@@ -330,7 +333,7 @@ hipError_t launch_ffn(const FfnArgs &a, hipStream_t s) {
         }
         return hipGetLastError();
     }
-    return hipErrorNotSupported;  // e4m3 handled in ffn_fp8.hip
+    return launch_ffn_fp8(a, s);
 }
 
 }  // namespace moe

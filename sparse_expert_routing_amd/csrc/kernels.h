@@ -56,6 +56,8 @@ struct FfnArgs {
     float *h_scale;   // e4m3: [M, I/128]
     // output: either y_perm (routed) or the combine (shared)
     void *y;          // routed: [M, d] f32 / bf16; shared: [M, d] f32
+    // which GEMMs to run: 1 = gate/up only, 2 = down only, 3 = both
+    int phases;
     // combine epilogue (shared only)
     bool combine;
     int k;
@@ -64,6 +66,7 @@ struct FfnArgs {
     const float *cw;
 };
 hipError_t launch_ffn(const FfnArgs &a, hipStream_t s);
+hipError_t launch_ffn_fp8(const FfnArgs &a, hipStream_t s);
 
 hipError_t launch_bias_update(int E, int k, int T, const int32_t *counts, float gamma, float *bias,
                               hipStream_t s);

@@ -117,13 +117,14 @@ moe_status_t moe_dispatch(const moe_desc_t *d, const int32_t *idx, const void *x
     return hip_status(moe::launch_dispatch(a, static_cast<hipStream_t>(stream)));
 }
 
-moe_status_t moe_expert_ffn(const moe_desc_t *d, const void *x_perm, const float *x_perm_scale,
-                            const int32_t *offsets, const moe_ffn_weights_t *experts, void *y_perm,
-                            void *workspace, size_t ws_bytes, void *stream) {
+static moe_status_t expert_ffn_phases(const moe_desc_t *d, const void *x_perm, const float *x_perm_scale,
+                                      const int32_t *offsets, const moe_ffn_weights_t *experts, void *y_perm,
+                                      void *workspace, size_t ws_bytes, void *stream, int phases) {
     moe_status_t st = check_desc(d);
     if (st != MOE_OK) return st;
-    if (!x_perm || !offsets || !y_perm || !ffn_weights_ok(experts, d->wt)) return MOE_EINVAL;
-    if (d->wt == MOE_E4M3 && !x_perm_scale) return MOE_EINVAL;
+    if (!offsets || !ffn_weights_ok(experts, d->wt)) return MOE_EINVAL;
+    if ((phases & 1) && (!x_perm || (d->wt == MOE_E4M3 && !x_perm_scale))) return MOE_EINVAL;
+    if ((phases & 2) && !y_perm) return MOE_EINVAL;
     const FfnWs w = ffn_ws(d->T * d->k, d);
     if (!workspace || ws_bytes < w.total) return MOE_EWORKSPACE;
     char *ws = static_cast<char *>(workspace);
@@ -140,9 +141,27 @@ moe_status_t moe_expert_ffn(const moe_desc_t *d, const void *x_perm, const float
     a.h = ws;
     a.h_scale = w.h_scale ? reinterpret_cast<float *>(ws + w.h) : nullptr;
     a.y = y_perm;
+    a.phases = phases;
     a.combine = false;
     a.k = d->k;
     return hip_status(moe::launch_ffn(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_expert_ffn(const moe_desc_t *d, const void *x_perm, const float *x_perm_scale,
+                            const int32_t *offsets, const moe_ffn_weights_t *experts, void *y_perm,
+                            void *workspace, size_t ws_bytes, void *stream) {
+    return expert_ffn_phases(d, x_perm, x_perm_scale, offsets, experts, y_perm, workspace, ws_bytes, stream, 3);
+}
+
+moe_status_t moe_expert_gate_up(const moe_desc_t *d, const void *x_perm, const float *x_perm_scale,
+                                const int32_t *offsets, const moe_ffn_weights_t *experts, void *workspace,
+                                size_t ws_bytes, void *stream) {
+    return expert_ffn_phases(d, x_perm, x_perm_scale, offsets, experts, nullptr, workspace, ws_bytes, stream, 1);
+}
+
+moe_status_t moe_expert_down(const moe_desc_t *d, const int32_t *offsets, const moe_ffn_weights_t *experts,
+                             void *y_perm, void *workspace, size_t ws_bytes, void *stream) {
+    return expert_ffn_phases(d, nullptr, nullptr, offsets, experts, y_perm, workspace, ws_bytes, stream, 2);
 }
 
 moe_status_t moe_combine(const moe_desc_t *d, const void *x, const moe_ffn_weights_t *shared,
@@ -177,6 +196,7 @@ moe_status_t moe_combine(const moe_desc_t *d, const void *x, const moe_ffn_weigh
     a.h = ws;
     a.h_scale = w.h_scale ? reinterpret_cast<float *>(ws + w.h) : nullptr;
     a.y = y;
+    a.phases = 3;
     a.combine = true;
     a.k = d->k;
     a.y_perm = y_perm;

@@ -103,3 +103,19 @@ def test_layer_config3_decode_bf16():
     cfg = synth.CONFIGS[3]
     inp = synth.make_inputs(cfg)
     check_layer(cfg, inp, n_sample=24)
+
+
+def test_layer_config5_fp8_reduced():
+    """The fp8 workload's recipe at a size the oracle finishes in seconds:
+    T=600 (ragged), d=1024, I=256."""
+    cfg = synth.CONFIGS[5].with_(T=600, d=1024, I=256)
+    inp = synth.make_inputs(cfg)
+    check_layer(cfg, inp, n_sample=64)
+
+
+def test_layer_config4_skewed_reduced():
+    """The skewed workload's recipe (Zipf router rows, zero initial bias) at
+    T=2048, d=1024, I=256: a few experts take most tokens (multi-tile groups)."""
+    cfg = synth.CONFIGS[4].with_(T=2048, d=1024, I=256)
+    inp = synth.make_inputs(cfg)
+    check_layer(cfg, inp, n_sample=64)

@@ -163,7 +163,7 @@ def yvals(y, wt):
     return y.astype(np.float64) if wt == "f32" else bf16v(y).astype(np.float64)
 
 
-@pytest.mark.parametrize("wt", ["f32", "bf16"])
+@pytest.mark.parametrize("wt", ["f32", "bf16", "e4m3"])
 @pytest.mark.parametrize("kind,T", [("random", 40), ("same8", 300), ("skewed", 257)])
 def test_expert_ffn_small(wt, kind, T):
     act = "f32" if wt == "f32" else "bf16"
@@ -199,7 +199,7 @@ def test_expert_ffn_config2_sampled_rows():
 
 # ---------------------------------------------------------------- combine
 
-@pytest.mark.parametrize("wt,T", [("f32", 32), ("bf16", 100), ("bf16", 257)])
+@pytest.mark.parametrize("wt,T", [("f32", 32), ("bf16", 100), ("bf16", 257), ("e4m3", 100), ("e4m3", 257)])
 def test_combine(wt, T):
     act = "f32" if wt == "f32" else "bf16"
     cfg = synth.Config("comb", seed=31, T=T, d=256, I=128, act=act, wt=wt)
@@ -209,6 +209,8 @@ def test_combine(wt, T):
     idx = ids_case("random", T)
     _, _, _, row_of = oracle.dispatch(idx, 256)
     y_perm = synth.normal(cfg.seed, synth.TID_AUX, (cfg.A, cfg.d), 0.1, "f32" if wt == "f32" else "bf16")
+    if wt == "e4m3":
+        x[5] = 0  # an all-zero row: the shared expert's input tile scale is 1
     g = synth.uniform(cfg.seed, synth.TID_AUX + 1, cfg.A, 0.01, 1.0).reshape(T, 8)
     g = (g / g.sum(axis=1, keepdims=True)).astype(np.float32)
     ds = _lib.desc(T, cfg.d, 256, 8, cfg.I, act, wt)
