@@ -1,0 +1,458 @@
+// Grouped SwiGLU expert GEMMs in bf16 for large groups (prefill): persistent
+// workgroups, 256x256 tiles, XCD-aware grouped tile order, LDS-staged
+// vectorised epilogues.
+//
+// Routed experts and their gather/accumulate: Scaling Efficiency: A Deep Dive
+// into the DeepSeek-V3 Architecture, "Implementation: A Modular Look"; many
+// small routed experts plus one shared expert: DeepSeek V3 From Scratch,
+// "The idea".  Gated (SwiGLU) form: our reading (see the C ABI header).
+//
+// Design for gfx950:
+//   - 4 waves in a 2x2 layout, each owning a 128x128 block of the 256x256
+//     tile as 4x4 v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane, in
+//     AGPRs): per 16 of K a wave reads 8 fragments (8 KB) from LDS for 16
+//     MFMAs, half the LDS traffic per MFMA of a 64x64 wave tile;
+//   - K stages of 64 (each tile row a whole 128-byte line: reading half lines
+//     halves the L2 bandwidth), two 64 KB LDS slots filled straight from
+//     global memory by global_load_lds_dwordx4 (no VGPR staging).  A stage
+//     is 4 steps of 16 K; its fragments are all in registers after step 2,
+//     so a mid-stage barrier (after this wave's loads of the next stage have
+//     landed, s_waitcnt vmcnt) hands its slot to the stage after next: every
+//     stage has 4 steps (~2k cycles) to arrive, with one barrier per stage;
+//   - fragments are double-buffered in registers: the next 16-wide K step's
+//     8 fragments (the next stage's first step included) are read from LDS
+//     while the current step's 16 MFMAs run, pinned by scheduling barriers;
+//   - LDS layout: 128-byte rows whose 16-byte pieces are XOR-swizzled with
+//     (row & 7) ^ ((row >> 3) & 1), so the 32-row MFMA fragment reads hit
+//     distinct banks for both 32- and 64-bank LDS;
+//   - one persistent workgroup per CU.  Tile t of a round goes to workgroup
+//     w with t = r*P + (w % 8) * (P / 8) + w / 8, so the 32 workgroups an XCD
+//     runs together take 32 consecutive tiles; tiles are ordered in groups
+//     of 8 row tiles x all column tiles, so those 32 share 8 A row-blocks and
+//     4 B column-blocks in the XCD's L2 (and the 8 XCDs of a round share one
+//     group pair in the Infinity Cache);
+//   - the row tile -> (expert, first row) map is computed on the device from
+//     `offsets` (a wavefront scan over the 256 experts), never on the host;
+//   - epilogues stage the fp32 tile through LDS in 64-row chunks so every
+//     global store (and the combine's y_perm gathers) is a 16-byte access:
+//     SwiGLU -> bf16 h; bf16 y_perm; or the shared expert's combine
+//     y = acc + sum_j w_j * y_perm[row_of[t*k + j]] in fp32.
+#include "device.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kE = 256;
+constexpr int LM = 256;      // rows per tile
+constexpr int LB = 256;      // B rows per tile
+constexpr int LK = 64;       // K per stage: 128-byte rows (whole L2 lines)
+constexpr int NUNIT = 5;     // LDS ring units of one stage operand (5 x 32 KB)
+constexpr int UNIT_ELEMS = LM * LK;
+static_assert(LM == LB, "A and B stage slabs share the unit size");
+constexpr int kGroupM = 8;   // row tiles per ordering group
+constexpr int kChRows = 64;  // epilogue chunk rows
+constexpr int kChLd = LB + 4;
+
+enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_COMBINE = 2 };
+
+struct LargeParams {
+    int M;
+    const int32_t *offsets;
+    const uint16_t *A;
+    int K;
+    const uint16_t *B0, *B1;
+    int N;
+    uint16_t *out;
+    float *yout;
+    const uint16_t *y_perm;
+    const int32_t *row_of;
+    const float *cw;
+    int k;
+};
+
+// Row-tile map: lane owns experts 4*lane .. 4*lane+3.
+struct TileMap {
+    int off[5];
+    int nt[4];
+    int excl, total;
+};
+
+__device__ __forceinline__ void tilemap_init(TileMap &tm, const int32_t *__restrict__ offsets) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) tm.off[i] = offsets[lane * 4 + i];
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        tm.nt[i] = (tm.off[i + 1] - tm.off[i] + LM - 1) / LM;
+        s += tm.nt[i];
+    }
+    const int incl = wave_incl_scan(s);
+    tm.excl = incl - s;
+    tm.total = __shfl(incl, 63, 64);
+}
+
+__device__ __forceinline__ void tilemap_find(const TileMap &tm, int mt, int &e, int &m0, int &m_end) {
+    const int lane = threadIdx.x & 63;
+    const int mine = tm.nt[0] + tm.nt[1] + tm.nt[2] + tm.nt[3];
+    const bool own = mt >= tm.excl && mt < tm.excl + mine;
+    const int owner = __ffsll((unsigned long long)__ballot(own)) - 1;
+    int my_e = 0, my_m0 = 0, my_end = 0;
+    if (own) {
+        int s = mt - tm.excl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (s >= 0 && s < tm.nt[i]) {
+                my_e = lane * 4 + i;
+                my_m0 = tm.off[i] + s * LM;
+                my_end = tm.off[i + 1];
+            }
+            s -= tm.nt[i];
+        }
+    }
+    e = __shfl(my_e, owner, 64);
+    m0 = __shfl(my_m0, owner, 64);
+    m_end = __shfl(my_end, owner, 64);
+}
+
+// Element offset, inside one stage operand region, of the 16-byte piece c
+// (K elements 8c .. 8c+7) of tile row `row`: rows are 128 bytes; piece c is
+// stored at position c ^ (row & 7) ^ ((row >> 3) & 1), so 8 consecutive rows
+// (32 banks) and 16 consecutive rows (64 banks) reading one logical piece hit
+// distinct banks.
+__device__ __forceinline__ int lds_piece(int row, int c) {
+    return row * LK + ((c ^ (row & 7) ^ ((row >> 3) & 1)) * 8);
+}
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding and all its LDS operations are done (expcnt unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lds() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One 1 KB block (8 rows of 128 B) of a stage operand, global -> LDS.
+__device__ __forceinline__ void dma_block(const uint16_t *src, uint16_t *lds_block) {
+    __builtin_amdgcn_global_load_lds(static_cast<const void *>(src), (lds_void_t *)(lds_block),
+                                     16, 0, 0);
+}
+
+template <int EPI, bool ROUTED>
+__global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
+    constexpr bool DUAL = EPI == EPI_SWIGLU;
+    constexpr int BN = DUAL ? LB / 2 : LB;  // output columns per tile
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[NUNIT * UNIT_ELEMS];  // 160 KB
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS bases stay scalar
+    const int wm = wave >> 1, wn = wave & 1, g = lane >> 5;
+    const int K = p.K, nk = K / LK;
+
+    TileMap tm;
+    int Mt;
+    if (ROUTED) {
+        tilemap_init(tm, p.offsets);
+        Mt = tm.total;
+    } else {
+        Mt = (p.M + LM - 1) / LM;
+    }
+    const int NT = p.N / BN;
+    const int total = Mt * NT;
+    const int P = gridDim.x;
+
+    // DMA geometry: each operand (256 rows x 128 B = 32 blocks of 1 KB) is
+    // moved by 8 instructions per wave: wave w takes blocks w + 4*i; lane l
+    // fills physical piece (l & 7) of row 8*blk + (l >> 3).
+    int drow[8], dcol[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = 8 * (wave + 4 * i) + (lane >> 3);
+        drow[i] = row;
+        dcol[i] = ((lane & 7) ^ (row & 7) ^ ((row >> 3) & 1)) * 8;
+    }
+
+    for (int t = (blockIdx.x & 7) * (P >> 3) + (blockIdx.x >> 3); t < total; t += P) {
+        const int gsz = kGroupM * NT;
+        const int grp = t / gsz, within = t - grp * gsz;
+        const int mfirst = grp * kGroupM;
+        const int gm = min(kGroupM, Mt - mfirst);
+        const int mt = mfirst + within % gm, nt = within / gm;
+        int e, m0, m_end;
+        if (ROUTED) {
+            tilemap_find(tm, mt, e, m0, m_end);
+        } else {
+            e = 0;
+            m0 = mt * LM;
+            m_end = p.M;
+        }
+        const int n0 = nt * BN;
+
+        const uint16_t *Ab = p.A + (size_t)m0 * K;
+        const uint16_t *Bg = p.B0 + (size_t)e * p.N * K;
+        const uint16_t *Bu = DUAL ? p.B1 + (size_t)e * p.N * K : Bg;
+        const uint16_t *asrc[8], *bsrc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            int ar = m0 + drow[i];
+            ar = ar < m_end ? ar : m_end - 1;
+            asrc[i] = Ab + (size_t)(ar - m0) * K + dcol[i];
+            const int r = drow[i];
+            const uint16_t *Bm = (DUAL && r >= BN) ? Bu : Bg;
+            const int br = DUAL ? n0 + (r & (BN - 1)) : n0 + r;
+            bsrc[i] = Bm + (size_t)br * K + dcol[i];
+        }
+        f32x16 acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+        // LDS ring of NUNIT operand units: operand j of the tile's sequence
+        // A_0, B_0, A_1, B_1, ... (A_s / B_s: the A / B slab of stage s) lives
+        // in unit j % NUNIT.  Loads past the last stage are clamped to it:
+        // they fill units that are never read as that stage, which keeps
+        // every load and read unconditional.
+#define UNIT(j) (smem + ((j) % NUNIT) * UNIT_ELEMS)
+#define ISSUE_A(st_, i)                                                                        \
+        dma_block(asrc[i] + min((st_), nk - 1) * LK, UNIT(2 * (st_)) + (wave + 4 * (i)) * 512)
+#define ISSUE_B(st_, i)                                                                        \
+        dma_block(bsrc[i] + min((st_), nk - 1) * LK, UNIT(2 * (st_) + 1) + (wave + 4 * (i)) * 512)
+#define B_ROW(j) ((DUAL ? (((j) >> 1) * 128 + wn * 64 + ((j) & 1) * 32) : (wn * 128 + (j) * 32)) + (lane & 31))
+
+        // One 16-wide K step: 16 MFMAs on (AC, BC); after MFMA x, the load
+        // DMA(x) (if any) and, for x < 8, fragment x of the next step from
+        // the units nA / nB at piece column cn into (AN, BN_).  The order is
+        // fixed by scheduling barriers: a slot load blocks this wave's issue
+        // for up to about one MFMA's duration, so loads are spread between
+        // MFMAs rather than issued back to back.
+#define STEP(AC, BC, AN, BN_, nA, nB, cn, DMA)                                                 \
+        _Pragma("unroll") for (int x = 0; x < 16; ++x) {                                       \
+            acc[x >> 2][x & 3] =                                                               \
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(AC[x >> 2], BC[x & 3], acc[x >> 2][x & 3], 0, 0, 0); \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+            DMA(x);                                                                            \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+            if (x < 4)                                                                         \
+                AN[x] = *reinterpret_cast<const bf16x8 *>((nA) + lds_piece(wm * 128 + x * 32 + (lane & 31), (cn))); \
+            else if (x < 8)                                                                    \
+                BN_[x - 4] = *reinterpret_cast<const bf16x8 *>((nB) + lds_piece(B_ROW(x - 4), (cn))); \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+        }
+
+        // Prologue: A_0, B_0, A_1, B_1 in flight; A_0 and B_0 landed for every
+        // wave; then the first step's fragments.
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ISSUE_A(0, i);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ISSUE_B(0, i);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ISSUE_A(1, i);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ISSUE_B(1, i);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        wait_vmcnt_lds<16>();
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        bf16x8 a0[4], b0[4], a1[4], b1[4];
+        {
+            const uint16_t *sA = UNIT(0), *sB = UNIT(1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a0[i] = *reinterpret_cast<const bf16x8 *>(sA + lds_piece(wm * 128 + i * 32 + (lane & 31), g));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b0[j] = *reinterpret_cast<const bf16x8 *>(sB + lds_piece(B_ROW(j), g));
+        }
+
+        // Stage kt = 4 steps of 16 K; fragments of step s+1 are read during
+        // step s.  Steps 0-2 stream A_{kt+2} into the unit B_{kt-1} left
+        // (free since the previous stage's barrier), one load per 6 MFMAs.
+        // After step 2 every fragment of stage kt is in registers, so the
+        // mid-stage barrier (once A_{kt+1} and B_{kt+1} have landed: only
+        // A_{kt+2}'s 8 loads may remain in flight) frees A_kt's and B_kt's
+        // units; step 3 streams B_{kt+2} into A_kt's unit, one load per 2
+        // MFMAs, and reads stage kt+1's first fragments.  A gets about 1.5
+        // stages to arrive, B about one.
+        for (int kt = 0; kt < nk; ++kt) {
+            const uint16_t *cA = UNIT(2 * kt), *cB = UNIT(2 * kt + 1);
+#define DMA_S0(x) if ((x) == 2 || (x) == 8 || (x) == 14) ISSUE_A(kt + 2, ((x) - 2) / 6)
+#define DMA_S1(x) if ((x) == 4 || (x) == 10) ISSUE_A(kt + 2, 3 + ((x) - 4) / 6)
+#define DMA_S2(x) if ((x) == 0 || (x) == 6 || (x) == 12) ISSUE_A(kt + 2, 5 + (x) / 6)
+#define DMA_S3(x) if (((x) & 1) == 0) ISSUE_B(kt + 2, (x) >> 1)
+            STEP(a0, b0, a1, b1, cA, cB, 2 + g, DMA_S0);
+            STEP(a1, b1, a0, b0, cA, cB, 4 + g, DMA_S1);
+            STEP(a0, b0, a1, b1, cA, cB, 6 + g, DMA_S2);
+
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            wait_vmcnt_lds<8>();           // A_{kt+1}, B_{kt+1} landed for this wave
+            __builtin_amdgcn_s_barrier();  // ... for all waves; A_kt, B_kt no longer read
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            const uint16_t *nA = UNIT(2 * kt + 2), *nB = UNIT(2 * kt + 3);
+            STEP(a1, b1, a0, b0, nA, nB, g, DMA_S3);
+#undef DMA_S0
+#undef DMA_S1
+#undef DMA_S2
+#undef DMA_S3
+        }
+#undef STEP
+#undef B_ROW
+#undef ISSUE_A
+#undef ISSUE_B
+#undef UNIT
+        __syncthreads();  // every wave done with the ring before the epilogue reuses LDS
+
+        // Epilogue: four 64-row chunks of the fp32 tile through LDS.
+        float *ch = reinterpret_cast<float *>(smem);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if (wm == (c >> 1)) {
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii) {
+                    const int i = 2 * (c & 1) + ii;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int col = (DUAL ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32)) +
+                                        (lane & 31);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            ch[(ii * 32 + 8 * (r >> 2) + 4 * g + (r & 3)) * kChLd + col] = acc[i][j][r];
+                    }
+                }
+            }
+            __syncthreads();
+            const int rl = tid >> 2, part = tid & 3;
+            const int row = m0 + c * kChRows + rl;
+            const float *cr = ch + rl * kChLd;
+            if (row < m_end) {
+                if (DUAL) {
+                    // h columns part*32 .. +32: gate in chunk columns [0,128), up in [128,256)
+#pragma unroll
+                    for (int x = 0; x < 32; x += 8) {
+                        uint32_t pk[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            float hv[2];
+#pragma unroll
+                            for (int u = 0; u < 2; ++u) {
+                                const int cc = part * 32 + x + 2 * q + u;
+                                const float gv = cr[cc], uv = cr[128 + cc];
+                                hv[u] = gv / (1.0f + expf(-gv)) * uv;
+                            }
+                            pk[q] = pack_bf16x2(hv[0], hv[1]);
+                        }
+                        *reinterpret_cast<i32x4 *>(p.out + (size_t)row * p.N + n0 + part * 32 + x) =
+                            i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+                    }
+                } else if (EPI == EPI_STORE) {
+#pragma unroll
+                    for (int x = 0; x < 64; x += 8) {
+                        const int cc = part * 64 + x;
+                        *reinterpret_cast<i32x4 *>(p.out + (size_t)row * p.N + n0 + cc) =
+                            i32x4{(int)pack_bf16x2(cr[cc], cr[cc + 1]), (int)pack_bf16x2(cr[cc + 2], cr[cc + 3]),
+                                  (int)pack_bf16x2(cr[cc + 4], cr[cc + 5]), (int)pack_bf16x2(cr[cc + 6], cr[cc + 7])};
+                    }
+                } else {
+                    int rof[8];
+                    float wj[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        rof[j] = p.row_of[(size_t)row * 8 + j];
+                        wj[j] = p.cw[(size_t)row * 8 + j];
+                    }
+#pragma unroll 2
+                    for (int x = 0; x < 64; x += 8) {
+                        const int cc = part * 64 + x;
+                        float v[8];
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) v[u] = cr[cc + u];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const i32x4 yv = *reinterpret_cast<const i32x4 *>(p.y_perm + (size_t)rof[j] * p.N + n0 + cc);
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) {
+                                v[2 * u] += wj[j] * bf16_to_f32((uint32_t)yv[u] & 0xffffu);
+                                v[2 * u + 1] += wj[j] * bf16_to_f32((uint32_t)yv[u] >> 16);
+                            }
+                        }
+                        float *yo = p.yout + (size_t)row * p.N + n0 + cc;
+                        *reinterpret_cast<f32x4 *>(yo) = f32x4{v[0], v[1], v[2], v[3]};
+                        *reinterpret_cast<f32x4 *>(yo + 4) = f32x4{v[4], v[5], v[6], v[7]};
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+int cu_count() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+}  // namespace
+
+bool ffn_bf16_large_ok(const FfnArgs &a) {
+    const int groups = a.offsets ? a.E : 1;
+    return (long long)a.M >= 128LL * groups && a.I % 128 == 0 && a.d % 256 == 0 && a.d % LK == 0 &&
+           a.I % LK == 0;
+}
+
+hipError_t launch_ffn_bf16_large(const FfnArgs &a, hipStream_t s) {
+    const int P = (cu_count() / 8) * 8;
+    const bool routed = a.offsets != nullptr;
+    if (a.phases & 1) {
+        LargeParams p{};
+        p.M = a.M;
+        p.offsets = a.offsets;
+        p.A = static_cast<const uint16_t *>(a.a);
+        p.K = a.d;
+        p.B0 = static_cast<const uint16_t *>(a.w.gate);
+        p.B1 = static_cast<const uint16_t *>(a.w.up);
+        p.N = a.I;
+        p.out = static_cast<uint16_t *>(a.h);
+        if (routed)
+            hipLaunchKernelGGL((k_gemm_bf16_large<EPI_SWIGLU, true>), dim3(P), dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((k_gemm_bf16_large<EPI_SWIGLU, false>), dim3(P), dim3(256), 0, s, p);
+    }
+    if (a.phases & 2) {
+        LargeParams q{};
+        q.M = a.M;
+        q.offsets = a.offsets;
+        q.A = static_cast<const uint16_t *>(a.h);
+        q.K = a.I;
+        q.B0 = static_cast<const uint16_t *>(a.w.down);
+        q.N = a.d;
+        if (a.combine) {
+            q.yout = static_cast<float *>(a.y);
+            q.y_perm = static_cast<const uint16_t *>(a.y_perm);
+            q.row_of = a.row_of;
+            q.cw = a.cw;
+            q.k = a.k;
+            hipLaunchKernelGGL((k_gemm_bf16_large<EPI_COMBINE, false>), dim3(P), dim3(256), 0, s, q);
+        } else {
+            q.out = static_cast<uint16_t *>(a.y);
+            if (routed)
+                hipLaunchKernelGGL((k_gemm_bf16_large<EPI_STORE, true>), dim3(P), dim3(256), 0, s, q);
+            else
+                hipLaunchKernelGGL((k_gemm_bf16_large<EPI_STORE, false>), dim3(P), dim3(256), 0, s, q);
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -119,3 +119,12 @@ def test_layer_config4_skewed_reduced():
     cfg = synth.CONFIGS[4].with_(T=2048, d=1024, I=256)
     inp = synth.make_inputs(cfg)
     check_layer(cfg, inp, n_sample=64)
+
+
+def test_layer_config4_full_size_sampled():
+    """The skewed prefill workload at full size (T=16384, d=7168, I=2048, bf16),
+    the launch configuration bench.py times: the oracle checks 12 sampled
+    tokens; every token's routing is checked for near-tie-only differences."""
+    cfg = synth.CONFIGS[4]
+    inp = synth.make_inputs(cfg)
+    check_layer(cfg, inp, n_sample=12, route_all=False)

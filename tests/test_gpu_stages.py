@@ -178,6 +178,28 @@ def test_expert_ffn_small(wt, kind, T):
     assert err <= TOL[wt], err
 
 
+@pytest.mark.parametrize("kind", ["random", "skewed", "same8"])
+def test_expert_ffn_large_groups(kind):
+    """T=4096 tokens: 128+ rows per expert on average, the persistent
+    256x256-tile path; d=512, I=256 so several column tiles and K stages run.
+    The oracle checks 160 sampled permuted rows including group edges."""
+    cfg = synth.Config("ffn-large", seed=23, T=4096, d=512, I=256)
+    say(f"[ffn] large groups {kind}")
+    experts = synth.make_ffn(cfg, 256, (synth.TID_GATE, synth.TID_UP, synth.TID_DOWN))
+    offsets, a_rows, a_sc = ffn_inputs(cfg, kind)
+    y = run_ffn(cfg, offsets, a_rows, a_sc, experts)
+    rng = np.random.default_rng(1)
+    nz = np.where(np.diff(offsets) > 0)[0]
+    edges = np.concatenate([offsets[nz], offsets[nz + 1] - 1, offsets[nz] + 255, offsets[nz] + 256])
+    edges = edges[edges < cfg.A]
+    rows = np.unique(np.concatenate([rng.choice(edges, min(96, len(edges)), replace=False),
+                                     rng.integers(0, cfg.A, 64)])).astype(np.int32)
+    yo = oracle.expert_ffn(oracle.shape_of(cfg), experts, offsets, a_rows, a_sc, rows=rows)
+    err = max_rel(yvals(y[rows], "bf16"), yvals(yo, "bf16"))
+    say(f"[ffn] large groups {kind}: max rel err {err:.3e} on {len(rows)} rows")
+    assert err <= TOL["bf16"], err
+
+
 def test_expert_ffn_config2_sampled_rows():
     """Config 2 shapes (T=2048, d=2048, I=512), bf16, real routing; the oracle
     checks 64 sampled permuted rows, including each group's first and last."""
@@ -199,7 +221,8 @@ def test_expert_ffn_config2_sampled_rows():
 
 # ---------------------------------------------------------------- combine
 
-@pytest.mark.parametrize("wt,T", [("f32", 32), ("bf16", 100), ("bf16", 257), ("e4m3", 100), ("e4m3", 257)])
+@pytest.mark.parametrize("wt,T", [("f32", 32), ("bf16", 100), ("bf16", 257), ("bf16", 1000), ("e4m3", 100),
+                                  ("e4m3", 257)])
 def test_combine(wt, T):
     act = "f32" if wt == "f32" else "bf16"
     cfg = synth.Config("comb", seed=31, T=T, d=256, I=128, act=act, wt=wt)
