@@ -126,6 +126,7 @@ def main():
              for i, n in enumerate(names)}
     ch = counts_hist.cpu().numpy().astype(np.float64)
     imb = ch.max(axis=1) / ch.mean(axis=1)
+    tiles = np.ceil(ch / 256.0).sum(axis=1)  # launched 256-row tiles of the routed GEMMs
 
     gate_up_flops = 2.0 * A * d * (2 * I)
     gate_up_ms = phase["expert_gate_up"]
@@ -135,7 +136,8 @@ def main():
     ms_step = wall / K * 1e3
     log(f"[bench] {ms_step:.3f} ms/step, phases (ms): " + ", ".join(f"{n} {v:.3f}" for n, v in phase.items()))
     log(f"[bench] gate/up GEMM {achieved:.1f} TFLOP/s ({100 * achieved / peak:.1f}% of peak); "
-        f"layer {total_flops / (ms_step * 1e-3) / 1e12:.1f} TFLOP/s; max/mean load {imb[0]:.2f} -> {imb[-1]:.2f}")
+        f"layer {total_flops / (ms_step * 1e-3) / 1e12:.1f} TFLOP/s; max/mean load {imb[0]:.2f} -> {imb[-1]:.2f}; "
+        f"256-row tiles {tiles.mean():.0f} (ideal {A / 256:.0f})")
 
     out = {
         "metric": METRIC,
@@ -153,7 +155,7 @@ def main():
         "config": {"workload": cfg.name, "T": T, "d_model": d, "experts": E, "top_k": k, "shared_experts": 1,
                    "expert_intermediate": I, "router": "fp32 sigmoid", "router_row_skew": cfg.skew,
                    "bias_start": cfg.bias, "gamma": cfg.gamma, "loop_steps_timed": K, "seed": cfg.seed},
-        "roofline": {"kernel": "routed gate/up grouped GEMM (k_gemm_bf16 SwiGLU)" if cfg.wt != "e4m3"
+        "roofline": {"kernel": "routed gate/up grouped GEMM (k_gemm_bf16_large, SwiGLU epilogue)" if cfg.wt != "e4m3"
                      else "routed gate/up grouped GEMM (k_gemm_fp8 SwiGLU+quant)",
                      "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": None,
@@ -161,6 +163,7 @@ def main():
         "phases_ms": phase,
         "layer_tflops": total_flops / (ms_step * 1e-3) / 1e12,
         "imbalance_max_over_mean": {"first": float(imb[0]), "last": float(imb[-1])},
+        "routed_row_tiles_mean": float(tiles.mean()),
     }
 
     if not args.no_cpu_baseline:

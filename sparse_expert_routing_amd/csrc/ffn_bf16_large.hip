@@ -142,9 +142,35 @@ __device__ __forceinline__ void dma_block(const uint16_t *src, uint16_t *lds_blo
                                      16, 0, 0);
 }
 
+// acc += A_frag x B_frag^T.  TRANS swaps the operands, so the accumulator
+// holds the transposed 32x32 block: lane l then owns tile row l % 32 and, in
+// registers 4q .. 4q+3, the 4 consecutive tile columns 8q + 4(l / 32) .. +3,
+// which the epilogue stores straight from registers.
+template <bool TRANS>
+__device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
+    if constexpr (TRANS) return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// One accumulator element, copied from its AGPR where it is used: left to
+// the compiler, every accumulator is copied to VGPRs at the loop exit,
+// which needs 256 VGPRs and spills the tile loop's state.
+__device__ __forceinline__ float acc_read(float x) {
+    float r;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
+    return r;
+}
+
+// silu(g) * u in fp32 from the hardware exp2 and reciprocal (about 1 ulp
+// each; the product is rounded to bf16 next).
+__device__ __forceinline__ float swiglu(float g, float u) {
+    return g * u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
+
 template <int EPI, bool ROUTED>
 __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
     constexpr bool DUAL = EPI == EPI_SWIGLU;
+    constexpr bool TRANS = EPI != EPI_COMBINE;  // register epilogue (no LDS staging)
     constexpr int BN = DUAL ? LB / 2 : LB;  // output columns per tile
     __shared__ __attribute__((aligned(1024))) uint16_t smem[NUNIT * UNIT_ELEMS];  // 160 KB
 
@@ -234,8 +260,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
         // MFMAs rather than issued back to back.
 #define STEP(AC, BC, AN, BN_, nA, nB, cn, DMA)                                                 \
         _Pragma("unroll") for (int x = 0; x < 16; ++x) {                                       \
-            acc[x >> 2][x & 3] =                                                               \
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(AC[x >> 2], BC[x & 3], acc[x >> 2][x & 3], 0, 0, 0); \
+            acc[x >> 2][x & 3] = mma<TRANS>(AC[x >> 2], BC[x & 3], acc[x >> 2][x & 3]);         \
             __builtin_amdgcn_sched_barrier(0);                                                 \
             DMA(x);                                                                            \
             __builtin_amdgcn_sched_barrier(0);                                                 \
@@ -305,88 +330,102 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
 #undef ISSUE_A
 #undef ISSUE_B
 #undef UNIT
-        __syncthreads();  // every wave done with the ring before the epilogue reuses LDS
+        __syncthreads();  // every wave done with the ring (and its loads landed)
 
-        // Epilogue: four 64-row chunks of the fp32 tile through LDS.
-        float *ch = reinterpret_cast<float *>(smem);
+        if constexpr (TRANS) {
+            // Register epilogue: lane owns tile rows wm*128 + 32i + (lane & 31)
+            // and, per 32-column block, 4 runs of 4 consecutive columns: one
+            // 8-byte bf16 store per run.  Values are computed for every row
+            // (padding rows repeat the group's last row) and only the stores
+            // are predicated, so the epilogue stays one block whose scheduling
+            // barriers bound how many accumulators sit in VGPRs at once.
+            const int c4 = 4 * g;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            if (wm == (c >> 1)) {
+            for (int i = 0; i < 4; ++i) {
+                const int row = m0 + wm * 128 + 32 * i + (lane & 31);
+                const bool ok = row < m_end;
+                uint16_t *orow = p.out + (size_t)(ok ? row : m0) * p.N + n0;
 #pragma unroll
-                for (int ii = 0; ii < 2; ++ii) {
-                    const int i = 2 * (c & 1) + ii;
+                for (int jj = 0; jj < (DUAL ? 2 : 4); ++jj) {
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int col = (DUAL ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32)) +
-                                        (lane & 31);
+                    for (int q = 0; q < 4; ++q) {
+                        uint32_t lo, hi;
+                        if constexpr (DUAL) {
+                            float h[4];
 #pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            ch[(ii * 32 + 8 * (r >> 2) + 4 * g + (r & 3)) * kChLd + col] = acc[i][j][r];
+                            for (int u = 0; u < 4; ++u)
+                                h[u] = swiglu(acc_read(acc[i][jj][4 * q + u]), acc_read(acc[i][2 + jj][4 * q + u]));
+                            lo = pack_bf16x2(h[0], h[1]);
+                            hi = pack_bf16x2(h[2], h[3]);
+                        } else {
+                            lo = pack_bf16x2(acc_read(acc[i][jj][4 * q]), acc_read(acc[i][jj][4 * q + 1]));
+                            hi = pack_bf16x2(acc_read(acc[i][jj][4 * q + 2]), acc_read(acc[i][jj][4 * q + 3]));
+                        }
+                        const int col = (DUAL ? wn * 64 : wn * 128) + jj * 32 + 8 * q + c4;
+                        if (ok) *reinterpret_cast<uint2 *>(orow + col) = make_uint2(lo, hi);
                     }
                 }
             }
-            __syncthreads();
-            const int rl = tid >> 2, part = tid & 3;
-            const int row = m0 + c * kChRows + rl;
-            const float *cr = ch + rl * kChLd;
-            if (row < m_end) {
-                if (DUAL) {
-                    // h columns part*32 .. +32: gate in chunk columns [0,128), up in [128,256)
+        } else {
+            // Combine epilogue: four 64-row chunks of the fp32 tile through
+            // LDS, so every y_perm gather and y store is a 16-byte access.
+            float *ch = reinterpret_cast<float *>(smem);
 #pragma unroll
-                    for (int x = 0; x < 32; x += 8) {
-                        uint32_t pk[4];
+            for (int c = 0; c < 4; ++c) {
+                if (wm == (c >> 1)) {
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            float hv[2];
+                    for (int ii = 0; ii < 2; ++ii) {
+                        const int i = 2 * (c & 1) + ii;
 #pragma unroll
-                            for (int u = 0; u < 2; ++u) {
-                                const int cc = part * 32 + x + 2 * q + u;
-                                const float gv = cr[cc], uv = cr[128 + cc];
-                                hv[u] = gv / (1.0f + expf(-gv)) * uv;
-                            }
-                            pk[q] = pack_bf16x2(hv[0], hv[1]);
+                        for (int j = 0; j < 4; ++j) {
+                            const int col = wn * 128 + j * 32 + (lane & 31);
+#pragma unroll
+                            for (int r = 0; r < 16; ++r)
+                                ch[(ii * 32 + 8 * (r >> 2) + 4 * g + (r & 3)) * kChLd + col] = acc[i][j][r];
                         }
-                        *reinterpret_cast<i32x4 *>(p.out + (size_t)row * p.N + n0 + part * 32 + x) =
-                            i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
                     }
-                } else if (EPI == EPI_STORE) {
-#pragma unroll
-                    for (int x = 0; x < 64; x += 8) {
-                        const int cc = part * 64 + x;
-                        *reinterpret_cast<i32x4 *>(p.out + (size_t)row * p.N + n0 + cc) =
-                            i32x4{(int)pack_bf16x2(cr[cc], cr[cc + 1]), (int)pack_bf16x2(cr[cc + 2], cr[cc + 3]),
-                                  (int)pack_bf16x2(cr[cc + 4], cr[cc + 5]), (int)pack_bf16x2(cr[cc + 6], cr[cc + 7])};
-                    }
-                } else {
-                    int rof[8];
-                    float wj[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        rof[j] = p.row_of[(size_t)row * 8 + j];
-                        wj[j] = p.cw[(size_t)row * 8 + j];
-                    }
+                }
+                __syncthreads();
+                // Half-wave per row: lanes 0-31 take row 2*it, lanes 32-63 row
+                // 2*it+1 of this wave's 16 chunk rows, 8 columns per lane, so
+                // each gather of a routed output row is one contiguous 512-byte
+                // run (few lines and pages per load instruction).
+                const int cl = 8 * (lane & 31);
 #pragma unroll 2
-                    for (int x = 0; x < 64; x += 8) {
-                        const int cc = part * 64 + x;
-                        float v[8];
-#pragma unroll
-                        for (int u = 0; u < 8; ++u) v[u] = cr[cc + u];
+                for (int it = 0; it < 8; ++it) {
+                    const int rl = wave * 16 + 2 * it + g;
+                    const int row = m0 + c * kChRows + rl;
+                    if (row < m_end) {
+                        int rof[8];
+                        float wj[8];
 #pragma unroll
                         for (int j = 0; j < 8; ++j) {
-                            const i32x4 yv = *reinterpret_cast<const i32x4 *>(p.y_perm + (size_t)rof[j] * p.N + n0 + cc);
+                            rof[j] = p.row_of[(size_t)row * 8 + j];
+                            wj[j] = p.cw[(size_t)row * 8 + j];
+                        }
+                        i32x4 yv[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            yv[j] = *reinterpret_cast<const i32x4 *>(p.y_perm + (size_t)rof[j] * p.N + n0 + cl);
+                        const float *cr = ch + rl * kChLd + cl;
+                        const f32x4 s0 = *reinterpret_cast<const f32x4 *>(cr);
+                        const f32x4 s1 = *reinterpret_cast<const f32x4 *>(cr + 4);
+                        float v[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
 #pragma unroll
                             for (int u = 0; u < 4; ++u) {
-                                v[2 * u] += wj[j] * bf16_to_f32((uint32_t)yv[u] & 0xffffu);
-                                v[2 * u + 1] += wj[j] * bf16_to_f32((uint32_t)yv[u] >> 16);
+                                v[2 * u] += wj[j] * bf16_to_f32((uint32_t)yv[j][u] & 0xffffu);
+                                v[2 * u + 1] += wj[j] * bf16_to_f32((uint32_t)yv[j][u] >> 16);
                             }
-                        }
-                        float *yo = p.yout + (size_t)row * p.N + n0 + cc;
+                        float *yo = p.yout + (size_t)row * p.N + n0 + cl;
                         *reinterpret_cast<f32x4 *>(yo) = f32x4{v[0], v[1], v[2], v[3]};
                         *reinterpret_cast<f32x4 *>(yo + 4) = f32x4{v[4], v[5], v[6], v[7]};
                     }
                 }
+                __syncthreads();
             }
-            __syncthreads();
         }
     }
 }
