@@ -32,6 +32,8 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6   # dense bf16 MFMA, MI355X
 PEAK_FP8_TFLOPS = 5033.2    # dense fp8 MFMA, MI355X
 PEAK_HBM_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "sparse_expert_routing_amd", "csrc", "ffn_bf16_large.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_gemm_bf16_large_gateup_traffic_prefill-zipf-bf16.md")
 METRIC = "MoE-layer tokens/s (T=16384,d=7168,256e top-8) + % of MFMA/HBM peak"
 
 
@@ -48,6 +50,8 @@ def main():
                     help="workload (4: the skewed prefill layer the metric is quoted on)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 3 times (the byte-counter reference)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -64,6 +68,15 @@ def main():
     from sparse_expert_routing_amd.layer import layer_from_inputs, upload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copied 3 x 1 GiB")
+        return
     _lib.load()  # fails loudly without the HIP library
     cfg = synth.CONFIGS[args.config]
     T, d, I, E, k = cfg.T, cfg.d, cfg.I, cfg.E, cfg.k
@@ -158,7 +171,7 @@ def main():
         "roofline": {"kernel": "routed gate/up grouped GEMM (k_gemm_bf16_large, SwiGLU epilogue)" if cfg.wt != "e4m3"
                      else "routed gate/up grouped GEMM (k_gemm_fp8 SwiGLU+quant)",
                      "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None,
+                     "frac": achieved / peak, "traffic": measured_traffic() if cfg.wt != "e4m3" else None,
                      "flops_per_launch": gate_up_flops, "avg_launch_ms": gate_up_ms},
         "phases_ms": phase,
         "layer_tflops": total_flops / (ms_step * 1e-3) / 1e12,
@@ -169,6 +182,23 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed FETCH_SIZE / WRITE_SIZE
+    summary (counter runs scaled by a plain-copy calibration), or None when
+    the kernel source has changed since those counters were taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            kv = dict(line.split(":", 1) for line in f if line.startswith(("source_sha256:", "traffic_bytes_per_launch:")))
+        with open(KERNEL_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if kv.get("source_sha256", "").strip() != sha:
+        return None
+    return float(kv["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(cfg, inp, target_s):

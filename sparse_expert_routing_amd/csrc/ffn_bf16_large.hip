@@ -250,24 +250,29 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
         dma_block(asrc[i] + min((st_), nk - 1) * LK, UNIT(2 * (st_)) + (wave + 4 * (i)) * 512)
 #define ISSUE_B(st_, i)                                                                        \
         dma_block(bsrc[i] + min((st_), nk - 1) * LK, UNIT(2 * (st_) + 1) + (wave + 4 * (i)) * 512)
+#define READ_AT(r) (2 * (r))
 #define B_ROW(j) ((DUAL ? (((j) >> 1) * 128 + wn * 64 + ((j) & 1) * 32) : (wn * 128 + (j) * 32)) + (lane & 31))
 
-        // One 16-wide K step: 16 MFMAs on (AC, BC); after MFMA x, the load
-        // DMA(x) (if any) and, for x < 8, fragment x of the next step from
-        // the units nA / nB at piece column cn into (AN, BN_).  The order is
-        // fixed by scheduling barriers: a slot load blocks this wave's issue
-        // for up to about one MFMA's duration, so loads are spread between
-        // MFMAs rather than issued back to back.
+        // One 16-wide K step: 16 MFMAs on (AC, BC).  The next step's 8
+        // fragments (from the units nA / nB at piece column cn into AN, BN_)
+        // are read at READ_AT(r) (before MFMA READ_AT(r)), the load DMA(x)
+        // (if any) right after MFMA x.  The order is fixed by scheduling
+        // barriers: a slot load blocks this wave's issue for up to about one
+        // MFMA's duration, so loads are spread between MFMAs rather than
+        // issued back to back.
+#define FRAG_READ(r, AN, BN_, nA, nB, cn)                                                      \
+        if ((r) < 4)                                                                           \
+            AN[(r) & 3] = *reinterpret_cast<const bf16x8 *>((nA) + lds_piece(wm * 128 + ((r) & 3) * 32 + (lane & 31), (cn))); \
+        else                                                                                   \
+            BN_[(r) & 3] = *reinterpret_cast<const bf16x8 *>((nB) + lds_piece(B_ROW((r) & 3), (cn)));
 #define STEP(AC, BC, AN, BN_, nA, nB, cn, DMA)                                                 \
         _Pragma("unroll") for (int x = 0; x < 16; ++x) {                                       \
+            _Pragma("unroll") for (int r = 0; r < 8; ++r)                                      \
+                if (READ_AT(r) == x) { FRAG_READ(r, AN, BN_, nA, nB, cn) }                     \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
             acc[x >> 2][x & 3] = mma<TRANS>(AC[x >> 2], BC[x & 3], acc[x >> 2][x & 3]);         \
             __builtin_amdgcn_sched_barrier(0);                                                 \
             DMA(x);                                                                            \
-            __builtin_amdgcn_sched_barrier(0);                                                 \
-            if (x < 4)                                                                         \
-                AN[x] = *reinterpret_cast<const bf16x8 *>((nA) + lds_piece(wm * 128 + x * 32 + (lane & 31), (cn))); \
-            else if (x < 8)                                                                    \
-                BN_[x - 4] = *reinterpret_cast<const bf16x8 *>((nB) + lds_piece(B_ROW(x - 4), (cn))); \
             __builtin_amdgcn_sched_barrier(0);                                                 \
         }
 
@@ -326,6 +331,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
 #undef DMA_S3
         }
 #undef STEP
+#undef FRAG_READ
+#undef READ_AT
 #undef B_ROW
 #undef ISSUE_A
 #undef ISSUE_B
