@@ -99,10 +99,10 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         _lib.moe_dispatch(D, layer.idx, x, layer.counts, layer.offsets, layer.row_src, layer.row_of,
-                          layer.x_perm, layer.x_perm_scale, layer.ws, stream)
+                          None, None, layer.ws, stream)
         if ev is not None:
             ev[2].record(stream)
-        _lib.moe_expert_gate_up(D, layer.x_perm, layer.x_perm_scale, layer.offsets, layer.ex_w, layer.ws, stream)
+        _lib.moe_expert_gate_up_rows(D, x, layer.row_src, layer.offsets, layer.ex_w, layer.ws, stream)
         if ev is not None:
             ev[3].record(stream)
         _lib.moe_expert_down(D, layer.offsets, layer.ex_w, layer.y_perm, layer.ws, stream)

@@ -128,6 +128,9 @@ moe_status_t moe_route(const moe_desc_t *desc, const void *x, const float *w_rou
  *   x_perm_scale [T*k, d/128] fp32 out (e4m3 only, else NULL): scale = amax/448
  *                         (1 for an all-zero tile), code = e4m3_rne_sat(v / scale)
  *   workspace    >= moe_workspace_bytes(desc, MOE_WS_DISPATCH) bytes of device memory
+ * x_perm may be NULL: then only counts, offsets, row_src and row_of are
+ * written (x and x_perm_scale are not read), for moe_expert_gate_up_rows,
+ * which gathers the rows itself.
  * Integer outputs are bit-exact and deterministic (no atomics decide order).
  */
 moe_status_t moe_dispatch(const moe_desc_t *desc, const int32_t *idx, const void *x,
@@ -168,6 +171,23 @@ moe_status_t moe_expert_gate_up(const moe_desc_t *desc, const void *x_perm, cons
 moe_status_t moe_expert_down(const moe_desc_t *desc, const int32_t *offsets,
                              const moe_ffn_weights_t *experts, void *y_perm, void *workspace,
                              size_t ws_bytes, void *stream);
+
+/*
+ * moe_expert_gate_up with the dispatch gather folded into the GEMM: row r of
+ * the grouped GEMM's input is token row_src[r] / k of x, read in place, so no
+ * x_perm is materialised (the same rows in the same order as moe_dispatch's
+ * x_perm, hence the same h bit for bit).  With wt = e4m3, x is first
+ * quantised once per token (T rows, 1x128 tiles, as in moe_dispatch) into the
+ * workspace.
+ *   x         [T, d] act type (the layer input given to moe_dispatch)
+ *   row_src   [T*k]  int32 from moe_dispatch (flat assignment ids t*k + j;
+ *             row r of the GEMM reads token row_src[r] / k)
+ *   offsets, experts, workspace: as for moe_expert_gate_up
+ * Then moe_expert_down as usual.
+ */
+moe_status_t moe_expert_gate_up_rows(const moe_desc_t *desc, const void *x, const int32_t *row_src,
+                                     const int32_t *offsets, const moe_ffn_weights_t *experts,
+                                     void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * Shared expert plus weighted combine (Scaling Efficiency ..., "Implementation:

@@ -18,8 +18,8 @@ MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 MOE_WS_DISPATCH, MOE_WS_FFN, MOE_WS_COMBINE = 0, 1, 2
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_E4M3}
 
-EXPORTS = ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down",
-           "moe_combine", "moe_bias_update", "moe_workspace_bytes", "moe_status_str")
+EXPORTS = ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_gate_up_rows",
+           "moe_expert_down", "moe_combine", "moe_bias_update", "moe_workspace_bytes", "moe_status_str")
 
 
 class MoeError(RuntimeError):
@@ -57,11 +57,12 @@ def load(path: str = LIB_PATH):
     L.moe_dispatch.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_expert_ffn.argtypes = [pd, vp, vp, vp, pw, vp, vp, sz, vp]
     L.moe_expert_gate_up.argtypes = [pd, vp, vp, vp, pw, vp, sz, vp]
+    L.moe_expert_gate_up_rows.argtypes = [pd, vp, vp, vp, pw, vp, sz, vp]
     L.moe_expert_down.argtypes = [pd, vp, pw, vp, vp, sz, vp]
     L.moe_combine.argtypes = [pd, vp, pw, vp, vp, vp, vp, vp, sz, vp]
     L.moe_bias_update.argtypes = [pd, vp, f32, vp, vp]
-    for fn in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down",
-               "moe_combine", "moe_bias_update"):
+    for fn in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_gate_up_rows",
+               "moe_expert_down", "moe_combine", "moe_bias_update"):
         getattr(L, fn).restype = ctypes.c_int
     L.moe_workspace_bytes.argtypes = [pd, i32]
     L.moe_workspace_bytes.restype = sz
@@ -122,6 +123,12 @@ def moe_expert_ffn(ds, x_perm, x_perm_scale, offsets, experts: FfnWeights, y_per
 def moe_expert_gate_up(ds, x_perm, x_perm_scale, offsets, experts: FfnWeights, workspace, stream=None):
     _check("moe_expert_gate_up", load().moe_expert_gate_up(
         ctypes.byref(ds), _ptr(x_perm), _ptr(x_perm_scale), _ptr(offsets), ctypes.byref(experts),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_expert_gate_up_rows(ds, x, row_src, offsets, experts: FfnWeights, workspace, stream=None):
+    _check("moe_expert_gate_up_rows", load().moe_expert_gate_up_rows(
+        ctypes.byref(ds), _ptr(x), _ptr(row_src), _ptr(offsets), ctypes.byref(experts),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 

@@ -200,6 +200,7 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(k_disp_scan, dim3(1), dim3(kE), 0, s, nblk, a.block_base, a.counts, a.offsets);
     hipLaunchKernelGGL(k_disp_rank, dim3(nblk), dim3(kDispatchBlock), 0, s, a.T, a.idx, a.block_base,
                        a.row_src, a.row_of);
+    if (a.x_perm == nullptr) return hipGetLastError();  // bookkeeping only: the GEMM gathers through row_src
     const dim3 ggrid((a.T + 3) / 4), gblock(256);
     if (a.wt == kE4M3) {
         hipLaunchKernelGGL(k_disp_gather_e4m3, ggrid, gblock, 0, s, a.T, a.d,

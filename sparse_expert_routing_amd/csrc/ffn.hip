@@ -36,6 +36,8 @@ struct GemmParams {
     int M;                    // rows when offsets == nullptr
     const int32_t *offsets;   // [E+1] or nullptr
     const uint16_t *A;        // [rows, K]
+    const int32_t *a_rows;    // optional row indirection into A: row a_rows[r] / a_div
+    int a_div;
     int K;
     const uint16_t *B0, *B1;  // [G, N, K]: gate/up (dual) or down
     int N;                    // output columns (I for gate/up, d for down)
@@ -124,12 +126,13 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
         const int row = (tid >> 3) + 32 * i;
         int ar = m0 + row;
         ar = ar < m_end ? ar : m_end - 1;
-        aoff[i] = (uint32_t)(ar - m0) * (uint32_t)K + c16 * 8;
+        if (p.a_rows) ar = p.a_rows[ar] / p.a_div;
+        aoff[i] = (uint32_t)ar * (uint32_t)K + c16 * 8;
         const int br = DUAL ? n0 + (row & 63) : n0 + row;
         boff[i] = (uint32_t)br * (uint32_t)K + c16 * 8;
         soff[i] = row * BK + swz(row, c16) * 8;
     }
-    const uint16_t *Ab = p.A + (size_t)m0 * K;
+    const uint16_t *Ab = p.A;
 
     f32x16 acc[2][NT];
 #pragma unroll
@@ -244,13 +247,14 @@ __device__ __forceinline__ int expert_of_row(const int32_t *__restrict__ offsets
 
 // h[row, n] = silu(a_row . Wg[e, n]) * (a_row . Wu[e, n])
 __global__ __launch_bounds__(256) void k_f32_gateup(int M, int d, int I, const int32_t *__restrict__ offsets,
-                                                    const float *__restrict__ a, const float *__restrict__ wg,
+                                                    const float *__restrict__ a, const int32_t *__restrict__ a_rows,
+                                                    int a_div, const float *__restrict__ wg,
                                                     const float *__restrict__ wu, float *__restrict__ h) {
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int n = blockIdx.y * 64 + (threadIdx.x & 63);
     if (row >= M || n >= I) return;
     const int e = offsets ? expert_of_row(offsets, row) : 0;
-    const float *x = a + (size_t)row * d;
+    const float *x = a + (size_t)(a_rows ? a_rows[row] / a_div : row) * d;
     const float *g = wg + ((size_t)e * I + n) * d;
     const float *u = wu + ((size_t)e * I + n) * d;
     float sg = 0.f, su = 0.f;
@@ -291,7 +295,7 @@ hipError_t launch_ffn(const FfnArgs &a, hipStream_t s) {
         dim3 g1((a.M + 3) / 4, (a.I + 63) / 64), g2((a.M + 3) / 4, (a.d + 63) / 64);
         if (a.phases & 1)
             hipLaunchKernelGGL(k_f32_gateup, g1, dim3(256), 0, s, a.M, a.d, a.I, a.offsets,
-                               static_cast<const float *>(a.a), static_cast<const float *>(a.w.gate),
+                               static_cast<const float *>(a.a), a.a_rows, a.a_div, static_cast<const float *>(a.w.gate),
                                static_cast<const float *>(a.w.up), static_cast<float *>(a.h));
         if (a.phases & 2)
             hipLaunchKernelGGL(k_f32_down, g2, dim3(256), 0, s, a.M, a.d, a.I, a.offsets,
@@ -307,6 +311,8 @@ hipError_t launch_ffn(const FfnArgs &a, hipStream_t s) {
         p.M = a.M;
         p.offsets = a.offsets;
         p.A = static_cast<const uint16_t *>(a.a);
+        p.a_rows = a.a_rows;
+        p.a_div = a.a_div;
         p.K = a.d;
         p.B0 = static_cast<const uint16_t *>(a.w.gate);
         p.B1 = static_cast<const uint16_t *>(a.w.up);

@@ -61,6 +61,8 @@ struct LargeParams {
     int M;
     const int32_t *offsets;
     const uint16_t *A;
+    const int32_t *a_rows;  // optional row indirection into A: row a_rows[r] / a_div
+    int a_div;
     int K;
     const uint16_t *B0, *B1;
     int N;
@@ -218,7 +220,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
         }
         const int n0 = nt * BN;
 
-        const uint16_t *Ab = p.A + (size_t)m0 * K;
         const uint16_t *Bg = p.B0 + (size_t)e * p.N * K;
         const uint16_t *Bu = DUAL ? p.B1 + (size_t)e * p.N * K : Bg;
         const uint16_t *asrc[8], *bsrc[8];
@@ -226,7 +227,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
         for (int i = 0; i < 8; ++i) {
             int ar = m0 + drow[i];
             ar = ar < m_end ? ar : m_end - 1;
-            asrc[i] = Ab + (size_t)(ar - m0) * K + dcol[i];
+            if (p.a_rows) ar = p.a_rows[ar] / p.a_div;
+            asrc[i] = p.A + (size_t)ar * K + dcol[i];
             const int r = drow[i];
             const uint16_t *Bm = (DUAL && r >= BN) ? Bu : Bg;
             const int br = DUAL ? n0 + (r & (BN - 1)) : n0 + r;
@@ -465,6 +467,8 @@ hipError_t launch_ffn_bf16_large(const FfnArgs &a, hipStream_t s) {
         p.M = a.M;
         p.offsets = a.offsets;
         p.A = static_cast<const uint16_t *>(a.a);
+        p.a_rows = a.a_rows;
+        p.a_div = a.a_div;
         p.K = a.d;
         p.B0 = static_cast<const uint16_t *>(a.w.gate);
         p.B1 = static_cast<const uint16_t *>(a.w.up);

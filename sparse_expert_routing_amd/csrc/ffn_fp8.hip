@@ -35,6 +35,8 @@ struct Fp8Params {
     const int32_t *offsets;
     const uint8_t *A;        // [rows, K] codes
     const float *As;         // [rows, K/128]
+    const int32_t *a_rows;   // optional row indirection into A / As: row a_rows[r] / a_div
+    int a_div;
     int K;
     const uint8_t *B0, *B1;  // [G, N, K] codes
     const float *S0, *S1;    // [G, N/128, K/128]
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(Fp8Params p) {
     const int K = p.K, nkb = K / BK;
     const int c16 = tid & 7;
 
-    const uint8_t *Ab = p.A + (size_t)m0 * K;
+    const uint8_t *Ab = p.A;
     const uint8_t *Bg = p.B0 + (size_t)e * p.N * K;
     const uint8_t *Bu = DUAL ? p.B1 + (size_t)e * p.N * K : Bg;
     const float *Sg = p.S0 + ((size_t)e * (p.N / 128) + n0 / 128) * nkb;
@@ -136,7 +138,8 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(Fp8Params p) {
         const int row = (tid >> 3) + 32 * i;
         int ar = m0 + row;
         ar = ar < m_end ? ar : m_end - 1;
-        aoff[i] = (uint32_t)(ar - m0) * (uint32_t)K + c16 * 16;
+        if (p.a_rows) ar = p.a_rows[ar] / p.a_div;
+        aoff[i] = (uint32_t)ar * (uint32_t)K + c16 * 16;
         soffa[i] = row * BK + swz(row, c16) * 16;
     }
 #pragma unroll
@@ -149,6 +152,7 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(Fp8Params p) {
     // activation scale staging: threads 0..127, one row each
     int as_row = m0 + (tid & (BM - 1));
     as_row = as_row < m_end ? as_row : m_end - 1;
+    if (p.a_rows) as_row = p.a_rows[as_row] / p.a_div;
     const float *asp = p.As + (size_t)as_row * nkb;
 
     f32x16 acc[2][NJ];
@@ -296,6 +300,8 @@ hipError_t launch_ffn_fp8(const FfnArgs &a, hipStream_t s) {
     p.offsets = a.offsets;
     p.A = static_cast<const uint8_t *>(a.a);
     p.As = a.a_scale;
+    p.a_rows = a.a_rows;
+    p.a_div = a.a_div;
     p.K = a.d;
     p.B0 = static_cast<const uint8_t *>(a.w.gate);
     p.B1 = static_cast<const uint8_t *>(a.w.up);

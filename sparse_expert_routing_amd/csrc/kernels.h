@@ -27,7 +27,7 @@ struct DispatchArgs {
     const int32_t *idx;
     const void *x;
     int32_t *counts, *offsets, *row_src, *row_of;
-    void *x_perm;
+    void *x_perm;         // null: no gather (counts, offsets, row_src, row_of only)
     float *x_perm_scale;
     int32_t *block_base;  // workspace [ceil(T/256), E]
 };
@@ -49,8 +49,10 @@ struct FfnArgs {
     int d, I, E;      // E groups when offsets != nullptr
     int wt;           // kF32, kBF16, kE4M3
     const int32_t *offsets;
-    const void *a;    // [M, d] rows in wt type
-    const float *a_scale;  // e4m3: [M, d/128]
+    const void *a;    // [M, d] rows in wt type (or [*, d] rows picked by a_rows)
+    const float *a_scale;  // e4m3: [M, d/128] (row-aligned with a)
+    const int32_t *a_rows;  // optional: A row r of the GEMM is row a_rows[r] / a_div of a / a_scale
+    int a_div;
     FfnWeights w;
     void *h;          // workspace [M, I] in wt type
     float *h_scale;   // e4m3: [M, I/128]

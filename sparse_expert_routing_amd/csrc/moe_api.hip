@@ -47,16 +47,19 @@ FfnWs ffn_ws(int rows, const moe_desc_t *d) {
     return w;
 }
 
+// The routed FFN stage: h (+ its scales) for T*k rows, and for e4m3 room for
+// x quantised once per token (moe_expert_gate_up_rows).
+size_t xq_bytes(const moe_desc_t *d) {
+    return d->wt == MOE_E4M3 ? align_up((size_t)d->T * d->d) + align_up((size_t)d->T * (d->d / 128) * sizeof(float)) : 0;
+}
+size_t routed_ffn_ws(const moe_desc_t *d) { return ffn_ws(d->T * d->k, d).total + xq_bytes(d); }
+
 size_t dispatch_ws(const moe_desc_t *d) {
     const size_t nblk = (d->T + moe::kDispatchBlock - 1) / moe::kDispatchBlock;
     return align_up(nblk * d->E * sizeof(int32_t));
 }
 
-size_t combine_ws(const moe_desc_t *d) {
-    size_t t = ffn_ws(d->T, d).total;
-    if (d->wt == MOE_E4M3) t += align_up((size_t)d->T * d->d) + align_up((size_t)d->T * (d->d / 128) * sizeof(float));
-    return t;
-}
+size_t combine_ws(const moe_desc_t *d) { return ffn_ws(d->T, d).total + xq_bytes(d); }
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
@@ -89,7 +92,7 @@ size_t moe_workspace_bytes(const moe_desc_t *d, int32_t stage) {
     if (check_desc(d) != MOE_OK) return 0;
     switch (stage) {
         case MOE_WS_DISPATCH: return dispatch_ws(d);
-        case MOE_WS_FFN: return ffn_ws(d->T * d->k, d).total;
+        case MOE_WS_FFN: return routed_ffn_ws(d);
         case MOE_WS_COMBINE: return combine_ws(d);
     }
     return 0;
@@ -109,25 +112,39 @@ moe_status_t moe_dispatch(const moe_desc_t *d, const int32_t *idx, const void *x
                           float *x_perm_scale, void *workspace, size_t ws_bytes, void *stream) {
     moe_status_t st = check_desc(d);
     if (st != MOE_OK) return st;
-    if (!idx || !x || !counts || !offsets || !row_src || !row_of || !x_perm) return MOE_EINVAL;
-    if (d->wt == MOE_E4M3 && !x_perm_scale) return MOE_EINVAL;
+    if (!idx || !counts || !offsets || !row_src || !row_of) return MOE_EINVAL;
+    if (x_perm && (!x || (d->wt == MOE_E4M3 && !x_perm_scale))) return MOE_EINVAL;
     if (!workspace || ws_bytes < dispatch_ws(d)) return MOE_EWORKSPACE;
     moe::DispatchArgs a{d->T, d->d, d->E, d->k, d->act, d->wt, idx, x, counts, offsets, row_src, row_of,
                         x_perm, x_perm_scale, static_cast<int32_t *>(workspace)};
     return hip_status(moe::launch_dispatch(a, static_cast<hipStream_t>(stream)));
 }
 
+// a_rows == nullptr: A = x_perm (+ x_perm_scale), one row per routed row.
+// a_rows != nullptr: A row r is row a_rows[r] / k of x (T rows; quantised into the
+// workspace first for e4m3).
 static moe_status_t expert_ffn_phases(const moe_desc_t *d, const void *x_perm, const float *x_perm_scale,
-                                      const int32_t *offsets, const moe_ffn_weights_t *experts, void *y_perm,
-                                      void *workspace, size_t ws_bytes, void *stream, int phases) {
+                                      const int32_t *a_rows, const int32_t *offsets,
+                                      const moe_ffn_weights_t *experts, void *y_perm, void *workspace,
+                                      size_t ws_bytes, void *stream, int phases) {
     moe_status_t st = check_desc(d);
     if (st != MOE_OK) return st;
     if (!offsets || !ffn_weights_ok(experts, d->wt)) return MOE_EINVAL;
-    if ((phases & 1) && (!x_perm || (d->wt == MOE_E4M3 && !x_perm_scale))) return MOE_EINVAL;
+    if ((phases & 1) && (!x_perm || (d->wt == MOE_E4M3 && !a_rows && !x_perm_scale))) return MOE_EINVAL;
     if ((phases & 2) && !y_perm) return MOE_EINVAL;
     const FfnWs w = ffn_ws(d->T * d->k, d);
-    if (!workspace || ws_bytes < w.total) return MOE_EWORKSPACE;
+    if (!workspace || ws_bytes < routed_ffn_ws(d)) return MOE_EWORKSPACE;
     char *ws = static_cast<char *>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (a_rows && d->wt == MOE_E4M3 && (phases & 1)) {
+        char *xq = ws + w.total;
+        float *xs = reinterpret_cast<float *>(xq + align_up((size_t)d->T * d->d));
+        hipError_t e = moe::launch_quant_rows_e4m3(d->T, d->d, static_cast<const uint16_t *>(x_perm),
+                                                   reinterpret_cast<uint8_t *>(xq), xs, s);
+        if (e != hipSuccess) return MOE_EHIP;
+        x_perm = xq;
+        x_perm_scale = xs;
+    }
     moe::FfnArgs a{};
     a.M = d->T * d->k;
     a.d = d->d;
@@ -137,6 +154,8 @@ static moe_status_t expert_ffn_phases(const moe_desc_t *d, const void *x_perm, c
     a.offsets = offsets;
     a.a = x_perm;
     a.a_scale = x_perm_scale;
+    a.a_rows = a_rows;
+    a.a_div = d->k;
     a.w = to_internal(experts);
     a.h = ws;
     a.h_scale = w.h_scale ? reinterpret_cast<float *>(ws + w.h) : nullptr;
@@ -144,24 +163,34 @@ static moe_status_t expert_ffn_phases(const moe_desc_t *d, const void *x_perm, c
     a.phases = phases;
     a.combine = false;
     a.k = d->k;
-    return hip_status(moe::launch_ffn(a, static_cast<hipStream_t>(stream)));
+    return hip_status(moe::launch_ffn(a, s));
 }
 
 moe_status_t moe_expert_ffn(const moe_desc_t *d, const void *x_perm, const float *x_perm_scale,
                             const int32_t *offsets, const moe_ffn_weights_t *experts, void *y_perm,
                             void *workspace, size_t ws_bytes, void *stream) {
-    return expert_ffn_phases(d, x_perm, x_perm_scale, offsets, experts, y_perm, workspace, ws_bytes, stream, 3);
+    return expert_ffn_phases(d, x_perm, x_perm_scale, nullptr, offsets, experts, y_perm, workspace, ws_bytes,
+                             stream, 3);
 }
 
 moe_status_t moe_expert_gate_up(const moe_desc_t *d, const void *x_perm, const float *x_perm_scale,
                                 const int32_t *offsets, const moe_ffn_weights_t *experts, void *workspace,
                                 size_t ws_bytes, void *stream) {
-    return expert_ffn_phases(d, x_perm, x_perm_scale, offsets, experts, nullptr, workspace, ws_bytes, stream, 1);
+    return expert_ffn_phases(d, x_perm, x_perm_scale, nullptr, offsets, experts, nullptr, workspace, ws_bytes,
+                             stream, 1);
+}
+
+moe_status_t moe_expert_gate_up_rows(const moe_desc_t *d, const void *x, const int32_t *row_src,
+                                     const int32_t *offsets, const moe_ffn_weights_t *experts, void *workspace,
+                                     size_t ws_bytes, void *stream) {
+    if (!row_src) return MOE_EINVAL;
+    return expert_ffn_phases(d, x, nullptr, row_src, offsets, experts, nullptr, workspace, ws_bytes, stream, 1);
 }
 
 moe_status_t moe_expert_down(const moe_desc_t *d, const int32_t *offsets, const moe_ffn_weights_t *experts,
                              void *y_perm, void *workspace, size_t ws_bytes, void *stream) {
-    return expert_ffn_phases(d, nullptr, nullptr, offsets, experts, y_perm, workspace, ws_bytes, stream, 2);
+    return expert_ffn_phases(d, nullptr, nullptr, nullptr, offsets, experts, y_perm, workspace, ws_bytes, stream,
+                             2);
 }
 
 moe_status_t moe_combine(const moe_desc_t *d, const void *x, const moe_ffn_weights_t *shared,

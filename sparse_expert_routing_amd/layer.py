@@ -47,22 +47,37 @@ class MoeLayer:
         self.offsets = torch.empty(E + 1, **i32)
         self.row_src = torch.empty(A, **i32)
         self.row_of = torch.empty(A, **i32)
-        gin = _TORCH_STORAGE[self.wt]
-        self.x_perm = torch.empty((A, d), dtype=gin, device=dev)
-        self.x_perm_scale = (torch.empty((A, d // 128), dtype=torch.float32, device=dev)
-                             if self.wt == "e4m3" else None)
+        self.x_perm = self.x_perm_scale = None  # allocated on first use of the materialised dispatch
         self.y_perm = torch.empty((A, d), dtype=torch.float32 if self.wt == "f32" else torch.int16, device=dev)
         self.y = torch.empty((T, d), dtype=torch.float32, device=dev)
         ws = max(_lib.workspace_bytes(self.desc, s) for s in (0, 1, 2))
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
 
-    def forward(self, x, bias, gap=False, stream=None):
+    def ensure_x_perm(self):
+        if self.x_perm is None:
+            A, d = self.T * self.k, self.d
+            self.x_perm = torch.empty((A, d), dtype=_TORCH_STORAGE[self.wt], device=self.device)
+            self.x_perm_scale = (torch.empty((A, d // 128), dtype=torch.float32, device=self.device)
+                                 if self.wt == "e4m3" else None)
+
+    def forward(self, x, bias, gap=False, stream=None, gather_in_gemm=True):
+        """One pass of the layer.  gather_in_gemm: the gate/up GEMM reads the
+        token rows through row_src (no x_perm); otherwise moe_dispatch
+        materialises x_perm and moe_expert_ffn consumes it.  Both give the
+        same y bit for bit."""
         D = self.desc
         _lib.moe_route(D, x, self.wr, bias, self.idx, self.w, self.gap if gap else None, stream)
-        _lib.moe_dispatch(D, self.idx, x, self.counts, self.offsets, self.row_src, self.row_of, self.x_perm,
-                          self.x_perm_scale, self.ws, stream)
-        _lib.moe_expert_ffn(D, self.x_perm, self.x_perm_scale, self.offsets, self.ex_w, self.y_perm, self.ws,
-                            stream)
+        if gather_in_gemm:
+            _lib.moe_dispatch(D, self.idx, x, self.counts, self.offsets, self.row_src, self.row_of, None, None,
+                              self.ws, stream)
+            _lib.moe_expert_gate_up_rows(D, x, self.row_src, self.offsets, self.ex_w, self.ws, stream)
+            _lib.moe_expert_down(D, self.offsets, self.ex_w, self.y_perm, self.ws, stream)
+        else:
+            self.ensure_x_perm()
+            _lib.moe_dispatch(D, self.idx, x, self.counts, self.offsets, self.row_src, self.row_of, self.x_perm,
+                              self.x_perm_scale, self.ws, stream)
+            _lib.moe_expert_ffn(D, self.x_perm, self.x_perm_scale, self.offsets, self.ex_w, self.y_perm, self.ws,
+                                stream)
         _lib.moe_combine(D, x, self.sh_w, self.y_perm, self.row_of, self.w, self.y, self.ws, stream)
         return self.y
 

@@ -99,6 +99,21 @@ def test_layer_config2_ragged_T():
     check_layer(cfg, inp, n_sample=48)
 
 
+@pytest.mark.parametrize("cid,over", [(1, {}), (2, {"T": 777}), (5, {"T": 600, "d": 1024, "I": 256}),
+                                      (4, {"T": 2048, "d": 1024, "I": 256})])
+def test_layer_gather_in_gemm_equals_materialised(cid, over):
+    """The default forward (gate/up gathers through row_src) and the one over
+    a materialised x_perm give the same y bit for bit."""
+    cfg = synth.CONFIGS[cid].with_(**over) if over else synth.CONFIGS[cid]
+    say(f"[layer] {cfg.name}: gathered vs materialised x_perm")
+    inp = synth.make_inputs(cfg)
+    layer = layer_from_inputs(inp)
+    x, b = upload(inp["x"]), upload(inp["bias"])
+    y1 = host(layer.forward(x, b, gather_in_gemm=True)).copy()
+    y2 = host(layer.forward(x, b, gather_in_gemm=False))
+    assert np.array_equal(y1, y2)
+
+
 def test_layer_config3_decode_bf16():
     cfg = synth.CONFIGS[3]
     inp = synth.make_inputs(cfg)

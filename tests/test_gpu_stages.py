@@ -219,6 +219,62 @@ def test_expert_ffn_config2_sampled_rows():
     assert err <= TOL["bf16"], err
 
 
+# ------------------------------------- the dispatch gather folded into the GEMM
+
+@pytest.mark.parametrize("T", [1, 257, 4096])
+def test_dispatch_bookkeeping_only(T):
+    """x_perm = NULL: counts, offsets, row_src, row_of as the oracle's, nothing gathered."""
+    say(f"[dispatch] bookkeeping only T={T}")
+    ds = _lib.desc(T, 512, 256, 8, 128, "bf16", "bf16")
+    idx = ids_case("random", T)
+    counts, offsets = empty(256, torch.int32), empty(257, torch.int32)
+    row_src, row_of = empty(T * 8, torch.int32), empty(T * 8, torch.int32)
+    ws = empty(_lib.workspace_bytes(ds, _lib.MOE_WS_DISPATCH), torch.uint8)
+    moe.moe_dispatch(ds, dev(idx), None, counts, offsets, row_src, row_of, None, None, ws)
+    torch.cuda.synchronize()
+    oc, oo, osrc, oof = oracle.dispatch(idx, 256)
+    assert np.array_equal(host(counts), oc) and np.array_equal(host(offsets), oo)
+    assert np.array_equal(host(row_src), osrc) and np.array_equal(host(row_of), oof)
+
+
+def run_ffn_rows(cfg, offsets, row_src, x, experts):
+    ds = _lib.desc(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, cfg.act, cfg.wt)
+    w = {n: (dev(a) if a is not None else None) for n, a in experts.items()}
+    fw = _lib.ffn_weights(w["gate"], w["up"], w["down"], w["s_gate"], w["s_up"], w["s_down"])
+    y = empty((cfg.T * cfg.k, cfg.d), torch.float32 if cfg.wt == "f32" else torch.int16)
+    ws = empty(_lib.workspace_bytes(ds, _lib.MOE_WS_FFN), torch.uint8)
+    moe.moe_expert_gate_up_rows(ds, dev(x), dev(row_src), dev(offsets), fw, ws)
+    moe.moe_expert_down(ds, dev(offsets), fw, y, ws)
+    torch.cuda.synchronize()
+    return host(y)
+
+
+@pytest.mark.parametrize("wt,T,d,I,kind", [("f32", 40, 256, 128, "random"), ("bf16", 300, 256, 128, "same8"),
+                                           ("bf16", 4096, 512, 256, "skewed"), ("e4m3", 257, 256, 128, "skewed"),
+                                           ("e4m3", 1000, 256, 128, "random")])
+def test_gate_up_rows_matches_materialised(wt, T, d, I, kind):
+    """Gate/up reading the token rows through row_src (no x_perm) gives the
+    same y_perm bit for bit as the GEMM over the materialised x_perm (same
+    rows, same order, same kernels); small-group, large-group (T=4096) and
+    e4m3 (x quantised once per token) paths.  Parity of this path with the
+    oracle is the layer tests' (the layer uses it by default)."""
+    act = "f32" if wt == "f32" else "bf16"
+    cfg = synth.Config("ffn-rows", seed=25, T=T, d=d, I=I, act=act, wt=wt)
+    say(f"[ffn] gathered gate/up {wt} T={T} d={d} I={I} {kind}")
+    experts = synth.make_ffn(cfg, 256, (synth.TID_GATE, synth.TID_UP, synth.TID_DOWN))
+    x = synth.normal(cfg.seed, synth.TID_X, (T, d), 1.0, act)
+    _, offsets, row_src, _ = oracle.dispatch(ids_case(kind, T), 256)
+    tok = row_src // 8
+    if wt == "e4m3":
+        q, s = oracle.quant_e4m3_rows(x, act)
+        a_rows, a_sc = np.ascontiguousarray(q[tok]), np.ascontiguousarray(s[tok])
+    else:
+        a_rows, a_sc = np.ascontiguousarray(x[tok]), None
+    y_mat = run_ffn(cfg, offsets, a_rows, a_sc, experts)
+    y_rows = run_ffn_rows(cfg, offsets, row_src, x, experts)
+    assert np.array_equal(y_mat, y_rows)
+
+
 # ---------------------------------------------------------------- combine
 
 @pytest.mark.parametrize("wt,T", [("f32", 32), ("bf16", 100), ("bf16", 257), ("bf16", 1000), ("e4m3", 100),
