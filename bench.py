@@ -95,7 +95,7 @@ def main():
     def step(bias, ev=None):
         if ev is not None:
             ev[0].record(stream)
-        _lib.moe_route(D, x, layer.wr, bias, layer.idx, layer.w, None, stream)
+        _lib.moe_route(D, x, layer.wr, bias, layer.idx, layer.w, None, layer.ws, stream)
         if ev is not None:
             ev[1].record(stream)
         _lib.moe_dispatch(D, layer.idx, x, layer.counts, layer.offsets, layer.row_src, layer.row_of,

@@ -88,7 +88,7 @@ typedef struct {
 } moe_ffn_weights_t;
 
 /* Workspace stages for moe_workspace_bytes. */
-enum { MOE_WS_DISPATCH = 0, MOE_WS_FFN = 1, MOE_WS_COMBINE = 2 };
+enum { MOE_WS_DISPATCH = 0, MOE_WS_FFN = 1, MOE_WS_COMBINE = 2, MOE_WS_ROUTE = 3 };
 
 /*
  * Router, biased top-k choice and combine weights (DeepSeek V3 From Scratch,
@@ -103,11 +103,15 @@ enum { MOE_WS_DISPATCH = 0, MOE_WS_FFN = 1, MOE_WS_COMBINE = 2 };
  *                    the sum over the k chosen (bias not included)
  *   gap      [T]     fp32 out or NULL: k-th minus (k+1)-th largest biased
  *                    score, as the kernel computed it
- * All scores are computed in fp32 (bf16 x is widened exactly).
+ *   workspace >= moe_workspace_bytes(desc, MOE_WS_ROUTE) bytes of device memory
+ *                    (0 for fp32 activations; NULL allowed then)
+ * All scores are computed in fp32: the logit is an fp32 accumulation of
+ * exact products (bf16 x times the fp32 router split exactly into three bf16
+ * terms, or fp32 x times fp32 w).
  */
 moe_status_t moe_route(const moe_desc_t *desc, const void *x, const float *w_router,
                        const float *bias, int32_t *idx, float *weights, float *gap,
-                       void *stream);
+                       void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * Dispatch: per-expert load, its prefix sum and a stable grouping of the T*k

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = range(5)
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
-MOE_WS_DISPATCH, MOE_WS_FFN, MOE_WS_COMBINE = 0, 1, 2
+MOE_WS_DISPATCH, MOE_WS_FFN, MOE_WS_COMBINE, MOE_WS_ROUTE = 0, 1, 2, 3
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_E4M3}
 
 EXPORTS = ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_gate_up_rows",
@@ -53,7 +53,7 @@ def load(path: str = LIB_PATH):
     vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
     pd = ctypes.POINTER(Desc)
     pw = ctypes.POINTER(FfnWeights)
-    L.moe_route.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_route.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_dispatch.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_expert_ffn.argtypes = [pd, vp, vp, vp, pw, vp, vp, sz, vp]
     L.moe_expert_gate_up.argtypes = [pd, vp, vp, vp, pw, vp, sz, vp]
@@ -102,9 +102,10 @@ def workspace_bytes(ds: Desc, stage: int) -> int:
     return load().moe_workspace_bytes(ctypes.byref(ds), stage)
 
 
-def moe_route(ds, x, w_router, bias, idx, weights, gap=None, stream=None):
+def moe_route(ds, x, w_router, bias, idx, weights, gap=None, workspace=None, stream=None):
+    nb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("moe_route", load().moe_route(ctypes.byref(ds), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(idx),
-                                         _ptr(weights), _ptr(gap), _stream(stream)))
+                                         _ptr(weights), _ptr(gap), _ptr(workspace), nb, _stream(stream)))
 
 
 def moe_dispatch(ds, idx, x, counts, offsets, row_src, row_of, x_perm, x_perm_scale, workspace, stream=None):

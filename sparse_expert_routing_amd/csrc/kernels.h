@@ -18,6 +18,11 @@ struct RouteArgs {
     float *w, *gap;
 };
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
+// bf16 activations: split router + bf16 MFMA logits + top-k (workspace:
+// route_bf16_ws_bytes).
+bool route_bf16_ok(int d);
+size_t route_bf16_ws_bytes(int T, int d);
+hipError_t launch_route_bf16(const RouteArgs &a, void *ws, hipStream_t s);
 
 constexpr int kDispatchBlock = 256;  // tokens per dispatch workgroup
 

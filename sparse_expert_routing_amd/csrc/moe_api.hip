@@ -59,6 +59,10 @@ size_t dispatch_ws(const moe_desc_t *d) {
     return align_up(nblk * d->E * sizeof(int32_t));
 }
 
+size_t route_ws(const moe_desc_t *d) {
+    return d->act == MOE_BF16 && moe::route_bf16_ok(d->d) ? align_up(moe::route_bf16_ws_bytes(d->T, d->d)) : 0;
+}
+
 size_t combine_ws(const moe_desc_t *d) { return ffn_ws(d->T, d).total + xq_bytes(d); }
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
@@ -91,6 +95,7 @@ const char *moe_status_str(moe_status_t s) {
 size_t moe_workspace_bytes(const moe_desc_t *d, int32_t stage) {
     if (check_desc(d) != MOE_OK) return 0;
     switch (stage) {
+        case MOE_WS_ROUTE: return route_ws(d);
         case MOE_WS_DISPATCH: return dispatch_ws(d);
         case MOE_WS_FFN: return routed_ffn_ws(d);
         case MOE_WS_COMBINE: return combine_ws(d);
@@ -99,12 +104,17 @@ size_t moe_workspace_bytes(const moe_desc_t *d, int32_t stage) {
 }
 
 moe_status_t moe_route(const moe_desc_t *d, const void *x, const float *w_router, const float *bias,
-                       int32_t *idx, float *weights, float *gap, void *stream) {
+                       int32_t *idx, float *weights, float *gap, void *workspace, size_t ws_bytes,
+                       void *stream) {
     moe_status_t st = check_desc(d);
     if (st != MOE_OK) return st;
     if (!x || !w_router || !bias || !idx || !weights) return MOE_EINVAL;
+    const size_t need = route_ws(d);
+    if (need && (!workspace || ws_bytes < need)) return MOE_EWORKSPACE;
     moe::RouteArgs a{d->T, d->d, d->act == MOE_BF16, x, w_router, bias, idx, weights, gap};
-    return hip_status(moe::launch_route(a, static_cast<hipStream_t>(stream)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (need) return hip_status(moe::launch_route_bf16(a, workspace, s));
+    return hip_status(moe::launch_route(a, s));
 }
 
 moe_status_t moe_dispatch(const moe_desc_t *d, const int32_t *idx, const void *x, int32_t *counts,

@@ -50,7 +50,7 @@ class MoeLayer:
         self.x_perm = self.x_perm_scale = None  # allocated on first use of the materialised dispatch
         self.y_perm = torch.empty((A, d), dtype=torch.float32 if self.wt == "f32" else torch.int16, device=dev)
         self.y = torch.empty((T, d), dtype=torch.float32, device=dev)
-        ws = max(_lib.workspace_bytes(self.desc, s) for s in (0, 1, 2))
+        ws = max(_lib.workspace_bytes(self.desc, s) for s in (0, 1, 2, 3))
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
 
     def ensure_x_perm(self):
@@ -66,7 +66,7 @@ class MoeLayer:
         materialises x_perm and moe_expert_ffn consumes it.  Both give the
         same y bit for bit."""
         D = self.desc
-        _lib.moe_route(D, x, self.wr, bias, self.idx, self.w, self.gap if gap else None, stream)
+        _lib.moe_route(D, x, self.wr, bias, self.idx, self.w, self.gap if gap else None, self.ws, stream)
         if gather_in_gemm:
             _lib.moe_dispatch(D, self.idx, x, self.counts, self.offsets, self.row_src, self.row_of, None, None,
                               self.ws, stream)

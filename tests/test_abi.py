@@ -41,7 +41,7 @@ def good_desc(**kw):
 
 def call_route(ds, ptrs=True):
     p = ctypes.c_void_p(0x1000) if ptrs else None
-    return _lib.load().moe_route(ctypes.byref(ds), p, p, p, p, p, None, None)
+    return _lib.load().moe_route(ctypes.byref(ds), p, p, p, p, p, None, None, 0, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -60,7 +60,7 @@ def test_null_pointers_rejected():
     assert call_route(good_desc(), ptrs=False) == _lib.MOE_EINVAL
     L = _lib.load()
     ds = good_desc()
-    assert L.moe_route(None, None, None, None, None, None, None, None) == _lib.MOE_EINVAL
+    assert L.moe_route(None, None, None, None, None, None, None, None, 0, None) == _lib.MOE_EINVAL
     assert L.moe_bias_update(ctypes.byref(ds), None, ctypes.c_float(1e-3), None, None) == _lib.MOE_EINVAL
     w = _lib.FfnWeights(0x1000, 0x1000, None, None, None, None)  # missing down
     p = ctypes.c_void_p(0x1000)
@@ -74,6 +74,11 @@ def test_small_workspace_rejected():
     L = _lib.load()
     ds = good_desc()
     p = ctypes.c_void_p(0x1000)
+    need_r = _lib.workspace_bytes(ds, _lib.MOE_WS_ROUTE)
+    assert need_r >= 3 * 256 * 256 * 2 + 64 * 256 * 4  # bf16 router split + fp32 logits
+    assert call_route(ds) == _lib.MOE_EWORKSPACE
+    assert L.moe_route(ctypes.byref(ds), p, p, p, p, p, None, p, need_r - 1, None) == _lib.MOE_EWORKSPACE
+    assert _lib.workspace_bytes(good_desc(act="f32", wt="f32"), _lib.MOE_WS_ROUTE) == 0
     need = _lib.workspace_bytes(ds, _lib.MOE_WS_DISPATCH)
     assert need > 0
     st = L.moe_dispatch(ctypes.byref(ds), p, p, p, p, p, p, p, None, p, need - 1, None)

@@ -33,7 +33,8 @@ def run_route(cfg, x, wr, bias):
     idx = empty((cfg.T, cfg.k), torch.int32)
     w = empty((cfg.T, cfg.k), torch.float32)
     gap = empty(cfg.T, torch.float32)
-    moe.moe_route(ds, dev(x), dev(wr), dev(bias), idx, w, gap)
+    ws = empty(max(_lib.workspace_bytes(ds, _lib.MOE_WS_ROUTE), 256), torch.uint8)
+    moe.moe_route(ds, dev(x), dev(wr), dev(bias), idx, w, gap, ws)
     torch.cuda.synchronize()
     return host(idx), host(w), host(gap)
 
