@@ -138,10 +138,17 @@ __device__ __forceinline__ void wait_vmcnt_lds() {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// One 1 KB block (8 rows of 128 B) of a stage operand, global -> LDS.
-__device__ __forceinline__ void dma_block(const uint16_t *src, uint16_t *lds_block) {
-    __builtin_amdgcn_global_load_lds(static_cast<const void *>(src), (lds_void_t *)(lds_block),
-                                     16, 0, 0);
+// Raw buffer resource over `bytes` bytes at p (gfx9 descriptor word 3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// One 1 KB block (8 rows of 128 B) of a stage operand, global -> LDS
+// (buffer_load_dwordx4 ... lds): the operand's resource and the stage's
+// byte offset live in scalar registers, the lane's byte offset in a fixed
+// VGPR, so a stage's loads need no vector address arithmetic.
+__device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint16_t *lds_block) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(lds_block), 16, voff, soff, 0, 0);
 }
 
 // acc += A_frag x B_frag^T.  TRANS swaps the operands, so the accumulator
@@ -220,19 +227,25 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
         }
         const int n0 = nt * BN;
 
-        const uint16_t *Bg = p.B0 + (size_t)e * p.N * K;
-        const uint16_t *Bu = DUAL ? p.B1 + (size_t)e * p.N * K : Bg;
-        const uint16_t *asrc[8], *bsrc[8];
+        // Operand resources (wave-uniform) and per-lane byte offsets of this
+        // tile's DMA blocks; DMA block i of B comes from the up matrix for
+        // i >= 4 in the SwiGLU tile (rows 128..255 of its B operand).
+        const int eu = __builtin_amdgcn_readfirstlane(e);
+        const uint32_t a_rows_total = p.a_rows ? (uint32_t)(p.M / p.a_div) : (uint32_t)p.M;
+        const __amdgpu_buffer_rsrc_t rA = buf_rsrc(p.A, a_rows_total * (uint32_t)K * 2u);
+        const __amdgpu_buffer_rsrc_t rBg = buf_rsrc(p.B0 + (size_t)eu * p.N * K, (uint32_t)p.N * (uint32_t)K * 2u);
+        const __amdgpu_buffer_rsrc_t rBu =
+            DUAL ? buf_rsrc(p.B1 + (size_t)eu * p.N * K, (uint32_t)p.N * (uint32_t)K * 2u) : rBg;
+        uint32_t aoff[8], boff[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             int ar = m0 + drow[i];
             ar = ar < m_end ? ar : m_end - 1;
             if (p.a_rows) ar = p.a_rows[ar] / p.a_div;
-            asrc[i] = p.A + (size_t)ar * K + dcol[i];
+            aoff[i] = ((uint32_t)ar * (uint32_t)K + (uint32_t)dcol[i]) * 2u;
             const int r = drow[i];
-            const uint16_t *Bm = (DUAL && r >= BN) ? Bu : Bg;
             const int br = DUAL ? n0 + (r & (BN - 1)) : n0 + r;
-            bsrc[i] = Bm + (size_t)br * K + dcol[i];
+            boff[i] = ((uint32_t)br * (uint32_t)K + (uint32_t)dcol[i]) * 2u;
         }
         f32x16 acc[4][4];
 #pragma unroll
@@ -247,11 +260,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
         // in unit j % NUNIT.  Loads past the last stage are clamped to it:
         // they fill units that are never read as that stage, which keeps
         // every load and read unconditional.
-#define UNIT(j) (smem + ((j) % NUNIT) * UNIT_ELEMS)
-#define ISSUE_A(st_, i)                                                                        \
-        dma_block(asrc[i] + min((st_), nk - 1) * LK, UNIT(2 * (st_)) + (wave + 4 * (i)) * 512)
-#define ISSUE_B(st_, i)                                                                        \
-        dma_block(bsrc[i] + min((st_), nk - 1) * LK, UNIT(2 * (st_) + 1) + (wave + 4 * (i)) * 512)
+#define UNIT(u) (smem + (u) * UNIT_ELEMS)
+#define ISSUE_A(st_, i, unit_)                                                                 \
+        dma_buf(rA, aoff[i], (uint32_t)min((st_), nk - 1) * (LK * 2), (unit_) + (wave + 4 * (i)) * 512)
+#define ISSUE_B(st_, i, unit_)                                                                 \
+        dma_buf((DUAL && (i) >= 4) ? rBu : rBg, boff[i], (uint32_t)min((st_), nk - 1) * (LK * 2),     \
+                (unit_) + (wave + 4 * (i)) * 512)
 #define READ_AT(r) (2 * (r))
 #define B_ROW(j) ((DUAL ? (((j) >> 1) * 128 + wn * 64 + ((j) & 1) * 32) : (wn * 128 + (j) * 32)) + (lane & 31))
 
@@ -281,20 +295,20 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
         // Prologue: A_0, B_0, A_1, B_1 in flight; A_0 and B_0 landed for every
         // wave; then the first step's fragments.
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ISSUE_A(0, i);
+        for (int i = 0; i < 8; ++i) ISSUE_A(0, i, UNIT(0));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ISSUE_B(0, i);
+        for (int i = 0; i < 8; ++i) ISSUE_B(0, i, UNIT(1));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ISSUE_A(1, i);
+        for (int i = 0; i < 8; ++i) ISSUE_A(1, i, UNIT(2));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ISSUE_B(1, i);
+        for (int i = 0; i < 8; ++i) ISSUE_B(1, i, UNIT(3));
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         wait_vmcnt_lds<16>();
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         bf16x8 a0[4], b0[4], a1[4], b1[4];
         {
-            const uint16_t *sA = UNIT(0), *sB = UNIT(1);
+            const uint16_t *sA = UNIT(0), *sB = UNIT(1);  // A_0, B_0
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 a0[i] = *reinterpret_cast<const bf16x8 *>(sA + lds_piece(wm * 128 + i * 32 + (lane & 31), g));
@@ -311,12 +325,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
         // units; step 3 streams B_{kt+2} into A_kt's unit, one load per 2
         // MFMAs, and reads stage kt+1's first fragments.  A gets about 1.5
         // stages to arrive, B about one.
+        // u0 = unit of A_kt (2kt mod 5), carried instead of recomputed
+        int u0 = 0;
         for (int kt = 0; kt < nk; ++kt) {
-            const uint16_t *cA = UNIT(2 * kt), *cB = UNIT(2 * kt + 1);
-#define DMA_S0(x) if ((x) == 2 || (x) == 8 || (x) == 14) ISSUE_A(kt + 2, ((x) - 2) / 6)
-#define DMA_S1(x) if ((x) == 4 || (x) == 10) ISSUE_A(kt + 2, 3 + ((x) - 4) / 6)
-#define DMA_S2(x) if ((x) == 0 || (x) == 6 || (x) == 12) ISSUE_A(kt + 2, 5 + (x) / 6)
-#define DMA_S3(x) if (((x) & 1) == 0) ISSUE_B(kt + 2, (x) >> 1)
+            const int u1 = u0 + 1 - (u0 + 1 >= NUNIT ? NUNIT : 0), u2 = u0 + 2 - (u0 + 2 >= NUNIT ? NUNIT : 0);
+            const int u3 = u0 + 3 - (u0 + 3 >= NUNIT ? NUNIT : 0), u4 = u0 + 4 - (u0 + 4 >= NUNIT ? NUNIT : 0);
+            const uint16_t *cA = UNIT(u0), *cB = UNIT(u1);
+            uint16_t *fA = UNIT(u4), *fB = UNIT(u0);  // A_{kt+2}, B_{kt+2}
+#define DMA_S0(x) if ((x) == 2 || (x) == 8 || (x) == 14) ISSUE_A(kt + 2, ((x) - 2) / 6, fA)
+#define DMA_S1(x) if ((x) == 4 || (x) == 10) ISSUE_A(kt + 2, 3 + ((x) - 4) / 6, fA)
+#define DMA_S2(x) if ((x) == 0 || (x) == 6 || (x) == 12) ISSUE_A(kt + 2, 5 + (x) / 6, fA)
+#define DMA_S3(x) if (((x) & 1) == 0) ISSUE_B(kt + 2, (x) >> 1, fB)
             STEP(a0, b0, a1, b1, cA, cB, 2 + g, DMA_S0);
             STEP(a1, b1, a0, b0, cA, cB, 4 + g, DMA_S1);
             STEP(a0, b0, a1, b1, cA, cB, 6 + g, DMA_S2);
@@ -325,8 +344,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
             wait_vmcnt_lds<8>();           // A_{kt+1}, B_{kt+1} landed for this wave
             __builtin_amdgcn_s_barrier();  // ... for all waves; A_kt, B_kt no longer read
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            const uint16_t *nA = UNIT(2 * kt + 2), *nB = UNIT(2 * kt + 3);
+            const uint16_t *nA = UNIT(u2), *nB = UNIT(u3);
             STEP(a1, b1, a0, b0, nA, nB, g, DMA_S3);
+            u0 = u2;
 #undef DMA_S0
 #undef DMA_S1
 #undef DMA_S2
@@ -455,7 +475,12 @@ int cu_count() {
 
 bool ffn_bf16_large_ok(const FfnArgs &a) {
     const int groups = a.offsets ? a.E : 1;
-    return (long long)a.M >= 128LL * groups && a.I % 128 == 0 && a.d % 256 == 0 && a.d % LK == 0 &&
+    // DMA offsets are 32-bit bytes from each operand's base (A rows, h rows,
+    // one expert's weights)
+    const unsigned long long lim = 1ULL << 32;
+    const bool fits = (unsigned long long)a.M * a.d * 2 < lim && (unsigned long long)a.M * a.I * 2 < lim &&
+                      (unsigned long long)a.I * a.d * 2 < lim;
+    return fits && (long long)a.M >= 128LL * groups && a.I % 128 == 0 && a.d % 256 == 0 && a.d % LK == 0 &&
            a.I % LK == 0;
 }
 
