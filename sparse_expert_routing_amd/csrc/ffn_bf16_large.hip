@@ -137,10 +137,20 @@ __device__ __forceinline__ void wait_vmcnt_lds() {
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 // Raw buffer resource over `bytes` bytes at p (gfx9 descriptor word 3).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// A pointer the caller knows to be wave-uniform, in scalar registers: a
+// buffer resource built from it then needs no per-lane (waterfall) loop.
+__device__ __forceinline__ const void *uniform_ptr(const void *p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const void *>(((uint64_t)hi << 32) | lo);
 }
 
 // One 1 KB block (8 rows of 128 B) of a stage operand, global -> LDS
@@ -181,6 +191,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
     constexpr bool DUAL = EPI == EPI_SWIGLU;
     constexpr bool TRANS = EPI != EPI_COMBINE;  // register epilogue (no LDS staging)
     constexpr int BN = DUAL ? LB / 2 : LB;  // output columns per tile
+    constexpr int kEpiStores = TRANS ? (DUAL ? 32 : 64) : 0;  // buffer stores per lane per register epilogue
     __shared__ __attribute__((aligned(1024))) uint16_t smem[NUNIT * UNIT_ELEMS];  // 160 KB
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -211,42 +222,84 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
         dcol[i] = ((lane & 7) ^ (row & 7) ^ ((row >> 3) & 1)) * 8;
     }
 
-    for (int t = (blockIdx.x & 7) * (P >> 3) + (blockIdx.x >> 3); t < total; t += P) {
-        const int gsz = kGroupM * NT;
-        const int grp = t / gsz, within = t - grp * gsz;
-        const int mfirst = grp * kGroupM;
-        const int gm = min(kGroupM, Mt - mfirst);
-        const int mt = mfirst + within % gm, nt = within / gm;
-        int e, m0, m_end;
-        if (ROUTED) {
-            tilemap_find(tm, mt, e, m0, m_end);
-        } else {
-            e = 0;
-            m0 = mt * LM;
-            m_end = p.M;
-        }
-        const int n0 = nt * BN;
+    // State of the tile about to run (TILE_SETUP): expert, rows, columns,
+    // its B matrices and the per-lane byte offsets of its DMA blocks.
+    int e = 0, m0 = 0, m_end = 0, n0 = 0;
+    const uint32_t a_rows_total = p.a_rows ? (uint32_t)(p.M / p.a_div) : (uint32_t)p.M;
+    const __amdgpu_buffer_rsrc_t rA = buf_rsrc(p.A, a_rows_total * (uint32_t)K * 2u);
+    const uint32_t b_bytes = (uint32_t)p.N * (uint32_t)K * 2u;  // one expert's B matrix
+    const uint16_t *pBg = p.B0, *pBu = p.B1;                     // the tile's expert
+    uint32_t aoff[8], boff[8];
 
-        // Operand resources (wave-uniform) and per-lane byte offsets of this
-        // tile's DMA blocks; DMA block i of B comes from the up matrix for
-        // i >= 4 in the SwiGLU tile (rows 128..255 of its B operand).
-        const int eu = __builtin_amdgcn_readfirstlane(e);
-        const uint32_t a_rows_total = p.a_rows ? (uint32_t)(p.M / p.a_div) : (uint32_t)p.M;
-        const __amdgpu_buffer_rsrc_t rA = buf_rsrc(p.A, a_rows_total * (uint32_t)K * 2u);
-        const __amdgpu_buffer_rsrc_t rBg = buf_rsrc(p.B0 + (size_t)eu * p.N * K, (uint32_t)p.N * (uint32_t)K * 2u);
-        const __amdgpu_buffer_rsrc_t rBu =
-            DUAL ? buf_rsrc(p.B1 + (size_t)eu * p.N * K, (uint32_t)p.N * (uint32_t)K * 2u) : rBg;
-        uint32_t aoff[8], boff[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            int ar = m0 + drow[i];
-            ar = ar < m_end ? ar : m_end - 1;
-            if (p.a_rows) ar = p.a_rows[ar] / p.a_div;
-            aoff[i] = ((uint32_t)ar * (uint32_t)K + (uint32_t)dcol[i]) * 2u;
-            const int r = drow[i];
-            const int br = DUAL ? n0 + (r & (BN - 1)) : n0 + r;
-            boff[i] = ((uint32_t)br * (uint32_t)K + (uint32_t)dcol[i]) * 2u;
-        }
+    // LDS ring of NUNIT operand units: operand j of the tile's sequence
+    // A_0, B_0, A_1, B_1, ... (A_s / B_s: the A / B slab of stage s) lives
+    // in unit j % NUNIT.  Loads past the last stage are clamped to it:
+    // they fill units that are never read as that stage, which keeps
+    // every load and read unconditional.
+#define UNIT(u) (smem + (u) * UNIT_ELEMS)
+#define ISSUE_A(st_, i, unit_)                                                                 \
+        dma_buf(rA, aoff[i], (uint32_t)min((st_), nk - 1) * (LK * 2), (unit_) + (wave + 4 * (i)) * 512)
+    // ISSUE_B reads rBg_ / rBu_: the B resources of the tile whose loads are
+    // being issued, built once per tile in scalar registers.
+#define B_RSRC()                                                                               \
+        const __amdgpu_buffer_rsrc_t rBg_ = buf_rsrc(uniform_ptr(pBg), b_bytes);               \
+        const __amdgpu_buffer_rsrc_t rBu_ = DUAL ? buf_rsrc(uniform_ptr(pBu), b_bytes) : rBg_;
+#define ISSUE_B(st_, i, unit_)                                                                 \
+        dma_buf((DUAL && (i) >= 4) ? rBu_ : rBg_, boff[i], (uint32_t)min((st_), nk - 1) * (LK * 2), \
+                (unit_) + (wave + 4 * (i)) * 512)
+    // Tile tt -> (e, m0, m_end, n0), B matrices (DMA block i of B comes
+    // from the up matrix for i >= 4 in the SwiGLU tile: rows 128..255 of its
+    // B operand) and DMA offsets.
+#define TILE_SETUP(tt)                                                                         \
+    {                                                                                          \
+        const int gsz_ = kGroupM * NT;                                                         \
+        const int grp_ = (tt) / gsz_, within_ = (tt) - grp_ * gsz_;                            \
+        const int mfirst_ = grp_ * kGroupM;                                                    \
+        const int gm_ = min(kGroupM, Mt - mfirst_);                                            \
+        const int mt_ = mfirst_ + within_ % gm_, nt_ = within_ / gm_;                          \
+        if (ROUTED) {                                                                          \
+            tilemap_find(tm, mt_, e, m0, m_end);                                               \
+        } else {                                                                               \
+            e = 0;                                                                             \
+            m0 = mt_ * LM;                                                                     \
+            m_end = p.M;                                                                       \
+        }                                                                                      \
+        e = __builtin_amdgcn_readfirstlane(e);                                                 \
+        m0 = __builtin_amdgcn_readfirstlane(m0);                                               \
+        m_end = __builtin_amdgcn_readfirstlane(m_end);                                         \
+        n0 = nt_ * BN;                                                                         \
+        pBg = p.B0 + (size_t)e * p.N * K;                                                      \
+        pBu = DUAL ? p.B1 + (size_t)e * p.N * K : pBg;                                         \
+        int ar_[8];                                                                            \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) ar_[i] = min(m0 + drow[i], m_end - 1);    \
+        if (p.a_rows) { /* 8 independent lookups, issued together */                            \
+            _Pragma("unroll") for (int i = 0; i < 8; ++i) ar_[i] = p.a_rows[ar_[i]];            \
+            _Pragma("unroll") for (int i = 0; i < 8; ++i) ar_[i] /= p.a_div;                    \
+        }                                                                                      \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                        \
+            aoff[i] = ((uint32_t)ar_[i] * (uint32_t)K + (uint32_t)dcol[i]) * 2u;               \
+            const int r = drow[i];                                                             \
+            const int br = DUAL ? n0 + (r & (BN - 1)) : n0 + r;                                \
+            boff[i] = ((uint32_t)br * (uint32_t)K + (uint32_t)dcol[i]) * 2u;                   \
+        }                                                                                      \
+    }
+    // A_0, B_0, A_1, B_1 of the tile just set up (32 loads per wave).
+#define PROLOGUE_LOADS()                                                                       \
+    {                                                                                          \
+        B_RSRC()                                                                               \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) ISSUE_A(0, i, UNIT(0));                  \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) ISSUE_B(0, i, UNIT(1));                  \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) ISSUE_A(1, i, UNIT(2));                  \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) ISSUE_B(1, i, UNIT(3));                  \
+    }
+
+    int t = (blockIdx.x & 7) * (P >> 3) + (blockIdx.x >> 3);
+    if (t < total) {
+        TILE_SETUP(t);
+        PROLOGUE_LOADS();
+    }
+    bool first = true;
+    for (; t < total; t += P) {
         f32x16 acc[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -255,17 +308,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-        // LDS ring of NUNIT operand units: operand j of the tile's sequence
-        // A_0, B_0, A_1, B_1, ... (A_s / B_s: the A / B slab of stage s) lives
-        // in unit j % NUNIT.  Loads past the last stage are clamped to it:
-        // they fill units that are never read as that stage, which keeps
-        // every load and read unconditional.
-#define UNIT(u) (smem + (u) * UNIT_ELEMS)
-#define ISSUE_A(st_, i, unit_)                                                                 \
-        dma_buf(rA, aoff[i], (uint32_t)min((st_), nk - 1) * (LK * 2), (unit_) + (wave + 4 * (i)) * 512)
-#define ISSUE_B(st_, i, unit_)                                                                 \
-        dma_buf((DUAL && (i) >= 4) ? rBu : rBg, boff[i], (uint32_t)min((st_), nk - 1) * (LK * 2),     \
-                (unit_) + (wave + 4 * (i)) * 512)
 #define READ_AT(r) (2 * (r))
 #define B_ROW(j) ((DUAL ? (((j) >> 1) * 128 + wn * 64 + ((j) & 1) * 32) : (wn * 128 + (j) * 32)) + (lane & 31))
 
@@ -281,31 +323,36 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
             AN[(r) & 3] = *reinterpret_cast<const bf16x8 *>((nA) + lds_piece(wm * 128 + ((r) & 3) * 32 + (lane & 31), (cn))); \
         else                                                                                   \
             BN_[(r) & 3] = *reinterpret_cast<const bf16x8 *>((nB) + lds_piece(B_ROW((r) & 3), (cn)));
-#define STEP(AC, BC, AN, BN_, nA, nB, cn, DMA)                                                 \
+#define STEP(AC, BC, AN, BN_, nA, nB, cn, DMA, NB_)                                            \
         _Pragma("unroll") for (int x = 0; x < 16; ++x) {                                       \
             _Pragma("unroll") for (int r = 0; r < 8; ++r)                                      \
                 if (READ_AT(r) == x) { FRAG_READ(r, AN, BN_, nA, nB, cn) }                     \
             __builtin_amdgcn_sched_barrier(0);                                                 \
-            acc[x >> 2][x & 3] = mma<TRANS>(AC[x >> 2], BC[x & 3], acc[x >> 2][x & 3]);         \
+            if ((NB_) > (x >> 2)) /* 32-row blocks wholly past the group's end: no MFMA */       \
+                acc[x >> 2][x & 3] = mma<TRANS>(AC[x >> 2], BC[x & 3], acc[x >> 2][x & 3]);     \
             __builtin_amdgcn_sched_barrier(0);                                                 \
             DMA(x);                                                                            \
             __builtin_amdgcn_sched_barrier(0);                                                 \
         }
 
-        // Prologue: A_0, B_0, A_1, B_1 in flight; A_0 and B_0 landed for every
-        // wave; then the first step's fragments.
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ISSUE_A(0, i, UNIT(0));
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ISSUE_B(0, i, UNIT(1));
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ISSUE_A(1, i, UNIT(2));
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ISSUE_B(1, i, UNIT(3));
+        // A_0, B_0, A_1, B_1 are in flight (issued before the previous tile's
+        // epilogue, or before the loop): wait until A_0 and B_0 landed for
+        // every wave, then read the first step's fragments.  Behind those
+        // loads this wave may have queued the previous register epilogue's
+        // stores (kEpiStores of them, always all issued); memory operations
+        // retire in order, so at most 16 + kEpiStores may remain.
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        wait_vmcnt_lds<16>();
+        if (TRANS && !first)
+            wait_vmcnt_lds<(16 + kEpiStores < 63 ? 16 + kEpiStores : 63)>();
+        else
+            wait_vmcnt_lds<16>();
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        B_RSRC()  // this tile's B resources, for the loads of stages 2..
+        // Rows of this wave's 128 that belong to the group (wave-uniform):
+        // the MFMAs of a 32-row block with none are left out (its loads and
+        // fragment reads still run, keeping the schedule and barriers).
+        const int live = m_end - m0 - wm * 128;
         bf16x8 a0[4], b0[4], a1[4], b1[4];
         {
             const uint16_t *sA = UNIT(0), *sB = UNIT(1);  // A_0, B_0
@@ -325,55 +372,77 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
         // units; step 3 streams B_{kt+2} into A_kt's unit, one load per 2
         // MFMAs, and reads stage kt+1's first fragments.  A gets about 1.5
         // stages to arrive, B about one.
-        // u0 = unit of A_kt (2kt mod 5), carried instead of recomputed
-        int u0 = 0;
-        for (int kt = 0; kt < nk; ++kt) {
-            const int u1 = u0 + 1 - (u0 + 1 >= NUNIT ? NUNIT : 0), u2 = u0 + 2 - (u0 + 2 >= NUNIT ? NUNIT : 0);
-            const int u3 = u0 + 3 - (u0 + 3 >= NUNIT ? NUNIT : 0), u4 = u0 + 4 - (u0 + 4 >= NUNIT ? NUNIT : 0);
-            const uint16_t *cA = UNIT(u0), *cB = UNIT(u1);
-            uint16_t *fA = UNIT(u4), *fB = UNIT(u0);  // A_{kt+2}, B_{kt+2}
+        // The K loop, for NB_ (compile-time) 32-row blocks of this wave that
+        // hold group rows; u0 = unit of A_kt (2kt mod 5), carried.
 #define DMA_S0(x) if ((x) == 2 || (x) == 8 || (x) == 14) ISSUE_A(kt + 2, ((x) - 2) / 6, fA)
 #define DMA_S1(x) if ((x) == 4 || (x) == 10) ISSUE_A(kt + 2, 3 + ((x) - 4) / 6, fA)
 #define DMA_S2(x) if ((x) == 0 || (x) == 6 || (x) == 12) ISSUE_A(kt + 2, 5 + (x) / 6, fA)
 #define DMA_S3(x) if (((x) & 1) == 0) ISSUE_B(kt + 2, (x) >> 1, fB)
-            STEP(a0, b0, a1, b1, cA, cB, 2 + g, DMA_S0);
-            STEP(a1, b1, a0, b0, cA, cB, 4 + g, DMA_S1);
-            STEP(a0, b0, a1, b1, cA, cB, 6 + g, DMA_S2);
-
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            wait_vmcnt_lds<8>();           // A_{kt+1}, B_{kt+1} landed for this wave
-            __builtin_amdgcn_s_barrier();  // ... for all waves; A_kt, B_kt no longer read
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            const uint16_t *nA = UNIT(u2), *nB = UNIT(u3);
-            STEP(a1, b1, a0, b0, nA, nB, g, DMA_S3);
-            u0 = u2;
+#define KLOOP(NB_)                                                                             \
+        {                                                                                      \
+            int u0 = 0;                                                                        \
+            for (int kt = 0; kt < nk; ++kt) {                                                  \
+                const int u1 = u0 + 1 - (u0 + 1 >= NUNIT ? NUNIT : 0);                         \
+                const int u2 = u0 + 2 - (u0 + 2 >= NUNIT ? NUNIT : 0);                         \
+                const int u3 = u0 + 3 - (u0 + 3 >= NUNIT ? NUNIT : 0);                         \
+                const int u4 = u0 + 4 - (u0 + 4 >= NUNIT ? NUNIT : 0);                         \
+                const uint16_t *cA = UNIT(u0), *cB = UNIT(u1);                                 \
+                uint16_t *fA = UNIT(u4), *fB = UNIT(u0); /* A_{kt+2}, B_{kt+2} */              \
+                STEP(a0, b0, a1, b1, cA, cB, 2 + g, DMA_S0, NB_);                              \
+                STEP(a1, b1, a0, b0, cA, cB, 4 + g, DMA_S1, NB_);                              \
+                STEP(a0, b0, a1, b1, cA, cB, 6 + g, DMA_S2, NB_);                              \
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);                                       \
+                wait_vmcnt_lds<8>();          /* A_{kt+1}, B_{kt+1} landed for this wave */    \
+                __builtin_amdgcn_s_barrier(); /* ... for all waves; A_kt, B_kt no longer read */ \
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);                                       \
+                const uint16_t *nA = UNIT(u2), *nB = UNIT(u3);                                 \
+                STEP(a1, b1, a0, b0, nA, nB, g, DMA_S3, NB_);                                  \
+                u0 = u2;                                                                       \
+            }                                                                                  \
+        }
+        switch (live <= 0 ? 0 : live >= 128 ? 4 : (live + 31) / 32) {
+            case 4: KLOOP(4) break;
+            case 3: KLOOP(3) break;
+            case 2: KLOOP(2) break;
+            case 1: KLOOP(1) break;
+            default: KLOOP(0) break;
+        }
+#undef KLOOP
 #undef DMA_S0
 #undef DMA_S1
 #undef DMA_S2
 #undef DMA_S3
-        }
 #undef STEP
 #undef FRAG_READ
 #undef READ_AT
 #undef B_ROW
-#undef ISSUE_A
-#undef ISSUE_B
-#undef UNIT
         __syncthreads();  // every wave done with the ring (and its loads landed)
+        first = false;
+        const int cm0 = m0, cm_end = m_end, cn0 = n0;  // this tile, for its epilogue
 
         if constexpr (TRANS) {
+            // The ring is free and this epilogue does not use LDS: start the
+            // next tile's loads first, so they land while the epilogue runs.
+            if (t + P < total) {
+                TILE_SETUP(t + P);
+                PROLOGUE_LOADS();
+            }
             // Register epilogue: lane owns tile rows wm*128 + 32i + (lane & 31)
             // and, per 32-column block, 4 runs of 4 consecutive columns: one
-            // 8-byte bf16 store per run.  Values are computed for every row
-            // (padding rows repeat the group's last row) and only the stores
-            // are predicated, so the epilogue stays one block whose scheduling
-            // barriers bound how many accumulators sit in VGPRs at once.
+            // 8-byte bf16 buffer store per run.  Values are computed for every
+            // row (padding rows repeat the group's last row); a padding row's
+            // stores get an offset past the end of the output resource, which
+            // the hardware drops, so every lane issues every store (the wait
+            // count above relies on it) and the epilogue stays one block whose
+            // scheduling barriers bound how many accumulators sit in VGPRs.
             const int c4 = 4 * g;
+            const __amdgpu_buffer_rsrc_t rOut = buf_rsrc(p.out, (uint32_t)p.M * (uint32_t)p.N * 2u);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int row = m0 + wm * 128 + 32 * i + (lane & 31);
-                const bool ok = row < m_end;
-                uint16_t *orow = p.out + (size_t)(ok ? row : m0) * p.N + n0;
+                const int row = cm0 + wm * 128 + 32 * i + (lane & 31);
+                const uint32_t obase =
+                    row < cm_end ? ((uint32_t)row * (uint32_t)p.N + (uint32_t)cn0) * 2u : 0xfffff000u;
+                const bool blk = cm_end - cm0 - wm * 128 > 32 * i;  // block has rows (uniform)
 #pragma unroll
                 for (int jj = 0; jj < (DUAL ? 2 : 4); ++jj) {
                     __builtin_amdgcn_sched_barrier(0);
@@ -381,18 +450,22 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
                     for (int q = 0; q < 4; ++q) {
                         uint32_t lo, hi;
                         if constexpr (DUAL) {
-                            float h[4];
+                            lo = hi = 0;
+                            if (blk) {  // an empty block's stores are dropped: skip its math
+                                float h[4];
 #pragma unroll
-                            for (int u = 0; u < 4; ++u)
-                                h[u] = swiglu(acc_read(acc[i][jj][4 * q + u]), acc_read(acc[i][2 + jj][4 * q + u]));
-                            lo = pack_bf16x2(h[0], h[1]);
-                            hi = pack_bf16x2(h[2], h[3]);
+                                for (int u = 0; u < 4; ++u)
+                                    h[u] = swiglu(acc_read(acc[i][jj][4 * q + u]), acc_read(acc[i][2 + jj][4 * q + u]));
+                                lo = pack_bf16x2(h[0], h[1]);
+                                hi = pack_bf16x2(h[2], h[3]);
+                            }
                         } else {
                             lo = pack_bf16x2(acc_read(acc[i][jj][4 * q]), acc_read(acc[i][jj][4 * q + 1]));
                             hi = pack_bf16x2(acc_read(acc[i][jj][4 * q + 2]), acc_read(acc[i][jj][4 * q + 3]));
                         }
                         const int col = (DUAL ? wn * 64 : wn * 128) + jj * 32 + 8 * q + c4;
-                        if (ok) *reinterpret_cast<uint2 *>(orow + col) = make_uint2(lo, hi);
+                        __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)lo, (int)hi}, rOut,
+                                                                   obase + (uint32_t)col * 2u, 0, 0);
                     }
                 }
             }
@@ -424,8 +497,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
 #pragma unroll 2
                 for (int it = 0; it < 8; ++it) {
                     const int rl = wave * 16 + 2 * it + g;
-                    const int row = m0 + c * kChRows + rl;
-                    if (row < m_end) {
+                    const int row = cm0 + c * kChRows + rl;
+                    if (row < cm_end) {
                         int rof[8];
                         float wj[8];
 #pragma unroll
@@ -436,7 +509,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
                         i32x4 yv[8];
 #pragma unroll
                         for (int j = 0; j < 8; ++j)
-                            yv[j] = *reinterpret_cast<const i32x4 *>(p.y_perm + (size_t)rof[j] * p.N + n0 + cl);
+                            yv[j] = *reinterpret_cast<const i32x4 *>(p.y_perm + (size_t)rof[j] * p.N + cn0 + cl);
                         const float *cr = ch + rl * kChLd + cl;
                         const f32x4 s0 = *reinterpret_cast<const f32x4 *>(cr);
                         const f32x4 s1 = *reinterpret_cast<const f32x4 *>(cr + 4);
@@ -448,15 +521,26 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
                                 v[2 * u] += wj[j] * bf16_to_f32((uint32_t)yv[j][u] & 0xffffu);
                                 v[2 * u + 1] += wj[j] * bf16_to_f32((uint32_t)yv[j][u] >> 16);
                             }
-                        float *yo = p.yout + (size_t)row * p.N + n0 + cl;
+                        float *yo = p.yout + (size_t)row * p.N + cn0 + cl;
                         *reinterpret_cast<f32x4 *>(yo) = f32x4{v[0], v[1], v[2], v[3]};
                         *reinterpret_cast<f32x4 *>(yo + 4) = f32x4{v[4], v[5], v[6], v[7]};
                     }
                 }
                 __syncthreads();
             }
+            // LDS free again: the next tile's loads
+            if (t + P < total) {
+                TILE_SETUP(t + P);
+                PROLOGUE_LOADS();
+            }
         }
     }
+#undef TILE_SETUP
+#undef PROLOGUE_LOADS
+#undef B_RSRC
+#undef ISSUE_A
+#undef ISSUE_B
+#undef UNIT
 }
 
 int cu_count() {
