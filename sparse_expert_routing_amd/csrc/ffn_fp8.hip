@@ -275,16 +275,10 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(Fp8Params p) {
                 for (int j = 0; j < NJ; ++j) {
                     const int col = n0 + wn * 64 + j * 32 + (lane & 31);
                     const float v = acc[i][j][r];
-                    if (EPI == EPI_STORE) {
+                    if (EPI == EPI_STORE)
                         p.out[(size_t)row * p.N + col] = (uint16_t)f32_to_bf16(v);
-                    } else {
-                        float y = v;
-                        for (int jj = 0; jj < p.k; ++jj) {
-                            const size_t f = (size_t)row * p.k + jj;
-                            y += p.cw[f] * bf16_to_f32(p.y_perm[(size_t)p.row_of[f] * p.N + col]);
-                        }
-                        p.yout[(size_t)row * p.N + col] = y;
-                    }
+                    else  // the shared expert's fp32 output; the routed sum is added by k_combine_add
+                        p.yout[(size_t)row * p.N + col] = v;
                 }
             }
     }
@@ -328,6 +322,10 @@ hipError_t launch_ffn_fp8(const FfnArgs &a, hipStream_t s) {
         q.cw = a.cw;
         q.k = a.k;
         hipLaunchKernelGGL(k_gemm_fp8<EPI_COMBINE>, dim3(slots, a.d / BN), dim3(256), 0, s, q);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_combine_add(a.M, a.d, a.k, static_cast<const uint16_t *>(a.y_perm), a.row_of, a.cw,
+                                  static_cast<float *>(a.y), s);
     } else {
         q.out = static_cast<uint16_t *>(a.y);
         hipLaunchKernelGGL(k_gemm_fp8<EPI_STORE>, dim3(slots, a.d / BN), dim3(256), 0, s, q);

@@ -73,6 +73,9 @@ struct FfnArgs {
     const float *cw;
 };
 hipError_t launch_ffn(const FfnArgs &a, hipStream_t s);
+// y[t] += sum_{j<k} cw[t*k+j] * y_perm[row_of[t*k+j]] (bf16 rows, fp32, ascending j).
+hipError_t launch_combine_add(int T, int d, int k, const uint16_t *y_perm, const int32_t *row_of, const float *cw,
+                              float *y, hipStream_t s);
 hipError_t launch_ffn_fp8(const FfnArgs &a, hipStream_t s);
 // Large-group bf16 path (persistent 256x256 tiles): usable when every group
 // averages at least 128 rows and the widths tile evenly.
