@@ -26,13 +26,21 @@ FLAGS = [
 ]
 
 
+# Per-file extra flags.  The fp8 large-tile GEMM folds each MFMA partial into
+# its accumulator with vector-ALU work, so its MFMAs must write VGPRs (the
+# partials), not AGPRs (which hold the accumulators).
+FILE_FLAGS = {
+    "ffn_fp8_large.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

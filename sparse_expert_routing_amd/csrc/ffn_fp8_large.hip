@@ -1,0 +1,551 @@
+// Grouped SwiGLU expert GEMMs in OCP fp8 e4m3 with fine-grained scales, for
+// large groups (prefill): persistent workgroups, 256x256 tiles.
+//
+// crackai.dev DeepSeek-V3 summary, "How It Works": FP8 matmuls with a scale
+// per tile and FP32 accumulation at chosen points; DeepSeek V3 From Scratch,
+// "The idea": fine-grained quantisation tiles.  Tile shapes (ours, as in the
+// rest of the library): one fp32 scale per 1x128 activation tile and per
+// 128x128 weight block; partial sums are promoted to fp32 every 128 of K.
+//
+// Design for gfx950 (shared with the bf16 large-tile kernel where it can be):
+//   - 4 waves (2x2), each a 128x128 block of the 256x256 tile; the fp32
+//     accumulators (256 per lane) live in AGPRs;
+//   - one stage = 128 of K = one scale block: A and B slabs of 256 rows x
+//     128 bytes (whole L2 lines) in a ring of five 32 KB LDS units filled by
+//     buffer_load_dwordx4 ... lds (scalar resource, fixed per-lane offset,
+//     stage offset in an SGPR); at the start of stage s, after one barrier,
+//     B_{s+1} and A_{s+2} are issued into the two units stage s-1 left, so
+//     B has a stage and A two stages to land;
+//   - a stage's fragments (32 bytes per lane per 32x64 block) are read once
+//     into VGPRs; each 32x32 output block takes two
+//     v_mfma_scale_f32_32x32x64_f8f6f4 (scales 0: plain fp8) into a fresh
+//     VGPR partial, which is folded into its AGPR accumulator scaled by
+//     s_a[row, kb] * s_w[block, kb] (v_accvgpr_read, fma, v_accvgpr_write:
+//     the promotion is vector-ALU work of 3 operations per output element
+//     per 128 of K, the price of fp32 scales that are not powers of two);
+//   - the MFMA operands are swapped, so a lane owns one tile row and runs
+//     of 4 consecutive output columns: per-row activation scales are per
+//     lane, weight scales per wave;
+//   - the activation scales of the next stage are loaded before its slot
+//     loads, so one vmcnt wait per stage covers both;
+//   - epilogues: gate/up forms h = silu(g) * u in fp32 and quantises it per
+//     1x128 tile (the tile's 128 h columns; the row amax is combined across
+//     the two column waves through LDS), scale = amax / 448 (1 for an all-zero
+//     tile), code = e4m3(h / scale); down stores bf16 y_perm, or the shared
+//     expert's fp32 output (the routed sum is added by k_combine_add).
+#include "device.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kE = 256;
+constexpr int LM = 256;      // rows per tile
+constexpr int LB = 256;      // B rows per tile
+constexpr int LK = 128;      // K (bytes) per stage = one scale block
+constexpr int NUNIT = 5;     // LDS ring units (5 x 32 KB)
+constexpr int UNIT_BYTES = LM * LK;
+constexpr int kGroupM = 8;   // row tiles per ordering group
+
+enum { EPI_SWIGLU_Q = 0, EPI_STORE = 1, EPI_F32 = 2 };
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+struct F8Params {
+    int M;
+    const int32_t *offsets;
+    const uint8_t *A;         // [rows, K] codes
+    const float *As;          // [rows, K/128]
+    const int32_t *a_rows;    // optional: GEMM row r reads row a_rows[r] / a_div of A / As
+    int a_div;
+    int K;
+    const uint8_t *B0, *B1;   // [G, N, K] codes
+    const float *S0, *S1;     // [G, N/128, K/128]
+    int N;
+    uint8_t *hq;              // EPI_SWIGLU_Q: [M, H] codes
+    float *hs;                // EPI_SWIGLU_Q: [M, H/128]
+    int H;                    // EPI_SWIGLU_Q: h columns (= N)
+    uint16_t *out;            // EPI_STORE: bf16 [M, N]
+    float *yout;              // EPI_F32: f32 [M, N]
+};
+
+struct TileMap {
+    int off[5];
+    int nt[4];
+    int excl, total;
+};
+
+__device__ __forceinline__ void tilemap_init(TileMap &tm, const int32_t *__restrict__ offsets) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) tm.off[i] = offsets[lane * 4 + i];
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        tm.nt[i] = (tm.off[i + 1] - tm.off[i] + LM - 1) / LM;
+        s += tm.nt[i];
+    }
+    const int incl = wave_incl_scan(s);
+    tm.excl = incl - s;
+    tm.total = __shfl(incl, 63, 64);
+}
+
+__device__ __forceinline__ void tilemap_find(const TileMap &tm, int mt, int &e, int &m0, int &m_end) {
+    const int lane = threadIdx.x & 63;
+    const int mine = tm.nt[0] + tm.nt[1] + tm.nt[2] + tm.nt[3];
+    const bool own = mt >= tm.excl && mt < tm.excl + mine;
+    const int owner = __ffsll((unsigned long long)__ballot(own)) - 1;
+    int my_e = 0, my_m0 = 0, my_end = 0;
+    if (own) {
+        int s = mt - tm.excl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (s >= 0 && s < tm.nt[i]) {
+                my_e = lane * 4 + i;
+                my_m0 = tm.off[i] + s * LM;
+                my_end = tm.off[i + 1];
+            }
+            s -= tm.nt[i];
+        }
+    }
+    e = __shfl(my_e, owner, 64);
+    m0 = __shfl(my_m0, owner, 64);
+    m_end = __shfl(my_end, owner, 64);
+}
+
+// Byte offset, inside one operand unit, of the 16-byte piece c (K bytes
+// 16c .. 16c+15) of tile row `row`: the same XOR swizzle as the bf16 kernel.
+__device__ __forceinline__ int piece(int row, int c) {
+    return row * LK + ((c ^ (row & 7) ^ ((row >> 3) & 1)) * 16);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lds() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ const void *uniform_ptr(const void *p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const void *>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t *lds_block) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(lds_block), 16, voff, soff, 0, 0);
+}
+
+// 32 bytes of K (pieces c and c+1 of the row) as one MFMA operand.
+__device__ __forceinline__ i32x8 frag32(const uint8_t *unit, int row, int c) {
+    const i32x4 lo = *reinterpret_cast<const i32x4 *>(unit + piece(row, c));
+    const i32x4 hi = *reinterpret_cast<const i32x4 *>(unit + piece(row, c + 1));
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// AGPR-resident accumulator element: the moves keep it in an AGPR between
+// uses (left to the compiler, 256 accumulators touched by vector ALU work
+// would be placed in VGPRs and spill).
+__device__ __forceinline__ float acc_get(float a) {
+    float r;
+    asm("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(a));
+    return r;
+}
+__device__ __forceinline__ float acc_put(float v) {
+    float a;
+    asm("v_accvgpr_write_b32 %0, %1" : "=a"(a) : "v"(v));
+    return a;
+}
+
+__device__ __forceinline__ float swiglu(float g, float u) {
+    return g * u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
+
+template <int EPI, bool ROUTED>
+__global__ __launch_bounds__(256, 1) void k_gemm_fp8_large(F8Params p) {
+    constexpr bool DUAL = EPI == EPI_SWIGLU_Q;
+    constexpr int BN = DUAL ? LB / 2 : LB;  // output columns per tile
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NUNIT * UNIT_BYTES];  // 160 KB
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1, g = lane >> 5;
+    const int K = p.K, nk = K / LK;
+
+    TileMap tm;
+    int Mt;
+    if (ROUTED) {
+        tilemap_init(tm, p.offsets);
+        Mt = tm.total;
+    } else {
+        Mt = (p.M + LM - 1) / LM;
+    }
+    const int NT = p.N / BN;
+    const int total = Mt * NT;
+    const int P = gridDim.x;
+
+    // DMA geometry (bytes, as the bf16 kernel): wave w moves blocks w + 4i of
+    // each operand; lane l fills physical piece (l & 7) of row 8*blk + (l >> 3).
+    int drow[8], dcol[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = 8 * (wave + 4 * i) + (lane >> 3);
+        drow[i] = row;
+        dcol[i] = ((lane & 7) ^ (row & 7) ^ ((row >> 3) & 1)) * 16;
+    }
+    const uint32_t a_rows_total = p.a_rows ? (uint32_t)(p.M / p.a_div) : (uint32_t)p.M;
+    const __amdgpu_buffer_rsrc_t rA = buf_rsrc(p.A, a_rows_total * (uint32_t)K);
+    const __amdgpu_buffer_rsrc_t rAs = buf_rsrc(p.As, a_rows_total * (uint32_t)nk * 4u);
+    const uint32_t b_bytes = (uint32_t)p.N * (uint32_t)K;
+    const int nbk = p.N / 128;  // weight scale blocks along N
+
+#define UNIT(u) (smem + (u) * UNIT_BYTES)
+
+    for (int t = (blockIdx.x & 7) * (P >> 3) + (blockIdx.x >> 3); t < total; t += P) {
+        const int gsz = kGroupM * NT;
+        const int grp = t / gsz, within = t - grp * gsz;
+        const int mfirst = grp * kGroupM;
+        const int gm = min(kGroupM, Mt - mfirst);
+        const int mt = mfirst + within % gm, nt = within / gm;
+        int e, m0, m_end;
+        if (ROUTED) {
+            tilemap_find(tm, mt, e, m0, m_end);
+        } else {
+            e = 0;
+            m0 = mt * LM;
+            m_end = p.M;
+        }
+        e = __builtin_amdgcn_readfirstlane(e);
+        m0 = __builtin_amdgcn_readfirstlane(m0);
+        m_end = __builtin_amdgcn_readfirstlane(m_end);
+        const int n0 = nt * BN;
+
+        const __amdgpu_buffer_rsrc_t rBg = buf_rsrc(uniform_ptr(p.B0 + (size_t)e * p.N * K), b_bytes);
+        const __amdgpu_buffer_rsrc_t rBu = DUAL ? buf_rsrc(uniform_ptr(p.B1 + (size_t)e * p.N * K), b_bytes) : rBg;
+        uint32_t aoff[8], boff[8];
+        {
+            int ar_[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ar_[i] = min(m0 + drow[i], m_end - 1);
+            if (p.a_rows) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ar_[i] = p.a_rows[ar_[i]];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ar_[i] /= p.a_div;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                aoff[i] = (uint32_t)ar_[i] * (uint32_t)K + (uint32_t)dcol[i];
+                const int r = drow[i];
+                const int br = DUAL ? n0 + (r & (BN - 1)) : n0 + r;
+                boff[i] = (uint32_t)br * (uint32_t)K + (uint32_t)dcol[i];
+            }
+        }
+        // this lane's 4 tile rows (wm*128 + 32i + (lane & 31)): activation-
+        // scale byte offsets (row * nk * 4; rows past the group repeat its last)
+        uint32_t soff[4];
+        {
+            int sr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sr[i] = min(m0 + wm * 128 + 32 * i + (lane & 31), m_end - 1);
+            if (p.a_rows) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sr[i] = p.a_rows[sr[i]] / p.a_div;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) soff[i] = (uint32_t)sr[i] * (uint32_t)nk * 4u;
+        }
+        // weight scales: block row of this wave's B columns (gate and up for
+        // the SwiGLU tile), [G, N/128, K/128]
+        const float *swg_p = p.S0 + ((size_t)e * nbk + (DUAL ? n0 : n0 + wn * 128) / 128) * nk;
+        const float *swu_p = DUAL ? p.S1 + ((size_t)e * nbk + n0 / 128) * nk : swg_p;
+
+#define ISSUE_A(st_, i, unit_)                                                                 \
+        dma_buf(rA, aoff[i], (uint32_t)min((st_), nk - 1) * LK, (unit_) + (wave + 4 * (i)) * 1024)
+#define ISSUE_B(st_, i, unit_)                                                                 \
+        dma_buf((DUAL && (i) >= 4) ? rBu : rBg, boff[i], (uint32_t)min((st_), nk - 1) * LK,        \
+                (unit_) + (wave + 4 * (i)) * 1024)
+        // scales of stage st_ into sa_[4], sw_[2] (5-6 vector loads per lane)
+#define LOAD_SCALES(st_, sa_, sw_)                                                             \
+        {                                                                                      \
+            const int kb_ = min((st_), nk - 1);                                                \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i)                                      \
+                sa_[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rAs, soff[i] + kb_ * 4u, 0, 0)); \
+            sw_[0] = swg_p[kb_];                                                               \
+            sw_[1] = DUAL ? swu_p[kb_] : sw_[0];                                               \
+        }
+
+        float acc[4][4][16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = acc_put(0.f);
+
+        // Prologue: scales(0), A_0, B_0, A_1 in flight.
+        float sa[4], sw[2], sa_n[4], sw_n[2];
+        LOAD_SCALES(0, sa, sw);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ISSUE_A(0, i, UNIT(0));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ISSUE_B(0, i, UNIT(1));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ISSUE_A(1, i, UNIT(2));
+
+        int u0 = 0;  // unit of A_kt (2kt mod 5)
+        for (int kt = 0; kt < nk; ++kt) {
+            const int u1 = u0 + 1 - (u0 + 1 >= NUNIT ? NUNIT : 0);
+            const int u3 = u0 + 3 - (u0 + 3 >= NUNIT ? NUNIT : 0);
+            const int u4 = u0 + 4 - (u0 + 4 >= NUNIT ? NUNIT : 0);
+            // A_kt, B_kt and this stage's scales landed (only A_{kt+1}, 8
+            // loads, may still be in flight) for every wave; the units of
+            // stage kt-1 are no longer read by anyone.
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            wait_vmcnt_lds<8>();
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            LOAD_SCALES(kt + 1, sa_n, sw_n);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ISSUE_B(kt + 1, i, UNIT(u3));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ISSUE_A(kt + 2, i, UNIT(u4));
+
+            const uint8_t *cA = UNIT(u0), *cB = UNIT(u1);
+            // B fragments of the whole stage (4 column blocks x 2 K halves);
+            // A fragments per row block, double-buffered: row block i+1 is read
+            // while row block i is multiplied.
+            i32x8 bf[4][2], af[2][2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int brow = (DUAL ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32)) + (lane & 31);
+#pragma unroll
+                for (int s = 0; s < 2; ++s) bf[j][s] = frag32(cB, brow, 4 * s + 2 * g);
+            }
+#define READ_A(i_, buf_)                                                                       \
+            _Pragma("unroll") for (int s = 0; s < 2; ++s)                                      \
+                af[buf_][s] = frag32(cA, wm * 128 + 32 * (i_) + (lane & 31), 4 * s + 2 * g);
+            READ_A(0, 0);
+            // Block n = (i, j) = (n >> 2, n & 3).  Software pipeline with two
+            // partials: the MFMA pair of block n+1 is issued before block n is
+            // folded, so the matrix pipe works while the vector ALU folds.
+            f32x16 tp[2];
+            const f32x16 zero = {};
+#define MF2(n_, T_)                                                                            \
+            T_ = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[(n_) & 3][0], af[((n_) >> 2) & 1][0], zero, 0, 0, \
+                                                                 0, 0, 0, 0);                  \
+            T_ = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[(n_) & 3][1], af[((n_) >> 2) & 1][1], T_, 0, 0, 0, \
+                                                                 0, 0, 0);
+            MF2(0, tp[0]);
+#pragma unroll
+            for (int n = 0; n < 16; ++n) {
+                if ((n & 3) == 0 && n + 4 < 16) {
+                    READ_A((n >> 2) + 1, ((n >> 2) + 1) & 1);
+                }
+                if (n + 1 < 16) {
+                    MF2(n + 1, tp[(n + 1) & 1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                const int i = n >> 2, j = n & 3;
+                const float sc = sa[i] * sw[DUAL ? (j >> 1) : 0];
+                float cur[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) cur[r] = acc_get(acc[i][j][r]);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) cur[r] = fmaf(tp[n & 1][r], sc, cur[r]);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = acc_put(cur[r]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#undef MF2
+#undef READ_A
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sa[i] = sa_n[i];
+            sw[0] = sw_n[0];
+            sw[1] = sw_n[1];
+            u0 = u0 + 2 - (u0 + 2 >= NUNIT ? NUNIT : 0);
+        }
+#undef ISSUE_A
+#undef ISSUE_B
+#undef LOAD_SCALES
+        __syncthreads();  // every wave done with the ring (and all its loads landed)
+
+        // lane: tile rows wm*128 + 32i + (lane & 31); per 32-column block j,
+        // columns 8q + 4g + u (u = 0..3) in acc[i][j][4q + u]
+        const int c4 = 4 * g;
+        if constexpr (DUAL) {
+            // h columns of this wave: wn*64 + jj*32 + 8q + 4g + u; the tile's
+            // 128 h columns are one quantisation tile
+            float *xch = reinterpret_cast<float *>(UNIT(4));  // [2][256] partial row amax
+            float hv[4][2][16];
+            float am[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float m = 0.f;
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float h = swiglu(acc_get(acc[i][jj][r]), acc_get(acc[i][2 + jj][r]));
+                        hv[i][jj][r] = h;
+                        m = fmaxf(m, fabsf(h));
+                    }
+                m = fmaxf(m, __shfl_xor(m, 32, 64));  // the other 32 columns of this wave
+                am[i] = m;
+                if (g == 0) xch[wn * 256 + wm * 128 + 32 * i + lane] = m;
+            }
+            __syncthreads();
+            const __amdgpu_buffer_rsrc_t rQ = buf_rsrc(p.hq, (uint32_t)p.M * (uint32_t)p.H);
+            const __amdgpu_buffer_rsrc_t rS = buf_rsrc(p.hs, (uint32_t)p.M * (uint32_t)(p.H / 128) * 4u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tr = wm * 128 + 32 * i + (lane & 31);
+                const int row = m0 + tr;
+                const float amax = fmaxf(am[i], xch[(wn ^ 1) * 256 + tr]);
+                const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+                const bool ok = row < m_end;
+                const uint32_t qbase = ok ? (uint32_t)row * (uint32_t)p.H + (uint32_t)n0 : 0xfffff000u;
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        uint32_t w = 0;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) w |= f32_to_e4m3(hv[i][jj][4 * q + u] / s) << (8 * u);
+                        __builtin_amdgcn_raw_buffer_store_b32((int)w, rQ,
+                                                              qbase + (uint32_t)(wn * 64 + jj * 32 + 8 * q + c4), 0, 0);
+                    }
+                if (wn == 0 && g == 0) {
+                    const uint32_t so = ok ? ((uint32_t)row * (uint32_t)(p.H / 128) + (uint32_t)(n0 / 128)) * 4u
+                                           : 0xfffff000u;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(s), rS, so, 0, 0);
+                }
+            }
+            __syncthreads();  // xch read by all before the next tile's loads reuse the ring
+        } else if constexpr (EPI == EPI_STORE) {
+            const __amdgpu_buffer_rsrc_t rOut = buf_rsrc(p.out, (uint32_t)p.M * (uint32_t)p.N * 2u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = m0 + wm * 128 + 32 * i + (lane & 31);
+                const uint32_t obase = row < m_end ? ((uint32_t)row * (uint32_t)p.N + (uint32_t)n0) * 2u : 0xfffff000u;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t lo = pack_bf16x2(acc_get(acc[i][j][4 * q]), acc_get(acc[i][j][4 * q + 1]));
+                        const uint32_t hi = pack_bf16x2(acc_get(acc[i][j][4 * q + 2]), acc_get(acc[i][j][4 * q + 3]));
+                        const int col = wn * 128 + j * 32 + 8 * q + c4;
+                        __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)lo, (int)hi}, rOut, obase + (uint32_t)col * 2u,
+                                                              0, 0);
+                    }
+            }
+        } else {
+            const __amdgpu_buffer_rsrc_t rOut = buf_rsrc(p.yout, (uint32_t)p.M * (uint32_t)p.N * 4u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = m0 + wm * 128 + 32 * i + (lane & 31);
+                const uint32_t obase = row < m_end ? ((uint32_t)row * (uint32_t)p.N + (uint32_t)n0) * 4u : 0xfffff000u;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int col = wn * 128 + j * 32 + 8 * q + c4;
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            i32x4{__float_as_int(acc_get(acc[i][j][4 * q])), __float_as_int(acc_get(acc[i][j][4 * q + 1])),
+                                  __float_as_int(acc_get(acc[i][j][4 * q + 2])),
+                                  __float_as_int(acc_get(acc[i][j][4 * q + 3]))},
+                            rOut, obase + (uint32_t)col * 4u, 0, 0);
+                    }
+            }
+        }
+    }
+#undef UNIT
+}
+
+int cu_count() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+}  // namespace
+
+bool ffn_fp8_large_ok(const FfnArgs &a) {
+    const int groups = a.offsets ? a.E : 1;
+    const unsigned long long lim = 1ULL << 32;
+    const bool fits = (unsigned long long)a.M * a.d < lim && (unsigned long long)a.M * a.I * 2 < lim &&
+                      (unsigned long long)a.M * a.d * 4 < lim && (unsigned long long)a.I * a.d < lim;
+    return fits && (long long)a.M >= 128LL * groups && a.I % 128 == 0 && a.d % 256 == 0 && a.d % LK == 0 &&
+           a.I % LK == 0;
+}
+
+// Phase 1 (gate/up, fused SwiGLU + h quantisation) and / or phase 2 (down:
+// bf16 y_perm, or the shared expert's fp32 output for k_combine_add).
+hipError_t launch_ffn_fp8_large(const FfnArgs &a, hipStream_t s) {
+    const int P = (cu_count() / 8) * 8;
+    const bool routed = a.offsets != nullptr;
+    if (a.phases & 1) {
+        F8Params p{};
+        p.M = a.M;
+        p.offsets = a.offsets;
+        p.A = static_cast<const uint8_t *>(a.a);
+        p.As = a.a_scale;
+        p.a_rows = a.a_rows;
+        p.a_div = a.a_div;
+        p.K = a.d;
+        p.B0 = static_cast<const uint8_t *>(a.w.gate);
+        p.B1 = static_cast<const uint8_t *>(a.w.up);
+        p.S0 = a.w.s_gate;
+        p.S1 = a.w.s_up;
+        p.N = a.I;  // rows of each of gate / up; a tile takes 128 of each
+        p.hq = static_cast<uint8_t *>(a.h);
+        p.hs = a.h_scale;
+        p.H = a.I;
+        if (routed)
+            hipLaunchKernelGGL((k_gemm_fp8_large<EPI_SWIGLU_Q, true>), dim3(P), dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((k_gemm_fp8_large<EPI_SWIGLU_Q, false>), dim3(P), dim3(256), 0, s, p);
+    }
+    if (a.phases & 2) {
+        F8Params q{};
+        q.M = a.M;
+        q.offsets = a.offsets;
+        q.A = static_cast<const uint8_t *>(a.h);
+        q.As = a.h_scale;
+        q.K = a.I;
+        q.B0 = static_cast<const uint8_t *>(a.w.down);
+        q.S0 = a.w.s_down;
+        q.N = a.d;
+        if (a.combine) {
+            q.yout = static_cast<float *>(a.y);
+            if (routed)
+                hipLaunchKernelGGL((k_gemm_fp8_large<EPI_F32, true>), dim3(P), dim3(256), 0, s, q);
+            else
+                hipLaunchKernelGGL((k_gemm_fp8_large<EPI_F32, false>), dim3(P), dim3(256), 0, s, q);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            return launch_combine_add(a.M, a.d, a.k, static_cast<const uint16_t *>(a.y_perm), a.row_of, a.cw,
+                                      static_cast<float *>(a.y), s);
+        }
+        q.out = static_cast<uint16_t *>(a.y);
+        if (routed)
+            hipLaunchKernelGGL((k_gemm_fp8_large<EPI_STORE, true>), dim3(P), dim3(256), 0, s, q);
+        else
+            hipLaunchKernelGGL((k_gemm_fp8_large<EPI_STORE, false>), dim3(P), dim3(256), 0, s, q);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -81,6 +81,9 @@ hipError_t launch_ffn_fp8(const FfnArgs &a, hipStream_t s);
 // averages at least 128 rows and the widths tile evenly.
 bool ffn_bf16_large_ok(const FfnArgs &a);
 hipError_t launch_ffn_bf16_large(const FfnArgs &a, hipStream_t s);
+// Large-group e4m3 path (persistent 256x256 tiles, fp32 promotion per 128 of K).
+bool ffn_fp8_large_ok(const FfnArgs &a);
+hipError_t launch_ffn_fp8_large(const FfnArgs &a, hipStream_t s);
 
 hipError_t launch_bias_update(int E, int k, int T, const int32_t *counts, float gamma, float *bias,
                               hipStream_t s);

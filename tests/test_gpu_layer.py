@@ -143,3 +143,12 @@ def test_layer_config4_full_size_sampled():
     cfg = synth.CONFIGS[4]
     inp = synth.make_inputs(cfg)
     check_layer(cfg, inp, n_sample=12, route_all=False)
+
+
+def test_layer_config5_full_size_sampled():
+    """The fp8 workload at full size (T=16384, d=7168, I=2048, e4m3 weights and
+    activations): the persistent fp8 GEMMs for the routed and shared experts;
+    the oracle checks 12 sampled tokens."""
+    cfg = synth.CONFIGS[5]
+    inp = synth.make_inputs(cfg)
+    check_layer(cfg, inp, n_sample=12, route_all=False)

@@ -179,13 +179,16 @@ def test_expert_ffn_small(wt, kind, T):
     assert err <= TOL[wt], err
 
 
+@pytest.mark.parametrize("wt", ["bf16", "e4m3"])
 @pytest.mark.parametrize("kind", ["random", "skewed", "same8"])
-def test_expert_ffn_large_groups(kind):
+def test_expert_ffn_large_groups(kind, wt):
     """T=4096 tokens: 128+ rows per expert on average, the persistent
-    256x256-tile path; d=512, I=256 so several column tiles and K stages run.
-    The oracle checks 160 sampled permuted rows including group edges."""
-    cfg = synth.Config("ffn-large", seed=23, T=4096, d=512, I=256)
-    say(f"[ffn] large groups {kind}")
+    256x256-tile path (bf16, and e4m3 with its fp32 promotion per 128 of K
+    and the fused h quantisation); d=512, I=256 so several column tiles and
+    K stages run.  The oracle checks 160 sampled permuted rows including
+    group edges."""
+    cfg = synth.Config("ffn-large", seed=23, T=4096, d=512, I=256, wt=wt)
+    say(f"[ffn] large groups {wt} {kind}")
     experts = synth.make_ffn(cfg, 256, (synth.TID_GATE, synth.TID_UP, synth.TID_DOWN))
     offsets, a_rows, a_sc = ffn_inputs(cfg, kind)
     y = run_ffn(cfg, offsets, a_rows, a_sc, experts)
@@ -196,9 +199,9 @@ def test_expert_ffn_large_groups(kind):
     rows = np.unique(np.concatenate([rng.choice(edges, min(96, len(edges)), replace=False),
                                      rng.integers(0, cfg.A, 64)])).astype(np.int32)
     yo = oracle.expert_ffn(oracle.shape_of(cfg), experts, offsets, a_rows, a_sc, rows=rows)
-    err = max_rel(yvals(y[rows], "bf16"), yvals(yo, "bf16"))
-    say(f"[ffn] large groups {kind}: max rel err {err:.3e} on {len(rows)} rows")
-    assert err <= TOL["bf16"], err
+    err = max_rel(yvals(y[rows], wt), yvals(yo, wt))
+    say(f"[ffn] large groups {wt} {kind}: max rel err {err:.3e} on {len(rows)} rows")
+    assert err <= TOL[wt], err
 
 
 def test_expert_ffn_config2_sampled_rows():
