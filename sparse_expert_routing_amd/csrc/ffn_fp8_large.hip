@@ -13,9 +13,9 @@
 //   - one stage = 128 of K = one scale block: A and B slabs of 256 rows x
 //     128 bytes (whole L2 lines) in a ring of five 32 KB LDS units filled by
 //     buffer_load_dwordx4 ... lds (scalar resource, fixed per-lane offset,
-//     stage offset in an SGPR); at the start of stage s, after one barrier,
-//     B_{s+1} and A_{s+2} are issued into the two units stage s-1 left, so
-//     B has a stage and A two stages to land;
+//     stage offset in an SGPR); during stage s, after its one barrier,
+//     B_{s+1} and A_{s+2} stream into the two units stage s-1 left, one load
+//     per output block, so B has about a stage and A two stages to land;
 //   - a stage's fragments (32 bytes per lane per 32x64 block) are read once
 //     into VGPRs; each 32x32 output block takes two
 //     v_mfma_scale_f32_32x32x64_f8f6f4 (scales 0: plain fp8) into a fresh
@@ -312,10 +312,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_large(F8Params p) {
             __builtin_amdgcn_s_barrier();
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             LOAD_SCALES(kt + 1, sa_n, sw_n);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ISSUE_B(kt + 1, i, UNIT(u3));
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ISSUE_A(kt + 2, i, UNIT(u4));
+            uint8_t *fB = UNIT(u3), *fA = UNIT(u4);  // B_{kt+1}, A_{kt+2}: one load per block below
 
             const uint8_t *cA = UNIT(u0), *cB = UNIT(u1);
             // B fragments of the whole stage (4 column blocks x 2 K halves);
@@ -351,6 +348,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_large(F8Params p) {
                 if (n + 1 < 16) {
                     MF2(n + 1, tp[(n + 1) & 1]);
                 }
+                // one slot load per block (B first: it has one stage to land)
+                if (n < 8) ISSUE_B(kt + 1, n, fB);
+                else ISSUE_A(kt + 2, n - 8, fA);
                 __builtin_amdgcn_sched_barrier(0);
                 const int i = n >> 2, j = n & 3;
                 const float sc = sa[i] * sw[DUAL ? (j >> 1) : 0];
