@@ -23,7 +23,9 @@
 // (A: 128 x 64 bf16, B: 3 x 128 x 64 bf16 per stage, two stages), rows of
 // 128 bytes with XOR-swizzled 16-byte pieces; the next stage's loads are
 // spread over the current stage's MFMAs.  As in the fused fp32 router, the
-// accumulators are folded into running totals every 512 of K.
+// accumulators are folded into running totals every 512 of K.  For small T
+// the K range is split over blockIdx.z so about 256 workgroups run; the
+// top-k kernel adds the partial logits in split order.
 #include "device.h"
 #include "kernels.h"
 
@@ -59,6 +61,8 @@ __device__ __forceinline__ int piece(int row, int c) {
     return row * RK + ((c ^ (row & 7) ^ ((row >> 3) & 1)) * 8);
 }
 
+// blockIdx.z: K range [z*nk/S, (z+1)*nk/S) of the S = gridDim.z splits; its
+// partial logits go to logits + z*T*E (the top-k kernel sums them in order).
 __global__ __launch_bounds__(256, 1) void k_router_logits(int T, int d, const uint16_t *__restrict__ x,
                                                          const uint16_t *__restrict__ wsplit,
                                                          float *__restrict__ logits) {
@@ -67,7 +71,9 @@ __global__ __launch_bounds__(256, 1) void k_router_logits(int T, int d, const ui
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1, g = lane >> 5;
     const int m0 = blockIdx.x * RM, n0 = blockIdx.y * RN;
-    const int nk = d / RK;
+    const int nk_all = d / RK, S = gridDim.z, z = blockIdx.z;
+    const int kb0 = (int)((long long)nk_all * z / S), nk = (int)((long long)nk_all * (z + 1) / S) - kb0;
+    logits += (size_t)z * T * kE;
 
     // DMA geometry: each region is 16 blocks of 8 rows x 128 B; wave w moves
     // blocks w, w+4, w+8, w+12 of every region (16 loads per stage).
@@ -80,9 +86,9 @@ __global__ __launch_bounds__(256, 1) void k_router_logits(int T, int d, const ui
         const int col = ((lane & 7) ^ (row & 7) ^ ((row >> 3) & 1)) * 8;
         if (region == 0) {
             const int t = min(m0 + row, T - 1);
-            src[i] = x + (size_t)t * d + col;
+            src[i] = x + (size_t)t * d + (size_t)kb0 * RK + col;
         } else {
-            src[i] = wsplit + ((size_t)(region - 1) * kE + n0 + row) * d + col;
+            src[i] = wsplit + ((size_t)(region - 1) * kE + n0 + row) * d + (size_t)kb0 * RK + col;
         }
         dst[i] = region * kRegion + rb * 512;
     }
@@ -136,7 +142,7 @@ __global__ __launch_bounds__(256, 1) void k_router_logits(int T, int d, const ui
                         if (s == 2 && i == 1 && j == 1) ISSUE(4 * kk + 3, kn, nslot);
                     }
         }
-        if ((kt + 1) * RK % kFlush == 0 || kt + 1 == nk) {
+        if ((kb0 + kt + 1) * RK % kFlush == 0 || kt + 1 == nk) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -171,7 +177,7 @@ __global__ __launch_bounds__(256, 1) void k_router_logits(int T, int d, const ui
 // id), ids ascending, weights = chosen affinities over their sum, and the
 // k-th minus (k+1)-th biased score when asked.
 template <int kK>
-__global__ __launch_bounds__(256) void k_route_topk(int T, const float *__restrict__ logits,
+__global__ __launch_bounds__(256) void k_route_topk(int T, int S, const float *__restrict__ logits,
                                                    const float *__restrict__ bias, int32_t *__restrict__ idx,
                                                    float *__restrict__ wts, float *__restrict__ gap) {
     const int lane = threadIdx.x & 63;
@@ -182,7 +188,9 @@ __global__ __launch_bounds__(256) void k_route_topk(int T, const float *__restri
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int e = lane + 64 * q;
-        sv[q] = 1.0f / (1.0f + expf(-logits[(size_t)t * kE + e]));
+        float l = logits[(size_t)t * kE + e];
+        for (int z = 1; z < S; ++z) l += logits[((size_t)z * T + t) * kE + e];  // K splits, in order
+        sv[q] = 1.0f / (1.0f + expf(-l));
         key[q] = ((uint64_t)f32_order_key(sv[q] + bias[e]) << 32) | (uint32_t)(kE - 1 - e);
     }
     constexpr int kRounds = kK + 1;  // one extra round gives the gap
@@ -233,9 +241,18 @@ __global__ __launch_bounds__(256) void k_route_topk(int T, const float *__restri
 
 }  // namespace
 
+// K splits of the logits GEMM: up to about 256 workgroups for small T, each
+// split keeping at least 4 K steps so its prologue and epilogue stay small.
+static int route_ksplit(int T, int d) {
+    const int tiles = (T + RM - 1) / RM * (kE / RN);
+    const int cap = d / RK / 4;
+    const int S = 256 / tiles;
+    return S > cap ? (cap < 1 ? 1 : cap) : (S < 1 ? 1 : S);
+}
+
 size_t route_bf16_ws_bytes(int T, int d) {
     const size_t split = ((size_t)3 * kE * d * sizeof(uint16_t) + 255) / 256 * 256;
-    return split + (size_t)T * kE * sizeof(float);
+    return split + (size_t)route_ksplit(T, d) * T * kE * sizeof(float);
 }
 
 bool route_bf16_ok(int d) { return d % RK == 0; }
@@ -247,10 +264,11 @@ hipError_t launch_route_bf16(const RouteArgs &a, void *ws, hipStream_t s) {
     const int n = kE * a.d;
     hipLaunchKernelGGL(k_router_split, dim3((n + 255) / 256), dim3(256), 0, s, n, a.wr, wsplit, wsplit + n,
                        wsplit + 2 * (size_t)n);
-    hipLaunchKernelGGL(k_router_logits, dim3((a.T + RM - 1) / RM, kE / RN), dim3(256), 0, s, a.T, a.d,
+    const int S = route_ksplit(a.T, a.d);
+    hipLaunchKernelGGL(k_router_logits, dim3((a.T + RM - 1) / RM, kE / RN, S), dim3(256), 0, s, a.T, a.d,
                        static_cast<const uint16_t *>(a.x), wsplit, logits);
-    hipLaunchKernelGGL((k_route_topk<8>), dim3((a.T + 3) / 4), dim3(256), 0, s, a.T, logits, a.bias, a.idx, a.w,
-                       a.gap);
+    hipLaunchKernelGGL((k_route_topk<8>), dim3((a.T + 3) / 4), dim3(256), 0, s, a.T, S, logits, a.bias, a.idx,
+                       a.w, a.gap);
     return hipGetLastError();
 }
 

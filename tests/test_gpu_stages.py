@@ -65,6 +65,15 @@ def test_route_configs(cid, T):
     check_route(cfg, x, wr, bias, f"config {cid}")
 
 
+@pytest.mark.parametrize("T,d", [(100, 896), (100, 1408), (129, 7168)])
+def test_route_uneven_k_splits(T, d):
+    # small T splits the router's K range over several workgroups; these d
+    # give splits of unequal length and fold points inside a split
+    cfg = synth.CONFIGS[2].with_(T=T, d=d)
+    x, wr, bias = synth.make_router(cfg)
+    check_route(cfg, x, wr, bias, f"T={T} d={d}")
+
+
 def test_route_zero_router_ties_go_to_lower_ids():
     cfg = synth.CONFIGS[2].with_(T=130, d=512)
     x, _, _ = synth.make_router(cfg)
