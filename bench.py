@@ -12,10 +12,13 @@ in HBM before the timed region starts.
 
 Prints ONE JSON line on stdout (progress goes to stderr).
   value          tokens/s over the timed steps (T * steps / wall time)
-  roofline       the dominant kernel (the routed gate/up grouped GEMM):
-                 algorithmic FLOPs per launch (2 * T*k * d * 2I) over its
-                 average duration from HIP events on the launch stream,
-                 against the dense bf16 MFMA peak
+  roofline       the dominant kernel (the routed gate/up grouped GEMM),
+                 average duration from HIP events on the launch stream:
+                 MFMA-bound workloads report algorithmic FLOPs per launch
+                 (2 * T*k * d * 2I) against the dense MFMA peak of the weight
+                 type; HBM-bound ones (FLOP/byte under the ridge, e.g. decode)
+                 report algorithmic bytes (touched experts' gate/up weights
+                 once, x once, h once) against 8 TB/s
   cpu_baseline   the CPU oracle (fp64, plain loops) timed on a sample of the
                  same workload's tokens through the whole forward
 """
@@ -35,6 +38,7 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "sparse_expert_routing_amd", "csrc", "ffn_bf16_large.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_gemm_bf16_large_gateup_traffic_prefill-zipf-bf16.md")
 METRIC = "MoE-layer tokens/s (T=16384,d=7168,256e top-8) + % of MFMA/HBM peak"
+TRAFFIC_WORKLOAD = "prefill-zipf-bf16 T16384 d7168 I2048"  # the workload the counter summary covers
 
 
 def log(*a):
@@ -143,12 +147,27 @@ def main():
 
     gate_up_flops = 2.0 * A * d * (2 * I)
     gate_up_ms = phase["expert_gate_up"]
-    achieved = gate_up_flops / (gate_up_ms * 1e-3) / 1e12
-    peak = PEAK_FP8_TFLOPS if cfg.wt == "e4m3" else PEAK_BF16_TFLOPS
+    # algorithmic bytes of one gate/up launch: the touched experts' gate and
+    # up weights (+ block scales) read once, x read once, h written once
+    touched = float((ch > 0).sum(axis=1).mean())
+    s_w = 1 if cfg.wt == "e4m3" else 2
+    w_bytes = 2.0 * I * d * s_w + (2.0 * (I // 128) * (d // 128) * 4 if cfg.wt == "e4m3" else 0.0)
+    gate_up_bytes = touched * w_bytes + T * d * 2.0 + A * I * s_w
+    peak_flops = PEAK_FP8_TFLOPS if cfg.wt == "e4m3" else PEAK_BF16_TFLOPS
+    hbm_bound = gate_up_flops / gate_up_bytes < peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if hbm_bound:
+        achieved = gate_up_bytes / (gate_up_ms * 1e-3) / 1e9
+        peak = PEAK_HBM_GBS
+    else:
+        achieved = gate_up_flops / (gate_up_ms * 1e-3) / 1e12
+        peak = peak_flops
+    large = A >= 128 * E
+    kname = ("k_gemm_fp8_large" if large else "k_gemm_fp8") if cfg.wt == "e4m3" else \
+        ("k_gemm_bf16_large" if large else "k_gemm_bf16")
     total_flops = 2.0 * T * d * E + 6.0 * (A + T) * d * I
     ms_step = wall / K * 1e3
     log(f"[bench] {ms_step:.3f} ms/step, phases (ms): " + ", ".join(f"{n} {v:.3f}" for n, v in phase.items()))
-    log(f"[bench] gate/up GEMM {achieved:.1f} TFLOP/s ({100 * achieved / peak:.1f}% of peak); "
+    log(f"[bench] gate/up GEMM {achieved:.1f} {'GB/s' if hbm_bound else 'TFLOP/s'} ({100 * achieved / peak:.1f}% of peak); "
         f"layer {total_flops / (ms_step * 1e-3) / 1e12:.1f} TFLOP/s; max/mean load {imb[0]:.2f} -> {imb[-1]:.2f}; "
         f"256-row tiles {tiles.mean():.0f} (ideal {A / 256:.0f})")
 
@@ -168,11 +187,13 @@ def main():
         "config": {"workload": cfg.name, "T": T, "d_model": d, "experts": E, "top_k": k, "shared_experts": 1,
                    "expert_intermediate": I, "router": "fp32 sigmoid", "router_row_skew": cfg.skew,
                    "bias_start": cfg.bias, "gamma": cfg.gamma, "loop_steps_timed": K, "seed": cfg.seed},
-        "roofline": {"kernel": "routed gate/up grouped GEMM (k_gemm_bf16_large, SwiGLU epilogue)" if cfg.wt != "e4m3"
-                     else "routed gate/up grouped GEMM (k_gemm_fp8 SwiGLU+quant)",
-                     "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": measured_traffic() if cfg.wt != "e4m3" else None,
-                     "flops_per_launch": gate_up_flops, "avg_launch_ms": gate_up_ms},
+        "roofline": {"kernel": f"routed gate/up grouped GEMM ({kname}, SwiGLU epilogue"
+                               + (" + e4m3 quantisation)" if cfg.wt == "e4m3" else ")"),
+                     "bound": "hbm" if hbm_bound else "mfma", "achieved": achieved, "peak": peak,
+                     "unit": "GB/s" if hbm_bound else "TFLOP/s", "frac": achieved / peak,
+                     "traffic": measured_traffic() if cfg.name == TRAFFIC_WORKLOAD else None,
+                     "flops_per_launch": gate_up_flops, "bytes_per_launch": gate_up_bytes,
+                     "touched_experts": touched, "avg_launch_ms": gate_up_ms},
         "phases_ms": phase,
         "layer_tflops": total_flops / (ms_step * 1e-3) / 1e12,
         "imbalance_max_over_mean": {"first": float(imb[0]), "last": float(imb[-1])},

@@ -200,7 +200,9 @@ moe_status_t moe_expert_gate_up_rows(const moe_desc_t *desc, const void *x, cons
  * token).
  *   y[t] = shared(x[t]) + sum_{j<k} weights[t, j] * y_perm[row_of[t*k + j]]
  * with the j-sum in ascending expert-id order, in fp32; the shared expert's
- * fp32 accumulator is not rounded before the sum.  The shared expert has the
+ * fp32 accumulator is not rounded before the sum (at small T with bf16
+ * weights its K range is split over workgroups and the fp32 partial sums are
+ * added in a fixed order, so the result is still deterministic).  The shared expert has the
  * SwiGLU form of the routed ones; with wt = e4m3 its input is x quantised per
  * 1x128 tile (as in moe_dispatch) inside the workspace.
  *   x        [T, d] act type

@@ -16,7 +16,11 @@
 //   - down: plain bf16 store into y_perm, or (shared expert) the combine
 //     y = acc + sum_j w_j * y_perm[row_of[t*k + j]] in fp32;
 //   - tile -> (expert, first row) is computed on the device from `offsets`
-//     (no host synchronisation); slots past the last tile exit at once.
+//     (no host synchronisation); slots past the last tile exit at once;
+//   - shared expert at small T (few row tiles): K is split over blockIdx.z
+//     so about 256 workgroups stream the weights; each split stores fp32
+//     partial sums and a second pass adds them in split order and applies
+//     the SwiGLU (gate/up) or the combine (down).
 // fp32 path: one thread per output, plain FMA loops (tiny fp32 layer only).
 #include "device.h"
 #include "kernels.h"
@@ -30,7 +34,7 @@ constexpr int BM = 128;  // rows per workgroup tile
 constexpr int BNB = 128; // B rows per workgroup tile
 constexpr int BK = 64;   // K per stage
 
-enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_COMBINE = 2 };
+enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_COMBINE = 2, EPI_PART_DUAL = 3, EPI_PART = 4 };
 
 struct GemmParams {
     int M;                    // rows when offsets == nullptr
@@ -47,6 +51,7 @@ struct GemmParams {
     const int32_t *row_of;    // [rows*k]
     const float *cw;          // [rows*k]
     int k;
+    float *part;              // split K: fp32 partials [gridDim.z, rows, N] (x2 columns for gate/up)
 };
 
 // Map a row-tile slot to (expert, first row, end row).  All lanes of all waves
@@ -100,7 +105,7 @@ __device__ __forceinline__ int swz(int row, int c16) { return c16 ^ (row & 7); }
 
 template <int EPI>
 __global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
-    constexpr bool DUAL = EPI == EPI_SWIGLU;
+    constexpr bool DUAL = EPI == EPI_SWIGLU || EPI == EPI_PART_DUAL;
     constexpr int BN = DUAL ? BNB / 2 : BNB;      // output columns per workgroup
     constexpr int NT = DUAL ? 2 : 2;              // 32-wide B fragments per wave
     __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
@@ -112,6 +117,11 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int K = p.K;
+    // K range of this split (the whole K when gridDim.z == 1)
+    const int nk_all = K / BK, z = blockIdx.z;
+    const int kb0 = nk_all * z / (int)gridDim.z;
+    const int nk = nk_all * (z + 1) / (int)gridDim.z - kb0;
+    const int kbase = kb0 * BK;
 
     // global -> register staging: 4 chunks of 16 bytes per thread per operand.
     // Chunk i covers row tid/8 + 32*i and K columns (tid%8)*8 .. +8; for the
@@ -145,11 +155,10 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
     uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
     const uint16_t *Bu2 = DUAL ? Bu : Bg;  // B matrix of chunks 2 and 3
 
-    const int nk = K / BK;
     for (int kt = -1; kt < nk; ++kt) {
         // stage kt+1: global -> registers (issued before the MFMAs of stage kt)
         if (kt + 1 < nk) {
-            const int k0 = (kt + 1) * BK;
+            const int k0 = kbase + (kt + 1) * BK;
             ra0 = *reinterpret_cast<const uint4 *>(Ab + aoff[0] + k0);
             ra1 = *reinterpret_cast<const uint4 *>(Ab + aoff[1] + k0);
             ra2 = *reinterpret_cast<const uint4 *>(Ab + aoff[2] + k0);
@@ -208,7 +217,12 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
             for (int r = 0; r < 4; ++r) {
                 const int row = m0 + wm * 64 + i * 32 + 8 * q + 4 * (lane >> 5) + r;
                 if (row >= m_end) continue;
-                if (DUAL) {
+                if (EPI == EPI_PART_DUAL) {
+                    const int col = n0 + wn * 32 + (lane & 31);
+                    float *pr = p.part + ((size_t)z * p.M + row) * (2 * N);
+                    pr[col] = acc[i][0][4 * q + r];
+                    pr[N + col] = acc[i][1][4 * q + r];
+                } else if (DUAL) {
                     const int col = n0 + wn * 32 + (lane & 31);
                     const float g = acc[i][0][4 * q + r], u = acc[i][1][4 * q + r];
                     const float h = g / (1.0f + expf(-g)) * u;
@@ -220,6 +234,8 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
                         const float v = acc[i][j][4 * q + r];
                         if (EPI == EPI_STORE) {
                             p.out[(size_t)row * N + col] = (uint16_t)f32_to_bf16(v);
+                        } else if (EPI == EPI_PART) {
+                            p.part[((size_t)z * p.M + row) * N + col] = v;
                         } else {
                             float y = v;
                             for (int jj = 0; jj < p.k; ++jj) {
@@ -232,6 +248,67 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
                 }
             }
     }
+}
+
+// Split-K second passes, 4 columns per thread.
+// h[r, c] = bf16(silu(g) * u), g and u the split partials added in split order.
+__global__ __launch_bounds__(256) void k_split_swiglu(int M, int I, int S, const float *__restrict__ part,
+                                                      uint16_t *__restrict__ h) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    const int w4 = I / 4;
+    if (i >= M * w4) return;
+    const int row = i / w4, c = (i - row * w4) * 4;
+    const size_t zs = (size_t)M * 2 * I;
+    const float *pg = part + (size_t)row * 2 * I + c;
+    float4 g = *reinterpret_cast<const float4 *>(pg), u = *reinterpret_cast<const float4 *>(pg + I);
+    for (int z = 1; z < S; ++z) {
+        const float4 gz = *reinterpret_cast<const float4 *>(pg + z * zs);
+        const float4 uz = *reinterpret_cast<const float4 *>(pg + z * zs + I);
+        g.x += gz.x; g.y += gz.y; g.z += gz.z; g.w += gz.w;
+        u.x += uz.x; u.y += uz.y; u.z += uz.z; u.w += uz.w;
+    }
+    const float hx = g.x / (1.0f + expf(-g.x)) * u.x, hy = g.y / (1.0f + expf(-g.y)) * u.y;
+    const float hz = g.z / (1.0f + expf(-g.z)) * u.z, hw = g.w / (1.0f + expf(-g.w)) * u.w;
+    uint2 o;
+    o.x = f32_to_bf16(hx) | (f32_to_bf16(hy) << 16);
+    o.y = f32_to_bf16(hz) | (f32_to_bf16(hw) << 16);
+    *reinterpret_cast<uint2 *>(h + (size_t)row * I + c) = o;
+}
+
+// y[t, n] = (sum over splits of the shared down GEMM) + sum_j cw[t*k+j] * y_perm[row_of[t*k+j], n]
+__global__ __launch_bounds__(256) void k_split_combine(int M, int d, int S, int k, const float *__restrict__ part,
+                                                       const uint16_t *__restrict__ y_perm,
+                                                       const int32_t *__restrict__ row_of,
+                                                       const float *__restrict__ cw, float *__restrict__ y) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    const int w4 = d / 4;
+    if (i >= M * w4) return;
+    const int row = i / w4, c = (i - row * w4) * 4;
+    const size_t zs = (size_t)M * d;
+    const float *pp = part + (size_t)row * d + c;
+    float4 v = *reinterpret_cast<const float4 *>(pp);
+    for (int z = 1; z < S; ++z) {
+        const float4 vz = *reinterpret_cast<const float4 *>(pp + z * zs);
+        v.x += vz.x; v.y += vz.y; v.z += vz.z; v.w += vz.w;
+    }
+    for (int j = 0; j < k; ++j) {
+        const size_t f = (size_t)row * k + j;
+        const float w = cw[f];
+        const uint2 b = *reinterpret_cast<const uint2 *>(y_perm + (size_t)row_of[f] * d + c);
+        v.x += w * bf16_to_f32(b.x & 0xffffu);
+        v.y += w * bf16_to_f32(b.x >> 16);
+        v.z += w * bf16_to_f32(b.y & 0xffffu);
+        v.w += w * bf16_to_f32(b.y >> 16);
+    }
+    *reinterpret_cast<float4 *>(y + (size_t)row * d + c) = v;
+}
+
+// Number of K splits for a GEMM of `tiles` workgroup tiles over nk K steps:
+// about 256 workgroups, each split keeping at least 4 K steps.
+int ksplits(int tiles, int nk) {
+    const int cap = nk / 4;
+    const int s = 256 / tiles;
+    return s > cap ? (cap < 1 ? 1 : cap) : (s < 1 ? 1 : s);
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -289,6 +366,17 @@ __global__ __launch_bounds__(256) void k_f32_down(int M, int d, int I, const int
 
 }  // namespace
 
+// fp32 partial-sum bytes the shared expert's split-K passes need (0 when
+// T is large enough not to split, or for other weight types).
+size_t ffn_shared_split_bytes(int M, int d, int I, int wt) {
+    if (wt != kBF16 || d % BK || I % BK) return 0;
+    const int mt = (M + BM - 1) / BM;
+    const int s_gu = ksplits(mt * (I / (BNB / 2)), d / BK), s_dn = ksplits(mt * (d / BNB), I / BK);
+    const size_t gu = s_gu > 1 ? (size_t)s_gu * M * 2 * I * sizeof(float) : 0;
+    const size_t dn = s_dn > 1 ? (size_t)s_dn * M * d * sizeof(float) : 0;
+    return gu > dn ? gu : dn;
+}
+
 hipError_t launch_ffn(const FfnArgs &a, hipStream_t s) {
     const bool routed = a.offsets != nullptr;
     if (a.wt == kF32) {
@@ -318,7 +406,17 @@ hipError_t launch_ffn(const FfnArgs &a, hipStream_t s) {
         p.B1 = static_cast<const uint16_t *>(a.w.up);
         p.N = a.I;
         p.out = static_cast<uint16_t *>(a.h);
-        if (a.phases & 1) hipLaunchKernelGGL(k_gemm_bf16<EPI_SWIGLU>, dim3(slots, a.I / (BNB / 2)), dim3(256), 0, s, p);
+        const int mt = (a.M + BM - 1) / BM;
+        const int s_gu = routed || !a.part ? 1 : ksplits(mt * (a.I / (BNB / 2)), a.d / BK);
+        const int s_dn = routed || !a.part ? 1 : ksplits(mt * (a.d / BNB), a.I / BK);
+        if ((a.phases & 1) && s_gu > 1) {
+            p.part = a.part;
+            hipLaunchKernelGGL(k_gemm_bf16<EPI_PART_DUAL>, dim3(slots, a.I / (BNB / 2), s_gu), dim3(256), 0, s, p);
+            hipLaunchKernelGGL(k_split_swiglu, dim3((a.M * (a.I / 4) + 255) / 256), dim3(256), 0, s, a.M, a.I, s_gu,
+                               a.part, static_cast<uint16_t *>(a.h));
+        } else if (a.phases & 1) {
+            hipLaunchKernelGGL(k_gemm_bf16<EPI_SWIGLU>, dim3(slots, a.I / (BNB / 2)), dim3(256), 0, s, p);
+        }
         if (!(a.phases & 2)) return hipGetLastError();
         GemmParams q{};
         q.M = a.M;
@@ -327,7 +425,13 @@ hipError_t launch_ffn(const FfnArgs &a, hipStream_t s) {
         q.K = a.I;
         q.B0 = static_cast<const uint16_t *>(a.w.down);
         q.N = a.d;
-        if (a.combine) {
+        if (a.combine && s_dn > 1) {
+            q.part = a.part;
+            hipLaunchKernelGGL(k_gemm_bf16<EPI_PART>, dim3(slots, a.d / BNB, s_dn), dim3(256), 0, s, q);
+            hipLaunchKernelGGL(k_split_combine, dim3((a.M * (a.d / 4) + 255) / 256), dim3(256), 0, s, a.M, a.d, s_dn,
+                               a.k, a.part, static_cast<const uint16_t *>(a.y_perm), a.row_of, a.cw,
+                               static_cast<float *>(a.y));
+        } else if (a.combine) {
             q.yout = static_cast<float *>(a.y);
             q.y_perm = static_cast<const uint16_t *>(a.y_perm);
             q.row_of = a.row_of;

@@ -71,8 +71,12 @@ struct FfnArgs {
     const void *y_perm;
     const int32_t *row_of;
     const float *cw;
+    // shared expert at small T: fp32 workspace for split-K partial sums
+    // (ffn_shared_split_bytes; nullptr = no split)
+    float *part;
 };
 hipError_t launch_ffn(const FfnArgs &a, hipStream_t s);
+size_t ffn_shared_split_bytes(int M, int d, int I, int wt);
 // y[t] += sum_{j<k} cw[t*k+j] * y_perm[row_of[t*k+j]] (bf16 rows, fp32, ascending j).
 hipError_t launch_combine_add(int T, int d, int k, const uint16_t *y_perm, const int32_t *row_of, const float *cw,
                               float *y, hipStream_t s);

@@ -63,7 +63,11 @@ size_t route_ws(const moe_desc_t *d) {
     return d->act == MOE_BF16 && moe::route_bf16_ok(d->d) ? align_up(moe::route_bf16_ws_bytes(d->T, d->d)) : 0;
 }
 
-size_t combine_ws(const moe_desc_t *d) { return ffn_ws(d->T, d).total + xq_bytes(d); }
+// The shared expert + combine: h (+ scales), x quantised (e4m3), and fp32
+// split-K partials at small T (bf16).
+size_t combine_ws(const moe_desc_t *d) {
+    return ffn_ws(d->T, d).total + xq_bytes(d) + align_up(moe::ffn_shared_split_bytes(d->T, d->d, d->I, d->wt));
+}
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
@@ -241,6 +245,8 @@ moe_status_t moe_combine(const moe_desc_t *d, const void *x, const moe_ffn_weigh
     a.y_perm = y_perm;
     a.row_of = row_of;
     a.cw = weights;
+    if (moe::ffn_shared_split_bytes(d->T, d->d, d->I, d->wt))
+        a.part = reinterpret_cast<float *>(ws + w.total + xq_bytes(d));
     return hip_status(moe::launch_ffn(a, s));
 }
 

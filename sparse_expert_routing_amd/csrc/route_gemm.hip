@@ -183,14 +183,22 @@ __global__ __launch_bounds__(256) void k_route_topk(int T, int S, const float *_
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    float sv[4];
+    float sv[4], l[4];
     uint64_t key[4];
+    const float *lt = logits + (size_t)t * kE + lane;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) l[q] = lt[64 * q];
+    // K splits, added in split order; unrolled so several loads are in flight
+#pragma unroll 4
+    for (int z = 1; z < S; ++z) {
+        const float *lz = lt + (size_t)z * T * kE;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) l[q] += lz[64 * q];
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int e = lane + 64 * q;
-        float l = logits[(size_t)t * kE + e];
-        for (int z = 1; z < S; ++z) l += logits[((size_t)z * T + t) * kE + e];  // K splits, in order
-        sv[q] = 1.0f / (1.0f + expf(-l));
+        sv[q] = 1.0f / (1.0f + expf(-l[q]));
         key[q] = ((uint64_t)f32_order_key(sv[q] + bias[e]) << 32) | (uint32_t)(kE - 1 - e);
     }
     constexpr int kRounds = kK + 1;  // one extra round gives the gap

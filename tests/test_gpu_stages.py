@@ -290,12 +290,15 @@ def test_gate_up_rows_matches_materialised(wt, T, d, I, kind):
 
 # ---------------------------------------------------------------- combine
 
-@pytest.mark.parametrize("wt,T", [("f32", 32), ("bf16", 100), ("bf16", 257), ("bf16", 1000), ("e4m3", 100),
-                                  ("e4m3", 257)])
-def test_combine(wt, T):
+@pytest.mark.parametrize("wt,T,d,I", [("f32", 32, 256, 128), ("bf16", 100, 256, 128), ("bf16", 257, 256, 128),
+                                      ("bf16", 1000, 256, 128), ("e4m3", 100, 256, 128), ("e4m3", 257, 256, 128),
+                                      # small T, wide d / I: the shared expert splits K (equal and
+                                      # unequal split lengths, one and two row tiles, a single token)
+                                      ("bf16", 100, 2048, 512), ("bf16", 1, 2048, 512), ("bf16", 130, 1024, 832)])
+def test_combine(wt, T, d, I):
     act = "f32" if wt == "f32" else "bf16"
-    cfg = synth.Config("comb", seed=31, T=T, d=256, I=128, act=act, wt=wt)
-    say(f"[combine] {wt} T={T}")
+    cfg = synth.Config("comb", seed=31, T=T, d=d, I=I, act=act, wt=wt)
+    say(f"[combine] {wt} T={T} d={d} I={I}")
     shared = synth.make_ffn(cfg, 1, (synth.TID_SGATE, synth.TID_SUP, synth.TID_SDOWN))
     x = synth.normal(cfg.seed, synth.TID_X, (T, cfg.d), 1.0, act)
     idx = ids_case("random", T)
