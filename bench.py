@@ -163,7 +163,7 @@ def main():
         peak = peak_flops
     large = A >= 128 * E
     kname = ("k_gemm_fp8_large" if large else "k_gemm_fp8") if cfg.wt == "e4m3" else \
-        ("k_gemm_bf16_large" if large else "k_gemm_bf16")
+        ("k_gemm_bf16_large" if large else "k_gemm_skinny" if A <= 4 * E else "k_gemm_bf16")
     total_flops = 2.0 * T * d * E + 6.0 * (A + T) * d * I
     ms_step = wall / K * 1e3
     log(f"[bench] {ms_step:.3f} ms/step, phases (ms): " + ", ".join(f"{n} {v:.3f}" for n, v in phase.items()))

@@ -393,6 +393,7 @@ hipError_t launch_ffn(const FfnArgs &a, hipStream_t s) {
         return hipGetLastError();
     }
     if (a.wt == kBF16) {
+        if (ffn_skinny_ok(a)) return launch_ffn_skinny(a, s);
         if (ffn_bf16_large_ok(a)) return launch_ffn_bf16_large(a, s);
         const int slots = (a.M + BM - 1) / BM + (routed ? kE : 0);
         GemmParams p{};

@@ -81,6 +81,10 @@ size_t ffn_shared_split_bytes(int M, int d, int I, int wt);
 hipError_t launch_combine_add(int T, int d, int k, const uint16_t *y_perm, const int32_t *row_of, const float *cw,
                               float *y, hipStream_t s);
 hipError_t launch_ffn_fp8(const FfnArgs &a, hipStream_t s);
+// Tiny-group bf16 path (decode: routed groups averaging at most 4 rows):
+// weights streamed from HBM into registers, K split over the 4 waves.
+bool ffn_skinny_ok(const FfnArgs &a);
+hipError_t launch_ffn_skinny(const FfnArgs &a, hipStream_t s);
 // Large-group bf16 path (persistent 256x256 tiles): usable when every group
 // averages at least 128 rows and the widths tile evenly.
 bool ffn_bf16_large_ok(const FfnArgs &a);

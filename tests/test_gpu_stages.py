@@ -188,6 +188,25 @@ def test_expert_ffn_small(wt, kind, T):
     assert err <= TOL[wt], err
 
 
+@pytest.mark.parametrize("kind,T,d,I", [("random", 40, 1024, 512), ("skewed", 100, 512, 512), ("same8", 17, 512, 1024),
+                                      ("random", 1, 512, 512), ("same8", 16, 1536, 512), ("random", 128, 512, 512)])
+def test_expert_ffn_tiny_groups(kind, T, d, I):
+    """Decode-sized groups (T*8 <= 4*256 rows, bf16): the weight-streaming
+    path with K split over the waves and 16-row passes.  Cases: empty
+    experts, a single row, exactly 16 rows, 17 rows (a second pass of one
+    row), 100-row hot experts (seven passes), odd chunk counts per wave
+    (d=1536), and the largest T the path takes."""
+    cfg = synth.Config("ffn-tiny", seed=22, T=T, d=d, I=I, wt="bf16")
+    say(f"[ffn] tiny groups {kind} T={T} d={d} I={I}")
+    experts = synth.make_ffn(cfg, 256, (synth.TID_GATE, synth.TID_UP, synth.TID_DOWN))
+    offsets, a_rows, a_sc = ffn_inputs(cfg, kind)
+    y = run_ffn(cfg, offsets, a_rows, a_sc, experts)
+    yo = oracle.expert_ffn(oracle.shape_of(cfg), experts, offsets, a_rows, a_sc)
+    err = max_rel(yvals(y, "bf16"), yvals(yo, "bf16"))
+    say(f"[ffn] tiny groups {kind} T={T}: max rel err {err:.3e}")
+    assert err <= TOL["bf16"], err
+
+
 @pytest.mark.parametrize("wt", ["bf16", "e4m3"])
 @pytest.mark.parametrize("kind", ["random", "skewed", "same8"])
 def test_expert_ffn_large_groups(kind, wt):
@@ -263,7 +282,8 @@ def run_ffn_rows(cfg, offsets, row_src, x, experts):
 
 
 @pytest.mark.parametrize("wt,T,d,I,kind", [("f32", 40, 256, 128, "random"), ("bf16", 300, 256, 128, "same8"),
-                                           ("bf16", 4096, 512, 256, "skewed"), ("e4m3", 257, 256, 128, "skewed"),
+                                           ("bf16", 4096, 512, 256, "skewed"), ("bf16", 100, 512, 512, "skewed"),
+                                           ("e4m3", 257, 256, 128, "skewed"),
                                            ("e4m3", 1000, 256, 128, "random")])
 def test_gate_up_rows_matches_materialised(wt, T, d, I, kind):
     """Gate/up reading the token rows through row_src (no x_perm) gives the
