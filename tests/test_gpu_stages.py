@@ -194,8 +194,8 @@ def test_expert_ffn_tiny_groups(kind, T, d, I):
     """Decode-sized groups (T*8 <= 4*256 rows, bf16): the weight-streaming
     path with K split over the waves and 16-row passes.  Cases: empty
     experts, a single row, exactly 16 rows, 17 rows (a second pass of one
-    row), 100-row hot experts (seven passes), odd chunk counts per wave
-    (d=1536), and the largest T the path takes."""
+    row), 100-row hot experts (seven passes), a chunk count per wave that is
+    not a power of two (d=1536: 6), and the largest T the path takes."""
     cfg = synth.Config("ffn-tiny", seed=22, T=T, d=d, I=I, wt="bf16")
     say(f"[ffn] tiny groups {kind} T={T} d={d} I={I}")
     experts = synth.make_ffn(cfg, 256, (synth.TID_GATE, synth.TID_UP, synth.TID_DOWN))
