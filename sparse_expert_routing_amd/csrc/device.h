@@ -58,13 +58,39 @@ __device__ __forceinline__ float f32_from_order_key(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+// v from lane (lane permuted by the DPP control CTRL), 64-bit.  A lane whose
+// source is out of range keeps its own value (old = v).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+    const uint32_t plo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xf, 0xf, false);
+    const uint32_t phi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xf, 0xf, false);
+    return ((uint64_t)phi << 32) | plo;
+}
+
+// Maximum over the 64 lanes of a full wave (every lane active), returned
+// wave-uniform: DPP within each 16-lane row (quad swaps xor 1 and xor 2, then
+// the half-row and row mirrors), then the four row maxima read from lanes
+// 0, 16, 32, 48.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    uint64_t o;
+    o = dpp_u64<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = o > v ? o : v;
+    o = dpp_u64<0x4E>(v);   // quad_perm [2,3,0,1]
+    v = o > v ? o : v;
+    o = dpp_u64<0x141>(v);  // row_half_mirror: lane i <-> 7 - i within 8
+    v = o > v ? o : v;
+    o = dpp_u64<0x140>(v);  // row_mirror: lane i <-> 15 - i within 16
+    v = o > v ? o : v;
+    uint64_t m = 0;
 #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-        uint64_t o = __shfl_xor(v, s, kWave);
-        v = o > v ? o : v;
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r);
+        const uint64_t x = ((uint64_t)hi << 32) | lo;
+        m = x > m ? x : m;
     }
-    return v;
+    return m;
 }
 
 __device__ __forceinline__ float wave_max_f32(float v, int width) {
