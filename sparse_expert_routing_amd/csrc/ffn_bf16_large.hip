@@ -49,6 +49,10 @@ constexpr int LM = 256;      // rows per tile
 constexpr int LB = 256;      // B rows per tile
 constexpr int LK = 64;       // K per stage: 128-byte rows (whole L2 lines)
 constexpr int NUNIT = 5;     // LDS ring units of one stage operand (5 x 32 KB)
+// A buffer-load byte offset past the end of every operand (the host keeps
+// operands below kOobOff - 1 MB, and a stage offset, < 1 MB, added to it
+// stays below 2^32): such a load fetches nothing.
+constexpr uint32_t kOobOff = 0xFFFF0000u;
 constexpr int UNIT_ELEMS = LM * LK;
 static_assert(LM == LB, "A and B stage slabs share the unit size");
 constexpr int kGroupM = 8;   // row tiles per ordering group
@@ -281,6 +285,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
             const int r = drow[i];                                                             \
             const int br = DUAL ? n0 + (r & (BN - 1)) : n0 + r;                                \
             boff[i] = ((uint32_t)br * (uint32_t)K + (uint32_t)dcol[i]) * 2u;                   \
+            /* rows past the group's end: an offset past the A resource, so the */             \
+            /* load fetches nothing (their outputs are dropped) */                              \
+            if (m0 + r >= m_end) aoff[i] = kOobOff;                                             \
         }                                                                                      \
     }
     // A_0, B_0, A_1, B_1 of the tile just set up (32 loads per wave).
@@ -560,12 +567,13 @@ int cu_count() {
 bool ffn_bf16_large_ok(const FfnArgs &a) {
     const int groups = a.offsets ? a.E : 1;
     // DMA offsets are 32-bit bytes from each operand's base (A rows, h rows,
-    // one expert's weights)
-    const unsigned long long lim = 1ULL << 32;
+    // one expert's weights); every operand ends below the out-of-range
+    // offset kOobOff (plus a stage offset) used for padding rows
+    const unsigned long long lim = kOobOff - (1ULL << 20);
     const bool fits = (unsigned long long)a.M * a.d * 2 < lim && (unsigned long long)a.M * a.I * 2 < lim &&
                       (unsigned long long)a.I * a.d * 2 < lim;
     return fits && (long long)a.M >= 128LL * groups && a.I % 128 == 0 && a.d % 256 == 0 && a.d % LK == 0 &&
-           a.I % LK == 0;
+           a.I % LK == 0 && a.d < (1 << 19) && a.I < (1 << 19);
 }
 
 hipError_t launch_ffn_bf16_large(const FfnArgs &a, hipStream_t s) {
