@@ -8,21 +8,21 @@
 // 128x128 weight block; partial sums are promoted to fp32 every 128 of K.
 //
 // Design for gfx950 (shared with the bf16 large-tile kernel where it can be):
-//   - 4 waves (2x2), each a 128x128 block of the 256x256 tile; the fp32
-//     accumulators (256 per lane) live in AGPRs;
+//   - 8 waves (2 per SIMD) in a 2x4 layout, each a 128x64 block of the
+//     256x256 tile; its fp32 accumulators (128 per lane) live in VGPRs;
 //   - one stage = 128 of K = one scale block: A and B slabs of 256 rows x
 //     128 bytes (whole L2 lines) in a ring of five 32 KB LDS units filled by
 //     buffer_load_dwordx4 ... lds (scalar resource, fixed per-lane offset,
 //     stage offset in an SGPR); during stage s, after its one barrier,
 //     B_{s+1} and A_{s+2} stream into the two units stage s-1 left, one load
 //     per output block, so B has about a stage and A two stages to land;
-//   - a stage's fragments (32 bytes per lane per 32x64 block) are read once
-//     into VGPRs; each 32x32 output block takes two
-//     v_mfma_scale_f32_32x32x64_f8f6f4 (scales 0: plain fp8) into a fresh
-//     VGPR partial, which is folded into its AGPR accumulator scaled by
-//     s_a[row, kb] * s_w[block, kb] (v_accvgpr_read, fma, v_accvgpr_write:
-//     the promotion is vector-ALU work of 3 operations per output element
-//     per 128 of K, the price of fp32 scales that are not powers of two);
+//   - each 32x32 output block takes two v_mfma_scale_f32_32x32x64_f8f6f4
+//     (scales 0: plain fp8) into a fresh VGPR partial, then one fma per
+//     element folds it into the accumulator scaled by
+//     s_a[row, kb] * s_w[block, kb] (the promotion every 128 of K; the
+//     scales are arbitrary fp32, so it cannot ride on the MFMA's
+//     power-of-two block scales); while one wave folds, the other wave of
+//     its SIMD keeps the matrix unit busy;
 //   - the MFMA operands are swapped, so a lane owns one tile row and runs
 //     of 4 consecutive output columns: per-row activation scales are per
 //     lane, weight scales per wave;
@@ -30,9 +30,9 @@
 //     loads, so one vmcnt wait per stage covers both;
 //   - epilogues: gate/up forms h = silu(g) * u in fp32 and quantises it per
 //     1x128 tile (the tile's 128 h columns; the row amax is combined across
-//     the two column waves through LDS), scale = amax / 448 (1 for an all-zero
-//     tile), code = e4m3(h / scale); down stores bf16 y_perm, or the shared
-//     expert's fp32 output (the routed sum is added by k_combine_add).
+//     the four column waves through LDS), scale = amax / 448 (1 for an
+//     all-zero tile), code = e4m3(h / scale); down stores bf16 y_perm, or the
+//     shared expert's fp32 output (the routed sum is added by k_combine_add).
 #include "device.h"
 #include "kernels.h"
 
@@ -149,40 +149,33 @@ __device__ __forceinline__ i32x8 frag32(const uint8_t *unit, int row, int c) {
     return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// AGPR-resident accumulator element: the moves keep it in an AGPR between
-// uses (left to the compiler, 256 accumulators touched by vector ALU work
-// would be placed in VGPRs and spill).
-__device__ __forceinline__ float acc_get(float a) {
-    float r;
-    asm("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(a));
-    return r;
-}
-__device__ __forceinline__ float acc_put(float v) {
-    float a;
-    asm("v_accvgpr_write_b32 %0, %1" : "=a"(a) : "v"(v));
-    return a;
-}
-
 __device__ __forceinline__ float swiglu(float g, float u) {
     return g * u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
 }
 
+// Eight waves (two per SIMD), each owning 128 rows x 64 columns of the
+// 256x256 tile: its 128 fp32 accumulators fit in VGPRs, so the per-128-K
+// promotion is one fma per element, and while one wave of a SIMD waits on
+// its MFMA result, LDS or the barrier, the other issues.  A wave's DMA
+// share is 4 of the 32 one-KB blocks of each operand slab.
 template <int EPI, bool ROUTED>
-__global__ __launch_bounds__(256, 1) void k_gemm_fp8_large(F8Params p) {
+__global__ __launch_bounds__(512, 1) void k_gemm_fp8_large(F8Params p) {
     constexpr bool DUAL = EPI == EPI_SWIGLU_Q;
     constexpr int BN = DUAL ? LB / 2 : LB;  // output columns per tile
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NUNIT * UNIT_BYTES];  // 160 KB
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1, g = lane >> 5;
+    const int wm = wave >> 2, wn = wave & 3, g = lane >> 5;
     const int K = p.K, nk = K / LK;
 
-    TileMap tm;
+    // (the tile map is rebuilt per tile rather than kept: its registers are
+    // needed by the K loop)
     int Mt;
     if (ROUTED) {
-        tilemap_init(tm, p.offsets);
-        Mt = tm.total;
+        TileMap tm0;
+        tilemap_init(tm0, p.offsets);
+        Mt = tm0.total;
     } else {
         Mt = (p.M + LM - 1) / LM;
     }
@@ -190,12 +183,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_large(F8Params p) {
     const int total = Mt * NT;
     const int P = gridDim.x;
 
-    // DMA geometry (bytes, as the bf16 kernel): wave w moves blocks w + 4i of
-    // each operand; lane l fills physical piece (l & 7) of row 8*blk + (l >> 3).
-    int drow[8], dcol[8];
+    // DMA geometry: wave w moves blocks w + 8i (i < 4) of each operand slab;
+    // lane l fills physical piece (l & 7) of row 8*blk + (l >> 3).
+    int drow[4], dcol[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = 8 * (wave + 4 * i) + (lane >> 3);
+    for (int i = 0; i < 4; ++i) {
+        const int row = 8 * (wave + 8 * i) + (lane >> 3);
         drow[i] = row;
         dcol[i] = ((lane & 7) ^ (row & 7) ^ ((row >> 3) & 1)) * 16;
     }
@@ -215,6 +208,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_large(F8Params p) {
         const int mt = mfirst + within % gm, nt = within / gm;
         int e, m0, m_end;
         if (ROUTED) {
+            TileMap tm;
+            tilemap_init(tm, p.offsets);
             tilemap_find(tm, mt, e, m0, m_end);
         } else {
             e = 0;
@@ -228,19 +223,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_large(F8Params p) {
 
         const __amdgpu_buffer_rsrc_t rBg = buf_rsrc(uniform_ptr(p.B0 + (size_t)e * p.N * K), b_bytes);
         const __amdgpu_buffer_rsrc_t rBu = DUAL ? buf_rsrc(uniform_ptr(p.B1 + (size_t)e * p.N * K), b_bytes) : rBg;
-        uint32_t aoff[8], boff[8];
+        uint32_t aoff[4], boff[4];
         {
-            int ar_[8];
+            int ar_[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) ar_[i] = min(m0 + drow[i], m_end - 1);
+            for (int i = 0; i < 4; ++i) ar_[i] = min(m0 + drow[i], m_end - 1);
             if (p.a_rows) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) ar_[i] = p.a_rows[ar_[i]];
+                for (int i = 0; i < 4; ++i) ar_[i] = p.a_rows[ar_[i]];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) ar_[i] /= p.a_div;
+                for (int i = 0; i < 4; ++i) ar_[i] /= p.a_div;
             }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 4; ++i) {
                 aoff[i] = (uint32_t)ar_[i] * (uint32_t)K + (uint32_t)dcol[i];
                 const int r = drow[i];
                 const int br = DUAL ? n0 + (r & (BN - 1)) : n0 + r;
@@ -248,7 +243,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_large(F8Params p) {
             }
         }
         // this lane's 4 tile rows (wm*128 + 32i + (lane & 31)): activation-
-        // scale byte offsets (row * nk * 4; rows past the group repeat its last)
+        // scale byte offsets (rows past the group repeat its last)
         uint32_t soff[4];
         {
             int sr[4];
@@ -261,17 +256,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_large(F8Params p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) soff[i] = (uint32_t)sr[i] * (uint32_t)nk * 4u;
         }
-        // weight scales: block row of this wave's B columns (gate and up for
-        // the SwiGLU tile), [G, N/128, K/128]
-        const float *swg_p = p.S0 + ((size_t)e * nbk + (DUAL ? n0 : n0 + wn * 128) / 128) * nk;
+        // weight scales: the 128-column block of this wave's columns (gate
+        // and up blocks of the SwiGLU tile), [G, N/128, K/128]
+        const float *swg_p = p.S0 + ((size_t)e * nbk + (DUAL ? n0 : n0 + wn * 64) / 128) * nk;
         const float *swu_p = DUAL ? p.S1 + ((size_t)e * nbk + n0 / 128) * nk : swg_p;
 
 #define ISSUE_A(st_, i, unit_)                                                                 \
-        dma_buf(rA, aoff[i], (uint32_t)min((st_), nk - 1) * LK, (unit_) + (wave + 4 * (i)) * 1024)
+        dma_buf(rA, aoff[i], (uint32_t)min((st_), nk - 1) * LK, (unit_) + (wave + 8 * (i)) * 1024)
 #define ISSUE_B(st_, i, unit_)                                                                 \
-        dma_buf((DUAL && (i) >= 4) ? rBu : rBg, boff[i], (uint32_t)min((st_), nk - 1) * LK,        \
-                (unit_) + (wave + 4 * (i)) * 1024)
-        // scales of stage st_ into sa_[4], sw_[2] (5-6 vector loads per lane)
+        dma_buf((DUAL && (i) >= 2) ? rBu : rBg, boff[i], (uint32_t)min((st_), nk - 1) * LK,        \
+                (unit_) + (wave + 8 * (i)) * 1024)
 #define LOAD_SCALES(st_, sa_, sw_)                                                             \
         {                                                                                      \
             const int kb_ = min((st_), nk - 1);                                                \
@@ -281,90 +275,65 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_large(F8Params p) {
             sw_[1] = DUAL ? swu_p[kb_] : sw_[0];                                               \
         }
 
-        float acc[4][4][16];
+        f32x16 acc[4][2];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = acc_put(0.f);
+            for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
         // Prologue: scales(0), A_0, B_0, A_1 in flight.
         float sa[4], sw[2], sa_n[4], sw_n[2];
         LOAD_SCALES(0, sa, sw);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ISSUE_A(0, i, UNIT(0));
+        for (int i = 0; i < 4; ++i) ISSUE_A(0, i, UNIT(0));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ISSUE_B(0, i, UNIT(1));
+        for (int i = 0; i < 4; ++i) ISSUE_B(0, i, UNIT(1));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ISSUE_A(1, i, UNIT(2));
+        for (int i = 0; i < 4; ++i) ISSUE_A(1, i, UNIT(2));
 
         int u0 = 0;  // unit of A_kt (2kt mod 5)
         for (int kt = 0; kt < nk; ++kt) {
             const int u1 = u0 + 1 - (u0 + 1 >= NUNIT ? NUNIT : 0);
             const int u3 = u0 + 3 - (u0 + 3 >= NUNIT ? NUNIT : 0);
             const int u4 = u0 + 4 - (u0 + 4 >= NUNIT ? NUNIT : 0);
-            // A_kt, B_kt and this stage's scales landed (only A_{kt+1}, 8
+            // A_kt, B_kt and this stage's scales landed (only A_{kt+1}, 4
             // loads, may still be in flight) for every wave; the units of
             // stage kt-1 are no longer read by anyone.
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            wait_vmcnt_lds<8>();
+            wait_vmcnt_lds<4>();
             __builtin_amdgcn_s_barrier();
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             LOAD_SCALES(kt + 1, sa_n, sw_n);
             uint8_t *fB = UNIT(u3), *fA = UNIT(u4);  // B_{kt+1}, A_{kt+2}: one load per block below
 
             const uint8_t *cA = UNIT(u0), *cB = UNIT(u1);
-            // B fragments of the whole stage (4 column blocks x 2 K halves);
-            // A fragments per row block, double-buffered: row block i+1 is read
-            // while row block i is multiplied.
-            i32x8 bf[4][2], af[2][2];
+            // B fragments of the whole stage (2 column blocks x 2 K halves);
+            // A fragments per row block.  One partial: while this wave folds
+            // it, the other wave on the SIMD keeps the matrix unit busy.
+            i32x8 bf[2][2], af[2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int brow = (DUAL ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32)) + (lane & 31);
+            for (int j = 0; j < 2; ++j) {
+                const int brow = (DUAL ? (j * 128 + wn * 32) : (wn * 64 + j * 32)) + (lane & 31);
 #pragma unroll
                 for (int s = 0; s < 2; ++s) bf[j][s] = frag32(cB, brow, 4 * s + 2 * g);
             }
-#define READ_A(i_, buf_)                                                                       \
-            _Pragma("unroll") for (int s = 0; s < 2; ++s)                                      \
-                af[buf_][s] = frag32(cA, wm * 128 + 32 * (i_) + (lane & 31), 4 * s + 2 * g);
-            READ_A(0, 0);
-            // Block n = (i, j) = (n >> 2, n & 3).  Software pipeline with two
-            // partials: the MFMA pair of block n+1 is issued before block n is
-            // folded, so the matrix pipe works while the vector ALU folds.
-            f32x16 tp[2];
             const f32x16 zero = {};
-#define MF2(n_, T_)                                                                            \
-            T_ = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[(n_) & 3][0], af[((n_) >> 2) & 1][0], zero, 0, 0, \
-                                                                 0, 0, 0, 0);                  \
-            T_ = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[(n_) & 3][1], af[((n_) >> 2) & 1][1], T_, 0, 0, 0, \
-                                                                 0, 0, 0);
-            MF2(0, tp[0]);
 #pragma unroll
-            for (int n = 0; n < 16; ++n) {
-                if ((n & 3) == 0 && n + 4 < 16) {
-                    READ_A((n >> 2) + 1, ((n >> 2) + 1) & 1);
+            for (int n = 0; n < 8; ++n) {
+                const int i = n >> 1, j = n & 1;
+                if (j == 0) {
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) af[s] = frag32(cA, wm * 128 + 32 * i + (lane & 31), 4 * s + 2 * g);
                 }
-                if (n + 1 < 16) {
-                    MF2(n + 1, tp[(n + 1) & 1]);
-                }
+                f32x16 tp = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j][0], af[0], zero, 0, 0, 0, 0, 0, 0);
+                tp = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j][1], af[1], tp, 0, 0, 0, 0, 0, 0);
                 // one slot load per block (B first: it has one stage to land)
-                if (n < 8) ISSUE_B(kt + 1, n, fB);
-                else ISSUE_A(kt + 2, n - 8, fA);
-                __builtin_amdgcn_sched_barrier(0);
-                const int i = n >> 2, j = n & 3;
-                const float sc = sa[i] * sw[DUAL ? (j >> 1) : 0];
-                float cur[16];
+                if (n < 4) ISSUE_B(kt + 1, n, fB);
+                else ISSUE_A(kt + 2, n - 4, fA);
+                const float sc = sa[i] * sw[DUAL ? j : 0];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) cur[r] = acc_get(acc[i][j][r]);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) cur[r] = fmaf(tp[n & 1][r], sc, cur[r]);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = acc_put(cur[r]);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(tp[r], sc, acc[i][j][r]);
             }
-#undef MF2
-#undef READ_A
 #pragma unroll
             for (int i = 0; i < 4; ++i) sa[i] = sa_n[i];
             sw[0] = sw_n[0];
@@ -380,23 +349,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_large(F8Params p) {
         // columns 8q + 4g + u (u = 0..3) in acc[i][j][4q + u]
         const int c4 = 4 * g;
         if constexpr (DUAL) {
-            // h columns of this wave: wn*64 + jj*32 + 8q + 4g + u; the tile's
-            // 128 h columns are one quantisation tile
-            float *xch = reinterpret_cast<float *>(UNIT(4));  // [2][256] partial row amax
-            float hv[4][2][16];
+            // h columns of this wave: wn*32 + 8q + 4g + u; the tile's 128 h
+            // columns are one quantisation tile, spread over the 4 column waves
+            float *xch = reinterpret_cast<float *>(UNIT(4));  // [4][256] partial row amax
+            float hv[4][16];
             float am[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float m = 0.f;
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float h = swiglu(acc_get(acc[i][jj][r]), acc_get(acc[i][2 + jj][r]));
-                        hv[i][jj][r] = h;
-                        m = fmaxf(m, fabsf(h));
-                    }
-                m = fmaxf(m, __shfl_xor(m, 32, 64));  // the other 32 columns of this wave
+                for (int r = 0; r < 16; ++r) {
+                    const float h = swiglu(acc[i][0][r], acc[i][1][r]);
+                    hv[i][r] = h;
+                    m = fmaxf(m, fabsf(h));
+                }
+                m = fmaxf(m, __shfl_xor(m, 32, 64));  // the other 16 columns of this wave
                 am[i] = m;
                 if (g == 0) xch[wn * 256 + wm * 128 + 32 * i + lane] = m;
             }
@@ -407,20 +374,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_large(F8Params p) {
             for (int i = 0; i < 4; ++i) {
                 const int tr = wm * 128 + 32 * i + (lane & 31);
                 const int row = m0 + tr;
-                const float amax = fmaxf(am[i], xch[(wn ^ 1) * 256 + tr]);
+                float amax = am[i];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) amax = fmaxf(amax, xch[w * 256 + tr]);
                 const float s = amax > 0.f ? amax / 448.0f : 1.0f;
                 const bool ok = row < m_end;
                 const uint32_t qbase = ok ? (uint32_t)row * (uint32_t)p.H + (uint32_t)n0 : 0xfffff000u;
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj)
+                for (int q = 0; q < 4; ++q) {
+                    uint32_t w = 0;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        uint32_t w = 0;
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) w |= f32_to_e4m3(hv[i][jj][4 * q + u] / s) << (8 * u);
-                        __builtin_amdgcn_raw_buffer_store_b32((int)w, rQ,
-                                                              qbase + (uint32_t)(wn * 64 + jj * 32 + 8 * q + c4), 0, 0);
-                    }
+                    for (int u = 0; u < 4; ++u) w |= f32_to_e4m3(hv[i][4 * q + u] / s) << (8 * u);
+                    __builtin_amdgcn_raw_buffer_store_b32((int)w, rQ, qbase + (uint32_t)(wn * 32 + 8 * q + c4), 0, 0);
+                }
                 if (wn == 0 && g == 0) {
                     const uint32_t so = ok ? ((uint32_t)row * (uint32_t)(p.H / 128) + (uint32_t)(n0 / 128)) * 4u
                                            : 0xfffff000u;
@@ -435,12 +401,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_large(F8Params p) {
                 const int row = m0 + wm * 128 + 32 * i + (lane & 31);
                 const uint32_t obase = row < m_end ? ((uint32_t)row * (uint32_t)p.N + (uint32_t)n0) * 2u : 0xfffff000u;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const uint32_t lo = pack_bf16x2(acc_get(acc[i][j][4 * q]), acc_get(acc[i][j][4 * q + 1]));
-                        const uint32_t hi = pack_bf16x2(acc_get(acc[i][j][4 * q + 2]), acc_get(acc[i][j][4 * q + 3]));
-                        const int col = wn * 128 + j * 32 + 8 * q + c4;
+                        const uint32_t lo = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+                        const uint32_t hi = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                        const int col = wn * 64 + j * 32 + 8 * q + c4;
                         __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)lo, (int)hi}, rOut, obase + (uint32_t)col * 2u,
                                                               0, 0);
                     }
@@ -452,14 +418,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_large(F8Params p) {
                 const int row = m0 + wm * 128 + 32 * i + (lane & 31);
                 const uint32_t obase = row < m_end ? ((uint32_t)row * (uint32_t)p.N + (uint32_t)n0) * 4u : 0xfffff000u;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const int col = wn * 128 + j * 32 + 8 * q + c4;
+                        const int col = wn * 64 + j * 32 + 8 * q + c4;
                         __builtin_amdgcn_raw_buffer_store_b128(
-                            i32x4{__float_as_int(acc_get(acc[i][j][4 * q])), __float_as_int(acc_get(acc[i][j][4 * q + 1])),
-                                  __float_as_int(acc_get(acc[i][j][4 * q + 2])),
-                                  __float_as_int(acc_get(acc[i][j][4 * q + 3]))},
+                            i32x4{__float_as_int(acc[i][j][4 * q]), __float_as_int(acc[i][j][4 * q + 1]),
+                                  __float_as_int(acc[i][j][4 * q + 2]), __float_as_int(acc[i][j][4 * q + 3])},
                             rOut, obase + (uint32_t)col * 4u, 0, 0);
                     }
             }
@@ -514,9 +479,9 @@ hipError_t launch_ffn_fp8_large(const FfnArgs &a, hipStream_t s) {
         p.hs = a.h_scale;
         p.H = a.I;
         if (routed)
-            hipLaunchKernelGGL((k_gemm_fp8_large<EPI_SWIGLU_Q, true>), dim3(P), dim3(256), 0, s, p);
+            hipLaunchKernelGGL((k_gemm_fp8_large<EPI_SWIGLU_Q, true>), dim3(P), dim3(512), 0, s, p);
         else
-            hipLaunchKernelGGL((k_gemm_fp8_large<EPI_SWIGLU_Q, false>), dim3(P), dim3(256), 0, s, p);
+            hipLaunchKernelGGL((k_gemm_fp8_large<EPI_SWIGLU_Q, false>), dim3(P), dim3(512), 0, s, p);
     }
     if (a.phases & 2) {
         F8Params q{};
@@ -531,9 +496,9 @@ hipError_t launch_ffn_fp8_large(const FfnArgs &a, hipStream_t s) {
         if (a.combine) {
             q.yout = static_cast<float *>(a.y);
             if (routed)
-                hipLaunchKernelGGL((k_gemm_fp8_large<EPI_F32, true>), dim3(P), dim3(256), 0, s, q);
+                hipLaunchKernelGGL((k_gemm_fp8_large<EPI_F32, true>), dim3(P), dim3(512), 0, s, q);
             else
-                hipLaunchKernelGGL((k_gemm_fp8_large<EPI_F32, false>), dim3(P), dim3(256), 0, s, q);
+                hipLaunchKernelGGL((k_gemm_fp8_large<EPI_F32, false>), dim3(P), dim3(512), 0, s, q);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             return launch_combine_add(a.M, a.d, a.k, static_cast<const uint16_t *>(a.y_perm), a.row_of, a.cw,
@@ -541,9 +506,9 @@ hipError_t launch_ffn_fp8_large(const FfnArgs &a, hipStream_t s) {
         }
         q.out = static_cast<uint16_t *>(a.y);
         if (routed)
-            hipLaunchKernelGGL((k_gemm_fp8_large<EPI_STORE, true>), dim3(P), dim3(256), 0, s, q);
+            hipLaunchKernelGGL((k_gemm_fp8_large<EPI_STORE, true>), dim3(P), dim3(512), 0, s, q);
         else
-            hipLaunchKernelGGL((k_gemm_fp8_large<EPI_STORE, false>), dim3(P), dim3(256), 0, s, q);
+            hipLaunchKernelGGL((k_gemm_fp8_large<EPI_STORE, false>), dim3(P), dim3(512), 0, s, q);
     }
     return hipGetLastError();
 }
