@@ -31,8 +31,10 @@
 //   - epilogues: gate/up forms h = silu(g) * u in fp32 and quantises it per
 //     1x128 tile (the tile's 128 h columns; the row amax is combined across
 //     the four column waves through LDS), scale = amax / 448 (1 for an
-//     all-zero tile), code = e4m3(h / scale); down stores bf16 y_perm, or the
-//     shared expert's fp32 output (the routed sum is added by k_combine_add).
+//     all-zero tile), code = e4m3(h / scale); down stores bf16 y_perm, or (the
+//     shared expert) forms y = acc + sum_j w_j * y_perm[row_of[t*k + j]] in
+//     fp32, ascending j, staging the tile through LDS in 64-row chunks so
+//     each routed row is gathered as one 512-byte run per half-wave.
 #include "device.h"
 #include "kernels.h"
 
@@ -48,7 +50,7 @@ constexpr int NUNIT = 5;     // LDS ring units (5 x 32 KB)
 constexpr int UNIT_BYTES = LM * LK;
 constexpr int kGroupM = 8;   // row tiles per ordering group
 
-enum { EPI_SWIGLU_Q = 0, EPI_STORE = 1, EPI_F32 = 2 };
+enum { EPI_SWIGLU_Q = 0, EPI_STORE = 1, EPI_COMBINE = 2 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef int i32x2 __attribute__((ext_vector_type(2)));
@@ -68,7 +70,10 @@ struct F8Params {
     float *hs;                // EPI_SWIGLU_Q: [M, H/128]
     int H;                    // EPI_SWIGLU_Q: h columns (= N)
     uint16_t *out;            // EPI_STORE: bf16 [M, N]
-    float *yout;              // EPI_F32: f32 [M, N]
+    float *yout;              // EPI_COMBINE: f32 [M, N]
+    const uint16_t *y_perm;   // EPI_COMBINE: routed outputs [M*k, N] bf16
+    const int32_t *row_of;    // EPI_COMBINE: [M*k]
+    const float *cw;          // EPI_COMBINE: combine weights [M*k]
 };
 
 struct TileMap {
@@ -412,21 +417,63 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_large(F8Params p) {
                     }
             }
         } else {
-            const __amdgpu_buffer_rsrc_t rOut = buf_rsrc(p.yout, (uint32_t)p.M * (uint32_t)p.N * 4u);
+            // four 64-row chunks of the fp32 tile through LDS (the ring is
+            // free), then each half-wave gathers one routed output row as a
+            // contiguous 512-byte run
+            constexpr int kChRows = 64, kChLd = LB + 4;
+            float *ch = reinterpret_cast<float *>(smem);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = m0 + wm * 128 + 32 * i + (lane & 31);
-                const uint32_t obase = row < m_end ? ((uint32_t)row * (uint32_t)p.N + (uint32_t)n0) * 4u : 0xfffff000u;
+            for (int c = 0; c < 4; ++c) {
+                if (wm == (c >> 1)) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                    for (int ii = 0; ii < 2; ++ii) {
+                        const int i = 2 * (c & 1) + ii;
+                        const int rl = ii * 32 + (lane & 31);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int col = wn * 64 + j * 32 + 8 * q + c4;
-                        __builtin_amdgcn_raw_buffer_store_b128(
-                            i32x4{__float_as_int(acc[i][j][4 * q]), __float_as_int(acc[i][j][4 * q + 1]),
-                                  __float_as_int(acc[i][j][4 * q + 2]), __float_as_int(acc[i][j][4 * q + 3])},
-                            rOut, obase + (uint32_t)col * 4u, 0, 0);
+                        for (int j = 0; j < 2; ++j)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const int col = wn * 64 + j * 32 + 8 * q + c4;
+                                *reinterpret_cast<f32x4 *>(ch + rl * kChLd + col) =
+                                    f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                            }
                     }
+                }
+                __syncthreads();
+                const int cl = 8 * (lane & 31);
+#pragma unroll 2
+                for (int it = 0; it < 4; ++it) {
+                    const int rl = wave * 8 + 2 * it + g;
+                    const int row = m0 + c * kChRows + rl;
+                    if (row < m_end) {
+                        int rof[8];
+                        float wj[8];
+#pragma unroll
+                        for (int jj = 0; jj < 8; ++jj) {
+                            rof[jj] = p.row_of[(size_t)row * 8 + jj];
+                            wj[jj] = p.cw[(size_t)row * 8 + jj];
+                        }
+                        i32x4 yv[8];
+#pragma unroll
+                        for (int jj = 0; jj < 8; ++jj)
+                            yv[jj] = *reinterpret_cast<const i32x4 *>(p.y_perm + (size_t)rof[jj] * p.N + n0 + cl);
+                        const float *cr = ch + rl * kChLd + cl;
+                        const f32x4 s0 = *reinterpret_cast<const f32x4 *>(cr);
+                        const f32x4 s1 = *reinterpret_cast<const f32x4 *>(cr + 4);
+                        float v[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+                        for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) {
+                                v[2 * u] += wj[jj] * bf16_to_f32((uint32_t)yv[jj][u] & 0xffffu);
+                                v[2 * u + 1] += wj[jj] * bf16_to_f32((uint32_t)yv[jj][u] >> 16);
+                            }
+                        float *yo = p.yout + (size_t)row * p.N + n0 + cl;
+                        *reinterpret_cast<f32x4 *>(yo) = f32x4{v[0], v[1], v[2], v[3]};
+                        *reinterpret_cast<f32x4 *>(yo + 4) = f32x4{v[4], v[5], v[6], v[7]};
+                    }
+                }
+                __syncthreads();
             }
         }
     }
@@ -457,7 +504,7 @@ bool ffn_fp8_large_ok(const FfnArgs &a) {
 }
 
 // Phase 1 (gate/up, fused SwiGLU + h quantisation) and / or phase 2 (down:
-// bf16 y_perm, or the shared expert's fp32 output for k_combine_add).
+// bf16 y_perm, or the shared expert's output with the weighted combine).
 hipError_t launch_ffn_fp8_large(const FfnArgs &a, hipStream_t s) {
     const int P = (cu_count() / 8) * 8;
     const bool routed = a.offsets != nullptr;
@@ -495,14 +542,12 @@ hipError_t launch_ffn_fp8_large(const FfnArgs &a, hipStream_t s) {
         q.N = a.d;
         if (a.combine) {
             q.yout = static_cast<float *>(a.y);
-            if (routed)
-                hipLaunchKernelGGL((k_gemm_fp8_large<EPI_F32, true>), dim3(P), dim3(512), 0, s, q);
-            else
-                hipLaunchKernelGGL((k_gemm_fp8_large<EPI_F32, false>), dim3(P), dim3(512), 0, s, q);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-            return launch_combine_add(a.M, a.d, a.k, static_cast<const uint16_t *>(a.y_perm), a.row_of, a.cw,
-                                      static_cast<float *>(a.y), s);
+            q.y_perm = static_cast<const uint16_t *>(a.y_perm);
+            q.row_of = a.row_of;
+            q.cw = a.cw;
+            // the combine belongs to the shared expert (one group)
+            hipLaunchKernelGGL((k_gemm_fp8_large<EPI_COMBINE, false>), dim3(P), dim3(512), 0, s, q);
+            return hipGetLastError();
         }
         q.out = static_cast<uint16_t *>(a.y);
         if (routed)

@@ -314,7 +314,10 @@ def test_gate_up_rows_matches_materialised(wt, T, d, I, kind):
                                       ("bf16", 1000, 256, 128), ("e4m3", 100, 256, 128), ("e4m3", 257, 256, 128),
                                       # small T, wide d / I: the shared expert splits K (equal and
                                       # unequal split lengths, one and two row tiles, a single token)
-                                      ("bf16", 100, 2048, 512), ("bf16", 1, 2048, 512), ("bf16", 130, 1024, 832)])
+                                      ("bf16", 100, 2048, 512), ("bf16", 1, 2048, 512), ("bf16", 130, 1024, 832),
+                                      # the large-tile kernels' fused combine epilogues (bf16, e4m3),
+                                      # with a ragged last row tile
+                                      ("bf16", 600, 512, 256), ("e4m3", 600, 512, 256)])
 def test_combine(wt, T, d, I):
     act = "f32" if wt == "f32" else "bf16"
     cfg = synth.Config("comb", seed=31, T=T, d=d, I=I, act=act, wt=wt)
