@@ -54,6 +54,9 @@ def main():
                     help="workload (4: the skewed prefill layer the metric is quoted on)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fresh-batches", type=int, default=0,
+                    help="N > 0: every step takes a new token batch (N batches resident in HBM, cycled); "
+                         "default: the same batch every step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (the byte-counter reference)")
     args = ap.parse_args()
@@ -91,12 +94,16 @@ def main():
     inp = synth.make_inputs(cfg)
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s; uploading")
     layer = layer_from_inputs(inp)
-    x = upload(inp["x"])
+    if args.fresh_batches > 0:
+        xs = [upload(synth.make_x_step(cfg, b)) for b in range(args.fresh_batches)]
+    else:
+        xs = [upload(inp["x"])]
     bias0 = upload(inp["bias"])
     D = layer.desc
     stream = torch.cuda.current_stream()
 
-    def step(bias, ev=None):
+    def step(bias, ev=None, s=0):
+        x = xs[s % len(xs)]
         if ev is not None:
             ev[0].record(stream)
         _lib.moe_route(D, x, layer.wr, bias, layer.idx, layer.w, None, layer.ws, stream)
@@ -121,8 +128,8 @@ def main():
 
     log(f"[bench] warmup {args.warmup} steps")
     scratch_bias = bias0.clone()
-    for _ in range(args.warmup):
-        step(scratch_bias)
+    for w_ in range(args.warmup):
+        step(scratch_bias, None, w_)
     torch.cuda.synchronize()
 
     K = args.steps
@@ -133,7 +140,7 @@ def main():
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(K):
-        step(bias, events[s])
+        step(bias, events[s], s)
         counts_hist[s].copy_(layer.counts, non_blocking=True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
@@ -186,7 +193,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": T, "d_model": d, "experts": E, "top_k": k, "shared_experts": 1,
                    "expert_intermediate": I, "router": "fp32 sigmoid", "router_row_skew": cfg.skew,
-                   "bias_start": cfg.bias, "gamma": cfg.gamma, "loop_steps_timed": K, "seed": cfg.seed},
+                   "bias_start": cfg.bias, "gamma": cfg.gamma, "loop_steps_timed": K, "seed": cfg.seed,
+                   "batches": "fixed" if args.fresh_batches <= 0 else f"fresh ({args.fresh_batches} cycled)"},
         "roofline": {"kernel": f"routed gate/up grouped GEMM ({kname}, SwiGLU epilogue"
                                + (" + e4m3 quantisation)" if cfg.wt == "e4m3" else ")"),
                      "bound": "hbm" if hbm_bound else "mfma", "achieved": achieved, "peak": peak,

@@ -84,10 +84,25 @@ class MoeLayer:
     def update_bias(self, bias, gamma=1e-3, stream=None):
         _lib.moe_bias_update(self.desc, self.counts, gamma, bias, stream)
 
-    def step(self, x, bias, gamma=1e-3, stream=None):
+    def step(self, x, bias, gamma=None, tokens_seen=0, stream=None):
+        """One training step's forward and bias update; gamma defaults to the
+        schedule's value for a step starting after `tokens_seen` tokens."""
         y = self.forward(x, bias, stream=stream)
-        self.update_bias(bias, gamma, stream)
+        self.update_bias(bias, bias_gamma(tokens_seen) if gamma is None else gamma, stream)
         return y
+
+
+# kbwen.com DeepSeek feed, "A bias term for each expert": the bias moves by
+# 0.001 per step for the first 14.3T training tokens and by 0 for the rest.
+# Reading: a step that starts before 14.3T tokens have been consumed uses
+# 0.001.
+GAMMA = 1e-3
+GAMMA_TOKENS = 14.3e12
+
+
+def bias_gamma(tokens_seen: float) -> float:
+    """The bias step size for a training step that starts after `tokens_seen` tokens."""
+    return GAMMA if tokens_seen < GAMMA_TOKENS else 0.0
 
 
 def layer_from_inputs(inp: dict, device="cuda") -> MoeLayer:

@@ -31,6 +31,7 @@ TID_GATE, TID_UP, TID_DOWN = 4, 5, 6
 TID_SGATE, TID_SUP, TID_SDOWN = 7, 8, 9
 TID_IDS = 10
 TID_AUX = 11
+TID_XSTEP = 100  # fresh batches of the balancing loop: step s >= 1 draws x from id 100 + s
 
 F32, BF16, E4M3 = "f32", "bf16", "e4m3"
 
@@ -196,6 +197,15 @@ def make_ffn(cfg: Config, G: int, tids):
                 up=normal(cfg.seed, tu, (G, cfg.I, cfg.d), cfg.std_w, dt),
                 down=normal(cfg.seed, td, (G, cfg.d, cfg.I), cfg.std_w, dt),
                 s_gate=None, s_up=None, s_down=None)
+
+
+def make_x_step(cfg: Config, step: int):
+    """The token batch of balancing-loop step `step` when every step takes a
+    fresh batch: step 0 is the workload's x, step s >= 1 the same
+    distribution under tensor id TID_XSTEP + s (host array)."""
+    if step == 0:
+        return make_router(cfg)[0]
+    return normal(cfg.seed, TID_XSTEP + step, (cfg.T, cfg.d), cfg.std_x, BF16 if cfg.act == BF16 else F32)
 
 
 def make_inputs(cfg: Config) -> dict:

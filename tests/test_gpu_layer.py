@@ -212,3 +212,57 @@ def test_balancing_loop_reduced():
         f"independent loops identical for {independent if independent is not None else cfg.steps} steps; "
         f"max/mean load {imb[0]:.2f} -> {imb[-1]:.2f}")
     assert imb[-1] < imb[0]
+
+
+def test_balancing_loop_fresh_batches_and_gamma_switch():
+    """The balancing loop as training runs it: a fresh batch every step
+    (skewed workload's recipe, T=2048, d=1024), and the bias step size from
+    the schedule (0.001, then 0 once 14.3T tokens have been consumed: the
+    loop starts 16 steps before that point).  Each step is checked against
+    the oracle fed the GPU's current bias and that step's batch: ids equal on
+    every token that is not a near-tie, counts and the new bias bit-exact;
+    after the switch the bias stays bit-for-bit constant while routing
+    goes on."""
+    from sparse_expert_routing_amd.layer import GAMMA, GAMMA_TOKENS, bias_gamma
+    cfg = synth.CONFIGS[4].with_(T=2048, d=1024, I=256)
+    T, k, E = cfg.T, cfg.k, cfg.E
+    steps, switch = 24, 16
+    inp = synth.make_inputs(cfg)
+    sh = oracle.shape_of(cfg)
+    ds = _lib.desc(T, cfg.d, E, k, cfg.I, cfg.act, cfg.wt)
+    wr, b = upload(inp["wr"]), upload(inp["bias"])
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    row_src = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    row_of = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    nws = max(_lib.workspace_bytes(ds, st) for st in (_lib.MOE_WS_DISPATCH, _lib.MOE_WS_ROUTE))
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    gb_prev = np.array(inp["bias"], dtype=np.float32)
+    flips = 0
+    imb = []
+    for step in range(steps):
+        tokens_seen = GAMMA_TOKENS - (switch - step) * T
+        gamma = bias_gamma(tokens_seen)
+        assert gamma == (GAMMA if step < switch else 0.0)
+        xs = synth.make_x_step(cfg, step)
+        _lib.moe_route(ds, upload(xs), wr, b, idx, w, None, ws)
+        _lib.moe_dispatch(ds, idx, None, counts, offsets, row_src, row_of, None, None, ws)
+        _lib.moe_bias_update(ds, counts, gamma, b)
+        torch.cuda.synchronize()
+        gi, gc, gb = host(idx), host(counts), host(b)
+        oi, _, ogap, _ = oracle.route(sh, xs, inp["wr"], gb_prev)
+        flip = np.any(gi != oi, axis=1)
+        assert not np.any(flip & (ogap >= NEAR_TIE)), f"step {step}: a non-near-tie token chose differently"
+        flips += int(flip.sum())
+        assert np.array_equal(gc, oracle.dispatch(gi, E)[0]), f"step {step}: counts differ"
+        nb = oracle.bias_update(gb_prev, gc, k, T, gamma)
+        assert np.array_equal(gb.view(np.uint32), nb.view(np.uint32)), f"step {step}: bias differs"
+        if step >= switch:
+            assert np.array_equal(gb.view(np.uint32), gb_prev.view(np.uint32)), f"step {step}: bias moved at gamma 0"
+        imb.append(gc.max() / gc.mean())
+        gb_prev = gb
+    say(f"[loop] fresh batches: {steps} steps stage-wise exact, gamma 0 from step {switch}; "
+        f"near-tie tokens choosing differently: {flips}; max/mean load {imb[0]:.2f} -> {imb[switch - 1]:.2f}")
+    assert imb[switch - 1] < imb[0]
