@@ -1,4 +1,5 @@
-"""CPU oracle for the DeepSeekMoE layer forward with bias (auxiliary-loss-free) routing.
+"""CPU oracle for the DeepSeekMoE layer with bias (auxiliary-loss-free) routing:
+the forward, and the backward (gradients of the layer output).
 
 TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 bench's ``cpu_baseline`` leg may import this package.  The product path (the
@@ -66,6 +67,7 @@ def lib():
             "oracle_expert_ffn": [vp, vp, vp, vp, vp, i64, vp, vp],
             "oracle_combine": [vp, vp, vp, vp, vp, vp, i64, vp, vp],
             "oracle_forward": [vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp],
+            "oracle_backward": [vp] * 16,
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -190,6 +192,27 @@ def combine(sh: Shape, shared: dict, x, y_perm, row_of, g, tokens=None):
                          _p(np.ascontiguousarray(g, dtype=np.float32)), n, _p(tok), _p(y))
     del keep
     return y
+
+
+def backward(sh: Shape, x, wr, idx, experts: dict, shared: dict, dy):
+    """Gradients of the layer output for the routing idx [T,k] given dy [T,d] f32:
+    dict of dx [T,d], dwr [E,d], dwg/dwu [E,I,d], dwd [E,d,I], dsg/dsu [I,d],
+    dsd [d,I], dg [T,k] (all f32).  f32 and bf16 weights only."""
+    assert sh.wt != E4M3, "the backward oracle covers f32 and bf16 weights"
+    T, d, E, k, I = sh.T, sh.d, sh.E, sh.k, sh.I
+    we, k1 = ffn(experts)
+    ws, k2 = ffn(shared)
+    out = dict(dx=np.empty((T, d), np.float32), dwr=np.empty((E, d), np.float32),
+               dwg=np.empty((E, I, d), np.float32), dwu=np.empty((E, I, d), np.float32),
+               dwd=np.empty((E, d, I), np.float32), dsg=np.empty((I, d), np.float32),
+               dsu=np.empty((I, d), np.float32), dsd=np.empty((d, I), np.float32),
+               dg=np.empty((T, k), np.float32))
+    lib().oracle_backward(ctypes.byref(sh), _p(x), _p(np.ascontiguousarray(wr, dtype=np.float32)),
+                          _p(np.ascontiguousarray(idx, dtype=np.int32)), ctypes.byref(we), ctypes.byref(ws),
+                          _p(np.ascontiguousarray(dy, dtype=np.float32)),
+                          *[_p(out[n]) for n in ("dx", "dwr", "dwg", "dwu", "dwd", "dsg", "dsu", "dsd", "dg")])
+    del k1, k2
+    return out
 
 
 def forward(sh: Shape, x, wr, bias, experts: dict, shared: dict, tokens=None):

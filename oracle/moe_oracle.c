@@ -1,6 +1,6 @@
 /*
  * CPU oracle for the DeepSeekMoE layer forward with auxiliary-loss-free
- * (bias) routing.  TEST INFRASTRUCTURE: only the tests, the smoke check and
+ * (bias) routing, and its backward (gradients of the layer output).  TEST INFRASTRUCTURE: only the tests, the smoke check and
  * the bench's CPU-baseline leg may load this library.  It shares no code,
  * header or table with the HIP path.
  *
@@ -487,6 +487,203 @@ void oracle_forward(const or_shape *sh, const void *x, const float *wr, const fl
         free(acc);
         free(h);
     }
+}
+
+/* ------------------------------------------------------ the backward pass */
+
+/* One SwiGLU expert's forward intermediates and backward on one row, fp64:
+ *   ug = Wg a, uu = Wu a, h = round(silu(ug) * uu) as the forward stores it;
+ *   given the output gradient dyr (already in the GEMM input type):
+ *   dh = Wd^T dyr;  d silu(z)/dz = sig(z) (1 + z (1 - sig(z)));
+ *   dug = round(dh * uu * silu'(ug)), duu = round(dh * silu(ug)) (the GEMM
+ *   inputs of the backward GEMMs, rounded like h);
+ *   da = Wg^T dug + Wu^T duu.
+ * The rounding of h and of the routed output is taken as the identity in
+ * the derivative. */
+static void ffn_row_backward(const or_shape *sh, const or_ffn *w, int64_t g, const double *a,
+                             const double *dyr, double *h, double *dug, double *duu, double *da) {
+    const int64_t d = sh->d, I = sh->I;
+    for (int64_t i = 0; i < I; ++i) {
+        double ug = 0.0, uu = 0.0;
+        for (int64_t j = 0; j < d; ++j) {
+            ug += w_at(sh->wt, w->gate, w->s_gate, I, d, g, i, j) * a[j];
+            uu += w_at(sh->wt, w->up, w->s_up, I, d, g, i, j) * a[j];
+        }
+        const double sg = 1.0 / (1.0 + exp(-ug));
+        double dh = 0.0;
+        for (int64_t n = 0; n < d; ++n) dh += w_at(sh->wt, w->down, w->s_down, d, I, g, n, i) * dyr[n];
+        h[i] = ug * sg * uu;
+        dug[i] = dh * uu * sg * (1.0 + ug * (1.0 - sg));
+        duu[i] = dh * ug * sg;
+    }
+    round_to_gemm_input(sh->wt, h, (int)I);
+    round_to_gemm_input(sh->wt, dug, (int)I);
+    round_to_gemm_input(sh->wt, duu, (int)I);
+    for (int64_t j = 0; j < d; ++j) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < I; ++i)
+            acc += w_at(sh->wt, w->gate, w->s_gate, I, d, g, i, j) * dug[i] +
+                   w_at(sh->wt, w->up, w->s_up, I, d, g, i, j) * duu[i];
+        da[j] = acc;
+    }
+}
+
+/* Gradients of the layer's output y (given dy = dL/dy, [T, d] fp32) for the
+ * routing idx [T, k] (ascending ids; the choice itself is piecewise constant
+ * and carries no gradient, and the bias, used only for the choice, gets none:
+ * kbwen.com DeepSeek feed, "A bias term for each expert").  Weights and
+ * activations as in the forward (f32 or bf16; the GEMM inputs of the
+ * backward -- the routed and shared output gradients, the SwiGLU input
+ * gradients -- are rounded to that type like h):
+ *   y = shared(x) + sum_j g_j * yperm_j,  g_j = s_j / sum_i s_i (chosen i),
+ *   s_e = sigmoid(x . wr_e);
+ *   dg_j = dy . yperm_j (yperm_j recomputed as the forward stores it);
+ *   the routed output gradient of (t, j) is round(g_j dy); the shared one
+ *   round(dy);
+ *   ds_j = (dg_j - sum_i g_i dg_i) / sum_i s_i,  dl_j = ds_j s_j (1 - s_j);
+ *   dx = sum_j (routed input gradient) + (shared input gradient)
+ *        + sum_j dl_j wr_{e_j};
+ *   dwr_e = sum over (t, j) with idx = e of dl_j x_t;
+ *   dWg_e = sum over e's rows of dug (x) a, dWu_e likewise with duu,
+ *   dWd_e = sum of (routed output gradient) (x) h; the shared expert's over
+ *   all tokens.
+ * Outputs fp32: dx [T, d], dwr [E, d], dwg, dwu [E, I, d], dwd [E, d, I],
+ * dsg, dsu [I, d], dsd [d, I], dg [T, k].  f32 and bf16 weights only. */
+void oracle_backward(const or_shape *sh, const void *x, const float *wr, const int32_t *idx,
+                     const or_ffn *experts, const or_ffn *shared, const float *dy, float *dx,
+                     float *dwr, float *dwg, float *dwu, float *dwd, float *dsg, float *dsu, float *dsd,
+                     float *dg_out) {
+    const int64_t T = sh->T, d = sh->d, I = sh->I, E = sh->E, k = sh->k;
+    if (sh->wt == OR_E4M3) return;
+    /* per (t, j) and per token intermediates for the weight gradients */
+    double *ry = (double *)malloc(sizeof(double) * T * k * d);  /* routed output gradient */
+    double *rh = (double *)malloc(sizeof(double) * T * k * I);
+    double *rug = (double *)malloc(sizeof(double) * T * k * I);
+    double *ruu = (double *)malloc(sizeof(double) * T * k * I);
+    double *sy = (double *)malloc(sizeof(double) * T * d);      /* shared output gradient */
+    double *sh_h = (double *)malloc(sizeof(double) * T * I);
+    double *sug = (double *)malloc(sizeof(double) * T * I);
+    double *suu = (double *)malloc(sizeof(double) * T * I);
+    double *dl = (double *)malloc(sizeof(double) * T * k);
+    double *xa = (double *)malloc(sizeof(double) * T * d);      /* x as the GEMMs read it */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+        double *a = xa + t * d;
+        double *yr = (double *)malloc(sizeof(double) * d);
+        double *da = (double *)malloc(sizeof(double) * d);
+        double *acc = (double *)malloc(sizeof(double) * d);
+        double *hb = (double *)malloc(sizeof(double) * I);
+        double s[64], dgv[64];
+        gemm_input_row(sh, x, t, a);
+        for (int64_t n = 0; n < d; ++n) acc[n] = 0.0;
+        /* routed experts */
+        double ssum = 0.0;
+        for (int64_t j = 0; j < k; ++j) {
+            const int e = idx[t * k + j];
+            double l = 0.0;
+            for (int64_t n = 0; n < d; ++n) l += x_at(sh, x, t, n) * (double)wr[(int64_t)e * d + n];
+            s[j] = 1.0 / (1.0 + exp(-l));
+            ssum += s[j];
+        }
+        for (int64_t j = 0; j < k; ++j) {
+            const int e = idx[t * k + j];
+            const double gj = s[j] / ssum;
+            ffn_row(sh, experts, e, a, yr, hb);
+            double dgj = 0.0;
+            for (int64_t n = 0; n < d; ++n) dgj += (double)dy[t * d + n] * round_yperm(sh, yr[n]);
+            dgv[j] = dgj;
+            double *dyr = ry + (t * k + j) * d;
+            for (int64_t n = 0; n < d; ++n) dyr[n] = gj * (double)dy[t * d + n];
+            round_to_gemm_input(sh->wt, dyr, (int)d);
+            ffn_row_backward(sh, experts, e, a, dyr, rh + (t * k + j) * I, rug + (t * k + j) * I,
+                             ruu + (t * k + j) * I, da);
+            for (int64_t n = 0; n < d; ++n) acc[n] += da[n];
+        }
+        /* shared expert */
+        double *dys = sy + t * d;
+        for (int64_t n = 0; n < d; ++n) dys[n] = (double)dy[t * d + n];
+        round_to_gemm_input(sh->wt, dys, (int)d);
+        ffn_row_backward(sh, shared, 0, a, dys, sh_h + t * I, sug + t * I, suu + t * I, da);
+        for (int64_t n = 0; n < d; ++n) acc[n] += da[n];
+        /* router: through the renormalised weights only */
+        double gdg = 0.0;
+        for (int64_t j = 0; j < k; ++j) gdg += s[j] / ssum * dgv[j];
+        for (int64_t j = 0; j < k; ++j) {
+            const double ds = (dgv[j] - gdg) / ssum;
+            dl[t * k + j] = ds * s[j] * (1.0 - s[j]);
+            const int e = idx[t * k + j];
+            for (int64_t n = 0; n < d; ++n) acc[n] += dl[t * k + j] * (double)wr[(int64_t)e * d + n];
+            dg_out[t * k + j] = (float)dgv[j];
+        }
+        for (int64_t n = 0; n < d; ++n) dx[t * d + n] = (float)acc[n];
+        free(yr);
+        free(da);
+        free(acc);
+        free(hb);
+    }
+    /* weight gradients: routed experts and router, one expert at a time */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t e = 0; e < E; ++e) {
+        double *gw = (double *)calloc((size_t)(I * d), sizeof(double));
+        double *uw = (double *)calloc((size_t)(I * d), sizeof(double));
+        double *dw = (double *)calloc((size_t)(d * I), sizeof(double));
+        double *rw = (double *)calloc((size_t)d, sizeof(double));
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t j = 0; j < k; ++j) {
+                if (idx[t * k + j] != e) continue;
+                const int64_t f = t * k + j;
+                const double *a = xa + t * d;
+                for (int64_t i = 0; i < I; ++i) {
+                    const double cg = rug[f * I + i], cu = ruu[f * I + i];
+                    for (int64_t n = 0; n < d; ++n) {
+                        gw[i * d + n] += cg * a[n];
+                        uw[i * d + n] += cu * a[n];
+                    }
+                }
+                for (int64_t n = 0; n < d; ++n)
+                    for (int64_t i = 0; i < I; ++i) dw[n * I + i] += ry[f * d + n] * rh[f * I + i];
+                for (int64_t n = 0; n < d; ++n) rw[n] += dl[f] * x_at(sh, x, t, n);
+            }
+        for (int64_t q = 0; q < I * d; ++q) {
+            dwg[e * I * d + q] = (float)gw[q];
+            dwu[e * I * d + q] = (float)uw[q];
+            dwd[e * d * I + q] = (float)dw[q];
+        }
+        for (int64_t n = 0; n < d; ++n) dwr[e * d + n] = (float)rw[n];
+        free(gw);
+        free(uw);
+        free(dw);
+        free(rw);
+    }
+    /* the shared expert's weight gradients: over all tokens, one row at a time */
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < I; ++i)
+        for (int64_t n = 0; n < d; ++n) {
+            double cg = 0.0, cu = 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                cg += sug[t * I + i] * xa[t * d + n];
+                cu += suu[t * I + i] * xa[t * d + n];
+            }
+            dsg[i * d + n] = (float)cg;
+            dsu[i * d + n] = (float)cu;
+        }
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < d; ++n)
+        for (int64_t i = 0; i < I; ++i) {
+            double c = 0.0;
+            for (int64_t t = 0; t < T; ++t) c += sy[t * d + n] * sh_h[t * I + i];
+            dsd[n * I + i] = (float)c;
+        }
+    free(ry);
+    free(rh);
+    free(rug);
+    free(ruu);
+    free(sy);
+    free(sh_h);
+    free(sug);
+    free(suu);
+    free(dl);
+    free(xa);
 }
 
 /* Threads an OpenMP region of this library uses (for reporting). */

@@ -40,6 +40,44 @@ MUTANTS = [
 ]
 
 
+# mistakes in the backward, against the backward pins
+BACKWARD_MUTANTS = [
+    ("silu derivative term dropped", "dug[i] = dh * uu * sg * (1.0 + ug * (1.0 - sg));", "dug[i] = dh * uu * sg;"),
+    ("gate/up gradients swapped", "dug[i] = dh * uu * sg * (1.0 + ug * (1.0 - sg));\n        duu[i] = dh * ug * sg;",
+     "duu[i] = dh * uu * sg * (1.0 + ug * (1.0 - sg));\n        dug[i] = dh * ug * sg;"),
+    ("router gradient not renormalised", "const double ds = (dgv[j] - gdg) / ssum;", "const double ds = dgv[j] / ssum;"),
+    ("sigmoid derivative dropped", "dl[t * k + j] = ds * s[j] * (1.0 - s[j]);", "dl[t * k + j] = ds;"),
+    ("routed gradient not scaled by g", "dyr[n] = gj * (double)dy[t * d + n];", "dyr[n] = (double)dy[t * d + n];"),
+    ("down gradient transposed", "dw[n * I + i] += ry[f * d + n] * rh[f * I + i];",
+     "dw[n * I + i] += ry[f * d + (n * I + i) % d] * rh[f * I + (n * I + i) / d % I];"),
+    ("router input gradient dropped", "acc[n] += dl[t * k + j] * (double)wr[(int64_t)e * d + n];", "(void)e;"),
+    ("shared input gradient dropped",
+     "ffn_row_backward(sh, shared, 0, a, dys, sh_h + t * I, sug + t * I, suu + t * I, da);\n        for (int64_t n = 0; n < d; ++n) acc[n] += da[n];",
+     "ffn_row_backward(sh, shared, 0, a, dys, sh_h + t * I, sug + t * I, suu + t * I, da);"),
+]
+
+
+def _run_pins(tmp_path, old, new, pins):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, "mutation site not found"
+    mut = src.replace(old, new, 1)
+    c = tmp_path / "mut.c"
+    c.write_text(mut)
+    so = tmp_path / "libmut.so"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fno-fast-math", "-ffp-contract=off", "-shared",
+                           "-fPIC", "-o", str(so), str(c), "-lm"])
+    env = dict(os.environ, MOE_ORACLE_LIB=str(so), OMP_NUM_THREADS="2")
+    return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                           os.path.join(ROOT, "tests", pins)],
+                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+
+
+@pytest.mark.parametrize("name,old,new", BACKWARD_MUTANTS, ids=[m[0] for m in BACKWARD_MUTANTS])
+def test_backward_pins_catch_mutant(tmp_path, name, old, new):
+    r = _run_pins(tmp_path, old, new, "test_oracle_backward_pins.py")
+    assert r.returncode != 0, f"mutant '{name}' survived the backward pins:\n{r.stdout[-2000:]}"
+
+
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pin_suite_catches_mutant(tmp_path, name, old, new):
     src = open(SRC).read()
