@@ -88,7 +88,7 @@ typedef struct {
 } moe_ffn_weights_t;
 
 /* Workspace stages for moe_workspace_bytes. */
-enum { MOE_WS_DISPATCH = 0, MOE_WS_FFN = 1, MOE_WS_COMBINE = 2, MOE_WS_ROUTE = 3 };
+enum { MOE_WS_DISPATCH = 0, MOE_WS_FFN = 1, MOE_WS_COMBINE = 2, MOE_WS_ROUTE = 3, MOE_WS_BACKWARD = 4 };
 
 /*
  * Router, biased top-k choice and combine weights (DeepSeek V3 From Scratch,
@@ -229,6 +229,43 @@ moe_status_t moe_bias_update(const moe_desc_t *desc, const int32_t *counts, floa
 /* Device workspace, in bytes, that a call of the given stage needs for this
  * shape (0 when the shape is invalid). */
 size_t moe_workspace_bytes(const moe_desc_t *desc, int32_t stage);
+
+/*
+ * Backward of the layer: the gradients of the layer output y for the
+ * routing the forward chose, given dy = dL/dy (act = wt = bf16 only; other
+ * types give MOE_ENOTSUP).  What is differentiated is the forward above
+ * (DeepSeek V3 From Scratch, "The idea", "In code"; Scaling Efficiency ...,
+ * "Implementation: A Modular Look"):
+ *   y = shared(x) + sum_j g_j * y_perm_j,  g_j = s_j / sum_i s_i over the
+ *   chosen experts,  s_e = sigmoid(x . w_router[e]).
+ * The choice is piecewise constant and carries no gradient; the bias is used
+ * only for the choice and gets no gradient (kbwen.com DeepSeek feed, "A bias
+ * term for each expert").  Inside: the routed and shared output gradients
+ * (g_j dy and dy) and the SwiGLU input gradients are rounded to bf16 as GEMM
+ * inputs, like h in the forward; the expert pre-activations are recomputed;
+ * accumulation is fp32.  Deterministic (no atomics).
+ *   x          [T, d] bf16, the forward's input
+ *   w_router   [E, d] fp32
+ *   idx, weights [T, k]: from moe_route
+ *   offsets, row_src, row_of: from moe_dispatch
+ *   experts, shared: as for the forward (bf16)
+ *   y_perm     [T*k, d] bf16: the forward's routed outputs (moe_expert_ffn)
+ *   dy         [T, d] fp32
+ * Outputs (fp32, written, not accumulated):
+ *   dx [T, d]; dw_router [E, d]; dw_gate, dw_up [E, I, d]; dw_down [E, d, I];
+ *   ds_gate, ds_up [I, d]; ds_down [d, I] (the shared expert);
+ *   dg [T, k] the combine-weight gradients dy . y_perm_j (NULL: not returned).
+ *   workspace >= moe_workspace_bytes(desc, MOE_WS_BACKWARD) bytes of device
+ *   memory (about (T*k + T) * (6d + 18I) bytes).
+ * Requires d % 128 == 0 and I % 128 == 0.
+ */
+moe_status_t moe_backward(const moe_desc_t *desc, const void *x, const float *w_router, const int32_t *idx,
+                          const float *weights, const int32_t *offsets, const int32_t *row_src,
+                          const int32_t *row_of, const moe_ffn_weights_t *experts,
+                          const moe_ffn_weights_t *shared, const void *y_perm, const float *dy, float *dx,
+                          float *dw_router, float *dw_gate, float *dw_up, float *dw_down, float *ds_gate,
+                          float *ds_up, float *ds_down, float *dg, void *workspace, size_t ws_bytes,
+                          void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *moe_status_str(moe_status_t status);

@@ -15,11 +15,12 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = range(5)
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
-MOE_WS_DISPATCH, MOE_WS_FFN, MOE_WS_COMBINE, MOE_WS_ROUTE = 0, 1, 2, 3
+MOE_WS_DISPATCH, MOE_WS_FFN, MOE_WS_COMBINE, MOE_WS_ROUTE, MOE_WS_BACKWARD = 0, 1, 2, 3, 4
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_E4M3}
 
 EXPORTS = ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_gate_up_rows",
-           "moe_expert_down", "moe_combine", "moe_bias_update", "moe_workspace_bytes", "moe_status_str")
+           "moe_expert_down", "moe_combine", "moe_bias_update", "moe_backward", "moe_workspace_bytes",
+           "moe_status_str")
 
 
 class MoeError(RuntimeError):
@@ -61,8 +62,10 @@ def load(path: str = LIB_PATH):
     L.moe_expert_down.argtypes = [pd, vp, pw, vp, vp, sz, vp]
     L.moe_combine.argtypes = [pd, vp, pw, vp, vp, vp, vp, vp, sz, vp]
     L.moe_bias_update.argtypes = [pd, vp, f32, vp, vp]
+    L.moe_backward.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, pw, pw, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                               vp, sz, vp]
     for fn in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_gate_up_rows",
-               "moe_expert_down", "moe_combine", "moe_bias_update"):
+               "moe_expert_down", "moe_combine", "moe_bias_update", "moe_backward"):
         getattr(L, fn).restype = ctypes.c_int
     L.moe_workspace_bytes.argtypes = [pd, i32]
     L.moe_workspace_bytes.restype = sz
@@ -143,6 +146,18 @@ def moe_combine(ds, x, shared: FfnWeights, y_perm, row_of, weights, y, workspace
     _check("moe_combine", load().moe_combine(
         ctypes.byref(ds), _ptr(x), ctypes.byref(shared), _ptr(y_perm), _ptr(row_of), _ptr(weights), _ptr(y),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_backward(ds, x, w_router, idx, weights, offsets, row_src, row_of, experts: FfnWeights,
+                 shared: FfnWeights, y_perm, dy, grads: dict, workspace, stream=None):
+    """grads: device tensors dx, dw_router, dw_gate, dw_up, dw_down, ds_gate, ds_up, ds_down, and
+    optionally dg (fp32, written)."""
+    _check("moe_backward", load().moe_backward(
+        ctypes.byref(ds), _ptr(x), _ptr(w_router), _ptr(idx), _ptr(weights), _ptr(offsets), _ptr(row_src),
+        _ptr(row_of), ctypes.byref(experts), ctypes.byref(shared), _ptr(y_perm), _ptr(dy),
+        *[_ptr(grads[n]) for n in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "ds_gate", "ds_up",
+                                    "ds_down")],
+        _ptr(grads.get("dg")), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def moe_bias_update(ds, counts, gamma, bias, stream=None):

@@ -1,0 +1,543 @@
+// Backward of the MoE layer (bf16 experts): gradients of the layer output
+// for the routing the forward chose.
+//
+// What is differentiated: DeepSeek V3 From Scratch, "The idea" and "In code"
+// (sigmoid affinities, top-8 by biased score, combine weights = the chosen
+// unbiased affinities renormalised); Scaling Efficiency: A Deep Dive into the
+// DeepSeek-V3 Architecture, "Implementation: A Modular Look" (shared output
+// plus the weighted routed outputs).  The choice is piecewise constant and
+// carries no gradient; the bias enters only the choice, so it gets none
+// (kbwen.com DeepSeek feed, "A bias term for each expert": the bias adds no
+// gradient of its own).
+//
+// Kernels:
+//   - k_bgemm: a grouped GEMM C (+)= A B on v_mfma_f32_32x32x16_bf16 with
+//     fp32 accumulation, 128x128 tiles, 32 of K per stage, register-staged
+//     double buffer in LDS.  Each operand is either K-contiguous (loaded as
+//     16-byte runs along K) or M/N-contiguous (16-byte runs along M or N,
+//     transposed into the K-contiguous LDS layout by 2-byte stores).  Groups
+//     split M (the expert's rows: data gradients, the pre-activation
+//     recompute; B per expert) or K (the expert's rows as the reduction:
+//     weight gradients; C per expert);
+//   - k_bwd_combine: per token, dg_j = dy . y_perm_j, the routed output
+//     gradient g_j dy (bf16) and the shared one dy (bf16);
+//   - k_bwd_swiglu: h, and the SwiGLU input gradients from the recomputed
+//     pre-activations (all rounded to bf16 as the forward rounds h);
+//   - k_bwd_router: per token, the chosen experts' affinities recomputed in
+//     fp32, ds_j = (dg_j - sum_i g_i dg_i) / sum_i s_i, dl_j = ds_j s_j (1-s_j),
+//     and the router's share of dx;
+//   - k_bwd_dwr: router weight gradient, expert rows in ascending order;
+//   - k_bwd_dx: dx += shared input gradient + sum_j routed input gradients.
+#include "device.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kE = 256;
+constexpr int GM = 128, GN = 128, GK = 32;
+constexpr int LDK = GK + 8;  // LDS row stride (elements): 80 bytes
+
+enum { GROUP_NONE = 0, GROUP_M = 1, GROUP_K = 2 };
+
+struct BGemm {
+    int M, N, K;              // K: the reduction length (GROUP_K: total rows)
+    const int32_t *offsets;   // [G+1] (GROUP_M: row ranges; GROUP_K: reduction ranges)
+    const uint16_t *A;        // A(m, k) = A[m*lda + k] (K-contiguous) or A[k*lda + m]
+    int64_t lda;
+    const int32_t *a_rows;    // K-contiguous A with GROUP_M: row m reads row a_rows[m] / a_div
+    int a_div;
+    const uint16_t *B;        // B(k, n) = B[n*ldb + k] (K-contiguous) or B[k*ldb + n]
+    int64_t ldb, bstride;     // bstride: per-group B offset (GROUP_M)
+    const int32_t *b_rows;    // N-contiguous B with GROUP_K: row k reads row b_rows[k] / b_div
+    int b_div;
+    float *C;                 // C[m*ldc + n] (+ cstride per group for GROUP_K)
+    int64_t ldc, cstride;
+};
+
+// Row-tile slot -> (group, first row, end row) for GROUP_M (all lanes agree).
+__device__ __forceinline__ bool bg_find_tile(const int32_t *__restrict__ offsets, int slot, int &gi, int &m0,
+                                             int &m_end) {
+    const int lane = threadIdx.x & 63;
+    const int base = lane * 4;
+    int off[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) off[i] = offsets[base + i];
+    int nt[4], lane_t = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        nt[i] = (off[i + 1] - off[i] + GM - 1) / GM;
+        lane_t += nt[i];
+    }
+    const int incl = wave_incl_scan(lane_t);
+    const int excl = incl - lane_t;
+    const int total = __shfl(incl, 63, 64);
+    if (slot >= total) return false;
+    const bool own = slot >= excl && slot < incl;
+    const int owner = __ffsll((unsigned long long)__ballot(own)) - 1;
+    int my_g = 0, my_m0 = 0, my_end = 0;
+    if (own) {
+        int s = slot - excl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (s >= 0 && s < nt[i]) {
+                my_g = base + i;
+                my_m0 = off[i] + s * GM;
+                my_end = off[i + 1];
+            }
+            s -= nt[i];
+        }
+    }
+    gi = __shfl(my_g, owner, 64);
+    m0 = __shfl(my_m0, owner, 64);
+    m_end = __shfl(my_end, owner, 64);
+    return true;
+}
+
+// One operand tile (128 rows of M or N x 32 of K) global -> registers:
+// two 16-byte pieces per thread.  KC: K-contiguous source.  Rows past
+// `rows_end` and K past `k_end` read as zeros.
+template <bool KC>
+struct TileLoad {
+    i32x4 v[2];
+    __device__ __forceinline__ void load(const uint16_t *__restrict__ P, int64_t ld, const int32_t *__restrict__ rows,
+                                         int rdiv, int r0, int rows_end, int k0, int k_end) {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int c = tid + 256 * h;
+            if (KC) {
+                const int row = c >> 2, kc = (c & 3) * 8;
+                const int gr = r0 + row;
+                v[h] = i32x4{0, 0, 0, 0};
+                if (gr < rows_end) {
+                    const int64_t src = rows ? rows[gr] / rdiv : gr;
+                    v[h] = *reinterpret_cast<const i32x4 *>(P + src * ld + k0 + kc);
+                }
+            } else {
+                const int k = c >> 4, mc = (c & 15) * 8;
+                const int gk = k0 + k;
+                v[h] = i32x4{0, 0, 0, 0};
+                if (gk < k_end) {
+                    const int64_t src = rows ? rows[gk] / rdiv : gk;
+                    v[h] = *reinterpret_cast<const i32x4 *>(P + src * ld + r0 + mc);
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t *__restrict__ S) const {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int c = tid + 256 * h;
+            if (KC) {
+                const int row = c >> 2, kc = (c & 3) * 8;
+                *reinterpret_cast<i32x4 *>(S + row * LDK + kc) = v[h];
+            } else {
+                const int k = c >> 4, mc = (c & 15) * 8;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t w = (uint32_t)v[h][i];
+                    S[(mc + 2 * i) * LDK + k] = (uint16_t)(w & 0xffffu);
+                    S[(mc + 2 * i + 1) * LDK + k] = (uint16_t)(w >> 16);
+                }
+            }
+        }
+    }
+};
+
+template <bool A_KC, bool B_KC, int GROUP, bool ACC>
+__global__ __launch_bounds__(256) void k_bgemm(BGemm p) {
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][GM * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[2][GN * LDK];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    int gi = 0, m0, m_end, k_begin = 0, k_end = p.K;
+    const int n0 = blockIdx.y * GN;
+    if (GROUP == GROUP_M) {
+        if (!bg_find_tile(p.offsets, blockIdx.x, gi, m0, m_end)) return;
+    } else {
+        m0 = blockIdx.x * GM;
+        m_end = p.M;
+        if (GROUP == GROUP_K) {
+            gi = blockIdx.z;
+            k_begin = p.offsets[gi];
+            k_end = p.offsets[gi + 1];
+        }
+    }
+    const uint16_t *B = p.B + (GROUP == GROUP_M ? (int64_t)gi * p.bstride : 0);
+    float *C = p.C + (GROUP == GROUP_K ? (int64_t)gi * p.cstride : 0);
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+    TileLoad<A_KC> la;
+    TileLoad<B_KC> lb;
+    // A rows: M (row indirection only for a K-contiguous A); B: N, with the
+    // row indirection on K for an N-contiguous B
+    const int nst = (k_end - k_begin + GK - 1) / GK;
+    if (nst > 0) {
+        la.load(p.A, p.lda, A_KC ? p.a_rows : nullptr, p.a_div, m0, m_end, k_begin, k_end);
+        lb.load(B, p.ldb, B_KC ? nullptr : p.b_rows, p.b_div, n0, p.N, k_begin, k_end);
+        la.store(sA[0]);
+        lb.store(sB[0]);
+    }
+    __syncthreads();
+    for (int st = 0; st < nst; ++st) {
+        const int buf = st & 1;
+        const bool more = st + 1 < nst;
+        if (more) {
+            const int k0 = k_begin + (st + 1) * GK;
+            la.load(p.A, p.lda, A_KC ? p.a_rows : nullptr, p.a_div, m0, m_end, k0, k_end);
+            lb.load(B, p.ldb, B_KC ? nullptr : p.b_rows, p.b_div, n0, p.N, k0, k_end);
+        }
+#pragma unroll
+        for (int ks = 0; ks < GK / 16; ++ks) {
+            const int kc = ks * 16 + (lane >> 5) * 8;
+            bf16x8 af[2], bfr[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                af[i] = *reinterpret_cast<const bf16x8 *>(&sA[buf][(wm * 64 + i * 32 + (lane & 31)) * LDK + kc]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8 *>(&sB[buf][(wn * 64 + j * 32 + (lane & 31)) * LDK + kc]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        if (more) {
+            la.store(sA[buf ^ 1]);
+            lb.store(sB[buf ^ 1]);
+        }
+        __syncthreads();
+    }
+    // C layout of a 32x32 block: lane holds column (lane & 31), rows
+    // 8q + 4(lane >> 5) + r in register 4q + r
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m0 + wm * 64 + i * 32 + 8 * q + 4 * (lane >> 5) + r;
+                if (row >= m_end) continue;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+                    float *c = C + (int64_t)row * p.ldc + col;
+                    const float v = acc[i][j][4 * q + r];
+                    *c = ACC ? *c + v : v;
+                }
+            }
+}
+
+// ------------------------------------------------------------ elementwise
+
+// Per token t (one wave): dg_j = sum_n dy[t,n] y_perm[r_j,n] (r_j =
+// row_of[t*k+j]); dyp[r_j] = bf16(g_j dy[t]); dys[t] = bf16(dy[t]).
+__global__ __launch_bounds__(256) void k_bwd_combine(int T, int d, const float *__restrict__ dy,
+                                                     const uint16_t *__restrict__ y_perm,
+                                                     const int32_t *__restrict__ row_of, const float *__restrict__ g,
+                                                     uint16_t *__restrict__ dyp, uint16_t *__restrict__ dys,
+                                                     float *__restrict__ dg) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const float *dyt = dy + (int64_t)t * d;
+    int r[8];
+    float gw[8], dot[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        r[j] = row_of[(int64_t)t * 8 + j];
+        gw[j] = g[(int64_t)t * 8 + j];
+        dot[j] = 0.f;
+    }
+    for (int n = lane * 2; n < d; n += 128) {
+        const float2 v = *reinterpret_cast<const float2 *>(dyt + n);
+        *reinterpret_cast<uint32_t *>(dys + (int64_t)t * d + n) = pack_bf16x2(v.x, v.y);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t yp = *reinterpret_cast<const uint32_t *>(y_perm + (int64_t)r[j] * d + n);
+            dot[j] += v.x * bf16_to_f32(yp & 0xffffu) + v.y * bf16_to_f32(yp >> 16);
+            *reinterpret_cast<uint32_t *>(dyp + (int64_t)r[j] * d + n) = pack_bf16x2(gw[j] * v.x, gw[j] * v.y);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float v = dot[j];
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
+        if (lane == j) dg[(int64_t)t * 8 + j] = v;
+    }
+}
+
+// From the pre-activations P [rows, 2I] (gate | up, fp32) and dh [rows, I]:
+// h = bf16(silu(a) b), da = bf16(dh b sig(a) (1 + a (1 - sig(a)))),
+// db = bf16(dh silu(a)).
+__global__ __launch_bounds__(256) void k_bwd_swiglu(int64_t n, int I, const float *__restrict__ P,
+                                                    const float *__restrict__ dh, uint16_t *__restrict__ h,
+                                                    uint16_t *__restrict__ da, uint16_t *__restrict__ db) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int64_t row = i / I, c = i - row * I;
+    const float a = P[row * 2 * I + c], b = P[row * 2 * I + I + c], g = dh[i];
+    const float sg = 1.0f / (1.0f + expf(-a));
+    h[i] = (uint16_t)f32_to_bf16(a * sg * b);
+    da[i] = (uint16_t)f32_to_bf16(g * b * sg * (1.0f + a * (1.0f - sg)));
+    db[i] = (uint16_t)f32_to_bf16(g * a * sg);
+}
+
+// Per token t (one workgroup): s_j = sigmoid(x_t . wr_{e_j}) in fp32, then
+// ds_j, dl_j (stored) and dx[t] = sum_j dl_j wr_{e_j} (written).
+__global__ __launch_bounds__(256) void k_bwd_router(int T, int d, const uint16_t *__restrict__ x,
+                                                    const float *__restrict__ wr, const int32_t *__restrict__ idx,
+                                                    const float *__restrict__ dg, float *__restrict__ dl,
+                                                    float *__restrict__ dx) {
+    __shared__ float part[4][8];
+    __shared__ float dls[8];
+    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint16_t *xt = x + (int64_t)t * d;
+    int e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = idx[(int64_t)t * 8 + j];
+    float l[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) l[j] = 0.f;
+    for (int n = tid; n < d; n += 256) {
+        const float xv = bf16_to_f32(xt[n]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) l[j] += xv * wr[(int64_t)e[j] * d + n];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float v = l[j];
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
+        if (lane == 0) part[wave][j] = v;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float s[8], S = 0.f, gdg = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float lj = part[0][j] + part[1][j] + part[2][j] + part[3][j];
+            s[j] = 1.0f / (1.0f + expf(-lj));
+            S += s[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) gdg += s[j] / S * dg[(int64_t)t * 8 + j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float ds = (dg[(int64_t)t * 8 + j] - gdg) / S;
+            const float v = ds * s[j] * (1.0f - s[j]);
+            dls[j] = v;
+            dl[(int64_t)t * 8 + j] = v;
+        }
+    }
+    __syncthreads();
+    for (int n = tid; n < d; n += 256) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc += dls[j] * wr[(int64_t)e[j] * d + n];
+        dx[(int64_t)t * d + n] = acc;
+    }
+}
+
+// dwr[e, n] = sum over e's rows r (ascending) of dl[row_src[r]] x[row_src[r] / 8, n].
+__global__ __launch_bounds__(256) void k_bwd_dwr(int d, const int32_t *__restrict__ offsets,
+                                                 const int32_t *__restrict__ row_src, const float *__restrict__ dl,
+                                                 const uint16_t *__restrict__ x, float *__restrict__ dwr) {
+    const int e = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
+    if (n >= d) return;
+    float acc = 0.f;
+    for (int r = offsets[e]; r < offsets[e + 1]; ++r) {
+        const int f = row_src[r];
+        acc += dl[f] * bf16_to_f32(x[(int64_t)(f / 8) * d + n]);
+    }
+    dwr[(int64_t)e * d + n] = acc;
+}
+
+// dx[t] += dxs[t] + sum_j dxp[row_of[t*8 + j]] (j ascending), 4 columns per thread.
+__global__ __launch_bounds__(256) void k_bwd_dx(int T, int d, const float *__restrict__ dxs,
+                                                const float *__restrict__ dxp, const int32_t *__restrict__ row_of,
+                                                float *__restrict__ dx) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int w4 = d / 4;
+    if (i >= (int64_t)T * w4) return;
+    const int64_t t = i / w4;
+    const int c = (int)(i - t * w4) * 4;
+    f32x4 v = *reinterpret_cast<const f32x4 *>(dx + t * d + c);
+    const f32x4 s = *reinterpret_cast<const f32x4 *>(dxs + t * d + c);
+    v += s;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int r = row_of[t * 8 + j];
+        v += *reinterpret_cast<const f32x4 *>(dxp + (int64_t)r * d + c);
+    }
+    *reinterpret_cast<f32x4 *>(dx + t * d + c) = v;
+}
+
+template <bool A_KC, bool B_KC, int GROUP, bool ACC>
+hipError_t bgemm(const BGemm &p, int G, hipStream_t s) {
+    dim3 grid;
+    if (GROUP == GROUP_M) grid = dim3((p.M + GM - 1) / GM + G, p.N / GN);
+    else if (GROUP == GROUP_K) grid = dim3(p.M / GM, p.N / GN, G);
+    else grid = dim3((p.M + GM - 1) / GM, p.N / GN);
+    hipLaunchKernelGGL((k_bgemm<A_KC, B_KC, GROUP, ACC>), grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t backward_ws_bytes(int T, int d, int I, int k) {
+    auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+    const size_t A = (size_t)T * k, R = A + T;  // routed rows, then the shared expert's T rows
+    return al(R * d * 2)          // output gradients (bf16): routed, then shared
+           + al(R * 2 * I * 4)    // pre-activations (fp32)
+           + al(R * I * 4)        // dh (fp32)
+           + 3 * al(R * I * 2)    // h, da, db (bf16)
+           + al(R * d * 4)        // input gradients (fp32)
+           + al((size_t)T * k * 4)  // dl
+           + al((size_t)T * k * 4);  // dg (when the caller does not ask for it)
+}
+
+bool backward_ok(int d, int I) { return d % GN == 0 && I % GN == 0 && d % GK == 0 && I % GK == 0 && d % 128 == 0; }
+
+hipError_t launch_backward(const BackwardArgs &a, void *ws, hipStream_t s) {
+    auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+    const int T = a.T, d = a.d, I = a.I, k = a.k, E = kE;
+    const int64_t A = (int64_t)T * k, R = A + T;
+    char *w = static_cast<char *>(ws);
+    uint16_t *dyo = reinterpret_cast<uint16_t *>(w);            // [R, d]: routed rows, then shared
+    w += al((size_t)R * d * 2);
+    float *P = reinterpret_cast<float *>(w);                    // [R, 2I]
+    w += al((size_t)R * 2 * I * 4);
+    float *dh = reinterpret_cast<float *>(w);                   // [R, I]
+    w += al((size_t)R * I * 4);
+    uint16_t *h16 = reinterpret_cast<uint16_t *>(w);
+    w += al((size_t)R * I * 2);
+    uint16_t *da16 = reinterpret_cast<uint16_t *>(w);
+    w += al((size_t)R * I * 2);
+    uint16_t *db16 = reinterpret_cast<uint16_t *>(w);
+    w += al((size_t)R * I * 2);
+    float *dxi = reinterpret_cast<float *>(w);                  // [R, d]
+    w += al((size_t)R * d * 4);
+    float *dl = reinterpret_cast<float *>(w);
+    w += al((size_t)T * k * 4);
+    float *dg = a.dg ? a.dg : reinterpret_cast<float *>(w);
+    const uint16_t *x = static_cast<const uint16_t *>(a.x);
+    // shared-expert slices of the row-major buffers
+    uint16_t *dys = dyo + A * d;
+    float *Ps = P + A * 2 * I, *dhs = dh + A * I, *dxs = dxi + A * d;
+    uint16_t *hs = h16 + A * I, *das = da16 + A * I, *dbs = db16 + A * I;
+    hipError_t e;
+#define CHK(call)                      \
+    if ((e = (call)) != hipSuccess) return e;
+
+    // 1. combine backward
+    hipLaunchKernelGGL(k_bwd_combine, dim3((T + 3) / 4), dim3(256), 0, s, T, d, a.dy,
+                       static_cast<const uint16_t *>(a.y_perm), a.row_of, a.weights, dyo, dys, dg);
+    CHK(hipGetLastError());
+    // 2. pre-activations: routed rows gather x through row_src; shared rows are x
+    {
+        BGemm p{};
+        p.M = (int)A; p.N = I; p.K = d; p.offsets = a.offsets;
+        p.A = x; p.lda = d; p.a_rows = a.row_src; p.a_div = k;
+        p.ldb = d; p.bstride = (int64_t)I * d; p.ldc = 2 * I;
+        p.B = static_cast<const uint16_t *>(a.experts.gate); p.C = P;
+        CHK((bgemm<true, true, GROUP_M, false>(p, E, s)));
+        p.B = static_cast<const uint16_t *>(a.experts.up); p.C = P + I;
+        CHK((bgemm<true, true, GROUP_M, false>(p, E, s)));
+        BGemm q{};
+        q.M = T; q.N = I; q.K = d; q.A = x; q.lda = d; q.a_div = 1; q.ldb = d; q.ldc = 2 * I;
+        q.B = static_cast<const uint16_t *>(a.shared.gate); q.C = Ps;
+        CHK((bgemm<true, true, GROUP_NONE, false>(q, 1, s)));
+        q.B = static_cast<const uint16_t *>(a.shared.up); q.C = Ps + I;
+        CHK((bgemm<true, true, GROUP_NONE, false>(q, 1, s)));
+    }
+    // 3. dh = (output gradient) W_down: B(k = n, i) = W_down[n*I + i], N-contiguous
+    {
+        BGemm p{};
+        p.M = (int)A; p.N = I; p.K = d; p.offsets = a.offsets; p.A = dyo; p.lda = d; p.a_div = 1;
+        p.B = static_cast<const uint16_t *>(a.experts.down); p.ldb = I; p.bstride = (int64_t)d * I;
+        p.C = dh; p.ldc = I;
+        CHK((bgemm<true, false, GROUP_M, false>(p, E, s)));
+        BGemm q{};
+        q.M = T; q.N = I; q.K = d; q.A = dys; q.lda = d; q.a_div = 1;
+        q.B = static_cast<const uint16_t *>(a.shared.down); q.ldb = I; q.C = dhs; q.ldc = I;
+        CHK((bgemm<true, false, GROUP_NONE, false>(q, 1, s)));
+    }
+    // 4. SwiGLU backward (routed and shared rows in one pass)
+    {
+        const int64_t n = R * I;
+        hipLaunchKernelGGL(k_bwd_swiglu, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n, I, P, dh, h16, da16,
+                           db16);
+        CHK(hipGetLastError());
+    }
+    // 5. input gradients: da W_gate + db W_up (B(k = i, n) = W[i*d + n], N-contiguous)
+    {
+        BGemm p{};
+        p.M = (int)A; p.N = d; p.K = I; p.offsets = a.offsets; p.lda = I; p.a_div = 1;
+        p.ldb = d; p.bstride = (int64_t)I * d; p.C = dxi; p.ldc = d;
+        p.A = da16; p.B = static_cast<const uint16_t *>(a.experts.gate);
+        CHK((bgemm<true, false, GROUP_M, false>(p, E, s)));
+        p.A = db16; p.B = static_cast<const uint16_t *>(a.experts.up);
+        CHK((bgemm<true, false, GROUP_M, true>(p, E, s)));
+        BGemm q{};
+        q.M = T; q.N = d; q.K = I; q.lda = I; q.a_div = 1; q.ldb = d; q.C = dxs; q.ldc = d;
+        q.A = das; q.B = static_cast<const uint16_t *>(a.shared.gate);
+        CHK((bgemm<true, false, GROUP_NONE, false>(q, 1, s)));
+        q.A = dbs; q.B = static_cast<const uint16_t *>(a.shared.up);
+        CHK((bgemm<true, false, GROUP_NONE, true>(q, 1, s)));
+    }
+    // 6. weight gradients: reductions over each expert's rows (A(m, k = r)
+    //    and B(k = r, n) both row-major over r)
+    {
+        BGemm p{};
+        p.M = I; p.N = d; p.K = (int)A; p.offsets = a.offsets; p.lda = I; p.a_div = 1;
+        p.B = x; p.ldb = d; p.b_rows = a.row_src; p.b_div = k; p.ldc = d; p.cstride = (int64_t)I * d;
+        p.A = da16; p.C = a.dw_gate;
+        CHK((bgemm<false, false, GROUP_K, false>(p, E, s)));
+        p.A = db16; p.C = a.dw_up;
+        CHK((bgemm<false, false, GROUP_K, false>(p, E, s)));
+        BGemm q{};
+        q.M = d; q.N = I; q.K = (int)A; q.offsets = a.offsets; q.A = dyo; q.lda = d; q.a_div = 1;
+        q.B = h16; q.ldb = I; q.b_div = 1; q.C = a.dw_down; q.ldc = I; q.cstride = (int64_t)d * I;
+        CHK((bgemm<false, false, GROUP_K, false>(q, E, s)));
+        // shared expert: one group over all T rows
+        BGemm r{};
+        r.M = I; r.N = d; r.K = T; r.lda = I; r.a_div = 1; r.B = x; r.ldb = d; r.b_div = 1; r.ldc = d;
+        r.A = das; r.C = a.ds_gate;
+        CHK((bgemm<false, false, GROUP_NONE, false>(r, 1, s)));
+        r.A = dbs; r.C = a.ds_up;
+        CHK((bgemm<false, false, GROUP_NONE, false>(r, 1, s)));
+        BGemm u{};
+        u.M = d; u.N = I; u.K = T; u.A = dys; u.lda = d; u.a_div = 1; u.B = hs; u.ldb = I; u.b_div = 1;
+        u.C = a.ds_down; u.ldc = I;
+        CHK((bgemm<false, false, GROUP_NONE, false>(u, 1, s)));
+    }
+    // 7. router: dl and its share of dx (written), then the router gradient
+    hipLaunchKernelGGL(k_bwd_router, dim3(T), dim3(256), 0, s, T, d, x, a.w_router, a.idx, dg, dl, a.dx);
+    CHK(hipGetLastError());
+    hipLaunchKernelGGL(k_bwd_dwr, dim3((d + 255) / 256, E), dim3(256), 0, s, d, a.offsets, a.row_src, dl, x,
+                       a.dw_router);
+    CHK(hipGetLastError());
+    // 8. dx += shared + routed input gradients
+    {
+        const int64_t n = (int64_t)T * (d / 4);
+        hipLaunchKernelGGL(k_bwd_dx, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, T, d, dxs, dxi, a.row_of,
+                           a.dx);
+        CHK(hipGetLastError());
+    }
+#undef CHK
+    return hipSuccess;
+}
+
+}  // namespace moe

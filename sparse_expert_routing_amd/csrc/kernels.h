@@ -96,4 +96,22 @@ hipError_t launch_ffn_fp8_large(const FfnArgs &a, hipStream_t s);
 hipError_t launch_bias_update(int E, int k, int T, const int32_t *counts, float gamma, float *bias,
                               hipStream_t s);
 
+// Backward of the layer (bf16 experts): gradients for the forward's routing.
+struct BackwardArgs {
+    int T, d, I, k;
+    const void *x;            // [T, d] bf16
+    const float *w_router;    // [E, d]
+    const int32_t *idx;       // [T, k] chosen ids (ascending)
+    const float *weights;     // [T, k] combine weights
+    const int32_t *offsets, *row_src, *row_of;
+    FfnWeights experts, shared;
+    const void *y_perm;       // [T*k, d] bf16 routed outputs of the forward
+    const float *dy;          // [T, d]
+    float *dx, *dw_router, *dw_gate, *dw_up, *dw_down, *ds_gate, *ds_up, *ds_down;
+    float *dg;                // [T, k] or nullptr
+};
+size_t backward_ws_bytes(int T, int d, int I, int k);
+bool backward_ok(int d, int I);
+hipError_t launch_backward(const BackwardArgs &a, void *ws, hipStream_t s);
+
 }  // namespace moe

@@ -65,6 +65,12 @@ size_t route_ws(const moe_desc_t *d) {
 
 // The shared expert + combine: h (+ scales), x quantised (e4m3), and fp32
 // split-K partials at small T (bf16).
+size_t backward_ws(const moe_desc_t *d) {
+    return d->act == MOE_BF16 && d->wt == MOE_BF16 && moe::backward_ok(d->d, d->I)
+               ? align_up(moe::backward_ws_bytes(d->T, d->d, d->I, d->k))
+               : 0;
+}
+
 size_t combine_ws(const moe_desc_t *d) {
     return ffn_ws(d->T, d).total + xq_bytes(d) + align_up(moe::ffn_shared_split_bytes(d->T, d->d, d->I, d->wt));
 }
@@ -103,6 +109,7 @@ size_t moe_workspace_bytes(const moe_desc_t *d, int32_t stage) {
         case MOE_WS_DISPATCH: return dispatch_ws(d);
         case MOE_WS_FFN: return routed_ffn_ws(d);
         case MOE_WS_COMBINE: return combine_ws(d);
+        case MOE_WS_BACKWARD: return backward_ws(d);
     }
     return 0;
 }
@@ -257,6 +264,49 @@ moe_status_t moe_bias_update(const moe_desc_t *d, const int32_t *counts, float g
     if (!counts || !bias) return MOE_EINVAL;
     return hip_status(moe::launch_bias_update(d->E, d->k, d->T, counts, gamma, bias,
                                               static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_backward(const moe_desc_t *d, const void *x, const float *w_router, const int32_t *idx,
+                          const float *weights, const int32_t *offsets, const int32_t *row_src,
+                          const int32_t *row_of, const moe_ffn_weights_t *experts,
+                          const moe_ffn_weights_t *shared, const void *y_perm, const float *dy, float *dx,
+                          float *dw_router, float *dw_gate, float *dw_up, float *dw_down, float *ds_gate,
+                          float *ds_up, float *ds_down, float *dg, void *workspace, size_t ws_bytes,
+                          void *stream) {
+    moe_status_t st = check_desc(d);
+    if (st != MOE_OK) return st;
+    if (d->act != MOE_BF16 || d->wt != MOE_BF16 || !moe::backward_ok(d->d, d->I)) return MOE_ENOTSUP;
+    if (!x || !w_router || !idx || !weights || !offsets || !row_src || !row_of || !y_perm || !dy || !dx ||
+        !dw_router || !dw_gate || !dw_up || !dw_down || !ds_gate || !ds_up || !ds_down ||
+        !ffn_weights_ok(experts, d->wt) || !ffn_weights_ok(shared, d->wt))
+        return MOE_EINVAL;
+    if (!workspace || ws_bytes < backward_ws(d)) return MOE_EWORKSPACE;
+    moe::BackwardArgs a{};
+    a.T = d->T;
+    a.d = d->d;
+    a.I = d->I;
+    a.k = d->k;
+    a.x = x;
+    a.w_router = w_router;
+    a.idx = idx;
+    a.weights = weights;
+    a.offsets = offsets;
+    a.row_src = row_src;
+    a.row_of = row_of;
+    a.experts = to_internal(experts);
+    a.shared = to_internal(shared);
+    a.y_perm = y_perm;
+    a.dy = dy;
+    a.dx = dx;
+    a.dw_router = dw_router;
+    a.dw_gate = dw_gate;
+    a.dw_up = dw_up;
+    a.dw_down = dw_down;
+    a.ds_gate = ds_gate;
+    a.ds_up = ds_up;
+    a.ds_down = ds_down;
+    a.dg = dg;
+    return hip_status(moe::launch_backward(a, workspace, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

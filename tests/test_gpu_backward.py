@@ -1,0 +1,96 @@
+"""GPU parity of the layer backward (moe_backward, bf16 experts) against the
+oracle's backward fed the GPU's own routing (conditional parity: the choice
+carries no gradient, so both sides differentiate the same routing).
+
+Per case: route, dispatch and the routed forward on the GPU (y_perm is a
+backward input), a seeded dy, then every gradient -- dx, the router's, the
+routed experts' and the shared expert's weights, and the combine weights --
+compared with the oracle at the bf16 tolerance (max |a - r| / max |r|)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from sparse_expert_routing_amd import _lib
+from tests.gpu_util import TOL, dev, empty, host, max_rel, say
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "ds_gate", "ds_up", "ds_down", "dg")
+ORACLE_NAME = dict(dx="dx", dw_router="dwr", dw_gate="dwg", dw_up="dwu", dw_down="dwd", ds_gate="dsg",
+                   ds_up="dsu", ds_down="dsd", dg="dg")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _lib.load()
+
+
+def skewed_ids(T, seed):
+    """Every token takes experts 0, 1, 2 plus 5 others: hot groups of T rows."""
+    tail = synth.random_ids(T + 1, seed, T, 253, 5) + 3
+    return np.ascontiguousarray(np.concatenate([np.tile(np.arange(3, dtype=np.int32), (T, 1)), tail], axis=1))
+
+
+def run_case(T, d, I, kind, seed):
+    cfg = synth.Config("bwd", seed=seed, T=T, d=d, I=I)
+    say(f"[backward] T={T} d={d} I={I} {kind}")
+    x, wr, bias = synth.make_router(cfg)
+    experts = synth.make_ffn(cfg, 256, (synth.TID_GATE, synth.TID_UP, synth.TID_DOWN))
+    shared = synth.make_ffn(cfg, 1, (synth.TID_SGATE, synth.TID_SUP, synth.TID_SDOWN))
+    dy = synth.normal(seed, synth.TID_AUX, (T, d), 1.0, "f32")
+    ds = _lib.desc(T, d, 256, 8, I, "bf16", "bf16")
+    xd, wrd = dev(x), dev(wr)
+    idx, g = empty((T, 8), torch.int32), empty((T, 8), torch.float32)
+    ws = empty(max(_lib.workspace_bytes(ds, s) for s in range(5)), torch.uint8)
+    if kind == "routed":
+        _lib.moe_route(ds, xd, wrd, dev(bias), idx, g, None, ws)
+    else:  # a given id pattern; combine weights from the oracle's affinities
+        ids = skewed_ids(T, seed)
+        _, _, _, s = oracle.route(oracle.shape_of(cfg), x, wr, bias, want_s=True)
+        sel = np.take_along_axis(s, ids, 1)
+        idx.copy_(torch.from_numpy(ids))
+        g.copy_(torch.from_numpy((sel / sel.sum(1, keepdims=True)).astype(np.float32)))
+    counts, offsets = empty(256, torch.int32), empty(257, torch.int32)
+    row_src, row_of = empty(T * 8, torch.int32), empty(T * 8, torch.int32)
+    _lib.moe_dispatch(ds, idx, None, counts, offsets, row_src, row_of, None, None, ws)
+    ew = {n: dev(a) for n, a in experts.items() if a is not None}
+    sw = {n: dev(a) for n, a in shared.items() if a is not None}
+    efw = _lib.ffn_weights(ew["gate"], ew["up"], ew["down"])
+    sfw = _lib.ffn_weights(sw["gate"], sw["up"], sw["down"])
+    y_perm = empty((T * 8, d), torch.int16)
+    _lib.moe_expert_gate_up_rows(ds, xd, row_src, offsets, efw, ws)
+    _lib.moe_expert_down(ds, offsets, efw, y_perm, ws)
+    grads = dict(dx=empty((T, d), torch.float32), dw_router=empty((256, d), torch.float32),
+                 dw_gate=empty((256, I, d), torch.float32), dw_up=empty((256, I, d), torch.float32),
+                 dw_down=empty((256, d, I), torch.float32), ds_gate=empty((I, d), torch.float32),
+                 ds_up=empty((I, d), torch.float32), ds_down=empty((d, I), torch.float32),
+                 dg=empty((T, 8), torch.float32))
+    for t in grads.values():
+        t.fill_(float("nan"))  # every element must be written
+    _lib.moe_backward(ds, xd, wrd, idx, g, offsets, row_src, row_of, efw, sfw, y_perm, dev(dy), grads, ws)
+    torch.cuda.synchronize()
+    gi = host(idx)
+    o = oracle.backward(oracle.shape_of(cfg), x, wr, gi, experts, shared, dy)
+    worst = 0.0
+    for n in GRADS:
+        a = host(grads[n])
+        assert np.isfinite(a).all(), f"{n}: unwritten or non-finite elements"
+        err = max_rel(a, o[ORACLE_NAME[n]])
+        worst = max(worst, err)
+        assert err <= TOL["bf16"], f"{n}: max rel err {err:.3e}"
+    say(f"[backward] T={T} {kind}: worst max rel err {worst:.3e} over {len(GRADS)} gradients")
+
+
+@pytest.mark.parametrize("T,d,I,kind,seed", [(300, 512, 256, "routed", 41), (1, 256, 128, "routed", 42),
+                                             (257, 256, 384, "skewed", 43)])
+def test_backward_matches_oracle(T, d, I, kind, seed):
+    run_case(T, d, I, kind, seed)
+
+
+def test_backward_rejects_other_types():
+    ds = _lib.desc(32, 256, 256, 8, 64, "f32", "f32")
+    assert _lib.workspace_bytes(ds, _lib.MOE_WS_BACKWARD) == 0
