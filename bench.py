@@ -54,6 +54,8 @@ def main():
                     help="workload (4: the skewed prefill layer the metric is quoted on)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the layer backward (moe_backward, bf16) after the timed loop and report it")
     ap.add_argument("--fresh-batches", type=int, default=0,
                     help="N > 0: every step takes a new token batch (N batches resident in HBM, cycled); "
                          "default: the same batch every step")
@@ -208,9 +210,52 @@ def main():
         "routed_row_tiles_mean": float(tiles.mean()),
     }
 
+    if args.backward:
+        out["backward"] = time_backward(cfg, layer, xs[(K - 1) % len(xs)], min(K, 20))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def time_backward(cfg, layer, x, n):
+    """moe_backward on the last timed step's routing (a seeded dy), n timed calls after
+    2 warm-up calls, HIP events on the launch stream.  Algorithmic FLOPs per call: per
+    routed row and per shared row 16*d*I (recompute gate/up 4, dh 2, dx 4, dW gate/up 4,
+    dW down 2, all x d*I), plus the router's 2 * 2*k*d per token."""
+    import torch
+    from sparse_expert_routing_amd import _lib
+    T, d, I, k, E = cfg.T, cfg.d, cfg.I, cfg.k, cfg.E
+    if cfg.act != "bf16" or cfg.wt != "bf16":
+        return None
+    D = layer.desc
+    stream = torch.cuda.current_stream()
+    dev = dict(device="cuda", dtype=torch.float32)
+    grads = dict(dx=torch.empty((T, d), **dev), dw_router=torch.empty((E, d), **dev),
+                 dw_gate=torch.empty((E, I, d), **dev), dw_up=torch.empty((E, I, d), **dev),
+                 dw_down=torch.empty((E, d, I), **dev), ds_gate=torch.empty((I, d), **dev),
+                 ds_up=torch.empty((I, d), **dev), ds_down=torch.empty((d, I), **dev),
+                 dg=torch.empty((T, k), **dev))
+    gen = torch.Generator(device="cuda").manual_seed(cfg.seed)
+    dy = torch.randn((T, d), generator=gen, **dev)
+    ws = torch.empty(_lib.workspace_bytes(D, _lib.MOE_WS_BACKWARD), dtype=torch.uint8, device="cuda")
+
+    def call():
+        _lib.moe_backward(D, x, layer.wr, layer.idx, layer.w, layer.offsets, layer.row_src, layer.row_of,
+                          layer.ex_w, layer.sh_w, layer.y_perm, dy, grads, ws, stream)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    flops = 16.0 * (T * k + T) * d * I + 4.0 * T * k * d
+    log(f"[bench] backward {ms:.3f} ms, {flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s algorithmic")
+    return {"ms": ms, "calls": n, "flops_per_call": flops, "tflops": flops / (ms * 1e-3) / 1e12,
+            "frac_of_bf16_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
 def measured_traffic():
