@@ -238,6 +238,96 @@ __global__ __launch_bounds__(256) void k_bgemm(BGemm p) {
             }
 }
 
+// ------------------------------------------------------------- transposes
+
+// out[g][c*ldo + coff + map(r)] = in[g][src(r)*ldi + c] for r < R, c < C, bf16,
+// through 64x64 LDS tiles (both sides coalesced).  src(r) = rows[r] / rdiv
+// (a row gather) or r; map(r) = rmap[r] (a padded row position) or r.
+__global__ __launch_bounds__(256) void k_transpose(int R, int C, const uint16_t *__restrict__ in, int64_t ldi,
+                                                   int64_t gin, const int32_t *__restrict__ rows, int rdiv,
+                                                   const int32_t *__restrict__ rmap, uint16_t *__restrict__ out,
+                                                   int64_t ldo, int64_t gout, int coff) {
+    __shared__ uint16_t tile[64][66];
+    const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64, g = blockIdx.z;
+    const int tid = threadIdx.x;
+    in += (int64_t)g * gin;
+    out += (int64_t)g * gout;
+    // load: 64 rows x 64 columns, 4 columns (8 bytes) per thread per pass
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+        const int rr = pass * 16 + (tid >> 4), cc = (tid & 15) * 4;
+        const int r = r0 + rr;
+        uint2 v = uint2{0u, 0u};
+        if (r < R) {
+            const int64_t src = rows ? rows[r] / rdiv : r;
+            v = *reinterpret_cast<const uint2 *>(in + src * ldi + c0 + cc);
+        }
+        tile[rr][cc] = (uint16_t)(v.x & 0xffffu);
+        tile[rr][cc + 1] = (uint16_t)(v.x >> 16);
+        tile[rr][cc + 2] = (uint16_t)(v.y & 0xffffu);
+        tile[rr][cc + 3] = (uint16_t)(v.y >> 16);
+    }
+    __syncthreads();
+    // store: 64 output rows (columns c) x 64 positions, one element per thread per pass
+#pragma unroll 4
+    for (int pass = 0; pass < 16; ++pass) {
+        const int cc = pass * 4 + (tid >> 6), rr = tid & 63;
+        const int r = r0 + rr;
+        if (r < R) {
+            const int64_t pos = rmap ? rmap[r] : r;
+            out[(int64_t)(c0 + cc) * ldo + coff + pos] = tile[rr][cc];
+        }
+    }
+}
+
+// Padded row positions: poff = exclusive scan of the group sizes rounded up
+// to 32 (one wave; 256 groups, 4 per lane), rmap[r] = poff[e] + r - off[e].
+__global__ __launch_bounds__(64) void k_pad_offsets(const int32_t *__restrict__ off, int32_t *__restrict__ poff) {
+    const int lane = threadIdx.x;
+    int c[4], s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane * 4 + i;
+        c[i] = (off[e + 1] - off[e] + 31) / 32 * 32;
+        s += c[i];
+    }
+    const int incl = wave_incl_scan(s);
+    int run = incl - s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        poff[lane * 4 + i] = run;
+        run += c[i];
+    }
+    if (lane == 63) poff[kE] = incl;
+}
+
+__global__ __launch_bounds__(256) void k_row_map(int A, const int32_t *__restrict__ off,
+                                                 const int32_t *__restrict__ poff, int32_t *__restrict__ rmap) {
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r >= A) return;
+    int lo = 0, hi = kE;  // the group e with off[e] <= r < off[e+1]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (off[mid] <= r) lo = mid; else hi = mid;
+    }
+    rmap[r] = poff[lo] + r - off[lo];
+}
+
+// Zero the padding positions [poff[e] + c_e, poff[e+1]) of `nrows` rows of a
+// transposed buffer (row stride ld).
+// (off == nullptr: one group whose padding is [start0, start0 + n0).)
+__global__ __launch_bounds__(256) void k_pad_zero(int nrows, const int32_t *__restrict__ off,
+                                                  const int32_t *__restrict__ poff, uint16_t *__restrict__ buf,
+                                                  int64_t ld, int start0, int n0) {
+    const int e = blockIdx.y;
+    const int start = off ? poff[e] + off[e + 1] - off[e] : start0;
+    const int n = off ? poff[e + 1] - start : n0;  // < 32
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < nrows * n; i += gridDim.x * 256) {
+        const int row = i / n, j = i - row * n;
+        buf[(int64_t)row * ld + start + j] = 0;
+    }
+}
+
 // ------------------------------------------------------------ elementwise
 
 // Per token t (one wave): dg_j = sum_n dy[t,n] y_perm[r_j,n] (r_j =
@@ -279,19 +369,19 @@ __global__ __launch_bounds__(256) void k_bwd_combine(int T, int d, const float *
 }
 
 // From the pre-activations P [rows, 2I] (gate | up, fp32) and dh [rows, I]:
-// h = bf16(silu(a) b), da = bf16(dh b sig(a) (1 + a (1 - sig(a)))),
-// db = bf16(dh silu(a)).
+// h = bf16(silu(a) b) [rows, I], and dab [rows, 2I] = (da | db) with
+// da = bf16(dh b sig(a) (1 + a (1 - sig(a)))), db = bf16(dh silu(a)).
 __global__ __launch_bounds__(256) void k_bwd_swiglu(int64_t n, int I, const float *__restrict__ P,
                                                     const float *__restrict__ dh, uint16_t *__restrict__ h,
-                                                    uint16_t *__restrict__ da, uint16_t *__restrict__ db) {
+                                                    uint16_t *__restrict__ dab) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
     const int64_t row = i / I, c = i - row * I;
     const float a = P[row * 2 * I + c], b = P[row * 2 * I + I + c], g = dh[i];
     const float sg = 1.0f / (1.0f + expf(-a));
     h[i] = (uint16_t)f32_to_bf16(a * sg * b);
-    da[i] = (uint16_t)f32_to_bf16(g * b * sg * (1.0f + a * (1.0f - sg)));
-    db[i] = (uint16_t)f32_to_bf16(g * a * sg);
+    dab[row * 2 * I + c] = (uint16_t)f32_to_bf16(g * b * sg * (1.0f + a * (1.0f - sg)));
+    dab[row * 2 * I + I + c] = (uint16_t)f32_to_bf16(g * a * sg);
 }
 
 // Per token t (one workgroup): s_j = sigmoid(x_t . wr_{e_j}) in fp32, then
@@ -396,143 +486,208 @@ hipError_t bgemm(const BGemm &p, int G, hipStream_t s) {
 
 }  // namespace
 
-size_t backward_ws_bytes(int T, int d, int I, int k) {
-    auto al = [](size_t b) { return (b + 255) / 256 * 256; };
-    const size_t A = (size_t)T * k, R = A + T;  // routed rows, then the shared expert's T rows
-    return al(R * d * 2)          // output gradients (bf16): routed, then shared
-           + al(R * 2 * I * 4)    // pre-activations (fp32)
-           + al(R * I * 4)        // dh (fp32)
-           + 3 * al(R * I * 2)    // h, da, db (bf16)
-           + al(R * d * 4)        // input gradients (fp32)
-           + al((size_t)T * k * 4)  // dl
-           + al((size_t)T * k * 4);  // dg (when the caller does not ask for it)
+namespace {
+
+// The backward's workspace, carved in a fixed order (base == nullptr: sizes only).
+struct BwdWs {
+    uint16_t *dyo;         // [R, d] output gradients: routed rows, then shared rows (bf16)
+    float *P;              // [R, 2I] pre-activations (gate | up)
+    float *dh;             // [R, I]
+    uint16_t *h16;         // [R, I]
+    uint16_t *dab;         // [R, 2I] SwiGLU input gradients (da | db)
+    float *dxi;            // [R, d] input gradients
+    float *dl, *dg;        // [T*k]
+    int32_t *poff, *rmap;  // [E+1], [A]
+    uint16_t *wdT;         // [E, I, d] down weights transposed
+    uint16_t *wguT;        // [E, d, 2I] gate | up weights transposed
+    uint16_t *sdT, *sguT;  // the shared expert's: [I, d], [d, 2I]
+    uint16_t *xT, *dyoT, *hT, *dabT;       // routed rows transposed, padded per expert: [*, Rp]
+    uint16_t *xsT, *dysT, *hsT, *dabsT;    // shared rows transposed: [*, Tp]
+    size_t bytes;
+};
+
+BwdWs carve(char *base, int T, int d, int I, int k) {
+    BwdWs w{};
+    size_t o = 0;
+    const size_t A = (size_t)T * k, R = A + T, Rp = A + 32 * (size_t)kE, Tp = ((size_t)T + 31) / 32 * 32;
+    auto take = [&](size_t n) -> char * {
+        char *p = base ? base + o : nullptr;
+        o += (n + 255) / 256 * 256;
+        return p;
+    };
+    w.dyo = reinterpret_cast<uint16_t *>(take(R * d * 2));
+    w.P = reinterpret_cast<float *>(take(R * 2 * I * 4));
+    w.dh = reinterpret_cast<float *>(take(R * I * 4));
+    w.h16 = reinterpret_cast<uint16_t *>(take(R * I * 2));
+    w.dab = reinterpret_cast<uint16_t *>(take(R * 2 * I * 2));
+    w.dxi = reinterpret_cast<float *>(take(R * d * 4));
+    w.dl = reinterpret_cast<float *>(take(A * 4));
+    w.dg = reinterpret_cast<float *>(take(A * 4));
+    w.poff = reinterpret_cast<int32_t *>(take((kE + 1) * 4));
+    w.rmap = reinterpret_cast<int32_t *>(take(A * 4));
+    w.wdT = reinterpret_cast<uint16_t *>(take((size_t)kE * I * d * 2));
+    w.wguT = reinterpret_cast<uint16_t *>(take((size_t)kE * d * 2 * I * 2));
+    w.sdT = reinterpret_cast<uint16_t *>(take((size_t)I * d * 2));
+    w.sguT = reinterpret_cast<uint16_t *>(take((size_t)d * 2 * I * 2));
+    w.xT = reinterpret_cast<uint16_t *>(take((size_t)d * Rp * 2));
+    w.dyoT = reinterpret_cast<uint16_t *>(take((size_t)d * Rp * 2));
+    w.hT = reinterpret_cast<uint16_t *>(take((size_t)I * Rp * 2));
+    w.dabT = reinterpret_cast<uint16_t *>(take((size_t)2 * I * Rp * 2));
+    w.xsT = reinterpret_cast<uint16_t *>(take((size_t)d * Tp * 2));
+    w.dysT = reinterpret_cast<uint16_t *>(take((size_t)d * Tp * 2));
+    w.hsT = reinterpret_cast<uint16_t *>(take((size_t)I * Tp * 2));
+    w.dabsT = reinterpret_cast<uint16_t *>(take((size_t)2 * I * Tp * 2));
+    w.bytes = o;
+    return w;
 }
 
-bool backward_ok(int d, int I) { return d % GN == 0 && I % GN == 0 && d % GK == 0 && I % GK == 0 && d % 128 == 0; }
+// out[g] = in[g] transposed (R x C -> C x R), see k_transpose
+hipError_t transpose(int R, int C, int G, const uint16_t *in, int64_t ldi, int64_t gin, const int32_t *rows,
+                     int rdiv, const int32_t *rmap, uint16_t *out, int64_t ldo, int64_t gout, int coff,
+                     hipStream_t s) {
+    if (R <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_transpose, dim3((R + 63) / 64, C / 64, G), dim3(256), 0, s, R, C, in, ldi, gin, rows, rdiv,
+                       rmap, out, ldo, gout, coff);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t backward_ws_bytes(int T, int d, int I, int k) { return carve(nullptr, T, d, I, k).bytes; }
+
+bool backward_ok(int d, int I) { return d % 128 == 0 && I % 128 == 0; }
 
 hipError_t launch_backward(const BackwardArgs &a, void *ws, hipStream_t s) {
-    auto al = [](size_t b) { return (b + 255) / 256 * 256; };
     const int T = a.T, d = a.d, I = a.I, k = a.k, E = kE;
-    const int64_t A = (int64_t)T * k, R = A + T;
-    char *w = static_cast<char *>(ws);
-    uint16_t *dyo = reinterpret_cast<uint16_t *>(w);            // [R, d]: routed rows, then shared
-    w += al((size_t)R * d * 2);
-    float *P = reinterpret_cast<float *>(w);                    // [R, 2I]
-    w += al((size_t)R * 2 * I * 4);
-    float *dh = reinterpret_cast<float *>(w);                   // [R, I]
-    w += al((size_t)R * I * 4);
-    uint16_t *h16 = reinterpret_cast<uint16_t *>(w);
-    w += al((size_t)R * I * 2);
-    uint16_t *da16 = reinterpret_cast<uint16_t *>(w);
-    w += al((size_t)R * I * 2);
-    uint16_t *db16 = reinterpret_cast<uint16_t *>(w);
-    w += al((size_t)R * I * 2);
-    float *dxi = reinterpret_cast<float *>(w);                  // [R, d]
-    w += al((size_t)R * d * 4);
-    float *dl = reinterpret_cast<float *>(w);
-    w += al((size_t)T * k * 4);
-    float *dg = a.dg ? a.dg : reinterpret_cast<float *>(w);
+    const int A = T * k;
+    const int64_t Rp = (int64_t)A + 32 * kE, Tp = ((int64_t)T + 31) / 32 * 32;
+    const BwdWs w = carve(static_cast<char *>(ws), T, d, I, k);
+    float *dg = a.dg ? a.dg : w.dg;
     const uint16_t *x = static_cast<const uint16_t *>(a.x);
+    const uint16_t *eg = static_cast<const uint16_t *>(a.experts.gate), *eu = static_cast<const uint16_t *>(a.experts.up),
+                   *ed = static_cast<const uint16_t *>(a.experts.down);
+    const uint16_t *sg = static_cast<const uint16_t *>(a.shared.gate), *su = static_cast<const uint16_t *>(a.shared.up),
+                   *sd = static_cast<const uint16_t *>(a.shared.down);
     // shared-expert slices of the row-major buffers
-    uint16_t *dys = dyo + A * d;
-    float *Ps = P + A * 2 * I, *dhs = dh + A * I, *dxs = dxi + A * d;
-    uint16_t *hs = h16 + A * I, *das = da16 + A * I, *dbs = db16 + A * I;
+    uint16_t *dys = w.dyo + (int64_t)A * d;
+    float *Ps = w.P + (int64_t)A * 2 * I, *dhs = w.dh + (int64_t)A * I, *dxs = w.dxi + (int64_t)A * d;
+    uint16_t *hs = w.h16 + (int64_t)A * I, *dabs = w.dab + (int64_t)A * 2 * I;
     hipError_t e;
 #define CHK(call)                      \
     if ((e = (call)) != hipSuccess) return e;
 
+    // 0. padded row positions of the expert groups; transposed weights
+    hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(64), 0, s, a.offsets, w.poff);
+    CHK(hipGetLastError());
+    hipLaunchKernelGGL(k_row_map, dim3((A + 255) / 256), dim3(256), 0, s, A, a.offsets, w.poff, w.rmap);
+    CHK(hipGetLastError());
+    CHK(transpose(d, I, E, ed, I, (int64_t)d * I, nullptr, 1, nullptr, w.wdT, d, (int64_t)I * d, 0, s));
+    CHK(transpose(I, d, E, eg, d, (int64_t)I * d, nullptr, 1, nullptr, w.wguT, 2 * I, (int64_t)d * 2 * I, 0, s));
+    CHK(transpose(I, d, E, eu, d, (int64_t)I * d, nullptr, 1, nullptr, w.wguT, 2 * I, (int64_t)d * 2 * I, I, s));
+    CHK(transpose(d, I, 1, sd, I, 0, nullptr, 1, nullptr, w.sdT, d, 0, 0, s));
+    CHK(transpose(I, d, 1, sg, d, 0, nullptr, 1, nullptr, w.sguT, 2 * I, 0, 0, s));
+    CHK(transpose(I, d, 1, su, d, 0, nullptr, 1, nullptr, w.sguT, 2 * I, 0, I, s));
+
     // 1. combine backward
     hipLaunchKernelGGL(k_bwd_combine, dim3((T + 3) / 4), dim3(256), 0, s, T, d, a.dy,
-                       static_cast<const uint16_t *>(a.y_perm), a.row_of, a.weights, dyo, dys, dg);
+                       static_cast<const uint16_t *>(a.y_perm), a.row_of, a.weights, w.dyo, dys, dg);
     CHK(hipGetLastError());
+    // The data-gradient GEMMs (and the recompute) are NT GEMMs grouped over
+    // M: the forward's persistent 256x256-tile kernel with an fp32 epilogue
+    // when the groups are large enough, else k_bgemm.
+    auto nt = [&](const LargeGemmArgs &g, const int32_t *offsets, int64_t lda) -> hipError_t {
+        if (bf16_large_gemm_ok(g)) return launch_bf16_large_gemm(g, s);
+        for (int half = 0; half < (g.dual ? 2 : 1); ++half) {
+            BGemm p{};
+            p.M = g.M; p.N = g.N; p.K = g.K; p.offsets = offsets; p.A = g.A; p.lda = lda;
+            p.a_rows = g.a_rows; p.a_div = g.a_div; p.B = half ? g.B1 : g.B0; p.ldb = g.K;
+            p.bstride = (int64_t)g.N * g.K; p.C = g.out + (half ? g.up_off : 0); p.ldc = g.ldo;
+            const hipError_t r = offsets ? bgemm<true, true, GROUP_M, false>(p, E, s)
+                                         : bgemm<true, true, GROUP_NONE, false>(p, 1, s);
+            if (r != hipSuccess) return r;
+        }
+        return hipSuccess;
+    };
     // 2. pre-activations: routed rows gather x through row_src; shared rows are x
-    {
-        BGemm p{};
-        p.M = (int)A; p.N = I; p.K = d; p.offsets = a.offsets;
-        p.A = x; p.lda = d; p.a_rows = a.row_src; p.a_div = k;
-        p.ldb = d; p.bstride = (int64_t)I * d; p.ldc = 2 * I;
-        p.B = static_cast<const uint16_t *>(a.experts.gate); p.C = P;
-        CHK((bgemm<true, true, GROUP_M, false>(p, E, s)));
-        p.B = static_cast<const uint16_t *>(a.experts.up); p.C = P + I;
-        CHK((bgemm<true, true, GROUP_M, false>(p, E, s)));
-        BGemm q{};
-        q.M = T; q.N = I; q.K = d; q.A = x; q.lda = d; q.a_div = 1; q.ldb = d; q.ldc = 2 * I;
-        q.B = static_cast<const uint16_t *>(a.shared.gate); q.C = Ps;
-        CHK((bgemm<true, true, GROUP_NONE, false>(q, 1, s)));
-        q.B = static_cast<const uint16_t *>(a.shared.up); q.C = Ps + I;
-        CHK((bgemm<true, true, GROUP_NONE, false>(q, 1, s)));
-    }
-    // 3. dh = (output gradient) W_down: B(k = n, i) = W_down[n*I + i], N-contiguous
-    {
-        BGemm p{};
-        p.M = (int)A; p.N = I; p.K = d; p.offsets = a.offsets; p.A = dyo; p.lda = d; p.a_div = 1;
-        p.B = static_cast<const uint16_t *>(a.experts.down); p.ldb = I; p.bstride = (int64_t)d * I;
-        p.C = dh; p.ldc = I;
-        CHK((bgemm<true, false, GROUP_M, false>(p, E, s)));
-        BGemm q{};
-        q.M = T; q.N = I; q.K = d; q.A = dys; q.lda = d; q.a_div = 1;
-        q.B = static_cast<const uint16_t *>(a.shared.down); q.ldb = I; q.C = dhs; q.ldc = I;
-        CHK((bgemm<true, false, GROUP_NONE, false>(q, 1, s)));
-    }
+    CHK(nt(LargeGemmArgs{A, a.offsets, x, a.row_src, k, T, d, eg, eu, I, w.P, 2 * I, I, true}, a.offsets, d));
+    CHK(nt(LargeGemmArgs{T, nullptr, x, nullptr, 1, T, d, sg, su, I, Ps, 2 * I, I, true}, nullptr, d));
+    // 3. dh = (output gradient) W_down, with W_down transposed to [E, I, d]
+    CHK(nt(LargeGemmArgs{A, a.offsets, w.dyo, nullptr, 1, A, d, w.wdT, nullptr, I, w.dh, I, 0, false}, a.offsets, d));
+    CHK(nt(LargeGemmArgs{T, nullptr, dys, nullptr, 1, T, d, w.sdT, nullptr, I, dhs, I, 0, false}, nullptr, d));
     // 4. SwiGLU backward (routed and shared rows in one pass)
     {
-        const int64_t n = R * I;
-        hipLaunchKernelGGL(k_bwd_swiglu, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n, I, P, dh, h16, da16,
-                           db16);
+        const int64_t n = ((int64_t)A + T) * I;
+        hipLaunchKernelGGL(k_bwd_swiglu, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n, I, w.P, w.dh, w.h16,
+                           w.dab);
         CHK(hipGetLastError());
     }
-    // 5. input gradients: da W_gate + db W_up (B(k = i, n) = W[i*d + n], N-contiguous)
+    // 5. input gradients: (da | db) [rows, 2I] times (W_gate | W_up) transposed to [E, d, 2I]
+    CHK(nt(LargeGemmArgs{A, a.offsets, w.dab, nullptr, 1, A, 2 * I, w.wguT, nullptr, d, w.dxi, d, 0, false}, a.offsets,
+           2 * I));
+    CHK(nt(LargeGemmArgs{T, nullptr, dabs, nullptr, 1, T, 2 * I, w.sguT, nullptr, d, dxs, d, 0, false}, nullptr, 2 * I));
+    // 6. weight gradients.  The rows each expert reduces over are transposed
+    //    into [*, Rp] buffers where expert e's rows start at poff[e] (32-aligned,
+    //    zero-padded), so both operands are K-contiguous and every K range is
+    //    whole 32-wide stages.
     {
+        CHK(transpose(A, d, 1, x, d, 0, a.row_src, k, w.rmap, w.xT, Rp, 0, 0, s));
+        CHK(transpose(A, d, 1, w.dyo, d, 0, nullptr, 1, w.rmap, w.dyoT, Rp, 0, 0, s));
+        CHK(transpose(A, I, 1, w.h16, I, 0, nullptr, 1, w.rmap, w.hT, Rp, 0, 0, s));
+        CHK(transpose(A, 2 * I, 1, w.dab, 2 * I, 0, nullptr, 1, w.rmap, w.dabT, Rp, 0, 0, s));
+        struct {
+            uint16_t *buf;
+            int rows;
+        } pads[4] = {{w.xT, d}, {w.dyoT, d}, {w.hT, I}, {w.dabT, 2 * I}};
+        for (auto &pd : pads) {
+            hipLaunchKernelGGL(k_pad_zero, dim3(16, E), dim3(256), 0, s, pd.rows, a.offsets, w.poff, pd.buf, Rp, 0, 0);
+            CHK(hipGetLastError());
+        }
         BGemm p{};
-        p.M = (int)A; p.N = d; p.K = I; p.offsets = a.offsets; p.lda = I; p.a_div = 1;
-        p.ldb = d; p.bstride = (int64_t)I * d; p.C = dxi; p.ldc = d;
-        p.A = da16; p.B = static_cast<const uint16_t *>(a.experts.gate);
-        CHK((bgemm<true, false, GROUP_M, false>(p, E, s)));
-        p.A = db16; p.B = static_cast<const uint16_t *>(a.experts.up);
-        CHK((bgemm<true, false, GROUP_M, true>(p, E, s)));
+        p.M = I; p.N = d; p.K = (int)Rp; p.offsets = w.poff; p.lda = Rp; p.a_div = 1;
+        p.B = w.xT; p.ldb = Rp; p.b_div = 1; p.ldc = d; p.cstride = (int64_t)I * d;
+        p.A = w.dabT; p.C = a.dw_gate;
+        CHK((bgemm<true, true, GROUP_K, false>(p, E, s)));
+        p.A = w.dabT + (int64_t)I * Rp; p.C = a.dw_up;
+        CHK((bgemm<true, true, GROUP_K, false>(p, E, s)));
         BGemm q{};
-        q.M = T; q.N = d; q.K = I; q.lda = I; q.a_div = 1; q.ldb = d; q.C = dxs; q.ldc = d;
-        q.A = das; q.B = static_cast<const uint16_t *>(a.shared.gate);
-        CHK((bgemm<true, false, GROUP_NONE, false>(q, 1, s)));
-        q.A = dbs; q.B = static_cast<const uint16_t *>(a.shared.up);
-        CHK((bgemm<true, false, GROUP_NONE, true>(q, 1, s)));
-    }
-    // 6. weight gradients: reductions over each expert's rows (A(m, k = r)
-    //    and B(k = r, n) both row-major over r)
-    {
-        BGemm p{};
-        p.M = I; p.N = d; p.K = (int)A; p.offsets = a.offsets; p.lda = I; p.a_div = 1;
-        p.B = x; p.ldb = d; p.b_rows = a.row_src; p.b_div = k; p.ldc = d; p.cstride = (int64_t)I * d;
-        p.A = da16; p.C = a.dw_gate;
-        CHK((bgemm<false, false, GROUP_K, false>(p, E, s)));
-        p.A = db16; p.C = a.dw_up;
-        CHK((bgemm<false, false, GROUP_K, false>(p, E, s)));
-        BGemm q{};
-        q.M = d; q.N = I; q.K = (int)A; q.offsets = a.offsets; q.A = dyo; q.lda = d; q.a_div = 1;
-        q.B = h16; q.ldb = I; q.b_div = 1; q.C = a.dw_down; q.ldc = I; q.cstride = (int64_t)d * I;
-        CHK((bgemm<false, false, GROUP_K, false>(q, E, s)));
-        // shared expert: one group over all T rows
+        q.M = d; q.N = I; q.K = (int)Rp; q.offsets = w.poff; q.A = w.dyoT; q.lda = Rp; q.a_div = 1;
+        q.B = w.hT; q.ldb = Rp; q.b_div = 1; q.C = a.dw_down; q.ldc = I; q.cstride = (int64_t)d * I;
+        CHK((bgemm<true, true, GROUP_K, false>(q, E, s)));
+        // shared expert: one group over all T rows (padded to Tp with zeros)
+        CHK(transpose(T, d, 1, x, d, 0, nullptr, 1, nullptr, w.xsT, Tp, 0, 0, s));
+        CHK(transpose(T, d, 1, dys, d, 0, nullptr, 1, nullptr, w.dysT, Tp, 0, 0, s));
+        CHK(transpose(T, I, 1, hs, I, 0, nullptr, 1, nullptr, w.hsT, Tp, 0, 0, s));
+        CHK(transpose(T, 2 * I, 1, dabs, 2 * I, 0, nullptr, 1, nullptr, w.dabsT, Tp, 0, 0, s));
+        struct {
+            uint16_t *buf;
+            int rows;
+        } spads[4] = {{w.xsT, d}, {w.dysT, d}, {w.hsT, I}, {w.dabsT, 2 * I}};
+        for (auto &pd : spads) {
+            hipLaunchKernelGGL(k_pad_zero, dim3(16, 1), dim3(256), 0, s, pd.rows, nullptr, nullptr, pd.buf, Tp, T,
+                               (int)(Tp - T));
+            CHK(hipGetLastError());
+        }
         BGemm r{};
-        r.M = I; r.N = d; r.K = T; r.lda = I; r.a_div = 1; r.B = x; r.ldb = d; r.b_div = 1; r.ldc = d;
-        r.A = das; r.C = a.ds_gate;
-        CHK((bgemm<false, false, GROUP_NONE, false>(r, 1, s)));
-        r.A = dbs; r.C = a.ds_up;
-        CHK((bgemm<false, false, GROUP_NONE, false>(r, 1, s)));
+        r.M = I; r.N = d; r.K = (int)Tp; r.lda = Tp; r.a_div = 1; r.B = w.xsT; r.ldb = Tp; r.b_div = 1; r.ldc = d;
+        r.A = w.dabsT; r.C = a.ds_gate;
+        CHK((bgemm<true, true, GROUP_NONE, false>(r, 1, s)));
+        r.A = w.dabsT + (int64_t)I * Tp; r.C = a.ds_up;
+        CHK((bgemm<true, true, GROUP_NONE, false>(r, 1, s)));
         BGemm u{};
-        u.M = d; u.N = I; u.K = T; u.A = dys; u.lda = d; u.a_div = 1; u.B = hs; u.ldb = I; u.b_div = 1;
+        u.M = d; u.N = I; u.K = (int)Tp; u.A = w.dysT; u.lda = Tp; u.a_div = 1; u.B = w.hsT; u.ldb = Tp; u.b_div = 1;
         u.C = a.ds_down; u.ldc = I;
-        CHK((bgemm<false, false, GROUP_NONE, false>(u, 1, s)));
+        CHK((bgemm<true, true, GROUP_NONE, false>(u, 1, s)));
     }
     // 7. router: dl and its share of dx (written), then the router gradient
-    hipLaunchKernelGGL(k_bwd_router, dim3(T), dim3(256), 0, s, T, d, x, a.w_router, a.idx, dg, dl, a.dx);
+    hipLaunchKernelGGL(k_bwd_router, dim3(T), dim3(256), 0, s, T, d, x, a.w_router, a.idx, dg, w.dl, a.dx);
     CHK(hipGetLastError());
-    hipLaunchKernelGGL(k_bwd_dwr, dim3((d + 255) / 256, E), dim3(256), 0, s, d, a.offsets, a.row_src, dl, x,
+    hipLaunchKernelGGL(k_bwd_dwr, dim3((d + 255) / 256, E), dim3(256), 0, s, d, a.offsets, a.row_src, w.dl, x,
                        a.dw_router);
     CHK(hipGetLastError());
     // 8. dx += shared + routed input gradients
     {
         const int64_t n = (int64_t)T * (d / 4);
-        hipLaunchKernelGGL(k_bwd_dx, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, T, d, dxs, dxi, a.row_of,
+        hipLaunchKernelGGL(k_bwd_dx, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, T, d, dxs, w.dxi, a.row_of,
                            a.dx);
         CHK(hipGetLastError());
     }

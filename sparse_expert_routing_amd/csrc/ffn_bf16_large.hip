@@ -59,7 +59,9 @@ constexpr int kGroupM = 8;   // row tiles per ordering group
 constexpr int kChRows = 64;  // epilogue chunk rows
 constexpr int kChLd = LB + 4;
 
-enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_COMBINE = 2 };
+// EPI_PRE / EPI_F32: fp32 outputs (the layer backward's GEMMs): the gate and up
+// pre-activations of a SwiGLU tile, or a plain fp32 product.
+enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_COMBINE = 2, EPI_PRE = 3, EPI_F32 = 4 };
 
 struct LargeParams {
     int M;
@@ -76,6 +78,8 @@ struct LargeParams {
     const int32_t *row_of;
     const float *cw;
     int k;
+    float *outf;  // EPI_PRE / EPI_F32: fp32 output, row stride ldo; EPI_PRE puts up at column + up_off
+    int ldo, up_off;
 };
 
 // Row-tile map: lane owns experts 4*lane .. 4*lane+3.
@@ -192,10 +196,10 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 
 template <int EPI, bool ROUTED>
 __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
-    constexpr bool DUAL = EPI == EPI_SWIGLU;
+    constexpr bool DUAL = EPI == EPI_SWIGLU || EPI == EPI_PRE;
     constexpr bool TRANS = EPI != EPI_COMBINE;  // register epilogue (no LDS staging)
     constexpr int BN = DUAL ? LB / 2 : LB;  // output columns per tile
-    constexpr int kEpiStores = TRANS ? (DUAL ? 32 : 64) : 0;  // buffer stores per lane per register epilogue
+    constexpr int kEpiStores = TRANS ? (EPI == EPI_SWIGLU ? 32 : 64) : 0;  // buffer stores per lane per register epilogue
     __shared__ __attribute__((aligned(1024))) uint16_t smem[NUNIT * UNIT_ELEMS];  // 160 KB
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -443,6 +447,36 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
             // count above relies on it) and the epilogue stays one block whose
             // scheduling barriers bound how many accumulators sit in VGPRs.
             const int c4 = 4 * g;
+            if constexpr (EPI == EPI_PRE || EPI == EPI_F32) {
+                // fp32: one 16-byte store per run of 4 columns (and its up twin);
+                // padding rows get kOobOff, which leaves room for the column offsets
+                const __amdgpu_buffer_rsrc_t rOutF = buf_rsrc(p.outf, (uint32_t)p.M * (uint32_t)p.ldo * 4u);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = cm0 + wm * 128 + 32 * i + (lane & 31);
+                    const uint32_t obase = row < cm_end ? ((uint32_t)row * (uint32_t)p.ldo + (uint32_t)cn0) * 4u : kOobOff;
+#pragma unroll
+                    for (int jj = 0; jj < (DUAL ? 2 : 4); ++jj) {
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int col = (DUAL ? wn * 64 : wn * 128) + jj * 32 + 8 * q + c4;
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                i32x4{__float_as_int(acc_read(acc[i][jj][4 * q])), __float_as_int(acc_read(acc[i][jj][4 * q + 1])),
+                                      __float_as_int(acc_read(acc[i][jj][4 * q + 2])),
+                                      __float_as_int(acc_read(acc[i][jj][4 * q + 3]))},
+                                rOutF, obase + (uint32_t)col * 4u, 0, 0);
+                            if constexpr (DUAL)
+                                __builtin_amdgcn_raw_buffer_store_b128(
+                                    i32x4{__float_as_int(acc_read(acc[i][2 + jj][4 * q])),
+                                          __float_as_int(acc_read(acc[i][2 + jj][4 * q + 1])),
+                                          __float_as_int(acc_read(acc[i][2 + jj][4 * q + 2])),
+                                          __float_as_int(acc_read(acc[i][2 + jj][4 * q + 3]))},
+                                    rOutF, obase + (uint32_t)(p.up_off + col) * 4u, 0, 0);
+                        }
+                    }
+                }
+            } else {
             const __amdgpu_buffer_rsrc_t rOut = buf_rsrc(p.out, (uint32_t)p.M * (uint32_t)p.N * 2u);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -475,6 +509,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
                                                                    obase + (uint32_t)col * 2u, 0, 0);
                     }
                 }
+            }
             }
         } else {
             // Combine epilogue: four 64-row chunks of the fp32 tile through
@@ -574,6 +609,41 @@ bool ffn_bf16_large_ok(const FfnArgs &a) {
                       (unsigned long long)a.I * a.d * 2 < lim;
     return fits && (long long)a.M >= 128LL * groups && a.I % 128 == 0 && a.d % 256 == 0 && a.d % LK == 0 &&
            a.I % LK == 0 && a.d < (1 << 19) && a.I < (1 << 19);
+}
+
+bool bf16_large_gemm_ok(const LargeGemmArgs &g) {
+    const int groups = g.offsets ? kE : 1;
+    const unsigned long long lim = kOobOff - (1ULL << 20);
+    const unsigned long long a_rows = g.a_rows ? (unsigned long long)g.a_src_rows : (unsigned long long)g.M;
+    const int bn = g.dual ? LB / 2 : LB;
+    return (long long)g.M >= 128LL * groups && g.N % bn == 0 && g.K % LK == 0 && g.K < (1 << 19) &&
+           a_rows * g.K * 2 < lim && (unsigned long long)g.N * g.K * 2 < lim &&
+           (unsigned long long)g.M * g.ldo * 4 < lim && (unsigned long long)(g.up_off + LB) * 4 < 65536;
+}
+
+hipError_t launch_bf16_large_gemm(const LargeGemmArgs &g, hipStream_t s) {
+    const int P = (cu_count() / 8) * 8;
+    LargeParams p{};
+    p.M = g.M;
+    p.offsets = g.offsets;
+    p.A = g.A;
+    p.a_rows = g.a_rows;
+    p.a_div = g.a_div;
+    p.K = g.K;
+    p.B0 = g.B0;
+    p.B1 = g.B1;
+    p.N = g.N;
+    p.outf = g.out;
+    p.ldo = g.ldo;
+    p.up_off = g.up_off;
+    if (g.dual) {
+        if (g.offsets) hipLaunchKernelGGL((k_gemm_bf16_large<EPI_PRE, true>), dim3(P), dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((k_gemm_bf16_large<EPI_PRE, false>), dim3(P), dim3(256), 0, s, p);
+    } else {
+        if (g.offsets) hipLaunchKernelGGL((k_gemm_bf16_large<EPI_F32, true>), dim3(P), dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((k_gemm_bf16_large<EPI_F32, false>), dim3(P), dim3(256), 0, s, p);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_ffn_bf16_large(const FfnArgs &a, hipStream_t s) {

@@ -89,6 +89,27 @@ hipError_t launch_ffn_skinny(const FfnArgs &a, hipStream_t s);
 // averages at least 128 rows and the widths tile evenly.
 bool ffn_bf16_large_ok(const FfnArgs &a);
 hipError_t launch_ffn_bf16_large(const FfnArgs &a, hipStream_t s);
+// The same persistent 256x256-tile kernel as a grouped NT GEMM with an fp32
+// output (the layer backward): out[m, n] = sum_k A[m, k] B_g[n, k] with B
+// per group (offsets != nullptr) or one B; dual: B0 / B1 are the gate / up
+// matrices of a SwiGLU tile and their products go to columns n and
+// up_off + n.  a_rows: A row m is row a_rows[m] / a_div (a_src_rows rows).
+struct LargeGemmArgs {
+    int M;
+    const int32_t *offsets;
+    const uint16_t *A;
+    const int32_t *a_rows;
+    int a_div;
+    int a_src_rows;
+    int K;
+    const uint16_t *B0, *B1;
+    int N;
+    float *out;
+    int ldo, up_off;
+    bool dual;
+};
+bool bf16_large_gemm_ok(const LargeGemmArgs &g);
+hipError_t launch_bf16_large_gemm(const LargeGemmArgs &g, hipStream_t s);
 // Large-group e4m3 path (persistent 256x256 tiles, fp32 promotion per 128 of K).
 bool ffn_fp8_large_ok(const FfnArgs &a);
 hipError_t launch_ffn_fp8_large(const FfnArgs &a, hipStream_t s);

@@ -86,7 +86,10 @@ def run_case(T, d, I, kind, seed):
 
 
 @pytest.mark.parametrize("T,d,I,kind,seed", [(300, 512, 256, "routed", 41), (1, 256, 128, "routed", 42),
-                                             (257, 256, 384, "skewed", 43)])
+                                             (257, 256, 384, "skewed", 43),
+                                             # 128+ rows per expert on average: the data-gradient GEMMs
+                                             # run on the persistent 256x256-tile kernel
+                                             (4096, 256, 256, "routed", 44), (4096, 512, 256, "skewed", 45)])
 def test_backward_matches_oracle(T, d, I, kind, seed):
     run_case(T, d, I, kind, seed)
 
