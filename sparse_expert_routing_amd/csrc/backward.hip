@@ -11,14 +11,17 @@
 // gradient of its own).
 //
 // Kernels:
-//   - k_bgemm: a grouped GEMM C (+)= A B on v_mfma_f32_32x32x16_bf16 with
-//     fp32 accumulation, 128x128 tiles, 32 of K per stage, register-staged
-//     double buffer in LDS.  Each operand is either K-contiguous (loaded as
-//     16-byte runs along K) or M/N-contiguous (16-byte runs along M or N,
-//     transposed into the K-contiguous LDS layout by 2-byte stores).  Groups
-//     split M (the expert's rows: data gradients, the pre-activation
-//     recompute; B per expert) or K (the expert's rows as the reduction:
-//     weight gradients; C per expert);
+//   - k_transpose: weights, and the rows each expert's weight gradient
+//     reduces over, transposed through LDS tiles so every GEMM below reads
+//     both operands K-contiguous; an expert's rows start at a 32-aligned
+//     position and are zero-padded to it;
+//   - the data-gradient GEMMs and the pre-activation recompute (NT, grouped
+//     over the experts' rows): the forward's persistent 256x256-tile kernel
+//     with an fp32 epilogue, or k_bgemm for small groups;
+//   - k_bgemm: a grouped GEMM C = A B on v_mfma_f32_32x32x16_bf16 with fp32
+//     accumulation, 128x128 tiles, 32 of K per stage, register-staged double
+//     buffer in LDS; groups split M (B per expert) or K (an expert's padded
+//     rows are the reduction: the weight gradients, C per expert);
 //   - k_bwd_combine: per token, dg_j = dy . y_perm_j, the routed output
 //     gradient g_j dy (bf16) and the shared one dy (bf16);
 //   - k_bwd_swiglu: h, and the SwiGLU input gradients from the recomputed
@@ -26,7 +29,8 @@
 //   - k_bwd_router: per token, the chosen experts' affinities recomputed in
 //     fp32, ds_j = (dg_j - sum_i g_i dg_i) / sum_i s_i, dl_j = ds_j s_j (1-s_j),
 //     and the router's share of dx;
-//   - k_bwd_dwr: router weight gradient, expert rows in ascending order;
+//   - k_bwd_dwr / k_bwd_dwr_sum: router weight gradient, each expert's rows
+//     summed in 16 ordered shares, the shares added in order;
 //   - k_bwd_dx: dx += shared input gradient + sum_j routed input gradients.
 #include "device.h"
 #include "kernels.h"
@@ -44,14 +48,12 @@ enum { GROUP_NONE = 0, GROUP_M = 1, GROUP_K = 2 };
 struct BGemm {
     int M, N, K;              // K: the reduction length (GROUP_K: total rows)
     const int32_t *offsets;   // [G+1] (GROUP_M: row ranges; GROUP_K: reduction ranges)
-    const uint16_t *A;        // A(m, k) = A[m*lda + k] (K-contiguous) or A[k*lda + m]
+    const uint16_t *A;        // A(m, k) = A[m*lda + k]
     int64_t lda;
-    const int32_t *a_rows;    // K-contiguous A with GROUP_M: row m reads row a_rows[m] / a_div
+    const int32_t *a_rows;    // optional: row m reads row a_rows[m] / a_div
     int a_div;
-    const uint16_t *B;        // B(k, n) = B[n*ldb + k] (K-contiguous) or B[k*ldb + n]
+    const uint16_t *B;        // B(k, n) = B[n*ldb + k]
     int64_t ldb, bstride;     // bstride: per-group B offset (GROUP_M)
-    const int32_t *b_rows;    // N-contiguous B with GROUP_K: row k reads row b_rows[k] / b_div
-    int b_div;
     float *C;                 // C[m*ldc + n] (+ cstride per group for GROUP_K)
     int64_t ldc, cstride;
 };
@@ -95,34 +97,23 @@ __device__ __forceinline__ bool bg_find_tile(const int32_t *__restrict__ offsets
     return true;
 }
 
-// One operand tile (128 rows of M or N x 32 of K) global -> registers:
-// two 16-byte pieces per thread.  KC: K-contiguous source.  Rows past
-// `rows_end` and K past `k_end` read as zeros.
-template <bool KC>
+// One operand tile (128 rows of M or N x 32 of K, K-contiguous) global ->
+// registers -> LDS: two 16-byte pieces per thread.  Rows past `rows_end`
+// read as zeros; row r reads source row rows[r] / rdiv when rows is given.
 struct TileLoad {
     i32x4 v[2];
     __device__ __forceinline__ void load(const uint16_t *__restrict__ P, int64_t ld, const int32_t *__restrict__ rows,
-                                         int rdiv, int r0, int rows_end, int k0, int k_end) {
+                                         int rdiv, int r0, int rows_end, int k0) {
         const int tid = threadIdx.x;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int c = tid + 256 * h;
-            if (KC) {
-                const int row = c >> 2, kc = (c & 3) * 8;
-                const int gr = r0 + row;
-                v[h] = i32x4{0, 0, 0, 0};
-                if (gr < rows_end) {
-                    const int64_t src = rows ? rows[gr] / rdiv : gr;
-                    v[h] = *reinterpret_cast<const i32x4 *>(P + src * ld + k0 + kc);
-                }
-            } else {
-                const int k = c >> 4, mc = (c & 15) * 8;
-                const int gk = k0 + k;
-                v[h] = i32x4{0, 0, 0, 0};
-                if (gk < k_end) {
-                    const int64_t src = rows ? rows[gk] / rdiv : gk;
-                    v[h] = *reinterpret_cast<const i32x4 *>(P + src * ld + r0 + mc);
-                }
+            const int row = c >> 2, kc = (c & 3) * 8;
+            const int gr = r0 + row;
+            v[h] = i32x4{0, 0, 0, 0};
+            if (gr < rows_end) {
+                const int64_t src = rows ? rows[gr] / rdiv : gr;
+                v[h] = *reinterpret_cast<const i32x4 *>(P + src * ld + k0 + kc);
             }
         }
     }
@@ -131,23 +122,13 @@ struct TileLoad {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int c = tid + 256 * h;
-            if (KC) {
-                const int row = c >> 2, kc = (c & 3) * 8;
-                *reinterpret_cast<i32x4 *>(S + row * LDK + kc) = v[h];
-            } else {
-                const int k = c >> 4, mc = (c & 15) * 8;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t w = (uint32_t)v[h][i];
-                    S[(mc + 2 * i) * LDK + k] = (uint16_t)(w & 0xffffu);
-                    S[(mc + 2 * i + 1) * LDK + k] = (uint16_t)(w >> 16);
-                }
-            }
+            const int row = c >> 2, kc = (c & 3) * 8;
+            *reinterpret_cast<i32x4 *>(S + row * LDK + kc) = v[h];
         }
     }
 };
 
-template <bool A_KC, bool B_KC, int GROUP, bool ACC>
+template <int GROUP, bool ACC>
 __global__ __launch_bounds__(256) void k_bgemm(BGemm p) {
     __shared__ __attribute__((aligned(16))) uint16_t sA[2][GM * LDK];
     __shared__ __attribute__((aligned(16))) uint16_t sB[2][GN * LDK];
@@ -176,14 +157,13 @@ __global__ __launch_bounds__(256) void k_bgemm(BGemm p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-    TileLoad<A_KC> la;
-    TileLoad<B_KC> lb;
+    TileLoad la, lb;
     // A rows: M (row indirection only for a K-contiguous A); B: N, with the
     // row indirection on K for an N-contiguous B
     const int nst = (k_end - k_begin + GK - 1) / GK;
     if (nst > 0) {
-        la.load(p.A, p.lda, A_KC ? p.a_rows : nullptr, p.a_div, m0, m_end, k_begin, k_end);
-        lb.load(B, p.ldb, B_KC ? nullptr : p.b_rows, p.b_div, n0, p.N, k_begin, k_end);
+        la.load(p.A, p.lda, p.a_rows, p.a_div, m0, m_end, k_begin);
+        lb.load(B, p.ldb, nullptr, 1, n0, p.N, k_begin);
         la.store(sA[0]);
         lb.store(sB[0]);
     }
@@ -193,8 +173,8 @@ __global__ __launch_bounds__(256) void k_bgemm(BGemm p) {
         const bool more = st + 1 < nst;
         if (more) {
             const int k0 = k_begin + (st + 1) * GK;
-            la.load(p.A, p.lda, A_KC ? p.a_rows : nullptr, p.a_div, m0, m_end, k0, k_end);
-            lb.load(B, p.ldb, B_KC ? nullptr : p.b_rows, p.b_div, n0, p.N, k0, k_end);
+            la.load(p.A, p.lda, p.a_rows, p.a_div, m0, m_end, k0);
+            lb.load(B, p.ldb, nullptr, 1, n0, p.N, k0);
         }
 #pragma unroll
         for (int ks = 0; ks < GK / 16; ++ks) {
@@ -240,25 +220,70 @@ __global__ __launch_bounds__(256) void k_bgemm(BGemm p) {
 
 // ------------------------------------------------------------- transposes
 
-// out[g][c*ldo + coff + map(r)] = in[g][src(r)*ldi + c] for r < R, c < C, bf16,
-// through 64x64 LDS tiles (both sides coalesced).  src(r) = rows[r] / rdiv
-// (a row gather) or r; map(r) = rmap[r] (a padded row position) or r.
+// out[g][c*ldo + coff + pos] = in[g][src(r)*ldi + c], bf16, through 64x64
+// LDS tiles (both sides coalesced; 8-byte stores).  src(r) = rows[r] / rdiv
+// (a row gather) or r.  Grouped (off != nullptr): the tiles run over each
+// group's rows [off[e], off[e+1]) and row r of group e lands at
+// pos = poff[e] + r - off[e]; positions up to poff[e+1] past the group's rows
+// are written as zeros (the padding).  Plain: pos = r for r < R, and zeros
+// for R <= pos < dend.
 __global__ __launch_bounds__(256) void k_transpose(int R, int C, const uint16_t *__restrict__ in, int64_t ldi,
                                                    int64_t gin, const int32_t *__restrict__ rows, int rdiv,
-                                                   const int32_t *__restrict__ rmap, uint16_t *__restrict__ out,
-                                                   int64_t ldo, int64_t gout, int coff) {
+                                                   const int32_t *__restrict__ off, const int32_t *__restrict__ poff,
+                                                   int dend_plain, uint16_t *__restrict__ out, int64_t ldo,
+                                                   int64_t gout, int coff) {
     __shared__ uint16_t tile[64][66];
-    const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64, g = blockIdx.z;
+    const int c0 = blockIdx.y * 64, g = blockIdx.z;
     const int tid = threadIdx.x;
+    int r0, rend, d0, dend;
+    if (off) {
+        // slot -> (group e, tile t) over sum_e ceil(c_e / 64) tiles (one wave's scan)
+        const int lane = tid & 63;
+        int o[5], nt[4], lt = 0;
+#pragma unroll
+        for (int i = 0; i < 5; ++i) o[i] = off[lane * 4 + i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            nt[i] = (o[i + 1] - o[i] + 63) / 64;
+            lt += nt[i];
+        }
+        const int incl = wave_incl_scan(lt), excl = incl - lt;
+        const int slot = blockIdx.x;
+        if (slot >= __shfl(incl, 63, 64)) return;
+        const bool own = slot >= excl && slot < incl;
+        const int owner = __ffsll((unsigned long long)__ballot(own)) - 1;
+        int my_e = 0, my_t = 0;
+        if (own) {
+            int q = slot - excl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (q >= 0 && q < nt[i]) {
+                    my_e = lane * 4 + i;
+                    my_t = q;
+                }
+                q -= nt[i];
+            }
+        }
+        const int e = __shfl(my_e, owner, 64), t = __shfl(my_t, owner, 64);
+        r0 = off[e] + 64 * t;
+        rend = off[e + 1];
+        d0 = poff[e] + 64 * t;
+        dend = min(d0 + 64, poff[e + 1]);
+    } else {
+        r0 = blockIdx.x * 64;
+        rend = R;
+        d0 = r0;
+        dend = min(d0 + 64, dend_plain);
+        if (d0 >= dend) return;
+    }
     in += (int64_t)g * gin;
     out += (int64_t)g * gout;
-    // load: 64 rows x 64 columns, 4 columns (8 bytes) per thread per pass
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
         const int rr = pass * 16 + (tid >> 4), cc = (tid & 15) * 4;
         const int r = r0 + rr;
         uint2 v = uint2{0u, 0u};
-        if (r < R) {
+        if (r < rend) {
             const int64_t src = rows ? rows[r] / rdiv : r;
             v = *reinterpret_cast<const uint2 *>(in + src * ldi + c0 + cc);
         }
@@ -268,27 +293,32 @@ __global__ __launch_bounds__(256) void k_transpose(int R, int C, const uint16_t 
         tile[rr][cc + 3] = (uint16_t)(v.y >> 16);
     }
     __syncthreads();
-    // store: 64 output rows (columns c) x 64 positions, one element per thread per pass
-#pragma unroll 4
-    for (int pass = 0; pass < 16; ++pass) {
-        const int cc = pass * 4 + (tid >> 6), rr = tid & 63;
-        const int r = r0 + rr;
-        if (r < R) {
-            const int64_t pos = rmap ? rmap[r] : r;
-            out[(int64_t)(c0 + cc) * ldo + coff + pos] = tile[rr][cc];
+    // 64 output rows (columns c) x 16 runs of 4 positions, one 8-byte store per run
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+        const int cc = pass * 16 + (tid >> 4), rq = (tid & 15) * 4;
+        const int pos = d0 + rq;
+        uint16_t *o = out + (int64_t)(c0 + cc) * ldo + coff + pos;
+        if (pos + 3 < dend) {
+            uint2 v;
+            v.x = (uint32_t)tile[rq][cc] | ((uint32_t)tile[rq + 1][cc] << 16);
+            v.y = (uint32_t)tile[rq + 2][cc] | ((uint32_t)tile[rq + 3][cc] << 16);
+            *reinterpret_cast<uint2 *>(o) = v;
+        } else {
+            for (int i = 0; i < 4 && pos + i < dend; ++i) o[i] = tile[rq + i][cc];
         }
     }
 }
 
 // Padded row positions: poff = exclusive scan of the group sizes rounded up
-// to 32 (one wave; 256 groups, 4 per lane), rmap[r] = poff[e] + r - off[e].
+// to 64 (one wave; 256 groups, 4 per lane).
 __global__ __launch_bounds__(64) void k_pad_offsets(const int32_t *__restrict__ off, int32_t *__restrict__ poff) {
     const int lane = threadIdx.x;
     int c[4], s = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = lane * 4 + i;
-        c[i] = (off[e + 1] - off[e] + 31) / 32 * 32;
+        c[i] = (off[e + 1] - off[e] + 63) / 64 * 64;
         s += c[i];
     }
     const int incl = wave_incl_scan(s);
@@ -301,34 +331,16 @@ __global__ __launch_bounds__(64) void k_pad_offsets(const int32_t *__restrict__ 
     if (lane == 63) poff[kE] = incl;
 }
 
-__global__ __launch_bounds__(256) void k_row_map(int A, const int32_t *__restrict__ off,
-                                                 const int32_t *__restrict__ poff, int32_t *__restrict__ rmap) {
-    const int r = blockIdx.x * 256 + threadIdx.x;
-    if (r >= A) return;
-    int lo = 0, hi = kE;  // the group e with off[e] <= r < off[e+1]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (off[mid] <= r) lo = mid; else hi = mid;
-    }
-    rmap[r] = poff[lo] + r - off[lo];
-}
-
-// Zero the padding positions [poff[e] + c_e, poff[e+1]) of `nrows` rows of a
-// transposed buffer (row stride ld).
-// (off == nullptr: one group whose padding is [start0, start0 + n0).)
-__global__ __launch_bounds__(256) void k_pad_zero(int nrows, const int32_t *__restrict__ off,
-                                                  const int32_t *__restrict__ poff, uint16_t *__restrict__ buf,
-                                                  int64_t ld, int start0, int n0) {
-    const int e = blockIdx.y;
-    const int start = off ? poff[e] + off[e + 1] - off[e] : start0;
-    const int n = off ? poff[e + 1] - start : n0;  // < 32
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < nrows * n; i += gridDim.x * 256) {
-        const int row = i / n, j = i - row * n;
-        buf[(int64_t)row * ld + start + j] = 0;
-    }
-}
-
 // ------------------------------------------------------------ elementwise
+
+// out[e] = 0 (per elements each) for the groups with no rows.
+__global__ __launch_bounds__(256) void k_zero_empty(int64_t per, const int32_t *__restrict__ off,
+                                                    float *__restrict__ out) {
+    const int e = blockIdx.y;
+    if (off[e + 1] > off[e]) return;
+    float *o = out + (int64_t)e * per;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < per; i += (int64_t)gridDim.x * 256) o[i] = 0.f;
+}
 
 // Per token t (one wave): dg_j = sum_n dy[t,n] y_perm[r_j,n] (r_j =
 // row_of[t*k+j]); dyp[r_j] = bf16(g_j dy[t]); dys[t] = bf16(dy[t]).
@@ -440,18 +452,34 @@ __global__ __launch_bounds__(256) void k_bwd_router(int T, int d, const uint16_t
     }
 }
 
-// dwr[e, n] = sum over e's rows r (ascending) of dl[row_src[r]] x[row_src[r] / 8, n].
+// Router weight gradient dwr[e, n] = sum over e's rows r (ascending) of
+// dl[row_src[r]] x[row_src[r] / 8, n]: each of kDwrChunks workgroups per
+// (expert, 256 columns) sums an equal share of the rows into part[chunk],
+// then k_bwd_dwr_sum adds the shares in chunk order (deterministic).
+constexpr int kDwrChunks = 16;
 __global__ __launch_bounds__(256) void k_bwd_dwr(int d, const int32_t *__restrict__ offsets,
                                                  const int32_t *__restrict__ row_src, const float *__restrict__ dl,
-                                                 const uint16_t *__restrict__ x, float *__restrict__ dwr) {
-    const int e = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
+                                                 const uint16_t *__restrict__ x, float *__restrict__ part) {
+    const int e = blockIdx.y, ch = blockIdx.z, n = blockIdx.x * 256 + threadIdx.x;
     if (n >= d) return;
+    const int b = offsets[e], c = offsets[e + 1] - b;
+    const int r0 = b + (int)((int64_t)c * ch / kDwrChunks), r1 = b + (int)((int64_t)c * (ch + 1) / kDwrChunks);
     float acc = 0.f;
-    for (int r = offsets[e]; r < offsets[e + 1]; ++r) {
+    for (int r = r0; r < r1; ++r) {
         const int f = row_src[r];
         acc += dl[f] * bf16_to_f32(x[(int64_t)(f / 8) * d + n]);
     }
-    dwr[(int64_t)e * d + n] = acc;
+    part[((int64_t)ch * kE + e) * d + n] = acc;
+}
+
+__global__ __launch_bounds__(256) void k_bwd_dwr_sum(int64_t n, const float *__restrict__ part,
+                                                     float *__restrict__ dwr) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float acc = part[i];
+#pragma unroll
+    for (int ch = 1; ch < kDwrChunks; ++ch) acc += part[ch * n + i];
+    dwr[i] = acc;
 }
 
 // dx[t] += dxs[t] + sum_j dxp[row_of[t*8 + j]] (j ascending), 4 columns per thread.
@@ -474,13 +502,13 @@ __global__ __launch_bounds__(256) void k_bwd_dx(int T, int d, const float *__res
     *reinterpret_cast<f32x4 *>(dx + t * d + c) = v;
 }
 
-template <bool A_KC, bool B_KC, int GROUP, bool ACC>
+template <int GROUP, bool ACC>
 hipError_t bgemm(const BGemm &p, int G, hipStream_t s) {
     dim3 grid;
     if (GROUP == GROUP_M) grid = dim3((p.M + GM - 1) / GM + G, p.N / GN);
     else if (GROUP == GROUP_K) grid = dim3(p.M / GM, p.N / GN, G);
     else grid = dim3((p.M + GM - 1) / GM, p.N / GN);
-    hipLaunchKernelGGL((k_bgemm<A_KC, B_KC, GROUP, ACC>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_bgemm<GROUP, ACC>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -497,7 +525,8 @@ struct BwdWs {
     uint16_t *dab;         // [R, 2I] SwiGLU input gradients (da | db)
     float *dxi;            // [R, d] input gradients
     float *dl, *dg;        // [T*k]
-    int32_t *poff, *rmap;  // [E+1], [A]
+    int32_t *poff;         // [E+1]
+    float *dwr_part;       // [16, E, d] router-gradient partial sums
     uint16_t *wdT;         // [E, I, d] down weights transposed
     uint16_t *wguT;        // [E, d, 2I] gate | up weights transposed
     uint16_t *sdT, *sguT;  // the shared expert's: [I, d], [d, 2I]
@@ -509,7 +538,7 @@ struct BwdWs {
 BwdWs carve(char *base, int T, int d, int I, int k) {
     BwdWs w{};
     size_t o = 0;
-    const size_t A = (size_t)T * k, R = A + T, Rp = A + 32 * (size_t)kE, Tp = ((size_t)T + 31) / 32 * 32;
+    const size_t A = (size_t)T * k, R = A + T, Rp = A + 64 * (size_t)kE, Tp = ((size_t)T + 31) / 32 * 32;
     auto take = [&](size_t n) -> char * {
         char *p = base ? base + o : nullptr;
         o += (n + 255) / 256 * 256;
@@ -524,7 +553,7 @@ BwdWs carve(char *base, int T, int d, int I, int k) {
     w.dl = reinterpret_cast<float *>(take(A * 4));
     w.dg = reinterpret_cast<float *>(take(A * 4));
     w.poff = reinterpret_cast<int32_t *>(take((kE + 1) * 4));
-    w.rmap = reinterpret_cast<int32_t *>(take(A * 4));
+    w.dwr_part = reinterpret_cast<float *>(take((size_t)16 * kE * d * 4));
     w.wdT = reinterpret_cast<uint16_t *>(take((size_t)kE * I * d * 2));
     w.wguT = reinterpret_cast<uint16_t *>(take((size_t)kE * d * 2 * I * 2));
     w.sdT = reinterpret_cast<uint16_t *>(take((size_t)I * d * 2));
@@ -541,13 +570,15 @@ BwdWs carve(char *base, int T, int d, int I, int k) {
     return w;
 }
 
-// out[g] = in[g] transposed (R x C -> C x R), see k_transpose
+// out[g] = in[g] transposed (R x C -> C x R), see k_transpose.  Plain: dend
+// positions (zeros past R).  Grouped (off, poff): R = the total rows.
 hipError_t transpose(int R, int C, int G, const uint16_t *in, int64_t ldi, int64_t gin, const int32_t *rows,
-                     int rdiv, const int32_t *rmap, uint16_t *out, int64_t ldo, int64_t gout, int coff,
-                     hipStream_t s) {
-    if (R <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_transpose, dim3((R + 63) / 64, C / 64, G), dim3(256), 0, s, R, C, in, ldi, gin, rows, rdiv,
-                       rmap, out, ldo, gout, coff);
+                     int rdiv, const int32_t *off, const int32_t *poff, int dend, uint16_t *out, int64_t ldo,
+                     int64_t gout, int coff, hipStream_t s) {
+    const int tiles = off ? R / 64 + kE + 1 : (dend + 63) / 64;
+    if (tiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_transpose, dim3(tiles, C / 64, G), dim3(256), 0, s, R, C, in, ldi, gin, rows, rdiv, off,
+                       poff, dend, out, ldo, gout, coff);
     return hipGetLastError();
 }
 
@@ -560,7 +591,7 @@ bool backward_ok(int d, int I) { return d % 128 == 0 && I % 128 == 0; }
 hipError_t launch_backward(const BackwardArgs &a, void *ws, hipStream_t s) {
     const int T = a.T, d = a.d, I = a.I, k = a.k, E = kE;
     const int A = T * k;
-    const int64_t Rp = (int64_t)A + 32 * kE, Tp = ((int64_t)T + 31) / 32 * 32;
+    const int64_t Rp = (int64_t)A + 64 * kE, Tp = ((int64_t)T + 31) / 32 * 32;
     const BwdWs w = carve(static_cast<char *>(ws), T, d, I, k);
     float *dg = a.dg ? a.dg : w.dg;
     const uint16_t *x = static_cast<const uint16_t *>(a.x);
@@ -579,14 +610,14 @@ hipError_t launch_backward(const BackwardArgs &a, void *ws, hipStream_t s) {
     // 0. padded row positions of the expert groups; transposed weights
     hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(64), 0, s, a.offsets, w.poff);
     CHK(hipGetLastError());
-    hipLaunchKernelGGL(k_row_map, dim3((A + 255) / 256), dim3(256), 0, s, A, a.offsets, w.poff, w.rmap);
-    CHK(hipGetLastError());
-    CHK(transpose(d, I, E, ed, I, (int64_t)d * I, nullptr, 1, nullptr, w.wdT, d, (int64_t)I * d, 0, s));
-    CHK(transpose(I, d, E, eg, d, (int64_t)I * d, nullptr, 1, nullptr, w.wguT, 2 * I, (int64_t)d * 2 * I, 0, s));
-    CHK(transpose(I, d, E, eu, d, (int64_t)I * d, nullptr, 1, nullptr, w.wguT, 2 * I, (int64_t)d * 2 * I, I, s));
-    CHK(transpose(d, I, 1, sd, I, 0, nullptr, 1, nullptr, w.sdT, d, 0, 0, s));
-    CHK(transpose(I, d, 1, sg, d, 0, nullptr, 1, nullptr, w.sguT, 2 * I, 0, 0, s));
-    CHK(transpose(I, d, 1, su, d, 0, nullptr, 1, nullptr, w.sguT, 2 * I, 0, I, s));
+    CHK(transpose(d, I, E, ed, I, (int64_t)d * I, nullptr, 1, nullptr, nullptr, d, w.wdT, d, (int64_t)I * d, 0, s));
+    CHK(transpose(I, d, E, eg, d, (int64_t)I * d, nullptr, 1, nullptr, nullptr, I, w.wguT, 2 * I, (int64_t)d * 2 * I, 0,
+                  s));
+    CHK(transpose(I, d, E, eu, d, (int64_t)I * d, nullptr, 1, nullptr, nullptr, I, w.wguT, 2 * I, (int64_t)d * 2 * I, I,
+                  s));
+    CHK(transpose(d, I, 1, sd, I, 0, nullptr, 1, nullptr, nullptr, d, w.sdT, d, 0, 0, s));
+    CHK(transpose(I, d, 1, sg, d, 0, nullptr, 1, nullptr, nullptr, I, w.sguT, 2 * I, 0, 0, s));
+    CHK(transpose(I, d, 1, su, d, 0, nullptr, 1, nullptr, nullptr, I, w.sguT, 2 * I, 0, I, s));
 
     // 1. combine backward
     hipLaunchKernelGGL(k_bwd_combine, dim3((T + 3) / 4), dim3(256), 0, s, T, d, a.dy,
@@ -602,8 +633,8 @@ hipError_t launch_backward(const BackwardArgs &a, void *ws, hipStream_t s) {
             p.M = g.M; p.N = g.N; p.K = g.K; p.offsets = offsets; p.A = g.A; p.lda = lda;
             p.a_rows = g.a_rows; p.a_div = g.a_div; p.B = half ? g.B1 : g.B0; p.ldb = g.K;
             p.bstride = (int64_t)g.N * g.K; p.C = g.out + (half ? g.up_off : 0); p.ldc = g.ldo;
-            const hipError_t r = offsets ? bgemm<true, true, GROUP_M, false>(p, E, s)
-                                         : bgemm<true, true, GROUP_NONE, false>(p, 1, s);
+            const hipError_t r = offsets ? bgemm<GROUP_M, false>(p, E, s)
+                                         : bgemm<GROUP_NONE, false>(p, 1, s);
             if (r != hipSuccess) return r;
         }
         return hipSuccess;
@@ -626,64 +657,62 @@ hipError_t launch_backward(const BackwardArgs &a, void *ws, hipStream_t s) {
            2 * I));
     CHK(nt(LargeGemmArgs{T, nullptr, dabs, nullptr, 1, T, 2 * I, w.sguT, nullptr, d, dxs, d, 0, false}, nullptr, 2 * I));
     // 6. weight gradients.  The rows each expert reduces over are transposed
-    //    into [*, Rp] buffers where expert e's rows start at poff[e] (32-aligned,
+    //    into [*, Rp] buffers where expert e's rows start at poff[e] (64-aligned,
     //    zero-padded), so both operands are K-contiguous and every K range is
-    //    whole 32-wide stages.
+    //    whole 64-wide stages.
     {
-        CHK(transpose(A, d, 1, x, d, 0, a.row_src, k, w.rmap, w.xT, Rp, 0, 0, s));
-        CHK(transpose(A, d, 1, w.dyo, d, 0, nullptr, 1, w.rmap, w.dyoT, Rp, 0, 0, s));
-        CHK(transpose(A, I, 1, w.h16, I, 0, nullptr, 1, w.rmap, w.hT, Rp, 0, 0, s));
-        CHK(transpose(A, 2 * I, 1, w.dab, 2 * I, 0, nullptr, 1, w.rmap, w.dabT, Rp, 0, 0, s));
-        struct {
-            uint16_t *buf;
-            int rows;
-        } pads[4] = {{w.xT, d}, {w.dyoT, d}, {w.hT, I}, {w.dabT, 2 * I}};
-        for (auto &pd : pads) {
-            hipLaunchKernelGGL(k_pad_zero, dim3(16, E), dim3(256), 0, s, pd.rows, a.offsets, w.poff, pd.buf, Rp, 0, 0);
-            CHK(hipGetLastError());
-        }
-        BGemm p{};
-        p.M = I; p.N = d; p.K = (int)Rp; p.offsets = w.poff; p.lda = Rp; p.a_div = 1;
-        p.B = w.xT; p.ldb = Rp; p.b_div = 1; p.ldc = d; p.cstride = (int64_t)I * d;
-        p.A = w.dabT; p.C = a.dw_gate;
-        CHK((bgemm<true, true, GROUP_K, false>(p, E, s)));
-        p.A = w.dabT + (int64_t)I * Rp; p.C = a.dw_up;
-        CHK((bgemm<true, true, GROUP_K, false>(p, E, s)));
-        BGemm q{};
-        q.M = d; q.N = I; q.K = (int)Rp; q.offsets = w.poff; q.A = w.dyoT; q.lda = Rp; q.a_div = 1;
-        q.B = w.hT; q.ldb = Rp; q.b_div = 1; q.C = a.dw_down; q.ldc = I; q.cstride = (int64_t)d * I;
-        CHK((bgemm<true, true, GROUP_K, false>(q, E, s)));
+        CHK(transpose(A, d, 1, x, d, 0, a.row_src, k, a.offsets, w.poff, 0, w.xT, Rp, 0, 0, s));
+        CHK(transpose(A, d, 1, w.dyo, d, 0, nullptr, 1, a.offsets, w.poff, 0, w.dyoT, Rp, 0, 0, s));
+        CHK(transpose(A, I, 1, w.h16, I, 0, nullptr, 1, a.offsets, w.poff, 0, w.hT, Rp, 0, 0, s));
+        CHK(transpose(A, 2 * I, 1, w.dab, 2 * I, 0, nullptr, 1, a.offsets, w.poff, 0, w.dabT, Rp, 0, 0, s));
+        // out_e = A[:, K_e] B[:, K_e]^T: the large-tile kernel in its K-grouped
+        // form (experts with no rows are zeroed separately), else k_bgemm
+        auto kg = [&](int M, int N, const uint16_t *Aop, const uint16_t *Bop, float *out) -> hipError_t {
+            LargeGemmArgs g{};
+            g.M = M; g.A = Aop; g.a_div = 1; g.K = (int)Rp; g.B0 = Bop; g.N = N; g.out = out; g.ldo = N;
+            g.kseg = w.poff; g.ldk = (int)Rp; g.cstride = (int64_t)M * N;
+            if (bf16_large_gemm_ok(g)) {
+                const hipError_t r = launch_bf16_large_gemm(g, s);
+                if (r != hipSuccess) return r;
+                hipLaunchKernelGGL(k_zero_empty, dim3(64, E), dim3(256), 0, s, (int64_t)M * N, a.offsets, out);
+                return hipGetLastError();
+            }
+            BGemm p{};
+            p.M = M; p.N = N; p.K = (int)Rp; p.offsets = w.poff; p.A = Aop; p.lda = Rp; p.a_div = 1;
+            p.B = Bop; p.ldb = Rp; p.C = out; p.ldc = N; p.cstride = (int64_t)M * N;
+            return bgemm<GROUP_K, false>(p, E, s);
+        };
+        CHK(kg(I, d, w.dabT, w.xT, a.dw_gate));
+        CHK(kg(I, d, w.dabT + (int64_t)I * Rp, w.xT, a.dw_up));
+        CHK(kg(d, I, w.dyoT, w.hT, a.dw_down));
         // shared expert: one group over all T rows (padded to Tp with zeros)
-        CHK(transpose(T, d, 1, x, d, 0, nullptr, 1, nullptr, w.xsT, Tp, 0, 0, s));
-        CHK(transpose(T, d, 1, dys, d, 0, nullptr, 1, nullptr, w.dysT, Tp, 0, 0, s));
-        CHK(transpose(T, I, 1, hs, I, 0, nullptr, 1, nullptr, w.hsT, Tp, 0, 0, s));
-        CHK(transpose(T, 2 * I, 1, dabs, 2 * I, 0, nullptr, 1, nullptr, w.dabsT, Tp, 0, 0, s));
-        struct {
-            uint16_t *buf;
-            int rows;
-        } spads[4] = {{w.xsT, d}, {w.dysT, d}, {w.hsT, I}, {w.dabsT, 2 * I}};
-        for (auto &pd : spads) {
-            hipLaunchKernelGGL(k_pad_zero, dim3(16, 1), dim3(256), 0, s, pd.rows, nullptr, nullptr, pd.buf, Tp, T,
-                               (int)(Tp - T));
-            CHK(hipGetLastError());
-        }
+        CHK(transpose(T, d, 1, x, d, 0, nullptr, 1, nullptr, nullptr, (int)Tp, w.xsT, Tp, 0, 0, s));
+        CHK(transpose(T, d, 1, dys, d, 0, nullptr, 1, nullptr, nullptr, (int)Tp, w.dysT, Tp, 0, 0, s));
+        CHK(transpose(T, I, 1, hs, I, 0, nullptr, 1, nullptr, nullptr, (int)Tp, w.hsT, Tp, 0, 0, s));
+        CHK(transpose(T, 2 * I, 1, dabs, 2 * I, 0, nullptr, 1, nullptr, nullptr, (int)Tp, w.dabsT, Tp, 0, 0, s));
         BGemm r{};
-        r.M = I; r.N = d; r.K = (int)Tp; r.lda = Tp; r.a_div = 1; r.B = w.xsT; r.ldb = Tp; r.b_div = 1; r.ldc = d;
+        r.M = I; r.N = d; r.K = (int)Tp; r.lda = Tp; r.a_div = 1; r.B = w.xsT; r.ldb = Tp; r.ldc = d;
         r.A = w.dabsT; r.C = a.ds_gate;
-        CHK((bgemm<true, true, GROUP_NONE, false>(r, 1, s)));
+        CHK((bgemm<GROUP_NONE, false>(r, 1, s)));
         r.A = w.dabsT + (int64_t)I * Tp; r.C = a.ds_up;
-        CHK((bgemm<true, true, GROUP_NONE, false>(r, 1, s)));
+        CHK((bgemm<GROUP_NONE, false>(r, 1, s)));
         BGemm u{};
-        u.M = d; u.N = I; u.K = (int)Tp; u.A = w.dysT; u.lda = Tp; u.a_div = 1; u.B = w.hsT; u.ldb = Tp; u.b_div = 1;
+        u.M = d; u.N = I; u.K = (int)Tp; u.A = w.dysT; u.lda = Tp; u.a_div = 1; u.B = w.hsT; u.ldb = Tp;
         u.C = a.ds_down; u.ldc = I;
-        CHK((bgemm<true, true, GROUP_NONE, false>(u, 1, s)));
+        CHK((bgemm<GROUP_NONE, false>(u, 1, s)));
     }
     // 7. router: dl and its share of dx (written), then the router gradient
     hipLaunchKernelGGL(k_bwd_router, dim3(T), dim3(256), 0, s, T, d, x, a.w_router, a.idx, dg, w.dl, a.dx);
     CHK(hipGetLastError());
-    hipLaunchKernelGGL(k_bwd_dwr, dim3((d + 255) / 256, E), dim3(256), 0, s, d, a.offsets, a.row_src, w.dl, x,
-                       a.dw_router);
+    hipLaunchKernelGGL(k_bwd_dwr, dim3((d + 255) / 256, E, kDwrChunks), dim3(256), 0, s, d, a.offsets, a.row_src,
+                       w.dl, x, w.dwr_part);
     CHK(hipGetLastError());
+    {
+        const int64_t n = (int64_t)E * d;
+        hipLaunchKernelGGL(k_bwd_dwr_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n, w.dwr_part,
+                           a.dw_router);
+        CHK(hipGetLastError());
+    }
     // 8. dx += shared + routed input gradients
     {
         const int64_t n = (int64_t)T * (d / 4);

@@ -80,6 +80,12 @@ struct LargeParams {
     int k;
     float *outf;  // EPI_PRE / EPI_F32: fp32 output, row stride ldo; EPI_PRE puts up at column + up_off
     int ldo, up_off;
+    // K-grouped form (weight gradients): group e reduces over K in
+    // [kseg[e], kseg[e+1]) (multiples of 64) of A [M, ldk] and B [N, ldk],
+    // into outf + e * cstride; groups with an empty range are skipped
+    const int32_t *kseg;
+    int ldk;
+    int64_t cstride;
 };
 
 // Row-tile map: lane owns experts 4*lane .. 4*lane+3.
@@ -125,6 +131,44 @@ __device__ __forceinline__ void tilemap_find(const TileMap &tm, int mt, int &e, 
     e = __shfl(my_e, owner, 64);
     m0 = __shfl(my_m0, owner, 64);
     m_end = __shfl(my_end, owner, 64);
+}
+
+// K-grouped tile map: lane owns groups 4*lane .. 4*lane+3; a group with a
+// non-empty K range has `per` tiles.
+__device__ __forceinline__ void kgmap_init(TileMap &tm, const int32_t *__restrict__ kseg, int per) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) tm.off[i] = kseg[lane * 4 + i];
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        tm.nt[i] = tm.off[i + 1] > tm.off[i] ? per : 0;
+        s += tm.nt[i];
+    }
+    const int incl = wave_incl_scan(s);
+    tm.excl = incl - s;
+    tm.total = __shfl(incl, 63, 64);
+}
+
+__device__ __forceinline__ void kgmap_find(const TileMap &tm, int slot, int &e, int &local) {
+    const int lane = threadIdx.x & 63;
+    const int mine = tm.nt[0] + tm.nt[1] + tm.nt[2] + tm.nt[3];
+    const bool own = slot >= tm.excl && slot < tm.excl + mine;
+    const int owner = __ffsll((unsigned long long)__ballot(own)) - 1;
+    int my_e = 0, my_l = 0;
+    if (own) {
+        int s = slot - tm.excl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (s >= 0 && s < tm.nt[i]) {
+                my_e = lane * 4 + i;
+                my_l = s;
+            }
+            s -= tm.nt[i];
+        }
+    }
+    e = __shfl(my_e, owner, 64);
+    local = __shfl(my_l, owner, 64);
 }
 
 // Element offset, inside one stage operand region, of the 16-byte piece c
@@ -194,7 +238,7 @@ __device__ __forceinline__ float swiglu(float g, float u) {
     return g * u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
 }
 
-template <int EPI, bool ROUTED>
+template <int EPI, bool ROUTED, bool KG = false>
 __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
     constexpr bool DUAL = EPI == EPI_SWIGLU || EPI == EPI_PRE;
     constexpr bool TRANS = EPI != EPI_COMBINE;  // register epilogue (no LDS staging)
@@ -205,18 +249,25 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS bases stay scalar
     const int wm = wave >> 1, wn = wave & 1, g = lane >> 5;
-    const int K = p.K, nk = K / LK;
+    const int K = p.K;
+    const int ldk = KG ? p.ldk : K;  // row stride of A and B (elements)
+    int nk = K / LK;                 // K-grouped: set per tile
 
     TileMap tm;
-    int Mt;
+    int Mt, total;
+    const int NT = p.N / BN;
     if (ROUTED) {
         tilemap_init(tm, p.offsets);
         Mt = tm.total;
+        total = Mt * NT;
+    } else if (KG) {
+        Mt = p.M / LM;
+        kgmap_init(tm, p.kseg, Mt * NT);
+        total = tm.total;
     } else {
         Mt = (p.M + LM - 1) / LM;
+        total = Mt * NT;
     }
-    const int NT = p.N / BN;
-    const int total = Mt * NT;
     const int P = gridDim.x;
 
     // DMA geometry: each operand (256 rows x 128 B = 32 blocks of 1 KB) is
@@ -232,10 +283,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
 
     // State of the tile about to run (TILE_SETUP): expert, rows, columns,
     // its B matrices and the per-lane byte offsets of its DMA blocks.
-    int e = 0, m0 = 0, m_end = 0, n0 = 0;
+    int e = 0, m0 = 0, m_end = 0, n0 = 0, kbase = 0;
     const uint32_t a_rows_total = p.a_rows ? (uint32_t)(p.M / p.a_div) : (uint32_t)p.M;
-    const __amdgpu_buffer_rsrc_t rA = buf_rsrc(p.A, a_rows_total * (uint32_t)K * 2u);
-    const uint32_t b_bytes = (uint32_t)p.N * (uint32_t)K * 2u;  // one expert's B matrix
+    const __amdgpu_buffer_rsrc_t rA = buf_rsrc(p.A, a_rows_total * (uint32_t)ldk * 2u);
+    const uint32_t b_bytes = (uint32_t)p.N * (uint32_t)ldk * 2u;  // one expert's B matrix
     const uint16_t *pBg = p.B0, *pBu = p.B1;                     // the tile's expert
     uint32_t aoff[8], boff[8];
 
@@ -260,23 +311,36 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
     // B operand) and DMA offsets.
 #define TILE_SETUP(tt)                                                                         \
     {                                                                                          \
-        const int gsz_ = kGroupM * NT;                                                         \
-        const int grp_ = (tt) / gsz_, within_ = (tt) - grp_ * gsz_;                            \
-        const int mfirst_ = grp_ * kGroupM;                                                    \
-        const int gm_ = min(kGroupM, Mt - mfirst_);                                            \
-        const int mt_ = mfirst_ + within_ % gm_, nt_ = within_ / gm_;                          \
-        if (ROUTED) {                                                                          \
-            tilemap_find(tm, mt_, e, m0, m_end);                                               \
-        } else {                                                                               \
-            e = 0;                                                                             \
+        int mt_, nt_;                                                                          \
+        if (KG) {                                                                              \
+            int loc_;                                                                          \
+            kgmap_find(tm, (tt), e, loc_);                                                     \
+            mt_ = loc_ % Mt;                                                                   \
+            nt_ = loc_ / Mt;                                                                   \
             m0 = mt_ * LM;                                                                     \
             m_end = p.M;                                                                       \
+            kbase = __builtin_amdgcn_readfirstlane(p.kseg[e]);                                 \
+            nk = __builtin_amdgcn_readfirstlane((p.kseg[e + 1] - kbase) / LK);                 \
+        } else {                                                                               \
+            const int gsz_ = kGroupM * NT;                                                     \
+            const int grp_ = (tt) / gsz_, within_ = (tt) - grp_ * gsz_;                        \
+            const int mfirst_ = grp_ * kGroupM;                                                \
+            const int gm_ = min(kGroupM, Mt - mfirst_);                                        \
+            mt_ = mfirst_ + within_ % gm_;                                                     \
+            nt_ = within_ / gm_;                                                               \
+            if (ROUTED) {                                                                      \
+                tilemap_find(tm, mt_, e, m0, m_end);                                           \
+            } else {                                                                           \
+                e = 0;                                                                         \
+                m0 = mt_ * LM;                                                                 \
+                m_end = p.M;                                                                   \
+            }                                                                                  \
         }                                                                                      \
         e = __builtin_amdgcn_readfirstlane(e);                                                 \
         m0 = __builtin_amdgcn_readfirstlane(m0);                                               \
         m_end = __builtin_amdgcn_readfirstlane(m_end);                                         \
         n0 = nt_ * BN;                                                                         \
-        pBg = p.B0 + (size_t)e * p.N * K;                                                      \
+        pBg = KG ? p.B0 : p.B0 + (size_t)e * p.N * K;                                          \
         pBu = DUAL ? p.B1 + (size_t)e * p.N * K : pBg;                                         \
         int ar_[8];                                                                            \
         _Pragma("unroll") for (int i = 0; i < 8; ++i) ar_[i] = min(m0 + drow[i], m_end - 1);    \
@@ -285,10 +349,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
             _Pragma("unroll") for (int i = 0; i < 8; ++i) ar_[i] /= p.a_div;                    \
         }                                                                                      \
         _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                        \
-            aoff[i] = ((uint32_t)ar_[i] * (uint32_t)K + (uint32_t)dcol[i]) * 2u;               \
+            aoff[i] = ((uint32_t)ar_[i] * (uint32_t)ldk + (uint32_t)(dcol[i] + kbase)) * 2u;   \
             const int r = drow[i];                                                             \
             const int br = DUAL ? n0 + (r & (BN - 1)) : n0 + r;                                \
-            boff[i] = ((uint32_t)br * (uint32_t)K + (uint32_t)dcol[i]) * 2u;                   \
+            boff[i] = ((uint32_t)br * (uint32_t)ldk + (uint32_t)(dcol[i] + kbase)) * 2u;       \
             /* rows past the group's end: an offset past the A resource, so the */             \
             /* load fetches nothing (their outputs are dropped) */                              \
             if (m0 + r >= m_end) aoff[i] = kOobOff;                                             \
@@ -429,7 +493,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
 #undef B_ROW
         __syncthreads();  // every wave done with the ring (and its loads landed)
         first = false;
-        const int cm0 = m0, cm_end = m_end, cn0 = n0;  // this tile, for its epilogue
+        const int cm0 = m0, cm_end = m_end, cn0 = n0, ce = e;  // this tile, for its epilogue
 
         if constexpr (TRANS) {
             // The ring is free and this epilogue does not use LDS: start the
@@ -450,7 +514,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
             if constexpr (EPI == EPI_PRE || EPI == EPI_F32) {
                 // fp32: one 16-byte store per run of 4 columns (and its up twin);
                 // padding rows get kOobOff, which leaves room for the column offsets
-                const __amdgpu_buffer_rsrc_t rOutF = buf_rsrc(p.outf, (uint32_t)p.M * (uint32_t)p.ldo * 4u);
+                const __amdgpu_buffer_rsrc_t rOutF =
+                    buf_rsrc(KG ? uniform_ptr(p.outf + (size_t)ce * p.cstride) : p.outf, (uint32_t)p.M * (uint32_t)p.ldo * 4u);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = cm0 + wm * 128 + 32 * i + (lane & 31);
@@ -612,6 +677,12 @@ bool ffn_bf16_large_ok(const FfnArgs &a) {
 }
 
 bool bf16_large_gemm_ok(const LargeGemmArgs &g) {
+    if (g.kseg) {
+        const unsigned long long lim = kOobOff - (1ULL << 20);
+        return !g.dual && !g.offsets && !g.a_rows && g.M % LM == 0 && g.N % LB == 0 && g.ldk % 8 == 0 &&
+               (unsigned long long)g.M * g.ldk * 2 < lim && (unsigned long long)g.N * g.ldk * 2 < lim &&
+               (unsigned long long)g.M * g.ldo * 4 < lim && (unsigned long long)LB * 4 < 65536;
+    }
     const int groups = g.offsets ? kE : 1;
     const unsigned long long lim = kOobOff - (1ULL << 20);
     const unsigned long long a_rows = g.a_rows ? (unsigned long long)g.a_src_rows : (unsigned long long)g.M;
@@ -636,7 +707,12 @@ hipError_t launch_bf16_large_gemm(const LargeGemmArgs &g, hipStream_t s) {
     p.outf = g.out;
     p.ldo = g.ldo;
     p.up_off = g.up_off;
-    if (g.dual) {
+    p.kseg = g.kseg;
+    p.ldk = g.ldk;
+    p.cstride = g.cstride;
+    if (g.kseg) {
+        hipLaunchKernelGGL((k_gemm_bf16_large<EPI_F32, false, true>), dim3(P), dim3(256), 0, s, p);
+    } else if (g.dual) {
         if (g.offsets) hipLaunchKernelGGL((k_gemm_bf16_large<EPI_PRE, true>), dim3(P), dim3(256), 0, s, p);
         else hipLaunchKernelGGL((k_gemm_bf16_large<EPI_PRE, false>), dim3(P), dim3(256), 0, s, p);
     } else {

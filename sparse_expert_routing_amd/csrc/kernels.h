@@ -90,7 +90,7 @@ hipError_t launch_ffn_skinny(const FfnArgs &a, hipStream_t s);
 bool ffn_bf16_large_ok(const FfnArgs &a);
 hipError_t launch_ffn_bf16_large(const FfnArgs &a, hipStream_t s);
 // The same persistent 256x256-tile kernel as a grouped NT GEMM with an fp32
-// output (the layer backward): out[m, n] = sum_k A[m, k] B_g[n, k] with B
+// output (the layer backward), grouped over M or (kseg) over K: out[m, n] = sum_k A[m, k] B_g[n, k] with B
 // per group (offsets != nullptr) or one B; dual: B0 / B1 are the gate / up
 // matrices of a SwiGLU tile and their products go to columns n and
 // up_off + n.  a_rows: A row m is row a_rows[m] / a_div (a_src_rows rows).
@@ -107,6 +107,12 @@ struct LargeGemmArgs {
     float *out;
     int ldo, up_off;
     bool dual;
+    // K-grouped form (weight gradients): out_e = A[:, K_e] B[:, K_e]^T with
+    // K_e = [kseg[e], kseg[e+1]) (multiples of 64) of A [M, ldk], B [N, ldk],
+    // written to out + e * cstride; groups with empty K_e are not written
+    const int32_t *kseg;
+    int ldk;
+    int64_t cstride;
 };
 bool bf16_large_gemm_ok(const LargeGemmArgs &g);
 hipError_t launch_bf16_large_gemm(const LargeGemmArgs &g, hipStream_t s);
