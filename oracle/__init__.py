@@ -67,7 +67,7 @@ def lib():
             "oracle_expert_ffn": [vp, vp, vp, vp, vp, i64, vp, vp],
             "oracle_combine": [vp, vp, vp, vp, vp, vp, i64, vp, vp],
             "oracle_forward": [vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp],
-            "oracle_backward": [vp] * 16,
+            "oracle_backward": [vp] * 16 + [i32],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -194,25 +194,34 @@ def combine(sh: Shape, shared: dict, x, y_perm, row_of, g, tokens=None):
     return y
 
 
-def backward(sh: Shape, x, wr, idx, experts: dict, shared: dict, dy):
+def backward(sh: Shape, x, wr, idx, experts: dict, shared: dict, dy, weight_grads=True):
     """Gradients of the layer output for the routing idx [T,k] given dy [T,d] f32:
     dict of dx [T,d], dwr [E,d], dwg/dwu [E,I,d], dwd [E,d,I], dsg/dsu [I,d],
-    dsd [d,I], dg [T,k] (all f32).  f32 and bf16 weights only."""
+    dsd [d,I], dg [T,k] (all f32).  weight_grads=False: dx and dg only; an
+    int e: dx, dg and routed expert e's dwr [1,d], dwg/dwu [1,I,d], dwd [1,d,I]
+    (the sums over the given tokens only).  f32 and bf16 weights only."""
     assert sh.wt != E4M3, "the backward oracle covers f32 and bf16 weights"
     T, d, E, k, I = sh.T, sh.d, sh.E, sh.k, sh.I
     we, k1 = ffn(experts)
     ws, k2 = ffn(shared)
-    out = dict(dx=np.empty((T, d), np.float32), dwr=np.empty((E, d), np.float32),
-               dwg=np.empty((E, I, d), np.float32), dwu=np.empty((E, I, d), np.float32),
-               dwd=np.empty((E, d, I), np.float32), dsg=np.empty((I, d), np.float32),
-               dsu=np.empty((I, d), np.float32), dsd=np.empty((d, I), np.float32),
-               dg=np.empty((T, k), np.float32))
+    shp = dict(dx=(T, d), dwr=(E, d), dwg=(E, I, d), dwu=(E, I, d), dwd=(E, d, I), dsg=(I, d), dsu=(I, d),
+               dsd=(d, I), dg=(T, k))
+    one = not isinstance(weight_grads, bool)
+    if one:
+        assert 0 <= weight_grads < E
+        shp.update(dwr=(1, d), dwg=(1, I, d), dwu=(1, I, d), dwd=(1, d, I), dsg=(1,), dsu=(1,), dsd=(1,))
+    elif not weight_grads:
+        shp = {n: (v if n in ("dx", "dg") else (1,)) for n, v in shp.items()}
+    out = {n: np.empty(v, np.float32) for n, v in shp.items()}
     lib().oracle_backward(ctypes.byref(sh), _p(x), _p(np.ascontiguousarray(wr, dtype=np.float32)),
                           _p(np.ascontiguousarray(idx, dtype=np.int32)), ctypes.byref(we), ctypes.byref(ws),
                           _p(np.ascontiguousarray(dy, dtype=np.float32)),
-                          *[_p(out[n]) for n in ("dx", "dwr", "dwg", "dwu", "dwd", "dsg", "dsu", "dsd", "dg")])
+                          *[_p(out[n]) for n in ("dx", "dwr", "dwg", "dwu", "dwd", "dsg", "dsu", "dsd", "dg")],
+                          int(weight_grads) if one else (-1 if weight_grads else -2))
     del k1, k2
-    return out
+    if one:
+        return {n: out[n] for n in ("dx", "dg", "dwr", "dwg", "dwu", "dwd")}
+    return out if weight_grads else dict(dx=out["dx"], dg=out["dg"])
 
 
 def forward(sh: Shape, x, wr, bias, experts: dict, shared: dict, tokens=None):

@@ -548,11 +548,15 @@ static void ffn_row_backward(const or_shape *sh, const or_ffn *w, int64_t g, con
  *   dWd_e = sum of (routed output gradient) (x) h; the shared expert's over
  *   all tokens.
  * Outputs fp32: dx [T, d], dwr [E, d], dwg, dwu [E, I, d], dwd [E, d, I],
- * dsg, dsu [I, d], dsd [d, I], dg [T, k].  f32 and bf16 weights only. */
+ * dsg, dsu [I, d], dsd [d, I], dg [T, k].  f32 and bf16 weights only.
+ * wsel selects the weight gradients: -1 all of them; -2 none (dx and dg
+ * only); e >= 0 routed expert e's alone (dwg, dwu, dwd and dwr hold one
+ * expert's slice, [1, I, d], [1, d, I] and [1, d]; the shared expert's are
+ * not computed). */
 void oracle_backward(const or_shape *sh, const void *x, const float *wr, const int32_t *idx,
                      const or_ffn *experts, const or_ffn *shared, const float *dy, float *dx,
                      float *dwr, float *dwg, float *dwu, float *dwd, float *dsg, float *dsu, float *dsd,
-                     float *dg_out) {
+                     float *dg_out, int32_t wsel) {
     const int64_t T = sh->T, d = sh->d, I = sh->I, E = sh->E, k = sh->k;
     if (sh->wt == OR_E4M3) return;
     /* per (t, j) and per token intermediates for the weight gradients */
@@ -622,8 +626,10 @@ void oracle_backward(const or_shape *sh, const void *x, const float *wr, const i
         free(hb);
     }
     /* weight gradients: routed experts and router, one expert at a time */
+    const int64_t e_lo = wsel >= 0 ? wsel : 0, e_hi = wsel >= 0 ? wsel + 1 : (wsel == -1 ? E : 0);
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t e = 0; e < E; ++e) {
+    for (int64_t e = e_lo; e < e_hi; ++e) {
+        const int64_t eo = e - e_lo;  /* output slot */
         double *gw = (double *)calloc((size_t)(I * d), sizeof(double));
         double *uw = (double *)calloc((size_t)(I * d), sizeof(double));
         double *dw = (double *)calloc((size_t)(d * I), sizeof(double));
@@ -645,11 +651,11 @@ void oracle_backward(const or_shape *sh, const void *x, const float *wr, const i
                 for (int64_t n = 0; n < d; ++n) rw[n] += dl[f] * x_at(sh, x, t, n);
             }
         for (int64_t q = 0; q < I * d; ++q) {
-            dwg[e * I * d + q] = (float)gw[q];
-            dwu[e * I * d + q] = (float)uw[q];
-            dwd[e * d * I + q] = (float)dw[q];
+            dwg[eo * I * d + q] = (float)gw[q];
+            dwu[eo * I * d + q] = (float)uw[q];
+            dwd[eo * d * I + q] = (float)dw[q];
         }
-        for (int64_t n = 0; n < d; ++n) dwr[e * d + n] = (float)rw[n];
+        for (int64_t n = 0; n < d; ++n) dwr[eo * d + n] = (float)rw[n];
         free(gw);
         free(uw);
         free(dw);
@@ -657,7 +663,7 @@ void oracle_backward(const or_shape *sh, const void *x, const float *wr, const i
     }
     /* the shared expert's weight gradients: over all tokens, one row at a time */
 #pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < I; ++i)
+    for (int64_t i = 0; i < (wsel == -1 ? I : 0); ++i)
         for (int64_t n = 0; n < d; ++n) {
             double cg = 0.0, cu = 0.0;
             for (int64_t t = 0; t < T; ++t) {
@@ -668,7 +674,7 @@ void oracle_backward(const or_shape *sh, const void *x, const float *wr, const i
             dsu[i * d + n] = (float)cu;
         }
 #pragma omp parallel for schedule(static)
-    for (int64_t n = 0; n < d; ++n)
+    for (int64_t n = 0; n < (wsel == -1 ? d : 0); ++n)
         for (int64_t i = 0; i < I; ++i) {
             double c = 0.0;
             for (int64_t t = 0; t < T; ++t) c += sy[t * d + n] * sh_h[t * I + i];

@@ -97,3 +97,63 @@ def test_backward_matches_oracle(T, d, I, kind, seed):
 def test_backward_rejects_other_types():
     ds = _lib.desc(32, 256, 256, 8, 64, "f32", "f32")
     assert _lib.workspace_bytes(ds, _lib.MOE_WS_BACKWARD) == 0
+
+
+@pytest.mark.timeout(400)
+def test_backward_full_size_sampled():
+    """The skewed prefill workload at full size (T=16384, d=7168, I=2048, bf16),
+    routed by the forward on the GPU, backward in the launch configuration
+    bench.py --backward times.  The oracle checks dx and dg on 8 sampled tokens
+    (both are per-token), and the weight gradients (dW gate/up/down and the
+    router row) of two experts -- the coldest one and one with about 100 rows --
+    from exactly the tokens that chose them; every gradient must be finite."""
+    from sparse_expert_routing_amd.layer import layer_from_inputs, upload
+    cfg = synth.CONFIGS[4]
+    T, d, I = cfg.T, cfg.d, cfg.I
+    say(f"[backward] full size T={T} d={d} I={I}: inputs + forward")
+    inp = synth.make_inputs(cfg)
+    layer = layer_from_inputs(inp)
+    x = upload(inp["x"])
+    layer.forward(x, upload(inp["bias"]))
+    dy = synth.normal(cfg.seed, synth.TID_AUX, (T, d), 1.0, "f32")
+    f32 = torch.float32
+    grads = dict(dx=empty((T, d), f32), dw_router=empty((256, d), f32), dw_gate=empty((256, I, d), f32),
+                 dw_up=empty((256, I, d), f32), dw_down=empty((256, d, I), f32), ds_gate=empty((I, d), f32),
+                 ds_up=empty((I, d), f32), ds_down=empty((d, I), f32), dg=empty((T, 8), f32))
+    for t in grads.values():
+        t.fill_(float("nan"))
+    ws = empty(_lib.workspace_bytes(layer.desc, _lib.MOE_WS_BACKWARD), torch.uint8)
+    say("[backward] full size: moe_backward")
+    _lib.moe_backward(layer.desc, x, layer.wr, layer.idx, layer.w, layer.offsets, layer.row_src, layer.row_of,
+                      layer.ex_w, layer.sh_w, layer.y_perm, dev(dy), grads, ws)
+    torch.cuda.synchronize()
+    for n, t in grads.items():
+        assert bool(torch.isfinite(t).all()), f"{n}: unwritten or non-finite elements"
+    gi, counts = host(layer.idx), host(layer.counts)
+    del ws
+
+    def sub(toks, wsel):
+        s = oracle.shape(len(toks), d, 256, 8, I, cfg.act, cfg.wt)
+        return oracle.backward(s, np.ascontiguousarray(inp["x"][toks]), inp["wr"], np.ascontiguousarray(gi[toks]),
+                               inp["experts"], inp["shared"], np.ascontiguousarray(dy[toks]), weight_grads=wsel)
+
+    rng = np.random.default_rng(7)
+    toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 6, replace=False)]))
+    say(f"[backward] full size: oracle dx, dg on tokens {toks.tolist()}")
+    o = sub(toks, False)
+    for n in ("dx", "dg"):
+        err = max_rel(host(grads[n][torch.from_numpy(toks).cuda()]), o[n])
+        say(f"[backward] full size: {n} max rel err {err:.3e}")
+        assert err <= TOL["bf16"], (n, err)
+    nz = np.flatnonzero(counts > 0)
+    cold = int(nz[np.argmin(counts[nz])])
+    mid = int(np.argmin(np.abs(counts.astype(np.int64) - 100)))
+    for e in dict.fromkeys([cold, mid]):
+        mine = np.flatnonzero((gi == e).any(1))
+        assert len(mine) == counts[e]
+        say(f"[backward] full size: oracle weight gradients of expert {e} ({len(mine)} rows)")
+        o = sub(mine, e)
+        for n, on in (("dw_gate", "dwg"), ("dw_up", "dwu"), ("dw_down", "dwd"), ("dw_router", "dwr")):
+            err = max_rel(host(grads[n][e]), o[on][0])
+            say(f"[backward] full size: expert {e} {n} max rel err {err:.3e}")
+            assert err <= TOL["bf16"], (e, n, err)

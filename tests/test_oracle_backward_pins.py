@@ -103,3 +103,27 @@ def test_bias_enters_only_through_the_choice():
     o2 = oracle.backward(sh, x, wr, idx2, ex, shd, dy)
     for n in o1:
         assert np.array_equal(o1[n], o2[n]), n
+
+
+def test_sampled_modes_equal_the_full_gradients():
+    """The reduced modes full-size checks use: dx and dg of a token subset
+    equal the full run's rows (they are per-token), and an expert's weight
+    gradients from only the tokens that chose it equal the full run's slice
+    (no other token's row enters them)."""
+    cfg, sh, x, wr, ex, shd, bias, idx, dy = setup("bf16", "bf16", T=24)
+    full = oracle.backward(sh, x, wr, idx, ex, shd, dy)
+    toks = np.array([1, 5, 17, 23])
+    sub = oracle.shape(len(toks), cfg.d, E, K, cfg.I, "bf16", "bf16")
+    part = oracle.backward(sub, np.ascontiguousarray(x[toks]), wr, np.ascontiguousarray(idx[toks]), ex, shd,
+                           np.ascontiguousarray(dy[toks]), weight_grads=False)
+    assert set(part) == {"dx", "dg"}
+    assert np.array_equal(part["dx"], full["dx"][toks]) and np.array_equal(part["dg"], full["dg"][toks])
+    e = int(np.bincount(idx.ravel(), minlength=E).argmax())
+    mine = np.flatnonzero((idx == e).any(1))
+    assert 0 < len(mine) < cfg.T
+    sub = oracle.shape(len(mine), cfg.d, E, K, cfg.I, "bf16", "bf16")
+    one = oracle.backward(sub, np.ascontiguousarray(x[mine]), wr, np.ascontiguousarray(idx[mine]), ex, shd,
+                          np.ascontiguousarray(dy[mine]), weight_grads=e)
+    for n in ("dwr", "dwg", "dwu", "dwd"):
+        assert np.allclose(one[n][0], full[n][e], rtol=1e-6, atol=1e-7 * np.abs(full[n][e]).max()), n
+    assert np.array_equal(one["dx"], full["dx"][mine])
