@@ -256,7 +256,10 @@ size_t moe_workspace_bytes(const moe_desc_t *desc, int32_t stage);
  *   ds_gate, ds_up [I, d]; ds_down [d, I] (the shared expert);
  *   dg [T, k] the combine-weight gradients dy . y_perm_j (NULL: not returned).
  *   workspace >= moe_workspace_bytes(desc, MOE_WS_BACKWARD) bytes of device
- *   memory (about (T*k + T) * (6d + 18I) bytes).
+ *   memory: about (T*k + T)(6d + 18I) for the per-row intermediates, plus
+ *   (T*k + 64E + T)(4d + 6I) for their K-contiguous transposes, plus
+ *   6(E + 1)*I*d for the transposed weights and 64*E*d for the router
+ *   partials (about 38 GiB at T=16384, d=7168, I=2048, E=256, k=8).
  * Requires d % 128 == 0 and I % 128 == 0.
  */
 moe_status_t moe_backward(const moe_desc_t *desc, const void *x, const float *w_router, const int32_t *idx,
