@@ -50,8 +50,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100, help="timed steps of the balancing loop")
     ap.add_argument("--warmup", type=int, default=5, help="untimed steps (on a scratch copy of the bias)")
-    ap.add_argument("--config", type=int, default=4, choices=[2, 3, 4, 5],
-                    help="workload (4: the skewed prefill layer the metric is quoted on)")
+    ap.add_argument("--config", type=int, default=4, choices=[2, 3, 4, 5, 6],
+                    help="workload (4: the skewed prefill layer the metric is quoted on; 6: one GPU's "
+                         "share of an 8-way expert-parallel layer, 32 experts of ~4096 rows)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",

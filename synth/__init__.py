@@ -10,7 +10,10 @@ describe -- 256 routed experts plus one shared expert, top-8 routing (DeepSeek
 V3 From Scratch, "The idea"; crackai.dev DeepSeek-V3 summary, "How It Works")
 -- with d_model, expert width, dtypes, distributions and seeds of our own
 choosing for each workload (tiny fp32, mid bf16, decode bf16, skewed prefill
-bf16 with a 100-step balancing loop, prefill fp8).
+bf16 with a 100-step balancing loop, prefill fp8).  A sixth workload stands
+for one GPU's share of an 8-way expert-parallel layer: the bias confines the
+choice to 32 experts, so the grouped GEMMs see 32 groups of about 4096 rows
+each, the shape one of 8 GPUs holding 32 experts each would run.
 """
 from __future__ import annotations
 
@@ -142,7 +145,7 @@ class Config:
     I: int
     act: str = BF16          # dtype of x
     wt: str = BF16           # dtype of expert weights (and of the expert GEMM inputs)
-    bias: str = "uniform"    # "zero" or "uniform" (U(-0.05, 0.05))
+    bias: str = "uniform"    # "zero", "uniform" (U(-0.05, 0.05)) or "shard32" (1 for experts 0-31, else 0)
     skew: float = 0.0        # router row power-law exponent (0 = none)
     steps: int = 1           # forward + bias-update steps of the balancing loop
     E: int = 256
@@ -166,6 +169,8 @@ CONFIGS = {
     4: Config("prefill-zipf-bf16 T16384 d7168 I2048", seed=3, T=16384, d=7168, I=2048,
               bias="zero", skew=1.1, steps=100),
     5: Config("prefill-fp8 T16384 d7168 I2048", seed=4, T=16384, d=7168, I=2048, wt=E4M3),
+    # one GPU's share of an 8-way expert-parallel layer (32 local experts)
+    6: Config("ep8-shard-bf16 T16384 d7168 I2048 E32", seed=5, T=16384, d=7168, I=2048, bias="shard32"),
 }
 
 
@@ -178,6 +183,10 @@ def make_router(cfg: Config):
         wr = normal(cfg.seed, TID_WR, (cfg.E, cfg.d), cfg.std_w, F32)
     if cfg.bias == "zero":
         bias = np.zeros(cfg.E, dtype=np.float32)
+    elif cfg.bias == "shard32":
+        # a sigmoid affinity lies in (0, 1): a bias of 1 on experts 0-31 puts
+        # every token's top 8 among them
+        bias = np.where(np.arange(cfg.E) < 32, 1.0, 0.0).astype(np.float32)
     else:
         bias = uniform(cfg.seed, TID_BIAS, cfg.E, -0.05, 0.05)
     return x, wr, bias

@@ -154,6 +154,17 @@ def test_layer_config5_full_size_sampled():
     check_layer(cfg, inp, n_sample=12, route_all=False)
 
 
+def test_layer_ep8_shard_full_size_sampled():
+    """One GPU's share of an 8-way expert-parallel layer at full size: the
+    bias confines the choice to experts 0-31, so the grouped GEMMs run 32
+    groups of about 4096 rows (T=16384, d=7168, I=2048, bf16); the oracle
+    checks 12 sampled tokens."""
+    cfg = synth.CONFIGS[6]
+    inp = synth.make_inputs(cfg)
+    gi, _ = check_layer(cfg, inp, n_sample=12, route_all=False)
+    assert gi.max() < 32
+
+
 def test_balancing_loop_reduced():
     """The bias-balancing loop (route -> counts -> sign-step update, 100 steps,
     bias carried) at the skewed workload's recipe, T=2048, d=1024, checked

@@ -81,3 +81,16 @@ def test_values_do_not_depend_on_thread_count():
         env = dict(os.environ, OMP_NUM_THREADS=n, PYTHONPATH=ROOT)
         outs.append(subprocess.check_output([sys.executable, "-c", code], cwd=ROOT, env=env, text=True).strip())
     assert outs[0] == outs[1] == _digest()
+
+
+def test_shard_workload_confines_the_choice_to_32_experts():
+    """The expert-parallel shard workload: its bias puts every token's top 8
+    among experts 0-31, with every one of them used (checked on the oracle's
+    routing of a reduced copy)."""
+    import oracle
+    cfg = synth.CONFIGS[6].with_(T=512, d=512)
+    x, wr, bias = synth.make_router(cfg)
+    assert np.array_equal(bias[:32], np.ones(32, np.float32)) and not bias[32:].any()
+    idx, _, _, _ = oracle.route(oracle.shape_of(cfg), x, wr, bias)
+    counts = np.bincount(idx.ravel(), minlength=256)
+    assert counts[32:].sum() == 0 and (counts[:32] > 0).all()
