@@ -199,8 +199,8 @@ def backward(sh: Shape, x, wr, idx, experts: dict, shared: dict, dy, weight_grad
     dict of dx [T,d], dwr [E,d], dwg/dwu [E,I,d], dwd [E,d,I], dsg/dsu [I,d],
     dsd [d,I], dg [T,k] (all f32).  weight_grads=False: dx and dg only; an
     int e: dx, dg and routed expert e's dwr [1,d], dwg/dwu [1,I,d], dwd [1,d,I]
-    (the sums over the given tokens only).  f32 and bf16 weights only."""
-    assert sh.wt != E4M3, "the backward oracle covers f32 and bf16 weights"
+    (the sums over the given tokens only).  e4m3 weights: every backward GEMM
+    on e4m3 operands (tiles along each GEMM's reduction; see the C source)."""
     T, d, E, k, I = sh.T, sh.d, sh.E, sh.k, sh.I
     we, k1 = ffn(experts)
     ws, k2 = ffn(shared)

@@ -499,9 +499,10 @@ void oracle_forward(const or_shape *sh, const void *x, const float *wr, const fl
  *   inputs of the backward GEMMs, rounded like h);
  *   da = Wg^T dug + Wu^T duu.
  * The rounding of h and of the routed output is taken as the identity in
- * the derivative. */
+ * the derivative.  raw (optional, [3][I]): h, dug, duu before rounding. */
 static void ffn_row_backward(const or_shape *sh, const or_ffn *w, int64_t g, const double *a,
-                             const double *dyr, double *h, double *dug, double *duu, double *da) {
+                             const double *dyr, double *h, double *dug, double *duu, double *da,
+                             double *raw) {
     const int64_t d = sh->d, I = sh->I;
     for (int64_t i = 0; i < I; ++i) {
         double ug = 0.0, uu = 0.0;
@@ -515,6 +516,11 @@ static void ffn_row_backward(const or_shape *sh, const or_ffn *w, int64_t g, con
         h[i] = ug * sg * uu;
         dug[i] = dh * uu * sg * (1.0 + ug * (1.0 - sg));
         duu[i] = dh * ug * sg;
+        if (raw) {
+            raw[i] = h[i];
+            raw[I + i] = dug[i];
+            raw[2 * I + i] = duu[i];
+        }
     }
     round_to_gemm_input(sh->wt, h, (int)I);
     round_to_gemm_input(sh->wt, dug, (int)I);
@@ -547,18 +553,94 @@ static void ffn_row_backward(const or_shape *sh, const or_ffn *w, int64_t g, con
  *   dWg_e = sum over e's rows of dug (x) a, dWu_e likewise with duu,
  *   dWd_e = sum of (routed output gradient) (x) h; the shared expert's over
  *   all tokens.
+ * e4m3 weights (fp8 GEMMs in the backward too: crackai.dev DeepSeek-V3
+ * summary, "How It Works"; our reading of where the tiles lie): every
+ * backward GEMM takes e4m3 operands, each quantised per 1x128 tile along
+ * that GEMM's reduction.  The data-gradient GEMMs reduce along a row: the
+ * output gradients (g_j dy, dy) per 1x128 tile of d, the SwiGLU input
+ * gradients per 1x128 tile of I (round_to_gemm_input), against the stored
+ * weight blocks.  The weight-gradient GEMMs reduce over an expert's rows:
+ * the rows in dispatch order (ascending t*k + j; the shared expert: tokens
+ * in order) form groups of 128 (the last one short, as if padded with
+ * zeros), and every column of a group is one tile, quantised from the
+ * unrounded fp32 values -- dug, duu, h = silu(ug) uu and the output
+ * gradient -- and from the bf16 x.  The router stays fp32.
  * Outputs fp32: dx [T, d], dwr [E, d], dwg, dwu [E, I, d], dwd [E, d, I],
- * dsg, dsu [I, d], dsd [d, I], dg [T, k].  f32 and bf16 weights only.
+ * dsg, dsu [I, d], dsd [d, I], dg [T, k].
  * wsel selects the weight gradients: -1 all of them; -2 none (dx and dg
  * only); e >= 0 routed expert e's alone (dwg, dwu, dwd and dwr hold one
  * expert's slice, [1, I, d], [1, d, I] and [1, d]; the shared expert's are
  * not computed). */
+/* Quantise each of the ncols columns of g [nr, ncols] (nr <= 128 rows of one
+ * group) as one 128-value tile, the rows past nr counting as zeros; g is
+ * replaced by the dequantised values. */
+static void quant_cols(double *g, int nr, int64_t ncols) {
+    float v[128];
+    uint8_t q[128];
+    for (int64_t c = 0; c < ncols; ++c) {
+        for (int i = 0; i < 128; ++i) v[i] = i < nr ? (float)g[i * ncols + c] : 0.0f;
+        const double sc = (double)quant_tile(v, 128, q);
+        for (int i = 0; i < nr; ++i) g[i * ncols + c] = e4m3_dec(q[i]) * sc;
+    }
+}
+
+/* e4m3 weight gradients of one FFN over the rows rows[0..n) (dispatch
+ * order), in groups of 128: gw, uw [I, d] += Q(dug)^T Q(x), Q(duu)^T Q(x);
+ * dw [d, I] += Q(dy)^T Q(h), each operand quantised per column of a group.
+ * xrow(r): the token of row r; draw: [rows, 3I] raw (h, dug, duu); dyraw:
+ * [rows, d] the unrounded output gradient. */
+static void wgrad_e4m3(const or_shape *sh, const void *x, const int64_t *rows, int64_t n, int64_t kdiv,
+                       const double *draw, const double *dyraw, double *gw, double *uw, double *dw) {
+    const int64_t d = sh->d, I = sh->I;
+    double *gx = (double *)malloc(sizeof(double) * 128 * d);
+    double *gy = (double *)malloc(sizeof(double) * 128 * d);
+    double *gg = (double *)malloc(sizeof(double) * 128 * I);
+    double *gu = (double *)malloc(sizeof(double) * 128 * I);
+    double *gh = (double *)malloc(sizeof(double) * 128 * I);
+    for (int64_t g0 = 0; g0 < n; g0 += 128) {
+        const int nr = (int)(n - g0 < 128 ? n - g0 : 128);
+        for (int i = 0; i < nr; ++i) {
+            const int64_t f = rows[g0 + i];
+            for (int64_t c = 0; c < d; ++c) {
+                gx[i * d + c] = x_at(sh, x, f / kdiv, c);
+                gy[i * d + c] = dyraw[f * d + c];
+            }
+            for (int64_t c = 0; c < I; ++c) {
+                gh[i * I + c] = draw[f * 3 * I + c];
+                gg[i * I + c] = draw[f * 3 * I + I + c];
+                gu[i * I + c] = draw[f * 3 * I + 2 * I + c];
+            }
+        }
+        quant_cols(gx, nr, d);
+        quant_cols(gy, nr, d);
+        quant_cols(gh, nr, I);
+        quant_cols(gg, nr, I);
+        quant_cols(gu, nr, I);
+        for (int i = 0; i < nr; ++i) {
+            for (int64_t c = 0; c < I; ++c) {
+                const double cg = gg[i * I + c], cu = gu[i * I + c];
+                for (int64_t m = 0; m < d; ++m) {
+                    gw[c * d + m] += cg * gx[i * d + m];
+                    uw[c * d + m] += cu * gx[i * d + m];
+                }
+            }
+            for (int64_t m = 0; m < d; ++m)
+                for (int64_t c = 0; c < I; ++c) dw[m * I + c] += gy[i * d + m] * gh[i * I + c];
+        }
+    }
+    free(gx);
+    free(gy);
+    free(gg);
+    free(gu);
+    free(gh);
+}
+
 void oracle_backward(const or_shape *sh, const void *x, const float *wr, const int32_t *idx,
                      const or_ffn *experts, const or_ffn *shared, const float *dy, float *dx,
                      float *dwr, float *dwg, float *dwu, float *dwd, float *dsg, float *dsu, float *dsd,
                      float *dg_out, int32_t wsel) {
     const int64_t T = sh->T, d = sh->d, I = sh->I, E = sh->E, k = sh->k;
-    if (sh->wt == OR_E4M3) return;
+    const int fp8 = sh->wt == OR_E4M3;
     /* per (t, j) and per token intermediates for the weight gradients */
     double *ry = (double *)malloc(sizeof(double) * T * k * d);  /* routed output gradient */
     double *rh = (double *)malloc(sizeof(double) * T * k * I);
@@ -570,6 +652,11 @@ void oracle_backward(const or_shape *sh, const void *x, const float *wr, const i
     double *suu = (double *)malloc(sizeof(double) * T * I);
     double *dl = (double *)malloc(sizeof(double) * T * k);
     double *xa = (double *)malloc(sizeof(double) * T * d);      /* x as the GEMMs read it */
+    /* e4m3: unrounded values for the weight-gradient tiles */
+    double *ryr = fp8 ? (double *)malloc(sizeof(double) * T * k * d) : NULL;
+    double *rraw = fp8 ? (double *)malloc(sizeof(double) * T * k * 3 * I) : NULL;
+    double *syr = fp8 ? (double *)malloc(sizeof(double) * T * d) : NULL;
+    double *sraw = fp8 ? (double *)malloc(sizeof(double) * T * 3 * I) : NULL;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t t = 0; t < T; ++t) {
         double *a = xa + t * d;
@@ -591,23 +678,29 @@ void oracle_backward(const or_shape *sh, const void *x, const float *wr, const i
         }
         for (int64_t j = 0; j < k; ++j) {
             const int e = idx[t * k + j];
+            const int64_t f = t * k + j;
             const double gj = s[j] / ssum;
             ffn_row(sh, experts, e, a, yr, hb);
             double dgj = 0.0;
             for (int64_t n = 0; n < d; ++n) dgj += (double)dy[t * d + n] * round_yperm(sh, yr[n]);
             dgv[j] = dgj;
-            double *dyr = ry + (t * k + j) * d;
+            double *dyr = ry + f * d;
             for (int64_t n = 0; n < d; ++n) dyr[n] = gj * (double)dy[t * d + n];
+            if (fp8)
+                for (int64_t n = 0; n < d; ++n) ryr[f * d + n] = dyr[n];
             round_to_gemm_input(sh->wt, dyr, (int)d);
-            ffn_row_backward(sh, experts, e, a, dyr, rh + (t * k + j) * I, rug + (t * k + j) * I,
-                             ruu + (t * k + j) * I, da);
+            ffn_row_backward(sh, experts, e, a, dyr, rh + f * I, rug + f * I, ruu + f * I, da,
+                             fp8 ? rraw + f * 3 * I : NULL);
             for (int64_t n = 0; n < d; ++n) acc[n] += da[n];
         }
         /* shared expert */
         double *dys = sy + t * d;
         for (int64_t n = 0; n < d; ++n) dys[n] = (double)dy[t * d + n];
+        if (fp8)
+            for (int64_t n = 0; n < d; ++n) syr[t * d + n] = dys[n];
         round_to_gemm_input(sh->wt, dys, (int)d);
-        ffn_row_backward(sh, shared, 0, a, dys, sh_h + t * I, sug + t * I, suu + t * I, da);
+        ffn_row_backward(sh, shared, 0, a, dys, sh_h + t * I, sug + t * I, suu + t * I, da,
+                         fp8 ? sraw + t * 3 * I : NULL);
         for (int64_t n = 0; n < d; ++n) acc[n] += da[n];
         /* router: through the renormalised weights only */
         double gdg = 0.0;
@@ -634,11 +727,16 @@ void oracle_backward(const or_shape *sh, const void *x, const float *wr, const i
         double *uw = (double *)calloc((size_t)(I * d), sizeof(double));
         double *dw = (double *)calloc((size_t)(d * I), sizeof(double));
         double *rw = (double *)calloc((size_t)d, sizeof(double));
-        for (int64_t t = 0; t < T; ++t)
-            for (int64_t j = 0; j < k; ++j) {
-                if (idx[t * k + j] != e) continue;
-                const int64_t f = t * k + j;
-                const double *a = xa + t * d;
+        int64_t *rows = (int64_t *)malloc(sizeof(int64_t) * (size_t)(T * k));
+        int64_t n_e = 0;
+        for (int64_t f = 0; f < T * k; ++f)
+            if (idx[f] == e) rows[n_e++] = f;
+        if (fp8) {
+            wgrad_e4m3(sh, x, rows, n_e, k, rraw, ryr, gw, uw, dw);
+        } else {
+            for (int64_t q = 0; q < n_e; ++q) {
+                const int64_t f = rows[q];
+                const double *a = xa + (f / k) * d;
                 for (int64_t i = 0; i < I; ++i) {
                     const double cg = rug[f * I + i], cu = ruu[f * I + i];
                     for (int64_t n = 0; n < d; ++n) {
@@ -648,8 +746,12 @@ void oracle_backward(const or_shape *sh, const void *x, const float *wr, const i
                 }
                 for (int64_t n = 0; n < d; ++n)
                     for (int64_t i = 0; i < I; ++i) dw[n * I + i] += ry[f * d + n] * rh[f * I + i];
-                for (int64_t n = 0; n < d; ++n) rw[n] += dl[f] * x_at(sh, x, t, n);
             }
+        }
+        for (int64_t q = 0; q < n_e; ++q) {
+            const int64_t f = rows[q];
+            for (int64_t n = 0; n < d; ++n) rw[n] += dl[f] * x_at(sh, x, f / k, n);
+        }
         for (int64_t q = 0; q < I * d; ++q) {
             dwg[eo * I * d + q] = (float)gw[q];
             dwu[eo * I * d + q] = (float)uw[q];
@@ -660,26 +762,57 @@ void oracle_backward(const or_shape *sh, const void *x, const float *wr, const i
         free(uw);
         free(dw);
         free(rw);
+        free(rows);
     }
-    /* the shared expert's weight gradients: over all tokens, one row at a time */
-#pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < (wsel == -1 ? I : 0); ++i)
-        for (int64_t n = 0; n < d; ++n) {
-            double cg = 0.0, cu = 0.0;
-            for (int64_t t = 0; t < T; ++t) {
-                cg += sug[t * I + i] * xa[t * d + n];
-                cu += suu[t * I + i] * xa[t * d + n];
+    /* the shared expert's weight gradients: over all tokens */
+    if (wsel == -1 && fp8) {
+        /* groups of 128 tokens; the groups are independent partial sums,
+         * added in group order */
+        const int64_t ng = (T + 127) / 128;
+        double *gw = (double *)calloc((size_t)(ng * I * d), sizeof(double));
+        double *uw = (double *)calloc((size_t)(ng * I * d), sizeof(double));
+        double *dw = (double *)calloc((size_t)(ng * d * I), sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t gi = 0; gi < ng; ++gi) {
+            int64_t rows[128];
+            const int64_t n = T - gi * 128 < 128 ? T - gi * 128 : 128;
+            for (int64_t i = 0; i < n; ++i) rows[i] = gi * 128 + i;
+            wgrad_e4m3(sh, x, rows, n, 1, sraw, syr, gw + gi * I * d, uw + gi * I * d, dw + gi * d * I);
+        }
+        for (int64_t q = 0; q < I * d; ++q) {
+            double a = 0.0, b = 0.0, c = 0.0;
+            for (int64_t gi = 0; gi < ng; ++gi) {
+                a += gw[gi * I * d + q];
+                b += uw[gi * I * d + q];
+                c += dw[gi * d * I + q];
             }
-            dsg[i * d + n] = (float)cg;
-            dsu[i * d + n] = (float)cu;
+            dsg[q] = (float)a;
+            dsu[q] = (float)b;
+            dsd[q] = (float)c;
         }
+        free(gw);
+        free(uw);
+        free(dw);
+    } else if (wsel == -1) {
 #pragma omp parallel for schedule(static)
-    for (int64_t n = 0; n < (wsel == -1 ? d : 0); ++n)
-        for (int64_t i = 0; i < I; ++i) {
-            double c = 0.0;
-            for (int64_t t = 0; t < T; ++t) c += sy[t * d + n] * sh_h[t * I + i];
-            dsd[n * I + i] = (float)c;
-        }
+        for (int64_t i = 0; i < I; ++i)
+            for (int64_t n = 0; n < d; ++n) {
+                double cg = 0.0, cu = 0.0;
+                for (int64_t t = 0; t < T; ++t) {
+                    cg += sug[t * I + i] * xa[t * d + n];
+                    cu += suu[t * I + i] * xa[t * d + n];
+                }
+                dsg[i * d + n] = (float)cg;
+                dsu[i * d + n] = (float)cu;
+            }
+#pragma omp parallel for schedule(static)
+        for (int64_t n = 0; n < d; ++n)
+            for (int64_t i = 0; i < I; ++i) {
+                double c = 0.0;
+                for (int64_t t = 0; t < T; ++t) c += sy[t * d + n] * sh_h[t * I + i];
+                dsd[n * I + i] = (float)c;
+            }
+    }
     free(ry);
     free(rh);
     free(rug);
@@ -690,6 +823,10 @@ void oracle_backward(const or_shape *sh, const void *x, const float *wr, const i
     free(suu);
     free(dl);
     free(xa);
+    free(ryr);
+    free(rraw);
+    free(syr);
+    free(sraw);
 }
 
 /* Threads an OpenMP region of this library uses (for reporting). */

@@ -333,13 +333,16 @@ __global__ __launch_bounds__(64) void k_pad_offsets(const int32_t *__restrict__ 
 
 // ------------------------------------------------------------ elementwise
 
-// out[e] = 0 (per elements each) for the groups with no rows.
+// out[e] = 0 (per elements each, per % 4 == 0) for the groups with no rows,
+// in 16-byte stores.
 __global__ __launch_bounds__(256) void k_zero_empty(int64_t per, const int32_t *__restrict__ off,
                                                     float *__restrict__ out) {
     const int e = blockIdx.y;
     if (off[e + 1] > off[e]) return;
-    float *o = out + (int64_t)e * per;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < per; i += (int64_t)gridDim.x * 256) o[i] = 0.f;
+    f32x4 *o = reinterpret_cast<f32x4 *>(out + (int64_t)e * per);
+    const int64_t n4 = per / 4;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+        o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // Per token t (one wave): dg_j = sum_n dy[t,n] y_perm[r_j,n] (r_j =
@@ -674,7 +677,7 @@ hipError_t launch_backward(const BackwardArgs &a, void *ws, hipStream_t s) {
             if (bf16_large_gemm_ok(g)) {
                 const hipError_t r = launch_bf16_large_gemm(g, s);
                 if (r != hipSuccess) return r;
-                hipLaunchKernelGGL(k_zero_empty, dim3(64, E), dim3(256), 0, s, (int64_t)M * N, a.offsets, out);
+                hipLaunchKernelGGL(k_zero_empty, dim3(256, E), dim3(256), 0, s, (int64_t)M * N, a.offsets, out);
                 return hipGetLastError();
             }
             BGemm p{};

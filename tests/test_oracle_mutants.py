@@ -52,8 +52,23 @@ BACKWARD_MUTANTS = [
      "dw[n * I + i] += ry[f * d + (n * I + i) % d] * rh[f * I + (n * I + i) / d % I];"),
     ("router input gradient dropped", "acc[n] += dl[t * k + j] * (double)wr[(int64_t)e * d + n];", "(void)e;"),
     ("shared input gradient dropped",
-     "ffn_row_backward(sh, shared, 0, a, dys, sh_h + t * I, sug + t * I, suu + t * I, da);\n        for (int64_t n = 0; n < d; ++n) acc[n] += da[n];",
-     "ffn_row_backward(sh, shared, 0, a, dys, sh_h + t * I, sug + t * I, suu + t * I, da);"),
+     "fp8 ? sraw + t * 3 * I : NULL);\n        for (int64_t n = 0; n < d; ++n) acc[n] += da[n];",
+     "fp8 ? sraw + t * 3 * I : NULL);"),
+]
+
+
+# mistakes in the e4m3 backward's quantisation points, against its pins
+FP8_BACKWARD_MUTANTS = [
+    ("weight gradient reads unquantised x", "quant_cols(gx, nr, d);", "(void)gx;"),
+    ("weight gradient reads unquantised h", "quant_cols(gh, nr, I);", "(void)gh;"),
+    ("weight-gradient groups of 64 rows",
+     "for (int64_t g0 = 0; g0 < n; g0 += 128) {\n        const int nr = (int)(n - g0 < 128 ? n - g0 : 128);",
+     "for (int64_t g0 = 0; g0 < n; g0 += 64) {\n        const int nr = (int)(n - g0 < 64 ? n - g0 : 64);"),
+    ("output gradient not quantised for the data gradient", "round_to_gemm_input(sh->wt, dyr, (int)d);",
+     "(void)0;"),
+    ("weight gradient reads the row-quantised output gradient",
+     "if (fp8)\n                for (int64_t n = 0; n < d; ++n) ryr[f * d + n] = dyr[n];\n            round_to_gemm_input(sh->wt, dyr, (int)d);",
+     "round_to_gemm_input(sh->wt, dyr, (int)d);\n            if (fp8)\n                for (int64_t n = 0; n < d; ++n) ryr[f * d + n] = dyr[n];"),
 ]
 
 
@@ -93,3 +108,9 @@ def test_pin_suite_catches_mutant(tmp_path, name, old, new):
                         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant '{name}' survived the pins:\n{r.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name,old,new", FP8_BACKWARD_MUTANTS, ids=[m[0] for m in FP8_BACKWARD_MUTANTS])
+def test_fp8_backward_pins_catch_mutant(tmp_path, name, old, new):
+    r = _run_pins(tmp_path, old, new, "test_oracle_backward_fp8_pins.py")
+    assert r.returncode != 0, f"mutant '{name}' survived the e4m3 backward pins:\n{r.stdout[-2000:]}"
