@@ -56,7 +56,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
-                    help="also time the layer backward (moe_backward, bf16) after the timed loop and report it")
+                    help="also time the layer backward (moe_backward: bf16 GEMMs, or e4m3 GEMMs with e4m3 weights) after the timed loop and report it")
     ap.add_argument("--fresh-batches", type=int, default=0,
                     help="N > 0: every step takes a new token batch (N batches resident in HBM, cycled); "
                          "default: the same batch every step")
@@ -226,7 +226,7 @@ def time_backward(cfg, layer, x, n):
     import torch
     from sparse_expert_routing_amd import _lib
     T, d, I, k, E = cfg.T, cfg.d, cfg.I, cfg.k, cfg.E
-    if cfg.act != "bf16" or cfg.wt != "bf16":
+    if cfg.act != "bf16" or cfg.wt not in ("bf16", "e4m3"):
         return None
     D = layer.desc
     stream = torch.cuda.current_stream()
@@ -254,9 +254,11 @@ def time_backward(cfg, layer, x, n):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
     flops = 16.0 * (T * k + T) * d * I + 4.0 * T * k * d
+    peak = PEAK_FP8_TFLOPS if cfg.wt == "e4m3" else PEAK_BF16_TFLOPS
     log(f"[bench] backward {ms:.3f} ms, {flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s algorithmic")
-    return {"ms": ms, "calls": n, "flops_per_call": flops, "tflops": flops / (ms * 1e-3) / 1e12,
-            "frac_of_bf16_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    return {"ms": ms, "calls": n, "gemm_dtype": cfg.wt, "flops_per_call": flops,
+            "tflops": flops / (ms * 1e-3) / 1e12, "peak_tflops": peak,
+            "frac_of_peak": flops / (ms * 1e-3) / 1e12 / peak}
 
 
 def measured_traffic():

@@ -232,8 +232,8 @@ size_t moe_workspace_bytes(const moe_desc_t *desc, int32_t stage);
 
 /*
  * Backward of the layer: the gradients of the layer output y for the
- * routing the forward chose, given dy = dL/dy (act = wt = bf16 only; other
- * types give MOE_ENOTSUP).  What is differentiated is the forward above
+ * routing the forward chose, given dy = dL/dy (act = bf16 with wt = bf16 or
+ * e4m3; other types give MOE_ENOTSUP).  What is differentiated is the forward above
  * (DeepSeek V3 From Scratch, "The idea", "In code"; Scaling Efficiency ...,
  * "Implementation: A Modular Look"):
  *   y = shared(x) + sum_j g_j * y_perm_j,  g_j = s_j / sum_i s_i over the
@@ -244,11 +244,18 @@ size_t moe_workspace_bytes(const moe_desc_t *desc, int32_t stage);
  * (g_j dy and dy) and the SwiGLU input gradients are rounded to bf16 as GEMM
  * inputs, like h in the forward; the expert pre-activations are recomputed;
  * accumulation is fp32.  Deterministic (no atomics).
+ * With e4m3 weights (crackai.dev DeepSeek-V3 summary, "How It Works": FP8
+ * in the backward pass too, a scale per tile) every backward GEMM takes e4m3
+ * operands quantised per 1x128 tile along its reduction: row tiles for the
+ * data gradients (against the weight blocks, transposed as blocks); for the
+ * weight gradients, each column of a group of 128 of an expert's rows
+ * (dispatch order; the shared expert: 128 consecutive tokens) is one tile,
+ * quantised from the fp32 values and the bf16 x.
  *   x          [T, d] bf16, the forward's input
  *   w_router   [E, d] fp32
  *   idx, weights [T, k]: from moe_route
  *   offsets, row_src, row_of: from moe_dispatch
- *   experts, shared: as for the forward (bf16)
+ *   experts, shared: as for the forward (bf16, or e4m3 with block scales)
  *   y_perm     [T*k, d] bf16: the forward's routed outputs (moe_expert_ffn)
  *   dy         [T, d] fp32
  * Outputs (fp32, written, not accumulated):
@@ -259,7 +266,8 @@ size_t moe_workspace_bytes(const moe_desc_t *desc, int32_t stage);
  *   memory: about (T*k + T)(6d + 18I) for the per-row intermediates, plus
  *   (T*k + 64E + T)(4d + 6I) for their K-contiguous transposes, plus
  *   6(E + 1)*I*d for the transposed weights and 64*E*d for the router
- *   partials (about 38 GiB at T=16384, d=7168, I=2048, E=256, k=8).
+ *   partials (about 38 GiB at T=16384, d=7168, I=2048, E=256, k=8; with
+ *   e4m3 weights about 31 GiB).
  * Requires d % 128 == 0 and I % 128 == 0.
  */
 moe_status_t moe_backward(const moe_desc_t *desc, const void *x, const float *w_router, const int32_t *idx,

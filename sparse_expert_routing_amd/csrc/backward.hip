@@ -32,6 +32,7 @@
 //   - k_bwd_dwr / k_bwd_dwr_sum: router weight gradient, each expert's rows
 //     summed in 16 ordered shares, the shares added in order;
 //   - k_bwd_dx: dx += shared input gradient + sum_j routed input gradients.
+#include "backward.h"
 #include "device.h"
 #include "kernels.h"
 
@@ -311,14 +312,15 @@ __global__ __launch_bounds__(256) void k_transpose(int R, int C, const uint16_t 
 }
 
 // Padded row positions: poff = exclusive scan of the group sizes rounded up
-// to 64 (one wave; 256 groups, 4 per lane).
+// to ALIGN (one wave; 256 groups, 4 per lane).
+template <int ALIGN>
 __global__ __launch_bounds__(64) void k_pad_offsets(const int32_t *__restrict__ off, int32_t *__restrict__ poff) {
     const int lane = threadIdx.x;
     int c[4], s = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = lane * 4 + i;
-        c[i] = (off[e + 1] - off[e] + 63) / 64 * 64;
+        c[i] = (off[e + 1] - off[e] + ALIGN - 1) / ALIGN * ALIGN;
         s += c[i];
     }
     const int incl = wave_incl_scan(s);
@@ -345,12 +347,20 @@ __global__ __launch_bounds__(256) void k_zero_empty(int64_t per, const int32_t *
         o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+// Stores two consecutive fp32 values as bf16 or fp32.
+template <bool F32>
+__device__ __forceinline__ void put2(void *base, int64_t i, float a, float b) {
+    if (F32) *reinterpret_cast<float2 *>(static_cast<float *>(base) + i) = float2{a, b};
+    else *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(base) + i) = pack_bf16x2(a, b);
+}
+
 // Per token t (one wave): dg_j = sum_n dy[t,n] y_perm[r_j,n] (r_j =
-// row_of[t*k+j]); dyp[r_j] = bf16(g_j dy[t]); dys[t] = bf16(dy[t]).
+// row_of[t*k+j]); dyp[r_j] = g_j dy[t]; dys[t] = dy[t] (bf16, or fp32 when F32).
+template <bool F32>
 __global__ __launch_bounds__(256) void k_bwd_combine(int T, int d, const float *__restrict__ dy,
                                                      const uint16_t *__restrict__ y_perm,
                                                      const int32_t *__restrict__ row_of, const float *__restrict__ g,
-                                                     uint16_t *__restrict__ dyp, uint16_t *__restrict__ dys,
+                                                     void *__restrict__ dyp, void *__restrict__ dys,
                                                      float *__restrict__ dg) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -366,12 +376,12 @@ __global__ __launch_bounds__(256) void k_bwd_combine(int T, int d, const float *
     }
     for (int n = lane * 2; n < d; n += 128) {
         const float2 v = *reinterpret_cast<const float2 *>(dyt + n);
-        *reinterpret_cast<uint32_t *>(dys + (int64_t)t * d + n) = pack_bf16x2(v.x, v.y);
+        put2<F32>(dys, (int64_t)t * d + n, v.x, v.y);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const uint32_t yp = *reinterpret_cast<const uint32_t *>(y_perm + (int64_t)r[j] * d + n);
             dot[j] += v.x * bf16_to_f32(yp & 0xffffu) + v.y * bf16_to_f32(yp >> 16);
-            *reinterpret_cast<uint32_t *>(dyp + (int64_t)r[j] * d + n) = pack_bf16x2(gw[j] * v.x, gw[j] * v.y);
+            put2<F32>(dyp, (int64_t)r[j] * d + n, gw[j] * v.x, gw[j] * v.y);
         }
     }
 #pragma unroll
@@ -384,19 +394,27 @@ __global__ __launch_bounds__(256) void k_bwd_combine(int T, int d, const float *
 }
 
 // From the pre-activations P [rows, 2I] (gate | up, fp32) and dh [rows, I]:
-// h = bf16(silu(a) b) [rows, I], and dab [rows, 2I] = (da | db) with
-// da = bf16(dh b sig(a) (1 + a (1 - sig(a)))), db = bf16(dh silu(a)).
+// h = silu(a) b [rows, I], and dab [rows, 2I] = (da | db) with
+// da = dh b sig(a) (1 + a (1 - sig(a))), db = dh silu(a); stored as bf16, or
+// fp32 when F32.
+template <bool F32>
+__device__ __forceinline__ void put1(void *base, int64_t i, float v) {
+    if (F32) static_cast<float *>(base)[i] = v;
+    else static_cast<uint16_t *>(base)[i] = (uint16_t)f32_to_bf16(v);
+}
+
+template <bool F32>
 __global__ __launch_bounds__(256) void k_bwd_swiglu(int64_t n, int I, const float *__restrict__ P,
-                                                    const float *__restrict__ dh, uint16_t *__restrict__ h,
-                                                    uint16_t *__restrict__ dab) {
+                                                    const float *__restrict__ dh, void *__restrict__ h,
+                                                    void *__restrict__ dab) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
     const int64_t row = i / I, c = i - row * I;
     const float a = P[row * 2 * I + c], b = P[row * 2 * I + I + c], g = dh[i];
     const float sg = 1.0f / (1.0f + expf(-a));
-    h[i] = (uint16_t)f32_to_bf16(a * sg * b);
-    dab[row * 2 * I + c] = (uint16_t)f32_to_bf16(g * b * sg * (1.0f + a * (1.0f - sg)));
-    dab[row * 2 * I + I + c] = (uint16_t)f32_to_bf16(g * a * sg);
+    put1<F32>(h, i, a * sg * b);
+    put1<F32>(dab, row * 2 * I + c, g * b * sg * (1.0f + a * (1.0f - sg)));
+    put1<F32>(dab, row * 2 * I + I + c, g * a * sg);
 }
 
 // Per token t (one workgroup): s_j = sigmoid(x_t . wr_{e_j}) in fp32, then
@@ -517,6 +535,61 @@ hipError_t bgemm(const BGemm &p, int G, hipStream_t s) {
 
 }  // namespace
 
+namespace bwd {
+
+hipError_t pad_offsets(const int32_t *off, int32_t *poff, int align, hipStream_t s) {
+    if (align == 128) hipLaunchKernelGGL(k_pad_offsets<128>, dim3(1), dim3(64), 0, s, off, poff);
+    else hipLaunchKernelGGL(k_pad_offsets<64>, dim3(1), dim3(64), 0, s, off, poff);
+    return hipGetLastError();
+}
+
+hipError_t combine(int T, int d, const float *dy, const uint16_t *y_perm, const int32_t *row_of, const float *g,
+                   void *dyp, void *dys, float *dg, bool f32_out, hipStream_t s) {
+    if (f32_out)
+        hipLaunchKernelGGL(k_bwd_combine<true>, dim3((T + 3) / 4), dim3(256), 0, s, T, d, dy, y_perm, row_of, g, dyp,
+                           dys, dg);
+    else
+        hipLaunchKernelGGL(k_bwd_combine<false>, dim3((T + 3) / 4), dim3(256), 0, s, T, d, dy, y_perm, row_of, g, dyp,
+                           dys, dg);
+    return hipGetLastError();
+}
+
+hipError_t swiglu(int64_t rows, int I, const float *P, const float *dh, void *h, void *dab, bool f32_out,
+                  hipStream_t s) {
+    const int64_t n = rows * I;
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (f32_out) hipLaunchKernelGGL(k_bwd_swiglu<true>, grid, dim3(256), 0, s, n, I, P, dh, h, dab);
+    else hipLaunchKernelGGL(k_bwd_swiglu<false>, grid, dim3(256), 0, s, n, I, P, dh, h, dab);
+    return hipGetLastError();
+}
+
+hipError_t router(int T, int d, const uint16_t *x, const float *wr, const int32_t *idx, const float *dg, float *dl,
+                  float *dx, hipStream_t s) {
+    hipLaunchKernelGGL(k_bwd_router, dim3(T), dim3(256), 0, s, T, d, x, wr, idx, dg, dl, dx);
+    return hipGetLastError();
+}
+
+size_t dwr_part_bytes(int d) { return (size_t)kDwrChunks * kE * d * 4; }
+
+hipError_t dwr(int d, const int32_t *offsets, const int32_t *row_src, const float *dl, const uint16_t *x,
+               float *part, float *dwr_out, hipStream_t s) {
+    hipLaunchKernelGGL(k_bwd_dwr, dim3((d + 255) / 256, kE, kDwrChunks), dim3(256), 0, s, d, offsets, row_src, dl, x,
+                       part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)kE * d;
+    hipLaunchKernelGGL(k_bwd_dwr_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n, part, dwr_out);
+    return hipGetLastError();
+}
+
+hipError_t dx(int T, int d, const float *dxs, const float *dxp, const int32_t *row_of, float *dx_out, hipStream_t s) {
+    const int64_t n = (int64_t)T * (d / 4);
+    hipLaunchKernelGGL(k_bwd_dx, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, T, d, dxs, dxp, row_of, dx_out);
+    return hipGetLastError();
+}
+
+}  // namespace bwd
+
 namespace {
 
 // The backward's workspace, carved in a fixed order (base == nullptr: sizes only).
@@ -556,7 +629,7 @@ BwdWs carve(char *base, int T, int d, int I, int k) {
     w.dl = reinterpret_cast<float *>(take(A * 4));
     w.dg = reinterpret_cast<float *>(take(A * 4));
     w.poff = reinterpret_cast<int32_t *>(take((kE + 1) * 4));
-    w.dwr_part = reinterpret_cast<float *>(take((size_t)16 * kE * d * 4));
+    w.dwr_part = reinterpret_cast<float *>(take(bwd::dwr_part_bytes(d)));
     w.wdT = reinterpret_cast<uint16_t *>(take((size_t)kE * I * d * 2));
     w.wguT = reinterpret_cast<uint16_t *>(take((size_t)kE * d * 2 * I * 2));
     w.sdT = reinterpret_cast<uint16_t *>(take((size_t)I * d * 2));
@@ -611,8 +684,7 @@ hipError_t launch_backward(const BackwardArgs &a, void *ws, hipStream_t s) {
     if ((e = (call)) != hipSuccess) return e;
 
     // 0. padded row positions of the expert groups; transposed weights
-    hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(64), 0, s, a.offsets, w.poff);
-    CHK(hipGetLastError());
+    CHK(bwd::pad_offsets(a.offsets, w.poff, 64, s));
     CHK(transpose(d, I, E, ed, I, (int64_t)d * I, nullptr, 1, nullptr, nullptr, d, w.wdT, d, (int64_t)I * d, 0, s));
     CHK(transpose(I, d, E, eg, d, (int64_t)I * d, nullptr, 1, nullptr, nullptr, I, w.wguT, 2 * I, (int64_t)d * 2 * I, 0,
                   s));
@@ -623,9 +695,8 @@ hipError_t launch_backward(const BackwardArgs &a, void *ws, hipStream_t s) {
     CHK(transpose(I, d, 1, su, d, 0, nullptr, 1, nullptr, nullptr, I, w.sguT, 2 * I, 0, I, s));
 
     // 1. combine backward
-    hipLaunchKernelGGL(k_bwd_combine, dim3((T + 3) / 4), dim3(256), 0, s, T, d, a.dy,
-                       static_cast<const uint16_t *>(a.y_perm), a.row_of, a.weights, w.dyo, dys, dg);
-    CHK(hipGetLastError());
+    CHK(bwd::combine(T, d, a.dy, static_cast<const uint16_t *>(a.y_perm), a.row_of, a.weights, w.dyo, dys, dg, false,
+                     s));
     // The data-gradient GEMMs (and the recompute) are NT GEMMs grouped over
     // M: the forward's persistent 256x256-tile kernel with an fp32 epilogue
     // when the groups are large enough, else k_bgemm.
@@ -649,12 +720,7 @@ hipError_t launch_backward(const BackwardArgs &a, void *ws, hipStream_t s) {
     CHK(nt(LargeGemmArgs{A, a.offsets, w.dyo, nullptr, 1, A, d, w.wdT, nullptr, I, w.dh, I, 0, false}, a.offsets, d));
     CHK(nt(LargeGemmArgs{T, nullptr, dys, nullptr, 1, T, d, w.sdT, nullptr, I, dhs, I, 0, false}, nullptr, d));
     // 4. SwiGLU backward (routed and shared rows in one pass)
-    {
-        const int64_t n = ((int64_t)A + T) * I;
-        hipLaunchKernelGGL(k_bwd_swiglu, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n, I, w.P, w.dh, w.h16,
-                           w.dab);
-        CHK(hipGetLastError());
-    }
+    CHK(bwd::swiglu((int64_t)A + T, I, w.P, w.dh, w.h16, w.dab, false, s));
     // 5. input gradients: (da | db) [rows, 2I] times (W_gate | W_up) transposed to [E, d, 2I]
     CHK(nt(LargeGemmArgs{A, a.offsets, w.dab, nullptr, 1, A, 2 * I, w.wguT, nullptr, d, w.dxi, d, 0, false}, a.offsets,
            2 * I));
@@ -705,24 +771,10 @@ hipError_t launch_backward(const BackwardArgs &a, void *ws, hipStream_t s) {
         CHK((bgemm<GROUP_NONE, false>(u, 1, s)));
     }
     // 7. router: dl and its share of dx (written), then the router gradient
-    hipLaunchKernelGGL(k_bwd_router, dim3(T), dim3(256), 0, s, T, d, x, a.w_router, a.idx, dg, w.dl, a.dx);
-    CHK(hipGetLastError());
-    hipLaunchKernelGGL(k_bwd_dwr, dim3((d + 255) / 256, E, kDwrChunks), dim3(256), 0, s, d, a.offsets, a.row_src,
-                       w.dl, x, w.dwr_part);
-    CHK(hipGetLastError());
-    {
-        const int64_t n = (int64_t)E * d;
-        hipLaunchKernelGGL(k_bwd_dwr_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n, w.dwr_part,
-                           a.dw_router);
-        CHK(hipGetLastError());
-    }
+    CHK(bwd::router(T, d, x, a.w_router, a.idx, dg, w.dl, a.dx, s));
+    CHK(bwd::dwr(d, a.offsets, a.row_src, w.dl, x, w.dwr_part, a.dw_router, s));
     // 8. dx += shared + routed input gradients
-    {
-        const int64_t n = (int64_t)T * (d / 4);
-        hipLaunchKernelGGL(k_bwd_dx, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, T, d, dxs, w.dxi, a.row_of,
-                           a.dx);
-        CHK(hipGetLastError());
-    }
+    CHK(bwd::dx(T, d, dxs, w.dxi, a.row_of, a.dx, s));
 #undef CHK
     return hipSuccess;
 }

@@ -140,5 +140,9 @@ struct BackwardArgs {
 size_t backward_ws_bytes(int T, int d, int I, int k);
 bool backward_ok(int d, int I);
 hipError_t launch_backward(const BackwardArgs &a, void *ws, hipStream_t s);
+// The same with e4m3 expert weights (128x128 block scales): every backward
+// GEMM on e4m3 operands (csrc/backward_fp8.hip).
+size_t backward_fp8_ws_bytes(int T, int d, int I, int k);
+hipError_t launch_backward_fp8(const BackwardArgs &a, void *ws, hipStream_t s);
 
 }  // namespace moe

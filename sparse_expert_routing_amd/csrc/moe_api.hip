@@ -66,9 +66,10 @@ size_t route_ws(const moe_desc_t *d) {
 // The shared expert + combine: h (+ scales), x quantised (e4m3), and fp32
 // split-K partials at small T (bf16).
 size_t backward_ws(const moe_desc_t *d) {
-    return d->act == MOE_BF16 && d->wt == MOE_BF16 && moe::backward_ok(d->d, d->I)
-               ? align_up(moe::backward_ws_bytes(d->T, d->d, d->I, d->k))
-               : 0;
+    if (d->act != MOE_BF16 || !moe::backward_ok(d->d, d->I)) return 0;
+    if (d->wt == MOE_BF16) return align_up(moe::backward_ws_bytes(d->T, d->d, d->I, d->k));
+    if (d->wt == MOE_E4M3) return align_up(moe::backward_fp8_ws_bytes(d->T, d->d, d->I, d->k));
+    return 0;
 }
 
 size_t combine_ws(const moe_desc_t *d) {
@@ -275,7 +276,8 @@ moe_status_t moe_backward(const moe_desc_t *d, const void *x, const float *w_rou
                           void *stream) {
     moe_status_t st = check_desc(d);
     if (st != MOE_OK) return st;
-    if (d->act != MOE_BF16 || d->wt != MOE_BF16 || !moe::backward_ok(d->d, d->I)) return MOE_ENOTSUP;
+    if (d->act != MOE_BF16 || (d->wt != MOE_BF16 && d->wt != MOE_E4M3) || !moe::backward_ok(d->d, d->I))
+        return MOE_ENOTSUP;
     if (!x || !w_router || !idx || !weights || !offsets || !row_src || !row_of || !y_perm || !dy || !dx ||
         !dw_router || !dw_gate || !dw_up || !dw_down || !ds_gate || !ds_up || !ds_down ||
         !ffn_weights_ok(experts, d->wt) || !ffn_weights_ok(shared, d->wt))
@@ -306,7 +308,9 @@ moe_status_t moe_backward(const moe_desc_t *d, const void *x, const float *w_rou
     a.ds_up = ds_up;
     a.ds_down = ds_down;
     a.dg = dg;
-    return hip_status(moe::launch_backward(a, workspace, static_cast<hipStream_t>(stream)));
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    return hip_status(d->wt == MOE_E4M3 ? moe::launch_backward_fp8(a, workspace, hs)
+                                        : moe::launch_backward(a, workspace, hs));
 }
 
 }  // extern "C"

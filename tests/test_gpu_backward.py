@@ -35,14 +35,14 @@ def skewed_ids(T, seed):
     return np.ascontiguousarray(np.concatenate([np.tile(np.arange(3, dtype=np.int32), (T, 1)), tail], axis=1))
 
 
-def run_case(T, d, I, kind, seed):
-    cfg = synth.Config("bwd", seed=seed, T=T, d=d, I=I)
-    say(f"[backward] T={T} d={d} I={I} {kind}")
+def run_case(T, d, I, kind, seed, wt="bf16"):
+    cfg = synth.Config("bwd", seed=seed, T=T, d=d, I=I, wt=wt)
+    say(f"[backward] T={T} d={d} I={I} {kind} {wt}")
     x, wr, bias = synth.make_router(cfg)
     experts = synth.make_ffn(cfg, 256, (synth.TID_GATE, synth.TID_UP, synth.TID_DOWN))
     shared = synth.make_ffn(cfg, 1, (synth.TID_SGATE, synth.TID_SUP, synth.TID_SDOWN))
     dy = synth.normal(seed, synth.TID_AUX, (T, d), 1.0, "f32")
-    ds = _lib.desc(T, d, 256, 8, I, "bf16", "bf16")
+    ds = _lib.desc(T, d, 256, 8, I, "bf16", wt)
     xd, wrd = dev(x), dev(wr)
     idx, g = empty((T, 8), torch.int32), empty((T, 8), torch.float32)
     ws = empty(max(_lib.workspace_bytes(ds, s) for s in range(5)), torch.uint8)
@@ -59,8 +59,9 @@ def run_case(T, d, I, kind, seed):
     _lib.moe_dispatch(ds, idx, None, counts, offsets, row_src, row_of, None, None, ws)
     ew = {n: dev(a) for n, a in experts.items() if a is not None}
     sw = {n: dev(a) for n, a in shared.items() if a is not None}
-    efw = _lib.ffn_weights(ew["gate"], ew["up"], ew["down"])
-    sfw = _lib.ffn_weights(sw["gate"], sw["up"], sw["down"])
+    names = ("gate", "up", "down", "s_gate", "s_up", "s_down")
+    efw = _lib.ffn_weights(*(ew.get(n) for n in names))
+    sfw = _lib.ffn_weights(*(sw.get(n) for n in names))
     y_perm = empty((T * 8, d), torch.int16)
     _lib.moe_expert_gate_up_rows(ds, xd, row_src, offsets, efw, ws)
     _lib.moe_expert_down(ds, offsets, efw, y_perm, ws)
@@ -81,8 +82,8 @@ def run_case(T, d, I, kind, seed):
         assert np.isfinite(a).all(), f"{n}: unwritten or non-finite elements"
         err = max_rel(a, o[ORACLE_NAME[n]])
         worst = max(worst, err)
-        assert err <= TOL["bf16"], f"{n}: max rel err {err:.3e}"
-    say(f"[backward] T={T} {kind}: worst max rel err {worst:.3e} over {len(GRADS)} gradients")
+        assert err <= TOL[wt], f"{n}: max rel err {err:.3e}"
+    say(f"[backward] T={T} {kind} {wt}: worst max rel err {worst:.3e} over {len(GRADS)} gradients")
 
 
 @pytest.mark.parametrize("T,d,I,kind,seed", [(300, 512, 256, "routed", 41), (1, 256, 128, "routed", 42),
@@ -94,23 +95,34 @@ def test_backward_matches_oracle(T, d, I, kind, seed):
     run_case(T, d, I, kind, seed)
 
 
+@pytest.mark.parametrize("T,d,I,kind,seed", [(300, 512, 256, "routed", 51), (1, 256, 128, "routed", 52),
+                                             (257, 256, 384, "skewed", 53),
+                                             # experts 0-2 with 4096 rows: 32 weight-gradient groups each
+                                             (4096, 512, 256, "skewed", 55)])
+def test_backward_e4m3_matches_oracle(T, d, I, kind, seed):
+    """Every backward GEMM on e4m3 operands (tiles along each GEMM's
+    reduction), against the oracle's e4m3 backward at the fp8 tolerance."""
+    run_case(T, d, I, kind, seed, wt="e4m3")
+
+
 def test_backward_rejects_other_types():
     ds = _lib.desc(32, 256, 256, 8, 64, "f32", "f32")
     assert _lib.workspace_bytes(ds, _lib.MOE_WS_BACKWARD) == 0
 
 
 @pytest.mark.timeout(400)
-def test_backward_full_size_sampled():
-    """The skewed prefill workload at full size (T=16384, d=7168, I=2048, bf16),
-    routed by the forward on the GPU, backward in the launch configuration
-    bench.py --backward times.  The oracle checks dx and dg on 8 sampled tokens
+@pytest.mark.parametrize("cid", [4, 5])
+def test_backward_full_size_sampled(cid):
+    """The skewed prefill workload (bf16) and the fp8 prefill workload (e4m3
+    weights) at full size (T=16384, d=7168, I=2048), routed by the forward on
+    the GPU, backward in the launch configuration bench.py --backward times.  The oracle checks dx and dg on 8 sampled tokens
     (both are per-token), and the weight gradients (dW gate/up/down and the
     router row) of two experts -- the coldest one and one with about 100 rows --
     from exactly the tokens that chose them; every gradient must be finite."""
     from sparse_expert_routing_amd.layer import layer_from_inputs, upload
-    cfg = synth.CONFIGS[4]
+    cfg = synth.CONFIGS[cid]
     T, d, I = cfg.T, cfg.d, cfg.I
-    say(f"[backward] full size T={T} d={d} I={I}: inputs + forward")
+    say(f"[backward] full size {cfg.name}: inputs + forward")
     inp = synth.make_inputs(cfg)
     layer = layer_from_inputs(inp)
     x = upload(inp["x"])
@@ -144,7 +156,7 @@ def test_backward_full_size_sampled():
     for n in ("dx", "dg"):
         err = max_rel(host(grads[n][torch.from_numpy(toks).cuda()]), o[n])
         say(f"[backward] full size: {n} max rel err {err:.3e}")
-        assert err <= TOL["bf16"], (n, err)
+        assert err <= TOL[cfg.wt], (n, err)
     nz = np.flatnonzero(counts > 0)
     cold = int(nz[np.argmin(counts[nz])])
     mid = int(np.argmin(np.abs(counts.astype(np.int64) - 100)))
@@ -156,4 +168,4 @@ def test_backward_full_size_sampled():
         for n, on in (("dw_gate", "dwg"), ("dw_up", "dwu"), ("dw_down", "dwd"), ("dw_router", "dwr")):
             err = max_rel(host(grads[n][e]), o[on][0])
             say(f"[backward] full size: expert {e} {n} max rel err {err:.3e}")
-            assert err <= TOL["bf16"], (e, n, err)
+            assert err <= TOL[cfg.wt], (e, n, err)
