@@ -18,6 +18,9 @@
 //   - the router, the combine backward and the dx assembly stay fp32 (the
 //     steps shared with the bf16 backward).
 //
+// The M-grouped and plain products with block-scaled weights (the recompute
+// and the data gradients) run on the forward's persistent e4m3 kernel with an
+// fp32 epilogue when the shape fits it.
 // k_fgemm: C = A B^T with both operands K-contiguous e4m3 codes, 128x128
 // tiles, one 128-wide scale block per stage (two v_mfma 32x32x64 fp8 per
 // 32x32 block), each stage's fp32 partial folded into the accumulator times
@@ -108,7 +111,7 @@ __device__ __forceinline__ i32x8 frag8(const uint8_t *tile, int row, int hf, int
 }
 
 template <int GROUP>
-__global__ __launch_bounds__(256) void k_fgemm(FGemm p) {
+__global__ __launch_bounds__(256, 2) void k_fgemm(FGemm p) {
     __shared__ __attribute__((aligned(16))) uint8_t sA[2][FM * FK];
     __shared__ __attribute__((aligned(16))) uint8_t sB[2][FN * FK];
     __shared__ float sAs[2][FM], sBs[2][FN];
@@ -397,33 +400,37 @@ __global__ __launch_bounds__(256) void k_q8_cols(int R, const void *__restrict__
 }
 
 // e4m3 codes transposed per group: out[g][c*ldo + coff + r] = in[g][r*C + c]
-// (R, C multiples of 64), through 64x64-byte LDS tiles.
+// (R, C multiples of 64), 64x64-byte tiles.  Thread (a, b) reads the 4x4
+// block of rows 4a.. and bytes 4b.. (each row's 16 threads read 64
+// contiguous bytes), transposes it in registers and stages the four words
+// in LDS as output row 4b + j, word a; then each thread stores 16 bytes of
+// one output row.
 __global__ __launch_bounds__(256) void k_t8(int R, int C, const uint8_t *__restrict__ in, int64_t gin,
                                             uint8_t *__restrict__ out, int64_t ldo, int64_t gout, int coff) {
-    __shared__ uint8_t tile[64][64 + 4];
+    __shared__ uint32_t tile[64][17];
     const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64, g = blockIdx.z, tid = threadIdx.x;
     in += (int64_t)g * gin;
     out += (int64_t)g * gout;
     {
-        const int rr = tid >> 2, cc = (tid & 3) * 16;
-        const i32x4 v = *reinterpret_cast<const i32x4 *>(in + (int64_t)(r0 + rr) * C + c0 + cc);
+        const int a = tid >> 4, b = tid & 15;
+        uint32_t v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
+            v[i] = *reinterpret_cast<const uint32_t *>(in + (int64_t)(r0 + 4 * a + i) * C + c0 + 4 * b);
+        // word j of the transposed block: byte j of rows 0..3
 #pragma unroll
-            for (int b = 0; b < 4; ++b) tile[rr][cc + 4 * i + b] = (uint8_t)(((uint32_t)v[i] >> (8 * b)) & 0xffu);
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t w = ((v[0] >> (8 * j)) & 0xffu) | (((v[1] >> (8 * j)) & 0xffu) << 8) |
+                               (((v[2] >> (8 * j)) & 0xffu) << 16) | (((v[3] >> (8 * j)) & 0xffu) << 24);
+            tile[4 * b + j][a] = w;
+        }
     }
     __syncthreads();
     {
-        const int cc = tid >> 2, rq = (tid & 3) * 16;
-        i32x4 v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t w = 0;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) w |= (uint32_t)tile[rq + 4 * i + b][cc] << (8 * b);
-            v[i] = (int)w;
-        }
-        *reinterpret_cast<i32x4 *>(out + (int64_t)(c0 + cc) * ldo + coff + r0 + rq) = v;
+        const int c = tid >> 2, q = tid & 3;
+        const i32x4 v = i32x4{(int)tile[c][4 * q], (int)tile[c][4 * q + 1], (int)tile[c][4 * q + 2],
+                              (int)tile[c][4 * q + 3]};
+        *reinterpret_cast<i32x4 *>(out + (int64_t)(c0 + c) * ldo + coff + r0 + 16 * q) = v;
     }
 }
 
@@ -580,6 +587,19 @@ hipError_t launch_backward_fp8(const BackwardArgs &a, void *ws, hipStream_t s) {
 
     FGemm base{};
     base.bdiv = 128;
+    // M-grouped (routed) or plain products with row-quantised A and
+    // block-scaled B: the forward's persistent e4m3 kernel when the shape
+    // fits it, else k_fgemm
+    auto mg = [&](const FGemm &p, bool routed) -> hipError_t {
+        Fp8GemmArgs g{};
+        g.M = p.M; g.offsets = routed ? p.offsets : nullptr; g.A = p.A; g.As = p.As; g.a_rows = p.a_rows;
+        g.a_div = p.a_div; g.a_src_rows = T; g.K = p.K; g.B = p.B; g.Bs = p.Bs; g.N = p.N; g.out = p.C; g.ldo = (int)p.ldc;
+        if (p.lda == p.K && p.ldas == p.K / FK && p.ldb == p.K && p.ldbs == p.K / FK && p.bdiv == 128 &&
+            (!routed || (p.bstride == (int64_t)p.N * p.K && p.bsstride == (int64_t)(p.N / 128) * (p.K / FK))) &&
+            fp8_large_gemm_ok(g))
+            return launch_fp8_large_gemm(g, s);
+        return routed ? fgemm<FG_M>(p, s) : fgemm<FG_NONE>(p, s);
+    };
     // 2. pre-activations, as the forward forms them: routed rows gather the
     //    quantised x through row_src; gate into columns 0..I, up into I..2I
     for (int half = 0; half < 2; ++half) {
@@ -589,12 +609,12 @@ hipError_t launch_backward_fp8(const BackwardArgs &a, void *ws, hipStream_t s) {
         p.B = static_cast<const uint8_t *>(half ? ex.up : ex.gate); p.ldb = d; p.bstride = (int64_t)I * d;
         p.Bs = half ? ex.s_up : ex.s_gate; p.ldbs = d / 128; p.bsstride = (int64_t)(I / 128) * (d / 128);
         p.C = w.P + (half ? I : 0); p.ldc = 2 * I;
-        CHK(fgemm<FG_M>(p, s));
+        CHK(mg(p, true));
         FGemm q = p;
         q.M = T; q.offsets = nullptr; q.a_rows = nullptr; q.a_div = 1;
         q.B = static_cast<const uint8_t *>(half ? sh.up : sh.gate); q.Bs = half ? sh.s_up : sh.s_gate;
         q.C = Ps + (half ? I : 0);
-        CHK(fgemm<FG_NONE>(q, s));
+        CHK(mg(q, false));
     }
     // 3. dh = Q(output gradient) W_down: rows per 1x128 tile of d; W_down as [E, I, d] blocks
     CHK(q8_rows<false>((int64_t)A + T, d, w.dyo, d, w.dyq, w.dyqs, s));
@@ -605,11 +625,11 @@ hipError_t launch_backward_fp8(const BackwardArgs &a, void *ws, hipStream_t s) {
         p.B = w.wdT; p.ldb = d; p.bstride = (int64_t)I * d;
         p.Bs = w.wdTs; p.ldbs = d / 128; p.bsstride = (int64_t)(I / 128) * (d / 128);
         p.C = w.dh; p.ldc = I;
-        CHK(fgemm<FG_M>(p, s));
+        CHK(mg(p, true));
         FGemm q = p;
         q.M = T; q.offsets = nullptr; q.A = w.dyq + (int64_t)A * d; q.As = w.dyqs + (int64_t)A * (d / 128);
         q.B = w.sdT; q.Bs = w.sdTs; q.C = dhs;
-        CHK(fgemm<FG_NONE>(q, s));
+        CHK(mg(q, false));
     }
     // 4. SwiGLU backward in fp32 (routed and shared rows in one pass)
     CHK(bwd::swiglu((int64_t)A + T, I, w.P, w.dh, w.h, w.dab, true, s));
@@ -622,11 +642,11 @@ hipError_t launch_backward_fp8(const BackwardArgs &a, void *ws, hipStream_t s) {
         p.B = w.wguT; p.ldb = 2 * I; p.bstride = (int64_t)d * 2 * I;
         p.Bs = w.wguTs; p.ldbs = 2 * I / 128; p.bsstride = (int64_t)(d / 128) * (2 * I / 128);
         p.C = w.dxi; p.ldc = d;
-        CHK(fgemm<FG_M>(p, s));
+        CHK(mg(p, true));
         FGemm q = p;
         q.M = T; q.offsets = nullptr; q.A = w.dabq + (int64_t)A * 2 * I; q.As = w.dabqs + (int64_t)A * (2 * I / 128);
         q.B = w.sguT; q.Bs = w.sguTs; q.C = dxs;
-        CHK(fgemm<FG_NONE>(q, s));
+        CHK(mg(q, false));
     }
     // 6. weight gradients: every operand column-quantised over 128-row groups
     //    of the expert's rows (positions poff), then K-grouped GEMMs

@@ -50,7 +50,11 @@ constexpr int NUNIT = 5;     // LDS ring units (5 x 32 KB)
 constexpr int UNIT_BYTES = LM * LK;
 constexpr int kGroupM = 8;   // row tiles per ordering group
 
-enum { EPI_SWIGLU_Q = 0, EPI_STORE = 1, EPI_COMBINE = 2 };
+// EPI_F32: a plain fp32 product (the layer backward's GEMMs), row stride ldo.
+enum { EPI_SWIGLU_Q = 0, EPI_STORE = 1, EPI_COMBINE = 2, EPI_F32 = 3 };
+// A buffer-store offset past the end of every fp32 output (the host keeps
+// them below kOobOff - 1 MB): stores of padding rows are dropped.
+constexpr uint32_t kOobOff = 0xFFFF0000u;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef int i32x2 __attribute__((ext_vector_type(2)));
@@ -70,7 +74,8 @@ struct F8Params {
     float *hs;                // EPI_SWIGLU_Q: [M, H/128]
     int H;                    // EPI_SWIGLU_Q: h columns (= N)
     uint16_t *out;            // EPI_STORE: bf16 [M, N]
-    float *yout;              // EPI_COMBINE: f32 [M, N]
+    float *yout;              // EPI_COMBINE: f32 [M, N]; EPI_F32: f32 rows of ldo
+    int ldo;                  // EPI_F32
     const uint16_t *y_perm;   // EPI_COMBINE: routed outputs [M*k, N] bf16
     const int32_t *row_of;    // EPI_COMBINE: [M*k]
     const float *cw;          // EPI_COMBINE: combine weights [M*k]
@@ -416,6 +421,24 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_large(F8Params p) {
                                                               0, 0);
                     }
             }
+        } else if constexpr (EPI == EPI_F32) {
+            // one 16-byte store per run of 4 columns; padding rows go to kOobOff
+            const __amdgpu_buffer_rsrc_t rOutF = buf_rsrc(p.yout, (uint32_t)p.M * (uint32_t)p.ldo * 4u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = m0 + wm * 128 + 32 * i + (lane & 31);
+                const uint32_t obase = row < m_end ? ((uint32_t)row * (uint32_t)p.ldo + (uint32_t)n0) * 4u : kOobOff;
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int col = wn * 64 + j * 32 + 8 * q + c4;
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            i32x4{__float_as_int(acc[i][j][4 * q]), __float_as_int(acc[i][j][4 * q + 1]),
+                                  __float_as_int(acc[i][j][4 * q + 2]), __float_as_int(acc[i][j][4 * q + 3])},
+                            rOutF, obase + (uint32_t)col * 4u, 0, 0);
+                    }
+            }
         } else {
             // four 64-row chunks of the fp32 tile through LDS (the ring is
             // free), then each half-wave gathers one routed output row as a
@@ -501,6 +524,35 @@ bool ffn_fp8_large_ok(const FfnArgs &a) {
                       (unsigned long long)a.M * a.d * 4 < lim && (unsigned long long)a.I * a.d < lim;
     return fits && (long long)a.M >= 128LL * groups && a.I % 128 == 0 && a.d % 256 == 0 && a.d % LK == 0 &&
            a.I % LK == 0;
+}
+
+bool fp8_large_gemm_ok(const Fp8GemmArgs &g) {
+    const int groups = g.offsets ? kE : 1;
+    const unsigned long long lim = 1ULL << 32;
+    const unsigned long long a_rows = g.a_rows ? (unsigned long long)g.a_src_rows : (unsigned long long)g.M;
+    return (long long)g.M >= 128LL * groups && g.N % LB == 0 && g.K % LK == 0 && a_rows * g.K < lim &&
+           a_rows * (g.K / LK) * 4 < lim && (unsigned long long)g.N * g.K < lim &&
+           (unsigned long long)g.M * g.ldo * 4 < kOobOff - (1ULL << 20) && g.ldo >= g.N;
+}
+
+hipError_t launch_fp8_large_gemm(const Fp8GemmArgs &g, hipStream_t s) {
+    const int P = (cu_count() / 8) * 8;
+    F8Params p{};
+    p.M = g.M;
+    p.offsets = g.offsets;
+    p.A = g.A;
+    p.As = g.As;
+    p.a_rows = g.a_rows;
+    p.a_div = g.a_rows ? g.a_div : 1;
+    p.K = g.K;
+    p.B0 = g.B;
+    p.S0 = g.Bs;
+    p.N = g.N;
+    p.yout = g.out;
+    p.ldo = g.ldo;
+    if (g.offsets) hipLaunchKernelGGL((k_gemm_fp8_large<EPI_F32, true>), dim3(P), dim3(512), 0, s, p);
+    else hipLaunchKernelGGL((k_gemm_fp8_large<EPI_F32, false>), dim3(P), dim3(512), 0, s, p);
+    return hipGetLastError();
 }
 
 // Phase 1 (gate/up, fused SwiGLU + h quantisation) and / or phase 2 (down:

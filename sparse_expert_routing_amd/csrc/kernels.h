@@ -116,6 +116,28 @@ struct LargeGemmArgs {
 };
 bool bf16_large_gemm_ok(const LargeGemmArgs &g);
 hipError_t launch_bf16_large_gemm(const LargeGemmArgs &g, hipStream_t s);
+
+// An e4m3 NT product on the persistent fp8 kernel with an fp32 output:
+// out[m*ldo + n] = sum_kb s_a(m, kb) s_b(n/128, kb) sum_k A(m,k) B(n,k), A rows
+// per 1x128 tile (As [rows, K/128]), B [G, N, K] with 128x128 block scales
+// Bs [G, N/128, K/128]; grouped over M by offsets (B per group) or one group.
+struct Fp8GemmArgs {
+    int M;
+    const int32_t *offsets;
+    const uint8_t *A;
+    const float *As;
+    const int32_t *a_rows;  // optional: row m reads row a_rows[m] / a_div of A / As
+    int a_div;
+    int a_src_rows;         // rows of A when a_rows is given
+    int K;
+    const uint8_t *B;
+    const float *Bs;
+    int N;
+    float *out;
+    int ldo;
+};
+bool fp8_large_gemm_ok(const Fp8GemmArgs &g);
+hipError_t launch_fp8_large_gemm(const Fp8GemmArgs &g, hipStream_t s);
 // Large-group e4m3 path (persistent 256x256 tiles, fp32 promotion per 128 of K).
 bool ffn_fp8_large_ok(const FfnArgs &a);
 hipError_t launch_ffn_fp8_large(const FfnArgs &a, hipStream_t s);
