@@ -151,6 +151,8 @@ def main():
     names = ["route", "dispatch", "expert_gate_up", "expert_down", "combine", "bias_update"]
     phase = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(K)]))
              for i, n in enumerate(names)}
+    # per-step device time (first to last event of a step): mean, median, extremes
+    step_dev = np.array([events[s][0].elapsed_time(events[s][6]) for s in range(K)])
     ch = counts_hist.cpu().numpy().astype(np.float64)
     imb = ch.max(axis=1) / ch.mean(axis=1)
     tiles = np.ceil(ch / 256.0).sum(axis=1)  # launched 256-row tiles of the routed GEMMs
@@ -206,6 +208,9 @@ def main():
                      "flops_per_launch": gate_up_flops, "bytes_per_launch": gate_up_bytes,
                      "touched_experts": touched, "avg_launch_ms": gate_up_ms},
         "phases_ms": phase,
+        "step_ms_device": {"mean": float(step_dev.mean()), "median": float(np.median(step_dev)),
+                           "min": float(step_dev.min()), "max": float(step_dev.max())},
+        "phase_roofline": phase_roofline(cfg, phase),
         "layer_tflops": total_flops / (ms_step * 1e-3) / 1e12,
         "imbalance_max_over_mean": {"first": float(imb[0]), "last": float(imb[-1])},
         "routed_row_tiles_mean": float(tiles.mean()),
@@ -216,6 +221,27 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def phase_roofline(cfg, phase):
+    """Route, dispatch and bias update against the HBM peak over the bytes
+    they must move (and the router's FLOPs): route reads x and W_r once and
+    writes idx and the weights; dispatch (the GEMM gathers x itself) reads
+    idx and writes counts, offsets, row_src and row_of; the bias update reads
+    the counts and reads and writes the bias."""
+    T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
+    xb = 4 if cfg.act == "f32" else 2
+    b = {"route": T * d * xb + E * d * 4 + T * k * 8,
+         "dispatch": T * k * 4 + E * 4 + (E + 1) * 4 + 2 * T * k * 4,
+         "bias_update": E * 4 + 2 * E * 4}
+    out = {}
+    for n, nb in b.items():
+        ms = phase[n]
+        out[n] = {"bytes": nb, "gbs": nb / (ms * 1e-3) / 1e9, "frac_of_hbm": nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    fl = 2.0 * T * d * E
+    out["route"]["flops"] = fl
+    out["route"]["tflops"] = fl / (phase["route"] * 1e-3) / 1e12
+    return out
 
 
 def time_backward(cfg, layer, x, n):
@@ -300,9 +326,18 @@ def cpu_baseline(cfg, inp, target_s):
     n = max(cores, (n // cores) * cores)
     log(f"[bench] oracle: {n0} tokens in {t0:.2f}s; timing {n} tokens on {cores} threads")
     t = run(n)
+    # the same on one core, on a few tokens (about 3 s)
+    n1 = max(2, min(n, round(3.0 / max(t0 * cores / n0, 1e-3))))
+    oracle.set_threads(1)
+    try:
+        t1 = run(n1)
+    finally:
+        oracle.set_threads(cores)
+    log(f"[bench] oracle on 1 core: {n1} tokens in {t1:.2f}s")
     return {"value": n / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} of the {cfg.T} tokens (every {cfg.T // n}th) through route + 8 routed experts + "
-                      f"shared expert + combine in fp64; {t:.1f}s"}
+                      f"shared expert + combine in fp64; {t:.1f}s",
+            "value_1core": n1 / t1, "sample_1core": f"{n1} tokens (every {cfg.T // n1}th) on 1 thread; {t1:.1f}s"}
 
 
 if __name__ == "__main__":

@@ -83,6 +83,8 @@ def lib():
         L.oracle_e4m3_encode.restype = ctypes.c_uint8
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_threads.argtypes = [ctypes.c_int32]
+        L.oracle_set_threads.restype = None
         _lib = L
     return _lib
 
@@ -110,6 +112,11 @@ def ffn(w: dict):
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads the oracle's later parallel regions use (from this thread)."""
+    lib().oracle_set_threads(int(n))
 
 
 def route(sh: Shape, x, wr, bias, tokens=None, want_s=False):

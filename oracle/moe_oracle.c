@@ -829,6 +829,9 @@ void oracle_backward(const or_shape *sh, const void *x, const float *wr, const i
     free(sraw);
 }
 
+/* Threads later OpenMP regions of this library use (from the calling thread). */
+void oracle_set_threads(int32_t n) { omp_set_num_threads(n > 0 ? n : 1); }
+
 /* Threads an OpenMP region of this library uses (for reporting). */
 int oracle_num_threads(void) {
     int n = 1;
