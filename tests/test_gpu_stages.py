@@ -121,12 +121,15 @@ def ids_case(kind, T):
     return np.ascontiguousarray(np.concatenate([np.tile(np.arange(3, dtype=np.int32), (T, 1)), tail], axis=1))
 
 
-@pytest.mark.parametrize("T", [1, 255, 256, 257, 1000, 4096])
+# random routings at every size; the degenerate ones (all tokens on the same
+# 8 experts, three hot experts) at two sizes
+DISPATCH_CASES = [(kind, T) for kind in ("random", "same8", "skewed")
+                  for T in ((1, 255, 256, 257, 1000, 4096) if kind == "random" else (257, 1000))]
+
+
+@pytest.mark.parametrize("kind,T", DISPATCH_CASES)
 @pytest.mark.parametrize("act,wt,d", [("f32", "f32", 256), ("bf16", "bf16", 512), ("bf16", "e4m3", 384)])
-@pytest.mark.parametrize("kind", ["random", "same8", "skewed"])
 def test_dispatch_bit_exact(T, act, wt, d, kind):
-    if kind != "random" and T not in (257, 1000):
-        pytest.skip("degenerate routings on two sizes only")
     say(f"[dispatch] T={T} d={d} {act}/{wt} {kind}")
     idx = ids_case(kind, T)
     x = synth.normal(7, synth.TID_X, (T, d), 1.0, act)
