@@ -81,7 +81,10 @@ typedef struct {
  * gate, up: [G, I, d]; down: [G, d, I] (each row contiguous along the reduced
  * dimension).  For e4m3 the fp32 scales hold one value per 128x128 block:
  * s_gate, s_up: [G, I/128, d/128]; s_down: [G, d/128, I/128]; the value of an
- * element is code * scale.  Scales are NULL for fp32 and bf16. */
+ * element is code * scale.  Each scale must be a power of two (2^-126 ..
+ * 2^127): the expert GEMMs apply it as the exponent the block-scaled MFMA
+ * takes (other values give wrong products).  Scales are NULL for fp32 and
+ * bf16. */
 typedef struct {
     const void *gate, *up, *down;
     const float *s_gate, *s_up, *s_down;
@@ -129,8 +132,9 @@ moe_status_t moe_route(const moe_desc_t *desc, const void *x, const float *w_rou
  *   row_of       [T*k]    int32 out: the inverse, permuted row of assignment t*k + j
  *   x_perm       [T*k, d] out, in the expert GEMM input type: row r = x[row_src[r] / k];
  *                         for e4m3 the row is quantised per 1x128 tile:
- *   x_perm_scale [T*k, d/128] fp32 out (e4m3 only, else NULL): scale = amax/448
- *                         (1 for an all-zero tile), code = e4m3_rne_sat(v / scale)
+ *   x_perm_scale [T*k, d/128] fp32 out (e4m3 only, else NULL): scale = the smallest
+ *                         power of two at or above amax/448 (1 for an all-zero
+ *                         tile), code = e4m3_rne_sat(v / scale)
  *   workspace    >= moe_workspace_bytes(desc, MOE_WS_DISPATCH) bytes of device memory
  * x_perm may be NULL: then only counts, offsets, row_src and row_of are
  * written (x and x_perm_scale are not read), for moe_expert_gate_up_rows,

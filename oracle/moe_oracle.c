@@ -34,8 +34,9 @@
  *   - rounding points: h and y_perm are rounded to the storage type the
  *     kernel keeps them in (fp32, bf16, or e4m3 per 1x128 tile for h), the
  *     shared expert's output and y stay unrounded until the fp32 output;
- *   - e4m3 (OCP E4M3FN) tile/block scale = amax / 448 in fp32 (1 if amax = 0),
- *     code = round-to-nearest-even(v / scale) with fp32 division, saturating.
+ *   - e4m3 (OCP E4M3FN) tile/block scale = the smallest power of two at or
+ *     above amax / 448 (fp32 quotient; 1 if amax = 0), code =
+ *     round-to-nearest-even(v / scale), saturating.
  *
  * Build: gcc -O2 -fopenmp -fno-fast-math -ffp-contract=off -shared -fPIC
  */
@@ -135,16 +136,30 @@ uint16_t oracle_bf16_encode(float f) { return bf16_enc(f); }
 double oracle_e4m3_decode(uint8_t c) { return e4m3_dec(c); }
 uint8_t oracle_e4m3_encode(float f) { return e4m3_enc(f); }
 
-/* One 1x128 tile: scale = amax / 448 (fp32), codes of v / scale (fp32 division).
- * Fine-grained fp8 tiles: crackai.dev DeepSeek-V3 summary, "How It Works"
- * (a scale per tile, FP32 accumulation); DeepSeek V3 From Scratch, "The idea". */
+/* The scale of a tile whose largest magnitude is amax: the smallest power of
+ * two at or above amax / 448 (the fp32 quotient), 1 when amax = 0. */
+static float tile_scale(float amax) {
+    if (!(amax > 0.0f)) return 1.0f;
+    float t = amax / 448.0f;
+    uint32_t b;
+    memcpy(&b, &t, 4);
+    if (b & 0x7FFFFFu) b = (b & 0xFF800000u) + 0x800000u; /* next power of two */
+    float s;
+    memcpy(&s, &b, 4);
+    return s;
+}
+
+/* One 1x128 tile: scale from tile_scale, codes of v / scale (fp32 division,
+ * exact for a power of two).  Fine-grained fp8 tiles: crackai.dev
+ * DeepSeek-V3 summary, "How It Works" (a scale per tile, FP32 accumulation);
+ * DeepSeek V3 From Scratch, "The idea". */
 static float quant_tile(const float *v, int n, uint8_t *q) {
     float amax = 0.0f;
     for (int i = 0; i < n; ++i) {
         float a = fabsf(v[i]);
         if (a > amax) amax = a;
     }
-    float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    float s = tile_scale(amax);
     for (int i = 0; i < n; ++i) q[i] = e4m3_enc(v[i] / s);
     return s;
 }

@@ -248,8 +248,8 @@ hipError_t fgemm(const FGemm &p, hipStream_t s) {
 // -------------------------------------------------------------- quantisers
 
 // Rows of C values (C % 128 == 0; fp32, or bf16 bits when BF16_IN; row
-// stride ldi) -> e4m3 per 1x128 tile: scale = amax / 448 (1 for an all-zero
-// tile), code = e4m3(v / scale) with fp32 division; codes [R, C] (row stride
+// stride ldi) -> e4m3 per 1x128 tile: scale = the power of two at or above
+// amax / 448 (1 for an all-zero tile), code = e4m3(v / scale); codes [R, C] (row stride
 // ldo), scales [R, C/128].  16 lanes per tile, 8 values per lane.
 template <bool BF16_IN>
 __global__ __launch_bounds__(256) void k_q8_rows(int64_t R, int C, const void *__restrict__ in, int64_t ldi,
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256) void k_q8_rows(int64_t R, int C, const void *_
     for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
 #pragma unroll
     for (int s = 1; s < 16; s <<= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
-    const float s = m > 0.f ? m / 448.0f : 1.0f;
+    const float s = e4m3_tile_scale(m);
     uint32_t w0 = 0, w1 = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(256) void k_q8_cols(int R, const void *__restrict__
     red[wave][lane] = m;
     __syncthreads();
     const float amax = fmaxf(fmaxf(red[0][lane], red[1][lane]), fmaxf(red[2][lane], red[3][lane]));
-    const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+    const float s = e4m3_tile_scale(amax);
     uint32_t w[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {

@@ -49,6 +49,17 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
     return sign | (code > 0x7eu ? 0x7eu : code);
 }
 
+// Scale of one e4m3 tile (1x128 activations, 128x128 weight blocks): the
+// smallest power of two at or above amax / 448 (fp32 division), 1 for an
+// all-zero tile.  A power of two: dividing by it is exact, and its exponent
+// field is the E8M0 scale the block-scaled MFMA takes.
+__device__ __forceinline__ float e4m3_tile_scale(float amax) {
+    if (!(amax > 0.f)) return 1.0f;
+    uint32_t b = __float_as_uint(amax / 448.0f);
+    if (b & 0x7fffffu) b = (b & 0xff800000u) + 0x800000u;
+    return __uint_as_float(b);
+}
+
 // Totally ordered key of a float (larger float -> larger unsigned key).
 __device__ __forceinline__ uint32_t f32_order_key(float f) {
     uint32_t u = __float_as_uint(f);

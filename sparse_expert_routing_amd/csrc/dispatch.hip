@@ -145,7 +145,7 @@ __device__ __forceinline__ uint2 quant8(uint4 raw, float &scale) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
     amax = wave_max_f32(amax, 16);
-    const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+    const float s = e4m3_tile_scale(amax);
     scale = s;
     uint32_t lo = 0, hi = 0;
 #pragma unroll

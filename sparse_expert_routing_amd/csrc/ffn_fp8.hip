@@ -14,7 +14,8 @@
 // of the 16-byte K chunks.
 // gate/up epilogue: h = silu(g) * u in fp32, then quantised per 1x128 tile of
 // h: the row amax over the workgroup's 128 columns is combined across the two
-// column waves through LDS; scale = amax / 448, code = e4m3(h / scale).
+// column waves through LDS; scale = the power of two at or above amax / 448,
+// code = e4m3(h / scale).
 // down epilogue: bf16 store of y_perm, or (shared expert) the fp32 combine.
 #include "device.h"
 #include "kernels.h"
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(Fp8Params p) {
                 const int tr = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
                 const int row = m0 + tr;
                 const float amax = fmaxf(pm[i][r], xch[(wn ^ 1) * BM + tr]);
-                const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+                const float s = e4m3_tile_scale(amax);
                 if (row < m_end) {
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {

@@ -30,8 +30,9 @@
 //     loads, so one vmcnt wait per stage covers both;
 //   - epilogues: gate/up forms h = silu(g) * u in fp32 and quantises it per
 //     1x128 tile (the tile's 128 h columns; the row amax is combined across
-//     the four column waves through LDS), scale = amax / 448 (1 for an
-//     all-zero tile), code = e4m3(h / scale); down stores bf16 y_perm, or (the
+//     the four column waves through LDS), scale = the power of two at or
+//     above amax / 448 (1 for an all-zero tile), code = e4m3(h / scale); down
+//     stores bf16 y_perm, or (the
 //     shared expert) forms y = acc + sum_j w_j * y_perm[row_of[t*k + j]] in
 //     fp32, ascending j, staging the tile through LDS in 64-row chunks so
 //     each routed row is gathered as one 512-byte run per half-wave.
@@ -387,7 +388,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_large(F8Params p) {
                 float amax = am[i];
 #pragma unroll
                 for (int w = 0; w < 4; ++w) amax = fmaxf(amax, xch[w * 256 + tr]);
-                const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+                const float s = e4m3_tile_scale(amax);
                 const bool ok = row < m_end;
                 const uint32_t qbase = ok ? (uint32_t)row * (uint32_t)p.H + (uint32_t)n0 : 0xfffff000u;
 #pragma unroll

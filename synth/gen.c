@@ -247,8 +247,8 @@ void synth_uniform(uint64_t seed, uint32_t tensor, int64_t n, double lo, double 
 /*
  * fp8 weight preparation for a stack of G matrices [R, C] (R, C multiples of
  * 128): the same bf16 values synth_normal gives for this seed and tensor
- * (element index (g*R + r)*C + c), then per 128x128 block: amax = max |v|, scale = amax / 448 (fp32
- * division; 1 when amax = 0), q = e4m3(v / scale) with fp32 division.
+ * (element index (g*R + r)*C + c), then per 128x128 block: amax = max |v|, scale = the smallest
+ * power of two at or above amax / 448 (the fp32 quotient; 1 when amax = 0), q = e4m3(v / scale).
  * q: [G, R, C] codes; scales: [G, R/128, C/128] fp32.
  */
 void synth_normal_e4m3_blocks(uint64_t seed, uint32_t tensor, int64_t G, int64_t R, int64_t C,
@@ -274,7 +274,14 @@ void synth_normal_e4m3_blocks(uint64_t seed, uint32_t tensor, int64_t G, int64_t
                 if (a > amax) amax = a;
             }
         }
-        float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+        float s = 1.0f;
+        if (amax > 0.0f) {
+            float t = amax / 448.0f;
+            uint32_t b;
+            memcpy(&b, &t, 4);
+            if (b & 0x7FFFFFu) b = (b & 0xFF800000u) + 0x800000u; /* next power of two */
+            memcpy(&s, &b, 4);
+        }
         scales[blk] = s;
         for (int r = 0; r < 128; ++r) {
             uint8_t *dst = q + (g * R + rb * 128 + r) * C + cb * 128;

@@ -1,0 +1,22 @@
+"""Library-side e4m3 tile quantisation for the CPU pins: torch's float8_e4m3fn
+cast, with the tile scale formed through frexp / ldexp (the smallest power of
+two at or above amax / 448, 1 for an all-zero tile)."""
+import torch
+
+
+def tile_scale(amax: torch.Tensor) -> torch.Tensor:
+    """amax: float32 tensor -> float32 power-of-two scales."""
+    t = amax.to(torch.float32) / 448.0
+    m, e = torch.frexp(t)
+    one = torch.ones_like(t)
+    s = torch.where(m == 0.5, torch.ldexp(one, e - 1), torch.ldexp(one, e))
+    return torch.where(amax > 0, s, one)
+
+
+def quant_last(v: torch.Tensor):
+    """1x128 tiles along the last dim: (codes as float8, scales float32 [..., n/128])."""
+    v32 = v.to(torch.float32)
+    t = v32.reshape(*v32.shape[:-1], -1, 128)
+    s = tile_scale(t.abs().amax(-1))
+    q = (t / s[..., None]).to(torch.float8_e4m3fn)
+    return q.reshape(v32.shape), s

@@ -20,19 +20,17 @@ import torch
 
 import oracle
 import synth
+from tests import e4m3_ref
 
 E, K, T, D, I = 16, 4, 160, 256, 128
 
 
 def q_last(v):
-    """1x128 tiles along the last dim, as the forward quantises: scale =
-    amax / 448 in fp32 (1 for an all-zero tile), code = e4m3(v / scale)."""
-    v32 = v.detach().to(torch.float32)
-    t = v32.reshape(*v32.shape[:-1], -1, 128)
-    amax = t.abs().amax(-1, keepdim=True)
-    s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
-    q = (t / s).to(torch.float8_e4m3fn).to(torch.float64) * s.to(torch.float64)
-    return q.reshape(v.shape)
+    """1x128 tiles along the last dim, as the forward quantises (power-of-two
+    scale at or above amax / 448), dequantised to fp64."""
+    q, s = e4m3_ref.quant_last(v.detach())
+    t = q.to(torch.float64).reshape(*v.shape[:-1], -1, 128) * s.to(torch.float64)[..., None]
+    return t.reshape(v.shape)
 
 
 def q_cols(v):

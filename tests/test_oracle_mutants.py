@@ -33,7 +33,9 @@ MUTANTS = [
      "    for (int64_t f = A - 1; f >= 0; --f) {\n        int e = idx[f];"),
     ("h not rounded to bf16", "for (int i = 0; i < n; ++i) h[i] = bf16_round(h[i]);", "(void)0;"),
     ("y_perm not rounded", "return sh->wt == OR_F32 ? (double)(float)v : bf16_round(v);", "return v;"),
-    ("tile scale off", "float s = amax > 0.0f ? amax / 448.0f : 1.0f;", "float s = amax > 0.0f ? amax / 240.0f : 1.0f;"),
+    ("tile scale off", "float t = amax / 448.0f;", "float t = amax / 240.0f;"),
+    ("tile scale not a power of two", "if (b & 0x7FFFFFu) b = (b & 0xFF800000u) + 0x800000u; /* next power of two */",
+     "(void)0;"),
     ("gap off by one", "if (r == k) k1th = v[best];", "if (r == k - 1) k1th = v[best];"),
     ("bf16 rounding truncates", "if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;", "(void)lower;"),
     ("e4m3 ties away from zero", "else c = (lo & 1) ? hi : lo;", "else c = hi;"),

@@ -23,6 +23,7 @@ from scipy.special import expit
 
 import oracle
 import synth
+from tests import e4m3_ref
 
 torch.set_num_threads(4)
 
@@ -36,12 +37,8 @@ def bf16_round_t(v: torch.Tensor) -> torch.Tensor:
 
 def e4m3_tiles_t(v: torch.Tensor) -> torch.Tensor:
     """Library e4m3 quantisation per 1x128 tile (torch cast), dequantised to fp64."""
-    v32 = v.to(torch.float32)
-    shp = v32.shape
-    t = v32.reshape(-1, 128)
-    amax = t.abs().amax(dim=1, keepdim=True)
-    s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
-    q = (t / s).to(torch.float8_e4m3fn)
+    shp = v.shape
+    q, s = e4m3_ref.quant_last(v.reshape(-1, 128))
     return (q.to(torch.float64) * s.to(torch.float64)).reshape(shp)
 
 
@@ -156,9 +153,15 @@ def test_tile_quantisation_matches_torch_cast():
     q, s = oracle.quant_e4m3_rows(x, "bf16")
     xv = torch.from_numpy(synth.bf16_to_f32(x)).reshape(7, 3, 128)
     amax = xv.abs().amax(dim=2)
-    assert np.array_equal(s, (amax / 448.0).numpy())
-    ref = (xv / (amax / 448.0)[..., None]).to(torch.float8_e4m3fn).view(torch.uint8).reshape(7, 384).numpy()
-    assert np.array_equal(q, ref)
+    ref_q, ref_s = e4m3_ref.quant_last(xv.reshape(7, 384))
+    assert np.array_equal(s, ref_s.numpy())
+    assert np.array_equal(q, ref_q.view(torch.uint8).reshape(7, 384).numpy())
+    # the scale is a power of two with amax / scale in (224, 448]: the tile's
+    # largest value lands in the top binade of e4m3
+    m, _ = np.frexp(s)
+    assert (m == 0.5).all()
+    r = amax.numpy() / s
+    assert (r > 224).all() and (r <= 448).all()
     # an all-zero tile gets scale 1 and zero codes
     z = np.zeros((1, 128), np.float32)
     qz, sz = oracle.quant_e4m3_rows(z, "f32")

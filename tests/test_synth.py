@@ -8,6 +8,7 @@ import numpy as np
 import torch
 
 import synth
+from tests import e4m3_ref
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -45,8 +46,9 @@ def test_e4m3_weights_are_the_bf16_draws_quantised():
     b = synth.normal(7, 4, (2, 256, 384), 0.02, "bf16")
     v = torch.from_numpy(synth.bf16_to_f32(b)).reshape(2, 2, 128, 3, 128)
     amax = v.abs().amax(dim=(2, 4))
-    assert np.array_equal(s, (amax / 448.0).numpy())
-    ref = (v / (amax / 448.0)[:, :, None, :, None]).to(torch.float8_e4m3fn)
+    sc = e4m3_ref.tile_scale(amax)
+    assert np.array_equal(s, sc.numpy())
+    ref = (v / sc[:, :, None, :, None]).to(torch.float8_e4m3fn)
     assert np.array_equal(q, ref.view(torch.uint8).reshape(2, 256, 384).numpy())
 
 
