@@ -4,8 +4,8 @@
 // crackai.dev DeepSeek-V3 summary, "How It Works": FP8 matmuls with a scale
 // per tile and FP32 accumulation at chosen points; DeepSeek V3 From Scratch,
 // "The idea": fine-grained quantisation tiles.  Tile shapes (ours, as in the
-// rest of the library): one fp32 scale per 1x128 activation tile and per
-// 128x128 weight block; partial sums are promoted to fp32 every 128 of K.
+// rest of the library): one power-of-two scale per 1x128 activation tile and
+// per 128x128 weight block, applied inside the MFMA; fp32 accumulation.
 //
 // Design for gfx950 (shared with the bf16 large-tile kernel where it can be):
 //   - 8 waves (2 per SIMD) in a 2x4 layout, each a 128x64 block of the
@@ -17,12 +17,10 @@
 //     B_{s+1} and A_{s+2} stream into the two units stage s-1 left, one load
 //     per output block, so B has about a stage and A two stages to land;
 //   - each 32x32 output block takes two v_mfma_scale_f32_32x32x64_f8f6f4
-//     (scales 0: plain fp8) into a fresh VGPR partial, then one fma per
-//     element folds it into the accumulator scaled by
-//     s_a[row, kb] * s_w[block, kb] (the promotion every 128 of K; the
-//     scales are arbitrary fp32, so it cannot ride on the MFMA's
-//     power-of-two block scales); while one wave folds, the other wave of
-//     its SIMD keeps the matrix unit busy;
+//     per stage that accumulate straight into the fp32 accumulator, the
+//     stage's scales given to the matrix unit as E8M0 exponents: the
+//     weight block's for the first operand (every lane), each A row's for
+//     the second (lanes l and l+32 carry row l % 32); no vector fold;
 //   - the MFMA operands are swapped, so a lane owns one tile row and runs
 //     of 4 consecutive output columns: per-row activation scales are per
 //     lane, weight scales per wave;
@@ -160,13 +158,15 @@ __device__ __forceinline__ i32x8 frag32(const uint8_t *unit, int row, int c) {
     return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// The E8M0 exponent of a power-of-two fp32 scale (its biased exponent field).
+__device__ __forceinline__ int e8m0(float pow2) { return (int)((__float_as_uint(pow2) >> 23) & 0xffu); }
+
 __device__ __forceinline__ float swiglu(float g, float u) {
     return g * u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
 }
 
 // Eight waves (two per SIMD), each owning 128 rows x 64 columns of the
-// 256x256 tile: its 128 fp32 accumulators fit in VGPRs, so the per-128-K
-// promotion is one fma per element, and while one wave of a SIMD waits on
+// 256x256 tile: its 128 fp32 accumulators fit in VGPRs, and while one wave of a SIMD waits on
 // its MFMA result, LDS or the barrier, the other issues.  A wave's DMA
 // share is 4 of the 32 one-KB blocks of each operand slab.
 template <int EPI, bool ROUTED>
@@ -319,8 +319,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_large(F8Params p) {
 
             const uint8_t *cA = UNIT(u0), *cB = UNIT(u1);
             // B fragments of the whole stage (2 column blocks x 2 K halves);
-            // A fragments per row block.  One partial: while this wave folds
-            // it, the other wave on the SIMD keeps the matrix unit busy.
+            // A fragments per row block.  The tile scales are powers of two,
+            // applied by the MFMA itself as E8M0 exponents: the weight block's
+            // (the same for every lane of the first operand) and each A row's
+            // (lanes l and l+32 of the second operand carry row l % 32), so
+            // the products accumulate straight into acc.
             i32x8 bf[2][2], af[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
@@ -328,22 +331,25 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_large(F8Params p) {
 #pragma unroll
                 for (int s = 0; s < 2; ++s) bf[j][s] = frag32(cB, brow, 4 * s + 2 * g);
             }
-            const f32x16 zero = {};
+            const int eb0 = e8m0(sw[0]), eb1 = DUAL ? e8m0(sw[1]) : eb0;
 #pragma unroll
-            for (int n = 0; n < 8; ++n) {
-                const int i = n >> 1, j = n & 1;
-                if (j == 0) {
+            for (int i = 0; i < 4; ++i) {
 #pragma unroll
-                    for (int s = 0; s < 2; ++s) af[s] = frag32(cA, wm * 128 + 32 * i + (lane & 31), 4 * s + 2 * g);
+                for (int s = 0; s < 2; ++s) af[s] = frag32(cA, wm * 128 + 32 * i + (lane & 31), 4 * s + 2 * g);
+                const int ea = e8m0(sa[i]);
+                // the two column blocks' first K halves, then their second
+                // halves (consecutive MFMAs independent); one slot load after
+                // each pair (B first: it has one stage to land)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j][h], af[h], acc[i][j], 0, 0, 0,
+                                                                                     j ? eb1 : eb0, 0, ea);
+                    const int n = 2 * i + h;
+                    if (n < 4) ISSUE_B(kt + 1, n, fB);
+                    else ISSUE_A(kt + 2, n - 4, fA);
                 }
-                f32x16 tp = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j][0], af[0], zero, 0, 0, 0, 0, 0, 0);
-                tp = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j][1], af[1], tp, 0, 0, 0, 0, 0, 0);
-                // one slot load per block (B first: it has one stage to land)
-                if (n < 4) ISSUE_B(kt + 1, n, fB);
-                else ISSUE_A(kt + 2, n - 4, fA);
-                const float sc = sa[i] * sw[DUAL ? j : 0];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(tp[r], sc, acc[i][j][r]);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) sa[i] = sa_n[i];
