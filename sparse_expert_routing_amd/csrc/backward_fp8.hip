@@ -22,10 +22,10 @@
 // and the data gradients) run on the forward's persistent e4m3 kernel with an
 // fp32 epilogue when the shape fits it.
 // k_fgemm: C = A B^T with both operands K-contiguous e4m3 codes, 128x128
-// tiles, one 128-wide scale block per stage (two v_mfma 32x32x64 fp8 per
-// 32x32 block), each stage's fp32 partial folded into the accumulator times
-// s_a[row, kb] * s_b[col, kb]; register-staged LDS double buffer with an XOR
-// swizzle of the 16-byte chunks.  Groups split M (a B per expert: the data
+// tiles, one 128-wide scale block per stage (two v_mfma_scale 32x32x64 fp8
+// per 32x32 block, accumulating in fp32, the power-of-two scales s_a[row, kb]
+// and s_b[col, kb] applied by the MFMA as E8M0 exponents); register-staged
+// LDS double buffer with an XOR swizzle of the 16-byte chunks.  Groups split M (a B per expert: the data
 // gradients) or K (an expert's padded rows: the weight gradients, a C per
 // expert).
 #include "backward.h"
@@ -192,24 +192,23 @@ __global__ __launch_bounds__(256, 2) void k_fgemm(FGemm p) {
                     af[i][hf] = frag8(sA[buf], wm * 64 + i * 32 + (lane & 31), hf, g);
                     bq[i][hf] = frag8(sB[buf], wn * 64 + i * 32 + (lane & 31), hf, g);
                 }
-            // the 16 rows (per 32-row block) and the column this lane accumulates
-            float sa[2][16], sb[2];
+            // the stage's scales (powers of two) go to the MFMA as E8M0
+            // exponents: lanes l and l+32 of each operand carry the scale of
+            // the operand row l % 32 they hold (A rows, B rows = C columns)
+            int ea[2], eb[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i) {
+                ea[i] = (int)((__float_as_uint(sAs[buf][wm * 64 + i * 32 + (lane & 31)]) >> 23) & 0xffu);
+                eb[i] = (int)((__float_as_uint(sBs[buf][wn * 64 + i * 32 + (lane & 31)]) >> 23) & 0xffu);
+            }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sa[i][r] = sAs[buf][wm * 64 + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3)];
+            for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) sb[j] = sBs[buf][wn * 64 + j * 32 + (lane & 31)];
+                for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    f32x16 t = {};
-                    t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i][0], bq[j][0], t, 0, 0, 0, 0, 0, 0);
-                    t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i][1], bq[j][1], t, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] += t[r] * (sa[i][r] * sb[j]);
-                }
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i][hf], bq[j][hf], acc[i][j], 0, 0,
+                                                                                     0, ea[i], 0, eb[j]);
         }
         if (kt + 1 < nkb) {
             const int nb = (kt + 1) & 1;

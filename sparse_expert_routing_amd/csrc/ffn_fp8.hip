@@ -7,8 +7,9 @@
 // block.
 //
 // Each 128-wide K block is one stage: the wave multiplies its e4m3 fragments
-// with v_mfma_f32_32x32x64_f8f6f4 (two per block) into a fresh fp32 partial,
-// then folds it into the fp32 accumulator scaled by s_a[row, kb] * s_w[nb, kb].
+// with v_mfma_scale_f32_32x32x64_f8f6f4 (two per block) straight into the fp32
+// accumulator, the power-of-two scales s_a[row, kb] and s_w[nb, kb] applied by
+// the MFMA as E8M0 exponents.
 // Workgroup tile 128 rows x 128 output columns (gate/up: 128 gate + 128 up
 // B rows), 4 waves in a 2x2 layout, LDS double-buffered with an XOR swizzle
 // of the 16-byte K chunks.
@@ -184,25 +185,24 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(Fp8Params p) {
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) af[i][hf] = frag(sA[buf], wm * 64 + i * 32 + (lane & 31), hf, g);
-            // per-lane activation scales of the 16 rows this lane accumulates, per m tile
-            float sa[2][16];
+            // the power-of-two scales go to the MFMA as E8M0 exponents: lanes
+            // l and l+32 of the A operand carry row l % 32's; the weight block's
+            // is the same for every lane
+            int ea[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sa[i][r] = sAs[buf][wm * 64 + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3)];
+                ea[i] = (int)((__float_as_uint(sAs[buf][wm * 64 + i * 32 + (lane & 31)]) >> 23) & 0xffu);
+            const int ebg = (int)((__float_as_uint(swg) >> 23) & 0xffu), ebu = (int)((__float_as_uint(swu) >> 23) & 0xffu);
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const int brow = DUAL ? ((j >> 1) * BN + wn * 64 + (j & 1) * 32 + (lane & 31))
                                       : (wn * 64 + j * 32 + (lane & 31));
                 const i32x8 b0 = frag(sB[buf], brow, 0, g), b1 = frag(sB[buf], brow, 1, g);
-                const float sw = (DUAL && j >= 2) ? swu : swg;
+                const int eb = (DUAL && j >= 2) ? ebu : ebg;
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    f32x16 t = {};
-                    t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i][0], b0, t, 0, 0, 0, 0, 0, 0);
-                    t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i][1], b1, t, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] += t[r] * (sa[i][r] * sw);
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i][0], b0, acc[i][j], 0, 0, 0, ea[i], 0, eb);
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i][1], b1, acc[i][j], 0, 0, 0, ea[i], 0, eb);
                 }
             }
         }
