@@ -174,7 +174,7 @@ def main():
         achieved = gate_up_flops / (gate_up_ms * 1e-3) / 1e12
         peak = peak_flops
     large = A >= 128 * E
-    kname = ("k_gemm_fp8_large" if large else "k_gemm_fp8") if cfg.wt == "e4m3" else \
+    kname = ("k_gemm_fp8_mx" if large and I % 256 == 0 and d % 256 == 0 else "k_gemm_fp8") if cfg.wt == "e4m3" else \
         ("k_gemm_bf16_large" if large else "k_gemm_skinny" if A <= 4 * E else "k_gemm_bf16")
     total_flops = 2.0 * T * d * E + 6.0 * (A + T) * d * I
     ms_step = wall / K * 1e3

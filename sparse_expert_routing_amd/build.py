@@ -30,7 +30,6 @@ FLAGS = [
 # its accumulator with vector-ALU work, so its MFMAs must write VGPRs (the
 # partials), not AGPRs (which hold the accumulators).
 FILE_FLAGS = {
-    "ffn_fp8_large.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -595,8 +595,8 @@ hipError_t launch_backward_fp8(const BackwardArgs &a, void *ws, hipStream_t s) {
         g.a_div = p.a_div; g.a_src_rows = T; g.K = p.K; g.B = p.B; g.Bs = p.Bs; g.N = p.N; g.out = p.C; g.ldo = (int)p.ldc;
         if (p.lda == p.K && p.ldas == p.K / FK && p.ldb == p.K && p.ldbs == p.K / FK && p.bdiv == 128 &&
             (!routed || (p.bstride == (int64_t)p.N * p.K && p.bsstride == (int64_t)(p.N / 128) * (p.K / FK))) &&
-            fp8_large_gemm_ok(g))
-            return launch_fp8_large_gemm(g, s);
+            fp8_mx_gemm_ok(g))
+            return launch_fp8_mx_gemm(g, s);
         return routed ? fgemm<FG_M>(p, s) : fgemm<FG_NONE>(p, s);
     };
     // 2. pre-activations, as the forward forms them: routed rows gather the

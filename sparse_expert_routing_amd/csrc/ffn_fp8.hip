@@ -288,7 +288,7 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(Fp8Params p) {
 }  // namespace
 
 hipError_t launch_ffn_fp8(const FfnArgs &a, hipStream_t s) {
-    if (ffn_fp8_large_ok(a)) return launch_ffn_fp8_large(a, s);
+    if (ffn_fp8_mx_ok(a)) return launch_ffn_fp8_mx(a, s);
     const bool routed = a.offsets != nullptr;
     const int slots = (a.M + BM - 1) / BM + (routed ? kE : 0);
     Fp8Params p{};

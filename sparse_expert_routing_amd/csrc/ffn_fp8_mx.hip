@@ -1,0 +1,692 @@
+// Grouped SwiGLU expert GEMMs in OCP fp8 e4m3 for large groups (prefill),
+// with the tile scales applied by the block-scaled MFMA: persistent
+// workgroups, 256x256 tiles, the bf16 large-tile kernel's schedule.
+//
+// crackai.dev DeepSeek-V3 summary, "How It Works": FP8 matmuls with a scale
+// per tile and FP32 accumulation; DeepSeek V3 From Scratch, "The idea":
+// fine-grained quantisation tiles.  Tiles (ours, as in the rest of the
+// library): one power-of-two scale per 1x128 activation tile and per 128x128
+// weight block.
+//
+// Design for gfx950:
+//   - a stage is 128 of K (one scale block): A and B slabs of 256 rows x 128
+//     bytes, the same 32 KB operand units, five-unit LDS ring and DMA
+//     geometry (buffer_load_dwordx4 ... lds) as the bf16 kernel, whose K
+//     stage is 64 bf16 of the same 128 bytes;
+//   - 4 waves (2x2), each a 128x128 block as 4x4 v_mfma_scale_f32_32x32x64
+//     accumulators in AGPRs; a stage is two steps of 64 of K, 16 MFMAs each,
+//     so the MFMA cycles and LDS fragment bytes per stage equal the bf16
+//     kernel's (each fragment is 32 bytes: two 16-byte pieces of the row);
+//   - the scales go to the MFMA as E8M0 exponents: the weight block's for
+//     every lane of the weight operand, the A row's for lanes l and l+32 of
+//     the activation operand (row l % 32), so the products accumulate in
+//     fp32 with no vector work; a stage's A-row scales are loaded one stage
+//     ahead (before that stage's slot loads, so the stage waits cover them);
+//   - schedule: step 0 streams A of stage s+2 into the unit B of stage s-1
+//     left, one load per two MFMAs, and reads step 1's fragments; after it
+//     every fragment of the stage is in registers, so a mid-stage barrier
+//     (once A and B of stage s+1 have landed) frees the stage's units; step
+//     1 streams B of stage s+2 into A_s's unit and reads stage s+1's first
+//     fragments;
+//   - epilogues as in the bf16 kernel (register stores straight from the
+//     transposed accumulators, the next tile's first two stages already in
+//     flight; the combine stages 64-row chunks through LDS), the gate/up one
+//     forming h = silu(g) u in fp32 and quantising it per 1x128 tile (the
+//     tile's 128 h columns; the row amax of the two column waves meets in
+//     the free fifth LDS unit).
+#include "device.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kE = 256;
+constexpr int LM = 256;        // rows per tile
+constexpr int LB = 256;        // B rows per tile
+constexpr int LKB = 128;       // K per stage (bytes = e4m3 elements): one scale block
+constexpr int NUNIT = 5;       // LDS ring units (5 x 32 KB)
+constexpr int UNIT_BYTES = LM * LKB;
+constexpr int kGroupM = 8;     // row tiles per ordering group
+constexpr int kChRows = 64;    // combine epilogue chunk rows
+constexpr int kChLd = LB + 4;
+// An offset past the end of every output resource: stores of padding rows
+// are dropped.
+constexpr uint32_t kOobOff = 0xFFFF0000u;
+
+enum { MX_SWIGLU_Q = 0, MX_STORE = 1, MX_COMBINE = 2, MX_F32 = 3 };
+
+struct MxParams {
+    int M;
+    const int32_t *offsets;   // routed: [E+1] row ranges
+    const uint8_t *A;         // [rows, K] codes
+    const float *As;          // [rows, K/128] power-of-two scales
+    const int32_t *a_rows;    // optional: GEMM row r reads row a_rows[r] / a_div of A / As
+    int a_div;
+    int K;
+    const uint8_t *B0, *B1;   // [G, N, K] codes (gate, up; or down)
+    const float *S0, *S1;     // [G, N/128, K/128] power-of-two block scales
+    int N;                    // B rows per expert (SwiGLU: rows of each of gate / up)
+    uint8_t *hq;              // MX_SWIGLU_Q: [M, N] codes
+    float *hs;                // MX_SWIGLU_Q: [M, N/128]
+    uint16_t *out;            // MX_STORE: bf16 [M, N]
+    float *yout;              // MX_COMBINE: f32 [M, N]; MX_F32: f32 rows of ldo
+    int ldo;
+    const uint16_t *y_perm;   // MX_COMBINE: routed outputs [M*k, N] bf16
+    const int32_t *row_of;    // MX_COMBINE: [M*k]
+    const float *cw;          // MX_COMBINE: combine weights [M*k]
+};
+
+struct TileMap {
+    int off[5];
+    int nt[4];
+    int excl, total;
+};
+
+__device__ __forceinline__ void tilemap_init(TileMap &tm, const int32_t *__restrict__ offsets) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) tm.off[i] = offsets[lane * 4 + i];
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        tm.nt[i] = (tm.off[i + 1] - tm.off[i] + LM - 1) / LM;
+        s += tm.nt[i];
+    }
+    const int incl = wave_incl_scan(s);
+    tm.excl = incl - s;
+    tm.total = __shfl(incl, 63, 64);
+}
+
+__device__ __forceinline__ void tilemap_find(const TileMap &tm, int mt, int &e, int &m0, int &m_end) {
+    const int lane = threadIdx.x & 63;
+    const int mine = tm.nt[0] + tm.nt[1] + tm.nt[2] + tm.nt[3];
+    const bool own = mt >= tm.excl && mt < tm.excl + mine;
+    const int owner = __ffsll((unsigned long long)__ballot(own)) - 1;
+    int my_e = 0, my_m0 = 0, my_end = 0;
+    if (own) {
+        int s = mt - tm.excl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (s >= 0 && s < tm.nt[i]) {
+                my_e = lane * 4 + i;
+                my_m0 = tm.off[i] + s * LM;
+                my_end = tm.off[i + 1];
+            }
+            s -= tm.nt[i];
+        }
+    }
+    e = __shfl(my_e, owner, 64);
+    m0 = __shfl(my_m0, owner, 64);
+    m_end = __shfl(my_end, owner, 64);
+}
+
+// Byte offset, inside one operand unit, of the 16-byte piece c of tile row
+// `row`: piece c sits at position c ^ (row & 7) ^ ((row >> 3) & 1), so the
+// 32 lanes reading one logical piece of 32 consecutive rows hit distinct banks.
+__device__ __forceinline__ int piece(int row, int c) { return row * LKB + ((c ^ (row & 7) ^ ((row >> 3) & 1)) * 16); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lds() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ const void *uniform_ptr(const void *p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const void *>(((uint64_t)hi << 32) | lo);
+}
+
+// One 1 KB block (8 rows of 128 B) of a stage operand, global -> LDS.
+__device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t *lds_block) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(lds_block), 16, voff, soff, 0, 0);
+}
+
+// 32 bytes of K (pieces c and c+1 of the row) as one MFMA operand.
+__device__ __forceinline__ i32x8 frag32(const uint8_t *unit, int row, int c) {
+    const i32x4 lo = *reinterpret_cast<const i32x4 *>(unit + piece(row, c));
+    const i32x4 hi = *reinterpret_cast<const i32x4 *>(unit + piece(row, c + 1));
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// The E8M0 exponent of a power-of-two fp32 scale (its biased exponent field).
+__device__ __forceinline__ int e8m0(float pow2) { return (int)((__float_as_uint(pow2) >> 23) & 0xffu); }
+
+// acc += A x B^T for one 32x32 block and 64 of K, the scales (E8M0) of the A
+// row this lane carries (ea) and of the B rows (eb).  TRANS swaps the
+// operands, so the accumulator holds the transposed block: lane l owns tile
+// row l % 32 and, in registers 4q .. 4q+3, the 4 consecutive tile columns
+// 8q + 4(l / 32) .. +3.
+template <bool TRANS>
+__device__ __forceinline__ f32x16 mma(i32x8 a, i32x8 b, f32x16 c, int ea, int eb) {
+    if constexpr (TRANS) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, eb, 0, ea);
+    else return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
+}
+
+__device__ __forceinline__ float acc_read(float x) {
+    float r;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
+    return r;
+}
+
+__device__ __forceinline__ float swiglu(float g, float u) {
+    return g * u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
+
+template <int EPI, bool ROUTED>
+__global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
+    constexpr bool DUAL = EPI == MX_SWIGLU_Q;
+    constexpr bool TRANS = EPI != MX_COMBINE;
+    constexpr int BN = DUAL ? LB / 2 : LB;  // output columns per tile
+    // buffer stores per lane per register epilogue: gate/up 4 x (8 codes + 1 scale); store 64; fp32 64
+    constexpr int kEpiStores = TRANS ? (DUAL ? 36 : 64) : 0;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NUNIT * UNIT_BYTES];  // 160 KB
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1, g = lane >> 5;
+    const int K = p.K, nk = K / LKB;
+
+    TileMap tm;
+    int Mt;
+    const int NT = p.N / BN;
+    if (ROUTED) {
+        tilemap_init(tm, p.offsets);
+        Mt = tm.total;
+    } else {
+        Mt = (p.M + LM - 1) / LM;
+    }
+    const int total = Mt * NT;
+    const int P = gridDim.x;
+
+    // DMA geometry: each operand (256 rows x 128 B = 32 blocks of 1 KB) is
+    // moved by 8 instructions per wave: wave w takes blocks w + 4*i; lane l
+    // fills physical piece (l & 7) of row 8*blk + (l >> 3).
+    int drow[8], dcol[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = 8 * (wave + 4 * i) + (lane >> 3);
+        drow[i] = row;
+        dcol[i] = ((lane & 7) ^ (row & 7) ^ ((row >> 3) & 1)) * 16;
+    }
+
+    int e = 0, m0 = 0, m_end = 0, n0 = 0;
+    const uint32_t a_rows_total = p.a_rows ? (uint32_t)(p.M / p.a_div) : (uint32_t)p.M;
+    const __amdgpu_buffer_rsrc_t rA = buf_rsrc(p.A, a_rows_total * (uint32_t)K);
+    const __amdgpu_buffer_rsrc_t rAs = buf_rsrc(p.As, a_rows_total * (uint32_t)nk * 4u);
+    const uint32_t b_bytes = (uint32_t)p.N * (uint32_t)K;
+    const int nbk = p.N / 128;  // weight scale blocks along N
+    const uint8_t *pBg = p.B0, *pBu = p.B1;
+    const float *swg_p = p.S0, *swu_p = p.S0;
+    uint32_t aoff[8], boff[8], soff[4];
+
+#define UNIT(u) (smem + (u) * UNIT_BYTES)
+#define ISSUE_A(st_, i, unit_)                                                                 \
+        dma_buf(rA, aoff[i], (uint32_t)min((st_), nk - 1) * LKB, (unit_) + (wave + 4 * (i)) * 1024)
+#define B_RSRC()                                                                               \
+        const __amdgpu_buffer_rsrc_t rBg_ = buf_rsrc(uniform_ptr(pBg), b_bytes);               \
+        const __amdgpu_buffer_rsrc_t rBu_ = DUAL ? buf_rsrc(uniform_ptr(pBu), b_bytes) : rBg_;
+#define ISSUE_B(st_, i, unit_)                                                                 \
+        dma_buf((DUAL && (i) >= 4) ? rBu_ : rBg_, boff[i], (uint32_t)min((st_), nk - 1) * LKB, \
+                (unit_) + (wave + 4 * (i)) * 1024)
+    // The stage's A-row scales of this lane's 4 rows (one per 32-row block)
+    // and the weight block scales of this wave's columns (gate and up).
+#define LOAD_SCALES(st_, sa_, sw_)                                                             \
+        {                                                                                      \
+            const int kb_ = min((st_), nk - 1);                                                \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i)                                      \
+                sa_[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rAs, soff[i] + kb_ * 4u, 0, 0)); \
+            sw_[0] = swg_p[kb_];                                                               \
+            sw_[1] = DUAL ? swu_p[kb_] : sw_[0];                                               \
+        }
+#define TILE_SETUP(tt)                                                                         \
+    {                                                                                          \
+        const int gsz_ = kGroupM * NT;                                                         \
+        const int grp_ = (tt) / gsz_, within_ = (tt) - grp_ * gsz_;                            \
+        const int mfirst_ = grp_ * kGroupM;                                                    \
+        const int gm_ = min(kGroupM, Mt - mfirst_);                                            \
+        const int mt_ = mfirst_ + within_ % gm_, nt_ = within_ / gm_;                          \
+        if (ROUTED) {                                                                          \
+            tilemap_find(tm, mt_, e, m0, m_end);                                               \
+        } else {                                                                               \
+            e = 0;                                                                             \
+            m0 = mt_ * LM;                                                                     \
+            m_end = p.M;                                                                       \
+        }                                                                                      \
+        e = __builtin_amdgcn_readfirstlane(e);                                                 \
+        m0 = __builtin_amdgcn_readfirstlane(m0);                                               \
+        m_end = __builtin_amdgcn_readfirstlane(m_end);                                         \
+        n0 = nt_ * BN;                                                                         \
+        pBg = p.B0 + (size_t)e * p.N * K;                                                      \
+        pBu = DUAL ? p.B1 + (size_t)e * p.N * K : pBg;                                         \
+        swg_p = p.S0 + ((size_t)e * nbk + (DUAL ? n0 : n0 + wn * 128) / 128) * nk;             \
+        swu_p = DUAL ? p.S1 + ((size_t)e * nbk + n0 / 128) * nk : swg_p;                       \
+        int ar_[8];                                                                            \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) ar_[i] = min(m0 + drow[i], m_end - 1);    \
+        if (p.a_rows) {                                                                        \
+            _Pragma("unroll") for (int i = 0; i < 8; ++i) ar_[i] = p.a_rows[ar_[i]];            \
+            _Pragma("unroll") for (int i = 0; i < 8; ++i) ar_[i] /= p.a_div;                    \
+        }                                                                                      \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                        \
+            aoff[i] = (uint32_t)ar_[i] * (uint32_t)K + (uint32_t)dcol[i];                      \
+            const int r = drow[i];                                                             \
+            const int br = DUAL ? n0 + (r & (BN - 1)) : n0 + r;                                \
+            boff[i] = (uint32_t)br * (uint32_t)K + (uint32_t)dcol[i];                          \
+            if (m0 + r >= m_end) aoff[i] = kOobOff; /* padding rows fetch nothing */           \
+        }                                                                                      \
+        int sr_[4];                                                                            \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                          \
+            sr_[i] = min(m0 + wm * 128 + 32 * i + (lane & 31), m_end - 1);                     \
+        if (p.a_rows) {                                                                        \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i) sr_[i] = p.a_rows[sr_[i]] / p.a_div;  \
+        }                                                                                      \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) soff[i] = (uint32_t)sr_[i] * (uint32_t)nk * 4u; \
+    }
+    // Stage 0's scales, then A_0, B_0, A_1, B_1 of the tile just set up.
+#define PROLOGUE_LOADS()                                                                       \
+    {                                                                                          \
+        LOAD_SCALES(0, sa, sw);                                                                \
+        B_RSRC()                                                                               \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) ISSUE_A(0, i, UNIT(0));                  \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) ISSUE_B(0, i, UNIT(1));                  \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) ISSUE_A(1, i, UNIT(2));                  \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) ISSUE_B(1, i, UNIT(3));                  \
+    }
+
+    float sa[4], sw[2], sa_n[4], sw_n[2];
+    int t = (blockIdx.x & 7) * (P >> 3) + (blockIdx.x >> 3);
+    if (t < total) {
+        TILE_SETUP(t);
+        PROLOGUE_LOADS();
+    }
+    bool first = true;
+    for (; t < total; t += P) {
+        f32x16 acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+#define READ_AT(r) (2 * (r))
+#define B_ROW(j) ((DUAL ? (((j) >> 1) * 128 + wn * 64 + ((j) & 1) * 32) : (wn * 128 + (j) * 32)) + (lane & 31))
+        // One 64-wide K step: 16 MFMAs on (AC, BC) with the stage's exponents
+        // (EA per row block, EB0 / EB1 for the gate / up column blocks).  The
+        // next step's 8 fragments (units nA / nB, piece column cn) are read at
+        // READ_AT(r), the slot load DMA(x) right after MFMA x; scheduling
+        // barriers keep the order.
+#define FRAG_READ(r, AN, BN_, nA, nB, cn)                                                      \
+        if ((r) < 4)                                                                           \
+            AN[(r) & 3] = frag32((nA), wm * 128 + ((r) & 3) * 32 + (lane & 31), (cn));         \
+        else                                                                                   \
+            BN_[(r) & 3] = frag32((nB), B_ROW((r) & 3), (cn));
+#define STEP(AC, BC, AN, BN_, nA, nB, cn, DMA, NB_, EA, EB0, EB1)                              \
+        _Pragma("unroll") for (int x = 0; x < 16; ++x) {                                       \
+            _Pragma("unroll") for (int r = 0; r < 8; ++r)                                      \
+                if (READ_AT(r) == x) { FRAG_READ(r, AN, BN_, nA, nB, cn) }                     \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+            if ((NB_) > (x >> 2))                                                              \
+                acc[x >> 2][x & 3] = mma<TRANS>(AC[x >> 2], BC[x & 3], acc[x >> 2][x & 3], EA[x >> 2], \
+                                                (DUAL && (x & 3) >= 2) ? (EB1) : (EB0));       \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+            DMA(x);                                                                            \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+        }
+
+        // A_0, B_0 (and stage 0's scales) landed for every wave; behind them
+        // this wave may have queued the previous register epilogue's stores.
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (TRANS && !first)
+            wait_vmcnt_lds<(16 + kEpiStores < 63 ? 16 + kEpiStores : 63)>();
+        else
+            wait_vmcnt_lds<16>();
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        B_RSRC()
+        const int live = m_end - m0 - wm * 128;
+        i32x8 a0[4], b0[4], a1[4], b1[4];
+        {
+            const uint8_t *sA = UNIT(0), *sB = UNIT(1);  // A_0, B_0: step 0's fragments
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a0[i] = frag32(sA, wm * 128 + i * 32 + (lane & 31), 2 * g);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b0[j] = frag32(sB, B_ROW(j), 2 * g);
+        }
+
+        // Stage kt: step 0 (K bytes 0-63 of the rows: pieces 2g, 2g+1) then
+        // step 1 (pieces 4 + 2g, 5 + 2g).  Step 0 streams A_{kt+2} into the
+        // unit B_{kt-1} left, one load per two MFMAs, and reads step 1's
+        // fragments; then, once A_{kt+1} and B_{kt+1} have landed (only
+        // A_{kt+2}'s 8 loads may remain), a barrier frees A_kt's and B_kt's
+        // units; step 1 streams B_{kt+2} into A_kt's unit and reads stage
+        // kt+1's first fragments.  Stage kt+1's scales are loaded first.
+#define DMA_S0(x) if ((x) & 1) ISSUE_A(kt + 2, (x) >> 1, fA)
+#define DMA_S1(x) if (((x) & 1) == 0) ISSUE_B(kt + 2, (x) >> 1, fB)
+#define KLOOP(NB_)                                                                             \
+        {                                                                                      \
+            int u0 = 0;                                                                        \
+            for (int kt = 0; kt < nk; ++kt) {                                                  \
+                const int u1 = u0 + 1 - (u0 + 1 >= NUNIT ? NUNIT : 0);                         \
+                const int u2 = u0 + 2 - (u0 + 2 >= NUNIT ? NUNIT : 0);                         \
+                const int u3 = u0 + 3 - (u0 + 3 >= NUNIT ? NUNIT : 0);                         \
+                const int u4 = u0 + 4 - (u0 + 4 >= NUNIT ? NUNIT : 0);                         \
+                const uint8_t *cA = UNIT(u0), *cB = UNIT(u1);                                  \
+                uint8_t *fA = UNIT(u4), *fB = UNIT(u0); /* A_{kt+2}, B_{kt+2} */               \
+                int ea_[4];                                                                    \
+                _Pragma("unroll") for (int i = 0; i < 4; ++i) ea_[i] = e8m0(sa[i]);            \
+                const int eb0_ = e8m0(sw[0]), eb1_ = e8m0(sw[1]);                              \
+                LOAD_SCALES(kt + 1, sa_n, sw_n);                                               \
+                STEP(a0, b0, a1, b1, cA, cB, 4 + 2 * g, DMA_S0, NB_, ea_, eb0_, eb1_);         \
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);                                       \
+                wait_vmcnt_lds<8>();          /* A_{kt+1}, B_{kt+1} landed for this wave */    \
+                __builtin_amdgcn_s_barrier(); /* ... for all waves; A_kt, B_kt no longer read */ \
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);                                       \
+                const uint8_t *nA = UNIT(u2), *nB = UNIT(u3);                                  \
+                STEP(a1, b1, a0, b0, nA, nB, 2 * g, DMA_S1, NB_, ea_, eb0_, eb1_);             \
+                _Pragma("unroll") for (int i = 0; i < 4; ++i) sa[i] = sa_n[i];                 \
+                sw[0] = sw_n[0];                                                               \
+                sw[1] = sw_n[1];                                                               \
+                u0 = u2;                                                                       \
+            }                                                                                  \
+        }
+        switch (live <= 0 ? 0 : live >= 128 ? 4 : (live + 31) / 32) {
+            case 4: KLOOP(4) break;
+            case 3: KLOOP(3) break;
+            case 2: KLOOP(2) break;
+            case 1: KLOOP(1) break;
+            default: KLOOP(0) break;
+        }
+#undef KLOOP
+#undef DMA_S0
+#undef DMA_S1
+#undef STEP
+#undef FRAG_READ
+#undef READ_AT
+#undef B_ROW
+        __syncthreads();  // every wave done with the ring (and its loads landed)
+        first = false;
+        const int cm0 = m0, cm_end = m_end, cn0 = n0;  // this tile, for its epilogue
+        const int c4 = 4 * g;
+
+        if constexpr (TRANS) {
+            // The ring's first four units take the next tile's first two
+            // stages now, so they land while the epilogue runs.
+            if (t + P < total) {
+                TILE_SETUP(t + P);
+                PROLOGUE_LOADS();
+            }
+            // Lane: tile rows wm*128 + 32i + (lane & 31); per 32-column block,
+            // 4 runs of 4 consecutive columns.  Every lane issues every store
+            // (padding rows, and lanes that do not own a scale, get an offset
+            // past the end of the resource, which the hardware drops).
+            if constexpr (DUAL) {
+                // h = silu(g) u; the tile's 128 h columns are one quantisation
+                // tile: this wave's 64 (both lane halves), then the other
+                // column wave's through the free fifth unit
+                float *xch = reinterpret_cast<float *>(UNIT(4));  // [2][256] row amax
+                float am[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float m = 0.f;
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            m = fmaxf(m, fabsf(swiglu(acc_read(acc[i][jj][r]), acc_read(acc[i][2 + jj][r]))));
+                    m = fmaxf(m, __shfl_xor(m, 32, 64));
+                    am[i] = m;
+                    if (g == 0) xch[wn * 256 + wm * 128 + 32 * i + lane] = m;
+                }
+                __syncthreads();
+                const __amdgpu_buffer_rsrc_t rQ = buf_rsrc(p.hq, (uint32_t)p.M * (uint32_t)p.N);
+                const __amdgpu_buffer_rsrc_t rS = buf_rsrc(p.hs, (uint32_t)p.M * (uint32_t)(p.N / 128) * 4u);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tr = wm * 128 + 32 * i + (lane & 31);
+                    const int row = cm0 + tr;
+                    const float s = e4m3_tile_scale(fmaxf(am[i], xch[(wn ^ 1) * 256 + tr]));
+                    const float inv = 1.0f / s;  // a power of two: h * inv == h / s exactly
+                    const bool ok = row < cm_end;
+                    const uint32_t qbase = ok ? (uint32_t)row * (uint32_t)p.N + (uint32_t)cn0 : kOobOff;
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) {
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            uint32_t w = 0;
+#pragma unroll
+                            for (int u = 0; u < 4; ++u)
+                                w |= f32_to_e4m3(swiglu(acc_read(acc[i][jj][4 * q + u]), acc_read(acc[i][2 + jj][4 * q + u])) * inv)
+                                     << (8 * u);
+                            const int col = wn * 64 + jj * 32 + 8 * q + c4;
+                            __builtin_amdgcn_raw_buffer_store_b32((int)w, rQ, qbase + (uint32_t)col, 0, 0);
+                        }
+                    }
+                    const uint32_t so = (ok && wn == 0 && g == 0)
+                                            ? ((uint32_t)row * (uint32_t)(p.N / 128) + (uint32_t)(cn0 / 128)) * 4u
+                                            : kOobOff;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(s), rS, so, 0, 0);
+                }
+            } else if constexpr (EPI == MX_STORE) {
+                const __amdgpu_buffer_rsrc_t rOut = buf_rsrc(p.out, (uint32_t)p.M * (uint32_t)p.N * 2u);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = cm0 + wm * 128 + 32 * i + (lane & 31);
+                    const uint32_t obase = row < cm_end ? ((uint32_t)row * (uint32_t)p.N + (uint32_t)cn0) * 2u : kOobOff;
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const uint32_t lo = pack_bf16x2(acc_read(acc[i][jj][4 * q]), acc_read(acc[i][jj][4 * q + 1]));
+                            const uint32_t hi = pack_bf16x2(acc_read(acc[i][jj][4 * q + 2]), acc_read(acc[i][jj][4 * q + 3]));
+                            const int col = wn * 128 + jj * 32 + 8 * q + c4;
+                            __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)lo, (int)hi}, rOut, obase + (uint32_t)col * 2u,
+                                                                  0, 0);
+                        }
+                    }
+                }
+            } else {
+                const __amdgpu_buffer_rsrc_t rOutF = buf_rsrc(p.yout, (uint32_t)p.M * (uint32_t)p.ldo * 4u);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = cm0 + wm * 128 + 32 * i + (lane & 31);
+                    const uint32_t obase = row < cm_end ? ((uint32_t)row * (uint32_t)p.ldo + (uint32_t)cn0) * 4u : kOobOff;
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int col = wn * 128 + jj * 32 + 8 * q + c4;
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                i32x4{__float_as_int(acc_read(acc[i][jj][4 * q])), __float_as_int(acc_read(acc[i][jj][4 * q + 1])),
+                                      __float_as_int(acc_read(acc[i][jj][4 * q + 2])),
+                                      __float_as_int(acc_read(acc[i][jj][4 * q + 3]))},
+                                rOutF, obase + (uint32_t)col * 4u, 0, 0);
+                        }
+                    }
+                }
+            }
+        } else {
+            // Combine epilogue: four 64-row chunks of the fp32 tile through
+            // LDS, so every y_perm gather and y store is a 16-byte access.
+            float *ch = reinterpret_cast<float *>(smem);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (wm == (c >> 1)) {
+#pragma unroll
+                    for (int ii = 0; ii < 2; ++ii) {
+                        const int i = 2 * (c & 1) + ii;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int col = wn * 128 + j * 32 + (lane & 31);
+#pragma unroll
+                            for (int r = 0; r < 16; ++r)
+                                ch[(ii * 32 + 8 * (r >> 2) + 4 * g + (r & 3)) * kChLd + col] = acc[i][j][r];
+                        }
+                    }
+                }
+                __syncthreads();
+                const int cl = 8 * (lane & 31);
+#pragma unroll 2
+                for (int it = 0; it < 8; ++it) {
+                    const int rl = wave * 16 + 2 * it + g;
+                    const int row = cm0 + c * kChRows + rl;
+                    if (row < cm_end) {
+                        int rof[8];
+                        float wj[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            rof[j] = p.row_of[(size_t)row * 8 + j];
+                            wj[j] = p.cw[(size_t)row * 8 + j];
+                        }
+                        i32x4 yv[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            yv[j] = *reinterpret_cast<const i32x4 *>(p.y_perm + (size_t)rof[j] * p.N + cn0 + cl);
+                        const float *cr = ch + rl * kChLd + cl;
+                        const f32x4 s0 = *reinterpret_cast<const f32x4 *>(cr);
+                        const f32x4 s1 = *reinterpret_cast<const f32x4 *>(cr + 4);
+                        float v[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) {
+                                v[2 * u] += wj[j] * bf16_to_f32((uint32_t)yv[j][u] & 0xffffu);
+                                v[2 * u + 1] += wj[j] * bf16_to_f32((uint32_t)yv[j][u] >> 16);
+                            }
+                        float *yo = p.yout + (size_t)row * p.N + cn0 + cl;
+                        *reinterpret_cast<f32x4 *>(yo) = f32x4{v[0], v[1], v[2], v[3]};
+                        *reinterpret_cast<f32x4 *>(yo + 4) = f32x4{v[4], v[5], v[6], v[7]};
+                    }
+                }
+                __syncthreads();
+            }
+            if (t + P < total) {
+                TILE_SETUP(t + P);
+                PROLOGUE_LOADS();
+            }
+        }
+    }
+#undef TILE_SETUP
+#undef PROLOGUE_LOADS
+#undef LOAD_SCALES
+#undef B_RSRC
+#undef ISSUE_A
+#undef ISSUE_B
+#undef UNIT
+}
+
+int cu_count_mx() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+}  // namespace
+
+bool ffn_fp8_mx_ok(const FfnArgs &a) {
+    const int groups = a.offsets ? a.E : 1;
+    const unsigned long long lim = kOobOff - (1ULL << 20);
+    const unsigned long long arows = a.a_rows ? (unsigned long long)a.M / a.a_div : (unsigned long long)a.M;
+    const bool fits = arows * a.d < lim && (unsigned long long)a.M * a.I < lim && (unsigned long long)a.I * a.d < lim &&
+                      (unsigned long long)a.M * a.d * 4 < lim && (unsigned long long)a.M * a.d * 2 < lim;
+    return fits && (long long)a.M >= 128LL * groups && a.I % 256 == 0 && a.d % 256 == 0;
+}
+
+// Phase 1 (gate/up, fused SwiGLU + h quantisation) and / or phase 2 (down:
+// bf16 y_perm, or the shared expert's output with the weighted combine).
+hipError_t launch_ffn_fp8_mx(const FfnArgs &a, hipStream_t s) {
+    const int P = (cu_count_mx() / 8) * 8;
+    const bool routed = a.offsets != nullptr;
+    if (a.phases & 1) {
+        MxParams p{};
+        p.M = a.M;
+        p.offsets = a.offsets;
+        p.A = static_cast<const uint8_t *>(a.a);
+        p.As = a.a_scale;
+        p.a_rows = a.a_rows;
+        p.a_div = a.a_rows ? a.a_div : 1;
+        p.K = a.d;
+        p.B0 = static_cast<const uint8_t *>(a.w.gate);
+        p.B1 = static_cast<const uint8_t *>(a.w.up);
+        p.S0 = a.w.s_gate;
+        p.S1 = a.w.s_up;
+        p.N = a.I;
+        p.hq = static_cast<uint8_t *>(a.h);
+        p.hs = a.h_scale;
+        if (routed) hipLaunchKernelGGL((k_gemm_fp8_mx<MX_SWIGLU_Q, true>), dim3(P), dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((k_gemm_fp8_mx<MX_SWIGLU_Q, false>), dim3(P), dim3(256), 0, s, p);
+    }
+    if (a.phases & 2) {
+        MxParams q{};
+        q.M = a.M;
+        q.offsets = a.offsets;
+        q.A = static_cast<const uint8_t *>(a.h);
+        q.As = a.h_scale;
+        q.a_div = 1;
+        q.K = a.I;
+        q.B0 = static_cast<const uint8_t *>(a.w.down);
+        q.S0 = a.w.s_down;
+        q.N = a.d;
+        if (a.combine) {
+            q.yout = static_cast<float *>(a.y);
+            q.y_perm = static_cast<const uint16_t *>(a.y_perm);
+            q.row_of = a.row_of;
+            q.cw = a.cw;
+            hipLaunchKernelGGL((k_gemm_fp8_mx<MX_COMBINE, false>), dim3(P), dim3(256), 0, s, q);
+            return hipGetLastError();
+        }
+        q.out = static_cast<uint16_t *>(a.y);
+        if (routed) hipLaunchKernelGGL((k_gemm_fp8_mx<MX_STORE, true>), dim3(P), dim3(256), 0, s, q);
+        else hipLaunchKernelGGL((k_gemm_fp8_mx<MX_STORE, false>), dim3(P), dim3(256), 0, s, q);
+    }
+    return hipGetLastError();
+}
+
+bool fp8_mx_gemm_ok(const Fp8GemmArgs &g) {
+    const int groups = g.offsets ? kE : 1;
+    const unsigned long long lim = kOobOff - (1ULL << 20);
+    const unsigned long long a_rows = g.a_rows ? (unsigned long long)g.a_src_rows : (unsigned long long)g.M;
+    return (long long)g.M >= 128LL * groups && g.N % LB == 0 && g.K % LKB == 0 && a_rows * g.K < lim &&
+           a_rows * (g.K / LKB) * 4 < lim && (unsigned long long)g.N * g.K < lim &&
+           (unsigned long long)g.M * g.ldo * 4 < lim && g.ldo >= g.N && (!g.a_rows || g.M / g.a_div == g.a_src_rows);
+}
+
+hipError_t launch_fp8_mx_gemm(const Fp8GemmArgs &g, hipStream_t s) {
+    const int P = (cu_count_mx() / 8) * 8;
+    MxParams p{};
+    p.M = g.M;
+    p.offsets = g.offsets;
+    p.A = g.A;
+    p.As = g.As;
+    p.a_rows = g.a_rows;
+    p.a_div = g.a_rows ? g.a_div : 1;
+    p.K = g.K;
+    p.B0 = g.B;
+    p.S0 = g.Bs;
+    p.N = g.N;
+    p.yout = g.out;
+    p.ldo = g.ldo;
+    if (g.offsets) hipLaunchKernelGGL((k_gemm_fp8_mx<MX_F32, true>), dim3(P), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((k_gemm_fp8_mx<MX_F32, false>), dim3(P), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace moe

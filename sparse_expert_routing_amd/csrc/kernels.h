@@ -117,7 +117,7 @@ struct LargeGemmArgs {
 bool bf16_large_gemm_ok(const LargeGemmArgs &g);
 hipError_t launch_bf16_large_gemm(const LargeGemmArgs &g, hipStream_t s);
 
-// An e4m3 NT product on the persistent fp8 kernel with an fp32 output:
+// An e4m3 NT product on the persistent e4m3 kernel with an fp32 output:
 // out[m*ldo + n] = sum_kb s_a(m, kb) s_b(n/128, kb) sum_k A(m,k) B(n,k), A rows
 // per 1x128 tile (As [rows, K/128]), B [G, N, K] with 128x128 block scales
 // Bs [G, N/128, K/128]; grouped over M by offsets (B per group) or one group.
@@ -136,11 +136,13 @@ struct Fp8GemmArgs {
     float *out;
     int ldo;
 };
-bool fp8_large_gemm_ok(const Fp8GemmArgs &g);
-hipError_t launch_fp8_large_gemm(const Fp8GemmArgs &g, hipStream_t s);
 // Large-group e4m3 path (persistent 256x256 tiles, fp32 promotion per 128 of K).
-bool ffn_fp8_large_ok(const FfnArgs &a);
-hipError_t launch_ffn_fp8_large(const FfnArgs &a, hipStream_t s);
+// The e4m3 large-group path on the bf16 kernel's schedule (4 waves, AGPR
+// accumulators), scales applied by the block-scaled MFMA (csrc/ffn_fp8_mx.hip).
+bool ffn_fp8_mx_ok(const FfnArgs &a);
+hipError_t launch_ffn_fp8_mx(const FfnArgs &a, hipStream_t s);
+bool fp8_mx_gemm_ok(const Fp8GemmArgs &g);
+hipError_t launch_fp8_mx_gemm(const Fp8GemmArgs &g, hipStream_t s);
 
 hipError_t launch_bias_update(int E, int k, int T, const int32_t *counts, float gamma, float *bias,
                               hipStream_t s);
