@@ -26,9 +26,7 @@ FLAGS = [
 ]
 
 
-# Per-file extra flags.  The fp8 large-tile GEMM folds each MFMA partial into
-# its accumulator with vector-ALU work, so its MFMAs must write VGPRs (the
-# partials), not AGPRs (which hold the accumulators).
+# Per-file extra flags (none needed at present).
 FILE_FLAGS = {
 }
 

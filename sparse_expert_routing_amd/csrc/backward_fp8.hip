@@ -282,12 +282,9 @@ __global__ __launch_bounds__(256) void k_q8_rows(int64_t R, int C, const void *_
 #pragma unroll
     for (int s = 1; s < 16; s <<= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
     const float s = e4m3_tile_scale(m);
-    uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        w0 |= f32_to_e4m3(v[i] / s) << (8 * i);
-        w1 |= f32_to_e4m3(v[4 + i] / s) << (8 * i);
-    }
+    const float inv = 1.0f / s;  // a power of two: v * inv == v / s exactly
+    const uint32_t w0 = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    const uint32_t w1 = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
     *reinterpret_cast<uint2 *>(q + r * ldo + c0) = uint2{w0, w1};
     if (l == 0) sc[r * tpr + tb] = s;
 }
@@ -384,13 +381,12 @@ __global__ __launch_bounds__(256) void k_q8_cols(int R, const void *__restrict__
     __syncthreads();
     const float amax = fmaxf(fmaxf(red[0][lane], red[1][lane]), fmaxf(red[2][lane], red[3][lane]));
     const float s = e4m3_tile_scale(amax);
+    const float inv = 1.0f / s;  // a power of two: v * inv == v / s exactly
     uint32_t w[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-        uint32_t v = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) v |= f32_to_e4m3(tile[32 * wave + 4 * q + b][lane] / s) << (8 * b);
-        w[q] = v;
+        const int r0 = 32 * wave + 4 * q;
+        w[q] = e4m3x4(tile[r0][lane] * inv, tile[r0 + 1][lane] * inv, tile[r0 + 2][lane] * inv, tile[r0 + 3][lane] * inv);
     }
     i32x4 *o = reinterpret_cast<i32x4 *>(out + (int64_t)(c0 + lane) * ldo + pos0 + 32 * wave);
     o[0] = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};

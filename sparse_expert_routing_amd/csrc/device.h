@@ -49,6 +49,17 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
     return sign | (code > 0x7eu ? 0x7eu : code);
 }
 
+// Four values already in the e4m3 range (|v| <= 448, as a tile's values
+// divided by its scale are) -> four OCP e4m3 codes in one word (byte i from
+// the i-th value), by the hardware conversion: round to nearest even, the
+// same codes as f32_to_e4m3 on that range (checked exhaustively over ties,
+// subnormals and the top of the range on gfx950).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
 // Scale of one e4m3 tile (1x128 activations, 128x128 weight blocks): the
 // smallest power of two at or above amax / 448 (fp32 division), 1 for an
 // all-zero tile.  A power of two: dividing by it is exact, and its exponent

@@ -147,11 +147,9 @@ __device__ __forceinline__ uint2 quant8(uint4 raw, float &scale) {
     amax = wave_max_f32(amax, 16);
     const float s = e4m3_tile_scale(amax);
     scale = s;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(v[i] / s) << (8 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(v[4 + i] / s) << (8 * i);
+    const float inv = 1.0f / s;  // a power of two: v * inv == v / s exactly
+    const uint32_t lo = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    const uint32_t hi = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
     return make_uint2(lo, hi);
 }
 

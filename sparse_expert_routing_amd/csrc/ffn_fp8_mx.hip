@@ -270,11 +270,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
         pBu = DUAL ? p.B1 + (size_t)e * p.N * K : pBg;                                         \
         swg_p = p.S0 + ((size_t)e * nbk + (DUAL ? n0 : n0 + wn * 128) / 128) * nk;             \
         swu_p = DUAL ? p.S1 + ((size_t)e * nbk + n0 / 128) * nk : swg_p;                       \
-        int ar_[8];                                                                            \
+        int ar_[8], sr_[4];                                                                    \
         _Pragma("unroll") for (int i = 0; i < 8; ++i) ar_[i] = min(m0 + drow[i], m_end - 1);    \
-        if (p.a_rows) {                                                                        \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                          \
+            sr_[i] = min(m0 + wm * 128 + 32 * i + (lane & 31), m_end - 1);                     \
+        if (p.a_rows) { /* the 12 row lookups issued together */                               \
             _Pragma("unroll") for (int i = 0; i < 8; ++i) ar_[i] = p.a_rows[ar_[i]];            \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i) sr_[i] = p.a_rows[sr_[i]];            \
             _Pragma("unroll") for (int i = 0; i < 8; ++i) ar_[i] /= p.a_div;                    \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i) sr_[i] /= p.a_div;                    \
         }                                                                                      \
         _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                        \
             aoff[i] = (uint32_t)ar_[i] * (uint32_t)K + (uint32_t)dcol[i];                      \
@@ -282,12 +286,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
             const int br = DUAL ? n0 + (r & (BN - 1)) : n0 + r;                                \
             boff[i] = (uint32_t)br * (uint32_t)K + (uint32_t)dcol[i];                          \
             if (m0 + r >= m_end) aoff[i] = kOobOff; /* padding rows fetch nothing */           \
-        }                                                                                      \
-        int sr_[4];                                                                            \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                          \
-            sr_[i] = min(m0 + wm * 128 + 32 * i + (lane & 31), m_end - 1);                     \
-        if (p.a_rows) {                                                                        \
-            _Pragma("unroll") for (int i = 0; i < 4; ++i) sr_[i] = p.a_rows[sr_[i]] / p.a_div;  \
         }                                                                                      \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) soff[i] = (uint32_t)sr_[i] * (uint32_t)nk * 4u; \
     }
@@ -433,21 +431,30 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
                 // h = silu(g) u; the tile's 128 h columns are one quantisation
                 // tile: this wave's 64 (both lane halves), then the other
                 // column wave's through the free fifth unit
+                // h is formed once and kept in registers (the K loop's fragment
+                // registers are free here) for the quantisation pass
                 float *xch = reinterpret_cast<float *>(UNIT(4));  // [2][256] row amax
                 float am[4];
+                float hv[4][2][16];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float m = 0.f;
 #pragma unroll
                     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            m = fmaxf(m, fabsf(swiglu(acc_read(acc[i][jj][r]), acc_read(acc[i][2 + jj][r]))));
+                        for (int r = 0; r < 16; ++r) {
+                            hv[i][jj][r] = swiglu(acc_read(acc[i][jj][r]), acc_read(acc[i][2 + jj][r]));
+                            m = fmaxf(m, fabsf(hv[i][jj][r]));
+                        }
                     m = fmaxf(m, __shfl_xor(m, 32, 64));
                     am[i] = m;
                     if (g == 0) xch[wn * 256 + wm * 128 + 32 * i + lane] = m;
                 }
-                __syncthreads();
+                // LDS only: the next tile's loads (issued above) stay in flight
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                wait_vmcnt_lds<63>();
+                __builtin_amdgcn_s_barrier();
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
                 const __amdgpu_buffer_rsrc_t rQ = buf_rsrc(p.hq, (uint32_t)p.M * (uint32_t)p.N);
                 const __amdgpu_buffer_rsrc_t rS = buf_rsrc(p.hs, (uint32_t)p.M * (uint32_t)(p.N / 128) * 4u);
 #pragma unroll
@@ -463,11 +470,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
                         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            uint32_t w = 0;
-#pragma unroll
-                            for (int u = 0; u < 4; ++u)
-                                w |= f32_to_e4m3(swiglu(acc_read(acc[i][jj][4 * q + u]), acc_read(acc[i][2 + jj][4 * q + u])) * inv)
-                                     << (8 * u);
+                            const uint32_t w = e4m3x4(hv[i][jj][4 * q] * inv, hv[i][jj][4 * q + 1] * inv,
+                                                      hv[i][jj][4 * q + 2] * inv, hv[i][jj][4 * q + 3] * inv);
                             const int col = wn * 64 + jj * 32 + 8 * q + c4;
                             __builtin_amdgcn_raw_buffer_store_b32((int)w, rQ, qbase + (uint32_t)col, 0, 0);
                         }
