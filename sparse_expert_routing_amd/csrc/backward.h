@@ -31,6 +31,10 @@ size_t dwr_part_bytes(int d);
 hipError_t dwr(int d, const int32_t *offsets, const int32_t *row_src, const float *dl, const uint16_t *x,
                float *part, float *dwr, hipStream_t s);
 
+// Zeroes out + e*per [per floats] for every group e with no rows
+// (off[e+1] == off[e]); per a multiple of 4.
+hipError_t zero_empty(int64_t per, const int32_t *off, float *out, hipStream_t s);
+
 // dx[t] += dxs[t] + sum_j dxp[row_of[t*k+j]].
 hipError_t dx(int T, int d, const float *dxs, const float *dxp, const int32_t *row_of, float *dx, hipStream_t s);
 

@@ -582,6 +582,11 @@ hipError_t dwr(int d, const int32_t *offsets, const int32_t *row_src, const floa
     return hipGetLastError();
 }
 
+hipError_t zero_empty(int64_t per, const int32_t *off, float *out, hipStream_t s) {
+    hipLaunchKernelGGL(k_zero_empty, dim3(256, kE), dim3(256), 0, s, per, off, out);
+    return hipGetLastError();
+}
+
 hipError_t dx(int T, int d, const float *dxs, const float *dxp, const int32_t *row_of, float *dx_out, hipStream_t s) {
     const int64_t n = (int64_t)T * (d / 4);
     hipLaunchKernelGGL(k_bwd_dx, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, T, d, dxs, dxp, row_of, dx_out);

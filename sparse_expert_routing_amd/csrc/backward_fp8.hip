@@ -20,7 +20,8 @@
 //
 // The M-grouped and plain products with block-scaled weights (the recompute
 // and the data gradients) run on the forward's persistent e4m3 kernel with an
-// fp32 epilogue when the shape fits it.
+// fp32 epilogue, and the weight gradients on its K-grouped form, when the
+// shape fits it; k_fgemm takes the rest.
 // k_fgemm: C = A B^T with both operands K-contiguous e4m3 codes, 128x128
 // tiles, one 128-wide scale block per stage (two v_mfma_scale 32x32x64 fp8
 // per 32x32 block, accumulating in fp32, the power-of-two scales s_a[row, kb]
@@ -649,6 +650,20 @@ hipError_t launch_backward_fp8(const BackwardArgs &a, void *ws, hipStream_t s) {
     CHK(q8_cols<false>(A, d, w.dyo, d, nullptr, 1, a.offsets, w.poff, Rp, w.dyT, w.dyTs, s));
     CHK(q8_cols<false>(A, I, w.h, I, nullptr, 1, a.offsets, w.poff, Rp, w.hT, w.hTs, s));
     CHK(q8_cols<false>(A, 2 * I, w.dab, 2 * I, nullptr, 1, a.offsets, w.poff, Rp, w.dabT, w.dabTs, s));
+    // K-grouped products (row scales on both operands): the persistent e4m3
+    // kernel's K-grouped form when the shape fits it (it skips empty groups,
+    // which are zeroed here), else k_fgemm
+    auto kg = [&](const FGemm &p, bool grouped) -> hipError_t {
+        Fp8KgArgs g{};
+        g.M = p.M; g.N = p.N; g.K = p.K; g.kseg = grouped ? p.offsets : nullptr; g.A = p.A; g.As = p.As;
+        g.B = p.B; g.Bs = p.Bs; g.out = p.C; g.ldo = (int)p.ldc; g.cstride = p.cstride;
+        if (p.lda == p.K && p.ldb == p.K && p.ldas == p.K / FK && p.ldbs == p.K / FK && fp8_mx_kg_ok(g)) {
+            const hipError_t r = launch_fp8_mx_kg(g, s);
+            if (r != hipSuccess || !grouped) return r;
+            return bwd::zero_empty((int64_t)p.M * p.ldc, p.offsets, p.C, s);
+        }
+        return grouped ? fgemm<FG_K>(p, s) : fgemm<FG_NONE>(p, s);
+    };
     {
         FGemm p{};
         p.K = (int)Rp; p.offsets = w.poff; p.lda = Rp; p.ldas = Rp / 128; p.a_div = 1; p.ldb = Rp; p.ldbs = Rp / 128;
@@ -656,13 +671,13 @@ hipError_t launch_backward_fp8(const BackwardArgs &a, void *ws, hipStream_t s) {
         // dW_gate[e] = Q(da)^T Q(x), dW_up[e] = Q(db)^T Q(x): [I, d]
         p.M = I; p.N = d; p.B = w.xT; p.Bs = w.xTs; p.ldc = d; p.cstride = (int64_t)I * d;
         p.A = w.dabT; p.As = w.dabTs; p.C = a.dw_gate;
-        CHK(fgemm<FG_K>(p, s));
+        CHK(kg(p, true));
         p.A = w.dabT + (int64_t)I * Rp; p.As = w.dabTs + (int64_t)I * (Rp / 128); p.C = a.dw_up;
-        CHK(fgemm<FG_K>(p, s));
+        CHK(kg(p, true));
         // dW_down[e] = Q(output gradient)^T Q(h): [d, I]
         p.M = d; p.N = I; p.A = w.dyT; p.As = w.dyTs; p.B = w.hT; p.Bs = w.hTs; p.ldc = I; p.cstride = (int64_t)d * I;
         p.C = a.dw_down;
-        CHK(fgemm<FG_K>(p, s));
+        CHK(kg(p, true));
     }
     // the shared expert: its T rows in token order, groups of 128 tokens
     CHK(q8_cols<true>(T, d, x, d, nullptr, 1, nullptr, nullptr, Tp, w.xsT, w.xsTs, s));
@@ -674,11 +689,11 @@ hipError_t launch_backward_fp8(const BackwardArgs &a, void *ws, hipStream_t s) {
         p.K = (int)Tp; p.lda = Tp; p.ldas = Tp / 128; p.a_div = 1; p.ldb = Tp; p.ldbs = Tp / 128; p.bdiv = 1;
         p.M = I; p.N = d; p.B = w.xsT; p.Bs = w.xsTs; p.ldc = d;
         p.A = w.dabsT; p.As = w.dabsTs; p.C = a.ds_gate;
-        CHK(fgemm<FG_NONE>(p, s));
+        CHK(kg(p, false));
         p.A = w.dabsT + (int64_t)I * Tp; p.As = w.dabsTs + (int64_t)I * (Tp / 128); p.C = a.ds_up;
-        CHK(fgemm<FG_NONE>(p, s));
+        CHK(kg(p, false));
         p.M = d; p.N = I; p.A = w.dysT; p.As = w.dysTs; p.B = w.hsT; p.Bs = w.hsTs; p.ldc = I; p.C = a.ds_down;
-        CHK(fgemm<FG_NONE>(p, s));
+        CHK(kg(p, false));
     }
     // 7. router (fp32): dl and its share of dx, then the router gradient
     CHK(bwd::router(T, d, x, a.w_router, a.idx, dg, w.dl, a.dx, s));

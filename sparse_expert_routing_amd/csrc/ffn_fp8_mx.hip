@@ -75,6 +75,13 @@ struct MxParams {
     const uint16_t *y_perm;   // MX_COMBINE: routed outputs [M*k, N] bf16
     const int32_t *row_of;    // MX_COMBINE: [M*k]
     const float *cw;          // MX_COMBINE: combine weights [M*k]
+    // K-grouped form (weight gradients, MX_F32): group e reduces over K in
+    // [kseg[e], kseg[e+1]) (multiples of 128) of A [M, K] and B0 [N, K], both
+    // with a scale per row and 128 of K (As [M, K/128], Bs [N, K/128]), into
+    // yout + e * cstride; groups with an empty range are skipped.
+    const int32_t *kseg;
+    const float *Bs;
+    int64_t cstride;
 };
 
 struct TileMap {
@@ -119,6 +126,44 @@ __device__ __forceinline__ void tilemap_find(const TileMap &tm, int mt, int &e, 
     e = __shfl(my_e, owner, 64);
     m0 = __shfl(my_m0, owner, 64);
     m_end = __shfl(my_end, owner, 64);
+}
+
+// K-grouped tile map: lane owns groups 4*lane .. 4*lane+3; a group with a
+// non-empty K range has `per` tiles.  No kseg: one group over [0, K).
+__device__ __forceinline__ void kgmap_init(TileMap &tm, const int32_t *__restrict__ kseg, int K, int per) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) tm.off[i] = kseg ? kseg[lane * 4 + i] : (lane == 0 && i == 0 ? 0 : K);
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        tm.nt[i] = tm.off[i + 1] > tm.off[i] ? per : 0;
+        s += tm.nt[i];
+    }
+    const int incl = wave_incl_scan(s);
+    tm.excl = incl - s;
+    tm.total = __shfl(incl, 63, 64);
+}
+
+__device__ __forceinline__ void kgmap_find(const TileMap &tm, int slot, int &e, int &local) {
+    const int lane = threadIdx.x & 63;
+    const int mine = tm.nt[0] + tm.nt[1] + tm.nt[2] + tm.nt[3];
+    const bool own = slot >= tm.excl && slot < tm.excl + mine;
+    const int owner = __ffsll((unsigned long long)__ballot(own)) - 1;
+    int my_e = 0, my_l = 0;
+    if (own) {
+        int s = slot - tm.excl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (s >= 0 && s < tm.nt[i]) {
+                my_e = lane * 4 + i;
+                my_l = s;
+            }
+            s -= tm.nt[i];
+        }
+    }
+    e = __shfl(my_e, owner, 64);
+    local = __shfl(my_l, owner, 64);
 }
 
 // Byte offset, inside one operand unit, of the 16-byte piece c of tile row
@@ -182,8 +227,9 @@ __device__ __forceinline__ float swiglu(float g, float u) {
     return g * u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
 }
 
-template <int EPI, bool ROUTED>
+template <int EPI, bool ROUTED, bool KG = false>
 __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
+    static_assert(!KG || (EPI == MX_F32 && !ROUTED), "the K-grouped form has an fp32 output, one B");
     constexpr bool DUAL = EPI == MX_SWIGLU_Q;
     constexpr bool TRANS = EPI != MX_COMBINE;
     constexpr int BN = DUAL ? LB / 2 : LB;  // output columns per tile
@@ -194,18 +240,24 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1, g = lane >> 5;
-    const int K = p.K, nk = K / LKB;
+    const int K = p.K, nkall = K / LKB;  // K: the row stride of A and B (bytes)
+    int nk = nkall;                     // stages of the tile (K-grouped: set per tile)
 
     TileMap tm;
-    int Mt;
+    int Mt, total;
     const int NT = p.N / BN;
     if (ROUTED) {
         tilemap_init(tm, p.offsets);
         Mt = tm.total;
+        total = Mt * NT;
+    } else if (KG) {
+        Mt = p.M / LM;
+        kgmap_init(tm, p.kseg, K, Mt * NT);
+        total = tm.total;
     } else {
         Mt = (p.M + LM - 1) / LM;
+        total = Mt * NT;
     }
-    const int total = Mt * NT;
     const int P = gridDim.x;
 
     // DMA geometry: each operand (256 rows x 128 B = 32 blocks of 1 KB) is
@@ -219,15 +271,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
         dcol[i] = ((lane & 7) ^ (row & 7) ^ ((row >> 3) & 1)) * 16;
     }
 
-    int e = 0, m0 = 0, m_end = 0, n0 = 0;
+    int e = 0, m0 = 0, m_end = 0, n0 = 0, kbase = 0;
     const uint32_t a_rows_total = p.a_rows ? (uint32_t)(p.M / p.a_div) : (uint32_t)p.M;
     const __amdgpu_buffer_rsrc_t rA = buf_rsrc(p.A, a_rows_total * (uint32_t)K);
-    const __amdgpu_buffer_rsrc_t rAs = buf_rsrc(p.As, a_rows_total * (uint32_t)nk * 4u);
+    const __amdgpu_buffer_rsrc_t rAs = buf_rsrc(p.As, a_rows_total * (uint32_t)nkall * 4u);
+    const __amdgpu_buffer_rsrc_t rBs = buf_rsrc(KG ? p.Bs : p.As, KG ? (uint32_t)p.N * (uint32_t)nkall * 4u : 4u);
     const uint32_t b_bytes = (uint32_t)p.N * (uint32_t)K;
     const int nbk = p.N / 128;  // weight scale blocks along N
     const uint8_t *pBg = p.B0, *pBu = p.B1;
     const float *swg_p = p.S0, *swu_p = p.S0;
-    uint32_t aoff[8], boff[8], soff[4];
+    uint32_t aoff[8], boff[8], soff[4], bsoff[4];
 
 #define UNIT(u) (smem + (u) * UNIT_BYTES)
 #define ISSUE_A(st_, i, unit_)                                                                 \
@@ -240,33 +293,51 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
                 (unit_) + (wave + 4 * (i)) * 1024)
     // The stage's A-row scales of this lane's 4 rows (one per 32-row block)
     // and the weight block scales of this wave's columns (gate and up).
-#define LOAD_SCALES(st_, sa_, sw_)                                                             \
+#define LOAD_SCALES(st_, sa_, sw_, sb_)                                                        \
         {                                                                                      \
             const int kb_ = min((st_), nk - 1);                                                \
             _Pragma("unroll") for (int i = 0; i < 4; ++i)                                      \
                 sa_[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rAs, soff[i] + kb_ * 4u, 0, 0)); \
-            sw_[0] = swg_p[kb_];                                                               \
-            sw_[1] = DUAL ? swu_p[kb_] : sw_[0];                                               \
+            if (KG) {                                                                          \
+                _Pragma("unroll") for (int j = 0; j < 4; ++j)                                  \
+                    sb_[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rBs, bsoff[j] + kb_ * 4u, 0, 0)); \
+            } else {                                                                           \
+                sw_[0] = swg_p[kb_];                                                           \
+                sw_[1] = DUAL ? swu_p[kb_] : sw_[0];                                           \
+            }                                                                                  \
         }
 #define TILE_SETUP(tt)                                                                         \
     {                                                                                          \
-        const int gsz_ = kGroupM * NT;                                                         \
-        const int grp_ = (tt) / gsz_, within_ = (tt) - grp_ * gsz_;                            \
-        const int mfirst_ = grp_ * kGroupM;                                                    \
-        const int gm_ = min(kGroupM, Mt - mfirst_);                                            \
-        const int mt_ = mfirst_ + within_ % gm_, nt_ = within_ / gm_;                          \
-        if (ROUTED) {                                                                          \
-            tilemap_find(tm, mt_, e, m0, m_end);                                               \
-        } else {                                                                               \
-            e = 0;                                                                             \
+        int mt_, nt_;                                                                          \
+        if (KG) {                                                                              \
+            int loc_;                                                                          \
+            kgmap_find(tm, (tt), e, loc_);                                                     \
+            mt_ = loc_ % Mt;                                                                   \
+            nt_ = loc_ / Mt;                                                                   \
             m0 = mt_ * LM;                                                                     \
             m_end = p.M;                                                                       \
+            kbase = p.kseg ? __builtin_amdgcn_readfirstlane(p.kseg[e]) : 0;                    \
+            nk = p.kseg ? __builtin_amdgcn_readfirstlane((p.kseg[e + 1] - kbase) / LKB) : nkall; \
+        } else {                                                                               \
+            const int gsz_ = kGroupM * NT;                                                     \
+            const int grp_ = (tt) / gsz_, within_ = (tt) - grp_ * gsz_;                        \
+            const int mfirst_ = grp_ * kGroupM;                                                \
+            const int gm_ = min(kGroupM, Mt - mfirst_);                                        \
+            mt_ = mfirst_ + within_ % gm_;                                                     \
+            nt_ = within_ / gm_;                                                               \
+            if (ROUTED) {                                                                      \
+                tilemap_find(tm, mt_, e, m0, m_end);                                           \
+            } else {                                                                           \
+                e = 0;                                                                         \
+                m0 = mt_ * LM;                                                                 \
+                m_end = p.M;                                                                   \
+            }                                                                                  \
         }                                                                                      \
         e = __builtin_amdgcn_readfirstlane(e);                                                 \
         m0 = __builtin_amdgcn_readfirstlane(m0);                                               \
         m_end = __builtin_amdgcn_readfirstlane(m_end);                                         \
         n0 = nt_ * BN;                                                                         \
-        pBg = p.B0 + (size_t)e * p.N * K;                                                      \
+        pBg = KG ? p.B0 : p.B0 + (size_t)e * p.N * K;                                          \
         pBu = DUAL ? p.B1 + (size_t)e * p.N * K : pBg;                                         \
         swg_p = p.S0 + ((size_t)e * nbk + (DUAL ? n0 : n0 + wn * 128) / 128) * nk;             \
         swu_p = DUAL ? p.S1 + ((size_t)e * nbk + n0 / 128) * nk : swg_p;                       \
@@ -281,18 +352,22 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
             _Pragma("unroll") for (int i = 0; i < 4; ++i) sr_[i] /= p.a_div;                    \
         }                                                                                      \
         _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                        \
-            aoff[i] = (uint32_t)ar_[i] * (uint32_t)K + (uint32_t)dcol[i];                      \
+            aoff[i] = (uint32_t)ar_[i] * (uint32_t)K + (uint32_t)(dcol[i] + kbase);            \
             const int r = drow[i];                                                             \
             const int br = DUAL ? n0 + (r & (BN - 1)) : n0 + r;                                \
-            boff[i] = (uint32_t)br * (uint32_t)K + (uint32_t)dcol[i];                          \
+            boff[i] = (uint32_t)br * (uint32_t)K + (uint32_t)(dcol[i] + kbase);                \
             if (m0 + r >= m_end) aoff[i] = kOobOff; /* padding rows fetch nothing */           \
         }                                                                                      \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) soff[i] = (uint32_t)sr_[i] * (uint32_t)nk * 4u; \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                          \
+            soff[i] = ((uint32_t)sr_[i] * (uint32_t)nkall + (uint32_t)(kbase / LKB)) * 4u;     \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j)                                          \
+            bsoff[j] = ((uint32_t)(n0 + wn * 128 + 32 * j + (lane & 31)) * (uint32_t)nkall +   \
+                        (uint32_t)(kbase / LKB)) * 4u;                                         \
     }
     // Stage 0's scales, then A_0, B_0, A_1, B_1 of the tile just set up.
 #define PROLOGUE_LOADS()                                                                       \
     {                                                                                          \
-        LOAD_SCALES(0, sa, sw);                                                                \
+        LOAD_SCALES(0, sa, sw, sb);                                                            \
         B_RSRC()                                                                               \
         _Pragma("unroll") for (int i = 0; i < 8; ++i) ISSUE_A(0, i, UNIT(0));                  \
         _Pragma("unroll") for (int i = 0; i < 8; ++i) ISSUE_B(0, i, UNIT(1));                  \
@@ -300,14 +375,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
         _Pragma("unroll") for (int i = 0; i < 8; ++i) ISSUE_B(1, i, UNIT(3));                  \
     }
 
-    float sa[4], sw[2], sa_n[4], sw_n[2];
+    float sa[4], sw[2], sa_n[4], sw_n[2], sb[4], sb_n[4];
+    // Tile order: every XCD's P/8 workgroups take P/8 consecutive tiles at a
+    // time (one L2 shares their operands): tiles (8i + xcd) P/8 + w in the
+    // i-th pass.
+    const int tlim = total, tstep = P;
     int t = (blockIdx.x & 7) * (P >> 3) + (blockIdx.x >> 3);
-    if (t < total) {
+    if (t < tlim) {
         TILE_SETUP(t);
         PROLOGUE_LOADS();
     }
     bool first = true;
-    for (; t < total; t += P) {
+    for (; t < tlim; t += tstep) {
         f32x16 acc[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -328,14 +407,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
             AN[(r) & 3] = frag32((nA), wm * 128 + ((r) & 3) * 32 + (lane & 31), (cn));         \
         else                                                                                   \
             BN_[(r) & 3] = frag32((nB), B_ROW((r) & 3), (cn));
-#define STEP(AC, BC, AN, BN_, nA, nB, cn, DMA, NB_, EA, EB0, EB1)                              \
+#define STEP(AC, BC, AN, BN_, nA, nB, cn, DMA, NB_, EA, EB)                                   \
         _Pragma("unroll") for (int x = 0; x < 16; ++x) {                                       \
             _Pragma("unroll") for (int r = 0; r < 8; ++r)                                      \
                 if (READ_AT(r) == x) { FRAG_READ(r, AN, BN_, nA, nB, cn) }                     \
             __builtin_amdgcn_sched_barrier(0);                                                 \
             if ((NB_) > (x >> 2))                                                              \
                 acc[x >> 2][x & 3] = mma<TRANS>(AC[x >> 2], BC[x & 3], acc[x >> 2][x & 3], EA[x >> 2], \
-                                                (DUAL && (x & 3) >= 2) ? (EB1) : (EB0));       \
+                                                EB[x & 3]);                                    \
             __builtin_amdgcn_sched_barrier(0);                                                 \
             DMA(x);                                                                            \
             __builtin_amdgcn_sched_barrier(0);                                                 \
@@ -380,18 +459,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
                 const int u4 = u0 + 4 - (u0 + 4 >= NUNIT ? NUNIT : 0);                         \
                 const uint8_t *cA = UNIT(u0), *cB = UNIT(u1);                                  \
                 uint8_t *fA = UNIT(u4), *fB = UNIT(u0); /* A_{kt+2}, B_{kt+2} */               \
-                int ea_[4];                                                                    \
+                int ea_[4], eb_[4];                                                            \
                 _Pragma("unroll") for (int i = 0; i < 4; ++i) ea_[i] = e8m0(sa[i]);            \
-                const int eb0_ = e8m0(sw[0]), eb1_ = e8m0(sw[1]);                              \
-                LOAD_SCALES(kt + 1, sa_n, sw_n);                                               \
-                STEP(a0, b0, a1, b1, cA, cB, 4 + 2 * g, DMA_S0, NB_, ea_, eb0_, eb1_);         \
+                /* B exponents per column block: per lane (K-grouped rows) or the block's */   \
+                _Pragma("unroll") for (int j = 0; j < 4; ++j)                                  \
+                    eb_[j] = KG ? e8m0(sb[j]) : e8m0(sw[DUAL && j >= 2 ? 1 : 0]);              \
+                LOAD_SCALES(kt + 1, sa_n, sw_n, sb_n);                                         \
+                STEP(a0, b0, a1, b1, cA, cB, 4 + 2 * g, DMA_S0, NB_, ea_, eb_);                \
                 __atomic_signal_fence(__ATOMIC_SEQ_CST);                                       \
                 wait_vmcnt_lds<8>();          /* A_{kt+1}, B_{kt+1} landed for this wave */    \
                 __builtin_amdgcn_s_barrier(); /* ... for all waves; A_kt, B_kt no longer read */ \
                 __atomic_signal_fence(__ATOMIC_SEQ_CST);                                       \
                 const uint8_t *nA = UNIT(u2), *nB = UNIT(u3);                                  \
-                STEP(a1, b1, a0, b0, nA, nB, 2 * g, DMA_S1, NB_, ea_, eb0_, eb1_);             \
+                STEP(a1, b1, a0, b0, nA, nB, 2 * g, DMA_S1, NB_, ea_, eb_);                    \
                 _Pragma("unroll") for (int i = 0; i < 4; ++i) sa[i] = sa_n[i];                 \
+                _Pragma("unroll") for (int j = 0; j < 4; ++j) sb[j] = sb_n[j];                 \
                 sw[0] = sw_n[0];                                                               \
                 sw[1] = sw_n[1];                                                               \
                 u0 = u2;                                                                       \
@@ -413,14 +495,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
 #undef B_ROW
         __syncthreads();  // every wave done with the ring (and its loads landed)
         first = false;
-        const int cm0 = m0, cm_end = m_end, cn0 = n0;  // this tile, for its epilogue
+        const int cm0 = m0, cm_end = m_end, cn0 = n0, ce = e;  // this tile, for its epilogue
         const int c4 = 4 * g;
 
         if constexpr (TRANS) {
             // The ring's first four units take the next tile's first two
             // stages now, so they land while the epilogue runs.
-            if (t + P < total) {
-                TILE_SETUP(t + P);
+            if (t + tstep < tlim) {
+                TILE_SETUP(t + tstep);
                 PROLOGUE_LOADS();
             }
             // Lane: tile rows wm*128 + 32i + (lane & 31); per 32-column block,
@@ -501,7 +583,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
                     }
                 }
             } else {
-                const __amdgpu_buffer_rsrc_t rOutF = buf_rsrc(p.yout, (uint32_t)p.M * (uint32_t)p.ldo * 4u);
+                const __amdgpu_buffer_rsrc_t rOutF =
+                    buf_rsrc(KG ? uniform_ptr(p.yout + (size_t)ce * p.cstride) : p.yout, (uint32_t)p.M * (uint32_t)p.ldo * 4u);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = cm0 + wm * 128 + 32 * i + (lane & 31);
@@ -576,8 +659,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
                 }
                 __syncthreads();
             }
-            if (t + P < total) {
-                TILE_SETUP(t + P);
+            if (t + tstep < tlim) {
+                TILE_SETUP(t + tstep);
                 PROLOGUE_LOADS();
             }
         }
@@ -671,6 +754,33 @@ bool fp8_mx_gemm_ok(const Fp8GemmArgs &g) {
     return (long long)g.M >= 128LL * groups && g.N % LB == 0 && g.K % LKB == 0 && a_rows * g.K < lim &&
            a_rows * (g.K / LKB) * 4 < lim && (unsigned long long)g.N * g.K < lim &&
            (unsigned long long)g.M * g.ldo * 4 < lim && g.ldo >= g.N && (!g.a_rows || g.M / g.a_div == g.a_src_rows);
+}
+
+bool fp8_mx_kg_ok(const Fp8KgArgs &g) {
+    const unsigned long long lim = kOobOff - (1ULL << 20);
+    return g.M > 0 && g.M % LM == 0 && g.N % LB == 0 && g.K % LKB == 0 && g.ldo >= g.N &&
+           (unsigned long long)g.M * g.K < lim && (unsigned long long)g.N * g.K < lim &&
+           (unsigned long long)g.M * (g.K / LKB) * 4 < lim && (unsigned long long)g.N * (g.K / LKB) * 4 < lim &&
+           (unsigned long long)g.M * g.ldo * 4 < lim;
+}
+
+hipError_t launch_fp8_mx_kg(const Fp8KgArgs &g, hipStream_t s) {
+    const int P = (cu_count_mx() / 8) * 8;
+    MxParams p{};
+    p.M = g.M;
+    p.A = g.A;
+    p.As = g.As;
+    p.a_div = 1;
+    p.K = g.K;
+    p.B0 = g.B;
+    p.Bs = g.Bs;
+    p.N = g.N;
+    p.yout = g.out;
+    p.ldo = g.ldo;
+    p.kseg = g.kseg;
+    p.cstride = g.cstride;
+    hipLaunchKernelGGL((k_gemm_fp8_mx<MX_F32, false, true>), dim3(P), dim3(256), 0, s, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_fp8_mx_gemm(const Fp8GemmArgs &g, hipStream_t s) {

@@ -136,13 +136,32 @@ struct Fp8GemmArgs {
     float *out;
     int ldo;
 };
-// Large-group e4m3 path (persistent 256x256 tiles, fp32 promotion per 128 of K).
-// The e4m3 large-group path on the bf16 kernel's schedule (4 waves, AGPR
-// accumulators), scales applied by the block-scaled MFMA (csrc/ffn_fp8_mx.hip).
+// K-grouped e4m3 product (weight gradients): for each group e with a
+// non-empty range [kseg[e], kseg[e+1]) (multiples of 128; kseg [257], or
+// nullptr for one group over [0, K)), out + e*cstride [M, ldo] =
+// sum_kb As(m, kb) Bs(n, kb) sum_k A(m,k) B(n,k) over that range.  A [M, K],
+// B [N, K] codes (K the row stride), As [M, K/128], Bs [N, K/128] power-of-two
+// scales.  Groups with an empty range are not written.
+struct Fp8KgArgs {
+    int M, N, K;
+    const int32_t *kseg;
+    const uint8_t *A;
+    const float *As;
+    const uint8_t *B;
+    const float *Bs;
+    float *out;
+    int ldo;
+    int64_t cstride;
+};
+// The e4m3 large-group path on the bf16 kernel's schedule (persistent 256x256
+// tiles, 4 waves, AGPR accumulators), scales applied by the block-scaled
+// MFMA (csrc/ffn_fp8_mx.hip).
 bool ffn_fp8_mx_ok(const FfnArgs &a);
 hipError_t launch_ffn_fp8_mx(const FfnArgs &a, hipStream_t s);
 bool fp8_mx_gemm_ok(const Fp8GemmArgs &g);
 hipError_t launch_fp8_mx_gemm(const Fp8GemmArgs &g, hipStream_t s);
+bool fp8_mx_kg_ok(const Fp8KgArgs &g);
+hipError_t launch_fp8_mx_kg(const Fp8KgArgs &g, hipStream_t s);
 
 hipError_t launch_bias_update(int E, int k, int T, const int32_t *counts, float gamma, float *bias,
                               hipStream_t s);

@@ -35,6 +35,12 @@ def skewed_ids(T, seed):
     return np.ascontiguousarray(np.concatenate([np.tile(np.arange(3, dtype=np.int32), (T, 1)), tail], axis=1))
 
 
+def few_ids(T, seed):
+    """Every token's 8 experts among 16 (every 16th id): the other 240 get no
+    rows, so their weight gradients must come out zero."""
+    return np.ascontiguousarray(synth.random_ids(T + 2, seed, T, 16, 8) * 16)
+
+
 def run_case(T, d, I, kind, seed, wt="bf16"):
     cfg = synth.Config("bwd", seed=seed, T=T, d=d, I=I, wt=wt)
     say(f"[backward] T={T} d={d} I={I} {kind} {wt}")
@@ -49,7 +55,7 @@ def run_case(T, d, I, kind, seed, wt="bf16"):
     if kind == "routed":
         _lib.moe_route(ds, xd, wrd, dev(bias), idx, g, None, ws)
     else:  # a given id pattern; combine weights from the oracle's affinities
-        ids = skewed_ids(T, seed)
+        ids = skewed_ids(T, seed) if kind == "skewed" else few_ids(T, seed)
         _, _, _, s = oracle.route(oracle.shape_of(cfg), x, wr, bias, want_s=True)
         sel = np.take_along_axis(s, ids, 1)
         idx.copy_(torch.from_numpy(ids))
@@ -90,7 +96,8 @@ def run_case(T, d, I, kind, seed, wt="bf16"):
                                              (257, 256, 384, "skewed", 43),
                                              # 128+ rows per expert on average: the data-gradient GEMMs
                                              # run on the persistent 256x256-tile kernel
-                                             (4096, 256, 256, "routed", 44), (4096, 512, 256, "skewed", 45)])
+                                             (4096, 256, 256, "routed", 44), (4096, 512, 256, "skewed", 45),
+                                             (512, 512, 256, "few", 46)])
 def test_backward_matches_oracle(T, d, I, kind, seed):
     run_case(T, d, I, kind, seed)
 
@@ -98,7 +105,9 @@ def test_backward_matches_oracle(T, d, I, kind, seed):
 @pytest.mark.parametrize("T,d,I,kind,seed", [(300, 512, 256, "routed", 51), (1, 256, 128, "routed", 52),
                                              (257, 256, 384, "skewed", 53),
                                              # experts 0-2 with 4096 rows: 32 weight-gradient groups each
-                                             (4096, 512, 256, "skewed", 55)])
+                                             (4096, 512, 256, "skewed", 55),
+                                             # 240 experts with no rows (K-grouped groups skipped, then zeroed)
+                                             (512, 512, 256, "few", 56)])
 def test_backward_e4m3_matches_oracle(T, d, I, kind, seed):
     """Every backward GEMM on e4m3 operands (tiles along each GEMM's
     reduction), against the oracle's e4m3 backward at the fp8 tolerance."""
