@@ -396,36 +396,43 @@ __global__ __launch_bounds__(256) void k_q8_cols(int R, const void *__restrict__
 }
 
 // e4m3 codes transposed per group: out[g][c*ldo + coff + r] = in[g][r*C + c]
-// (R, C multiples of 64), 64x64-byte tiles.  Thread (a, b) reads the 4x4
-// block of rows 4a.. and bytes 4b.. (each row's 16 threads read 64
-// contiguous bytes), transposes it in registers and stages the four words
-// in LDS as output row 4b + j, word a; then each thread stores 16 bytes of
-// one output row.
+// (R, C multiples of 128), 128x128-byte tiles.  Thread (a = tid % 32,
+// b = tid / 32) reads 16 bytes of each of rows 4a .. 4a+3 at columns
+// 16b .. 16b+15 (four 16-byte loads in flight), transposes the four 4x4
+// blocks in registers and puts word a of output rows 16b .. 16b+15 in LDS;
+// then each output row's 128 bytes go out as eight 16-byte stores.  In LDS,
+// output row c holds its 32 words with bits 3-4 of the word index flipped by
+// (c / 16) % 4, so the 64 lanes of a write hit 32 distinct banks twice.
 __global__ __launch_bounds__(256) void k_t8(int R, int C, const uint8_t *__restrict__ in, int64_t gin,
                                             uint8_t *__restrict__ out, int64_t ldo, int64_t gout, int coff) {
-    __shared__ uint32_t tile[64][17];
-    const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64, g = blockIdx.z, tid = threadIdx.x;
+    __shared__ __attribute__((aligned(16))) uint32_t tile[128 * 32];
+    const int r0 = blockIdx.x * 128, c0 = blockIdx.y * 128, g = blockIdx.z, tid = threadIdx.x;
     in += (int64_t)g * gin;
     out += (int64_t)g * gout;
     {
-        const int a = tid >> 4, b = tid & 15;
-        uint32_t v[4];
+        const int a = tid & 31, b = tid >> 5;
+        i32x4 v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            v[i] = *reinterpret_cast<const uint32_t *>(in + (int64_t)(r0 + 4 * a + i) * C + c0 + 4 * b);
-        // word j of the transposed block: byte j of rows 0..3
+            v[i] = *reinterpret_cast<const i32x4 *>(in + (int64_t)(r0 + 4 * a + i) * C + c0 + 16 * b);
+        const int sw = 8 * (b & 3);  // output rows 16b .. 16b+15 share (c / 16) % 4 = b % 4
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t w = ((v[0] >> (8 * j)) & 0xffu) | (((v[1] >> (8 * j)) & 0xffu) << 8) |
-                               (((v[2] >> (8 * j)) & 0xffu) << 16) | (((v[3] >> (8 * j)) & 0xffu) << 24);
-            tile[4 * b + j][a] = w;
-        }
+        for (int sblk = 0; sblk < 4; ++sblk)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // byte j of the four rows' word sblk: output row 16b + 4 sblk + j, rows 4a .. 4a+3
+                const uint32_t w = (((uint32_t)v[0][sblk] >> (8 * j)) & 0xffu) |
+                                   ((((uint32_t)v[1][sblk] >> (8 * j)) & 0xffu) << 8) |
+                                   ((((uint32_t)v[2][sblk] >> (8 * j)) & 0xffu) << 16) |
+                                   ((((uint32_t)v[3][sblk] >> (8 * j)) & 0xffu) << 24);
+                tile[(16 * b + 4 * sblk + j) * 32 + (a ^ sw)] = w;
+            }
     }
     __syncthreads();
-    {
-        const int c = tid >> 2, q = tid & 3;
-        const i32x4 v = i32x4{(int)tile[c][4 * q], (int)tile[c][4 * q + 1], (int)tile[c][4 * q + 2],
-                              (int)tile[c][4 * q + 3]};
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+        const int c = 32 * pass + (tid >> 3), q = tid & 7;
+        const i32x4 v = *reinterpret_cast<const i32x4 *>(&tile[c * 32 + ((4 * q) ^ (8 * ((c >> 4) & 3)))]);
         *reinterpret_cast<i32x4 *>(out + (int64_t)(c0 + c) * ldo + coff + r0 + 16 * q) = v;
     }
 }
@@ -440,7 +447,8 @@ __global__ __launch_bounds__(256) void k_tscale(int Rb, int Cb, const float *__r
 }
 
 hipError_t t8(int R, int C, int G, const void *in, uint8_t *out, int64_t ldo, int coff, hipStream_t s) {
-    hipLaunchKernelGGL(k_t8, dim3(R / 64, C / 64, G), dim3(256), 0, s, R, C, static_cast<const uint8_t *>(in),
+    if (R % 128 != 0 || C % 128 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_t8, dim3(R / 128, C / 128, G), dim3(256), 0, s, R, C, static_cast<const uint8_t *>(in),
                        (int64_t)R * C, out, ldo, (int64_t)C * ldo, coff);
     return hipGetLastError();
 }
