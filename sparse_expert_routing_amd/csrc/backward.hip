@@ -651,6 +651,49 @@ BwdWs carve(char *base, int T, int d, int I, int k) {
     return w;
 }
 
+// Weights transposed per group: out[g][c*ldo + coff + r] = in[g][r*C + c]
+// (bf16; R a multiple of 64, C of 128), 64-row x 128-column tiles.  Thread
+// (a = tid % 16, b = tid / 16) reads 16 bytes (8 values) of each of rows
+// 4a .. 4a+3 at columns 8b .. 8b+7 (four 16-byte loads in flight), and
+// writes each column's 4 values as one 8-byte LDS word of output row 8b + j;
+// each output row's 128 bytes then go out as eight 16-byte stores.
+__global__ __launch_bounds__(256) void k_t16(int R, int C, const uint16_t *__restrict__ in, int64_t gin,
+                                             uint16_t *__restrict__ out, int64_t ldo, int64_t gout, int coff) {
+    __shared__ __attribute__((aligned(16))) uint64_t tile[128 * 16];
+    const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 128, g = blockIdx.z, tid = threadIdx.x;
+    in += (int64_t)g * gin;
+    out += (int64_t)g * gout;
+    {
+        const int a = tid & 15, b = tid >> 4;
+        i32x4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] = *reinterpret_cast<const i32x4 *>(in + (int64_t)(r0 + 4 * a + i) * C + c0 + 8 * b);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            // value j of each row (word j / 2, half j % 2): output row 8b + j, rows 4a .. 4a+3
+            const int sh = 16 * (j & 1);
+            const uint32_t lo = (((uint32_t)v[0][j >> 1] >> sh) & 0xffffu) | ((((uint32_t)v[1][j >> 1] >> sh) & 0xffffu) << 16);
+            const uint32_t hi = (((uint32_t)v[2][j >> 1] >> sh) & 0xffffu) | ((((uint32_t)v[3][j >> 1] >> sh) & 0xffffu) << 16);
+            tile[(8 * b + j) * 16 + a] = (uint64_t)lo | ((uint64_t)hi << 32);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+        const int c = 32 * pass + (tid >> 3), q = tid & 7;
+        const i32x4 v = *reinterpret_cast<const i32x4 *>(&tile[c * 16 + 2 * q]);
+        *reinterpret_cast<i32x4 *>(out + (int64_t)(c0 + c) * ldo + coff + r0 + 8 * q) = v;
+    }
+}
+
+hipError_t t16(int R, int C, int G, const uint16_t *in, uint16_t *out, int64_t ldo, int coff, hipStream_t s) {
+    if (R % 64 != 0 || C % 128 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_t16, dim3(R / 64, C / 128, G), dim3(256), 0, s, R, C, in, (int64_t)R * C, out, ldo,
+                       (int64_t)C * ldo, coff);
+    return hipGetLastError();
+}
+
 // out[g] = in[g] transposed (R x C -> C x R), see k_transpose.  Plain: dend
 // positions (zeros past R).  Grouped (off, poff): R = the total rows.
 hipError_t transpose(int R, int C, int G, const uint16_t *in, int64_t ldi, int64_t gin, const int32_t *rows,
@@ -690,14 +733,12 @@ hipError_t launch_backward(const BackwardArgs &a, void *ws, hipStream_t s) {
 
     // 0. padded row positions of the expert groups; transposed weights
     CHK(bwd::pad_offsets(a.offsets, w.poff, 64, s));
-    CHK(transpose(d, I, E, ed, I, (int64_t)d * I, nullptr, 1, nullptr, nullptr, d, w.wdT, d, (int64_t)I * d, 0, s));
-    CHK(transpose(I, d, E, eg, d, (int64_t)I * d, nullptr, 1, nullptr, nullptr, I, w.wguT, 2 * I, (int64_t)d * 2 * I, 0,
-                  s));
-    CHK(transpose(I, d, E, eu, d, (int64_t)I * d, nullptr, 1, nullptr, nullptr, I, w.wguT, 2 * I, (int64_t)d * 2 * I, I,
-                  s));
-    CHK(transpose(d, I, 1, sd, I, 0, nullptr, 1, nullptr, nullptr, d, w.sdT, d, 0, 0, s));
-    CHK(transpose(I, d, 1, sg, d, 0, nullptr, 1, nullptr, nullptr, I, w.sguT, 2 * I, 0, 0, s));
-    CHK(transpose(I, d, 1, su, d, 0, nullptr, 1, nullptr, nullptr, I, w.sguT, 2 * I, 0, I, s));
+    CHK(t16(d, I, E, ed, w.wdT, d, 0, s));       // [E, I, d]
+    CHK(t16(I, d, E, eg, w.wguT, 2 * I, 0, s));  // [E, d, 2I]: gate | up
+    CHK(t16(I, d, E, eu, w.wguT, 2 * I, I, s));
+    CHK(t16(d, I, 1, sd, w.sdT, d, 0, s));
+    CHK(t16(I, d, 1, sg, w.sguT, 2 * I, 0, s));
+    CHK(t16(I, d, 1, su, w.sguT, 2 * I, I, s));
 
     // 1. combine backward
     CHK(bwd::combine(T, d, a.dy, static_cast<const uint16_t *>(a.y_perm), a.row_of, a.weights, w.dyo, dys, dg, false,
