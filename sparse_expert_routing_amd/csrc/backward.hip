@@ -731,14 +731,32 @@ hipError_t launch_backward(const BackwardArgs &a, void *ws, hipStream_t s) {
 #define CHK(call)                      \
     if ((e = (call)) != hipSuccess) return e;
 
-    // 0. padded row positions of the expert groups; transposed weights
+    // The data-gradient products dh = (output gradient) W_down and
+    // dx = (da | db) (W_gate | W_up) reduce along the weights' rows: the
+    // persistent kernel reads such a B K-major, as stored (W_down [E, d, I]:
+    // K = d; W_gate and W_up [E, I, d]: K = 2I, gate rows then up rows).
+    // Shapes it does not take run on k_bgemm from transposed copies.
+    const LargeGemmArgs gdh{A, a.offsets, w.dyo, nullptr, 1, A, d, ed, nullptr, I, w.dh, I, 0, false,
+                            nullptr, 0, 0, true, 0};
+    const LargeGemmArgs gdhs{T, nullptr, dys, nullptr, 1, T, d, sd, nullptr, I, dhs, I, 0, false, nullptr, 0, 0, true, 0};
+    const LargeGemmArgs gdx{A, a.offsets, w.dab, nullptr, 1, A, 2 * I, eg, eu, d, w.dxi, d, 0, false,
+                            nullptr, 0, 0, true, I};
+    const LargeGemmArgs gdxs{T, nullptr, dabs, nullptr, 1, T, 2 * I, sg, su, d, dxs, d, 0, false, nullptr, 0, 0, true, I};
+    const bool kn_dh = bf16_large_gemm_ok(gdh), kn_dhs = bf16_large_gemm_ok(gdhs);
+    const bool kn_dx = bf16_large_gemm_ok(gdx), kn_dxs = bf16_large_gemm_ok(gdxs);
+
+    // 0. padded row positions of the expert groups; transposed weights where needed
     CHK(bwd::pad_offsets(a.offsets, w.poff, 64, s));
-    CHK(t16(d, I, E, ed, w.wdT, d, 0, s));       // [E, I, d]
-    CHK(t16(I, d, E, eg, w.wguT, 2 * I, 0, s));  // [E, d, 2I]: gate | up
-    CHK(t16(I, d, E, eu, w.wguT, 2 * I, I, s));
-    CHK(t16(d, I, 1, sd, w.sdT, d, 0, s));
-    CHK(t16(I, d, 1, sg, w.sguT, 2 * I, 0, s));
-    CHK(t16(I, d, 1, su, w.sguT, 2 * I, I, s));
+    if (!kn_dh) CHK(t16(d, I, E, ed, w.wdT, d, 0, s));  // [E, I, d]
+    if (!kn_dx) {
+        CHK(t16(I, d, E, eg, w.wguT, 2 * I, 0, s));  // [E, d, 2I]: gate | up
+        CHK(t16(I, d, E, eu, w.wguT, 2 * I, I, s));
+    }
+    if (!kn_dhs) CHK(t16(d, I, 1, sd, w.sdT, d, 0, s));
+    if (!kn_dxs) {
+        CHK(t16(I, d, 1, sg, w.sguT, 2 * I, 0, s));
+        CHK(t16(I, d, 1, su, w.sguT, 2 * I, I, s));
+    }
 
     // 1. combine backward
     CHK(bwd::combine(T, d, a.dy, static_cast<const uint16_t *>(a.y_perm), a.row_of, a.weights, w.dyo, dys, dg, false,
@@ -762,15 +780,20 @@ hipError_t launch_backward(const BackwardArgs &a, void *ws, hipStream_t s) {
     // 2. pre-activations: routed rows gather x through row_src; shared rows are x
     CHK(nt(LargeGemmArgs{A, a.offsets, x, a.row_src, k, T, d, eg, eu, I, w.P, 2 * I, I, true}, a.offsets, d));
     CHK(nt(LargeGemmArgs{T, nullptr, x, nullptr, 1, T, d, sg, su, I, Ps, 2 * I, I, true}, nullptr, d));
-    // 3. dh = (output gradient) W_down, with W_down transposed to [E, I, d]
-    CHK(nt(LargeGemmArgs{A, a.offsets, w.dyo, nullptr, 1, A, d, w.wdT, nullptr, I, w.dh, I, 0, false}, a.offsets, d));
-    CHK(nt(LargeGemmArgs{T, nullptr, dys, nullptr, 1, T, d, w.sdT, nullptr, I, dhs, I, 0, false}, nullptr, d));
+    // 3. dh = (output gradient) W_down (K-major W_down, or transposed to [E, I, d])
+    CHK(kn_dh ? launch_bf16_large_gemm(gdh, s)
+              : nt(LargeGemmArgs{A, a.offsets, w.dyo, nullptr, 1, A, d, w.wdT, nullptr, I, w.dh, I, 0, false}, a.offsets, d));
+    CHK(kn_dhs ? launch_bf16_large_gemm(gdhs, s)
+               : nt(LargeGemmArgs{T, nullptr, dys, nullptr, 1, T, d, w.sdT, nullptr, I, dhs, I, 0, false}, nullptr, d));
     // 4. SwiGLU backward (routed and shared rows in one pass)
     CHK(bwd::swiglu((int64_t)A + T, I, w.P, w.dh, w.h16, w.dab, false, s));
-    // 5. input gradients: (da | db) [rows, 2I] times (W_gate | W_up) transposed to [E, d, 2I]
-    CHK(nt(LargeGemmArgs{A, a.offsets, w.dab, nullptr, 1, A, 2 * I, w.wguT, nullptr, d, w.dxi, d, 0, false}, a.offsets,
-           2 * I));
-    CHK(nt(LargeGemmArgs{T, nullptr, dabs, nullptr, 1, T, 2 * I, w.sguT, nullptr, d, dxs, d, 0, false}, nullptr, 2 * I));
+    // 5. input gradients: (da | db) [rows, 2I] times (W_gate | W_up) (K-major, or transposed to [E, d, 2I])
+    CHK(kn_dx ? launch_bf16_large_gemm(gdx, s)
+              : nt(LargeGemmArgs{A, a.offsets, w.dab, nullptr, 1, A, 2 * I, w.wguT, nullptr, d, w.dxi, d, 0, false},
+                   a.offsets, 2 * I));
+    CHK(kn_dxs ? launch_bf16_large_gemm(gdxs, s)
+               : nt(LargeGemmArgs{T, nullptr, dabs, nullptr, 1, T, 2 * I, w.sguT, nullptr, d, dxs, d, 0, false}, nullptr,
+                    2 * I));
     // 6. weight gradients.  The rows each expert reduces over are transposed
     //    into [*, Rp] buffers where expert e's rows start at poff[e] (64-aligned,
     //    zero-padded), so both operands are K-contiguous and every K range is

@@ -86,6 +86,10 @@ struct LargeParams {
     const int32_t *kseg;
     int ldk;
     int64_t cstride;
+    // B stored K-major ([K, N] per group, N contiguous): K rows [0, ksplit)
+    // come from B0 [G, ksplit, N] and [ksplit, K) from B1 (ksplit 0: all of
+    // K from B0 [G, K, N])
+    int ksplit;
 };
 
 // Row-tile map: lane owns experts 4*lane .. 4*lane+3.
@@ -213,6 +217,27 @@ __device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(lds_block), 16, voff, soff, 0, 0);
 }
 
+// The same load issued from inline assembly, for the K-major B form: the
+// compiler does not see these LDS writes, so it adds no wait for them before
+// the transposing LDS reads (for which it cannot tell the units apart and
+// would wait on every load in flight).  The kernel's own vmcnt waits and
+// barriers order them, as they do the builtin's.  M0 is set right before
+// the load; this kernel form makes no other use of M0.
+__device__ __forceinline__ void dma_asm(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint16_t *lds_block) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)(lds_block));
+    const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(r), "s"(so)
+                 : "memory");
+}
+
+template <bool ASM>
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint16_t *lds_block) {
+    if constexpr (ASM) dma_asm(r, voff, soff, lds_block);
+    else dma_buf(r, voff, soff, lds_block);
+}
+
 // acc += A_frag x B_frag^T.  TRANS swaps the operands, so the accumulator
 // holds the transposed 32x32 block: lane l then owns tile row l % 32 and, in
 // registers 4q .. 4q+3, the 4 consecutive tile columns 8q + 4(l / 32) .. +3,
@@ -226,6 +251,27 @@ __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
 // One accumulator element, copied from its AGPR where it is used: left to
 // the compiler, every accumulator is copied to VGPRs at the loop exit,
 // which needs 256 VGPRs and spills the tile loop's state.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 *lds_v4i16_t;
+
+// K-major B unit: 64 K rows of LB columns; the 16-byte piece c of row k sits
+// at position c ^ 4 (k % 4).  B fragment (32 columns from ncol0, K values
+// 16 ks + 8 (lane / 32) .. +7 of column ncol0 + lane % 32) from two
+// transposing reads: within each 16 lanes, lane 4a + c receives element c of
+// the 8 bytes that lanes a, a+4, a+8, a+12 point at, so lane s points at row
+// 16 ks + 8 (s / 32) + (s % 16) / 4 (+ 4 for the second read), columns
+// ncol0 + 16 ((s / 16) % 2) + 4 (s % 4) .. +3.
+__device__ __forceinline__ int kn_off(int k, int col) { return k * LB + ((((col >> 3) ^ (4 * (k & 3))) << 3) | (col & 7)); }
+
+__device__ __forceinline__ bf16x8 frag_kn(const uint16_t *unit, int ks, int ncol0, int lane) {
+    const int h = lane >> 4, a = lane & 15;
+    const int k = 16 * ks + 8 * (h >> 1) + (a >> 2);
+    const int off = kn_off(k, ncol0 + 16 * (h & 1) + 4 * (a & 3));
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)(unit + off));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)(unit + off + 4 * LB));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 __device__ __forceinline__ float acc_read(float x) {
     float r;
     asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
@@ -238,8 +284,9 @@ __device__ __forceinline__ float swiglu(float g, float u) {
     return g * u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
 }
 
-template <int EPI, bool ROUTED, bool KG = false>
+template <int EPI, bool ROUTED, bool KG = false, bool BKN = false>
 __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
+    static_assert(!BKN || (EPI == EPI_F32 && !KG), "K-major B: plain fp32 products only");
     constexpr bool DUAL = EPI == EPI_SWIGLU || EPI == EPI_PRE;
     constexpr bool TRANS = EPI != EPI_COMBINE;  // register epilogue (no LDS staging)
     constexpr int BN = DUAL ? LB / 2 : LB;  // output columns per tile
@@ -286,7 +333,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
     int e = 0, m0 = 0, m_end = 0, n0 = 0, kbase = 0;
     const uint32_t a_rows_total = p.a_rows ? (uint32_t)(p.M / p.a_div) : (uint32_t)p.M;
     const __amdgpu_buffer_rsrc_t rA = buf_rsrc(p.A, a_rows_total * (uint32_t)ldk * 2u);
-    const uint32_t b_bytes = (uint32_t)p.N * (uint32_t)ldk * 2u;  // one expert's B matrix
+    const int kb_rows = BKN && p.ksplit ? p.ksplit : K;           // K-major B: K rows per matrix
+    const uint32_t b_bytes = (uint32_t)p.N * (uint32_t)(BKN ? kb_rows : ldk) * 2u;  // one expert's B matrix
     const uint16_t *pBg = p.B0, *pBu = p.B1;                     // the tile's expert
     uint32_t aoff[8], boff[8];
 
@@ -297,14 +345,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
     // every load and read unconditional.
 #define UNIT(u) (smem + (u) * UNIT_ELEMS)
 #define ISSUE_A(st_, i, unit_)                                                                 \
-        dma_buf(rA, aoff[i], (uint32_t)min((st_), nk - 1) * (LK * 2), (unit_) + (wave + 4 * (i)) * 512)
+        dma16<BKN>(rA, aoff[i], (uint32_t)min((st_), nk - 1) * (LK * 2), (unit_) + (wave + 4 * (i)) * 512)
     // ISSUE_B reads rBg_ / rBu_: the B resources of the tile whose loads are
     // being issued, built once per tile in scalar registers.
 #define B_RSRC()                                                                               \
         const __amdgpu_buffer_rsrc_t rBg_ = buf_rsrc(uniform_ptr(pBg), b_bytes);               \
-        const __amdgpu_buffer_rsrc_t rBu_ = DUAL ? buf_rsrc(uniform_ptr(pBu), b_bytes) : rBg_;
+        const __amdgpu_buffer_rsrc_t rBu_ = (DUAL || BKN) ? buf_rsrc(uniform_ptr(pBu), b_bytes) : rBg_;
+    // K-major B: stage st's 64 rows start at row st*LK of B0, or of B1 past ksplit
+#define B_UP(st_) (BKN && p.ksplit && min((st_), nk - 1) * LK >= p.ksplit)
 #define ISSUE_B(st_, i, unit_)                                                                 \
-        dma_buf((DUAL && (i) >= 4) ? rBu_ : rBg_, boff[i], (uint32_t)min((st_), nk - 1) * (LK * 2), \
+        dma16<BKN>((B_UP(st_) || (DUAL && (i) >= 4)) ? rBu_ : rBg_, boff[i],                    \
+                BKN ? (uint32_t)(min((st_), nk - 1) * LK - (B_UP(st_) ? p.ksplit : 0)) * (uint32_t)p.N * 2u \
+                    : (uint32_t)min((st_), nk - 1) * (LK * 2),                                 \
                 (unit_) + (wave + 4 * (i)) * 512)
     // Tile tt -> (e, m0, m_end, n0), B matrices (DMA block i of B comes
     // from the up matrix for i >= 4 in the SwiGLU tile: rows 128..255 of its
@@ -340,8 +392,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
         m0 = __builtin_amdgcn_readfirstlane(m0);                                               \
         m_end = __builtin_amdgcn_readfirstlane(m_end);                                         \
         n0 = nt_ * BN;                                                                         \
-        pBg = KG ? p.B0 : p.B0 + (size_t)e * p.N * K;                                          \
-        pBu = DUAL ? p.B1 + (size_t)e * p.N * K : pBg;                                         \
+        pBg = KG ? p.B0 : p.B0 + (size_t)e * p.N * (BKN ? kb_rows : K);                       \
+        pBu = DUAL ? p.B1 + (size_t)e * p.N * K : (BKN && p.ksplit) ? p.B1 + (size_t)e * p.N * kb_rows : pBg; \
         int ar_[8];                                                                            \
         _Pragma("unroll") for (int i = 0; i < 8; ++i) ar_[i] = min(m0 + drow[i], m_end - 1);    \
         if (p.a_rows) { /* 8 independent lookups, issued together */                            \
@@ -353,6 +405,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
             const int r = drow[i];                                                             \
             const int br = DUAL ? n0 + (r & (BN - 1)) : n0 + r;                                \
             boff[i] = ((uint32_t)br * (uint32_t)ldk + (uint32_t)(dcol[i] + kbase)) * 2u;       \
+            if (BKN) { /* 1 KB block = K rows 2 blk, 2 blk + 1; lane: physical piece lane % 32 */ \
+                const int kr_ = 2 * (wave + 4 * i) + (lane >> 5);                              \
+                const int pc_ = (lane & 31) ^ (4 * (kr_ & 3));                                 \
+                boff[i] = ((uint32_t)kr_ * (uint32_t)p.N + (uint32_t)(n0 + 8 * pc_)) * 2u;     \
+            }                                                                                  \
             /* rows past the group's end: an offset past the A resource, so the */             \
             /* load fetches nothing (their outputs are dropped) */                              \
             if (m0 + r >= m_end) aoff[i] = kOobOff;                                             \
@@ -396,6 +453,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
 #define FRAG_READ(r, AN, BN_, nA, nB, cn)                                                      \
         if ((r) < 4)                                                                           \
             AN[(r) & 3] = *reinterpret_cast<const bf16x8 *>((nA) + lds_piece(wm * 128 + ((r) & 3) * 32 + (lane & 31), (cn))); \
+        else if (BKN)                                                                          \
+            BN_[(r) & 3] = frag_kn((nB), (cn) >> 1, wn * 128 + ((r) & 3) * 32, lane);          \
         else                                                                                   \
             BN_[(r) & 3] = *reinterpret_cast<const bf16x8 *>((nB) + lds_piece(B_ROW((r) & 3), (cn)));
 #define STEP(AC, BC, AN, BN_, nA, nB, cn, DMA, NB_)                                            \
@@ -435,7 +494,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
             for (int i = 0; i < 4; ++i)
                 a0[i] = *reinterpret_cast<const bf16x8 *>(sA + lds_piece(wm * 128 + i * 32 + (lane & 31), g));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b0[j] = *reinterpret_cast<const bf16x8 *>(sB + lds_piece(B_ROW(j), g));
+            for (int j = 0; j < 4; ++j)
+                b0[j] = BKN ? frag_kn(sB, 0, wn * 128 + j * 32, lane)
+                            : *reinterpret_cast<const bf16x8 *>(sB + lds_piece(B_ROW(j), g));
         }
 
         // Stage kt = 4 steps of 16 K; fragments of step s+1 are read during
@@ -491,6 +552,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
 #undef FRAG_READ
 #undef READ_AT
 #undef B_ROW
+        if (BKN) wait_vmcnt_lds<0>();  // loads the compiler does not see
         __syncthreads();  // every wave done with the ring (and its loads landed)
         first = false;
         const int cm0 = m0, cm_end = m_end, cn0 = n0, ce = e;  // this tile, for its epilogue
@@ -647,6 +709,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
 #undef B_RSRC
 #undef ISSUE_A
 #undef ISSUE_B
+#undef B_UP
 #undef UNIT
 }
 
@@ -677,6 +740,16 @@ bool ffn_bf16_large_ok(const FfnArgs &a) {
 }
 
 bool bf16_large_gemm_ok(const LargeGemmArgs &g) {
+    if (g.b_kn) {
+        const int groups = g.offsets ? kE : 1;
+        const unsigned long long lim = kOobOff - (1ULL << 20);
+        const unsigned long long a_rows = g.a_rows ? (unsigned long long)g.a_src_rows : (unsigned long long)g.M;
+        const int kb = g.ksplit ? g.ksplit : g.K;
+        return !g.dual && !g.kseg && (long long)g.M >= 128LL * groups && g.N % LB == 0 && g.K % LK == 0 &&
+               kb % LK == 0 && g.ksplit < g.K && (g.ksplit == 0 || g.K == 2 * g.ksplit) && g.K < (1 << 19) &&
+               a_rows * g.K * 2 < lim && (unsigned long long)g.N * kb * 2 < lim &&
+               (unsigned long long)g.M * g.ldo * 4 < lim;
+    }
     if (g.kseg) {
         const unsigned long long lim = kOobOff - (1ULL << 20);
         return !g.dual && !g.offsets && !g.a_rows && g.M % LM == 0 && g.N % LB == 0 && g.ldk % 8 == 0 &&
@@ -710,7 +783,11 @@ hipError_t launch_bf16_large_gemm(const LargeGemmArgs &g, hipStream_t s) {
     p.kseg = g.kseg;
     p.ldk = g.ldk;
     p.cstride = g.cstride;
-    if (g.kseg) {
+    p.ksplit = g.ksplit;
+    if (g.b_kn) {
+        if (g.offsets) hipLaunchKernelGGL((k_gemm_bf16_large<EPI_F32, true, false, true>), dim3(P), dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((k_gemm_bf16_large<EPI_F32, false, false, true>), dim3(P), dim3(256), 0, s, p);
+    } else if (g.kseg) {
         hipLaunchKernelGGL((k_gemm_bf16_large<EPI_F32, false, true>), dim3(P), dim3(256), 0, s, p);
     } else if (g.dual) {
         if (g.offsets) hipLaunchKernelGGL((k_gemm_bf16_large<EPI_PRE, true>), dim3(P), dim3(256), 0, s, p);

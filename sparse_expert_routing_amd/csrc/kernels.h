@@ -113,6 +113,12 @@ struct LargeGemmArgs {
     const int32_t *kseg;
     int ldk;
     int64_t cstride;
+    // B stored K-major, [G, K, N] (N contiguous), instead of [G, N, K]; with
+    // ksplit, K rows [0, ksplit) come from B0 [G, ksplit, N] and the rest
+    // from B1 (K = 2 ksplit).  Plain fp32 products only (not dual, not
+    // K-grouped).
+    bool b_kn;
+    int ksplit;
 };
 bool bf16_large_gemm_ok(const LargeGemmArgs &g);
 hipError_t launch_bf16_large_gemm(const LargeGemmArgs &g, hipStream_t s);
