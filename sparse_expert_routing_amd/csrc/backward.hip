@@ -828,16 +828,15 @@ hipError_t launch_backward(const BackwardArgs &a, void *ws, hipStream_t s) {
         CHK(transpose(T, d, 1, dys, d, 0, nullptr, 1, nullptr, nullptr, (int)Tp, w.dysT, Tp, 0, 0, s));
         CHK(transpose(T, I, 1, hs, I, 0, nullptr, 1, nullptr, nullptr, (int)Tp, w.hsT, Tp, 0, 0, s));
         CHK(transpose(T, 2 * I, 1, dabs, 2 * I, 0, nullptr, 1, nullptr, nullptr, (int)Tp, w.dabsT, Tp, 0, 0, s));
-        BGemm r{};
-        r.M = I; r.N = d; r.K = (int)Tp; r.lda = Tp; r.a_div = 1; r.B = w.xsT; r.ldb = Tp; r.ldc = d;
-        r.A = w.dabsT; r.C = a.ds_gate;
-        CHK((bgemm<GROUP_NONE, false>(r, 1, s)));
-        r.A = w.dabsT + (int64_t)I * Tp; r.C = a.ds_up;
-        CHK((bgemm<GROUP_NONE, false>(r, 1, s)));
-        BGemm u{};
-        u.M = d; u.N = I; u.K = (int)Tp; u.A = w.dysT; u.lda = Tp; u.a_div = 1; u.B = w.hsT; u.ldb = Tp;
-        u.C = a.ds_down; u.ldc = I;
-        CHK((bgemm<GROUP_NONE, false>(u, 1, s)));
+        // plain NT products over K = Tp: the persistent kernel when it takes them
+        const int tp = (int)Tp;
+        CHK(nt(LargeGemmArgs{I, nullptr, w.dabsT, nullptr, 1, I, tp, w.xsT, nullptr, d, a.ds_gate, d, 0, false}, nullptr,
+               Tp));
+        CHK(nt(LargeGemmArgs{I, nullptr, w.dabsT + (int64_t)I * Tp, nullptr, 1, I, tp, w.xsT, nullptr, d, a.ds_up, d, 0,
+                             false},
+               nullptr, Tp));
+        CHK(nt(LargeGemmArgs{d, nullptr, w.dysT, nullptr, 1, d, tp, w.hsT, nullptr, I, a.ds_down, I, 0, false}, nullptr,
+               Tp));
     }
     // 7. router: dl and its share of dx (written), then the router gradient
     CHK(bwd::router(T, d, x, a.w_router, a.idx, dg, w.dl, a.dx, s));
