@@ -268,10 +268,13 @@ size_t moe_workspace_bytes(const moe_desc_t *desc, int32_t stage);
  *   dg [T, k] the combine-weight gradients dy . y_perm_j (NULL: not returned).
  *   workspace >= moe_workspace_bytes(desc, MOE_WS_BACKWARD) bytes of device
  *   memory: about (T*k + T)(6d + 18I) for the per-row intermediates, plus
- *   (T*k + 64E + T)(4d + 6I) for their K-contiguous transposes, plus
- *   6(E + 1)*I*d for the transposed weights and 64*E*d for the router
- *   partials (about 38 GiB at T=16384, d=7168, I=2048, E=256, k=8; with
- *   e4m3 weights about 31 GiB).
+ *   (T*k + 64E + T)(4d + 6I) for their K-contiguous transposes, 64*E*d
+ *   for the router partials, and, only where the data-gradient products
+ *   cannot read the weights as stored (fewer than 128 rows per expert on
+ *   average, or d or I not a multiple of 256), 6(E + 1)*I*d for transposed
+ *   weights
+ *   (about 17 GiB at T=16384, d=7168, I=2048, E=256, k=8; with e4m3 weights,
+ *   which are always transposed as blocks, about 31 GiB).
  * Requires d % 128 == 0 and I % 128 == 0.
  */
 moe_status_t moe_backward(const moe_desc_t *desc, const void *x, const float *w_router, const int32_t *idx,

@@ -616,8 +616,31 @@ struct BwdWs {
     size_t bytes;
 };
 
+// Which data-gradient products the persistent kernel takes with K-major
+// weights (dh, dx; routed, shared): a function of the shape only.  Those that
+// it does not take need transposed weight copies in the workspace.
+struct KnPlan {
+    bool dh, dhs, dx, dxs;
+};
+
+LargeGemmArgs kn_args(int M, const int32_t *offsets, int K, int N, int ksplit) {
+    LargeGemmArgs g{};
+    g.M = M; g.offsets = offsets; g.a_div = 1; g.a_src_rows = M; g.K = K; g.N = N; g.ldo = N;
+    g.b_kn = true; g.ksplit = ksplit;
+    return g;
+}
+
+KnPlan kn_plan(int T, int d, int I, int k) {
+    static const int32_t grouped = 0;  // stands for an offsets array: only its presence is read
+    const int A = T * k;
+    return KnPlan{bf16_large_gemm_ok(kn_args(A, &grouped, d, I, 0)), bf16_large_gemm_ok(kn_args(T, nullptr, d, I, 0)),
+                  bf16_large_gemm_ok(kn_args(A, &grouped, 2 * I, d, I)),
+                  bf16_large_gemm_ok(kn_args(T, nullptr, 2 * I, d, I))};
+}
+
 BwdWs carve(char *base, int T, int d, int I, int k) {
     BwdWs w{};
+    const KnPlan kn = kn_plan(T, d, I, k);
     size_t o = 0;
     const size_t A = (size_t)T * k, R = A + T, Rp = A + 64 * (size_t)kE, Tp = ((size_t)T + 31) / 32 * 32;
     auto take = [&](size_t n) -> char * {
@@ -635,10 +658,11 @@ BwdWs carve(char *base, int T, int d, int I, int k) {
     w.dg = reinterpret_cast<float *>(take(A * 4));
     w.poff = reinterpret_cast<int32_t *>(take((kE + 1) * 4));
     w.dwr_part = reinterpret_cast<float *>(take(bwd::dwr_part_bytes(d)));
-    w.wdT = reinterpret_cast<uint16_t *>(take((size_t)kE * I * d * 2));
-    w.wguT = reinterpret_cast<uint16_t *>(take((size_t)kE * d * 2 * I * 2));
-    w.sdT = reinterpret_cast<uint16_t *>(take((size_t)I * d * 2));
-    w.sguT = reinterpret_cast<uint16_t *>(take((size_t)d * 2 * I * 2));
+    // transposed weights, only for products that do not read them K-major
+    w.wdT = kn.dh ? nullptr : reinterpret_cast<uint16_t *>(take((size_t)kE * I * d * 2));
+    w.wguT = kn.dx ? nullptr : reinterpret_cast<uint16_t *>(take((size_t)kE * d * 2 * I * 2));
+    w.sdT = kn.dhs ? nullptr : reinterpret_cast<uint16_t *>(take((size_t)I * d * 2));
+    w.sguT = kn.dxs ? nullptr : reinterpret_cast<uint16_t *>(take((size_t)d * 2 * I * 2));
     w.xT = reinterpret_cast<uint16_t *>(take((size_t)d * Rp * 2));
     w.dyoT = reinterpret_cast<uint16_t *>(take((size_t)d * Rp * 2));
     w.hT = reinterpret_cast<uint16_t *>(take((size_t)I * Rp * 2));
@@ -742,8 +766,12 @@ hipError_t launch_backward(const BackwardArgs &a, void *ws, hipStream_t s) {
     const LargeGemmArgs gdx{A, a.offsets, w.dab, nullptr, 1, A, 2 * I, eg, eu, d, w.dxi, d, 0, false,
                             nullptr, 0, 0, true, I};
     const LargeGemmArgs gdxs{T, nullptr, dabs, nullptr, 1, T, 2 * I, sg, su, d, dxs, d, 0, false, nullptr, 0, 0, true, I};
-    const bool kn_dh = bf16_large_gemm_ok(gdh), kn_dhs = bf16_large_gemm_ok(gdhs);
-    const bool kn_dx = bf16_large_gemm_ok(gdx), kn_dxs = bf16_large_gemm_ok(gdxs);
+    // the workspace holds transposed copies exactly where the plan says so
+    const KnPlan kn = kn_plan(T, d, I, k);
+    const bool kn_dh = kn.dh, kn_dhs = kn.dhs, kn_dx = kn.dx, kn_dxs = kn.dxs;
+    if (kn_dh != bf16_large_gemm_ok(gdh) || kn_dhs != bf16_large_gemm_ok(gdhs) || kn_dx != bf16_large_gemm_ok(gdx) ||
+        kn_dxs != bf16_large_gemm_ok(gdxs))
+        return hipErrorInvalidValue;
 
     // 0. padded row positions of the expert groups; transposed weights where needed
     CHK(bwd::pad_offsets(a.offsets, w.poff, 64, s));
