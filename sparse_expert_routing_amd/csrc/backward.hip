@@ -234,7 +234,9 @@ __global__ __launch_bounds__(256) void k_transpose(int R, int C, const uint16_t 
                                                    int dend_plain, uint16_t *__restrict__ out, int64_t ldo,
                                                    int64_t gout, int coff) {
     __shared__ uint16_t tile[64][66];
-    const int c0 = blockIdx.y * 64, g = blockIdx.z;
+    // blockIdx.x: the 64-column block (consecutive workgroups read consecutive
+    // pieces of the same rows); blockIdx.y: the row tile or slot
+    const int c0 = blockIdx.x * 64, g = blockIdx.z;
     const int tid = threadIdx.x;
     int r0, rend, d0, dend;
     if (off) {
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(256) void k_transpose(int R, int C, const uint16_t 
             lt += nt[i];
         }
         const int incl = wave_incl_scan(lt), excl = incl - lt;
-        const int slot = blockIdx.x;
+        const int slot = blockIdx.y;
         if (slot >= __shfl(incl, 63, 64)) return;
         const bool own = slot >= excl && slot < incl;
         const int owner = __ffsll((unsigned long long)__ballot(own)) - 1;
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(256) void k_transpose(int R, int C, const uint16_t 
         d0 = poff[e] + 64 * t;
         dend = min(d0 + 64, poff[e + 1]);
     } else {
-        r0 = blockIdx.x * 64;
+        r0 = blockIdx.y * 64;
         rend = R;
         d0 = r0;
         dend = min(d0 + 64, dend_plain);
@@ -725,7 +727,8 @@ hipError_t transpose(int R, int C, int G, const uint16_t *in, int64_t ldi, int64
                      int64_t gout, int coff, hipStream_t s) {
     const int tiles = off ? R / 64 + kE + 1 : (dend + 63) / 64;
     if (tiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_transpose, dim3(tiles, C / 64, G), dim3(256), 0, s, R, C, in, ldi, gin, rows, rdiv, off,
+    if (tiles > 65535) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_transpose, dim3(C / 64, tiles, G), dim3(256), 0, s, R, C, in, ldi, gin, rows, rdiv, off,
                        poff, dend, out, ldo, gout, coff);
     return hipGetLastError();
 }

@@ -306,7 +306,9 @@ __global__ __launch_bounds__(256) void k_q8_cols(int R, const void *__restrict__
                                                  float *__restrict__ sc, int64_t ldso) {
     __shared__ float tile[128][65];
     __shared__ float red[4][64];
-    const int c0 = blockIdx.y * 64, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // blockIdx.x: the 64-column block (consecutive workgroups read consecutive
+    // pieces of the same rows); blockIdx.y: the 128-position slot
+    const int c0 = blockIdx.x * 64, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int r0, rend, pos0;
     if (off) {
         // slot -> (group e, tile t) over sum_e ceil(c_e / 128) tiles
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(256) void k_q8_cols(int R, const void *__restrict__
             lt += nt[i];
         }
         const int incl = wave_incl_scan(lt), excl = incl - lt;
-        const int slot = blockIdx.x;
+        const int slot = blockIdx.y;
         if (slot >= __shfl(incl, 63, 64)) return;
         const bool own = slot >= excl && slot < incl;
         const int owner = __ffsll((unsigned long long)__ballot(own)) - 1;
@@ -340,7 +342,7 @@ __global__ __launch_bounds__(256) void k_q8_cols(int R, const void *__restrict__
         rend = off[e + 1];
         pos0 = poff[e] + 128 * t;
     } else {
-        r0 = blockIdx.x * 128;
+        r0 = blockIdx.y * 128;
         if (r0 >= Rp) return;
         rend = R;
         pos0 = r0;
@@ -473,7 +475,8 @@ template <bool BF16_IN>
 hipError_t q8_cols(int R, int C, const void *in, int64_t ldi, const int32_t *rows, int rdiv, const int32_t *off,
                    const int32_t *poff, int64_t Rp, uint8_t *out, float *sc, hipStream_t s) {
     const int slots = off ? R / 128 + kE + 1 : (int)(Rp / 128);
-    hipLaunchKernelGGL(k_q8_cols<BF16_IN>, dim3(slots, C / 64), dim3(256), 0, s, R, in, ldi, rows, rdiv, off, poff,
+    if (slots > 65535) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_q8_cols<BF16_IN>, dim3(C / 64, slots), dim3(256), 0, s, R, in, ldi, rows, rdiv, off, poff,
                        (int)Rp, out, Rp, sc, Rp / 128);
     return hipGetLastError();
 }
