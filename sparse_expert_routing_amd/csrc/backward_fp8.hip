@@ -102,7 +102,7 @@ __device__ __forceinline__ bool fg_find_tile(const int32_t *__restrict__ offsets
 
 __device__ __forceinline__ int swz8(int row, int c16) { return c16 ^ (row & 7); }
 
-// 32 K-bytes of one operand row for v_mfma_f32_32x32x64_f8f6f4: K half `hf`
+// 32 K-bytes of one operand row for v_mfma_scale_f32_32x32x64_f8f6f4: K half `hf`
 // of the 128-byte row; lane group g = lane / 32 takes bytes 64*hf + 32*g.
 __device__ __forceinline__ i32x8 frag8(const uint8_t *tile, int row, int hf, int g) {
     const int c0 = 4 * hf + 2 * g;

@@ -33,7 +33,12 @@
 //     flight; the combine stages 64-row chunks through LDS), the gate/up one
 //     forming h = silu(g) u in fp32 and quantising it per 1x128 tile (the
 //     tile's 128 h columns; the row amax of the two column waves meets in
-//     the free fifth LDS unit).
+//     the free fifth LDS unit);
+//   - for the layer backward: an fp32 epilogue (M-grouped or plain
+//     products), and a K-grouped form for the weight gradients (a group per
+//     expert over its 128-aligned K range, both operands with a scale per
+//     row and 128 of K, which each lane passes to the MFMA for its own
+//     rows; groups with no rows are skipped).
 #include "device.h"
 #include "kernels.h"
 
