@@ -33,7 +33,7 @@
  *     hipStream_t; NULL is the default stream) and the call returns.
  *   - Arguments are validated on the host before anything is launched:
  *     MOE_EINVAL for a null required pointer, non-positive sizes, k > E, or
- *     d / I not multiples of 128 with e4m3; MOE_ENOTSUP for shapes this build
+ *     d / I not multiples of 128 with e4m3; MOE_ENOTSUP for shapes the library
  *     does not cover (E != 256, k != 8, d or I not a multiple of 64, an
  *     unsupported dtype pair); MOE_EWORKSPACE when ws_bytes is below
  *     moe_workspace_bytes(); MOE_EHIP when a launch reports an error.

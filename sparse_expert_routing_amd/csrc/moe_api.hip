@@ -96,7 +96,7 @@ const char *moe_status_str(moe_status_t s) {
     switch (s) {
         case MOE_OK: return "MOE_OK";
         case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
-        case MOE_ENOTSUP: return "MOE_ENOTSUP: shape or dtype not supported by this build";
+        case MOE_ENOTSUP: return "MOE_ENOTSUP: shape or dtype not supported by the library";
         case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace smaller than moe_workspace_bytes()";
         case MOE_EHIP: return "MOE_EHIP: HIP launch error";
     }
