@@ -19,8 +19,14 @@ Prints ONE JSON line on stdout (progress goes to stderr).
                  type; HBM-bound ones (FLOP/byte under the ridge, e.g. decode)
                  report algorithmic bytes (touched experts' gate/up weights
                  once, x once, h once) against 8 TB/s
+  roofline_down  the same for the routed down GEMM (2 * T*k * I * d FLOPs)
+  imbalance_curve  max/mean expert load at every step of the 100-step loop
+                 (steps past --steps run untimed, continuing the same loop)
   cpu_baseline   the CPU oracle (fp64, plain loops) timed on a sample of the
                  same workload's tokens through the whole forward
+  sub_results    (default workload only) the fp8 prefill and the decode
+                 workloads, 20 timed steps each, with their own roofline
+                 entries
 """
 import argparse
 import json
@@ -55,6 +61,8 @@ def main():
                          "share of an 8-way expert-parallel layer, 32 experts of ~4096 rows)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="skewed workload only: skip the fp8 and decode sub-results")
     ap.add_argument("--backward", action="store_true",
                     help="also time the layer backward (moe_backward: bf16 GEMMs, or e4m3 GEMMs with e4m3 weights) after the timed loop and report it")
     ap.add_argument("--fresh-batches", type=int, default=0,
@@ -70,12 +78,10 @@ def main():
               "the layer has no multi-GPU implementation", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import synth
     from sparse_expert_routing_amd import _lib
-    from sparse_expert_routing_amd.layer import layer_from_inputs, upload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration:
@@ -89,6 +95,47 @@ def main():
         return
     _lib.load()  # fails loudly without the HIP library
     cfg = synth.CONFIGS[args.config]
+    K = args.steps
+    # the balancing loop of the skewed workload always runs its full length
+    # (100 steps) for the imbalance curve; steps past the timed ones are untimed
+    curve_steps = max(K, cfg.steps)
+    out, inp = measure(cfg, K, args.warmup, curve_steps, args.fresh_batches, backward=args.backward)
+    out["metric"] = METRIC
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    del inp
+    if args.config == 4 and not args.no_sub:
+        # the other full-size workloads, each with its own roofline entry
+        sub = {}
+        for cid in (5, 3):
+            release()
+            r, _ = measure(synth.CONFIGS[cid], max(10, min(K, 20)), min(args.warmup, 3), 0, 0)
+            sub[r["config"]["workload"]] = r
+        out["sub_results"] = sub
+    print(json.dumps(out), flush=True)
+
+
+def release():
+    import gc
+
+    import torch
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def measure(cfg, K, warmup, curve_steps, fresh_batches, backward=False):
+    """Time K steps of the workload's loop (each step the whole path plus the
+    bias step, the bias carried from step to step) after `warmup` untimed
+    steps on a scratch copy of the bias; then, up to `curve_steps`, more
+    untimed steps continuing the same loop, for the imbalance curve.
+    Returns (result dict, host inputs)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from sparse_expert_routing_amd import _lib
+    from sparse_expert_routing_amd.layer import layer_from_inputs, upload
+
     T, d, I, E, k = cfg.T, cfg.d, cfg.I, cfg.E, cfg.k
     A = T * k
 
@@ -97,8 +144,8 @@ def main():
     inp = synth.make_inputs(cfg)
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s; uploading")
     layer = layer_from_inputs(inp)
-    if args.fresh_batches > 0:
-        xs = [upload(synth.make_x_step(cfg, b)) for b in range(args.fresh_batches)]
+    if fresh_batches > 0:
+        xs = [upload(synth.make_x_step(cfg, b)) for b in range(fresh_batches)]
     else:
         xs = [upload(inp["x"])]
     bias0 = upload(inp["bias"])
@@ -129,17 +176,17 @@ def main():
         if ev is not None:
             ev[6].record(stream)
 
-    log(f"[bench] warmup {args.warmup} steps")
+    log(f"[bench] {cfg.name}: warmup {warmup} steps")
     scratch_bias = bias0.clone()
-    for w_ in range(args.warmup):
+    for w_ in range(warmup):
         step(scratch_bias, None, w_)
     torch.cuda.synchronize()
 
-    K = args.steps
+    n_all = max(K, curve_steps)
     bias = bias0.clone()
-    counts_hist = torch.empty((K, E), dtype=torch.int32, device="cuda")
+    counts_hist = torch.empty((n_all, E), dtype=torch.int32, device="cuda")
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
-    log(f"[bench] timing {K} steps")
+    log(f"[bench] {cfg.name}: timing {K} steps")
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(K):
@@ -147,49 +194,58 @@ def main():
         counts_hist[s].copy_(layer.counts, non_blocking=True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    if n_all > K:
+        log(f"[bench] {cfg.name}: {n_all - K} more loop steps (untimed) for the imbalance curve")
+        for s in range(K, n_all):
+            step(bias, None, s)
+            counts_hist[s].copy_(layer.counts, non_blocking=True)
+        torch.cuda.synchronize()
 
     names = ["route", "dispatch", "expert_gate_up", "expert_down", "combine", "bias_update"]
     phase = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(K)]))
              for i, n in enumerate(names)}
     # per-step device time (first to last event of a step): mean, median, extremes
     step_dev = np.array([events[s][0].elapsed_time(events[s][6]) for s in range(K)])
-    ch = counts_hist.cpu().numpy().astype(np.float64)
-    imb = ch.max(axis=1) / ch.mean(axis=1)
+    ch_all = counts_hist.cpu().numpy().astype(np.float64)
+    imb = ch_all.max(axis=1) / ch_all.mean(axis=1)
+    ch = ch_all[:K]  # the timed steps
     tiles = np.ceil(ch / 256.0).sum(axis=1)  # launched 256-row tiles of the routed GEMMs
 
-    gate_up_flops = 2.0 * A * d * (2 * I)
-    gate_up_ms = phase["expert_gate_up"]
-    # algorithmic bytes of one gate/up launch: the touched experts' gate and
-    # up weights (+ block scales) read once, x read once, h written once
     touched = float((ch > 0).sum(axis=1).mean())
     s_w = 1 if cfg.wt == "e4m3" else 2
-    w_bytes = 2.0 * I * d * s_w + (2.0 * (I // 128) * (d // 128) * 4 if cfg.wt == "e4m3" else 0.0)
-    gate_up_bytes = touched * w_bytes + T * d * 2.0 + A * I * s_w
     peak_flops = PEAK_FP8_TFLOPS if cfg.wt == "e4m3" else PEAK_BF16_TFLOPS
-    hbm_bound = gate_up_flops / gate_up_bytes < peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
-    if hbm_bound:
-        achieved = gate_up_bytes / (gate_up_ms * 1e-3) / 1e9
-        peak = PEAK_HBM_GBS
-    else:
-        achieved = gate_up_flops / (gate_up_ms * 1e-3) / 1e12
-        peak = peak_flops
+    sc = 4.0 * (I // 128) * (d // 128) if cfg.wt == "e4m3" else 0.0  # one expert matrix's block scales
+    # gate/up: 2 * A * d * 2I FLOPs; bytes: the touched experts' gate and up
+    # weights (+ block scales) read once, x read once, h written once
+    gu = roofline_entry(2.0 * A * d * (2 * I), touched * (2.0 * I * d * s_w + 2 * sc) + T * d * 2.0 + A * I * s_w,
+                        phase["expert_gate_up"], peak_flops)
+    # down: 2 * A * I * d FLOPs; bytes: the touched experts' down weights
+    # (+ scales) once, h read once, y_perm (bf16) written once
+    dn = roofline_entry(2.0 * A * I * d, touched * (1.0 * I * d * s_w + sc) + A * I * s_w + A * d * 2.0,
+                        phase["expert_down"], peak_flops)
     large = A >= 128 * E
     kname = ("k_gemm_fp8_mx" if large and I % 256 == 0 and d % 256 == 0 else "k_gemm_fp8") if cfg.wt == "e4m3" else \
         ("k_gemm_bf16_large" if large else "k_gemm_skinny" if A <= 4 * E else "k_gemm_bf16")
     total_flops = 2.0 * T * d * E + 6.0 * (A + T) * d * I
     ms_step = wall / K * 1e3
-    log(f"[bench] {ms_step:.3f} ms/step, phases (ms): " + ", ".join(f"{n} {v:.3f}" for n, v in phase.items()))
-    log(f"[bench] gate/up GEMM {achieved:.1f} {'GB/s' if hbm_bound else 'TFLOP/s'} ({100 * achieved / peak:.1f}% of peak); "
-        f"layer {total_flops / (ms_step * 1e-3) / 1e12:.1f} TFLOP/s; max/mean load {imb[0]:.2f} -> {imb[-1]:.2f}; "
-        f"256-row tiles {tiles.mean():.0f} (ideal {A / 256:.0f})")
+    log(f"[bench] {cfg.name}: {ms_step:.3f} ms/step, phases (ms): " + ", ".join(f"{n} {v:.3f}" for n, v in phase.items()))
+    log(f"[bench] gate/up GEMM {gu['achieved']:.1f} {gu['unit']} ({100 * gu['frac']:.1f}% of peak); down "
+        f"{dn['achieved']:.1f} {dn['unit']} ({100 * dn['frac']:.1f}%); layer {total_flops / (ms_step * 1e-3) / 1e12:.1f} "
+        f"TFLOP/s; max/mean load {imb[0]:.2f} -> {imb[-1]:.2f} over {len(imb)} steps; 256-row tiles "
+        f"{tiles.mean():.0f} (ideal {A / 256:.0f})")
 
+    gu.update({"kernel": f"routed gate/up grouped GEMM ({kname}, SwiGLU epilogue"
+                         + (" + e4m3 quantisation)" if cfg.wt == "e4m3" else ")"),
+               "traffic": measured_traffic() if cfg.name == TRAFFIC_WORKLOAD else None,
+               "touched_experts": touched})
+    dn.update({"kernel": f"routed down grouped GEMM ({kname}, bf16 store epilogue)", "touched_experts": touched})
     out = {
-        "metric": METRIC,
+        "metric": f"MoE-layer tokens/s ({cfg.name}) + % of MFMA/HBM peak",
         "value": T * K / wall,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -199,28 +255,36 @@ def main():
         "config": {"workload": cfg.name, "T": T, "d_model": d, "experts": E, "top_k": k, "shared_experts": 1,
                    "expert_intermediate": I, "router": "fp32 sigmoid", "router_row_skew": cfg.skew,
                    "bias_start": cfg.bias, "gamma": cfg.gamma, "loop_steps_timed": K, "seed": cfg.seed,
-                   "batches": "fixed" if args.fresh_batches <= 0 else f"fresh ({args.fresh_batches} cycled)"},
-        "roofline": {"kernel": f"routed gate/up grouped GEMM ({kname}, SwiGLU epilogue"
-                               + (" + e4m3 quantisation)" if cfg.wt == "e4m3" else ")"),
-                     "bound": "hbm" if hbm_bound else "mfma", "achieved": achieved, "peak": peak,
-                     "unit": "GB/s" if hbm_bound else "TFLOP/s", "frac": achieved / peak,
-                     "traffic": measured_traffic() if cfg.name == TRAFFIC_WORKLOAD else None,
-                     "flops_per_launch": gate_up_flops, "bytes_per_launch": gate_up_bytes,
-                     "touched_experts": touched, "avg_launch_ms": gate_up_ms},
+                   "batches": "fixed" if fresh_batches <= 0 else f"fresh ({fresh_batches} cycled)"},
+        "roofline": gu,
+        "roofline_down": dn,
         "phases_ms": phase,
         "step_ms_device": {"mean": float(step_dev.mean()), "median": float(np.median(step_dev)),
                            "min": float(step_dev.min()), "max": float(step_dev.max())},
         "phase_roofline": phase_roofline(cfg, phase),
         "layer_tflops": total_flops / (ms_step * 1e-3) / 1e12,
         "imbalance_max_over_mean": {"first": float(imb[0]), "last": float(imb[-1])},
+        "imbalance_curve": [round(float(v), 4) for v in imb],
+        "imbalance_curve_steps": {"timed": K, "untimed_after": int(n_all - K)},
         "routed_row_tiles_mean": float(tiles.mean()),
     }
-
-    if args.backward:
+    if backward:
         out["backward"] = time_backward(cfg, layer, xs[(K - 1) % len(xs)], min(K, 20))
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+    return out, inp
+
+
+def roofline_entry(flops, nbytes, ms, peak_flops):
+    """Achieved rate of one GEMM launch against its bound: MFMA (algorithmic
+    FLOPs) when its FLOPs per algorithmic byte exceed the ridge point
+    (peak FLOP/s / 8 TB/s), else HBM (algorithmic bytes)."""
+    hbm = flops / nbytes < peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if hbm:
+        achieved, peak = nbytes / (ms * 1e-3) / 1e9, PEAK_HBM_GBS
+    else:
+        achieved, peak = flops / (ms * 1e-3) / 1e12, peak_flops
+    return {"bound": "hbm" if hbm else "mfma", "achieved": achieved, "peak": peak,
+            "unit": "GB/s" if hbm else "TFLOP/s", "frac": achieved / peak,
+            "flops_per_launch": flops, "bytes_per_launch": nbytes, "avg_launch_ms": ms}
 
 
 def phase_roofline(cfg, phase):

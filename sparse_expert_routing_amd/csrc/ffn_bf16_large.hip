@@ -222,14 +222,15 @@ __device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff,
 // the transposing LDS reads (for which it cannot tell the units apart and
 // would wait on every load in flight).  The kernel's own vmcnt waits and
 // barriers order them, as they do the builtin's.  M0 is set right before
-// the load; this kernel form makes no other use of M0.
+// the load and declared clobbered, so the compiler keeps nothing in it
+// across the block.
 __device__ __forceinline__ void dma_asm(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint16_t *lds_block) {
     const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)(lds_block));
     const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  :
                  : "s"(lds), "v"(voff), "s"(r), "s"(so)
-                 : "memory");
+                 : "memory", "m0");
 }
 
 template <bool ASM>

@@ -5,6 +5,7 @@ runs in the HIP kernels behind include/moe.h.
 """
 from __future__ import annotations
 
+import numpy as np
 import torch
 
 from . import _lib
@@ -103,6 +104,24 @@ GAMMA_TOKENS = 14.3e12
 def bias_gamma(tokens_seen: float) -> float:
     """The bias step size for a training step that starts after `tokens_seen` tokens."""
     return GAMMA if tokens_seen < GAMMA_TOKENS else 0.0
+
+
+def save_bias(path, bias) -> None:
+    """Checkpoint the balancing state: the fp32 bias is the layer's only state
+    that changes from step to step (DeepSeek V3 From Scratch, "In code":
+    update_bias returns the new bias; kbwen.com DeepSeek feed, "A bias term
+    for each expert").  Written as a .npy file holding the exact fp32 bits."""
+    if isinstance(bias, torch.Tensor):
+        bias = bias.detach().to("cpu").numpy()
+    np.save(path, np.ascontiguousarray(bias, dtype=np.float32), allow_pickle=False)
+
+
+def load_bias(path, device="cuda") -> torch.Tensor:
+    """The bias saved by save_bias, as an fp32 tensor on `device` (bit-exact)."""
+    b = np.load(path, allow_pickle=False)
+    if b.dtype != np.float32 or b.ndim != 1:
+        raise ValueError(f"{path}: expected a 1-D float32 bias, got {b.dtype} {b.shape}")
+    return torch.from_numpy(b).to(device)
 
 
 def layer_from_inputs(inp: dict, device="cuda") -> MoeLayer:

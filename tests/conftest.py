@@ -16,3 +16,12 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_terminal_summary(terminalreporter):
+    gu = sys.modules.get("tests.gpu_util")
+    notes = getattr(gu, "NOTES", None)
+    if notes:
+        terminalreporter.section("parity notes (near-ties, flips, errors)")
+        for line in notes:
+            terminalreporter.write_line(line)

@@ -38,10 +38,18 @@ def bf16v(a_u16: np.ndarray) -> np.ndarray:
     return synth.bf16_to_f32(a_u16)
 
 
+# parity notes (near-tie and flip counts, errors) repeated in the session's
+# terminal summary, where pytest shows them even for passing tests
+NOTES = []
+
+
 def say(*args):
     """Progress line that names the case (flushed before the GPU step runs)."""
-    print(*args, flush=True)
+    msg = " ".join(str(a) for a in args)
+    print(msg, flush=True)
     sys.stdout.flush()
+    if any(w in msg for w in ("near-tie", "flipped", "max rel err", "bit-identical", "stage-wise")):
+        NOTES.append(msg)
 
 
 TOL = {"f32": 1e-4, "bf16": 2e-2, "e4m3": 5e-2}
