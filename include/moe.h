@@ -123,7 +123,10 @@ moe_status_t moe_route(const moe_desc_t *desc, const void *x, const float *w_rou
  * Efficiency ..., "Implementation: A Modular Look": each expert sees the
  * tokens that chose it).  Every assignment is kept: no capacity, no drops
  * (kbwen.com DeepSeek feed, "A bias term for each expert").
- *   idx          [T, k]   int32 from moe_route (ids in [0, E), distinct per token)
+ *   idx          [T, k]   int32 from moe_route (ids in [0, E), distinct per token; an id
+ *                         outside [0, E) is not dispatched: it takes no row, its row_of
+ *                         entry is -1 and offsets[E] falls short of T*k by the number
+ *                         of such ids; the later calls need a complete dispatch)
  *   x            [T, d]   act type
  *   counts       [E]      int32 out: assignments per expert (the load)
  *   offsets      [E+1]    int32 out: exclusive prefix sum of counts; offsets[E] = T*k

@@ -27,6 +27,8 @@ constexpr int kK = 8;
 constexpr int kWaves = kDispatchBlock / 64;
 
 // Build mask[w][e] for the block's tokens.  Each token's k ids are distinct.
+// An id outside [0, E) is not dispatched (no mask bit; k_disp_rank gives it
+// row -1), so it can neither write out of bounds nor take a row.
 __device__ __forceinline__ void build_masks(uint64_t (*mask)[kE], int T, const int32_t *__restrict__ idx,
                                             int t, int lane, int wave, int32_t (&ids)[kK]) {
     for (int e = threadIdx.x; e < kWaves * kE; e += blockDim.x) (&mask[0][0])[e] = 0ull;
@@ -37,7 +39,9 @@ __device__ __forceinline__ void build_masks(uint64_t (*mask)[kE], int T, const i
         ids[0] = a.x; ids[1] = a.y; ids[2] = a.z; ids[3] = a.w;
         ids[4] = b.x; ids[5] = b.y; ids[6] = b.z; ids[7] = b.w;
 #pragma unroll
-        for (int j = 0; j < kK; ++j) atomicOr(reinterpret_cast<unsigned long long *>(&mask[wave][ids[j]]), 1ull << lane);
+        for (int j = 0; j < kK; ++j)
+            if ((unsigned)ids[j] < (unsigned)kE)
+                atomicOr(reinterpret_cast<unsigned long long *>(&mask[wave][ids[j]]), 1ull << lane);
     }
     __syncthreads();
 }
@@ -105,9 +109,13 @@ __global__ __launch_bounds__(kDispatchBlock) void k_disp_rank(int T, const int32
 #pragma unroll
     for (int j = 0; j < kK; ++j) {
         const int e = ids[j];
+        const int f = t * kK + j;
+        if ((unsigned)e >= (unsigned)kE) {  // not dispatched
+            row_of[f] = -1;
+            continue;
+        }
         int r = block_base[(size_t)blockIdx.x * kE + e] + __popcll(mask[wave][e] & below);
         for (int w = 0; w < wave; ++w) r += __popcll(mask[w][e]);
-        const int f = t * kK + j;
         row_src[r] = f;
         row_of[f] = r;
     }
@@ -129,7 +137,8 @@ __global__ __launch_bounds__(256) void k_disp_gather_copy(int T, int row_bytes, 
     for (int c = lane; c < nchunk; c += 64) {
         const uint4 v = src[c];
 #pragma unroll
-        for (int j = 0; j < kK; ++j) reinterpret_cast<uint4 *>(x_perm + (size_t)dst[j] * row_bytes)[c] = v;
+        for (int j = 0; j < kK; ++j)
+            if (dst[j] >= 0) reinterpret_cast<uint4 *>(x_perm + (size_t)dst[j] * row_bytes)[c] = v;
     }
 }
 
@@ -169,6 +178,7 @@ __global__ __launch_bounds__(256) void k_disp_gather_e4m3(int T, int d, const ui
         const uint2 q = quant8(src[c], s);
 #pragma unroll
         for (int j = 0; j < kK; ++j) {
+            if (dst[j] < 0) continue;
             reinterpret_cast<uint2 *>(xq + (size_t)dst[j] * d)[c] = q;
             if ((lane & 15) == 0) xs[(size_t)dst[j] * ntile + c / 16] = s;
         }

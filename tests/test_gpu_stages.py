@@ -147,6 +147,32 @@ def test_dispatch_bit_exact(T, act, wt, d, kind):
         assert np.array_equal(x_perm, x[tok])
 
 
+def test_dispatch_out_of_range_ids_are_not_dispatched():
+    """Ids outside [0, E) (a precondition violation) stay in bounds: they take
+    no row, their row_of entry is -1 and offsets[E] falls short of T*k by
+    their number; the valid assignments are grouped as usual (the stable
+    order of numpy's argsort over the valid flat assignments)."""
+    T, d = 600, 256
+    say(f"[dispatch] T={T}: out-of-range ids")
+    idx = synth.random_ids(5, synth.TID_IDS, T, 256, 8)
+    idx[::7, 3] = -1
+    idx[::11, 6] = 256
+    idx[5, 0] = 1 << 30
+    x = synth.normal(7, synth.TID_X, (T, d), 1.0, "bf16")
+    counts, offsets, row_src, row_of, x_perm, _ = run_dispatch(T, d, "bf16", "bf16", idx, x)
+    flat = idx.ravel()
+    valid = (flat >= 0) & (flat < 256)
+    nv = int(valid.sum())
+    assert nv < T * 8
+    assert np.array_equal(counts, np.bincount(flat[valid], minlength=256))
+    assert offsets[-1] == nv and np.array_equal(offsets[:-1], np.concatenate([[0], np.cumsum(counts)[:-1]]))
+    fv = np.where(valid)[0]
+    order = fv[np.argsort(flat[fv], kind="stable")]
+    assert np.array_equal(row_src[:nv], order)
+    assert np.all(row_of[~valid] == -1) and np.array_equal(row_of[order], np.arange(nv))
+    assert np.array_equal(x_perm[:nv], x[order // 8])
+
+
 # ------------------------------------------------------------- expert FFN
 
 def run_ffn(cfg, offsets, a_rows, a_scales, experts):
