@@ -36,11 +36,14 @@
  *     d / I not multiples of 128 with e4m3; MOE_ENOTSUP for shapes the library
  *     does not cover (E != 256, k != 8, d or I not a multiple of 64, an
  *     unsupported dtype pair); MOE_EWORKSPACE when ws_bytes is below
- *     moe_workspace_bytes(); MOE_EHIP when a launch reports an error.
+ *     moe_workspace_bytes(); MOE_ESCRATCH when moe_dispatch_noalloc gets
+ *     more tokens than its static scratch holds; MOE_EHIP when a launch
+ *     reports an error.
  *     Device faults surface at the caller's next synchronisation.
  *   - No C++ exception crosses the ABI; the library never aborts.
- *   - Calls are stateless and re-entrant; calls on different streams that
- *     share output buffers race, as with any kernel launch.
+ *   - Calls are stateless and re-entrant (moe_dispatch_noalloc aside: its
+ *     calls share one static scratch per GPU); calls on different streams
+ *     that share output buffers race, as with any kernel launch.
  *
  * Storage types (moe_dtype_t): fp32; bf16 as 16-bit patterns (upper half of
  * binary32); e4m3 as OCP FP8 E4M3FN bytes with fp32 scales.  Supported
@@ -62,7 +65,8 @@ typedef enum {
     MOE_EINVAL = 1,
     MOE_ENOTSUP = 2,
     MOE_EWORKSPACE = 3,
-    MOE_EHIP = 4
+    MOE_EHIP = 4,
+    MOE_ESCRATCH = 5  /* moe_dispatch_noalloc: more tokens than its static scratch holds */
 } moe_status_t;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2 } moe_dtype_t;
@@ -148,6 +152,24 @@ moe_status_t moe_dispatch(const moe_desc_t *desc, const int32_t *idx, const void
                           int32_t *counts, int32_t *offsets, int32_t *row_src, int32_t *row_of,
                           void *x_perm, float *x_perm_scale, void *workspace, size_t ws_bytes,
                           void *stream);
+
+/*
+ * moe_dispatch for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments (minus the workspace) and the same outputs, bit for bit;
+ * the per-block count table lives in a static device array of the library
+ * instead (4 MiB on each GPU the library runs on, held until the process
+ * ends), so T is limited to 1048576 tokens: MOE_ESCRATCH above that, checked
+ * before anything is launched.  The array's device address is looked up on
+ * the first call on each device (MOE_EHIP if that fails).  No allocation or
+ * free happens in any call.  Every call on one GPU uses the same array:
+ * calls that overlap in time on one GPU (several streams or host threads)
+ * race and must be serialised by the caller.  Each call overwrites every
+ * entry it reads, so nothing carries over from an earlier call.
+ */
+moe_status_t moe_dispatch_noalloc(const moe_desc_t *desc, const int32_t *idx, const void *x,
+                                  int32_t *counts, int32_t *offsets, int32_t *row_src, int32_t *row_of,
+                                  void *x_perm, float *x_perm_scale, void *stream);
 
 /*
  * Routed expert FFNs, grouped: rows [offsets[e], offsets[e+1]) of x_perm go

@@ -13,12 +13,12 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
-MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = range(5)
+MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP, MOE_ESCRATCH = range(6)
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 MOE_WS_DISPATCH, MOE_WS_FFN, MOE_WS_COMBINE, MOE_WS_ROUTE, MOE_WS_BACKWARD = 0, 1, 2, 3, 4
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_E4M3}
 
-EXPORTS = ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_gate_up_rows",
+EXPORTS = ("moe_route", "moe_dispatch", "moe_dispatch_noalloc", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_gate_up_rows",
            "moe_expert_down", "moe_combine", "moe_bias_update", "moe_backward", "moe_workspace_bytes",
            "moe_status_str")
 
@@ -56,6 +56,7 @@ def load(path: str = LIB_PATH):
     pw = ctypes.POINTER(FfnWeights)
     L.moe_route.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_dispatch.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_dispatch_noalloc.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_expert_ffn.argtypes = [pd, vp, vp, vp, pw, vp, vp, sz, vp]
     L.moe_expert_gate_up.argtypes = [pd, vp, vp, vp, pw, vp, sz, vp]
     L.moe_expert_gate_up_rows.argtypes = [pd, vp, vp, vp, pw, vp, sz, vp]
@@ -64,7 +65,7 @@ def load(path: str = LIB_PATH):
     L.moe_bias_update.argtypes = [pd, vp, f32, vp, vp]
     L.moe_backward.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, pw, pw, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                vp, sz, vp]
-    for fn in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_gate_up_rows",
+    for fn in ("moe_route", "moe_dispatch", "moe_dispatch_noalloc", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_gate_up_rows",
                "moe_expert_down", "moe_combine", "moe_bias_update", "moe_backward"):
         getattr(L, fn).restype = ctypes.c_int
     L.moe_workspace_bytes.argtypes = [pd, i32]
@@ -116,6 +117,12 @@ def moe_dispatch(ds, idx, x, counts, offsets, row_src, row_of, x_perm, x_perm_sc
         ctypes.byref(ds), _ptr(idx), _ptr(x), _ptr(counts), _ptr(offsets), _ptr(row_src), _ptr(row_of),
         _ptr(x_perm), _ptr(x_perm_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+def moe_dispatch_noalloc(ds, idx, x, counts, offsets, row_src, row_of, x_perm, x_perm_scale, stream=None):
+    _check("moe_dispatch_noalloc", load().moe_dispatch_noalloc(
+        ctypes.byref(ds), _ptr(idx), _ptr(x), _ptr(counts), _ptr(offsets), _ptr(row_src), _ptr(row_of),
+        _ptr(x_perm), _ptr(x_perm_scale), _stream(stream)))
 
 
 def moe_expert_ffn(ds, x_perm, x_perm_scale, offsets, experts: FfnWeights, y_perm, workspace, stream=None):

@@ -200,7 +200,45 @@ __global__ __launch_bounds__(256) void k_quant_rows_e4m3(int rows, int d, const 
     }
 }
 
+// Static scratch of the allocation-free dispatch: the per-block count
+// table [ceil(T/256), E] int32 for up to kDispatchScratchTokens tokens
+// (4 MiB), one copy per GPU, held until the process ends.  Every entry a
+// call reads is written by that call's k_disp_count first, so nothing needs
+// clearing between calls; calls that overlap on one GPU share it and race.
+constexpr size_t kScratchInts = (size_t)(kDispatchScratchTokens / kDispatchBlock) * kE;
+__device__ __align__(256) int32_t scratch[kScratchInts];
+
+constexpr int kMaxDevices = 64;
+// Device address of `scratch` on each GPU, looked up once per device with
+// that device current (host code never passes the array's own name).
+int32_t *g_scratch[kMaxDevices];
+
+hipError_t scratch_ptr(int32_t **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int32_t *p = __atomic_load_n(&g_scratch[dev], __ATOMIC_ACQUIRE);
+    if (p == nullptr) {
+        void *q = nullptr;
+        e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (q == nullptr) return hipErrorInvalidSymbol;
+        p = static_cast<int32_t *>(q);
+        __atomic_store_n(&g_scratch[dev], p, __ATOMIC_RELEASE);
+    }
+    *out = p;
+    return hipSuccess;
+}
+
 }  // namespace
+
+hipError_t launch_dispatch_noalloc(DispatchArgs a, hipStream_t s) {
+    if (a.T > kDispatchScratchTokens) return hipErrorInvalidValue;  // the caller checks first
+    hipError_t e = scratch_ptr(&a.block_base);
+    if (e != hipSuccess) return e;
+    return launch_dispatch(a, s);
+}
 
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s) {
     const int nblk = (a.T + kDispatchBlock - 1) / kDispatchBlock;

@@ -37,6 +37,12 @@ struct DispatchArgs {
     int32_t *block_base;  // workspace [ceil(T/256), E]
 };
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s);
+// The same dispatch with the block counts in the library's static device
+// scratch instead of a caller workspace (a.block_base is ignored): at most
+// kDispatchScratchTokens tokens (checked by the caller); the scratch
+// address is looked up once per device (its HIP error is returned).
+constexpr int kDispatchScratchTokens = 1 << 20;
+hipError_t launch_dispatch_noalloc(DispatchArgs a, hipStream_t s);
 
 // Quantise T rows of bf16 x to e4m3 per 1x128 tile (no permutation).
 hipError_t launch_quant_rows_e4m3(int rows, int d, const uint16_t *x, uint8_t *q, float *scales,

@@ -99,6 +99,7 @@ const char *moe_status_str(moe_status_t s) {
         case MOE_ENOTSUP: return "MOE_ENOTSUP: shape or dtype not supported by the library";
         case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace smaller than moe_workspace_bytes()";
         case MOE_EHIP: return "MOE_EHIP: HIP launch error";
+        case MOE_ESCRATCH: return "MOE_ESCRATCH: request larger than the library's static scratch";
     }
     return "unknown moe_status_t";
 }
@@ -140,6 +141,19 @@ moe_status_t moe_dispatch(const moe_desc_t *d, const int32_t *idx, const void *x
     moe::DispatchArgs a{d->T, d->d, d->E, d->k, d->act, d->wt, idx, x, counts, offsets, row_src, row_of,
                         x_perm, x_perm_scale, static_cast<int32_t *>(workspace)};
     return hip_status(moe::launch_dispatch(a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_dispatch_noalloc(const moe_desc_t *d, const int32_t *idx, const void *x, int32_t *counts,
+                                  int32_t *offsets, int32_t *row_src, int32_t *row_of, void *x_perm,
+                                  float *x_perm_scale, void *stream) {
+    moe_status_t st = check_desc(d);
+    if (st != MOE_OK) return st;
+    if (!idx || !counts || !offsets || !row_src || !row_of) return MOE_EINVAL;
+    if (x_perm && (!x || (d->wt == MOE_E4M3 && !x_perm_scale))) return MOE_EINVAL;
+    if (d->T > moe::kDispatchScratchTokens) return MOE_ESCRATCH;
+    moe::DispatchArgs a{d->T, d->d, d->E, d->k, d->act, d->wt, idx, x, counts, offsets, row_src, row_of,
+                        x_perm, x_perm_scale, nullptr};
+    return hip_status(moe::launch_dispatch_noalloc(a, static_cast<hipStream_t>(stream)));
 }
 
 // a_rows == nullptr: A = x_perm (+ x_perm_scale), one row per routed row.

@@ -112,3 +112,14 @@ def test_product_path_does_not_import_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f"{f} mentions the oracle"
+
+
+def test_dispatch_noalloc_limit_checked_before_launch():
+    """More tokens than the static scratch holds: MOE_ESCRATCH from the host
+    check, before any device work."""
+    L = _lib.load()
+    p = ctypes.c_void_p(0x1000)
+    ds = good_desc(T=(1 << 20) + 1)
+    assert L.moe_dispatch_noalloc(ctypes.byref(ds), p, p, p, p, p, p, None, None, None) == _lib.MOE_ESCRATCH
+    assert L.moe_dispatch_noalloc(ctypes.byref(good_desc()), None, p, p, p, p, p, None, None, None) == _lib.MOE_EINVAL
+    assert L.moe_status_str(_lib.MOE_ESCRATCH).decode().startswith("MOE_ESCRATCH")
