@@ -46,7 +46,12 @@
  *     that share output buffers race, as with any kernel launch.
  *
  * Storage types (moe_dtype_t): fp32; bf16 as 16-bit patterns (upper half of
- * binary32); e4m3 as OCP FP8 E4M3FN bytes with fp32 scales.  Supported
+ * binary32); e4m3 as OCP FP8 E4M3FN bytes, each 1x128 activation tile and
+ * 128x128 weight block with one scale stored as an OCP MX E8M0 byte: byte e
+ * stands for 2^(e-127) (e = 0 .. 254), so a scale is a power of two by
+ * construction; 255 is the format's NaN, and every output that a tile or
+ * block with that byte feeds comes out NaN.  The block-scaled MFMA of gfx950
+ * takes these bytes as they are.  Supported
  * (act, wt) pairs: (F32, F32), (BF16, BF16), (BF16, E4M3).  The router is
  * always fp32.
  */
@@ -83,15 +88,12 @@ typedef struct {
 
 /* Weights of a stack of G SwiGLU experts (G = E routed, or G = 1 shared):
  * gate, up: [G, I, d]; down: [G, d, I] (each row contiguous along the reduced
- * dimension).  For e4m3 the fp32 scales hold one value per 128x128 block:
+ * dimension).  For e4m3 the scales hold one E8M0 byte per 128x128 block:
  * s_gate, s_up: [G, I/128, d/128]; s_down: [G, d/128, I/128]; the value of an
- * element is code * scale.  Each scale must be a power of two (2^-126 ..
- * 2^127): the expert GEMMs apply it as the exponent the block-scaled MFMA
- * takes (other values give wrong products).  Scales are NULL for fp32 and
- * bf16. */
+ * element is code * 2^(s - 127).  Scales are NULL for fp32 and bf16. */
 typedef struct {
     const void *gate, *up, *down;
-    const float *s_gate, *s_up, *s_down;
+    const uint8_t *s_gate, *s_up, *s_down;
 } moe_ffn_weights_t;
 
 /* Workspace stages for moe_workspace_bytes. */
@@ -139,9 +141,10 @@ moe_status_t moe_route(const moe_desc_t *desc, const void *x, const float *w_rou
  *   row_of       [T*k]    int32 out: the inverse, permuted row of assignment t*k + j
  *   x_perm       [T*k, d] out, in the expert GEMM input type: row r = x[row_src[r] / k];
  *                         for e4m3 the row is quantised per 1x128 tile:
- *   x_perm_scale [T*k, d/128] fp32 out (e4m3 only, else NULL): scale = the smallest
- *                         power of two at or above amax/448 (1 for an all-zero
- *                         tile), code = e4m3_rne_sat(v / scale)
+ *   x_perm_scale [T*k, d/128] E8M0 bytes out (e4m3 only, else NULL): scale = the
+ *                         smallest power of two at or above amax/448 (the fp32
+ *                         quotient; 1 for an all-zero tile), code =
+ *                         e4m3_rne_sat(v / scale)
  *   workspace    >= moe_workspace_bytes(desc, MOE_WS_DISPATCH) bytes of device memory
  * x_perm may be NULL: then only counts, offsets, row_src and row_of are
  * written (x and x_perm_scale are not read), for moe_expert_gate_up_rows,
@@ -150,7 +153,7 @@ moe_status_t moe_route(const moe_desc_t *desc, const void *x, const float *w_rou
  */
 moe_status_t moe_dispatch(const moe_desc_t *desc, const int32_t *idx, const void *x,
                           int32_t *counts, int32_t *offsets, int32_t *row_src, int32_t *row_of,
-                          void *x_perm, float *x_perm_scale, void *workspace, size_t ws_bytes,
+                          void *x_perm, uint8_t *x_perm_scale, void *workspace, size_t ws_bytes,
                           void *stream);
 
 /*
@@ -169,7 +172,7 @@ moe_status_t moe_dispatch(const moe_desc_t *desc, const int32_t *idx, const void
  */
 moe_status_t moe_dispatch_noalloc(const moe_desc_t *desc, const int32_t *idx, const void *x,
                                   int32_t *counts, int32_t *offsets, int32_t *row_src, int32_t *row_of,
-                                  void *x_perm, float *x_perm_scale, void *stream);
+                                  void *x_perm, uint8_t *x_perm_scale, void *stream);
 
 /*
  * Routed expert FFNs, grouped: rows [offsets[e], offsets[e+1]) of x_perm go
@@ -177,7 +180,7 @@ moe_status_t moe_dispatch_noalloc(const moe_desc_t *desc, const int32_t *idx, co
  * experts; crackai.dev DeepSeek-V3 summary, "How It Works": FP8 matmuls with
  * per-tile scales and FP32 accumulation).
  *   h = silu(x_perm W_gate[e]^T) * (x_perm W_up[e]^T), fp32 accumulation,
- *       rounded to the wt type (bf16; or e4m3 per 1x128 tile with an fp32
+ *       rounded to the wt type (bf16; or e4m3 per 1x128 tile with an E8M0
  *       scale, as in moe_dispatch; or fp32), kept in the workspace;
  *   y_perm = h W_down[e]^T, fp32 accumulation, stored as fp32 (wt = F32) or
  *       bf16 (otherwise).
@@ -187,7 +190,7 @@ moe_status_t moe_dispatch_noalloc(const moe_desc_t *desc, const int32_t *idx, co
  *   y_perm    [T*k, d] out
  *   workspace >= moe_workspace_bytes(desc, MOE_WS_FFN) bytes of device memory
  */
-moe_status_t moe_expert_ffn(const moe_desc_t *desc, const void *x_perm, const float *x_perm_scale,
+moe_status_t moe_expert_ffn(const moe_desc_t *desc, const void *x_perm, const uint8_t *x_perm_scale,
                             const int32_t *offsets, const moe_ffn_weights_t *experts,
                             void *y_perm, void *workspace, size_t ws_bytes, void *stream);
 
@@ -198,7 +201,7 @@ moe_status_t moe_expert_ffn(const moe_desc_t *desc, const void *x_perm, const fl
  * in that order on one stream with one workspace they are exactly
  * moe_expert_ffn.  Arguments as for moe_expert_ffn.
  */
-moe_status_t moe_expert_gate_up(const moe_desc_t *desc, const void *x_perm, const float *x_perm_scale,
+moe_status_t moe_expert_gate_up(const moe_desc_t *desc, const void *x_perm, const uint8_t *x_perm_scale,
                                 const int32_t *offsets, const moe_ffn_weights_t *experts,
                                 void *workspace, size_t ws_bytes, void *stream);
 moe_status_t moe_expert_down(const moe_desc_t *desc, const int32_t *offsets,

@@ -81,6 +81,8 @@ def lib():
         L.oracle_e4m3_decode.restype = ctypes.c_double
         L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
         L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_e8m0_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e8m0_decode.restype = ctypes.c_double
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_set_threads.argtypes = [ctypes.c_int32]
@@ -164,11 +166,12 @@ def bias_update(bias: np.ndarray, counts: np.ndarray, k: int, T: int, gamma: flo
 
 
 def quant_e4m3_rows(v: np.ndarray, in_dtype="bf16"):
-    """1x128-tile e4m3 quantisation of rows: codes uint8 [rows, cols], scales f32 [rows, cols/128]."""
+    """1x128-tile e4m3 quantisation of rows: codes uint8 [rows, cols], scales as
+    E8M0 bytes uint8 [rows, cols/128] (byte e stands for 2^(e - 127))."""
     rows, cols = v.shape
     v = np.ascontiguousarray(v)
     q = np.empty((rows, cols), np.uint8)
-    s = np.empty((rows, cols // 128), np.float32)
+    s = np.empty((rows, cols // 128), np.uint8)
     lib().oracle_quant_e4m3_rows(rows, cols, _DT[in_dtype], _p(v), _p(q), _p(s))
     return q, s
 
@@ -261,3 +264,7 @@ def e4m3_encode(v: float) -> int:
 
 def e4m3_decode(c: int) -> float:
     return lib().oracle_e4m3_decode(c)
+
+
+def e8m0_decode(e: int) -> float:
+    return lib().oracle_e8m0_decode(e)

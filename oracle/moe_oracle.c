@@ -36,7 +36,9 @@
  *     shared expert's output and y stay unrounded until the fp32 output;
  *   - e4m3 (OCP E4M3FN) tile/block scale = the smallest power of two at or
  *     above amax / 448 (fp32 quotient; 1 if amax = 0), code =
- *     round-to-nearest-even(v / scale), saturating.
+ *     round-to-nearest-even(v / scale), saturating; every scale that crosses
+ *     the interface is stored as an OCP MX E8M0 byte (byte e stands for
+ *     2^(e - 127), 255 for NaN).
  *
  * Build: gcc -O2 -fopenmp -fno-fast-math -ffp-contract=off -shared -fPIC
  */
@@ -56,7 +58,7 @@ typedef struct {
 
 typedef struct {
     const void *gate, *up, *down;           /* [G,I,d], [G,I,d], [G,d,I] */
-    const float *s_gate, *s_up, *s_down;    /* e4m3 only: 128x128 block scales */
+    const uint8_t *s_gate, *s_up, *s_down;  /* e4m3 only: 128x128 block scales, E8M0 */
 } or_ffn;
 
 /* ------------------------------------------------------------------ codecs */
@@ -130,7 +132,20 @@ static uint8_t e4m3_enc(float vf) {
     return sign | (uint8_t)c;
 }
 
+/* OCP MX E8M0 scale byte: an 8-bit biased exponent with no sign and no
+ * mantissa, bias 127; 255 encodes NaN. */
+static double e8m0_dec(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+
+/* The E8M0 byte of a power of two s (2^-127 <= s <= 2^127): s = 0.5 * 2^ex
+ * by frexp, so its exponent is ex - 1. */
+static uint8_t e8m0_enc(double s) {
+    int ex = 0;
+    frexp(s, &ex);
+    return (uint8_t)(ex - 1 + 127);
+}
+
 /* Exposed for the codec pins. */
+double oracle_e8m0_decode(uint8_t e) { return e8m0_dec(e); }
 double oracle_bf16_decode(uint16_t b) { return bf16_dec(b); }
 uint16_t oracle_bf16_encode(float f) { return bf16_enc(f); }
 double oracle_e4m3_decode(uint8_t c) { return e4m3_dec(c); }
@@ -165,9 +180,9 @@ static float quant_tile(const float *v, int n, uint8_t *q) {
 }
 
 /* Quantise rows of `cols` values (cols % 128 == 0) per 1x128 tile.
- * in_dtype OR_F32 or OR_BF16.  q: [rows, cols], scales: [rows, cols/128]. */
+ * in_dtype OR_F32 or OR_BF16.  q: [rows, cols], scales: [rows, cols/128] E8M0. */
 void oracle_quant_e4m3_rows(int64_t rows, int32_t cols, int32_t in_dtype, const void *in,
-                            uint8_t *q, float *scales) {
+                            uint8_t *q, uint8_t *scales) {
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         float v[128];
@@ -177,7 +192,7 @@ void oracle_quant_e4m3_rows(int64_t rows, int32_t cols, int32_t in_dtype, const 
                 v[i] = in_dtype == OR_BF16 ? (float)bf16_dec(((const uint16_t *)in)[j])
                                            : ((const float *)in)[j];
             }
-            scales[r * (cols / 128) + tb] = quant_tile(v, 128, q + r * cols + tb * 128);
+            scales[r * (cols / 128) + tb] = e8m0_enc(quant_tile(v, 128, q + r * cols + tb * 128));
         }
     }
 }
@@ -191,12 +206,12 @@ static double x_at(const or_shape *sh, const void *x, int64_t t, int64_t j) {
 
 /* Weight element [g, n, j] of a [G, N, K] stack (with [G, N/128, K/128]
  * block scales for e4m3). */
-static double w_at(int dtype, const void *w, const float *s, int64_t N, int64_t K, int64_t g,
+static double w_at(int dtype, const void *w, const uint8_t *s, int64_t N, int64_t K, int64_t g,
                    int64_t n, int64_t j) {
     int64_t i = (g * N + n) * K + j;
     if (dtype == OR_F32) return (double)((const float *)w)[i];
     if (dtype == OR_BF16) return bf16_dec(((const uint16_t *)w)[i]);
-    double sc = (double)s[(g * (N / 128) + n / 128) * (K / 128) + j / 128];
+    double sc = e8m0_dec(s[(g * (N / 128) + n / 128) * (K / 128) + j / 128]);
     return e4m3_dec(((const uint8_t *)w)[i]) * sc;
 }
 
@@ -407,7 +422,7 @@ void oracle_bias_update(int32_t E, int32_t k, int32_t T, const int32_t *counts, 
  * a_scales [A, d/128]).  Rows computed: `rows` (nrows of them) or 0..nrows-1.
  * y_perm: [nrows, d] fp32 or bf16 bits (see round_yperm), in list order. */
 void oracle_expert_ffn(const or_shape *sh, const or_ffn *w, const int32_t *offsets,
-                       const void *a_rows, const float *a_scales, int64_t nrows, const int32_t *rows,
+                       const void *a_rows, const uint8_t *a_scales, int64_t nrows, const int32_t *rows,
                        void *y_perm) {
     const int64_t d = sh->d;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -422,7 +437,7 @@ void oracle_expert_ffn(const or_shape *sh, const or_ffn *w, const int32_t *offse
             int64_t i = r * d + j;
             if (sh->wt == OR_F32) a[j] = ((const float *)a_rows)[i];
             else if (sh->wt == OR_BF16) a[j] = bf16_dec(((const uint16_t *)a_rows)[i]);
-            else a[j] = e4m3_dec(((const uint8_t *)a_rows)[i]) * (double)a_scales[r * (d / 128) + j / 128];
+            else a[j] = e4m3_dec(((const uint8_t *)a_rows)[i]) * e8m0_dec(a_scales[r * (d / 128) + j / 128]);
         }
         ffn_row(sh, w, e, a, y, h);
         for (int64_t j = 0; j < d; ++j) {

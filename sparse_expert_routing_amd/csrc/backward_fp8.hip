@@ -1,5 +1,5 @@
 // Backward of the MoE layer with e4m3 expert weights: every GEMM of the
-// backward on e4m3 operands with fp32 scales per tile and fp32 accumulation.
+// backward on e4m3 operands with an E8M0 scale per tile and fp32 accumulation.
 //
 // crackai.dev DeepSeek-V3 summary, "How It Works": FP8 in the forward and
 // the backward pass, a scale per tile, FP32 accumulation at chosen points.
@@ -24,8 +24,8 @@
 // shape fits it; k_fgemm takes the rest.
 // k_fgemm: C = A B^T with both operands K-contiguous e4m3 codes, 128x128
 // tiles, one 128-wide scale block per stage (two v_mfma_scale 32x32x64 fp8
-// per 32x32 block, accumulating in fp32, the power-of-two scales s_a[row, kb]
-// and s_b[col, kb] applied by the MFMA as E8M0 exponents); register-staged
+// per 32x32 block, accumulating in fp32, the E8M0 scales s_a[row, kb] and
+// s_b[col, kb] applied by the MFMA); register-staged
 // LDS double buffer with an XOR swizzle of the 16-byte chunks.  Groups split M (a B per expert: the data
 // gradients) or K (an expert's padded rows: the weight gradients, a C per
 // expert).
@@ -47,13 +47,13 @@ struct FGemm {
     const int32_t *offsets;   // [E+1]: FG_M row ranges; FG_K 128-aligned K ranges
     const uint8_t *A;         // A(m, k) = A[m*lda + k]
     int64_t lda;
-    const float *As;          // s_a(m, kb) = As[m*ldas + kb]
+    const uint8_t *As;        // s_a(m, kb) = As[m*ldas + kb] (E8M0)
     int64_t ldas;
     const int32_t *a_rows;    // optional: row m reads row a_rows[m] / a_div of A and As
     int a_div;
     const uint8_t *B;         // B(n, k) = B[g*bstride + n*ldb + k]
     int64_t ldb, bstride;
-    const float *Bs;          // s_b(n, kb) = Bs[g*bsstride + (n / bdiv)*ldbs + kb]
+    const uint8_t *Bs;        // s_b(n, kb) = Bs[g*bsstride + (n / bdiv)*ldbs + kb] (E8M0)
     int64_t ldbs, bsstride;
     int bdiv;                 // 128: weight blocks; 1: a scale per row
     float *C;                 // C[g*cstride + m*ldc + n]
@@ -115,7 +115,7 @@ template <int GROUP>
 __global__ __launch_bounds__(256, 2) void k_fgemm(FGemm p) {
     __shared__ __attribute__((aligned(16))) uint8_t sA[2][FM * FK];
     __shared__ __attribute__((aligned(16))) uint8_t sB[2][FN * FK];
-    __shared__ float sAs[2][FM], sBs[2][FN];
+    __shared__ int sAs[2][FM], sBs[2][FN];  // E8M0 bytes
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1, g = lane >> 5, c16 = tid & 7;
 
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256, 2) void k_fgemm(FGemm p) {
         }
     }
     const uint8_t *B = p.B + (GROUP == FG_M ? (int64_t)gi * p.bstride : 0);
-    const float *Bs = p.Bs + (GROUP == FG_M ? (int64_t)gi * p.bsstride : 0);
+    const uint8_t *Bs = p.Bs + (GROUP == FG_M ? (int64_t)gi * p.bsstride : 0);
     float *C = p.C + (GROUP == FG_K ? (int64_t)gi * p.cstride : 0);
 
     // this thread's 16-byte chunks of the A and B stage tiles: rows
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256, 2) void k_fgemm(FGemm p) {
         soff[i] = row * FK + swz8(row, c16) * 16;
     }
     // scale staging: threads 0..127 carry A row tid, 128..255 B row tid - 128
-    const float *sp;
+    const uint8_t *sp;
     if (tid < FM) {
         int ar = m0 + tid;
         ar = ar < m_end ? ar : m_end - 1;
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256, 2) void k_fgemm(FGemm p) {
 
     const int nkb = (k_end - k_begin) / FK;  // K ranges are whole stages
     i32x4 ra[4], rb[4];
-    float rs = 0.f;
+    int rs = 0;
     for (int kt = -1; kt < nkb; ++kt) {
         if (kt + 1 < nkb) {
             const int64_t k0 = k_begin + (int64_t)(kt + 1) * FK;
@@ -193,14 +193,14 @@ __global__ __launch_bounds__(256, 2) void k_fgemm(FGemm p) {
                     af[i][hf] = frag8(sA[buf], wm * 64 + i * 32 + (lane & 31), hf, g);
                     bq[i][hf] = frag8(sB[buf], wn * 64 + i * 32 + (lane & 31), hf, g);
                 }
-            // the stage's scales (powers of two) go to the MFMA as E8M0
-            // exponents: lanes l and l+32 of each operand carry the scale of
-            // the operand row l % 32 they hold (A rows, B rows = C columns)
+            // the stage's E8M0 scales go to the MFMA as they are: lanes l and
+            // l+32 of each operand carry the scale of the operand row l % 32
+            // they hold (A rows, B rows = C columns)
             int ea[2], eb[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                ea[i] = (int)((__float_as_uint(sAs[buf][wm * 64 + i * 32 + (lane & 31)]) >> 23) & 0xffu);
-                eb[i] = (int)((__float_as_uint(sBs[buf][wn * 64 + i * 32 + (lane & 31)]) >> 23) & 0xffu);
+                ea[i] = sAs[buf][wm * 64 + i * 32 + (lane & 31)];
+                eb[i] = sBs[buf][wn * 64 + i * 32 + (lane & 31)];
             }
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf)
@@ -250,10 +250,10 @@ hipError_t fgemm(const FGemm &p, hipStream_t s) {
 // Rows of C values (C % 128 == 0; fp32, or bf16 bits when BF16_IN; row
 // stride ldi) -> e4m3 per 1x128 tile: scale = the power of two at or above
 // amax / 448 (1 for an all-zero tile), code = e4m3(v / scale); codes [R, C] (row stride
-// ldo), scales [R, C/128].  16 lanes per tile, 8 values per lane.
+// ldo), E8M0 scales [R, C/128].  16 lanes per tile, 8 values per lane.
 template <bool BF16_IN>
 __global__ __launch_bounds__(256) void k_q8_rows(int64_t R, int C, const void *__restrict__ in, int64_t ldi,
-                                                 uint8_t *__restrict__ q, int64_t ldo, float *__restrict__ sc) {
+                                                 uint8_t *__restrict__ q, int64_t ldo, uint8_t *__restrict__ sc) {
     const int tpr = C / 128;
     const int64_t tile = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
     if (tile >= R * tpr) return;  // whole 16-lane groups leave together
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(256) void k_q8_rows(int64_t R, int C, const void *_
     const uint32_t w0 = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
     const uint32_t w1 = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
     *reinterpret_cast<uint2 *>(q + r * ldo + c0) = uint2{w0, w1};
-    if (l == 0) sc[r * tpr + tb] = s;
+    if (l == 0) sc[r * tpr + tb] = (uint8_t)e8m0_of(s);
 }
 
 // Column tiles over groups of 128 row positions.  Grouped (off != nullptr):
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(256) void k_q8_cols(int R, const void *__restrict__
                                                  const int32_t *__restrict__ rows, int rdiv,
                                                  const int32_t *__restrict__ off, const int32_t *__restrict__ poff,
                                                  int Rp, uint8_t *__restrict__ out, int64_t ldo,
-                                                 float *__restrict__ sc, int64_t ldso) {
+                                                 uint8_t *__restrict__ sc, int64_t ldso) {
     __shared__ float tile[128][65];
     __shared__ float red[4][64];
     // blockIdx.x: the 64-column block (consecutive workgroups read consecutive
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(256) void k_q8_cols(int R, const void *__restrict__
     i32x4 *o = reinterpret_cast<i32x4 *>(out + (int64_t)(c0 + lane) * ldo + pos0 + 32 * wave);
     o[0] = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
     o[1] = i32x4{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
-    if (wave == 0) sc[(int64_t)(c0 + lane) * ldso + pos0 / 128] = s;
+    if (wave == 0) sc[(int64_t)(c0 + lane) * ldso + pos0 / 128] = (uint8_t)e8m0_of(s);
 }
 
 // e4m3 codes transposed per group: out[g][c*ldo + coff + r] = in[g][r*C + c]
@@ -440,8 +440,8 @@ __global__ __launch_bounds__(256) void k_t8(int R, int C, const uint8_t *__restr
 }
 
 // Block scales transposed per group: out[g][cb*ldo + coff + rb] = in[g][rb*Cb + cb].
-__global__ __launch_bounds__(256) void k_tscale(int Rb, int Cb, const float *__restrict__ in,
-                                                float *__restrict__ out, int ldo, int coff) {
+__global__ __launch_bounds__(256) void k_tscale(int Rb, int Cb, const uint8_t *__restrict__ in,
+                                                uint8_t *__restrict__ out, int ldo, int coff) {
     const int g = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
     if (i >= Rb * Cb) return;
     const int rb = i / Cb, cb = i - rb * Cb;
@@ -455,14 +455,14 @@ hipError_t t8(int R, int C, int G, const void *in, uint8_t *out, int64_t ldo, in
     return hipGetLastError();
 }
 
-hipError_t tscale(int R, int C, int G, const float *in, float *out, int ldo, int coff, hipStream_t s) {
+hipError_t tscale(int R, int C, int G, const uint8_t *in, uint8_t *out, int ldo, int coff, hipStream_t s) {
     const int n = (R / 128) * (C / 128);
     hipLaunchKernelGGL(k_tscale, dim3((n + 255) / 256, G), dim3(256), 0, s, R / 128, C / 128, in, out, ldo, coff);
     return hipGetLastError();
 }
 
 template <bool BF16_IN>
-hipError_t q8_rows(int64_t R, int C, const void *in, int64_t ldi, uint8_t *q, float *sc, hipStream_t s) {
+hipError_t q8_rows(int64_t R, int C, const void *in, int64_t ldi, uint8_t *q, uint8_t *sc, hipStream_t s) {
     const int64_t tiles = R * (C / 128);
     hipLaunchKernelGGL(k_q8_rows<BF16_IN>, dim3((unsigned)((tiles + 15) / 16)), dim3(256), 0, s, R, C, in, ldi, q,
                        (int64_t)C, sc);
@@ -473,7 +473,7 @@ hipError_t q8_rows(int64_t R, int C, const void *in, int64_t ldi, uint8_t *q, fl
 // [C, Rp] at the 128-aligned positions poff, or plain rows [0, R) into [C, Rp].
 template <bool BF16_IN>
 hipError_t q8_cols(int R, int C, const void *in, int64_t ldi, const int32_t *rows, int rdiv, const int32_t *off,
-                   const int32_t *poff, int64_t Rp, uint8_t *out, float *sc, hipStream_t s) {
+                   const int32_t *poff, int64_t Rp, uint8_t *out, uint8_t *sc, hipStream_t s) {
     const int slots = off ? R / 128 + kE + 1 : (int)(Rp / 128);
     if (slots > 65535) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_q8_cols<BF16_IN>, dim3(C / 64, slots), dim3(256), 0, s, R, in, ldi, rows, rdiv, off, poff,
@@ -484,16 +484,16 @@ hipError_t q8_cols(int R, int C, const void *in, int64_t ldi, const int32_t *row
 // The workspace, carved in a fixed order (base == nullptr: sizes only).
 struct Bw8 {
     uint8_t *xq, *dyq, *dabq;                 // row-quantised: [T, d], [R, d], [R, 2I]
-    float *xqs, *dyqs, *dabqs;                //   their scales
+    uint8_t *xqs, *dyqs, *dabqs;              //   their E8M0 scales
     float *dyo, *P, *dh, *h, *dab, *dxi;      // fp32 rows [R, *] (routed rows, then T shared rows)
     float *dl, *dg, *dwr_part;
     int32_t *poff;
     uint8_t *wdT, *wguT, *sdT, *sguT;         // transposed weights
-    float *wdTs, *wguTs, *sdTs, *sguTs;       //   their block scales
+    uint8_t *wdTs, *wguTs, *sdTs, *sguTs;     //   their block scales
     uint8_t *xT, *dyT, *hT, *dabT;            // column-quantised [*, Rp]
-    float *xTs, *dyTs, *hTs, *dabTs;
+    uint8_t *xTs, *dyTs, *hTs, *dabTs;
     uint8_t *xsT, *dysT, *hsT, *dabsT;        // shared expert: [*, Tp]
-    float *xsTs, *dysTs, *hsTs, *dabsTs;
+    uint8_t *xsTs, *dysTs, *hsTs, *dabsTs;
     size_t bytes;
 };
 
@@ -510,11 +510,11 @@ Bw8 carve8(char *base, int T, int d, int I, int k) {
     auto u8 = [&](size_t n) { return reinterpret_cast<uint8_t *>(take(n)); };
     auto f32 = [&](size_t n) { return reinterpret_cast<float *>(take(n * 4)); };
     w.xq = u8((size_t)T * d);
-    w.xqs = f32((size_t)T * d / 128);
+    w.xqs = u8((size_t)T * d / 128);
     w.dyq = u8(R * d);
-    w.dyqs = f32(R * d / 128);
+    w.dyqs = u8(R * d / 128);
     w.dabq = u8(R * 2 * I);
-    w.dabqs = f32(R * 2 * I / 128);
+    w.dabqs = u8(R * 2 * I / 128);
     w.dyo = f32(R * d);
     w.P = f32(R * 2 * I);
     w.dh = f32(R * I);
@@ -526,29 +526,29 @@ Bw8 carve8(char *base, int T, int d, int I, int k) {
     w.dwr_part = reinterpret_cast<float *>(take(bwd::dwr_part_bytes(d)));
     w.poff = reinterpret_cast<int32_t *>(take((E + 1) * 4));
     w.wdT = u8(E * I * d);
-    w.wdTs = f32(E * (I / 128) * (d / 128));
+    w.wdTs = u8(E * (I / 128) * (d / 128));
     w.wguT = u8(E * d * 2 * I);
-    w.wguTs = f32(E * (d / 128) * (2 * I / 128));
+    w.wguTs = u8(E * (d / 128) * (2 * I / 128));
     w.sdT = u8((size_t)I * d);
-    w.sdTs = f32((size_t)(I / 128) * (d / 128));
+    w.sdTs = u8((size_t)(I / 128) * (d / 128));
     w.sguT = u8((size_t)d * 2 * I);
-    w.sguTs = f32((size_t)(d / 128) * (2 * I / 128));
+    w.sguTs = u8((size_t)(d / 128) * (2 * I / 128));
     w.xT = u8(d * Rp);
-    w.xTs = f32(d * Rp / 128);
+    w.xTs = u8(d * Rp / 128);
     w.dyT = u8(d * Rp);
-    w.dyTs = f32(d * Rp / 128);
+    w.dyTs = u8(d * Rp / 128);
     w.hT = u8(I * Rp);
-    w.hTs = f32(I * Rp / 128);
+    w.hTs = u8(I * Rp / 128);
     w.dabT = u8(2 * I * Rp);
-    w.dabTs = f32(2 * I * Rp / 128);
+    w.dabTs = u8(2 * I * Rp / 128);
     w.xsT = u8(d * Tp);
-    w.xsTs = f32(d * Tp / 128);
+    w.xsTs = u8(d * Tp / 128);
     w.dysT = u8(d * Tp);
-    w.dysTs = f32(d * Tp / 128);
+    w.dysTs = u8(d * Tp / 128);
     w.hsT = u8(I * Tp);
-    w.hsTs = f32(I * Tp / 128);
+    w.hsTs = u8(I * Tp / 128);
     w.dabsT = u8(2 * I * Tp);
-    w.dabsTs = f32(2 * I * Tp / 128);
+    w.dabsTs = u8(2 * I * Tp / 128);
     w.bytes = o;
     return w;
 }

@@ -71,6 +71,11 @@ __device__ __forceinline__ float e4m3_tile_scale(float amax) {
     return __uint_as_float(b);
 }
 
+// The E8M0 byte of a tile scale from e4m3_tile_scale: its biased exponent
+// field (OCP MX E8M0: byte e stands for 2^(e-127); the scales here are
+// 2^-126 .. 2^127, bytes 1 .. 254).
+__device__ __forceinline__ uint32_t e8m0_of(float pow2) { return (__float_as_uint(pow2) >> 23) & 0xffu; }
+
 // Totally ordered key of a float (larger float -> larger unsigned key).
 __device__ __forceinline__ uint32_t f32_order_key(float f) {
     uint32_t u = __float_as_uint(f);

@@ -143,8 +143,9 @@ __global__ __launch_bounds__(256) void k_disp_gather_copy(int T, int row_bytes, 
 }
 
 // Quantise one bf16 row piece: lane holds 8 values of a 128-wide tile that 16
-// consecutive lanes share.  Returns the 8 codes packed in a uint2 and the scale.
-__device__ __forceinline__ uint2 quant8(uint4 raw, float &scale) {
+// consecutive lanes share.  Returns the 8 codes packed in a uint2 and the
+// tile scale's E8M0 byte.
+__device__ __forceinline__ uint2 quant8(uint4 raw, uint8_t &scale) {
     float v[8];
     v[0] = bf16_to_f32(raw.x & 0xffffu); v[1] = bf16_to_f32(raw.x >> 16);
     v[2] = bf16_to_f32(raw.y & 0xffffu); v[3] = bf16_to_f32(raw.y >> 16);
@@ -155,7 +156,7 @@ __device__ __forceinline__ uint2 quant8(uint4 raw, float &scale) {
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
     amax = wave_max_f32(amax, 16);
     const float s = e4m3_tile_scale(amax);
-    scale = s;
+    scale = (uint8_t)e8m0_of(s);
     const float inv = 1.0f / s;  // a power of two: v * inv == v / s exactly
     const uint32_t lo = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
     const uint32_t hi = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
@@ -164,7 +165,7 @@ __device__ __forceinline__ uint2 quant8(uint4 raw, float &scale) {
 
 __global__ __launch_bounds__(256) void k_disp_gather_e4m3(int T, int d, const uint16_t *__restrict__ x,
                                                           const int32_t *__restrict__ row_of,
-                                                          uint8_t *__restrict__ xq, float *__restrict__ xs) {
+                                                          uint8_t *__restrict__ xq, uint8_t *__restrict__ xs) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(256) void k_disp_gather_e4m3(int T, int d, const ui
     const int ntile = d / 128;
     const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)t * d);
     for (int c = lane; c < d / 8; c += 64) {  // d % 128 == 0: a tile's 16 lanes are all in or all out
-        float s;
+        uint8_t s;
         const uint2 q = quant8(src[c], s);
 #pragma unroll
         for (int j = 0; j < kK; ++j) {
@@ -186,14 +187,14 @@ __global__ __launch_bounds__(256) void k_disp_gather_e4m3(int T, int d, const ui
 }
 
 __global__ __launch_bounds__(256) void k_quant_rows_e4m3(int rows, int d, const uint16_t *__restrict__ x,
-                                                         uint8_t *__restrict__ xq, float *__restrict__ xs) {
+                                                         uint8_t *__restrict__ xq, uint8_t *__restrict__ xs) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= rows) return;
     const int ntile = d / 128;
     const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)t * d);
     for (int c = lane; c < d / 8; c += 64) {
-        float s;
+        uint8_t s;
         const uint2 q = quant8(src[c], s);
         reinterpret_cast<uint2 *>(xq + (size_t)t * d)[c] = q;
         if ((lane & 15) == 0) xs[(size_t)t * ntile + c / 16] = s;
@@ -260,7 +261,7 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_quant_rows_e4m3(int rows, int d, const uint16_t *x, uint8_t *q, float *scales, hipStream_t s) {
+hipError_t launch_quant_rows_e4m3(int rows, int d, const uint16_t *x, uint8_t *q, uint8_t *scales, hipStream_t s) {
     hipLaunchKernelGGL(k_quant_rows_e4m3, dim3((rows + 3) / 4), dim3(256), 0, s, rows, d, x, q, scales);
     return hipGetLastError();
 }

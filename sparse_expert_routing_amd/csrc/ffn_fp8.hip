@@ -2,14 +2,14 @@
 //
 // crackai.dev DeepSeek-V3 summary, "How It Works": FP8 matmuls with a scale
 // per tile and FP32 accumulation at chosen points; DeepSeek V3 From Scratch,
-// "The idea": fine-grained quantisation tiles.  Tile shapes (ours): one fp32
-// scale per 1x128 activation tile (x_perm rows, h rows) and per 128x128 weight
-// block.
+// "The idea": fine-grained quantisation tiles.  Tile shapes (ours): one E8M0
+// scale byte per 1x128 activation tile (x_perm rows, h rows) and per 128x128
+// weight block.
 //
 // Each 128-wide K block is one stage: the wave multiplies its e4m3 fragments
 // with v_mfma_scale_f32_32x32x64_f8f6f4 (two per block) straight into the fp32
-// accumulator, the power-of-two scales s_a[row, kb] and s_w[nb, kb] applied by
-// the MFMA as E8M0 exponents.
+// accumulator, the E8M0 scales s_a[row, kb] and s_w[nb, kb] applied by the
+// MFMA.
 // Workgroup tile 128 rows x 128 output columns (gate/up: 128 gate + 128 up
 // B rows), 4 waves in a 2x2 layout, LDS double-buffered with an XOR swizzle
 // of the 16-byte K chunks.
@@ -36,15 +36,15 @@ struct Fp8Params {
     int M;
     const int32_t *offsets;
     const uint8_t *A;        // [rows, K] codes
-    const float *As;         // [rows, K/128]
+    const uint8_t *As;       // [rows, K/128] E8M0
     const int32_t *a_rows;   // optional row indirection into A / As: row a_rows[r] / a_div
     int a_div;
     int K;
     const uint8_t *B0, *B1;  // [G, N, K] codes
-    const float *S0, *S1;    // [G, N/128, K/128]
+    const uint8_t *S0, *S1;  // [G, N/128, K/128] E8M0
     int N;
     uint8_t *hq;             // EPI_SWIGLU_Q: [rows, N] codes
-    float *hs;               // EPI_SWIGLU_Q: [rows, N/128]
+    uint8_t *hs;             // EPI_SWIGLU_Q: [rows, N/128] E8M0
     uint16_t *out;           // EPI_STORE: bf16 [rows, N]
     float *yout;             // EPI_COMBINE: f32 [rows, N]
     const uint16_t *y_perm;
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(Fp8Params p) {
     constexpr int BCH = BROWS * 8 / 256;       // 16-byte B chunks per thread per stage
     __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * BK];
     __shared__ __attribute__((aligned(16))) uint8_t sB[2][BROWS * BK];
-    __shared__ float sAs[2][BM];
+    __shared__ int sAs[2][BM];  // E8M0 bytes
 
     int e, m0, m_end;
     if (!find_tile(p.offsets, p.M, blockIdx.x, e, m0, m_end)) return;
@@ -130,8 +130,8 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(Fp8Params p) {
     const uint8_t *Ab = p.A;
     const uint8_t *Bg = p.B0 + (size_t)e * p.N * K;
     const uint8_t *Bu = DUAL ? p.B1 + (size_t)e * p.N * K : Bg;
-    const float *Sg = p.S0 + ((size_t)e * (p.N / 128) + n0 / 128) * nkb;
-    const float *Su = DUAL ? p.S1 + ((size_t)e * (p.N / 128) + n0 / 128) * nkb : Sg;
+    const uint8_t *Sg = p.S0 + ((size_t)e * (p.N / 128) + n0 / 128) * nkb;
+    const uint8_t *Su = DUAL ? p.S1 + ((size_t)e * (p.N / 128) + n0 / 128) * nkb : Sg;
 
     uint32_t aoff[4], boff[BCH];
     int soffa[4], soffb[BCH];
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(Fp8Params p) {
     int as_row = m0 + (tid & (BM - 1));
     as_row = as_row < m_end ? as_row : m_end - 1;
     if (p.a_rows) as_row = p.a_rows[as_row] / p.a_div;
-    const float *asp = p.As + (size_t)as_row * nkb;
+    const uint8_t *asp = p.As + (size_t)as_row * nkb;
 
     f32x16 acc[2][NJ];
 #pragma unroll
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(Fp8Params p) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     i32x4 ra[4], rb[BCH];
-    float ras = 0.f;
+    int ras = 0;
     for (int kt = -1; kt < nkb; ++kt) {
         if (kt + 1 < nkb) {
             const int k0 = (kt + 1) * BK;
@@ -179,20 +179,18 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(Fp8Params p) {
         }
         if (kt >= 0) {
             const int buf = kt & 1;
-            const float swg = Sg[kt], swu = Su[kt];
+            const int ebg = Sg[kt], ebu = Su[kt];
             i32x8 af[2][2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) af[i][hf] = frag(sA[buf], wm * 64 + i * 32 + (lane & 31), hf, g);
-            // the power-of-two scales go to the MFMA as E8M0 exponents: lanes
-            // l and l+32 of the A operand carry row l % 32's; the weight block's
-            // is the same for every lane
+            // the E8M0 scale bytes go to the MFMA as they are: lanes l and
+            // l+32 of the A operand carry row l % 32's; the weight block's is
+            // the same for every lane
             int ea[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                ea[i] = (int)((__float_as_uint(sAs[buf][wm * 64 + i * 32 + (lane & 31)]) >> 23) & 0xffu);
-            const int ebg = (int)((__float_as_uint(swg) >> 23) & 0xffu), ebu = (int)((__float_as_uint(swu) >> 23) & 0xffu);
+            for (int i = 0; i < 2; ++i) ea[i] = sAs[buf][wm * 64 + i * 32 + (lane & 31)];
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const int brow = DUAL ? ((j >> 1) * BN + wn * 64 + (j & 1) * 32 + (lane & 31))
@@ -262,7 +260,7 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(Fp8Params p) {
                         const int col = n0 + wn * 64 + j * 32 + (lane & 31);
                         p.hq[(size_t)row * p.N + col] = (uint8_t)f32_to_e4m3(h[i][j][r] / s);
                     }
-                    if (wn == 0 && (lane & 31) == 0) p.hs[(size_t)row * (p.N / 128) + n0 / 128] = s;
+                    if (wn == 0 && (lane & 31) == 0) p.hs[(size_t)row * (p.N / 128) + n0 / 128] = (uint8_t)e8m0_of(s);
                 }
             }
     } else {

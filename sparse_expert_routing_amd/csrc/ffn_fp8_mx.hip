@@ -5,8 +5,8 @@
 // crackai.dev DeepSeek-V3 summary, "How It Works": FP8 matmuls with a scale
 // per tile and FP32 accumulation; DeepSeek V3 From Scratch, "The idea":
 // fine-grained quantisation tiles.  Tiles (ours, as in the rest of the
-// library): one power-of-two scale per 1x128 activation tile and per 128x128
-// weight block.
+// library): one scale per 1x128 activation tile and per 128x128 weight
+// block, each an E8M0 byte (OCP MX: byte e is 2^(e-127)).
 //
 // Design for gfx950:
 //   - a stage is 128 of K (one scale block): A and B slabs of 256 rows x 128
@@ -17,7 +17,7 @@
 //     accumulators in AGPRs; a stage is two steps of 64 of K, 16 MFMAs each,
 //     so the MFMA cycles and LDS fragment bytes per stage equal the bf16
 //     kernel's (each fragment is 32 bytes: two 16-byte pieces of the row);
-//   - the scales go to the MFMA as E8M0 exponents: the weight block's for
+//   - the E8M0 scale bytes go to the MFMA as they are: the weight block's for
 //     every lane of the weight operand, the A row's for lanes l and l+32 of
 //     the activation operand (row l % 32), so the products accumulate in
 //     fp32 with no vector work; a stage's A-row scales are loaded one stage
@@ -65,15 +65,15 @@ struct MxParams {
     int M;
     const int32_t *offsets;   // routed: [E+1] row ranges
     const uint8_t *A;         // [rows, K] codes
-    const float *As;          // [rows, K/128] power-of-two scales
+    const uint8_t *As;        // [rows, K/128] E8M0 scales (byte e: 2^(e-127))
     const int32_t *a_rows;    // optional: GEMM row r reads row a_rows[r] / a_div of A / As
     int a_div;
     int K;
     const uint8_t *B0, *B1;   // [G, N, K] codes (gate, up; or down)
-    const float *S0, *S1;     // [G, N/128, K/128] power-of-two block scales
+    const uint8_t *S0, *S1;   // [G, N/128, K/128] E8M0 block scales
     int N;                    // B rows per expert (SwiGLU: rows of each of gate / up)
     uint8_t *hq;              // MX_SWIGLU_Q: [M, N] codes
-    float *hs;                // MX_SWIGLU_Q: [M, N/128]
+    uint8_t *hs;              // MX_SWIGLU_Q: [M, N/128] E8M0
     uint16_t *out;            // MX_STORE: bf16 [M, N]
     float *yout;              // MX_COMBINE: f32 [M, N]; MX_F32: f32 rows of ldo
     int ldo;
@@ -85,7 +85,7 @@ struct MxParams {
     // with a scale per row and 128 of K (As [M, K/128], Bs [N, K/128]), into
     // yout + e * cstride; groups with an empty range are skipped.
     const int32_t *kseg;
-    const float *Bs;
+    const uint8_t *Bs;
     int64_t cstride;
 };
 
@@ -208,9 +208,6 @@ __device__ __forceinline__ i32x8 frag32(const uint8_t *unit, int row, int c) {
     return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// The E8M0 exponent of a power-of-two fp32 scale (its biased exponent field).
-__device__ __forceinline__ int e8m0(float pow2) { return (int)((__float_as_uint(pow2) >> 23) & 0xffu); }
-
 // acc += A x B^T for one 32x32 block and 64 of K, the scales (E8M0) of the A
 // row this lane carries (ea) and of the B rows (eb).  TRANS swaps the
 // operands, so the accumulator holds the transposed block: lane l owns tile
@@ -279,12 +276,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
     int e = 0, m0 = 0, m_end = 0, n0 = 0, kbase = 0;
     const uint32_t a_rows_total = p.a_rows ? (uint32_t)(p.M / p.a_div) : (uint32_t)p.M;
     const __amdgpu_buffer_rsrc_t rA = buf_rsrc(p.A, a_rows_total * (uint32_t)K);
-    const __amdgpu_buffer_rsrc_t rAs = buf_rsrc(p.As, a_rows_total * (uint32_t)nkall * 4u);
-    const __amdgpu_buffer_rsrc_t rBs = buf_rsrc(KG ? p.Bs : p.As, KG ? (uint32_t)p.N * (uint32_t)nkall * 4u : 4u);
+    const __amdgpu_buffer_rsrc_t rAs = buf_rsrc(p.As, a_rows_total * (uint32_t)nkall);
+    const __amdgpu_buffer_rsrc_t rBs = buf_rsrc(KG ? p.Bs : p.As, KG ? (uint32_t)p.N * (uint32_t)nkall : 1u);
     const uint32_t b_bytes = (uint32_t)p.N * (uint32_t)K;
     const int nbk = p.N / 128;  // weight scale blocks along N
     const uint8_t *pBg = p.B0, *pBu = p.B1;
-    const float *swg_p = p.S0, *swu_p = p.S0;
+    const uint8_t *swg_p = p.S0, *swu_p = p.S0;
     uint32_t aoff[8], boff[8], soff[4], bsoff[4];
 
 #define UNIT(u) (smem + (u) * UNIT_BYTES)
@@ -297,15 +294,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
         dma_buf((DUAL && (i) >= 4) ? rBu_ : rBg_, boff[i], (uint32_t)min((st_), nk - 1) * LKB, \
                 (unit_) + (wave + 4 * (i)) * 1024)
     // The stage's A-row scales of this lane's 4 rows (one per 32-row block)
-    // and the weight block scales of this wave's columns (gate and up).
+    // and the weight block scales of this wave's columns (gate and up): E8M0
+    // bytes, which the block-scaled MFMA takes as they are.
 #define LOAD_SCALES(st_, sa_, sw_, sb_)                                                        \
         {                                                                                      \
             const int kb_ = min((st_), nk - 1);                                                \
             _Pragma("unroll") for (int i = 0; i < 4; ++i)                                      \
-                sa_[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rAs, soff[i] + kb_ * 4u, 0, 0)); \
+                sa_[i] = __builtin_amdgcn_raw_buffer_load_b8(rAs, soff[i] + kb_, 0, 0);        \
             if (KG) {                                                                          \
                 _Pragma("unroll") for (int j = 0; j < 4; ++j)                                  \
-                    sb_[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rBs, bsoff[j] + kb_ * 4u, 0, 0)); \
+                    sb_[j] = __builtin_amdgcn_raw_buffer_load_b8(rBs, bsoff[j] + kb_, 0, 0);   \
             } else {                                                                           \
                 sw_[0] = swg_p[kb_];                                                           \
                 sw_[1] = DUAL ? swu_p[kb_] : sw_[0];                                           \
@@ -364,10 +362,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
             if (m0 + r >= m_end) aoff[i] = kOobOff; /* padding rows fetch nothing */           \
         }                                                                                      \
         _Pragma("unroll") for (int i = 0; i < 4; ++i)                                          \
-            soff[i] = ((uint32_t)sr_[i] * (uint32_t)nkall + (uint32_t)(kbase / LKB)) * 4u;     \
+            soff[i] = (uint32_t)sr_[i] * (uint32_t)nkall + (uint32_t)(kbase / LKB);            \
         _Pragma("unroll") for (int j = 0; j < 4; ++j)                                          \
-            bsoff[j] = ((uint32_t)(n0 + wn * 128 + 32 * j + (lane & 31)) * (uint32_t)nkall +   \
-                        (uint32_t)(kbase / LKB)) * 4u;                                         \
+            bsoff[j] = (uint32_t)(n0 + wn * 128 + 32 * j + (lane & 31)) * (uint32_t)nkall +    \
+                       (uint32_t)(kbase / LKB);                                                \
     }
     // Stage 0's scales, then A_0, B_0, A_1, B_1 of the tile just set up.
 #define PROLOGUE_LOADS()                                                                       \
@@ -380,7 +378,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
         _Pragma("unroll") for (int i = 0; i < 8; ++i) ISSUE_B(1, i, UNIT(3));                  \
     }
 
-    float sa[4], sw[2], sa_n[4], sw_n[2], sb[4], sb_n[4];
+    int sa[4], sw[2], sa_n[4], sw_n[2], sb[4], sb_n[4];  // E8M0 exponents
     // Tile order: every XCD's P/8 workgroups take P/8 consecutive tiles at a
     // time (one L2 shares their operands): tiles (8i + xcd) P/8 + w in the
     // i-th pass.
@@ -465,10 +463,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
                 const uint8_t *cA = UNIT(u0), *cB = UNIT(u1);                                  \
                 uint8_t *fA = UNIT(u4), *fB = UNIT(u0); /* A_{kt+2}, B_{kt+2} */               \
                 int ea_[4], eb_[4];                                                            \
-                _Pragma("unroll") for (int i = 0; i < 4; ++i) ea_[i] = e8m0(sa[i]);            \
+                _Pragma("unroll") for (int i = 0; i < 4; ++i) ea_[i] = sa[i];                  \
                 /* B exponents per column block: per lane (K-grouped rows) or the block's */   \
                 _Pragma("unroll") for (int j = 0; j < 4; ++j)                                  \
-                    eb_[j] = KG ? e8m0(sb[j]) : e8m0(sw[DUAL && j >= 2 ? 1 : 0]);              \
+                    eb_[j] = KG ? sb[j] : sw[DUAL && j >= 2 ? 1 : 0];                          \
                 LOAD_SCALES(kt + 1, sa_n, sw_n, sb_n);                                         \
                 STEP(a0, b0, a1, b1, cA, cB, 4 + 2 * g, DMA_S0, NB_, ea_, eb_);                \
                 __atomic_signal_fence(__ATOMIC_SEQ_CST);                                       \
@@ -543,7 +541,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
                 __builtin_amdgcn_s_barrier();
                 __atomic_signal_fence(__ATOMIC_SEQ_CST);
                 const __amdgpu_buffer_rsrc_t rQ = buf_rsrc(p.hq, (uint32_t)p.M * (uint32_t)p.N);
-                const __amdgpu_buffer_rsrc_t rS = buf_rsrc(p.hs, (uint32_t)p.M * (uint32_t)(p.N / 128) * 4u);
+                const __amdgpu_buffer_rsrc_t rS = buf_rsrc(p.hs, (uint32_t)p.M * (uint32_t)(p.N / 128));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tr = wm * 128 + 32 * i + (lane & 31);
@@ -564,9 +562,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
                         }
                     }
                     const uint32_t so = (ok && wn == 0 && g == 0)
-                                            ? ((uint32_t)row * (uint32_t)(p.N / 128) + (uint32_t)(cn0 / 128)) * 4u
+                                            ? (uint32_t)row * (uint32_t)(p.N / 128) + (uint32_t)(cn0 / 128)
                                             : kOobOff;
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(s), rS, so, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)e8m0_of(s), rS, so, 0, 0);
                 }
             } else if constexpr (EPI == MX_STORE) {
                 const __amdgpu_buffer_rsrc_t rOut = buf_rsrc(p.out, (uint32_t)p.M * (uint32_t)p.N * 2u);
@@ -757,7 +755,7 @@ bool fp8_mx_gemm_ok(const Fp8GemmArgs &g) {
     const unsigned long long lim = kOobOff - (1ULL << 20);
     const unsigned long long a_rows = g.a_rows ? (unsigned long long)g.a_src_rows : (unsigned long long)g.M;
     return (long long)g.M >= 128LL * groups && g.N % LB == 0 && g.K % LKB == 0 && a_rows * g.K < lim &&
-           a_rows * (g.K / LKB) * 4 < lim && (unsigned long long)g.N * g.K < lim &&
+           a_rows * (g.K / LKB) < lim && (unsigned long long)g.N * g.K < lim &&
            (unsigned long long)g.M * g.ldo * 4 < lim && g.ldo >= g.N && (!g.a_rows || g.M / g.a_div == g.a_src_rows);
 }
 
@@ -765,7 +763,7 @@ bool fp8_mx_kg_ok(const Fp8KgArgs &g) {
     const unsigned long long lim = kOobOff - (1ULL << 20);
     return g.M > 0 && g.M % LM == 0 && g.N % LB == 0 && g.K % LKB == 0 && g.ldo >= g.N &&
            (unsigned long long)g.M * g.K < lim && (unsigned long long)g.N * g.K < lim &&
-           (unsigned long long)g.M * (g.K / LKB) * 4 < lim && (unsigned long long)g.N * (g.K / LKB) * 4 < lim &&
+           (unsigned long long)g.M * (g.K / LKB) < lim && (unsigned long long)g.N * (g.K / LKB) < lim &&
            (unsigned long long)g.M * g.ldo * 4 < lim;
 }
 

@@ -33,7 +33,7 @@ struct DispatchArgs {
     const void *x;
     int32_t *counts, *offsets, *row_src, *row_of;
     void *x_perm;         // null: no gather (counts, offsets, row_src, row_of only)
-    float *x_perm_scale;
+    uint8_t *x_perm_scale;  // e4m3: [T*k, d/128] E8M0
     int32_t *block_base;  // workspace [ceil(T/256), E]
 };
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s);
@@ -44,13 +44,14 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s);
 constexpr int kDispatchScratchTokens = 1 << 20;
 hipError_t launch_dispatch_noalloc(DispatchArgs a, hipStream_t s);
 
-// Quantise T rows of bf16 x to e4m3 per 1x128 tile (no permutation).
-hipError_t launch_quant_rows_e4m3(int rows, int d, const uint16_t *x, uint8_t *q, float *scales,
+// Quantise T rows of bf16 x to e4m3 per 1x128 tile (no permutation); E8M0 scales.
+hipError_t launch_quant_rows_e4m3(int rows, int d, const uint16_t *x, uint8_t *q, uint8_t *scales,
                                   hipStream_t s);
 
+// Every e4m3 scale in the library is an E8M0 byte (OCP MX): byte e is 2^(e-127).
 struct FfnWeights {
     const void *gate, *up, *down;
-    const float *s_gate, *s_up, *s_down;
+    const uint8_t *s_gate, *s_up, *s_down;
 };
 
 // Grouped SwiGLU FFN over permuted rows (routed: offsets != nullptr, E groups)
@@ -61,12 +62,12 @@ struct FfnArgs {
     int wt;           // kF32, kBF16, kE4M3
     const int32_t *offsets;
     const void *a;    // [M, d] rows in wt type (or [*, d] rows picked by a_rows)
-    const float *a_scale;  // e4m3: [M, d/128] (row-aligned with a)
+    const uint8_t *a_scale;  // e4m3: [M, d/128] E8M0 (row-aligned with a)
     const int32_t *a_rows;  // optional: A row r of the GEMM is row a_rows[r] / a_div of a / a_scale
     int a_div;
     FfnWeights w;
     void *h;          // workspace [M, I] in wt type
-    float *h_scale;   // e4m3: [M, I/128]
+    uint8_t *h_scale;  // e4m3: [M, I/128] E8M0
     // output: either y_perm (routed) or the combine (shared)
     void *y;          // routed: [M, d] f32 / bf16; shared: [M, d] f32
     // which GEMMs to run: 1 = gate/up only, 2 = down only, 3 = both
@@ -137,13 +138,13 @@ struct Fp8GemmArgs {
     int M;
     const int32_t *offsets;
     const uint8_t *A;
-    const float *As;
+    const uint8_t *As;
     const int32_t *a_rows;  // optional: row m reads row a_rows[m] / a_div of A / As
     int a_div;
     int a_src_rows;         // rows of A when a_rows is given
     int K;
     const uint8_t *B;
-    const float *Bs;
+    const uint8_t *Bs;
     int N;
     float *out;
     int ldo;
@@ -152,15 +153,15 @@ struct Fp8GemmArgs {
 // non-empty range [kseg[e], kseg[e+1]) (multiples of 128; kseg [257], or
 // nullptr for one group over [0, K)), out + e*cstride [M, ldo] =
 // sum_kb As(m, kb) Bs(n, kb) sum_k A(m,k) B(n,k) over that range.  A [M, K],
-// B [N, K] codes (K the row stride), As [M, K/128], Bs [N, K/128] power-of-two
+// B [N, K] codes (K the row stride), As [M, K/128], Bs [N, K/128] E8M0
 // scales.  Groups with an empty range are not written.
 struct Fp8KgArgs {
     int M, N, K;
     const int32_t *kseg;
     const uint8_t *A;
-    const float *As;
+    const uint8_t *As;
     const uint8_t *B;
-    const float *Bs;
+    const uint8_t *Bs;
     float *out;
     int ldo;
     int64_t cstride;

@@ -42,7 +42,7 @@ struct FfnWs {
 FfnWs ffn_ws(int rows, const moe_desc_t *d) {
     FfnWs w{};
     w.h = align_up((size_t)rows * d->I * elem_bytes(d->wt));
-    w.h_scale = d->wt == MOE_E4M3 ? align_up((size_t)rows * (d->I / 128) * sizeof(float)) : 0;
+    w.h_scale = d->wt == MOE_E4M3 ? align_up((size_t)rows * (d->I / 128)) : 0;  // E8M0 bytes
     w.total = w.h + w.h_scale;
     return w;
 }
@@ -50,7 +50,7 @@ FfnWs ffn_ws(int rows, const moe_desc_t *d) {
 // The routed FFN stage: h (+ its scales) for T*k rows, and for e4m3 room for
 // x quantised once per token (moe_expert_gate_up_rows).
 size_t xq_bytes(const moe_desc_t *d) {
-    return d->wt == MOE_E4M3 ? align_up((size_t)d->T * d->d) + align_up((size_t)d->T * (d->d / 128) * sizeof(float)) : 0;
+    return d->wt == MOE_E4M3 ? align_up((size_t)d->T * d->d) + align_up((size_t)d->T * (d->d / 128)) : 0;
 }
 size_t routed_ffn_ws(const moe_desc_t *d) { return ffn_ws(d->T * d->k, d).total + xq_bytes(d); }
 
@@ -132,7 +132,7 @@ moe_status_t moe_route(const moe_desc_t *d, const void *x, const float *w_router
 
 moe_status_t moe_dispatch(const moe_desc_t *d, const int32_t *idx, const void *x, int32_t *counts,
                           int32_t *offsets, int32_t *row_src, int32_t *row_of, void *x_perm,
-                          float *x_perm_scale, void *workspace, size_t ws_bytes, void *stream) {
+                          uint8_t *x_perm_scale, void *workspace, size_t ws_bytes, void *stream) {
     moe_status_t st = check_desc(d);
     if (st != MOE_OK) return st;
     if (!idx || !counts || !offsets || !row_src || !row_of) return MOE_EINVAL;
@@ -145,7 +145,7 @@ moe_status_t moe_dispatch(const moe_desc_t *d, const int32_t *idx, const void *x
 
 moe_status_t moe_dispatch_noalloc(const moe_desc_t *d, const int32_t *idx, const void *x, int32_t *counts,
                                   int32_t *offsets, int32_t *row_src, int32_t *row_of, void *x_perm,
-                                  float *x_perm_scale, void *stream) {
+                                  uint8_t *x_perm_scale, void *stream) {
     moe_status_t st = check_desc(d);
     if (st != MOE_OK) return st;
     if (!idx || !counts || !offsets || !row_src || !row_of) return MOE_EINVAL;
@@ -159,7 +159,7 @@ moe_status_t moe_dispatch_noalloc(const moe_desc_t *d, const int32_t *idx, const
 // a_rows == nullptr: A = x_perm (+ x_perm_scale), one row per routed row.
 // a_rows != nullptr: A row r is row a_rows[r] / k of x (T rows; quantised into the
 // workspace first for e4m3).
-static moe_status_t expert_ffn_phases(const moe_desc_t *d, const void *x_perm, const float *x_perm_scale,
+static moe_status_t expert_ffn_phases(const moe_desc_t *d, const void *x_perm, const uint8_t *x_perm_scale,
                                       const int32_t *a_rows, const int32_t *offsets,
                                       const moe_ffn_weights_t *experts, void *y_perm, void *workspace,
                                       size_t ws_bytes, void *stream, int phases) {
@@ -174,7 +174,7 @@ static moe_status_t expert_ffn_phases(const moe_desc_t *d, const void *x_perm, c
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (a_rows && d->wt == MOE_E4M3 && (phases & 1)) {
         char *xq = ws + w.total;
-        float *xs = reinterpret_cast<float *>(xq + align_up((size_t)d->T * d->d));
+        uint8_t *xs = reinterpret_cast<uint8_t *>(xq + align_up((size_t)d->T * d->d));
         hipError_t e = moe::launch_quant_rows_e4m3(d->T, d->d, static_cast<const uint16_t *>(x_perm),
                                                    reinterpret_cast<uint8_t *>(xq), xs, s);
         if (e != hipSuccess) return MOE_EHIP;
@@ -194,7 +194,7 @@ static moe_status_t expert_ffn_phases(const moe_desc_t *d, const void *x_perm, c
     a.a_div = d->k;
     a.w = to_internal(experts);
     a.h = ws;
-    a.h_scale = w.h_scale ? reinterpret_cast<float *>(ws + w.h) : nullptr;
+    a.h_scale = w.h_scale ? reinterpret_cast<uint8_t *>(ws + w.h) : nullptr;
     a.y = y_perm;
     a.phases = phases;
     a.combine = false;
@@ -202,14 +202,14 @@ static moe_status_t expert_ffn_phases(const moe_desc_t *d, const void *x_perm, c
     return hip_status(moe::launch_ffn(a, s));
 }
 
-moe_status_t moe_expert_ffn(const moe_desc_t *d, const void *x_perm, const float *x_perm_scale,
+moe_status_t moe_expert_ffn(const moe_desc_t *d, const void *x_perm, const uint8_t *x_perm_scale,
                             const int32_t *offsets, const moe_ffn_weights_t *experts, void *y_perm,
                             void *workspace, size_t ws_bytes, void *stream) {
     return expert_ffn_phases(d, x_perm, x_perm_scale, nullptr, offsets, experts, y_perm, workspace, ws_bytes,
                              stream, 3);
 }
 
-moe_status_t moe_expert_gate_up(const moe_desc_t *d, const void *x_perm, const float *x_perm_scale,
+moe_status_t moe_expert_gate_up(const moe_desc_t *d, const void *x_perm, const uint8_t *x_perm_scale,
                                 const int32_t *offsets, const moe_ffn_weights_t *experts, void *workspace,
                                 size_t ws_bytes, void *stream) {
     return expert_ffn_phases(d, x_perm, x_perm_scale, nullptr, offsets, experts, nullptr, workspace, ws_bytes,
@@ -250,7 +250,7 @@ moe_status_t moe_combine(const moe_desc_t *d, const void *x, const moe_ffn_weigh
     a.a_scale = nullptr;
     if (d->wt == MOE_E4M3) {
         char *xq = ws + w.total;
-        float *xs = reinterpret_cast<float *>(xq + align_up((size_t)d->T * d->d));
+        uint8_t *xs = reinterpret_cast<uint8_t *>(xq + align_up((size_t)d->T * d->d));
         hipError_t e = moe::launch_quant_rows_e4m3(d->T, d->d, static_cast<const uint16_t *>(x),
                                                    reinterpret_cast<uint8_t *>(xq), xs, s);
         if (e != hipSuccess) return MOE_EHIP;
@@ -259,7 +259,7 @@ moe_status_t moe_combine(const moe_desc_t *d, const void *x, const moe_ffn_weigh
     }
     a.w = to_internal(shared);
     a.h = ws;
-    a.h_scale = w.h_scale ? reinterpret_cast<float *>(ws + w.h) : nullptr;
+    a.h_scale = w.h_scale ? reinterpret_cast<uint8_t *>(ws + w.h) : nullptr;
     a.y = y;
     a.phases = 3;
     a.combine = true;

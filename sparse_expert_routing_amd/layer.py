@@ -58,7 +58,7 @@ class MoeLayer:
         if self.x_perm is None:
             A, d = self.T * self.k, self.d
             self.x_perm = torch.empty((A, d), dtype=_TORCH_STORAGE[self.wt], device=self.device)
-            self.x_perm_scale = (torch.empty((A, d // 128), dtype=torch.float32, device=self.device)
+            self.x_perm_scale = (torch.empty((A, d // 128), dtype=torch.uint8, device=self.device)
                                  if self.wt == "e4m3" else None)
 
     def forward(self, x, bias, gap=False, stream=None, gather_in_gemm=True):

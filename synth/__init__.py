@@ -113,7 +113,7 @@ def uniform(seed, tensor, n, lo, hi):
 def normal_e4m3_blocks(seed, tensor, G, R, C, std):
     assert R % 128 == 0 and C % 128 == 0
     q = np.empty((G, R, C), dtype=np.uint8)
-    s = np.empty((G, R // 128, C // 128), dtype=np.float32)
+    s = np.empty((G, R // 128, C // 128), dtype=np.uint8)  # E8M0 bytes: 2^(s - 127)
     lib().synth_normal_e4m3_blocks(seed, tensor, G, R, C, std, _p(q), _p(s))
     return q, s
 
@@ -194,7 +194,7 @@ def make_router(cfg: Config):
 
 def make_ffn(cfg: Config, G: int, tids):
     """Weights of G SwiGLU experts: gate, up [G, I, d] and down [G, d, I], plus
-    128x128 block scales when stored as e4m3 (None otherwise)."""
+    128x128 block scales (E8M0 bytes) when stored as e4m3 (None otherwise)."""
     tg, tu, td = tids
     if cfg.wt == E4M3:
         g, sg = normal_e4m3_blocks(cfg.seed, tg, G, cfg.I, cfg.d, cfg.std_w)

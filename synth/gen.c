@@ -249,10 +249,11 @@ void synth_uniform(uint64_t seed, uint32_t tensor, int64_t n, double lo, double 
  * 128): the same bf16 values synth_normal gives for this seed and tensor
  * (element index (g*R + r)*C + c), then per 128x128 block: amax = max |v|, scale = the smallest
  * power of two at or above amax / 448 (the fp32 quotient; 1 when amax = 0), q = e4m3(v / scale).
- * q: [G, R, C] codes; scales: [G, R/128, C/128] fp32.
+ * q: [G, R, C] codes; scales: [G, R/128, C/128] as OCP MX E8M0 bytes (the
+ * biased exponent of the power of two: byte e stands for 2^(e-127)).
  */
 void synth_normal_e4m3_blocks(uint64_t seed, uint32_t tensor, int64_t G, int64_t R, int64_t C,
-                              double std, uint8_t *q, float *scales) {
+                              double std, uint8_t *q, uint8_t *scales) {
     uint16_t *tbl = bf16_quantile_table(std);
     int64_t RB = R / 128, CB = C / 128;
     int64_t nb = G * RB * CB;
@@ -282,7 +283,11 @@ void synth_normal_e4m3_blocks(uint64_t seed, uint32_t tensor, int64_t G, int64_t
             if (b & 0x7FFFFFu) b = (b & 0xFF800000u) + 0x800000u; /* next power of two */
             memcpy(&s, &b, 4);
         }
-        scales[blk] = s;
+        {
+            uint32_t sb;
+            memcpy(&sb, &s, 4);
+            scales[blk] = (uint8_t)(sb >> 23); /* s is a positive normal power of two */
+        }
         for (int r = 0; r < 128; ++r) {
             uint8_t *dst = q + (g * R + rb * 128 + r) * C + cb * 128;
             for (int c = 0; c < 128; ++c) dst[c] = e4m3_encode_sat(v[r * 128 + c] / s);

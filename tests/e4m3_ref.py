@@ -1,7 +1,22 @@
 """Library-side e4m3 tile quantisation for the CPU pins: torch's float8_e4m3fn
 cast, with the tile scale formed through frexp / ldexp (the smallest power of
-two at or above amax / 448, 1 for an all-zero tile)."""
+two at or above amax / 448, 1 for an all-zero tile), and the OCP MX E8M0
+scale bytes (byte e stands for 2^(e - 127)) through numpy's frexp / ldexp."""
+import numpy as np
 import torch
+
+
+def to_e8m0(s) -> np.ndarray:
+    """Power-of-two scales (tensor or array) -> E8M0 bytes: s = 0.5 * 2^e by frexp."""
+    s = s.numpy() if isinstance(s, torch.Tensor) else np.asarray(s)
+    m, e = np.frexp(s.astype(np.float64))
+    assert (m == 0.5).all(), "not a power of two"
+    return (e - 1 + 127).astype(np.uint8)
+
+
+def from_e8m0(b) -> np.ndarray:
+    """E8M0 bytes -> fp64 scales 2^(b - 127)."""
+    return np.ldexp(1.0, np.asarray(b).astype(np.int32) - 127)
 
 
 def tile_scale(amax: torch.Tensor) -> torch.Tensor:

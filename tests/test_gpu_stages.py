@@ -104,7 +104,7 @@ def run_dispatch(T, d, act, wt, idx, x):
     row_src, row_of = empty(A, torch.int32), empty(A, torch.int32)
     gin = {"f32": torch.float32, "bf16": torch.int16, "e4m3": torch.uint8}[wt]
     x_perm = empty((A, d), gin)
-    xs = empty((A, d // 128), torch.float32) if wt == "e4m3" else None
+    xs = empty((A, d // 128), torch.uint8) if wt == "e4m3" else None
     ws = empty(_lib.workspace_bytes(ds, _lib.MOE_WS_DISPATCH), torch.uint8)
     moe.moe_dispatch(ds, dev(idx), dev(x), counts, offsets, row_src, row_of, x_perm, xs, ws)
     torch.cuda.synchronize()
@@ -215,6 +215,50 @@ def test_expert_ffn_small(wt, kind, T):
     err = max_rel(yvals(y, wt), yvals(yo, wt))
     say(f"[ffn] {wt} {kind} T={T}: max rel err {err:.3e}")
     assert err <= TOL[wt], err
+
+
+@pytest.mark.parametrize("T,d,I", [(257, 256, 128), (4096, 512, 256)])
+def test_expert_ffn_e4m3_arbitrary_scale_bytes(T, d, I):
+    """Every e4m3 scale crosses the interface as an E8M0 byte (2^(e - 127)),
+    so a scale is a power of two by construction.  Here the weight block
+    scales and the activation tile scales are not the quantiser's: random
+    bytes over 2^-12 .. 2^12 (block by block and tile by tile), which the
+    block-scaled MFMAs must apply exactly as the oracle's E8M0 decoder reads
+    them (small-tile kernel at T=257, the persistent kernel at T=4096)."""
+    cfg = synth.Config("ffn-e8m0", seed=27, T=T, d=d, I=I, wt="e4m3")
+    say(f"[ffn] e4m3 arbitrary scale bytes T={T} d={d} I={I}")
+    experts = synth.make_ffn(cfg, 256, (synth.TID_GATE, synth.TID_UP, synth.TID_DOWN))
+    rng = np.random.default_rng(T)
+    for n in ("s_gate", "s_up", "s_down"):
+        experts[n] = rng.integers(127 - 12, 127 + 13, experts[n].shape).astype(np.uint8)
+    offsets, a_rows, a_sc = ffn_inputs(cfg, "random")
+    a_sc = rng.integers(127 - 12, 127 + 13, a_sc.shape).astype(np.uint8)
+    y = run_ffn(cfg, offsets, a_rows, a_sc, experts)
+    rows = None if T <= 257 else np.unique(rng.integers(0, cfg.A, 256)).astype(np.int32)
+    yo = oracle.expert_ffn(oracle.shape_of(cfg), experts, offsets, a_rows, a_sc, rows=rows)
+    yg = y if rows is None else y[rows]
+    err = max_rel(yvals(yg, "e4m3"), yvals(yo, "e4m3"))
+    say(f"[ffn] e4m3 arbitrary scale bytes T={T}: max rel err {err:.3e}")
+    assert err <= TOL["e4m3"], err
+
+
+@pytest.mark.parametrize("T,d,I", [(40, 256, 128), (4096, 512, 256)])
+def test_expert_ffn_e4m3_nan_scale_byte(T, d, I):
+    """E8M0 byte 255 is the format's NaN, not a scale: a weight block given it
+    makes exactly the outputs that block feeds NaN (the down block (0, 0) of
+    the largest group: that expert's rows x output columns 0..127) and
+    leaves every other output finite (small-tile and persistent kernels)."""
+    cfg = synth.Config("ffn-nan", seed=21, T=T, d=d, I=I, wt="e4m3")
+    say(f"[ffn] e4m3 NaN scale byte T={T} d={d} I={I}")
+    experts = synth.make_ffn(cfg, 256, (synth.TID_GATE, synth.TID_UP, synth.TID_DOWN))
+    offsets, a_rows, a_sc = ffn_inputs(cfg, "random")
+    e = int(np.argmax(np.diff(offsets)))
+    experts["s_down"][e, 0, 0] = 255
+    yv = yvals(run_ffn(cfg, offsets, a_rows, a_sc, experts), "e4m3")
+    rows = np.zeros(cfg.A, bool)
+    rows[offsets[e]:offsets[e + 1]] = True
+    assert np.isnan(yv[rows, :128]).all()
+    assert np.isfinite(yv[rows, 128:]).all() and np.isfinite(yv[~rows]).all()
 
 
 @pytest.mark.parametrize("kind,T,d,I", [("random", 40, 1024, 512), ("skewed", 100, 512, 512), ("same8", 17, 512, 1024),

@@ -67,7 +67,7 @@ def bf16_round(v):
 
 def dequant_blocks(codes, scales):
     c = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64)
-    s = torch.from_numpy(scales).to(torch.float64)
+    s = torch.from_numpy(e4m3_ref.from_e8m0(scales))
     return c * s.repeat_interleave(128, -2).repeat_interleave(128, -1)
 
 

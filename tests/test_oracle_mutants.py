@@ -34,6 +34,8 @@ MUTANTS = [
     ("h not rounded to bf16", "for (int i = 0; i < n; ++i) h[i] = bf16_round(h[i]);", "(void)0;"),
     ("y_perm not rounded", "return sh->wt == OR_F32 ? (double)(float)v : bf16_round(v);", "return v;"),
     ("tile scale off", "float t = amax / 448.0f;", "float t = amax / 240.0f;"),
+    ("E8M0 bias off by one", "ldexp(1.0, (int)e - 127)", "ldexp(1.0, (int)e - 126)"),
+    ("E8M0 encoder off by one", "return (uint8_t)(ex - 1 + 127);", "return (uint8_t)(ex + 127);"),
     ("tile scale not a power of two", "if (b & 0x7FFFFFu) b = (b & 0xFF800000u) + 0x800000u; /* next power of two */",
      "(void)0;"),
     ("gap off by one", "if (r == k) k1th = v[best];", "if (r == k - 1) k1th = v[best];"),

@@ -49,7 +49,7 @@ def dequant_weights(w, s, dt):
     if dt == "bf16":
         return torch.from_numpy(synth.bf16_to_f32(w).astype(np.float64))
     q = torch.from_numpy(w).view(torch.float8_e4m3fn).to(torch.float64)
-    sc = torch.from_numpy(s.astype(np.float64))
+    sc = torch.from_numpy(e4m3_ref.from_e8m0(s))
     sc = sc.repeat_interleave(128, dim=1).repeat_interleave(128, dim=2)
     return q * sc
 
@@ -154,18 +154,24 @@ def test_tile_quantisation_matches_torch_cast():
     xv = torch.from_numpy(synth.bf16_to_f32(x)).reshape(7, 3, 128)
     amax = xv.abs().amax(dim=2)
     ref_q, ref_s = e4m3_ref.quant_last(xv.reshape(7, 384))
-    assert np.array_equal(s, ref_s.numpy())
+    assert s.dtype == np.uint8 and np.array_equal(s, e4m3_ref.to_e8m0(ref_s))
     assert np.array_equal(q, ref_q.view(torch.uint8).reshape(7, 384).numpy())
     # the scale is a power of two with amax / scale in (224, 448]: the tile's
     # largest value lands in the top binade of e4m3
-    m, _ = np.frexp(s)
-    assert (m == 0.5).all()
-    r = amax.numpy() / s
+    r = amax.numpy() / e4m3_ref.from_e8m0(s)
     assert (r > 224).all() and (r <= 448).all()
-    # an all-zero tile gets scale 1 and zero codes
+    # an all-zero tile gets scale 1 (E8M0 byte 127) and zero codes
     z = np.zeros((1, 128), np.float32)
     qz, sz = oracle.quant_e4m3_rows(z, "f32")
-    assert sz[0, 0] == 1.0 and not qz.any()
+    assert sz[0, 0] == 127 and not qz.any()
+
+
+def test_e8m0_codec_matches_ldexp():
+    """The oracle's E8M0 decoder over all 256 bytes: 2^(e - 127) by numpy's
+    ldexp for e = 0 .. 254, NaN for 255 (OCP MX scale format)."""
+    for e in range(255):
+        assert oracle.e8m0_decode(e) == float(np.ldexp(1.0, e - 127)), e
+    assert np.isnan(oracle.e8m0_decode(255))
 
 
 # ------------------------------------------------------------------ router
