@@ -61,6 +61,9 @@ def main():
                          "share of an 8-way expert-parallel layer, 32 experts of ~4096 rows)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--loop-steps", type=int, default=None,
+                    help="length of the balancing loop for the imbalance curve (default: the workload's, 100 for "
+                         "the skewed prefill); steps past --steps run untimed; 0: only the timed steps")
     ap.add_argument("--no-sub", action="store_true",
                     help="skewed workload only: skip the fp8 and decode sub-results")
     ap.add_argument("--backward", action="store_true",
@@ -98,7 +101,7 @@ def main():
     K = args.steps
     # the balancing loop of the skewed workload always runs its full length
     # (100 steps) for the imbalance curve; steps past the timed ones are untimed
-    curve_steps = max(K, cfg.steps)
+    curve_steps = max(K, cfg.steps if args.loop_steps is None else args.loop_steps)
     out, inp = measure(cfg, K, args.warmup, curve_steps, args.fresh_batches, backward=args.backward)
     out["metric"] = METRIC
     if not args.no_cpu_baseline:
