@@ -221,16 +221,16 @@ __device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff,
 // compiler does not see these LDS writes, so it adds no wait for them before
 // the transposing LDS reads (for which it cannot tell the units apart and
 // would wait on every load in flight).  The kernel's own vmcnt waits and
-// barriers order them, as they do the builtin's.  M0 is set right before
-// the load and declared clobbered, so the compiler keeps nothing in it
-// across the block.
+// barriers order them, as they do the builtin's.  The LDS address goes in
+// through an M0 operand, so the compiler itself writes M0 for the block
+// (and knows it does); the s_nop covers the M0 write -> LDS DMA hazard.
 __device__ __forceinline__ void dma_asm(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint16_t *lds_block) {
     const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)(lds_block));
     const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
-                 : "s"(lds), "v"(voff), "s"(r), "s"(so)
-                 : "memory", "m0");
+                 : "v"(voff), "s"(r), "s"(so), "{m0}"(lds)
+                 : "memory");
 }
 
 template <bool ASM>
@@ -446,8 +446,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
 
         // One 16-wide K step: 16 MFMAs on (AC, BC).  The next step's 8
         // fragments (from the units nA / nB at piece column cn into AN, BN_)
-        // are read at READ_AT(r) (before MFMA READ_AT(r)), the load DMA(x)
-        // (if any) right after MFMA x.  The order is fixed by scheduling
+        // are read at READ_AT(r) (before MFMA READ_AT(r); only those of the
+        // NB_ live row blocks), the load DMA(x) (if any) right after MFMA
+        // x.  The order is fixed by scheduling
         // barriers: a slot load blocks this wave's issue for up to about one
         // MFMA's duration, so loads are spread between MFMAs rather than
         // issued back to back.
@@ -461,7 +462,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
 #define STEP(AC, BC, AN, BN_, nA, nB, cn, DMA, NB_)                                            \
         _Pragma("unroll") for (int x = 0; x < 16; ++x) {                                       \
             _Pragma("unroll") for (int r = 0; r < 8; ++r)                                      \
-                if (READ_AT(r) == x) { FRAG_READ(r, AN, BN_, nA, nB, cn) }                     \
+                if (READ_AT(r) == x && ((r) < 4 ? (r) < (NB_) : (NB_) > 0)) {                  \
+                    FRAG_READ(r, AN, BN_, nA, nB, cn)                                          \
+                }                                                                              \
             __builtin_amdgcn_sched_barrier(0);                                                 \
             if ((NB_) > (x >> 2)) /* 32-row blocks wholly past the group's end: no MFMA */       \
                 acc[x >> 2][x & 3] = mma<TRANS>(AC[x >> 2], BC[x & 3], acc[x >> 2][x & 3]);     \
@@ -485,8 +488,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         B_RSRC()  // this tile's B resources, for the loads of stages 2..
         // Rows of this wave's 128 that belong to the group (wave-uniform):
-        // the MFMAs of a 32-row block with none are left out (its loads and
-        // fragment reads still run, keeping the schedule and barriers).
+        // the MFMAs and A fragment reads of a 32-row block with none are
+        // left out, and a wave with no rows reads no B fragments either
+        // (its slot loads still run, keeping the schedule and barriers).
         const int live = m_end - m0 - wm * 128;
         bf16x8 a0[4], b0[4], a1[4], b1[4];
         {

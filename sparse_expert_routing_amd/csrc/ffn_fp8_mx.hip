@@ -403,7 +403,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
         // One 64-wide K step: 16 MFMAs on (AC, BC) with the stage's exponents
         // (EA per row block, EB0 / EB1 for the gate / up column blocks).  The
         // next step's 8 fragments (units nA / nB, piece column cn) are read at
-        // READ_AT(r), the slot load DMA(x) right after MFMA x; scheduling
+        // READ_AT(r) (A only for the NB_ live row blocks, B only if any is
+        // live), the slot load DMA(x) right after MFMA x; scheduling
         // barriers keep the order.
 #define FRAG_READ(r, AN, BN_, nA, nB, cn)                                                      \
         if ((r) < 4)                                                                           \
@@ -413,7 +414,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
 #define STEP(AC, BC, AN, BN_, nA, nB, cn, DMA, NB_, EA, EB)                                   \
         _Pragma("unroll") for (int x = 0; x < 16; ++x) {                                       \
             _Pragma("unroll") for (int r = 0; r < 8; ++r)                                      \
-                if (READ_AT(r) == x) { FRAG_READ(r, AN, BN_, nA, nB, cn) }                     \
+                if (READ_AT(r) == x && ((r) < 4 ? (r) < (NB_) : (NB_) > 0)) {                  \
+                    FRAG_READ(r, AN, BN_, nA, nB, cn)                                          \
+                }                                                                              \
             __builtin_amdgcn_sched_barrier(0);                                                 \
             if ((NB_) > (x >> 2))                                                              \
                 acc[x >> 2][x & 3] = mma<TRANS>(AC[x >> 2], BC[x & 3], acc[x >> 2][x & 3], EA[x >> 2], \
