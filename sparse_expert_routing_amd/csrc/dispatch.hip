@@ -232,7 +232,24 @@ hipError_t scratch_ptr(int32_t **out) {
     return hipSuccess;
 }
 
+// One GEMM row per thread: its token's E8M0 tile scales, written per
+// 128-block (each block's writes coalesced over consecutive rows).
+__global__ __launch_bounds__(256) void k_gather_scales_km(int M, int nkb, int div, const int32_t *__restrict__ rows,
+                                                          const uint8_t *__restrict__ scales,
+                                                          uint8_t *__restrict__ out) {
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r >= M) return;
+    const uint8_t *in = scales + (size_t)(rows[r] / div) * nkb;
+    for (int kb = 0; kb < nkb; ++kb) out[(size_t)kb * M + r] = in[kb];
+}
+
 }  // namespace
+
+hipError_t launch_gather_scales_kmajor(int M, int nkb, int div, const int32_t *rows, const uint8_t *scales,
+                                       uint8_t *out, hipStream_t s) {
+    hipLaunchKernelGGL(k_gather_scales_km, dim3((M + 255) / 256), dim3(256), 0, s, M, nkb, div, rows, scales, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_dispatch_noalloc(DispatchArgs a, hipStream_t s) {
     if (a.T > kDispatchScratchTokens) return hipErrorInvalidValue;  // the caller checks first

@@ -65,7 +65,8 @@ struct MxParams {
     int M;
     const int32_t *offsets;   // routed: [E+1] row ranges
     const uint8_t *A;         // [rows, K] codes
-    const uint8_t *As;        // [rows, K/128] E8M0 scales (byte e: 2^(e-127))
+    const uint8_t *As;        // [rows, K/128] E8M0 scales (byte e: 2^(e-127)); as_km: [K/128, M]
+    int as_km;                // As per 128-block in GEMM row order (rows gathered through a_rows)
     const int32_t *a_rows;    // optional: GEMM row r reads row a_rows[r] / a_div of A / As
     int a_div;
     int K;
@@ -276,7 +277,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
     int e = 0, m0 = 0, m_end = 0, n0 = 0, kbase = 0;
     const uint32_t a_rows_total = p.a_rows ? (uint32_t)(p.M / p.a_div) : (uint32_t)p.M;
     const __amdgpu_buffer_rsrc_t rA = buf_rsrc(p.A, a_rows_total * (uint32_t)K);
-    const __amdgpu_buffer_rsrc_t rAs = buf_rsrc(p.As, a_rows_total * (uint32_t)nkall);
+    const __amdgpu_buffer_rsrc_t rAs = buf_rsrc(p.As, (p.as_km ? (uint32_t)p.M : a_rows_total) * (uint32_t)nkall);
+    const uint32_t sstride = p.as_km ? (uint32_t)p.M : 1u;  // A-row scale bytes between 128-blocks
     const __amdgpu_buffer_rsrc_t rBs = buf_rsrc(KG ? p.Bs : p.As, KG ? (uint32_t)p.N * (uint32_t)nkall : 1u);
     const uint32_t b_bytes = (uint32_t)p.N * (uint32_t)K;
     const int nbk = p.N / 128;  // weight scale blocks along N
@@ -300,7 +302,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
         {                                                                                      \
             const int kb_ = min((st_), nk - 1);                                                \
             _Pragma("unroll") for (int i = 0; i < 4; ++i)                                      \
-                sa_[i] = __builtin_amdgcn_raw_buffer_load_b8(rAs, soff[i] + kb_, 0, 0);        \
+                sa_[i] = __builtin_amdgcn_raw_buffer_load_b8(rAs, soff[i] + kb_ * sstride, 0, 0); \
             if (KG) {                                                                          \
                 _Pragma("unroll") for (int j = 0; j < 4; ++j)                                  \
                     sb_[j] = __builtin_amdgcn_raw_buffer_load_b8(rBs, bsoff[j] + kb_, 0, 0);   \
@@ -348,11 +350,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
         _Pragma("unroll") for (int i = 0; i < 8; ++i) ar_[i] = min(m0 + drow[i], m_end - 1);    \
         _Pragma("unroll") for (int i = 0; i < 4; ++i)                                          \
             sr_[i] = min(m0 + wm * 128 + 32 * i + (lane & 31), m_end - 1);                     \
-        if (p.a_rows) { /* the 12 row lookups issued together */                               \
+        if (p.a_rows) { /* the row lookups issued together */                                  \
             _Pragma("unroll") for (int i = 0; i < 8; ++i) ar_[i] = p.a_rows[ar_[i]];            \
-            _Pragma("unroll") for (int i = 0; i < 4; ++i) sr_[i] = p.a_rows[sr_[i]];            \
+            if (!p.as_km) {                                                                    \
+                _Pragma("unroll") for (int i = 0; i < 4; ++i) sr_[i] = p.a_rows[sr_[i]];        \
+            }                                                                                  \
             _Pragma("unroll") for (int i = 0; i < 8; ++i) ar_[i] /= p.a_div;                    \
-            _Pragma("unroll") for (int i = 0; i < 4; ++i) sr_[i] /= p.a_div;                    \
+            if (!p.as_km) {                                                                    \
+                _Pragma("unroll") for (int i = 0; i < 4; ++i) sr_[i] /= p.a_div;                \
+            }                                                                                  \
         }                                                                                      \
         _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                        \
             aoff[i] = (uint32_t)ar_[i] * (uint32_t)K + (uint32_t)(dcol[i] + kbase);            \
@@ -362,7 +368,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
             if (m0 + r >= m_end) aoff[i] = kOobOff; /* padding rows fetch nothing */           \
         }                                                                                      \
         _Pragma("unroll") for (int i = 0; i < 4; ++i)                                          \
-            soff[i] = (uint32_t)sr_[i] * (uint32_t)nkall + (uint32_t)(kbase / LKB);            \
+            soff[i] = p.as_km ? (uint32_t)sr_[i] : (uint32_t)sr_[i] * (uint32_t)nkall + (uint32_t)(kbase / LKB); \
         _Pragma("unroll") for (int j = 0; j < 4; ++j)                                          \
             bsoff[j] = (uint32_t)(n0 + wn * 128 + 32 * j + (lane & 31)) * (uint32_t)nkall +    \
                        (uint32_t)(kbase / LKB);                                                \
@@ -714,6 +720,7 @@ hipError_t launch_ffn_fp8_mx(const FfnArgs &a, hipStream_t s) {
         p.offsets = a.offsets;
         p.A = static_cast<const uint8_t *>(a.a);
         p.As = a.a_scale;
+        p.as_km = a.a_rows && a.a_scale_kmajor;
         p.a_rows = a.a_rows;
         p.a_div = a.a_rows ? a.a_div : 1;
         p.K = a.d;

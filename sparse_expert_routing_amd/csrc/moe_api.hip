@@ -52,7 +52,11 @@ FfnWs ffn_ws(int rows, const moe_desc_t *d) {
 size_t xq_bytes(const moe_desc_t *d) {
     return d->wt == MOE_E4M3 ? align_up((size_t)d->T * d->d) + align_up((size_t)d->T * (d->d / 128)) : 0;
 }
-size_t routed_ffn_ws(const moe_desc_t *d) { return ffn_ws(d->T * d->k, d).total + xq_bytes(d); }
+// e4m3 gathered rows: their tile scales per 128-block in GEMM row order.
+size_t xs_km_bytes(const moe_desc_t *d) {
+    return d->wt == MOE_E4M3 ? align_up((size_t)d->T * d->k * (d->d / 128)) : 0;
+}
+size_t routed_ffn_ws(const moe_desc_t *d) { return ffn_ws(d->T * d->k, d).total + xq_bytes(d) + xs_km_bytes(d); }
 
 size_t dispatch_ws(const moe_desc_t *d) {
     const size_t nblk = (d->T + moe::kDispatchBlock - 1) / moe::kDispatchBlock;
@@ -198,6 +202,16 @@ static moe_status_t expert_ffn_phases(const moe_desc_t *d, const void *x_perm, c
     a.y = y_perm;
     a.phases = phases;
     a.combine = false;
+    if (a_rows && d->wt == MOE_E4M3 && (phases & 1) && moe::ffn_fp8_mx_ok(a)) {
+        // the persistent e4m3 kernel reads each stage's A-row scales of a
+        // tile as one contiguous run: lay the gathered rows' scales out per
+        // 128-block in GEMM row order (instead of one scattered byte per row)
+        uint8_t *xs_km = reinterpret_cast<uint8_t *>(ws + w.total + xq_bytes(d));
+        hipError_t e = moe::launch_gather_scales_kmajor(a.M, d->d / 128, d->k, a_rows, x_perm_scale, xs_km, s);
+        if (e != hipSuccess) return MOE_EHIP;
+        a.a_scale = xs_km;
+        a.a_scale_kmajor = true;
+    }
     a.k = d->k;
     return hip_status(moe::launch_ffn(a, s));
 }

@@ -357,13 +357,16 @@ def run_ffn_rows(cfg, offsets, row_src, x, experts):
 @pytest.mark.parametrize("wt,T,d,I,kind", [("f32", 40, 256, 128, "random"), ("bf16", 300, 256, 128, "same8"),
                                            ("bf16", 4096, 512, 256, "skewed"), ("bf16", 100, 512, 512, "skewed"),
                                            ("e4m3", 257, 256, 128, "skewed"),
-                                           ("e4m3", 1000, 256, 128, "random")])
+                                           ("e4m3", 1000, 256, 128, "random"),
+                                           ("e4m3", 4096, 512, 256, "skewed"), ("e4m3", 4097, 512, 256, "random")])
 def test_gate_up_rows_matches_materialised(wt, T, d, I, kind):
     """Gate/up reading the token rows through row_src (no x_perm) gives the
     same y_perm bit for bit as the GEMM over the materialised x_perm (same
     rows, same order, same kernels); small-group, large-group (T=4096) and
-    e4m3 (x quantised once per token) paths.  Parity of this path with the
-    oracle is the layer tests' (the layer uses it by default)."""
+    e4m3 (x quantised once per token, its tile scales laid out per 128-block
+    in GEMM row order for the persistent kernel at T >= 4096) paths.  Parity
+    of this path with the oracle is the layer tests' (the layer uses it by
+    default)."""
     act = "f32" if wt == "f32" else "bf16"
     cfg = synth.Config("ffn-rows", seed=25, T=T, d=d, I=I, act=act, wt=wt)
     say(f"[ffn] gathered gate/up {wt} T={T} d={d} I={I} {kind}")
