@@ -239,7 +239,7 @@ __global__ __launch_bounds__(256) void k_gather_scales_km(int M, int nkb, int di
                                                           uint8_t *__restrict__ out) {
     const int r = blockIdx.x * 256 + threadIdx.x;
     if (r >= M) return;
-    const uint8_t *in = scales + (size_t)(rows[r] / div) * nkb;
+    const uint8_t *in = scales + (size_t)(rows ? rows[r] / div : r) * nkb;
     for (int kb = 0; kb < nkb; ++kb) out[(size_t)kb * M + r] = in[kb];
 }
 

@@ -66,7 +66,7 @@ struct MxParams {
     const int32_t *offsets;   // routed: [E+1] row ranges
     const uint8_t *A;         // [rows, K] codes
     const uint8_t *As;        // [rows, K/128] E8M0 scales (byte e: 2^(e-127)); as_km: [K/128, M]
-    int as_km;                // As per 128-block in GEMM row order (rows gathered through a_rows)
+    int as_km;                // As per 128-block in GEMM row order (no gather of the scales)
     const int32_t *a_rows;    // optional: GEMM row r reads row a_rows[r] / a_div of A / As
     int a_div;
     int K;
@@ -74,7 +74,7 @@ struct MxParams {
     const uint8_t *S0, *S1;   // [G, N/128, K/128] E8M0 block scales
     int N;                    // B rows per expert (SwiGLU: rows of each of gate / up)
     uint8_t *hq;              // MX_SWIGLU_Q: [M, N] codes
-    uint8_t *hs;              // MX_SWIGLU_Q: [M, N/128] E8M0
+    uint8_t *hs;              // MX_SWIGLU_Q: [N/128, M] E8M0, per 128-block in row order
     uint16_t *out;            // MX_STORE: bf16 [M, N]
     float *yout;              // MX_COMBINE: f32 [M, N]; MX_F32: f32 rows of ldo
     int ldo;
@@ -571,7 +571,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
                         }
                     }
                     const uint32_t so = (ok && wn == 0 && g == 0)
-                                            ? (uint32_t)row * (uint32_t)(p.N / 128) + (uint32_t)(cn0 / 128)
+                                            ? (uint32_t)(cn0 / 128) * (uint32_t)p.M + (uint32_t)row
                                             : kOobOff;
                     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)e8m0_of(s), rS, so, 0, 0);
                 }
@@ -720,7 +720,7 @@ hipError_t launch_ffn_fp8_mx(const FfnArgs &a, hipStream_t s) {
         p.offsets = a.offsets;
         p.A = static_cast<const uint8_t *>(a.a);
         p.As = a.a_scale;
-        p.as_km = a.a_rows && a.a_scale_kmajor;
+        p.as_km = a.a_scale_kmajor;
         p.a_rows = a.a_rows;
         p.a_div = a.a_rows ? a.a_div : 1;
         p.K = a.d;
@@ -740,6 +740,7 @@ hipError_t launch_ffn_fp8_mx(const FfnArgs &a, hipStream_t s) {
         q.offsets = a.offsets;
         q.A = static_cast<const uint8_t *>(a.h);
         q.As = a.h_scale;
+        q.as_km = 1;  // written so by the gate/up epilogue
         q.a_div = 1;
         q.K = a.I;
         q.B0 = static_cast<const uint8_t *>(a.w.down);

@@ -47,8 +47,9 @@ hipError_t launch_dispatch_noalloc(DispatchArgs a, hipStream_t s);
 // Quantise T rows of bf16 x to e4m3 per 1x128 tile (no permutation); E8M0 scales.
 hipError_t launch_quant_rows_e4m3(int rows, int d, const uint16_t *x, uint8_t *q, uint8_t *scales,
                                   hipStream_t s);
-// out[kb * M + r] = scales[(rows[r] / div) * nkb + kb]: the per-row E8M0 tile
-// scales of gathered rows laid out per 128-block in GEMM row order.
+// out[kb * M + r] = scales[(rows[r] / div) * nkb + kb] (rows == nullptr: row r):
+// the per-row E8M0 tile scales of (gathered) rows laid out per 128-block in
+// GEMM row order.
 hipError_t launch_gather_scales_kmajor(int M, int nkb, int div, const int32_t *rows, const uint8_t *scales,
                                        uint8_t *out, hipStream_t s);
 
@@ -68,13 +69,13 @@ struct FfnArgs {
     const void *a;    // [M, d] rows in wt type (or [*, d] rows picked by a_rows)
     const uint8_t *a_scale;  // e4m3: [M, d/128] E8M0 (row-aligned with a)
     const int32_t *a_rows;  // optional: A row r of the GEMM is row a_rows[r] / a_div of a / a_scale
-    // e4m3 with a_rows, persistent kernel only: a_scale is instead [d/128, M],
-    // each 128-block's scales in GEMM row order (no gather through a_rows)
+    // e4m3, persistent kernel only: a_scale is instead [d/128, M], each
+    // 128-block's scales in GEMM row order (no gather through a_rows)
     bool a_scale_kmajor;
     int a_div;
     FfnWeights w;
     void *h;          // workspace [M, I] in wt type
-    uint8_t *h_scale;  // e4m3: [M, I/128] E8M0
+    uint8_t *h_scale;  // e4m3: [M, I/128] E8M0 ([I/128, M] on the persistent e4m3 kernel)
     // output: either y_perm (routed) or the combine (shared)
     void *y;          // routed: [M, d] f32 / bf16; shared: [M, d] f32
     // which GEMMs to run: 1 = gate/up only, 2 = down only, 3 = both

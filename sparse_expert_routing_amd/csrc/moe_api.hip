@@ -77,7 +77,9 @@ size_t backward_ws(const moe_desc_t *d) {
 }
 
 size_t combine_ws(const moe_desc_t *d) {
-    return ffn_ws(d->T, d).total + xq_bytes(d) + align_up(moe::ffn_shared_split_bytes(d->T, d->d, d->I, d->wt));
+    const size_t xs_km = d->wt == MOE_E4M3 ? align_up((size_t)d->T * (d->d / 128)) : 0;
+    return ffn_ws(d->T, d).total + xq_bytes(d) + xs_km +
+           align_up(moe::ffn_shared_split_bytes(d->T, d->d, d->I, d->wt));
 }
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
@@ -281,8 +283,18 @@ moe_status_t moe_combine(const moe_desc_t *d, const void *x, const moe_ffn_weigh
     a.y_perm = y_perm;
     a.row_of = row_of;
     a.cw = weights;
+    if (d->wt == MOE_E4M3 && moe::ffn_fp8_mx_ok(a)) {
+        // the persistent e4m3 kernel reads each stage's A-row scales of a
+        // tile as one contiguous run: lay them out per 128-block
+        uint8_t *xs_km = reinterpret_cast<uint8_t *>(ws + w.total + xq_bytes(d));
+        hipError_t e = moe::launch_gather_scales_kmajor(d->T, d->d / 128, 1, nullptr, a.a_scale, xs_km, s);
+        if (e != hipSuccess) return MOE_EHIP;
+        a.a_scale = xs_km;
+        a.a_scale_kmajor = true;
+    }
     if (moe::ffn_shared_split_bytes(d->T, d->d, d->I, d->wt))
-        a.part = reinterpret_cast<float *>(ws + w.total + xq_bytes(d));
+        a.part = reinterpret_cast<float *>(
+            ws + w.total + xq_bytes(d) + (d->wt == MOE_E4M3 ? align_up((size_t)d->T * (d->d / 128)) : 0));
     return hip_status(moe::launch_ffn(a, s));
 }
 
