@@ -114,27 +114,45 @@ __device__ __forceinline__ void tilemap_init(TileMap &tm, const int32_t *__restr
     tm.total = __shfl(incl, 63, 64);
 }
 
-__device__ __forceinline__ void tilemap_find(const TileMap &tm, int mt, int &e, int &m0, int &m_end) {
+// Routed tile t -> expert e, rows [m0, m_end) of its row tile and column
+// tile nt.  Tiles run expert by expert (an expert with n row tiles owns
+// NT * n consecutive tiles); inside an expert, groups of at most kGroupM
+// row tiles with the row tile fastest, so the row tiles that read one
+// weight column slice run side by side and no group spans two experts'
+// weights.
+__device__ __forceinline__ void tilemap_tile(const TileMap &tm, int t, int NT, int &e, int &m0, int &m_end,
+                                             int &nt) {
     const int lane = threadIdx.x & 63;
+    const int rt = t / NT;
     const int mine = tm.nt[0] + tm.nt[1] + tm.nt[2] + tm.nt[3];
-    const bool own = mt >= tm.excl && mt < tm.excl + mine;
+    const bool own = rt >= tm.excl && rt < tm.excl + mine;
     const int owner = __ffsll((unsigned long long)__ballot(own)) - 1;
-    int my_e = 0, my_m0 = 0, my_end = 0;
+    int my_e = 0, my_first = 0, my_n = 1, my_off = 0, my_end = 0;
     if (own) {
-        int s = mt - tm.excl;
+        int s = rt - tm.excl, first = tm.excl;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (s >= 0 && s < tm.nt[i]) {
                 my_e = lane * 4 + i;
-                my_m0 = tm.off[i] + s * LM;
+                my_first = first;
+                my_n = tm.nt[i];
+                my_off = tm.off[i];
                 my_end = tm.off[i + 1];
             }
             s -= tm.nt[i];
+            first += tm.nt[i];
         }
     }
     e = __shfl(my_e, owner, 64);
-    m0 = __shfl(my_m0, owner, 64);
+    const int first = __shfl(my_first, owner, 64), n = __shfl(my_n, owner, 64);
+    const int off = __shfl(my_off, owner, 64);
     m_end = __shfl(my_end, owner, 64);
+    const int u = t - NT * first;
+    const int j = u / (kGroupM * NT);
+    const int gm = min(kGroupM, n - kGroupM * j);
+    const int within = u - j * kGroupM * NT;
+    m0 = off + (kGroupM * j + within % gm) * LM;
+    nt = within / gm;
 }
 
 // K-grouped tile map: lane owns groups 4*lane .. 4*lane+3; a group with a
@@ -374,6 +392,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
             m_end = p.M;                                                                       \
             kbase = __builtin_amdgcn_readfirstlane(p.kseg[e]);                                 \
             nk = __builtin_amdgcn_readfirstlane((p.kseg[e + 1] - kbase) / LK);                 \
+        } else if (ROUTED) {                                                                   \
+            tilemap_tile(tm, (tt), NT, e, m0, m_end, nt_);                                     \
         } else {                                                                               \
             const int gsz_ = kGroupM * NT;                                                     \
             const int grp_ = (tt) / gsz_, within_ = (tt) - grp_ * gsz_;                        \
@@ -381,13 +401,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
             const int gm_ = min(kGroupM, Mt - mfirst_);                                        \
             mt_ = mfirst_ + within_ % gm_;                                                     \
             nt_ = within_ / gm_;                                                               \
-            if (ROUTED) {                                                                      \
-                tilemap_find(tm, mt_, e, m0, m_end);                                           \
-            } else {                                                                           \
-                e = 0;                                                                         \
-                m0 = mt_ * LM;                                                                 \
-                m_end = p.M;                                                                   \
-            }                                                                                  \
+            e = 0;                                                                             \
+            m0 = mt_ * LM;                                                                     \
+            m_end = p.M;                                                                       \
         }                                                                                      \
         e = __builtin_amdgcn_readfirstlane(e);                                                 \
         m0 = __builtin_amdgcn_readfirstlane(m0);                                               \
