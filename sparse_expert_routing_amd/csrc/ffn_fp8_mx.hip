@@ -420,25 +420,27 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-#define READ_AT(r) (2 * (r))
 #define B_ROW(j) ((DUAL ? (((j) >> 1) * 128 + wn * 64 + ((j) & 1) * 32) : (wn * 128 + (j) * 32)) + (lane & 31))
         // One 64-wide K step: 16 MFMAs on (AC, BC) with the stage's exponents
         // (EA per row block, EB0 / EB1 for the gate / up column blocks).  The
-        // next step's 8 fragments (units nA / nB, piece column cn) are read at
-        // READ_AT(r) (A only for the NB_ live row blocks, B only if any is
-        // live), the slot load DMA(x) right after MFMA x; scheduling
-        // barriers keep the order.
+        // next step's 8 fragments (units nA / nB, piece column cn; fragments
+        // 0-3 of A, 4-7 of B) are read before MFMA RD(r) (A only for the NB_
+        // live row blocks, B only if any is live), HOOK(x) runs before MFMA
+        // x and the slot load DMA(x) right after it; scheduling barriers
+        // keep the order.
 #define FRAG_READ(r, AN, BN_, nA, nB, cn)                                                      \
         if ((r) < 4)                                                                           \
             AN[(r) & 3] = frag32((nA), wm * 128 + ((r) & 3) * 32 + (lane & 31), (cn));         \
         else                                                                                   \
             BN_[(r) & 3] = frag32((nB), B_ROW((r) & 3), (cn));
-#define STEP(AC, BC, AN, BN_, nA, nB, cn, DMA, NB_, EA, EB)                                   \
+#define STEP(AC, BC, AN, BN_, nA, nB, cn, RD, HOOK, DMA, NB_, EA, EB)                         \
         _Pragma("unroll") for (int x = 0; x < 16; ++x) {                                       \
             _Pragma("unroll") for (int r = 0; r < 8; ++r)                                      \
-                if (READ_AT(r) == x && ((r) < 4 ? (r) < (NB_) : (NB_) > 0)) {                  \
+                if (RD(r) == x && ((r) < 4 ? (r) < (NB_) : (NB_) > 0)) {                       \
                     FRAG_READ(r, AN, BN_, nA, nB, cn)                                          \
                 }                                                                              \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+            HOOK(x);                                                                           \
             __builtin_amdgcn_sched_barrier(0);                                                 \
             if ((NB_) > (x >> 2))                                                              \
                 acc[x >> 2][x & 3] = mma<TRANS>(AC[x >> 2], BC[x & 3], acc[x >> 2][x & 3], EA[x >> 2], \
@@ -469,42 +471,64 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
         }
 
         // Stage kt: step 0 (K bytes 0-63 of the rows: pieces 2g, 2g+1) then
-        // step 1 (pieces 4 + 2g, 5 + 2g).  Step 0 streams A_{kt+2} into the
-        // unit B_{kt-1} left, one load per two MFMAs, and reads step 1's
-        // fragments; then, once A_{kt+1} and B_{kt+1} have landed (only
-        // A_{kt+2}'s 8 loads may remain), a barrier frees A_kt's and B_kt's
-        // units; step 1 streams B_{kt+2} into A_kt's unit and reads stage
-        // kt+1's first fragments.  Stage kt+1's scales are loaded first.
-#define DMA_S0(x) if ((x) & 1) ISSUE_A(kt + 2, (x) >> 1, fA)
-#define DMA_S1(x) if (((x) & 1) == 0) ISSUE_B(kt + 2, (x) >> 1, fB)
+        // step 1 (pieces 4 + 2g, 5 + 2g).  The ring's five units hold A_kt,
+        // B_kt, A_{kt+1}, B_{kt+1} and A_{kt+2} (in flight).  Step 0 reads
+        // step 1's fragments, B's first; once every wave has them, a barrier
+        // frees B_kt's unit and B_{kt+2} streams into it.  Once A_{kt+1} and
+        // B_{kt+1} have landed, a second barrier makes them visible and frees
+        // A_kt's unit: step 1 streams A_{kt+3} into it and reads stage kt+1's
+        // first fragments.  One load per MFMA or two, eight per step, and each
+        // has two steps or more to land.  (Stage 0 also issues A_2, in step 0:
+        // the fifth unit serves the epilogue until the tile starts.)  Stage
+        // kt+1's scales are loaded first.
+#define RD_S0(r) ((r) < 4 ? 5 + (r) : (r) - 4)
+#define RD_S1(r) (2 * (r))
+#define HOOK_S0(x)                                                                             \
+        if ((x) == 4) {                                                                        \
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);                                           \
+            wait_vmcnt_lds<63>(); /* this wave's B_kt reads done */                            \
+            __builtin_amdgcn_s_barrier();                                                      \
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);                                           \
+        }
+#define HOOK_S1(x)
+#define DMA_S0(x)                                                                              \
+        if ((x) < 8 && kt == 0) ISSUE_A(2, (x), UNIT(uF));                                    \
+        if ((x) >= 6 && (x) < 14) ISSUE_B(kt + 2, (x) - 6, fB)
+#define DMA_S1(x) if (((x) & 1) == 0) ISSUE_A(kt + 3, (x) >> 1, fA)
+        // At least this many loads a wave issues after B_{kt+1}: A_{kt+2},
+        // stage kt+1's A-row (and, K-grouped, B-row) scale bytes, B_{kt+2}
+        // (the weight block scales may add one or two more).
+        constexpr int kStageWait = 16 + (KG ? 8 : 4);
 #define KLOOP(NB_)                                                                             \
         {                                                                                      \
-            int u0 = 0;                                                                        \
+            int uA = 0, uB = 1, uNA = 2, uNB = 3, uF = 4; /* ring units */                     \
             for (int kt = 0; kt < nk; ++kt) {                                                  \
-                const int u1 = u0 + 1 - (u0 + 1 >= NUNIT ? NUNIT : 0);                         \
-                const int u2 = u0 + 2 - (u0 + 2 >= NUNIT ? NUNIT : 0);                         \
-                const int u3 = u0 + 3 - (u0 + 3 >= NUNIT ? NUNIT : 0);                         \
-                const int u4 = u0 + 4 - (u0 + 4 >= NUNIT ? NUNIT : 0);                         \
-                const uint8_t *cA = UNIT(u0), *cB = UNIT(u1);                                  \
-                uint8_t *fA = UNIT(u4), *fB = UNIT(u0); /* A_{kt+2}, B_{kt+2} */               \
+                const uint8_t *cA = UNIT(uA), *cB = UNIT(uB);                                  \
+                uint8_t *fA = UNIT(uA), *fB = UNIT(uB); /* A_{kt+3}, B_{kt+2} */               \
                 int ea_[4], eb_[4];                                                            \
                 _Pragma("unroll") for (int i = 0; i < 4; ++i) ea_[i] = sa[i];                  \
                 /* B exponents per column block: per lane (K-grouped rows) or the block's */   \
                 _Pragma("unroll") for (int j = 0; j < 4; ++j)                                  \
                     eb_[j] = KG ? sb[j] : sw[DUAL && j >= 2 ? 1 : 0];                          \
                 LOAD_SCALES(kt + 1, sa_n, sw_n, sb_n);                                         \
-                STEP(a0, b0, a1, b1, cA, cB, 4 + 2 * g, DMA_S0, NB_, ea_, eb_);                \
+                STEP(a0, b0, a1, b1, cA, cB, 4 + 2 * g, RD_S0, HOOK_S0, DMA_S0, NB_, ea_, eb_); \
                 __atomic_signal_fence(__ATOMIC_SEQ_CST);                                       \
-                wait_vmcnt_lds<8>();          /* A_{kt+1}, B_{kt+1} landed for this wave */    \
-                __builtin_amdgcn_s_barrier(); /* ... for all waves; A_kt, B_kt no longer read */ \
+                wait_vmcnt_lds<kStageWait>(); /* A_{kt+1}, B_{kt+1} landed for this wave */    \
+                __builtin_amdgcn_s_barrier(); /* ... for all waves; A_kt no longer read */     \
                 __atomic_signal_fence(__ATOMIC_SEQ_CST);                                       \
-                const uint8_t *nA = UNIT(u2), *nB = UNIT(u3);                                  \
-                STEP(a1, b1, a0, b0, nA, nB, 2 * g, DMA_S1, NB_, ea_, eb_);                    \
+                const uint8_t *nA = UNIT(uNA), *nB = UNIT(uNB);                                \
+                STEP(a1, b1, a0, b0, nA, nB, 2 * g, RD_S1, HOOK_S1, DMA_S1, NB_, ea_, eb_);    \
                 _Pragma("unroll") for (int i = 0; i < 4; ++i) sa[i] = sa_n[i];                 \
                 _Pragma("unroll") for (int j = 0; j < 4; ++j) sb[j] = sb_n[j];                 \
                 sw[0] = sw_n[0];                                                               \
                 sw[1] = sw_n[1];                                                               \
-                u0 = u2;                                                                       \
+                const int fr_ = uA;                                                            \
+                uA = uNA;                                                                      \
+                uNA = uF;                                                                      \
+                uF = fr_;                                                                      \
+                const int nb_ = uB;                                                            \
+                uB = uNB;                                                                      \
+                uNB = nb_;                                                                     \
             }                                                                                  \
         }
         switch (live <= 0 ? 0 : live >= 128 ? 4 : (live + 31) / 32) {
@@ -515,11 +539,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
             default: KLOOP(0) break;
         }
 #undef KLOOP
+#undef RD_S0
+#undef RD_S1
+#undef HOOK_S0
+#undef HOOK_S1
 #undef DMA_S0
 #undef DMA_S1
 #undef STEP
 #undef FRAG_READ
-#undef READ_AT
 #undef B_ROW
         __syncthreads();  // every wave done with the ring (and its loads landed)
         first = false;
