@@ -18,17 +18,19 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
-// binary32 -> bf16 bits, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+// binary32 -> bf16 bits, round to nearest even; a NaN keeps its sign and
+// top payload bits and is made quiet ((u >> 16) | 0x40).  gfx950's
+// v_cvt_pk_bf16_f32 computes exactly this for every binary32 input in the
+// kernels' default mode (nearest-even rounding, denormals kept), two values
+// per instruction.
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_hw{lo, hi}, bf16x2_hw));
 }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.0f) & 0xffffu; }
 
 // binary32 -> OCP FP8 E4M3FN byte: round to nearest even, saturate to +-448
 // (the format has no infinity; S.1111.111 is NaN).  Normal range: keep the

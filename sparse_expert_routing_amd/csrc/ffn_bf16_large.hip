@@ -309,7 +309,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
     constexpr bool DUAL = EPI == EPI_SWIGLU || EPI == EPI_PRE;
     constexpr bool TRANS = EPI != EPI_COMBINE;  // register epilogue (no LDS staging)
     constexpr int BN = DUAL ? LB / 2 : LB;  // output columns per tile
-    constexpr int kEpiStores = TRANS ? (EPI == EPI_SWIGLU ? 32 : 64) : 0;  // buffer stores per lane per register epilogue
+    // buffer stores per lane per register epilogue
+    constexpr int kEpiStores = TRANS ? (EPI == EPI_SWIGLU ? 16 : EPI == EPI_STORE ? 32 : 64) : 0;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[NUNIT * UNIT_ELEMS];  // 160 KB
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -586,8 +587,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
                 PROLOGUE_LOADS();
             }
             // Register epilogue: lane owns tile rows wm*128 + 32i + (lane & 31)
-            // and, per 32-column block, 4 runs of 4 consecutive columns: one
-            // 8-byte bf16 buffer store per run.  Values are computed for every
+            // and, per 32-column block, 4 runs of 4 consecutive columns (bf16
+            // outputs: regrouped across the lane halves into 2 runs of 8, one
+            // 16-byte buffer store each).  Values are computed for every
             // row (padding rows repeat the group's last row); a padding row's
             // stores get an offset past the end of the output resource, which
             // the hardware drops, so every lane issues every store (the wait
@@ -635,26 +637,40 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
 #pragma unroll
                 for (int jj = 0; jj < (DUAL ? 2 : 4); ++jj) {
                     __builtin_amdgcn_sched_barrier(0);
+                    // w[q]: columns 8q + c4 .. +3 of the block as bf16
+                    uint32_t w[4][2];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        uint32_t lo, hi;
                         if constexpr (DUAL) {
-                            lo = hi = 0;
+                            w[q][0] = w[q][1] = 0;
                             if (blk) {  // an empty block's stores are dropped: skip its math
                                 float h[4];
 #pragma unroll
                                 for (int u = 0; u < 4; ++u)
                                     h[u] = swiglu(acc_read(acc[i][jj][4 * q + u]), acc_read(acc[i][2 + jj][4 * q + u]));
-                                lo = pack_bf16x2(h[0], h[1]);
-                                hi = pack_bf16x2(h[2], h[3]);
+                                w[q][0] = pack_bf16x2(h[0], h[1]);
+                                w[q][1] = pack_bf16x2(h[2], h[3]);
                             }
                         } else {
-                            lo = pack_bf16x2(acc_read(acc[i][jj][4 * q]), acc_read(acc[i][jj][4 * q + 1]));
-                            hi = pack_bf16x2(acc_read(acc[i][jj][4 * q + 2]), acc_read(acc[i][jj][4 * q + 3]));
+                            w[q][0] = pack_bf16x2(acc_read(acc[i][jj][4 * q]), acc_read(acc[i][jj][4 * q + 1]));
+                            w[q][1] = pack_bf16x2(acc_read(acc[i][jj][4 * q + 2]), acc_read(acc[i][jj][4 * q + 3]));
                         }
-                        const int col = (DUAL ? wn * 64 : wn * 128) + jj * 32 + 8 * q + c4;
-                        __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)lo, (int)hi}, rOut,
-                                                                   obase + (uint32_t)col * 2u, 0, 0);
+                    }
+                    // Lanes l and l + 32 hold one row: swapping w[2h+1] of
+                    // lanes 0-31 with w[2h] of lanes 32-63 leaves each lane
+                    // the 8 consecutive columns 16h + 8g .. +7.
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                        for (int k = 0; k < 2; ++k) {
+                            const auto sw2 = __builtin_amdgcn_permlane32_swap(w[2 * h][k], w[2 * h + 1][k], false, false);
+                            w[2 * h][k] = sw2[0];
+                            w[2 * h + 1][k] = sw2[1];
+                        }
+                        const int col = (DUAL ? wn * 64 : wn * 128) + jj * 32 + 16 * h + 8 * g;
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            i32x4{(int)w[2 * h][0], (int)w[2 * h][1], (int)w[2 * h + 1][0], (int)w[2 * h + 1][1]}, rOut,
+                            obase + (uint32_t)col * 2u, 0, 0);
                     }
                 }
             }

@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
     constexpr bool TRANS = EPI != MX_COMBINE;
     constexpr int BN = DUAL ? LB / 2 : LB;  // output columns per tile
     // buffer stores per lane per register epilogue: gate/up 4 x (8 codes + 1 scale); store 64; fp32 64
-    constexpr int kEpiStores = TRANS ? (DUAL ? 36 : 64) : 0;
+    constexpr int kEpiStores = TRANS ? (DUAL ? 36 : EPI == MX_STORE ? 32 : 64) : 0;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NUNIT * UNIT_BYTES];  // 160 KB
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -627,13 +627,29 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         __builtin_amdgcn_sched_barrier(0);
+                        // w[q]: columns 8q + c4 .. +3 of the block as bf16.
+                        // Lanes l and l + 32 hold one row; swapping w[2h+1]
+                        // of lanes 0-31 with w[2h] of lanes 32-63 leaves
+                        // each lane 8 consecutive columns, 16h + 8g .. +7:
+                        // one 16-byte store where there were two 8-byte ones.
+                        uint32_t w[4][2];
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            const uint32_t lo = pack_bf16x2(acc_read(acc[i][jj][4 * q]), acc_read(acc[i][jj][4 * q + 1]));
-                            const uint32_t hi = pack_bf16x2(acc_read(acc[i][jj][4 * q + 2]), acc_read(acc[i][jj][4 * q + 3]));
-                            const int col = wn * 128 + jj * 32 + 8 * q + c4;
-                            __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)lo, (int)hi}, rOut, obase + (uint32_t)col * 2u,
-                                                                  0, 0);
+                            w[q][0] = pack_bf16x2(acc_read(acc[i][jj][4 * q]), acc_read(acc[i][jj][4 * q + 1]));
+                            w[q][1] = pack_bf16x2(acc_read(acc[i][jj][4 * q + 2]), acc_read(acc[i][jj][4 * q + 3]));
+                        }
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                            for (int k = 0; k < 2; ++k) {
+                                const auto sw2 = __builtin_amdgcn_permlane32_swap(w[2 * h][k], w[2 * h + 1][k], false, false);
+                                w[2 * h][k] = sw2[0];
+                                w[2 * h + 1][k] = sw2[1];
+                            }
+                            const int col = wn * 128 + jj * 32 + 16 * h + 8 * g;
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                i32x4{(int)w[2 * h][0], (int)w[2 * h][1], (int)w[2 * h + 1][0], (int)w[2 * h + 1][1]}, rOut,
+                                obase + (uint32_t)col * 2u, 0, 0);
                         }
                     }
                 }
