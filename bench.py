@@ -213,6 +213,9 @@ def measure(cfg, K, warmup, curve_steps, fresh_batches, backward=False):
     imb = ch_all.max(axis=1) / ch_all.mean(axis=1)
     ch = ch_all[:K]  # the timed steps
     tiles = np.ceil(ch / 256.0).sum(axis=1)  # launched 256-row tiles of the routed GEMMs
+    # the same tiles weighted by their height: live 32-row blocks / 8 (a block
+    # with no rows issues no MFMA)
+    tiles_h = (np.ceil(ch / 32.0) / 8.0).sum(axis=1)
 
     touched = float((ch > 0).sum(axis=1).mean())
     s_w = 1 if cfg.wt == "e4m3" else 2
@@ -235,7 +238,7 @@ def measure(cfg, K, warmup, curve_steps, fresh_batches, backward=False):
     log(f"[bench] gate/up GEMM {gu['achieved']:.1f} {gu['unit']} ({100 * gu['frac']:.1f}% of peak); down "
         f"{dn['achieved']:.1f} {dn['unit']} ({100 * dn['frac']:.1f}%); layer {total_flops / (ms_step * 1e-3) / 1e12:.1f} "
         f"TFLOP/s; max/mean load {imb[0]:.2f} -> {imb[-1]:.2f} over {len(imb)} steps; 256-row tiles "
-        f"{tiles.mean():.0f} (ideal {A / 256:.0f})")
+        f"{tiles.mean():.0f}, weighted by height {tiles_h.mean():.1f} (ideal {A / 256:.0f})")
 
     gu.update({"kernel": f"routed gate/up grouped GEMM ({kname}, SwiGLU epilogue"
                          + (" + e4m3 quantisation)" if cfg.wt == "e4m3" else ")"),
@@ -270,6 +273,8 @@ def measure(cfg, K, warmup, curve_steps, fresh_batches, backward=False):
         "imbalance_curve": [round(float(v), 4) for v in imb],
         "imbalance_curve_steps": {"timed": K, "untimed_after": int(n_all - K)},
         "routed_row_tiles_mean": float(tiles.mean()),
+        "routed_row_tiles_height_weighted_mean": float(tiles_h.mean()),
+        "routed_row_tiles_ideal": A / 256.0,
     }
     if backward:
         out["backward"] = time_backward(cfg, layer, xs[(K - 1) % len(xs)], min(K, 20))
