@@ -678,7 +678,26 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
         } else {
             // Combine epilogue: four 64-row chunks of the fp32 tile through
             // LDS, so every y_perm gather and y store is a 16-byte access.
+            // The tile's routed-row indices and combine weights (256 rows x
+            // 8) go to LDS first, one 16-byte load pair per thread, so each
+            // gather depends on one global round trip instead of two; rows
+            // past the group's end are clamped to its last row (every load
+            // is valid, only the stores are skipped), which lets the gathers
+            // of several rows be in flight at once.
             float *ch = reinterpret_cast<float *>(smem);
+            int *sro = reinterpret_cast<int *>(reinterpret_cast<uint8_t *>(smem) + kChRows * kChLd * 4);  // [256][8]
+            float *scw = reinterpret_cast<float *>(sro + 256 * 8);            // [256][8]
+            {
+                const int rr = min(cm0 + tid, cm_end - 1);
+                const i32x4 *ro = reinterpret_cast<const i32x4 *>(p.row_of + (size_t)rr * 8);
+                const f32x4 *wo = reinterpret_cast<const f32x4 *>(p.cw + (size_t)rr * 8);
+                const i32x4 r0 = ro[0], r1 = ro[1];
+                const f32x4 w0 = wo[0], w1 = wo[1];
+                *reinterpret_cast<i32x4 *>(sro + tid * 8) = r0;
+                *reinterpret_cast<i32x4 *>(sro + tid * 8 + 4) = r1;
+                *reinterpret_cast<f32x4 *>(scw + tid * 8) = w0;
+                *reinterpret_cast<f32x4 *>(scw + tid * 8 + 4) = w1;
+            }
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 if (wm == (c >> 1)) {
@@ -696,33 +715,43 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
                 }
                 __syncthreads();
                 const int cl = 8 * (lane & 31);
-#pragma unroll 2
+#pragma unroll 4
                 for (int it = 0; it < 8; ++it) {
                     const int rl = wave * 16 + 2 * it + g;
-                    const int row = cm0 + c * kChRows + rl;
-                    if (row < cm_end) {
-                        int rof[8];
-                        float wj[8];
+                    const int tr = c * kChRows + rl;  // tile row
+                    const int row = cm0 + tr;
+                    const int trc = min(tr, cm_end - cm0 - 1);
+                    int rof[8];
+                    float wj[8];
+                    {
+                        const i32x4 a0 = *reinterpret_cast<const i32x4 *>(sro + trc * 8);
+                        const i32x4 a1 = *reinterpret_cast<const i32x4 *>(sro + trc * 8 + 4);
+                        const f32x4 b0 = *reinterpret_cast<const f32x4 *>(scw + trc * 8);
+                        const f32x4 b1 = *reinterpret_cast<const f32x4 *>(scw + trc * 8 + 4);
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            rof[j] = p.row_of[(size_t)row * 8 + j];
-                            wj[j] = p.cw[(size_t)row * 8 + j];
+                        for (int j = 0; j < 4; ++j) {
+                            rof[j] = a0[j];
+                            rof[4 + j] = a1[j];
+                            wj[j] = b0[j];
+                            wj[4 + j] = b1[j];
                         }
-                        i32x4 yv[8];
+                    }
+                    i32x4 yv[8];
 #pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            yv[j] = *reinterpret_cast<const i32x4 *>(p.y_perm + (size_t)rof[j] * p.N + cn0 + cl);
-                        const float *cr = ch + rl * kChLd + cl;
-                        const f32x4 s0 = *reinterpret_cast<const f32x4 *>(cr);
-                        const f32x4 s1 = *reinterpret_cast<const f32x4 *>(cr + 4);
-                        float v[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+                    for (int j = 0; j < 8; ++j)
+                        yv[j] = *reinterpret_cast<const i32x4 *>(p.y_perm + (size_t)rof[j] * p.N + cn0 + cl);
+                    const float *cr = ch + rl * kChLd + cl;
+                    const f32x4 s0 = *reinterpret_cast<const f32x4 *>(cr);
+                    const f32x4 s1 = *reinterpret_cast<const f32x4 *>(cr + 4);
+                    float v[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
 #pragma unroll
-                        for (int j = 0; j < 8; ++j)
+                    for (int j = 0; j < 8; ++j)
 #pragma unroll
-                            for (int u = 0; u < 4; ++u) {
-                                v[2 * u] += wj[j] * bf16_to_f32((uint32_t)yv[j][u] & 0xffffu);
-                                v[2 * u + 1] += wj[j] * bf16_to_f32((uint32_t)yv[j][u] >> 16);
-                            }
+                        for (int u = 0; u < 4; ++u) {
+                            v[2 * u] += wj[j] * bf16_to_f32((uint32_t)yv[j][u] & 0xffffu);
+                            v[2 * u + 1] += wj[j] * bf16_to_f32((uint32_t)yv[j][u] >> 16);
+                        }
+                    if (row < cm_end) {
                         float *yo = p.yout + (size_t)row * p.N + cn0 + cl;
                         *reinterpret_cast<f32x4 *>(yo) = f32x4{v[0], v[1], v[2], v[3]};
                         *reinterpret_cast<f32x4 *>(yo + 4) = f32x4{v[4], v[5], v[6], v[7]};
