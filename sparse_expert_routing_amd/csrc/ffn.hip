@@ -129,7 +129,8 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
     const int c16 = tid & 7;
     const uint16_t *Bg = p.B0 + (size_t)e * p.N * K;
     const uint16_t *Bu = DUAL ? p.B1 + (size_t)e * p.N * K : Bg;
-    uint32_t aoff[4], boff[4];
+    size_t aoff[4];  // A element offsets (the A operand can pass 2^32 elements: x_perm, h)
+    uint32_t boff[4];
     int soff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmParams p) {
         int ar = m0 + row;
         ar = ar < m_end ? ar : m_end - 1;
         if (p.a_rows) ar = p.a_rows[ar] / p.a_div;
-        aoff[i] = (uint32_t)ar * (uint32_t)K + c16 * 8;
+        aoff[i] = (size_t)ar * (size_t)K + c16 * 8;
         const int br = DUAL ? n0 + (row & 63) : n0 + row;
         boff[i] = (uint32_t)br * (uint32_t)K + c16 * 8;
         soff[i] = row * BK + swz(row, c16) * 8;

@@ -133,7 +133,8 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(Fp8Params p) {
     const uint8_t *Sg = p.S0 + ((size_t)e * (p.N / 128) + n0 / 128) * nkb;
     const uint8_t *Su = DUAL ? p.S1 + ((size_t)e * (p.N / 128) + n0 / 128) * nkb : Sg;
 
-    uint32_t aoff[4], boff[BCH];
+    size_t aoff[4];  // A byte offsets (the A operand can pass 4 GiB: x_perm, h)
+    uint32_t boff[BCH];
     int soffa[4], soffb[BCH];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(Fp8Params p) {
         int ar = m0 + row;
         ar = ar < m_end ? ar : m_end - 1;
         if (p.a_rows) ar = p.a_rows[ar] / p.a_div;
-        aoff[i] = (uint32_t)ar * (uint32_t)K + c16 * 16;
+        aoff[i] = (size_t)ar * (size_t)K + c16 * 16;
         soffa[i] = row * BK + swz(row, c16) * 16;
     }
 #pragma unroll

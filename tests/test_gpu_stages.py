@@ -305,6 +305,34 @@ def test_expert_ffn_large_groups(kind, wt):
     assert err <= TOL[wt], err
 
 
+@pytest.mark.parametrize("wt", ["bf16", "e4m3"])
+def test_expert_ffn_past_32bit_offsets(wt):
+    """The largest operands: T=80000 tokens at the prefill shape (d=7168,
+    I=2048), 640000 routed rows.  x_perm then holds 4.6e9 elements, past the
+    32-bit byte offsets of the persistent kernels (the host routes the
+    routed FFN to the small-tile kernels) and past 2^32 elements, so the
+    small-tile kernels' row offsets must be 64-bit.  The oracle checks the
+    rows at every group edge, the last row and random rows."""
+    T, d, I = 80000, 7168, 2048
+    cfg = synth.Config("ffn-huge", seed=27, T=T, d=d, I=I, wt=wt)
+    say(f"[ffn] past 32-bit offsets {wt} T={T} d={d} I={I}: generating inputs")
+    experts = synth.make_ffn(cfg, 256, (synth.TID_GATE, synth.TID_UP, synth.TID_DOWN))
+    offsets, a_rows, a_sc = ffn_inputs(cfg, "random")
+    assert cfg.A * d >= (1 << 32)
+    say(f"[ffn] past 32-bit offsets {wt}: GPU")
+    y = run_ffn(cfg, offsets, a_rows, a_sc, experts)
+    rng = np.random.default_rng(2)
+    nz = np.where(np.diff(offsets) > 0)[0]
+    edges = np.concatenate([offsets[nz], offsets[nz + 1] - 1, [cfg.A - 1]])
+    rows = np.unique(np.concatenate([edges, rng.integers(0, cfg.A, 32)])).astype(np.int32)
+    assert int(rows.max()) * d >= (1 << 32)
+    say(f"[ffn] past 32-bit offsets {wt}: oracle on {len(rows)} rows")
+    yo = oracle.expert_ffn(oracle.shape_of(cfg), experts, offsets, a_rows, a_sc, rows=rows)
+    err = max_rel(yvals(y[rows], wt), yvals(yo, wt))
+    say(f"[ffn] past 32-bit offsets {wt}: max rel err {err:.3e} on {len(rows)} rows")
+    assert err <= TOL[wt], err
+
+
 def test_expert_ffn_config2_sampled_rows():
     """Config 2 shapes (T=2048, d=2048, I=512), bf16, real routing; the oracle
     checks 64 sampled permuted rows, including each group's first and last."""
