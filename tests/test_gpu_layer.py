@@ -227,6 +227,20 @@ def test_layer_config5_full_size():
     check_layer(cfg, inp, n_sample=12, n_rows=512)
 
 
+def test_layer_past_32bit_offsets():
+    """The whole layer at T=80000 tokens (d=7168, I=2048, bf16; 640000 routed
+    rows, y_perm 4.6e9 elements): the routed GEMMs run on the small-tile
+    kernels (the persistent ones address operands with 32-bit byte offsets),
+    the shared expert and the combine on the persistent kernel; checked as
+    the full-size workloads are (every token's routing, the dispatch arrays
+    and the bias step bit-exact, y_perm at group and tile edges, sampled
+    tokens end to end)."""
+    cfg = synth.CONFIGS[4].with_(name="prefill-bf16 T80000 d7168 I2048", seed=28, T=80000, skew=0.0,
+                                 bias="uniform")
+    inp = synth.make_inputs(cfg)
+    check_layer(cfg, inp, n_sample=8, n_rows=512)
+
+
 def test_layer_ep8_shard_full_size():
     """One GPU's share of an 8-way expert-parallel layer at full size: the
     bias confines the choice to experts 0-31, so the grouped GEMMs run 32
