@@ -12,31 +12,33 @@
 //     tile as 4x4 v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane, in
 //     AGPRs): per 16 of K a wave reads 8 fragments (8 KB) from LDS for 16
 //     MFMAs, half the LDS traffic per MFMA of a 64x64 wave tile;
-//   - K stages of 64 (each tile row a whole 128-byte line: reading half lines
-//     halves the L2 bandwidth), two 64 KB LDS slots filled straight from
-//     global memory by global_load_lds_dwordx4 (no VGPR staging).  A stage
-//     is 4 steps of 16 K; its fragments are all in registers after step 2,
-//     so a mid-stage barrier (after this wave's loads of the next stage have
-//     landed, s_waitcnt vmcnt) hands its slot to the stage after next: every
-//     stage has 4 steps (~2k cycles) to arrive, with one barrier per stage;
+//   - K stages of 64 (each tile row a whole 128-byte line), the A and B slabs
+//     of a stage (32 KB each) in a ring of five LDS units filled straight
+//     from global memory by buffer_load_dwordx4 ... lds (a buffer resource
+//     per operand, a fixed per-lane offset, the stage offset in an SGPR).  A
+//     stage is 4 steps of 16 K; A of stage s+2 streams in during steps 0-2
+//     and B of stage s+2 during step 3, after a mid-stage barrier (this
+//     wave's loads of stage s+1 landed, s_waitcnt vmcnt) has freed stage s's
+//     units: one barrier per stage, loads spread between the MFMAs;
 //   - fragments are double-buffered in registers: the next 16-wide K step's
 //     8 fragments (the next stage's first step included) are read from LDS
 //     while the current step's 16 MFMAs run, pinned by scheduling barriers;
 //   - LDS layout: 128-byte rows whose 16-byte pieces are XOR-swizzled with
 //     (row & 7) ^ ((row >> 3) & 1), so the 32-row MFMA fragment reads hit
-//     distinct banks for both 32- and 64-bank LDS;
-//   - one persistent workgroup per CU.  Tile t of a round goes to workgroup
-//     w with t = r*P + (w % 8) * (P / 8) + w / 8, so the 32 workgroups an XCD
-//     runs together take 32 consecutive tiles; tiles are ordered in groups
-//     of 8 row tiles x all column tiles, so those 32 share 8 A row-blocks and
-//     4 B column-blocks in the XCD's L2 (and the 8 XCDs of a round share one
-//     group pair in the Infinity Cache);
+//     distinct banks;
+//   - one persistent workgroup per CU; the 32 workgroups an XCD runs together
+//     take 32 consecutive tiles.  Routed tiles run expert by expert, inside an
+//     expert in groups of at most 8 row tiles with the row tile fastest, so
+//     the row tiles that read one weight column slice run side by side in
+//     one L2 and no group spans two experts' weights;
 //   - the row tile -> (expert, first row) map is computed on the device from
 //     `offsets` (a wavefront scan over the 256 experts), never on the host;
-//   - epilogues stage the fp32 tile through LDS in 64-row chunks so every
-//     global store (and the combine's y_perm gathers) is a 16-byte access:
-//     SwiGLU -> bf16 h; bf16 y_perm; or the shared expert's combine
-//     y = acc + sum_j w_j * y_perm[row_of[t*k + j]] in fp32.
+//   - register epilogues from the transposed accumulators (the next tile's
+//     first two stages already in flight): SwiGLU -> bf16 h, or bf16 y_perm,
+//     converted two values per v_cvt_pk_bf16_f32 and stored 16 bytes per
+//     lane after a lane-half swap; the shared expert's combine
+//     y = acc + sum_j w_j * y_perm[row_of[t*k + j]] in fp32 stages 64-row
+//     chunks through LDS so its gathers and stores are 16-byte accesses.
 #include "device.h"
 #include "kernels.h"
 

@@ -21,16 +21,19 @@
 //     every lane of the weight operand, the A row's for lanes l and l+32 of
 //     the activation operand (row l % 32), so the products accumulate in
 //     fp32 with no vector work; a stage's A-row scales are loaded one stage
-//     ahead (before that stage's slot loads, so the stage waits cover them);
-//   - schedule: step 0 streams A of stage s+2 into the unit B of stage s-1
-//     left, one load per two MFMAs, and reads step 1's fragments; after it
-//     every fragment of the stage is in registers, so a mid-stage barrier
-//     (once A and B of stage s+1 have landed) frees the stage's units; step
-//     1 streams B of stage s+2 into A_s's unit and reads stage s+1's first
-//     fragments;
-//   - epilogues as in the bf16 kernel (register stores straight from the
-//     transposed accumulators, the next tile's first two stages already in
-//     flight; the combine stages 64-row chunks through LDS), the gate/up one
+//     ahead (before that stage's slot loads, so the stage waits cover them),
+//     from a layout with each 128-block's scales in GEMM row order (one
+//     contiguous run per stage and 32-row block);
+//   - schedule: the ring holds A_s, B_s, A_{s+1}, B_{s+1} and A_{s+2} (in
+//     flight); step 0 reads step 1's fragments, B's first, then a barrier
+//     frees B_s's unit and B_{s+2} streams into it; a mid-stage barrier
+//     (A_{s+1}, B_{s+1} landed) frees A_s's unit, and step 1 streams A_{s+3}
+//     into it and reads stage s+1's first fragments: eight loads per step,
+//     each with two steps or more to land;
+//   - epilogues as in the bf16 kernel (register stores from the transposed
+//     accumulators, bf16 as 16-byte stores after a lane-half swap, the next
+//     tile's first two stages already in flight; the combine stages 64-row
+//     chunks through LDS), the gate/up one
 //     forming h = silu(g) u in fp32 and quantising it per 1x128 tile (the
 //     tile's 128 h columns; the row amax of the two column waves meets in
 //     the free fifth LDS unit);
@@ -630,8 +633,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_mx(MxParams p) {
                         // w[q]: columns 8q + c4 .. +3 of the block as bf16.
                         // Lanes l and l + 32 hold one row; swapping w[2h+1]
                         // of lanes 0-31 with w[2h] of lanes 32-63 leaves
-                        // each lane 8 consecutive columns, 16h + 8g .. +7:
-                        // one 16-byte store where there were two 8-byte ones.
+                        // each lane 8 consecutive columns, 16h + 8g .. +7,
+                        // stored as one 16 bytes.
                         uint32_t w[4][2];
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
