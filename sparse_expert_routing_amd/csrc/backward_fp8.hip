@@ -398,8 +398,8 @@ __global__ __launch_bounds__(256) void k_q8_cols(int R, const void *__restrict__
 }
 
 // e4m3 codes transposed per group: out[g][c*ldo + coff + r] = in[g][r*C + c]
-// (R, C multiples of 128), 128x128-byte tiles.  Thread (a = tid % 32,
-// b = tid / 32) reads 16 bytes of each of rows 4a .. 4a+3 at columns
+// (R, C multiples of 128), 128x128-byte tiles.  Thread (a = tid / 8,
+// b = tid % 8) reads 16 bytes of each of rows 4a .. 4a+3 at columns
 // 16b .. 16b+15 (four 16-byte loads in flight), transposes the four 4x4
 // blocks in registers and puts word a of output rows 16b .. 16b+15 in LDS;
 // then each output row's 128 bytes go out as eight 16-byte stores.  In LDS,
@@ -412,7 +412,9 @@ __global__ __launch_bounds__(256) void k_t8(int R, int C, const uint8_t *__restr
     in += (int64_t)g * gin;
     out += (int64_t)g * gout;
     {
-        const int a = tid & 31, b = tid >> 5;
+        // eight consecutive threads take one row's whole 128 bytes, so each
+        // load instruction reads eight full lines
+        const int a = tid >> 3, b = tid & 7;
         i32x4 v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
