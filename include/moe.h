@@ -34,8 +34,10 @@
  *   - Arguments are validated on the host before anything is launched:
  *     MOE_EINVAL for a null required pointer, non-positive sizes, k > E, or
  *     d / I not multiples of 128 with e4m3; MOE_ENOTSUP for shapes the library
- *     does not cover (E != 256, k != 8, d or I not a multiple of 64, an
- *     unsupported dtype pair); MOE_EWORKSPACE when ws_bytes is below
+ *     does not cover (E != 256, k != 8, d or I not a multiple of 64, d not a
+ *     multiple of 128 with bf16 weights, T * k >= 2^31 routed rows (their
+ *     indices are int32), an unsupported dtype pair); MOE_EWORKSPACE when
+ *     ws_bytes is below
  *     moe_workspace_bytes(); MOE_ESCRATCH when moe_dispatch_noalloc gets
  *     more tokens than its static scratch holds; MOE_EHIP when a launch
  *     reports an error.

@@ -49,7 +49,8 @@ def call_route(ds, ptrs=True):
     (dict(E=128), _lib.MOE_ENOTSUP), (dict(k=6), _lib.MOE_ENOTSUP), (dict(d=96), _lib.MOE_ENOTSUP),
     (dict(I=100), _lib.MOE_ENOTSUP), (dict(act="f32", wt="bf16"), _lib.MOE_ENOTSUP),
     (dict(wt="e4m3", d=192), _lib.MOE_EINVAL), (dict(wt="e4m3", I=64), _lib.MOE_EINVAL),
-    (dict(act="e4m3", wt="e4m3"), _lib.MOE_ENOTSUP),
+    (dict(act="e4m3", wt="e4m3"), _lib.MOE_ENOTSUP), (dict(d=192), _lib.MOE_ENOTSUP),
+    (dict(T=1 << 28), _lib.MOE_ENOTSUP),  # T*k = 2^31: the routed rows' int32 indices
 ])
 def test_shape_validation(kw, status):
     assert call_route(good_desc(**kw)) == status
