@@ -51,3 +51,38 @@ def test_layer_bitwise_deterministic_full_size(cid):
     for n in runs[0]:
         assert torch.equal(_bits(runs[0][n]), _bits(runs[1][n])), f"{cfg.name}: {n} differs between runs"
     say(f"[determinism] {cfg.name}: every output bit-identical")
+
+
+@pytest.mark.parametrize("cid", [2, 4])
+def test_layer_on_a_side_stream(cid):
+    """Every kernel is launched on the caller's stream: the layer run on a
+    non-default stream, with only that stream synchronised, equals the
+    default-stream run bit for bit (the mid workload on the small-tile
+    kernels; the skewed prefill workload at T=4096, d=1024, I=512 on the
+    persistent ones)."""
+    cfg = synth.CONFIGS[cid] if cid == 2 else synth.CONFIGS[4].with_(name="prefill-zipf-bf16 T4096 d1024 I512",
+                                                                     T=4096, d=1024, I=512)
+    say(f"[stream] {cfg.name}: default stream, then a side stream")
+    inp = synth.make_inputs(cfg)
+    layer = layer_from_inputs(inp)
+    x = upload(inp["x"])
+    outs = []
+    side = torch.cuda.Stream()
+    for use_side in (False, True):
+        b = upload(inp["bias"])
+        for t in (layer.idx, layer.w, layer.counts, layer.row_src, layer.y_perm, layer.y, layer.ws):
+            t.view(torch.uint8).fill_(0xFF)
+        torch.cuda.synchronize()
+        ctx = torch.cuda.stream(side) if use_side else torch.cuda.stream(torch.cuda.current_stream())
+        with ctx:
+            layer.forward(x, b)
+            layer.update_bias(b, cfg.gamma)
+            snap = dict(idx=layer.idx.clone(), w=layer.w.clone(), counts=layer.counts.clone(),
+                        row_src=layer.row_src.clone(), y_perm=layer.y_perm.clone(), y=layer.y.clone(),
+                        bias=b.clone())
+        (side if use_side else torch.cuda.current_stream()).synchronize()
+        outs.append(snap)
+    torch.cuda.synchronize()
+    for n in outs[0]:
+        assert torch.equal(_bits(outs[0][n]), _bits(outs[1][n])), f"{cfg.name}: {n} differs on the side stream"
+    say(f"[stream] {cfg.name}: side-stream run bit-identical")
