@@ -27,6 +27,11 @@ Prints ONE JSON line on stdout (progress goes to stderr).
   sub_results    (default workload only) the fp8 prefill and the decode
                  workloads, 20 timed steps each, with their own roofline
                  entries
+
+--dense-reference instead prints {"dense_reference": [...]}: the routed
+gate/up kernel on one dense group (every row on one expert, M = 65536 and
+131072 rows) beside the vendor GEMM (torch.matmul / torch._scaled_mm) on the
+same product, bf16 and e4m3, for context on the kernel's own efficiency.
 """
 import argparse
 import json
@@ -73,6 +78,10 @@ def main():
                          "default: the same batch every step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (the byte-counter reference)")
+    ap.add_argument("--dense-reference", action="store_true",
+                    help="only time the routed gate/up kernel on one dense group (every row to one expert) "
+                         "beside the vendor GEMM (torch.matmul, torch._scaled_mm) on the same shape; one JSON line")
+    ap.add_argument("--dense-reps", type=int, default=100, help="launches per timing in --dense-reference")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -97,6 +106,9 @@ def main():
         log("[bench] copied 3 x 1 GiB")
         return
     _lib.load()  # fails loudly without the HIP library
+    if args.dense_reference:
+        print(json.dumps({"dense_reference": dense_reference(args.dense_reps)}), flush=True)
+        return
     cfg = synth.CONFIGS[args.config]
     K = args.steps
     # the balancing loop of the skewed workload always runs its full length
@@ -116,6 +128,87 @@ def main():
             sub[r["config"]["workload"]] = r
         out["sub_results"] = sub
     print(json.dumps(out), flush=True)
+
+
+def dense_reference(reps, rows=(65536, 131072)):
+    """The routed gate/up kernel (moe_expert_gate_up) on one dense group of M
+    rows (offsets put every row on expert 0), and the vendor GEMM on the same
+    [M, d] x [2I, d]^T product: torch.matmul in bf16, torch._scaled_mm in e4m3
+    (per-tensor scales; the library applies per-tile E8M0 scales and fuses
+    SwiGLU, writing h [M, I] instead of [M, 2I]).  Each timing is the mean of
+    the second half of `reps` back-to-back launches (sustained clock), the two
+    alternating twice."""
+    import torch
+
+    from sparse_expert_routing_amd import _lib
+    d, I, E, k = 7168, 2048, 256, 8
+
+    def timed(fn):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(reps):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+        tail = ms[reps // 2:]
+        return sum(tail) / len(tail)
+
+    g = torch.Generator(device="cuda").manual_seed(11)
+    res = []
+    for M in rows:
+        flops = 2.0 * M * 2 * I * d
+        for wt in ("bf16", "e4m3"):
+            ds = _lib.desc(M // k, d, E, k, I, "bf16", wt)
+            offsets = torch.full((E + 1,), M, dtype=torch.int32, device="cuda")
+            offsets[0] = 0
+            if wt == "bf16":
+                xp = torch.randn(M, d, device="cuda", generator=g).mul_(0.5).to(torch.bfloat16)
+                gate = torch.empty(E, I, d, device="cuda", dtype=torch.bfloat16)
+                up = torch.empty_like(gate)
+                gate[0].normal_(0, 0.02, generator=g)
+                up[0].normal_(0, 0.02, generator=g)
+                down = torch.empty(E, d, I, device="cuda", dtype=torch.bfloat16)
+                ew, xs = _lib.ffn_weights(gate, up, down), None
+                b = torch.cat([gate[0], up[0]], 0)
+                vendor = lambda: torch.matmul(xp, b.t())  # noqa: E731
+            else:
+                # random e4m3 codes below 0x78 (finite), E8M0 scales 2^-7
+                xp = torch.randint(0, 0x78, (M, d), device="cuda", dtype=torch.uint8, generator=g)
+                xs = torch.full((M, d // 128), 120, device="cuda", dtype=torch.uint8)
+                gate = torch.empty(E, I, d, device="cuda", dtype=torch.uint8)
+                up = torch.empty_like(gate)
+                gate[0].random_(0, 0x78, generator=g)
+                up[0].random_(0, 0x78, generator=g)
+                down = torch.empty(E, d, I, device="cuda", dtype=torch.uint8)
+                s_gu = torch.full((E, I // 128, d // 128), 120, device="cuda", dtype=torch.uint8)
+                s_d = torch.full((E, d // 128, I // 128), 120, device="cuda", dtype=torch.uint8)
+                ew = _lib.ffn_weights(gate, up, down, s_gu, s_gu, s_d)
+                a8 = xp.view(torch.float8_e4m3fn)
+                b8 = torch.cat([gate[0], up[0]], 0).view(torch.float8_e4m3fn)
+                one = torch.ones((), device="cuda", dtype=torch.float32)
+                vendor = lambda: torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one,  # noqa: E731
+                                                  out_dtype=torch.bfloat16)
+            ws = torch.empty(_lib.workspace_bytes(ds, _lib.MOE_WS_FFN), dtype=torch.uint8, device="cuda")
+            ours = lambda: _lib.moe_expert_gate_up(ds, xp, xs, offsets, ew, ws)  # noqa: E731
+            t_o, t_v = [], []
+            for _ in range(2):
+                t_o.append(timed(ours))
+                t_v.append(timed(vendor))
+            peak = PEAK_BF16_TFLOPS if wt == "bf16" else PEAK_FP8_TFLOPS
+            o, v = min(t_o), min(t_v)
+            r = {"dtype": wt, "M": M, "N": 2 * I, "K": d, "ours_ms": round(o, 4), "vendor_ms": round(v, 4),
+                 "ours_tflops": round(flops / o / 1e9, 1), "vendor_tflops": round(flops / v / 1e9, 1),
+                 "ours_frac": round(flops / o / 1e9 / peak, 4), "vendor_frac": round(flops / v / 1e9 / peak, 4)}
+            log(f"[bench] dense {wt} {M}x{2 * I}x{d}: ours {o:.3f} ms ({r['ours_frac']:.3f} of peak), "
+                f"vendor {v:.3f} ms ({r['vendor_frac']:.3f})")
+            res.append(r)
+            del xp, xs, gate, up, down, ws, ew
+            release()
+    return res
 
 
 def release():
