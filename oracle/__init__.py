@@ -68,6 +68,7 @@ def lib():
             "oracle_combine": [vp, vp, vp, vp, vp, vp, i64, vp, vp],
             "oracle_forward": [vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp],
             "oracle_backward": [vp] * 16 + [i32],
+            "oracle_backward_shared_cols": [vp, vp, vp, vp, i32, vp, vp, vp, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -232,6 +233,23 @@ def backward(sh: Shape, x, wr, idx, experts: dict, shared: dict, dy, weight_grad
     if one:
         return {n: out[n] for n in ("dx", "dg", "dwr", "dwg", "dwu", "dwd")}
     return out if weight_grads else dict(dx=out["dx"], dg=out["dg"])
+
+
+def backward_shared_cols(sh: Shape, x, shared: dict, dy, cols):
+    """The shared expert's weight gradients for the SwiGLU columns `cols` only,
+    over all sh.T tokens: dict of dsg, dsu [len(cols), d] (those rows of
+    backward()'s dsg, dsu) and dsd [d, len(cols)] (those columns of its dsd),
+    bit for bit what backward() gives there."""
+    cols = np.ascontiguousarray(cols, dtype=np.int32)
+    nc = len(cols)
+    ws, keep = ffn(shared)
+    out = dict(dsg=np.empty((nc, sh.d), np.float32), dsu=np.empty((nc, sh.d), np.float32),
+               dsd=np.empty((sh.d, nc), np.float32))
+    lib().oracle_backward_shared_cols(ctypes.byref(sh), _p(x), ctypes.byref(ws),
+                                      _p(np.ascontiguousarray(dy, dtype=np.float32)), nc, _p(cols),
+                                      _p(out["dsg"]), _p(out["dsu"]), _p(out["dsd"]))
+    del keep
+    return out
 
 
 def forward(sh: Shape, x, wr, bias, experts: dict, shared: dict, tokens=None):

@@ -859,6 +859,136 @@ void oracle_backward(const or_shape *sh, const void *x, const float *wr, const i
     free(sraw);
 }
 
+/* The shared expert's weight gradients restricted to columns cols[0..nc) of
+ * its SwiGLU width: dsg, dsu [nc, d] hold rows cols[c] of oracle_backward's
+ * [I, d] dsg, dsu and dsd [d, nc] columns cols[c] of its [d, I] dsd, over all
+ * T tokens, with the same arithmetic in the same order.  (Column i of these
+ * gradients needs only column i of the shared expert's hidden layer: its
+ * gate and up rows, its down column, the whole output gradient and x; with
+ * e4m3 weights every weight-gradient operand is quantised per column of a
+ * 128-token group, so the restriction changes no tile.)  This is the same
+ * computation as the shared part of oracle_backward, cut to a few columns so
+ * that it finishes in seconds at the full layer size. */
+void oracle_backward_shared_cols(const or_shape *sh, const void *x, const or_ffn *shared, const float *dy,
+                                 int32_t nc, const int32_t *cols, float *dsg, float *dsu, float *dsd) {
+    const int64_t T = sh->T, d = sh->d, I = sh->I;
+    const int fp8 = sh->wt == OR_E4M3;
+    double *xa = (double *)malloc(sizeof(double) * T * d);   /* x as the GEMMs read it */
+    double *dyw = (double *)malloc(sizeof(double) * T * d);  /* weight-gradient operand: dy rounded (raw for e4m3) */
+    double *hc = (double *)malloc(sizeof(double) * T * nc); /* h, dug, duu of the chosen columns */
+    double *gc = (double *)malloc(sizeof(double) * T * nc);
+    double *uc = (double *)malloc(sizeof(double) * T * nc);
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < T; ++t) {
+        double *a = xa + t * d;
+        double *r = (double *)malloc(sizeof(double) * d);
+        gemm_input_row(sh, x, t, a);
+        for (int64_t n = 0; n < d; ++n) r[n] = (double)dy[t * d + n];
+        for (int64_t n = 0; n < d; ++n) dyw[t * d + n] = r[n];
+        round_to_gemm_input(sh->wt, r, (int)d);  /* the data-gradient operand */
+        if (!fp8)
+            for (int64_t n = 0; n < d; ++n) dyw[t * d + n] = r[n];
+        for (int32_t c = 0; c < nc; ++c) {
+            const int64_t i = cols[c];
+            double ug = 0.0, uu = 0.0, dh = 0.0;
+            for (int64_t j = 0; j < d; ++j) {
+                ug += w_at(sh->wt, shared->gate, shared->s_gate, I, d, 0, i, j) * a[j];
+                uu += w_at(sh->wt, shared->up, shared->s_up, I, d, 0, i, j) * a[j];
+            }
+            const double sg = 1.0 / (1.0 + exp(-ug));
+            for (int64_t n = 0; n < d; ++n) dh += w_at(sh->wt, shared->down, shared->s_down, d, I, 0, n, i) * r[n];
+            double v[3] = {ug * sg * uu, dh * uu * sg * (1.0 + ug * (1.0 - sg)), dh * ug * sg};
+            if (!fp8)  /* fp32 and bf16 round each value on its own */
+                for (int q = 0; q < 3; ++q) round_to_gemm_input(sh->wt, v + q, 1);
+            hc[t * nc + c] = v[0];
+            gc[t * nc + c] = v[1];
+            uc[t * nc + c] = v[2];
+        }
+        free(r);
+    }
+    if (fp8) {
+        const int64_t ng = (T + 127) / 128;
+        double *gw = (double *)calloc((size_t)(ng * nc * d), sizeof(double));
+        double *uw = (double *)calloc((size_t)(ng * nc * d), sizeof(double));
+        double *dw = (double *)calloc((size_t)(ng * d * nc), sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t gi = 0; gi < ng; ++gi) {
+            const int nr = (int)(T - gi * 128 < 128 ? T - gi * 128 : 128);
+            double *gx = (double *)malloc(sizeof(double) * 128 * d);
+            double *gy = (double *)malloc(sizeof(double) * 128 * d);
+            double *gh = (double *)malloc(sizeof(double) * 128 * nc);
+            double *gg = (double *)malloc(sizeof(double) * 128 * nc);
+            double *gu = (double *)malloc(sizeof(double) * 128 * nc);
+            for (int i = 0; i < nr; ++i) {
+                const int64_t t = gi * 128 + i;
+                for (int64_t m = 0; m < d; ++m) {
+                    gx[i * d + m] = x_at(sh, x, t, m);
+                    gy[i * d + m] = dyw[t * d + m];
+                }
+                for (int32_t c = 0; c < nc; ++c) {
+                    gh[i * nc + c] = hc[t * nc + c];
+                    gg[i * nc + c] = gc[t * nc + c];
+                    gu[i * nc + c] = uc[t * nc + c];
+                }
+            }
+            quant_cols(gx, nr, d);
+            quant_cols(gy, nr, d);
+            quant_cols(gh, nr, nc);
+            quant_cols(gg, nr, nc);
+            quant_cols(gu, nr, nc);
+            double *pg = gw + gi * nc * d, *pu = uw + gi * nc * d, *pd = dw + gi * d * nc;
+            for (int i = 0; i < nr; ++i) {
+                for (int32_t c = 0; c < nc; ++c)
+                    for (int64_t m = 0; m < d; ++m) {
+                        pg[c * d + m] += gg[i * nc + c] * gx[i * d + m];
+                        pu[c * d + m] += gu[i * nc + c] * gx[i * d + m];
+                    }
+                for (int64_t m = 0; m < d; ++m)
+                    for (int32_t c = 0; c < nc; ++c) pd[m * nc + c] += gy[i * d + m] * gh[i * nc + c];
+            }
+            free(gx);
+            free(gy);
+            free(gh);
+            free(gg);
+            free(gu);
+        }
+        for (int64_t q = 0; q < nc * d; ++q) {
+            double a = 0.0, b = 0.0, c = 0.0;
+            for (int64_t gi = 0; gi < ng; ++gi) {
+                a += gw[gi * nc * d + q];
+                b += uw[gi * nc * d + q];
+                c += dw[gi * d * nc + q];
+            }
+            dsg[q] = (float)a;
+            dsu[q] = (float)b;
+            dsd[q] = (float)c;
+        }
+        free(gw);
+        free(uw);
+        free(dw);
+    } else {
+#pragma omp parallel for schedule(static)
+        for (int64_t n = 0; n < d; ++n) {
+            for (int32_t c = 0; c < nc; ++c) {
+                double cg = 0.0, cu = 0.0, cd = 0.0;
+                for (int64_t t = 0; t < T; ++t) {
+                    cg += gc[t * nc + c] * xa[t * d + n];
+                    cu += uc[t * nc + c] * xa[t * d + n];
+                    cd += dyw[t * d + n] * hc[t * nc + c];
+                }
+                dsg[c * d + n] = (float)cg;
+                dsu[c * d + n] = (float)cu;
+                dsd[n * nc + c] = (float)cd;
+            }
+        }
+    }
+    free(xa);
+    free(dyw);
+    free(hc);
+    free(gc);
+    free(uc);
+}
+
 /* Threads later OpenMP regions of this library use (from the calling thread). */
 void oracle_set_threads(int32_t n) { omp_set_num_threads(n > 0 ? n : 1); }
 

@@ -125,9 +125,11 @@ def test_backward_full_size_sampled(cid):
     """The skewed prefill workload (bf16) and the fp8 prefill workload (e4m3
     weights) at full size (T=16384, d=7168, I=2048), routed by the forward on
     the GPU, backward in the launch configuration bench.py --backward times.  The oracle checks dx and dg on 8 sampled tokens
-    (both are per-token), and the weight gradients (dW gate/up/down and the
+    (both are per-token), the weight gradients (dW gate/up/down and the
     router row) of two experts -- the coldest one and one with about 100 rows --
-    from exactly the tokens that chose them; every gradient must be finite."""
+    from exactly the tokens that chose them, and the shared expert's weight
+    gradients (over all 16384 tokens) for four SwiGLU columns; every gradient
+    must be finite."""
     from sparse_expert_routing_amd.layer import layer_from_inputs, upload
     cfg = synth.CONFIGS[cid]
     T, d, I = cfg.T, cfg.d, cfg.I
@@ -178,3 +180,16 @@ def test_backward_full_size_sampled(cid):
             err = max_rel(host(grads[n][e]), o[on][0])
             say(f"[backward] full size: expert {e} {n} max rel err {err:.3e}")
             assert err <= TOL[cfg.wt], (e, n, err)
+    # the shared expert's weight gradients sum over all T tokens: the oracle
+    # computes them for a few SwiGLU columns (its reduced mode, pinned
+    # against its full run on the CPU)
+    cols = np.array([0, 1, I // 2 + 3, I - 1])
+    say(f"[backward] full size: oracle shared-expert weight gradients, columns {cols.tolist()}")
+    o = oracle.backward_shared_cols(oracle.shape(T, d, 256, 8, I, cfg.act, cfg.wt), inp["x"], inp["shared"], dy,
+                                    cols)
+    tc = torch.from_numpy(cols).cuda()
+    for n, on, got in (("ds_gate", "dsg", grads["ds_gate"][tc]), ("ds_up", "dsu", grads["ds_up"][tc]),
+                       ("ds_down", "dsd", grads["ds_down"][:, tc])):
+        err = max_rel(host(got), o[on])
+        say(f"[backward] full size: shared {n} columns max rel err {err:.3e}")
+        assert err <= TOL[cfg.wt], (n, err)

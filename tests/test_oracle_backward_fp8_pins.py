@@ -153,3 +153,19 @@ def test_fp8_backward_is_near_the_unquantised_one():
     assert rel(o8["dx"], X.grad.numpy()) < 0.1
     assert 1e-4 < rel(o8["dx"], X.grad.numpy())  # the quantisers do act
     del a
+
+
+def test_fp8_shared_column_mode_equals_the_full_gradients():
+    """The reduced mode the full-size check uses, with e4m3 weights: the
+    shared expert's weight gradients for a few SwiGLU columns over all 160
+    tokens (a full and a short 128-token group) equal the full run's bit for
+    bit; every operand tile is one column of a group, so cutting the columns
+    changes no tile."""
+    cfg, x, wr, ex, shd, idx, dy = setup()
+    sh = oracle.shape(T, D, E, K, I, "bf16", "e4m3")
+    full = oracle.backward(sh, x, wr, idx, ex, shd, dy)
+    cols = [0, 77, I - 1]
+    part = oracle.backward_shared_cols(sh, x, shd, dy, cols)
+    assert np.array_equal(part["dsg"], full["dsg"][cols])
+    assert np.array_equal(part["dsu"], full["dsu"][cols])
+    assert np.array_equal(part["dsd"], full["dsd"][:, cols])

@@ -127,3 +127,17 @@ def test_sampled_modes_equal_the_full_gradients():
     for n in ("dwr", "dwg", "dwu", "dwd"):
         assert np.allclose(one[n][0], full[n][e], rtol=1e-6, atol=1e-7 * np.abs(full[n][e]).max()), n
     assert np.array_equal(one["dx"], full["dx"][mine])
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_shared_column_mode_equals_the_full_gradients(dt):
+    """The reduced mode the full-size check of the shared expert uses: its
+    weight gradients for a few SwiGLU columns (rows of dsg and dsu, columns
+    of dsd) over all tokens equal the full run's bit for bit."""
+    cfg, sh, x, wr, ex, shd, bias, idx, dy = setup(dt, dt, T=24)
+    full = oracle.backward(sh, x, wr, idx, ex, shd, dy)
+    cols = [0, 5, cfg.I - 1]
+    part = oracle.backward_shared_cols(sh, x, shd, dy, cols)
+    assert np.array_equal(part["dsg"], full["dsg"][cols])
+    assert np.array_equal(part["dsu"], full["dsu"][cols])
+    assert np.array_equal(part["dsd"], full["dsd"][:, cols])
