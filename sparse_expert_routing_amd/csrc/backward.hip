@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void k_bgemm(BGemm p) {
 // pos = poff[e] + r - off[e]; positions up to poff[e+1] past the group's rows
 // are written as zeros (the padding).  Plain: pos = r for r < R, and zeros
 // for R <= pos < dend.
-__global__ __launch_bounds__(256) void k_transpose(int R, int C, const uint16_t *__restrict__ in, int64_t ldi,
+__global__ __launch_bounds__(256) void k_transpose(int R, const uint16_t *__restrict__ in, int64_t ldi,
                                                    int64_t gin, const int32_t *__restrict__ rows, int rdiv,
                                                    const int32_t *__restrict__ off, const int32_t *__restrict__ poff,
                                                    int dend_plain, uint16_t *__restrict__ out, int64_t ldo,
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(256) void k_bwd_swiglu(int64_t n, int I, const floa
 
 // Per token t (one workgroup): s_j = sigmoid(x_t . wr_{e_j}) in fp32, then
 // ds_j, dl_j (stored) and dx[t] = sum_j dl_j wr_{e_j} (written).
-__global__ __launch_bounds__(256) void k_bwd_router(int T, int d, const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(256) void k_bwd_router(int d, const uint16_t *__restrict__ x,
                                                     const float *__restrict__ wr, const int32_t *__restrict__ idx,
                                                     const float *__restrict__ dg, float *__restrict__ dl,
                                                     float *__restrict__ dx) {
@@ -567,7 +567,7 @@ hipError_t swiglu(int64_t rows, int I, const float *P, const float *dh, void *h,
 
 hipError_t router(int T, int d, const uint16_t *x, const float *wr, const int32_t *idx, const float *dg, float *dl,
                   float *dx, hipStream_t s) {
-    hipLaunchKernelGGL(k_bwd_router, dim3(T), dim3(256), 0, s, T, d, x, wr, idx, dg, dl, dx);
+    hipLaunchKernelGGL(k_bwd_router, dim3(T), dim3(256), 0, s, d, x, wr, idx, dg, dl, dx);
     return hipGetLastError();
 }
 
@@ -683,7 +683,7 @@ BwdWs carve(char *base, int T, int d, int I, int k) {
 // 4a .. 4a+3 at columns 8b .. 8b+7 (four 16-byte loads in flight), and
 // writes each column's 4 values as one 8-byte LDS word of output row 8b + j;
 // each output row's 128 bytes then go out as eight 16-byte stores.
-__global__ __launch_bounds__(256) void k_t16(int R, int C, const uint16_t *__restrict__ in, int64_t gin,
+__global__ __launch_bounds__(256) void k_t16(int C, const uint16_t *__restrict__ in, int64_t gin,
                                              uint16_t *__restrict__ out, int64_t ldo, int64_t gout, int coff) {
     __shared__ __attribute__((aligned(16))) uint64_t tile[128 * 16];
     const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 128, g = blockIdx.z, tid = threadIdx.x;
@@ -715,7 +715,7 @@ __global__ __launch_bounds__(256) void k_t16(int R, int C, const uint16_t *__res
 
 hipError_t t16(int R, int C, int G, const uint16_t *in, uint16_t *out, int64_t ldo, int coff, hipStream_t s) {
     if (R % 64 != 0 || C % 128 != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_t16, dim3(R / 64, C / 128, G), dim3(256), 0, s, R, C, in, (int64_t)R * C, out, ldo,
+    hipLaunchKernelGGL(k_t16, dim3(R / 64, C / 128, G), dim3(256), 0, s, C, in, (int64_t)R * C, out, ldo,
                        (int64_t)C * ldo, coff);
     return hipGetLastError();
 }
@@ -728,7 +728,7 @@ hipError_t transpose(int R, int C, int G, const uint16_t *in, int64_t ldi, int64
     const int tiles = off ? R / 64 + kE + 1 : (dend + 63) / 64;
     if (tiles <= 0) return hipSuccess;
     if (tiles > 65535) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_transpose, dim3(C / 64, tiles, G), dim3(256), 0, s, R, C, in, ldi, gin, rows, rdiv, off,
+    hipLaunchKernelGGL(k_transpose, dim3(C / 64, tiles, G), dim3(256), 0, s, R, in, ldi, gin, rows, rdiv, off,
                        poff, dend, out, ldo, gout, coff);
     return hipGetLastError();
 }

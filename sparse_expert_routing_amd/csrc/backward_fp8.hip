@@ -405,7 +405,7 @@ __global__ __launch_bounds__(256) void k_q8_cols(int R, const void *__restrict__
 // then each output row's 128 bytes go out as eight 16-byte stores.  In LDS,
 // output row c holds its 32 words with bits 3-4 of the word index flipped by
 // (c / 16) % 4, so the 64 lanes of a write hit 32 distinct banks twice.
-__global__ __launch_bounds__(256) void k_t8(int R, int C, const uint8_t *__restrict__ in, int64_t gin,
+__global__ __launch_bounds__(256) void k_t8(int C, const uint8_t *__restrict__ in, int64_t gin,
                                             uint8_t *__restrict__ out, int64_t ldo, int64_t gout, int coff) {
     __shared__ __attribute__((aligned(16))) uint32_t tile[128 * 32];
     const int r0 = blockIdx.x * 128, c0 = blockIdx.y * 128, g = blockIdx.z, tid = threadIdx.x;
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(256) void k_tscale(int Rb, int Cb, const uint8_t *_
 
 hipError_t t8(int R, int C, int G, const void *in, uint8_t *out, int64_t ldo, int coff, hipStream_t s) {
     if (R % 128 != 0 || C % 128 != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_t8, dim3(R / 128, C / 128, G), dim3(256), 0, s, R, C, static_cast<const uint8_t *>(in),
+    hipLaunchKernelGGL(k_t8, dim3(R / 128, C / 128, G), dim3(256), 0, s, C, static_cast<const uint8_t *>(in),
                        (int64_t)R * C, out, ldo, (int64_t)C * ldo, coff);
     return hipGetLastError();
 }

@@ -125,15 +125,15 @@ struct LargeGemmArgs {
     // K-grouped form (weight gradients): out_e = A[:, K_e] B[:, K_e]^T with
     // K_e = [kseg[e], kseg[e+1]) (multiples of 64) of A [M, ldk], B [N, ldk],
     // written to out + e * cstride; groups with empty K_e are not written
-    const int32_t *kseg;
-    int ldk;
-    int64_t cstride;
+    const int32_t *kseg = nullptr;
+    int ldk = 0;
+    int64_t cstride = 0;
     // B stored K-major, [G, K, N] (N contiguous), instead of [G, N, K]; with
     // ksplit, K rows [0, ksplit) come from B0 [G, ksplit, N] and the rest
     // from B1 (K = 2 ksplit).  Plain fp32 products only (not dual, not
     // K-grouped).
-    bool b_kn;
-    int ksplit;
+    bool b_kn = false;
+    int ksplit = 0;
 };
 bool bf16_large_gemm_ok(const LargeGemmArgs &g);
 hipError_t launch_bf16_large_gemm(const LargeGemmArgs &g, hipStream_t s);
