@@ -9,9 +9,14 @@
 //
 // Design for gfx950:
 //   - 4 waves in a 2x2 layout, each owning a 128x128 block of the 256x256
-//     tile as 4x4 v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane, in
-//     AGPRs): per 16 of K a wave reads 8 fragments (8 KB) from LDS for 16
-//     MFMAs, half the LDS traffic per MFMA of a 64x64 wave tile;
+//     tile (256 fp32 accumulators per lane, in AGPRs), half the LDS traffic
+//     per MFMA of a 64x64 wave tile.  The forward's SwiGLU gate/up and bf16
+//     store (k_gemm_bf16_mi16) hold it as 8x8 v_mfma_f32_16x16x32_bf16
+//     accumulators, which run the same work at a lower power per FLOP and
+//     so at a higher clock under the chip's power limit; the backward's
+//     fp32 forms and the combine (k_gemm_bf16_large) as 4x4
+//     v_mfma_f32_32x32x16_bf16 accumulators, reading 8 fragments (8 KB) per
+//     16 of K;
 //   - K stages of 64 (each tile row a whole 128-byte line), the A and B slabs
 //     of a stage (32 KB each) in a ring of five LDS units filled straight
 //     from global memory by buffer_load_dwordx4 ... lds (a buffer resource
@@ -781,6 +786,290 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_large(LargeParams p) {
 #undef UNIT
 }
 
+// acc += the 16x16x32 product of two fragments.  A fragment is 16 tile rows
+// (lane l: row l % 16) by 32 K (K values 8 (l / 16) .. +7); the operands are
+// swapped, so the accumulator holds the transposed 16x16 block: lane l owns
+// tile row l % 16 and its 4 consecutive columns 4 (l / 16) .. +3.  Issued
+// from inline assembly with the accumulator tied to the destination: with
+// the builtin, the register allocator does not keep 64 four-register
+// accumulators in place in the 256 AGPRs and shuffles them between MFMAs.
+// The compiler still waits for the fragments' LDS reads (asm inputs); the
+// accumulators are read only after the tile's K loop, past the barrier.
+__device__ __forceinline__ void mma16t(bf16x8 a, bf16x8 b, f32x4 &c) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
+}
+
+// The forward's SwiGLU gate/up (routed or shared) and routed down (bf16
+// store) on the same persistent 256x256 tiles, LDS ring, tile order and
+// epilogue placement as k_gemm_bf16_large, with each wave's 128x128 block
+// as 8x8 v_mfma_f32_16x16x32_bf16 accumulators instead of 4x4 of
+// v_mfma_f32_32x32x16_bf16.  The work per K step is the same, but the
+// 16x16 instruction draws less power for the same FLOPs, so the chip holds
+// a higher clock under its power limit (register-only loops on every CU:
+// about 2.1 GHz against 1.8).  A stage of 64 K is 2 steps of 32.
+template <int EPI, bool ROUTED>
+__global__ __launch_bounds__(256, 1) void k_gemm_bf16_mi16(LargeParams p) {
+    static_assert(EPI == EPI_SWIGLU || EPI == EPI_STORE, "register bf16 epilogues only");
+    constexpr bool DUAL = EPI == EPI_SWIGLU;
+    constexpr int BN = DUAL ? LB / 2 : LB;      // output columns per tile
+    constexpr int kEpiStores = DUAL ? 16 : 32;  // buffer stores per lane per epilogue
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[NUNIT * UNIT_ELEMS];  // 160 KB
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int q = lane >> 4, l16 = lane & 15;
+    const int K = p.K;
+    const int nk = K / LK;
+
+    TileMap tm;
+    int Mt, total;
+    const int NT = p.N / BN;
+    if (ROUTED) {
+        tilemap_init(tm, p.offsets);
+        Mt = tm.total;
+        total = Mt * NT;
+    } else {
+        Mt = (p.M + LM - 1) / LM;
+        total = Mt * NT;
+    }
+    const int P = gridDim.x;
+
+    int drow[8], dcol[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = 8 * (wave + 4 * i) + (lane >> 3);
+        drow[i] = row;
+        dcol[i] = ((lane & 7) ^ (row & 7) ^ ((row >> 3) & 1)) * 8;
+    }
+
+    int e = 0, m0 = 0, m_end = 0, n0 = 0;
+    const uint32_t a_rows_total = p.a_rows ? (uint32_t)(p.M / p.a_div) : (uint32_t)p.M;
+    const __amdgpu_buffer_rsrc_t rA = buf_rsrc(p.A, a_rows_total * (uint32_t)K * 2u);
+    const uint32_t b_bytes = (uint32_t)p.N * (uint32_t)K * 2u;
+    const uint16_t *pBg = p.B0, *pBu = p.B1;
+    uint32_t aoff[8], boff[8];
+
+#define UNIT(u) (smem + (u) * UNIT_ELEMS)
+#define ISSUE_A(st_, i, unit_) \
+        dma_buf(rA, aoff[i], (uint32_t)min((st_), nk - 1) * (LK * 2), (unit_) + (wave + 4 * (i)) * 512)
+#define B_RSRC()                                                                               \
+        const __amdgpu_buffer_rsrc_t rBg_ = buf_rsrc(uniform_ptr(pBg), b_bytes);               \
+        const __amdgpu_buffer_rsrc_t rBu_ = DUAL ? buf_rsrc(uniform_ptr(pBu), b_bytes) : rBg_;
+#define ISSUE_B(st_, i, unit_)                                                                 \
+        dma_buf((DUAL && (i) >= 4) ? rBu_ : rBg_, boff[i], (uint32_t)min((st_), nk - 1) * (LK * 2), \
+                (unit_) + (wave + 4 * (i)) * 512)
+#define TILE_SETUP(tt)                                                                         \
+    {                                                                                          \
+        int mt_, nt_;                                                                          \
+        if (ROUTED) {                                                                          \
+            tilemap_tile(tm, (tt), NT, e, m0, m_end, nt_);                                     \
+        } else {                                                                               \
+            const int gsz_ = kGroupM * NT;                                                     \
+            const int grp_ = (tt) / gsz_, within_ = (tt) - grp_ * gsz_;                        \
+            const int mfirst_ = grp_ * kGroupM;                                                \
+            const int gm_ = min(kGroupM, Mt - mfirst_);                                        \
+            mt_ = mfirst_ + within_ % gm_;                                                     \
+            nt_ = within_ / gm_;                                                               \
+            e = 0;                                                                             \
+            m0 = mt_ * LM;                                                                     \
+            m_end = p.M;                                                                       \
+        }                                                                                      \
+        e = __builtin_amdgcn_readfirstlane(e);                                                 \
+        m0 = __builtin_amdgcn_readfirstlane(m0);                                               \
+        m_end = __builtin_amdgcn_readfirstlane(m_end);                                         \
+        n0 = nt_ * BN;                                                                         \
+        pBg = p.B0 + (size_t)e * p.N * K;                                                      \
+        pBu = DUAL ? p.B1 + (size_t)e * p.N * K : pBg;                                         \
+        int ar_[8];                                                                            \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) ar_[i] = min(m0 + drow[i], m_end - 1);    \
+        if (p.a_rows) {                                                                        \
+            _Pragma("unroll") for (int i = 0; i < 8; ++i) ar_[i] = p.a_rows[ar_[i]];            \
+            _Pragma("unroll") for (int i = 0; i < 8; ++i) ar_[i] /= p.a_div;                    \
+        }                                                                                      \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                        \
+            aoff[i] = ((uint32_t)ar_[i] * (uint32_t)K + (uint32_t)dcol[i]) * 2u;               \
+            const int r = drow[i];                                                             \
+            const int br = DUAL ? n0 + (r & (BN - 1)) : n0 + r;                                \
+            boff[i] = ((uint32_t)br * (uint32_t)K + (uint32_t)dcol[i]) * 2u;                   \
+            if (m0 + r >= m_end) aoff[i] = kOobOff;                                             \
+        }                                                                                      \
+    }
+#define PROLOGUE_LOADS()                                                                       \
+    {                                                                                          \
+        B_RSRC()                                                                               \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) ISSUE_A(0, i, UNIT(0));                  \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) ISSUE_B(0, i, UNIT(1));                  \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) ISSUE_A(1, i, UNIT(2));                  \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) ISSUE_B(1, i, UNIT(3));                  \
+    }
+
+    int t = (blockIdx.x & 7) * (P >> 3) + (blockIdx.x >> 3);
+    if (t < total) {
+        TILE_SETUP(t);
+        PROLOGUE_LOADS();
+    }
+    bool first = true;
+    for (; t < total; t += P) {
+        f32x4 acc[8][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // B operand rows of column block j (16 columns): the SwiGLU tile's B
+        // holds 128 gate rows, then 128 up rows; a wave takes 64 of each.
+#define B_ROW16(j) (DUAL ? (((j) >> 2) * 128 + wn * 64 + ((j) & 3) * 16) : (wn * 128 + (j) * 16))
+#define FRAG16(unit, row0, pc) (*reinterpret_cast<const bf16x8 *>((unit) + lds_piece((row0) + l16, (pc))))
+        // One 32-wide K step: 64 MFMAs on (AC, BC), row block by row block.
+        // The next step's 16 fragments (B first, then A; from the units nA /
+        // nB at piece 4 s + lane / 16) are read one per 4 MFMAs; the load
+        // DMA(x), if any, follows MFMA x.  Scheduling barriers fix the order.
+#define STEP16(AC, BC, AN, BN_, nA, nB, pc, DMA, NB_)                                          \
+        _Pragma("unroll") for (int x = 0; x < 64; ++x) {                                       \
+            if (((x) & 3) == 0) {                                                              \
+                if ((x) < 32) {                                                                \
+                    if ((NB_) > 0) BN_[(x) >> 2] = FRAG16((nB), B_ROW16((x) >> 2), (pc));      \
+                } else if ((((x) - 32) >> 2) < 2 * (NB_)) {                                    \
+                    AN[((x) - 32) >> 2] = FRAG16((nA), wm * 128 + (((x) - 32) >> 2) * 16, (pc)); \
+                }                                                                              \
+            }                                                                                  \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+            if (2 * (NB_) > (x >> 3)) /* 16-row blocks past the group's end: no MFMA */         \
+                mma16t(AC[x >> 3], BC[x & 7], acc[x >> 3][x & 7]);                             \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+            DMA(x);                                                                            \
+            __builtin_amdgcn_sched_barrier(0);                                                 \
+        }
+
+        // A_0, B_0 landed for every wave (behind them: A_1, B_1 and maybe the
+        // previous epilogue's stores), then step 0's fragments.
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (!first)
+            wait_vmcnt_lds<16 + kEpiStores>();
+        else
+            wait_vmcnt_lds<16>();
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        B_RSRC()
+        const int live = m_end - m0 - wm * 128;
+        bf16x8 a0[8], b0[8], a1[8], b1[8];
+        {
+            const uint16_t *sA = UNIT(0), *sB = UNIT(1);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a0[i] = FRAG16(sA, wm * 128 + i * 16, q);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) b0[j] = FRAG16(sB, B_ROW16(j), q);
+        }
+
+        // Stage kt = 2 steps of 32 K.  Step 0 streams A_{kt+2} into the free
+        // unit and reads step 1's fragments; then every fragment of stage kt
+        // is in registers, so the barrier (once A_{kt+1} and B_{kt+1} landed:
+        // only A_{kt+2}'s 8 loads may remain in flight) frees A_kt's and
+        // B_kt's units.  Step 1 streams B_{kt+2} into A_kt's unit and reads
+        // stage kt+1's first fragments.
+#define DMA16_S0(x) if (((x) & 7) == 2) ISSUE_A(kt + 2, (x) >> 3, fA)
+#define DMA16_S1(x) if (((x) & 7) == 2) ISSUE_B(kt + 2, (x) >> 3, fB)
+#define KLOOP16(NB_)                                                                           \
+        {                                                                                      \
+            int u0 = 0;                                                                        \
+            for (int kt = 0; kt < nk; ++kt) {                                                  \
+                const int u1 = u0 + 1 - (u0 + 1 >= NUNIT ? NUNIT : 0);                         \
+                const int u2 = u0 + 2 - (u0 + 2 >= NUNIT ? NUNIT : 0);                         \
+                const int u3 = u0 + 3 - (u0 + 3 >= NUNIT ? NUNIT : 0);                         \
+                const int u4 = u0 + 4 - (u0 + 4 >= NUNIT ? NUNIT : 0);                         \
+                const uint16_t *cA = UNIT(u0), *cB = UNIT(u1);                                 \
+                uint16_t *fA = UNIT(u4), *fB = UNIT(u0);                                       \
+                STEP16(a0, b0, a1, b1, cA, cB, 4 + q, DMA16_S0, NB_);                          \
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);                                       \
+                wait_vmcnt_lds<8>();                                                           \
+                __builtin_amdgcn_s_barrier();                                                  \
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);                                       \
+                const uint16_t *nA = UNIT(u2), *nB = UNIT(u3);                                 \
+                STEP16(a1, b1, a0, b0, nA, nB, q, DMA16_S1, NB_);                              \
+                u0 = u2;                                                                       \
+            }                                                                                  \
+        }
+        switch (live <= 0 ? 0 : live >= 128 ? 4 : (live + 31) / 32) {
+            case 4: KLOOP16(4) break;
+            case 3: KLOOP16(3) break;
+            case 2: KLOOP16(2) break;
+            case 1: KLOOP16(1) break;
+            default: KLOOP16(0) break;
+        }
+#undef KLOOP16
+        // the MFMAs are assembly the compiler does not track: give the last
+        // one its result latency before any accumulator read
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#undef DMA16_S0
+#undef DMA16_S1
+#undef STEP16
+#undef FRAG16
+#undef B_ROW16
+        __syncthreads();  // every wave done with the ring (and its loads landed)
+        first = false;
+        const int cm0 = m0, cm_end = m_end, cn0 = n0;
+        // the next tile's first two stages land while the epilogue runs
+        if (t + P < total) {
+            TILE_SETUP(t + P);
+            PROLOGUE_LOADS();
+        }
+        // Register epilogue: lane owns tile rows wm*128 + 16i + lane % 16 and,
+        // per 16-column block, the 4 columns 4 (lane / 16) .. +3.  Two blocks'
+        // values, swapped between the 16-lane rows of the wave (lanes
+        // 16-31 <-> 0-15 and 48-63 <-> 32-47), leave each lane 8 consecutive
+        // columns of one block: block 2jp + (lane / 16) % 2, columns
+        // 8 (lane / 32) .. +7, one 16-byte store.  Padding rows' stores get an
+        // offset past the end of the output, which the hardware drops, so
+        // every lane issues every store (the wait count above relies on it).
+        const __amdgpu_buffer_rsrc_t rOut = buf_rsrc(p.out, (uint32_t)p.M * (uint32_t)p.N * 2u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = cm0 + wm * 128 + 16 * i + l16;
+            const uint32_t obase =
+                row < cm_end ? ((uint32_t)row * (uint32_t)p.N + (uint32_t)cn0) * 2u : 0xfffff000u;
+            const bool blk = cm_end - cm0 - wm * 128 > 16 * i;  // block has rows (uniform)
+#pragma unroll
+            for (int jp = 0; jp < (DUAL ? 2 : 4); ++jp) {
+                __builtin_amdgcn_sched_barrier(0);
+                uint32_t w[2][2];  // [block 2jp + h][dword]: 4 bf16 values
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int j = 2 * jp + h;
+                    if constexpr (DUAL) {
+                        w[h][0] = w[h][1] = 0;
+                        if (blk) {  // an empty block's stores are dropped: skip its math
+                            float v[4];
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) v[u] = swiglu(acc_read(acc[i][j][u]), acc_read(acc[i][j + 4][u]));
+                            w[h][0] = pack_bf16x2(v[0], v[1]);
+                            w[h][1] = pack_bf16x2(v[2], v[3]);
+                        }
+                    } else {
+                        w[h][0] = pack_bf16x2(acc_read(acc[i][j][0]), acc_read(acc[i][j][1]));
+                        w[h][1] = pack_bf16x2(acc_read(acc[i][j][2]), acc_read(acc[i][j][3]));
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const auto sw = __builtin_amdgcn_permlane16_swap(w[0][k], w[1][k], false, false);
+                    w[0][k] = sw[0];
+                    w[1][k] = sw[1];
+                }
+                const int col = (DUAL ? wn * 64 : wn * 128) + 16 * (2 * jp + (q & 1)) + 8 * (q >> 1);
+                __builtin_amdgcn_raw_buffer_store_b128(i32x4{(int)w[0][0], (int)w[0][1], (int)w[1][0], (int)w[1][1]},
+                                                      rOut, obase + (uint32_t)col * 2u, 0, 0);
+            }
+        }
+    }
+#undef TILE_SETUP
+#undef PROLOGUE_LOADS
+#undef B_RSRC
+#undef ISSUE_A
+#undef ISSUE_B
+#undef UNIT
+}
+
 int cu_count() {
     static int cached[64];
     int dev = 0;
@@ -883,9 +1172,9 @@ hipError_t launch_ffn_bf16_large(const FfnArgs &a, hipStream_t s) {
         p.N = a.I;
         p.out = static_cast<uint16_t *>(a.h);
         if (routed)
-            hipLaunchKernelGGL((k_gemm_bf16_large<EPI_SWIGLU, true>), dim3(P), dim3(256), 0, s, p);
+            hipLaunchKernelGGL((k_gemm_bf16_mi16<EPI_SWIGLU, true>), dim3(P), dim3(256), 0, s, p);
         else
-            hipLaunchKernelGGL((k_gemm_bf16_large<EPI_SWIGLU, false>), dim3(P), dim3(256), 0, s, p);
+            hipLaunchKernelGGL((k_gemm_bf16_mi16<EPI_SWIGLU, false>), dim3(P), dim3(256), 0, s, p);
     }
     if (a.phases & 2) {
         LargeParams q{};
@@ -905,9 +1194,9 @@ hipError_t launch_ffn_bf16_large(const FfnArgs &a, hipStream_t s) {
         } else {
             q.out = static_cast<uint16_t *>(a.y);
             if (routed)
-                hipLaunchKernelGGL((k_gemm_bf16_large<EPI_STORE, true>), dim3(P), dim3(256), 0, s, q);
+                hipLaunchKernelGGL((k_gemm_bf16_mi16<EPI_STORE, true>), dim3(P), dim3(256), 0, s, q);
             else
-                hipLaunchKernelGGL((k_gemm_bf16_large<EPI_STORE, false>), dim3(P), dim3(256), 0, s, q);
+                hipLaunchKernelGGL((k_gemm_bf16_mi16<EPI_STORE, false>), dim3(P), dim3(256), 0, s, q);
         }
     }
     return hipGetLastError();
