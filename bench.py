@@ -47,7 +47,7 @@ PEAK_BF16_TFLOPS = 2516.6   # dense bf16 MFMA, MI355X
 PEAK_FP8_TFLOPS = 5033.2    # dense fp8 MFMA, MI355X
 PEAK_HBM_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "sparse_expert_routing_amd", "csrc", "ffn_bf16_large.hip")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_gemm_bf16_large_gateup_traffic_prefill-zipf-bf16.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_gemm_bf16_mi16_gateup_traffic_prefill-zipf-bf16.md")
 METRIC = "MoE-layer tokens/s (T=16384,d=7168,256e top-8) + % of MFMA/HBM peak"
 TRAFFIC_WORKLOAD = "prefill-zipf-bf16 T16384 d7168 I2048"  # the workload the counter summary covers
 
@@ -324,7 +324,7 @@ def measure(cfg, K, warmup, curve_steps, fresh_batches, backward=False):
                         phase["expert_down"], peak_flops)
     large = A >= 128 * E
     kname = ("k_gemm_fp8_mx" if large and I % 256 == 0 and d % 256 == 0 else "k_gemm_fp8") if cfg.wt == "e4m3" else \
-        ("k_gemm_bf16_large" if large else "k_gemm_skinny" if A <= 4 * E else "k_gemm_bf16")
+        ("k_gemm_bf16_mi16" if large else "k_gemm_skinny" if A <= 4 * E else "k_gemm_bf16")
     total_flops = 2.0 * T * d * E + 6.0 * (A + T) * d * I
     ms_step = wall / K * 1e3
     log(f"[bench] {cfg.name}: {ms_step:.3f} ms/step, phases (ms): " + ", ".join(f"{n} {v:.3f}" for n, v in phase.items()))

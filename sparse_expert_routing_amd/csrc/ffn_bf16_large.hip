@@ -799,6 +799,20 @@ __device__ __forceinline__ void mma16t(bf16x8 a, bf16x8 b, f32x4 &c) {
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
 }
 
+// The 16-byte piece swizzle of the 16x16 kernel: piece c of tile row `row`
+// sits at position c ^ s(row), s(row) = (row & 7) with its two low bits
+// swapped, ^ 2 for rows 8-15 of each 16.  A fragment read covers 16 rows and
+// 4 consecutive pieces (lanes 16q .. 16q+15: piece 4s + q); the lanes LDS
+// serves together (8 of one 32-lane half with the 8 beside them in the
+// other, and any 8 or 16 consecutive lanes) then hit distinct banks, where
+// the 32x32 kernel's swizzle puts rows r and r ^ 2 with pieces c and c ^ 2
+// on the same banks.
+__device__ __forceinline__ int swz16(int row) {
+    const int r3 = row & 7;
+    return ((r3 & 4) | ((r3 & 1) << 1) | ((r3 >> 1) & 1)) ^ (((row >> 3) & 1) << 1);
+}
+__device__ __forceinline__ int lds_piece16(int row, int c) { return row * LK + ((c ^ swz16(row)) * 8); }
+
 // The forward's SwiGLU gate/up (routed or shared) and routed down (bf16
 // store) on the same persistent 256x256 tiles, LDS ring, tile order and
 // epilogue placement as k_gemm_bf16_large, with each wave's 128x128 block
@@ -840,7 +854,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_mi16(LargeParams p) {
     for (int i = 0; i < 8; ++i) {
         const int row = 8 * (wave + 4 * i) + (lane >> 3);
         drow[i] = row;
-        dcol[i] = ((lane & 7) ^ (row & 7) ^ ((row >> 3) & 1)) * 8;
+        dcol[i] = ((lane & 7) ^ swz16(row)) * 8;
     }
 
     int e = 0, m0 = 0, m_end = 0, n0 = 0;
@@ -920,7 +934,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_mi16(LargeParams p) {
         // B operand rows of column block j (16 columns): the SwiGLU tile's B
         // holds 128 gate rows, then 128 up rows; a wave takes 64 of each.
 #define B_ROW16(j) (DUAL ? (((j) >> 2) * 128 + wn * 64 + ((j) & 3) * 16) : (wn * 128 + (j) * 16))
-#define FRAG16(unit, row0, pc) (*reinterpret_cast<const bf16x8 *>((unit) + lds_piece((row0) + l16, (pc))))
+#define FRAG16(unit, row0, pc) (*reinterpret_cast<const bf16x8 *>((unit) + lds_piece16((row0) + l16, (pc))))
         // One 32-wide K step: 64 MFMAs on (AC, BC), row block by row block.
         // The next step's 16 fragments (B first, then A; from the units nA /
         // nB at piece 4 s + lane / 16) are read one per 4 MFMAs; the load
