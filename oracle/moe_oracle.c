@@ -134,7 +134,25 @@ static uint8_t e4m3_enc(float vf) {
 
 /* OCP MX E8M0 scale byte: an 8-bit biased exponent with no sign and no
  * mantissa, bias 127; 255 encodes NaN. */
-static double e8m0_dec(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+static double e8m0_formula(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+
+/* The formula, evaluated once for each of the 256 bytes (the weight loops
+ * decode a block scale per element). */
+static double e8m0_table[256];
+static int e8m0_table_ready;
+
+static double e8m0_dec(uint8_t e) {
+    if (!e8m0_table_ready) {
+#pragma omp critical(e8m0_init)
+        {
+            if (!e8m0_table_ready) {
+                for (int i = 0; i < 256; ++i) e8m0_table[i] = e8m0_formula((uint8_t)i);
+                __atomic_store_n(&e8m0_table_ready, 1, __ATOMIC_RELEASE);
+            }
+        }
+    }
+    return e8m0_table[e];
+}
 
 /* The E8M0 byte of a power of two s (2^-127 <= s <= 2^127): s = 0.5 * 2^ex
  * by frexp, so its exponent is ex - 1. */

@@ -12,7 +12,7 @@ import torch
 import synth
 from sparse_expert_routing_amd import _lib
 from sparse_expert_routing_amd.layer import layer_from_inputs, upload
-from tests.gpu_util import say
+from tests.gpu_util import inputs_of, say
 
 pytestmark = pytest.mark.gpu
 
@@ -32,7 +32,7 @@ def _bits(t):
 def test_layer_bitwise_deterministic_full_size(cid):
     cfg = synth.CONFIGS[cid]
     say(f"[determinism] {cfg.name}: two forward + bias steps")
-    inp = synth.make_inputs(cfg)
+    inp = inputs_of(cfg)
     layer = layer_from_inputs(inp)
     x = upload(inp["x"])
     runs = []

@@ -10,7 +10,7 @@ import torch
 import synth
 from sparse_expert_routing_amd import _lib
 from sparse_expert_routing_amd.layer import layer_from_inputs, upload
-from tests.gpu_util import say
+from tests.gpu_util import inputs_of, say
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +39,7 @@ def test_layer_step_replays_from_a_hip_graph(case):
     cfg = CASES[case]()
     steps = 4
     say(f"[graph] {cfg.name}: {steps} eager loop steps, then one captured step replayed {steps} times")
-    inp = synth.make_inputs(cfg)
+    inp = inputs_of(cfg)
     layer = layer_from_inputs(inp)
     x = upload(inp["x"])
 

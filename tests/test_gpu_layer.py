@@ -18,7 +18,7 @@ import oracle
 import synth
 from sparse_expert_routing_amd import _lib
 from sparse_expert_routing_amd.layer import layer_from_inputs, upload
-from tests.gpu_util import NEAR_TIE, TOL, bf16v, host, max_rel, say
+from tests.gpu_util import NEAR_TIE, TOL, bf16v, host, inputs_of, max_rel, say
 
 pytestmark = pytest.mark.gpu
 
@@ -214,7 +214,7 @@ def test_layer_config4_full_size():
     at every group's first and last row and at the 256-row tile edges; y on
     12 sampled tokens through the oracle's whole forward."""
     cfg = synth.CONFIGS[4]
-    inp = synth.make_inputs(cfg)
+    inp = inputs_of(cfg)
     check_layer(cfg, inp, n_sample=12, n_rows=512)
 
 
@@ -223,7 +223,7 @@ def test_layer_config5_full_size():
     activations): the persistent e4m3 GEMMs for the routed and shared
     experts; checked as the skewed prefill workload is."""
     cfg = synth.CONFIGS[5]
-    inp = synth.make_inputs(cfg)
+    inp = inputs_of(cfg)
     check_layer(cfg, inp, n_sample=12, n_rows=512)
 
 
@@ -336,7 +336,7 @@ def test_balancing_loop_full_size():
     d=7168, I=2048): 24 steps of the whole layer as bench.py runs them, each
     checked stage by stage against the oracle (see loop_parity)."""
     cfg = synth.CONFIGS[4]
-    imb = loop_parity(cfg, synth.make_inputs(cfg), 24, whole_layer=True)
+    imb = loop_parity(cfg, inputs_of(cfg), 24, whole_layer=True)
     assert imb[-1] < imb[0]
 
 
