@@ -94,22 +94,11 @@ static double e4m3_formula(uint8_t c) {
     return s ? -v : v;
 }
 
-/* The formula, evaluated once for each of the 256 codes. */
+/* The formula, evaluated for each of the 256 codes when the library loads
+ * (codec_tables below). */
 static double e4m3_table[256];
-static int e4m3_table_ready;
 
-static double e4m3_dec(uint8_t c) {
-    if (!e4m3_table_ready) {
-#pragma omp critical(e4m3_init)
-        {
-            if (!e4m3_table_ready) {
-                for (int i = 0; i < 256; ++i) e4m3_table[i] = e4m3_formula((uint8_t)i);
-                __atomic_store_n(&e4m3_table_ready, 1, __ATOMIC_RELEASE);
-            }
-        }
-    }
-    return e4m3_table[c];
-}
+static double e4m3_dec(uint8_t c) { return e4m3_table[c]; }
 
 /* Nearest E4M3FN code to v (finite), ties to the code with even mantissa,
  * magnitudes beyond 448 saturate to 448.  Written as a search over the 127
@@ -136,22 +125,19 @@ static uint8_t e4m3_enc(float vf) {
  * mantissa, bias 127; 255 encodes NaN. */
 static double e8m0_formula(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
 
-/* The formula, evaluated once for each of the 256 bytes (the weight loops
- * decode a block scale per element). */
+/* The formula, evaluated for each of the 256 bytes when the library loads
+ * (the weight loops decode a block scale per element). */
 static double e8m0_table[256];
-static int e8m0_table_ready;
 
-static double e8m0_dec(uint8_t e) {
-    if (!e8m0_table_ready) {
-#pragma omp critical(e8m0_init)
-        {
-            if (!e8m0_table_ready) {
-                for (int i = 0; i < 256; ++i) e8m0_table[i] = e8m0_formula((uint8_t)i);
-                __atomic_store_n(&e8m0_table_ready, 1, __ATOMIC_RELEASE);
-            }
-        }
+static double e8m0_dec(uint8_t e) { return e8m0_table[e]; }
+
+/* Both decode tables, filled from their formulas before any exported
+ * function can run. */
+__attribute__((constructor)) static void codec_tables(void) {
+    for (int i = 0; i < 256; ++i) {
+        e4m3_table[i] = e4m3_formula((uint8_t)i);
+        e8m0_table[i] = e8m0_formula((uint8_t)i);
     }
-    return e8m0_table[e];
 }
 
 /* The E8M0 byte of a power of two s (2^-127 <= s <= 2^127): s = 0.5 * 2^ex
