@@ -41,7 +41,8 @@ def sample_tokens(T, n, seed=0):
 def edge_rows(offsets, A, n_min, seed=0):
     """Permuted rows at every non-empty expert group's first and last row and
     at the 256-row tile edges inside each group (the last row of one tile and
-    the first of the next), topped up with random rows to at least n_min."""
+    the first of the next), topped up with distinct random rows to at least
+    min(n_min, A) rows (all A rows when n_min >= A)."""
     nz = np.where(np.diff(offsets) > 0)[0]
     parts = [offsets[nz], offsets[nz + 1] - 1]
     for e in nz:
@@ -50,8 +51,10 @@ def edge_rows(offsets, A, n_min, seed=0):
     rows = np.unique(np.concatenate(parts))
     rows = rows[(rows >= 0) & (rows < A)]
     if len(rows) < n_min:
+        rest = np.setdiff1d(np.arange(A), rows)
         rng = np.random.default_rng(seed)
-        rows = np.unique(np.concatenate([rows, rng.integers(0, A, n_min - len(rows) + 16)]))
+        extra = rng.choice(rest, min(n_min - len(rows), len(rest)), replace=False)
+        rows = np.unique(np.concatenate([rows, extra]))
     return rows.astype(np.int32)
 
 
