@@ -24,9 +24,10 @@ Prints ONE JSON line on stdout (progress goes to stderr).
                  (steps past --steps run untimed, continuing the same loop)
   cpu_baseline   the CPU oracle (fp64, plain loops) timed on a sample of the
                  same workload's tokens through the whole forward
-  sub_results    (default workload only) the fp8 prefill and the decode
-                 workloads, 20 timed steps each, with their own roofline
-                 entries
+  sub_results    (default workload only) the fp8 prefill, decode, mid-size
+                 (T=2048, d=2048, I=512) and EP8-shard (one GPU's 32 experts
+                 of an 8-way expert-parallel layer) workloads, 20 timed steps
+                 each, with their own roofline entries
 
 --dense-reference instead prints {"dense_reference": [...]}: the routed
 gate/up kernel on one dense group (every row on one expert, M = 65536 and
@@ -122,7 +123,7 @@ def main():
     if args.config == 4 and not args.no_sub:
         # the other full-size workloads, each with its own roofline entry
         sub = {}
-        for cid in (5, 3):
+        for cid in (5, 3, 2, 6):
             release()
             r, _ = measure(synth.CONFIGS[cid], max(10, min(K, 20)), min(args.warmup, 3), 0, 0)
             sub[r["config"]["workload"]] = r
