@@ -383,7 +383,7 @@ size_t ffn_shared_split_bytes(int M, int d, int I, int wt) {
 // five-unit LDS ring keeps more of each expert's weight stream in flight than
 // this file's double-buffered 128 x 128 tiles: at T=2048, d=2048, I=512 the
 // routed gate/up took 0.224 ms against 0.250-0.254 and the down 0.138
-// against 0.154-0.158 (same box, alternating runs).  The large kernels'
+// against 0.154-0.158 (one GPU, alternating runs).  The large kernels'
 // own shape checks are applied at twice the rows: that meets their
 // 128-rows-per-group floor exactly when the groups average 64, and their
 // 32-bit offset bounds only get stricter.
